@@ -1,0 +1,294 @@
+"""Seeded synthetic inputs for the speculative verification step.
+
+This module only *makes inputs*: target logits, the draft distributions q and the
+draft tokens a stand-in drafter proposes from them, candidate trees, and the
+caller-side uniforms. It contains no part of the verifier (no acceptance test, no
+residual, no temperature softmax of the target, no sampling of emitted tokens), so
+both the float64 oracle and the GPU path can consume the same arrays without
+sharing any of the method's arithmetic.
+
+Recipes (shapes and distributions of the workloads the verifier is measured on):
+
+* chain  -- target logits ~ N(0, sigma^2), optionally with a fraction of entries
+  boosted by a constant to give peaked rows, stored as bf16 (round-to-nearest-even)
+  or fp32.  The drafter's logits are the *stored* target logits plus N(0, tau^2)
+  noise; q = softmax of that (no temperature: the temperature is a target-side
+  processor), stored fp32.  Draft token i is drawn from the stored fp32 row q_i by
+  the drafter's own inverse-CDF draw, so q_i(x_i) > 0 always holds.
+* greedy -- target logits ~ N(0, sigma^2) in bf16; each draft token equals the
+  row's first maximal index with probability `match_prob`, otherwise a uniformly
+  random *other* id.  (The drafter stand-in needs the row maximum to imitate a
+  well-aligned draft; the verifier's own argmax lives elsewhere.)
+* tree   -- per request a random ancestor-closed tree: node 0 is the frontier
+  root, node i > 0 picks a uniformly random parent among earlier nodes whose depth
+  is below `max_depth` and that have fewer than `max_children` children.  The
+  children of a node carry distinct tokens drawn without replacement from
+  softmax(row + N(0, tau^2)) of that node's own row (a noisy drafter).  The
+  optional `boost` adds a constant to the target logit of every child token in
+  its parent's row, which makes deep acceptance paths likely (used to exercise
+  depth).
+* uniforms -- fp32 values k * 2^-24 with k uniform on [0, 2^24), so every
+  uniform is exactly representable and strictly below 1.
+
+Every array comes from `numpy.random.Generator(PCG64)` streams spawned from one
+`SeedSequence(seed)`, so a (recipe, seed) pair always reproduces the same inputs.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "ChainInputs", "GreedyInputs", "TreeInputs",
+    "make_chain", "make_greedy", "make_tree", "make_config",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "uniforms", "CONFIGS",
+]
+
+TWO_M24 = np.float64(2.0 ** -24)
+
+
+# --------------------------------------------------------------------------- bf16
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return raw uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32)
+    bias = ((b >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    out = ((b + bias) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen raw bfloat16 bits to float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def uniforms(rng: np.random.Generator, shape) -> np.ndarray:
+    """fp32 uniforms on the 2^-24 grid of [0, 1)."""
+    k = rng.integers(0, 1 << 24, size=shape, dtype=np.int64)
+    return (k.astype(np.float64) * TWO_M24).astype(np.float32)
+
+
+def _drafter_softmax(z: np.ndarray) -> np.ndarray:
+    """The stand-in drafter's distribution: softmax over the last axis in float64."""
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def _draw_from_rows(rng: np.random.Generator, q: np.ndarray) -> np.ndarray:
+    """The stand-in drafter's sampler: one token per row of `q` (any leading shape)."""
+    flat = q.reshape(-1, q.shape[-1]).astype(np.float64)
+    c = np.cumsum(flat, axis=1)
+    t = rng.random(flat.shape[0]) * c[:, -1]
+    idx = np.empty(flat.shape[0], dtype=np.int64)
+    for r in range(flat.shape[0]):
+        idx[r] = np.searchsorted(c[r], t[r], side="right")
+    idx = np.minimum(idx, flat.shape[1] - 1)
+    # t can round up to the row total; then fall back to the last positive entry so a
+    # proposal never has zero draft probability
+    for r in np.nonzero(flat[np.arange(flat.shape[0]), idx] <= 0)[0]:
+        idx[r] = np.nonzero(flat[r] > 0)[0][-1]
+    return idx.reshape(q.shape[:-1]).astype(np.int32)
+
+
+def _normal_f32(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    x *= np.float32(sigma)
+    return x
+
+
+# --------------------------------------------------------------------------- chain
+@dataclass
+class ChainInputs:
+    B: int
+    gamma: int
+    V: int
+    temperature: np.float32
+    logit_dtype: str              # "bf16" (uint16 bits) or "f32"
+    logits: np.ndarray            # [B, gamma+1, V] uint16 bits or float32
+    q: np.ndarray                 # [B, gamma, V] float32
+    tokens: np.ndarray            # [B, gamma] int32
+    u: np.ndarray                 # [B, gamma+1] float32
+    q_dtype: str = "f32"
+    meta: dict = field(default_factory=dict)
+
+    def logits_f32(self) -> np.ndarray:
+        return bf16_bits_to_f32(self.logits) if self.logit_dtype == "bf16" else self.logits
+
+    @property
+    def nbytes(self) -> int:
+        return self.logits.nbytes + self.q.nbytes + self.tokens.nbytes + self.u.nbytes
+
+
+def make_chain(B: int, gamma: int, V: int, *, seed: int, logit_dtype: str = "bf16",
+               sigma: float = 3.0, boost_frac: float = 0.0, boost: float = 8.0,
+               noise: float = 1.0, temperature: float = 0.8) -> ChainInputs:
+    ss = np.random.SeedSequence(seed)
+    s_logit, s_boost, s_noise, s_draft, s_u = (np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(5))
+    R = gamma + 1
+    lg = _normal_f32(s_logit, (B, R, V), sigma)
+    if boost_frac > 0:
+        mask = s_boost.random(size=(B, R, V), dtype=np.float32) < np.float32(boost_frac)
+        lg[mask] += np.float32(boost)
+        del mask
+    if logit_dtype == "bf16":
+        stored = f32_to_bf16_bits(lg)
+        seen = bf16_bits_to_f32(stored)
+    elif logit_dtype == "f32":
+        stored = lg
+        seen = lg
+    else:
+        raise ValueError(logit_dtype)
+    q = np.empty((B, gamma, V), dtype=np.float32)
+    for b in range(B):  # per request to bound float64 temporaries
+        z = seen[b, :gamma].astype(np.float64) + s_noise.standard_normal(size=(gamma, V)) * noise
+        q[b] = _drafter_softmax(z).astype(np.float32)
+    tokens = _draw_from_rows(s_draft, q) if gamma > 0 else np.zeros((B, 0), np.int32)
+    u = uniforms(s_u, (B, R))
+    return ChainInputs(B, gamma, V, np.float32(temperature), logit_dtype, stored, q,
+                       tokens.astype(np.int32), u,
+                       meta=dict(seed=seed, sigma=sigma, boost_frac=boost_frac, boost=boost,
+                                 noise=noise))
+
+
+# --------------------------------------------------------------------------- greedy
+@dataclass
+class GreedyInputs:
+    B: int
+    gamma: int
+    V: int
+    logit_dtype: str
+    logits: np.ndarray            # [B, gamma+1, V]
+    tokens: np.ndarray            # [B, gamma] int32
+    meta: dict = field(default_factory=dict)
+
+    def logits_f32(self) -> np.ndarray:
+        return bf16_bits_to_f32(self.logits) if self.logit_dtype == "bf16" else self.logits
+
+
+def make_greedy(B: int, gamma: int, V: int, *, seed: int, logit_dtype: str = "bf16",
+                sigma: float = 3.0, match_prob: float = 0.7) -> GreedyInputs:
+    ss = np.random.SeedSequence(seed)
+    s_logit, s_match, s_other = (np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(3))
+    R = gamma + 1
+    lg = _normal_f32(s_logit, (B, R, V), sigma)
+    if logit_dtype == "bf16":
+        stored = f32_to_bf16_bits(lg)
+        del lg
+        seen = bf16_bits_to_f32(stored[:, :gamma])
+    else:
+        stored = lg
+        seen = lg[:, :gamma]
+    best = np.argmax(seen, axis=-1) if gamma > 0 else np.zeros((B, 0), np.int64)
+    del seen
+    match = s_match.random(size=(B, gamma)) < match_prob
+    other = s_other.integers(0, max(V - 1, 1), size=(B, gamma))
+    other = other + (other >= best)          # uniform over the V-1 ids != best
+    if V == 1:
+        other = np.zeros_like(best)
+    tokens = np.where(match, best, other).astype(np.int32)
+    return GreedyInputs(B, gamma, V, logit_dtype, stored, tokens,
+                        meta=dict(seed=seed, sigma=sigma, match_prob=match_prob))
+
+
+# --------------------------------------------------------------------------- tree
+@dataclass
+class TreeInputs:
+    B: int
+    N: int
+    V: int
+    temperature: np.float32
+    logit_dtype: str
+    logits: np.ndarray            # [B, N, V]
+    node_tokens: np.ndarray       # [B, N] int32 (node 0's entry is ignored by the verifier)
+    parents: np.ndarray           # [B, N] int32, parents[:, 0] == -1
+    u: np.ndarray                 # [B, N] float32
+    meta: dict = field(default_factory=dict)
+
+    def logits_f32(self) -> np.ndarray:
+        return bf16_bits_to_f32(self.logits) if self.logit_dtype == "bf16" else self.logits
+
+
+def random_tree(rng: np.random.Generator, N: int, max_depth: int, max_children: int) -> np.ndarray:
+    """Parent array of a random ancestor-closed tree with N nodes (node 0 = root)."""
+    parents = np.full(N, -1, dtype=np.int32)
+    depth = np.zeros(N, dtype=np.int32)
+    nchild = np.zeros(N, dtype=np.int32)
+    for i in range(1, N):
+        ok = np.nonzero((depth[:i] < max_depth) & (nchild[:i] < max_children))[0]
+        if ok.size == 0:
+            raise ValueError("tree capacity exhausted: raise max_depth or max_children")
+        p = int(ok[rng.integers(0, ok.size)])
+        parents[i] = p
+        depth[i] = depth[p] + 1
+        nchild[p] += 1
+    return parents
+
+
+def make_tree(B: int, N: int, V: int, *, seed: int, logit_dtype: str = "bf16", sigma: float = 3.0,
+              noise: float = 1.0, temperature: float = 1.0, max_depth: int = 6,
+              max_children: int = 4, boost: float = 0.0) -> TreeInputs:
+    ss = np.random.SeedSequence(seed)
+    s_logit, s_tree, s_noise, s_pick, s_u = (np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(5))
+    lg = _normal_f32(s_logit, (B, N, V), sigma)
+    parents = np.stack([random_tree(s_tree, N, max_depth, max_children) for _ in range(B)])
+    node_tokens = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        for v in range(N):
+            kids = np.nonzero(parents[b] == v)[0]
+            if kids.size == 0:
+                continue
+            z = lg[b, v].astype(np.float64) + s_noise.standard_normal(V) * noise
+            w = _drafter_softmax(z)
+            n = min(kids.size, V)
+            picked = s_pick.choice(V, size=n, replace=False, p=w)
+            node_tokens[b, kids[:n]] = picked
+            if kids.size > V:     # more children than vocabulary: repeat ids (invalid trie, tests only)
+                node_tokens[b, kids[n:]] = picked[0]
+            if boost:
+                lg[b, v, picked] += np.float32(boost)
+    stored = f32_to_bf16_bits(lg) if logit_dtype == "bf16" else lg
+    u = uniforms(s_u, (B, N))
+    return TreeInputs(B, N, V, np.float32(temperature), logit_dtype, stored, node_tokens,
+                      parents.astype(np.int32), u,
+                      meta=dict(seed=seed, sigma=sigma, noise=noise, max_depth=max_depth,
+                                max_children=max_children, boost=boost))
+
+
+# --------------------------------------------------------------------------- configs
+CONFIGS = {
+    # chain, correctness scale: fp32 logits ~ N(0, 2^2), drafter noise 0.5, T = 1
+    1: dict(kind="chain", B=4, gamma=4, V=32, logit_dtype="f32", sigma=2.0, boost_frac=0.0,
+            noise=0.5, temperature=1.0),
+    # chain, bf16, 1% of entries boosted by +8, drafter noise 1, T = 0.8
+    2: dict(kind="chain", B=64, gamma=5, V=32000, logit_dtype="bf16", sigma=3.0, boost_frac=0.01,
+            boost=8.0, noise=1.0, temperature=0.8),
+    # chain headline shape
+    3: dict(kind="chain", B=64, gamma=5, V=128256, logit_dtype="bf16", sigma=3.0, boost_frac=0.01,
+            boost=8.0, noise=1.0, temperature=0.8),
+    # greedy argmax-match
+    4: dict(kind="greedy", B=256, gamma=8, V=128256, logit_dtype="bf16", sigma=3.0, match_prob=0.7),
+    # tree, membership by target sample
+    5: dict(kind="tree", B=32, N=63, V=152064, logit_dtype="bf16", sigma=3.0, noise=1.0,
+            temperature=1.0, max_depth=6, max_children=4),
+}
+
+
+def make_config(k: int, run: int = 0, **override):
+    """Inputs for workload k (1..5) with seed 1000*k + run; keyword overrides change the recipe."""
+    spec = dict(CONFIGS[k])
+    spec.update(override)
+    kind = spec.pop("kind")
+    seed = spec.pop("seed", 1000 * k + run)
+    if kind == "chain":
+        return make_chain(seed=seed, **spec)
+    if kind == "greedy":
+        return make_greedy(seed=seed, **spec)
+    if kind == "tree":
+        return make_tree(seed=seed, **spec)
+    raise ValueError(kind)
