@@ -1,0 +1,228 @@
+"""Benchmark of the verification hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu]
+
+A step is one spec_verify_chain call over one batch of the headline workload:
+chain verification, B=64 requests, gamma=5 drafts, V=128256, bf16 target logits
+(N(0, 3^2), 1% of entries +8), fp32 draft distributions, T=0.8 -- 384 verified
+positions per step.  Inputs are synthetic (synth.make_config(3)), resident in HBM
+before timing starts, and rotated over several device copies whose total exceeds
+twice the 256 MB Infinity Cache, so every step streams from HBM.
+
+Prints ONE JSON line: throughput (verified positions/s) over K timed steps, the
+roofline of the verification call measured with HIP events on the stream it runs on,
+the oracle's CPU throughput on a bounded sample, and secondary measurements of the
+greedy (B=256, gamma=8, V=128256) and tree (B=32, N=63, V=152064) workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def device_copies(make, per_copy_bytes, min_copies=3):
+    n = max(min_copies, int(np.ceil(2 * MALL_BYTES / max(per_copy_bytes, 1))) + 1)
+    return [make() for _ in range(n)]
+
+
+def time_calls(fn, sets, steps, warmup, stream):
+    """Runs fn(set) over rotating sets: warmup untimed, then `steps` timed calls.
+
+    Returns (total seconds between the first and last event, per-call durations in ms,
+    last outputs per set)."""
+    import torch
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn(sets[i % len(sets)])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    span_ms = starts[0].elapsed_time(ends[-1])
+    return span_ms / 1e3, per, wall
+
+
+def bench_chain(args, torch, sv, synth):
+    x = synth.make_config(3, 0)
+    B, G, V = x.B, x.gamma, x.V
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    qt = torch.from_numpy(x.q).to(dev)
+    tt = torch.from_numpy(x.tokens).to(dev)
+    ut = torch.from_numpy(x.u).to(dev)
+    per_copy = lt.numel() * 2 + qt.numel() * 4
+    sets = device_copies(lambda: (lt.clone(), qt.clone(), tt.clone(), ut.clone()), per_copy)
+    del lt, qt
+    stream = torch.cuda.current_stream()
+    ws = torch.zeros(sv.chain_workspace_bytes(B, G, V) + 512, dtype=torch.uint8, device=dev)
+    outs = [dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                 out_tokens=torch.empty(B, G + 1, dtype=torch.int32, device=dev),
+                 req_status=torch.empty(B, dtype=torch.int32, device=dev)) for _ in sets]
+    idx = {id(s): k for k, s in enumerate(sets)}
+
+    def call(s):
+        sv.spec_verify_chain(s[0], s[1], s[2], s[3], float(x.temperature), workspace_tensor=ws,
+                             out=outs[idx[id(s)]])
+
+    span, per, wall = time_calls(call, sets, args.steps, args.warmup, stream)
+    acc = outs[0]["accepted_len"].cpu().numpy()
+    st = outs[0]["req_status"].cpu().numpy()
+    assert (st == 0).all(), "unexpected request errors in the benchmark workload"
+    n_rej = int((acc < G).sum())
+    logit_bytes = B * (G + 1) * V * 2
+    q_bytes = n_rej * V * 4
+    small = B * G * (4 + 4 + 2) + B * (G + 1) * 4 + B * (G + 2) * 4 * 2   # gathers, u, outputs
+    alg_bytes = logit_bytes + q_bytes + small
+    med_ms = float(np.median(per))
+    return dict(x=x, span=span, per=per, wall=wall, n_rej=n_rej, alg_bytes=alg_bytes,
+                logit_bytes=logit_bytes, q_bytes=q_bytes, med_ms=med_ms,
+                positions=B * (G + 1), mean_acc=float(acc.mean()), copies=len(sets))
+
+
+def bench_greedy(args, torch, sv, synth):
+    x = synth.make_config(4, 0)
+    B, G, V = x.B, x.gamma, x.V
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    tt = torch.from_numpy(x.tokens).to(dev)
+    sets = device_copies(lambda: (lt.clone(), tt.clone()), lt.numel() * 2)
+    del lt
+    stream = torch.cuda.current_stream()
+    ws = torch.zeros(sv.greedy_workspace_bytes(B, G, V) + 512, dtype=torch.uint8, device=dev)
+    out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+               out_tokens=torch.empty(B, G + 1, dtype=torch.int32, device=dev),
+               req_status=torch.empty(B, dtype=torch.int32, device=dev))
+    span, per, wall = time_calls(lambda s: sv.spec_verify_greedy(s[0], s[1], workspace_tensor=ws, out=out),
+                                 sets, max(20, args.steps // 4), args.warmup, stream)
+    alg = B * (G + 1) * V * 2 + B * G * 4 + B * (G + 2) * 8
+    med = float(np.median(per))
+    del sets
+    return dict(workload="greedy B=256 gamma=8 V=128256 bf16", positions_per_s=B * (G + 1) * len(per) / span,
+                median_us=med * 1e3, achieved_gbs=alg / (med * 1e-3) / 1e9,
+                frac=alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, alg_bytes=alg)
+
+
+def bench_tree(args, torch, sv, synth):
+    x = synth.make_config(5, 0)
+    B, N, V = x.B, x.N, x.V
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    nt = torch.from_numpy(x.node_tokens).to(dev)
+    pt = torch.from_numpy(x.parents).to(dev)
+    ut = torch.from_numpy(x.u).to(dev)
+    sets = device_copies(lambda: (lt.clone(), nt.clone(), pt.clone(), ut.clone()), lt.numel() * 2)
+    del lt
+    stream = torch.cuda.current_stream()
+    ws = torch.zeros(sv.tree_workspace_bytes(B, N, V) + 512, dtype=torch.uint8, device=dev)
+    out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+               out_tokens=torch.empty(B, N, dtype=torch.int32, device=dev),
+               out_nodes=torch.empty(B, N, dtype=torch.int32, device=dev),
+               req_status=torch.empty(B, dtype=torch.int32, device=dev))
+    span, per, wall = time_calls(
+        lambda s: sv.spec_verify_tree(s[0], s[1], s[2], s[3], float(x.temperature), workspace_tensor=ws, out=out),
+        sets, max(20, args.steps // 4), args.warmup, stream)
+    acc = out["accepted_len"].cpu().numpy()
+    visited = int((acc + 1).sum())
+    alg = visited * V * 2 + B * N * 12
+    med = float(np.median(per))
+    del sets
+    return dict(workload="tree B=32 N=63 V=152064 bf16 T=1", nodes_per_s=B * N * len(per) / span,
+                median_us=med * 1e3, visited_rows=visited,
+                achieved_gbs_visited=alg / (med * 1e-3) / 1e9,
+                dense_equivalent_gbs=B * N * V * 2 / (med * 1e-3) / 1e9)
+
+
+def cpu_baseline(x, budget_s):
+    """The float64 oracle on requests of the same workload until `budget_s` elapses."""
+    import oracle
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        b = n % x.B
+        oracle.verify_chain(x.logits, x.q, x.tokens, x.u, x.temperature, x.logit_dtype, requests=[b])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 4 * x.B:
+            break
+    return dict(value=n * (x.gamma + 1) / el, unit="verified positions/s", cores=1, kind="oracle",
+                sample=f"{n} requests of the B=64 gamma=5 V=128256 bf16 workload, float64 NumPy oracle, "
+                       f"{el:.1f} s on one host core")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps(dict(error="this build measures one GPU only; run with --gpus 1")))
+        sys.exit(2)
+
+    import torch
+    import exact_rejection_sampling_amd as sv
+    import synth
+    if not torch.cuda.is_available():
+        print(json.dumps(dict(error="no GPU visible")))
+        sys.exit(1)
+    sv.load_library()
+
+    log("[bench] chain headline workload")
+    c = bench_chain(args, torch, sv, synth)
+    value = c["positions"] * args.steps / c["span"]
+    achieved = c["alg_bytes"] / (c["med_ms"] * 1e-3) / 1e9
+    line = dict(
+        metric="verified positions/s + achieved HBM GB/s (% peak), B=64 gamma=5 V=128256 bf16",
+        value=value, unit="verified positions/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=c["span"] * 1e3 / args.steps, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload="chain verify B=64 gamma=5 V=128256 bf16 logits, fp32 q, T=0.8",
+                    B=64, gamma=5, V=128256, logits="bf16", q="fp32", temperature=0.8,
+                    input_copies=c["copies"]),
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=None,
+                      kernel="spec_verify_chain call (chain_stats_kernel + chain_terminal_kernel)",
+                      median_call_us=c["med_ms"] * 1e3,
+                      p10_us=float(np.percentile(c["per"], 10)) * 1e3,
+                      p90_us=float(np.percentile(c["per"], 90)) * 1e3,
+                      alg_bytes_per_call=c["alg_bytes"], rejecting_requests=c["n_rej"],
+                      mean_accepted=c["mean_acc"]),
+    )
+    if not args.no_secondary:
+        log("[bench] greedy workload")
+        line["secondary"] = dict(greedy=bench_greedy(args, torch, sv, synth))
+        torch.cuda.empty_cache()
+        log("[bench] tree workload")
+        line["secondary"]["tree"] = bench_tree(args, torch, sv, synth)
+    if not args.no_cpu:
+        log("[bench] oracle CPU baseline")
+        line["cpu_baseline"] = cpu_baseline(c["x"], args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,17 @@
+"""MI355X-native batched target-side verification for exact speculative decoding.
+
+The work runs in hand-written HIP kernels for gfx950 inside libspec_verify.so (C ABI
+declared in include/spec_verify.h).  This package is the thin Python binding: torch
+tensors in, torch tensors out, on the current CUDA (HIP) stream.
+
+    spec_verify_chain   rejection-sampling verification of draft chains
+    spec_verify_greedy  argmax-match verification
+    spec_verify_tree    tree verification by target-sample membership
+"""
+from ._binding import (REQ_STATUS, SpecError, chain_workspace_bytes, greedy_workspace_bytes,
+                       load_library, spec_verify_chain, spec_verify_greedy, spec_verify_tree,
+                       tree_workspace_bytes, LIB_PATH)
+
+__all__ = ["spec_verify_chain", "spec_verify_greedy", "spec_verify_tree", "load_library",
+           "chain_workspace_bytes", "greedy_workspace_bytes", "tree_workspace_bytes",
+           "SpecError", "REQ_STATUS", "LIB_PATH"]

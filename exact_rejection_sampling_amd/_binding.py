@@ -1,0 +1,255 @@
+"""ctypes binding of libspec_verify.so.
+
+Argument marshalling only: torch supplies device memory and the current stream; every
+step of verification runs in the library's HIP kernels.  There is no fallback path:
+if the library is missing or the tensors are not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+LIB_NAME = "libspec_verify.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+SPEC_F32, SPEC_BF16 = 0, 1
+REQ_STATUS = {0: "OK", 1: "NONFINITE", 2: "BADTOKEN", 3: "BADUNIFORM", 4: "QZERO",
+              5: "RESIDUAL_EMPTY", 6: "BADTREE"}
+
+_lib = None
+_lock = threading.Lock()
+
+_c_void_p, _c_int, _c_float, _c_size_t = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+_SIGNATURES = {
+    "spec_abi_version": (_c_int, []),
+    "spec_status_string": (ctypes.c_char_p, [_c_int]),
+    "spec_req_status_string": (ctypes.c_char_p, [_c_int]),
+    "spec_chain_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
+    "spec_greedy_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
+    "spec_tree_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
+    "spec_verify_chain": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                   _c_int, _c_int, _c_int, _c_float,
+                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_void_p, _c_size_t, _c_void_p]),
+    "spec_verify_greedy": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int,
+                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
+                                    _c_void_p]),
+    "spec_verify_tree": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_int, _c_int, _c_int, _c_float,
+                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_void_p, _c_size_t, _c_void_p]),
+}
+
+
+class SpecError(RuntimeError):
+    """A host-side error status returned by the library."""
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load (once) and return the shared library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                f"{LIB_NAME} not found at {p}: build it with "
+                "`python -m exact_rejection_sampling_amd.build` (there is no CPU fallback)")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        msg = load_library().spec_status_string(code).decode()
+        raise SpecError(f"libspec_verify status {code}: {msg}")
+
+
+def _dtype_code(t: torch.Tensor, what: str) -> int:
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError(f"{what} must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t: torch.Tensor, what: str, dtype=None, shape=None, device=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a GPU tensor (got {t.device}); there is no CPU path")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+_WS_CACHE = {}
+
+
+def workspace(kind: str, size: int, device: torch.device, stream: torch.cuda.Stream) -> torch.Tensor:
+    """A zero-initialised workspace of at least `size` bytes, kept per (kind, device, stream).
+
+    Calls on one stream run in order and leave the workspace zeroed, so it is reused;
+    calls on different streams get different workspaces.
+    """
+    key = (kind, device.index, stream.cuda_stream)
+    ws = _WS_CACHE.get(key)
+    if ws is None or ws.numel() < size:
+        with torch.cuda.stream(stream):
+            ws = torch.zeros(max(size, 256) + 256, dtype=torch.uint8, device=device)
+        _WS_CACHE[key] = ws
+    return ws
+
+
+def _aligned_ws(ws: torch.Tensor) -> tuple:
+    base = ws.data_ptr()
+    off = (-base) % 256
+    return ctypes.c_void_p(base + off), ws.numel() - off
+
+
+def spec_verify_chain(target_logits: torch.Tensor, draft_probs: torch.Tensor,
+                      draft_tokens: torch.Tensor, uniforms: torch.Tensor, temperature: float,
+                      *, with_stats: bool = False, workspace_tensor: Optional[torch.Tensor] = None,
+                      out: Optional[dict] = None) -> dict:
+    """Chain verification by rejection sampling (C entry point spec_verify_chain).
+
+    target_logits [B, gamma+1, V] bf16/fp32; draft_probs [B, gamma, V] fp32/bf16;
+    draft_tokens [B, gamma] int32; uniforms [B, gamma+1] fp32; temperature > 0.
+    Returns {accepted_len [B], out_tokens [B, gamma+1], req_status [B], stats?} (int32 /
+    fp32 GPU tensors, valid once the current stream reaches the call).
+    """
+    lib = load_library()
+    _need(target_logits, "target_logits")
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, gamma+1, V]")
+    B, R, V = target_logits.shape
+    G = R - 1
+    dev = target_logits.device
+    _need(draft_probs, "draft_probs", shape=(B, G, V), device=dev)
+    _need(draft_tokens, "draft_tokens", dtype=torch.int32, shape=(B, G), device=dev)
+    _need(uniforms, "uniforms", dtype=torch.float32, shape=(B, R), device=dev)
+    lt, qt = _dtype_code(target_logits, "target_logits"), _dtype_code(draft_probs, "draft_probs")
+    if out is None:
+        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty(B, R, dtype=torch.int32, device=dev),
+                   req_status=torch.empty(B, dtype=torch.int32, device=dev))
+        if with_stats:
+            out["stats"] = torch.empty(B, R, 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    need = lib.spec_chain_workspace_bytes(B, G, V)
+    if need == 0 and B > 0:
+        raise SpecError(f"unsupported sizes B={B} gamma={G} V={V}")
+    ws = workspace_tensor if workspace_tensor is not None else workspace("chain", need, dev, stream)
+    wp, wn = _aligned_ws(ws)
+    _check(lib.spec_verify_chain(
+        _ptr(target_logits), lt, _ptr(draft_probs), qt, _ptr(draft_tokens), _ptr(uniforms),
+        B, G, V, ctypes.c_float(float(temperature)),
+        _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
+        _ptr(out.get("stats")), wp, wn, ctypes.c_void_p(stream.cuda_stream)))
+    return out
+
+
+def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor, *,
+                       workspace_tensor: Optional[torch.Tensor] = None,
+                       out: Optional[dict] = None) -> dict:
+    """Greedy argmax-match verification (C entry point spec_verify_greedy).
+
+    target_logits [B, gamma+1, V] bf16/fp32; draft_tokens [B, gamma] int32.
+    """
+    lib = load_library()
+    _need(target_logits, "target_logits")
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, gamma+1, V]")
+    B, R, V = target_logits.shape
+    G = R - 1
+    dev = target_logits.device
+    _need(draft_tokens, "draft_tokens", dtype=torch.int32, shape=(B, G), device=dev)
+    lt = _dtype_code(target_logits, "target_logits")
+    if out is None:
+        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty(B, R, dtype=torch.int32, device=dev),
+                   req_status=torch.empty(B, dtype=torch.int32, device=dev))
+    stream = torch.cuda.current_stream(dev)
+    need = lib.spec_greedy_workspace_bytes(B, G, V)
+    if need == 0 and B > 0:
+        raise SpecError(f"unsupported sizes B={B} gamma={G} V={V}")
+    ws = workspace_tensor if workspace_tensor is not None else workspace("greedy", need, dev, stream)
+    wp, wn = _aligned_ws(ws)
+    _check(lib.spec_verify_greedy(
+        _ptr(target_logits), lt, _ptr(draft_tokens), B, G, V,
+        _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
+        wp, wn, ctypes.c_void_p(stream.cuda_stream)))
+    return out
+
+
+def spec_verify_tree(node_logits: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor,
+                     uniforms: torch.Tensor, temperature: float, *,
+                     workspace_tensor: Optional[torch.Tensor] = None,
+                     out: Optional[dict] = None) -> dict:
+    """Tree verification by target-sample membership (C entry point spec_verify_tree).
+
+    node_logits [B, N, V] bf16/fp32 (row v scores the children of node v); node_tokens,
+    parents [B, N] int32 (parents[:, 0] = -1, 0 <= parents[v] < v); uniforms [B, N] fp32.
+    Returns {accepted_len [B], out_tokens [B, N], out_nodes [B, N], req_status [B]}.
+    """
+    lib = load_library()
+    _need(node_logits, "node_logits")
+    if node_logits.dim() != 3:
+        raise ValueError("node_logits must be [B, N, V]")
+    B, N, V = node_logits.shape
+    dev = node_logits.device
+    _need(node_tokens, "node_tokens", dtype=torch.int32, shape=(B, N), device=dev)
+    _need(parents, "parents", dtype=torch.int32, shape=(B, N), device=dev)
+    _need(uniforms, "uniforms", dtype=torch.float32, shape=(B, N), device=dev)
+    lt = _dtype_code(node_logits, "node_logits")
+    if out is None:
+        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty(B, N, dtype=torch.int32, device=dev),
+                   out_nodes=torch.empty(B, N, dtype=torch.int32, device=dev),
+                   req_status=torch.empty(B, dtype=torch.int32, device=dev))
+    stream = torch.cuda.current_stream(dev)
+    need = lib.spec_tree_workspace_bytes(B, N, V)
+    if need == 0 and B > 0:
+        raise SpecError(f"unsupported sizes B={B} N={N} V={V}")
+    ws = workspace_tensor if workspace_tensor is not None else workspace("tree", need, dev, stream)
+    wp, wn = _aligned_ws(ws)
+    _check(lib.spec_verify_tree(
+        _ptr(node_logits), lt, _ptr(node_tokens), _ptr(parents), _ptr(uniforms),
+        B, N, V, ctypes.c_float(float(temperature)),
+        _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["out_nodes"]),
+        _ptr(out["req_status"]), wp, wn, ctypes.c_void_p(stream.cuda_stream)))
+    return out
+
+
+def chain_workspace_bytes(B: int, gamma: int, V: int) -> int:
+    return load_library().spec_chain_workspace_bytes(B, gamma, V)
+
+
+def greedy_workspace_bytes(B: int, gamma: int, V: int) -> int:
+    return load_library().spec_greedy_workspace_bytes(B, gamma, V)
+
+
+def tree_workspace_bytes(B: int, N: int, V: int) -> int:
+    return load_library().spec_tree_workspace_bytes(B, N, V)

@@ -1,0 +1,190 @@
+// C ABI of libspec_verify.so: host-side argument checks, workspace carving and launches.
+// The entry points and their contracts are declared in include/spec_verify.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "internal.h"
+#include "spec_verify.h"
+
+namespace {
+
+constexpr double kLog2e = 1.44269504088896340736;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+bool dtype_ok(int d) { return d == SPEC_F32 || d == SPEC_BF16; }
+bool temperature_ok(float t) {
+  return t >= SPEC_MIN_TEMPERATURE && t <= SPEC_MAX_TEMPERATURE;   // false for NaN
+}
+bool sizes_ok(int B, int gamma, int V) {
+  return B >= 0 && B <= SPEC_MAX_BATCH && gamma >= 0 && gamma <= SPEC_MAX_GAMMA && V >= 1 &&
+         V <= SPEC_MAX_VOCAB;
+}
+int chunks(long V, long per) { return static_cast<int>((V + per - 1) / per); }
+// one block per (row, 8192-element slice) must fit the 1-D grid
+bool grid_ok(long rows, long V) {
+  const long slices = (V + 4 * 2048 - 1) / (4 * 2048);
+  return rows * slices <= 0x7fffffffL && rows * ((V + sv::kTermChunk - 1) / sv::kTermChunk) <= 0x7fffffffL;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_abi_version(void) { return SPEC_ABI_VERSION; }
+
+const char* spec_status_string(int code) {
+  switch (code) {
+    case SPEC_OK: return "ok";
+    case SPEC_EINVAL: return "invalid argument (null pointer, size out of range or bad temperature)";
+    case SPEC_EDTYPE: return "unknown dtype";
+    case SPEC_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case SPEC_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* spec_req_status_string(int code) {
+  switch (code) {
+    case SPEC_REQ_OK: return "ok";
+    case SPEC_REQ_NONFINITE: return "reached logits row has NaN or +inf, or is entirely -inf";
+    case SPEC_REQ_BADTOKEN: return "draft token outside [0, V)";
+    case SPEC_REQ_BADUNIFORM: return "uniform outside [0, 1)";
+    case SPEC_REQ_QZERO: return "draft probability of a proposed token is not positive";
+    case SPEC_REQ_RESIDUAL_EMPTY: return "terminal mass not positive or q row invalid";
+    case SPEC_REQ_BADTREE: return "invalid parent array or node token";
+    default: return "unknown request status";
+  }
+}
+
+size_t spec_chain_workspace_bytes(int B, int gamma, int V) {
+  if (!sizes_ok(B, gamma, V)) return 0;
+  return sv::chain_layout(B, gamma, V).total;
+}
+
+size_t spec_greedy_workspace_bytes(int B, int gamma, int V) {
+  if (!sizes_ok(B, gamma, V)) return 0;
+  return sv::greedy_layout(B, gamma, V).total;
+}
+
+size_t spec_tree_workspace_bytes(int B, int N, int V) {
+  if (!(B >= 0 && B <= SPEC_MAX_BATCH && N >= 1 && N <= SPEC_MAX_NODES && V >= 1 && V <= SPEC_MAX_VOCAB))
+    return 0;
+  return sv::tree_layout(B, N, V).total;
+}
+
+spec_status spec_verify_chain(const void* target_logits, int logit_dtype, const void* draft_probs,
+                              int q_dtype, const int32_t* draft_tokens, const float* uniforms, int B,
+                              int gamma, int V, float temperature, int32_t* accepted_len,
+                              int32_t* out_tokens, int32_t* req_status, float* stats,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!sizes_ok(B, gamma, V) || !temperature_ok(temperature)) return SPEC_EINVAL;
+  if (!dtype_ok(logit_dtype) || !dtype_ok(q_dtype)) return SPEC_EDTYPE;
+  if (!grid_ok((long)B * (gamma + 1), V)) return SPEC_EINVAL;
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !uniforms || !accepted_len || !out_tokens || !req_status) return SPEC_EINVAL;
+  if (gamma > 0 && (!draft_probs || !draft_tokens)) return SPEC_EINVAL;
+  const sv::ChainLayout L = sv::chain_layout(B, gamma, V);
+  if (!workspace || workspace_bytes < L.total || !aligned256(workspace)) return SPEC_EWORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  sv::ChainParams p;
+  p.logits = target_logits;
+  p.q = draft_probs;
+  p.tokens = draft_tokens;
+  p.u = uniforms;
+  p.accepted_len = accepted_len;
+  p.out_tokens = out_tokens;
+  p.req_status = req_status;
+  p.stats = stats;
+  p.part = reinterpret_cast<float2*>(ws + L.part);
+  p.count1 = reinterpret_cast<unsigned*>(ws + L.count1);
+  p.dec = reinterpret_cast<sv::ChainDecision*>(ws + L.dec);
+  p.tmass = reinterpret_cast<double*>(ws + L.tmass);
+  p.count2 = reinterpret_cast<unsigned*>(ws + L.count2);
+  p.B = B;
+  p.G = gamma;
+  p.R = gamma + 1;
+  p.V = V;
+  p.P = chunks(V, sv::kWaveChunk);
+  p.WG1 = chunks(p.P, sv::kWavesPerBlock);
+  p.S2 = chunks(V, sv::kTermChunk);
+  p.q_dtype = q_dtype;
+  const double c2 = kLog2e / static_cast<double>(temperature);
+  p.c2 = static_cast<float>(c2);
+  p.inv_t = 1.0 / static_cast<double>(temperature);
+  const bool vec = (V % 8 == 0) && aligned16(target_logits) && (gamma == 0 || aligned16(draft_probs));
+  return sv::launch_chain(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+spec_status spec_verify_greedy(const void* target_logits, int logit_dtype, const int32_t* draft_tokens,
+                               int B, int gamma, int V, int32_t* accepted_len, int32_t* out_tokens,
+                               int32_t* req_status, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (!sizes_ok(B, gamma, V)) return SPEC_EINVAL;
+  if (!dtype_ok(logit_dtype)) return SPEC_EDTYPE;
+  if (!grid_ok((long)B * (gamma + 1), V)) return SPEC_EINVAL;
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !accepted_len || !out_tokens || !req_status) return SPEC_EINVAL;
+  if (gamma > 0 && !draft_tokens) return SPEC_EINVAL;
+  const sv::GreedyLayout L = sv::greedy_layout(B, gamma, V);
+  if (!workspace || workspace_bytes < L.total || !aligned256(workspace)) return SPEC_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  sv::GreedyParams p;
+  p.logits = target_logits;
+  p.tokens = draft_tokens;
+  p.accepted_len = accepted_len;
+  p.out_tokens = out_tokens;
+  p.req_status = req_status;
+  p.part = reinterpret_cast<sv::GreedyPart*>(ws + L.part);
+  p.count = reinterpret_cast<unsigned*>(ws + L.count);
+  p.B = B;
+  p.G = gamma;
+  p.R = gamma + 1;
+  p.V = V;
+  p.P = chunks(V, sv::kWaveChunk);
+  p.WG1 = chunks(p.P, sv::kWavesPerBlock);
+  const bool vec = (V % 8 == 0) && aligned16(target_logits);
+  return sv::launch_greedy(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+spec_status spec_verify_tree(const void* node_logits, int logit_dtype, const int32_t* node_tokens,
+                             const int32_t* parents, const float* uniforms, int B, int N, int V,
+                             float temperature, int32_t* accepted_len, int32_t* out_tokens,
+                             int32_t* out_nodes, int32_t* req_status, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (!(B >= 0 && B <= SPEC_MAX_BATCH && N >= 1 && N <= SPEC_MAX_NODES && V >= 1 && V <= SPEC_MAX_VOCAB))
+    return SPEC_EINVAL;
+  if (!temperature_ok(temperature)) return SPEC_EINVAL;
+  if (!dtype_ok(logit_dtype)) return SPEC_EDTYPE;
+  if (!grid_ok(B, V)) return SPEC_EINVAL;
+  if (B == 0) return SPEC_OK;
+  if (!node_logits || !node_tokens || !parents || !uniforms || !accepted_len || !out_tokens ||
+      !out_nodes || !req_status)
+    return SPEC_EINVAL;
+  const sv::TreeLayout L = sv::tree_layout(B, N, V);
+  if (!workspace || workspace_bytes < L.total || !aligned256(workspace)) return SPEC_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  sv::TreeParams p;
+  p.logits = node_logits;
+  p.node_tokens = node_tokens;
+  p.parents = parents;
+  p.u = uniforms;
+  p.accepted_len = accepted_len;
+  p.out_tokens = out_tokens;
+  p.out_nodes = out_nodes;
+  p.req_status = req_status;
+  p.part = reinterpret_cast<float2*>(ws + L.part);
+  p.count = reinterpret_cast<unsigned*>(ws + L.count);
+  p.B = B;
+  p.N = N;
+  p.V = V;
+  p.P = chunks(V, sv::kWaveChunk);
+  p.WG1 = chunks(p.P, sv::kWavesPerBlock);
+  p.c2 = static_cast<float>(kLog2e / static_cast<double>(temperature));
+  const bool vec = (V % 8 == 0) && aligned16(node_logits);
+  return sv::launch_tree(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,257 @@
+// Tree verification by target-sample membership (spec_verify_tree).
+//
+// One kernel, ceil(V / 8192) blocks per request.  All blocks of a request stream the
+// frontier row (node 0) together, one 2048-element chunk per wave, and write the chunks'
+// online-softmax summaries.  The last block to finish a request walks the tree:
+//   * combine the summaries of the current node's row into (reference, Z) and the
+//     chunk masses, pick the chunk where the running mass passes u_v * Z, rescan that
+//     chunk in vocabulary order to get the target sample y;
+//   * if a child of the node carries token y, accept it and stream the child's row
+//     with the same block; otherwise y is the terminal token.
+// Only rows on the walked path are read.
+//
+// Method: [M7.7] "M7.7 - Draft Sources, Dependent Heads, and Hardware-Aware Trees"
+// §0x02 (a node's row scores its children; parent index array), §0x04B and §0x09
+// (accept the candidate that matches the target's own sample), §0x0F (parent index
+// validity); [M16] "Module 16: Speculative Decoding", "Verify the Tree" (walk until no
+// child matches, then emit one more target token).
+#include "device_common.h"
+#include "internal.h"
+#include "spec_verify.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int kNoPick = 0x7fffffff;
+
+__device__ void tree_fail(const TreeParams& p, int b, int code) {
+  for (int i = threadIdx.x; i < p.N; i += blockDim.x) {
+    p.out_tokens[(size_t)b * p.N + i] = -1;
+    p.out_nodes[(size_t)b * p.N + i] = -1;
+  }
+  if (threadIdx.x == 0) {
+    p.accepted_len[b] = -1;
+    p.req_status[b] = code;
+  }
+}
+
+// Block-wide: sample one token from softmax(row / T) given the row's chunk summaries.
+// Returns the token, or -1 (row not finite) / -2 (bad uniform) through *status.
+template <int DT, bool VEC>
+__device__ int sample_row(const TreeParams& p, int b, const void* row, float uv, int* status) {
+  __shared__ double s_scan[kWavesPerBlock];
+  __shared__ float s_r;
+  __shared__ double s_z;
+  __shared__ int s_pick;
+  __shared__ double s_before;
+  __shared__ double s_total;
+  __shared__ int s_last_pos;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const float2* part = p.part + (size_t)b * p.P;
+  const float c2 = p.c2;
+
+  // reference exponent: fp32(max raw logit * c2), identical to the chunks' own r_j
+  if (wave == 0) {
+    float m = -INFINITY;
+    for (int j = lane; j < p.P; j += kWave) m = fmaxf(m, part[j].x);
+    m = wave_max(m);
+    if (lane == 0) s_r = m * c2;
+  }
+  __syncthreads();
+  const float R = s_r;
+
+  // chunk masses 2^(r_j - R) Z_j in vocabulary order; thread t owns a contiguous run
+  const int per = (p.P + kBlock - 1) / kBlock;
+  const int c_lo = min(tid * per, p.P), c_hi = min(c_lo + per, p.P);
+  double mine = 0.0;
+  for (int c = c_lo; c < c_hi; ++c) {
+    const float2 s = part[c];
+    mine += (double)s.y * exp2((double)(s.x * c2) - (double)R);
+  }
+  double tot;
+  const double excl = block_excl_scan_d(mine, s_scan, &tot);
+  double run_end = excl;
+  for (int c = c_lo; c < c_hi; ++c) {
+    const float2 s = part[c];
+    run_end += (double)s.y * exp2((double)(s.x * c2) - (double)R);
+  }
+  if (c_lo < c_hi && c_hi == p.P) s_total = run_end;
+  if (tid == 0) s_pick = kNoPick;
+  __syncthreads();
+  const double Z = s_total;
+  if (!(isfinite(Z) && Z > 0.0)) { *status = SPEC_REQ_NONFINITE; return -1; }
+  if (!(uv >= 0.0f && uv < 1.0f)) { *status = SPEC_REQ_BADUNIFORM; return -1; }
+  const double t = (double)uv * Z;
+  {
+    double run = excl;
+    for (int c = c_lo; c < c_hi; ++c) {
+      const float2 s = part[c];
+      const double nxt = run + (double)s.y * exp2((double)(s.x * c2) - (double)R);
+      if (nxt > t) { atomicMin(&s_pick, c); break; }
+      run = nxt;
+    }
+  }
+  __syncthreads();
+  // a chunk is always found (t < Z and the last running value is Z); clamp regardless
+  const int cstar = s_pick == kNoPick ? p.P - 1 : s_pick;
+  if (tid == 0) s_before = 0.0;
+  __syncthreads();
+  if (cstar >= c_lo && cstar < c_hi) {
+    double run = excl;
+    for (int c = c_lo; c < cstar; ++c) {
+      const float2 s = part[c];
+      run += (double)s.y * exp2((double)(s.x * c2) - (double)R);
+    }
+    s_before = run;
+  }
+  __syncthreads();
+  if (tid == 0) { s_pick = kNoPick; s_last_pos = -1; }
+  __syncthreads();
+
+  // rescan chunk cstar (one slab) in the chunk's own units 2^(l c2 - r_c)
+  const float rc = part[cstar].x * c2;
+  const double rem = (t - s_before) * exp2((double)R - (double)rc);
+  const long e0 = (long)cstar * kWaveChunk + (long)tid * kVec;
+  float v[8];
+  load8<DT, VEC, false>(row, e0, p.V, v, -INFINITY);
+  double incl[8];
+  double acc = 0.0;
+  int last_pos = -1;
+  float e[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    e[k] = scaled_exp(v[k], c2, rc);
+    acc += (double)e[k];
+    incl[k] = acc;
+    if (e[k] > 0.0f) last_pos = (int)(e0 + k);
+  }
+  double slab_total;
+  const double off = block_excl_scan_d(acc, s_scan, &slab_total);
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (off + incl[k] > rem && e[k] > 0.0f) { atomicMin(&s_pick, (int)(e0 + k)); break; }
+  __syncthreads();
+  if (s_pick == kNoPick) atomicMax(&s_last_pos, last_pos);
+  __syncthreads();
+  const int y = (s_pick != kNoPick) ? s_pick : s_last_pos;
+  __syncthreads();
+  *status = 0;
+  return y;
+}
+
+// Block-wide: summaries of one full row into p.part[b], by this block alone.
+template <int DT, bool VEC>
+__device__ void summarize_row(const TreeParams& p, int b, const void* row) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  for (int c = wave; c < p.P; c += kWavesPerBlock) {
+    float m, z;
+    chunk_summary<DT, VEC>(row, p.V, c, lane, p.c2, m, z);
+    if (lane == 0) {
+      p.part[(size_t)b * p.P + c] = make_float2(m, z);
+      release_device();
+    }
+  }
+  __syncthreads();
+  acquire_device();
+}
+
+template <int DT, bool VEC>
+__device__ void tree_walk(const TreeParams& p, int b) {
+  __shared__ int s_bad;
+  __shared__ int s_child;
+  const int tid = threadIdx.x;
+  const int N = p.N;
+  const int32_t* par = p.parents + (size_t)b * N;
+  const int32_t* tok = p.node_tokens + (size_t)b * N;
+
+  if (tid == 0) s_bad = (par[0] != -1);
+  __syncthreads();
+  for (int v = 1 + tid; v < N; v += kBlock) {
+    const int pv = par[v], tv = tok[v];
+    if (pv < 0 || pv >= v || tv < 0 || tv >= p.V) s_bad = 1;
+  }
+  __syncthreads();
+  if (s_bad) { tree_fail(p, b, SPEC_REQ_BADTREE); return; }
+
+  int v = 0, depth = 0;
+  while (true) {
+    const void* row = row_ptr<DT>(p.logits, (size_t)b * N + v, p.V);
+    int status = 0;
+    const int y = sample_row<DT, VEC>(p, b, row, p.u[(size_t)b * N + v], &status);
+    if (status != 0) { tree_fail(p, b, status); return; }
+    if (tid == 0) s_child = kNoPick;
+    __syncthreads();
+    for (int c = v + 1 + tid; c < N; c += kBlock)
+      if (par[c] == v && tok[c] == y) atomicMin(&s_child, c);
+    __syncthreads();
+    const int child = s_child;
+    __syncthreads();
+    if (child == kNoPick) {
+      for (int i = tid; i < N; i += kBlock) {
+        if (i > depth) {
+          p.out_tokens[(size_t)b * N + i] = -1;
+          p.out_nodes[(size_t)b * N + i] = -1;
+        } else if (i == depth) {
+          p.out_tokens[(size_t)b * N + i] = y;
+          p.out_nodes[(size_t)b * N + i] = -1;
+        }
+      }
+      if (tid == 0) {
+        p.accepted_len[b] = depth;
+        p.req_status[b] = 0;
+      }
+      return;
+    }
+    if (tid == 0) {
+      p.out_tokens[(size_t)b * N + depth] = tok[child];
+      p.out_nodes[(size_t)b * N + depth] = child;
+    }
+    ++depth;
+    v = child;
+    summarize_row<DT, VEC>(p, b, row_ptr<DT>(p.logits, (size_t)b * N + v, p.V));
+  }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int b = blockIdx.x / p.WG1;
+  const int slice = blockIdx.x % p.WG1;
+  const int chunk = slice * kWavesPerBlock + wave;
+  if (chunk < p.P) {
+    float m, z;
+    chunk_summary<DT, VEC>(row_ptr<DT>(p.logits, (size_t)b * p.N, p.V), p.V, chunk, lane, p.c2, m, z);
+    if (lane == 0) {
+      p.part[(size_t)b * p.P + chunk] = make_float2(m, z);
+      release_device();
+    }
+  }
+  __syncthreads();
+  __shared__ int s_last;
+  if (threadIdx.x == 0) {
+    const unsigned prev = arrive(&p.count[b]);
+    s_last = (prev == (unsigned)(p.WG1 - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  acquire_device();
+  tree_walk<DT, VEC>(p, b);
+  if (threadIdx.x == 0) reset_counter(&p.count[b]);
+}
+
+template <int DT, bool VEC>
+hipError_t launch_typed(const TreeParams& p, hipStream_t s) {
+  const unsigned g = (unsigned)((size_t)p.B * p.WG1);
+  tree_kernel<DT, VEC><<<dim3(g), dim3(kBlock), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tree(const TreeParams& p, int logit_dtype, bool vec, hipStream_t s) {
+  if (logit_dtype == kBF16) return vec ? launch_typed<kBF16, true>(p, s) : launch_typed<kBF16, false>(p, s);
+  return vec ? launch_typed<kF32, true>(p, s) : launch_typed<kF32, false>(p, s);
+}
+
+}  // namespace sv

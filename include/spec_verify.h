@@ -1,0 +1,191 @@
+/*
+ * spec_verify.h -- C ABI of libspec_verify.so: batched target-side verification for
+ * exact speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * Three entry points, one per verification rule:
+ *   spec_verify_chain   rejection-sampling verification of a draft chain
+ *   spec_verify_greedy  argmax-match verification of a draft chain
+ *   spec_verify_tree    tree verification by target-sample membership
+ *
+ * Pages that define the operations (cited by title and section):
+ *   [M7.1]  "M7.1 - Speculative Decoding: Draft, Verify, Accept, Reject"
+ *   [M7.7]  "M7.7 - Draft Sources, Dependent Heads, and Hardware-Aware Trees"
+ *   [Atlas] "Speculative decoding: proposals and verified output" (AI-atlas lesson data)
+ *   [M16]   "Module 16: Speculative Decoding"
+ *   [Tiny]  "Exact Speculative and Assisted Decoding for TinyRustLM"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every array pointer is a DEVICE pointer, owned by the caller, in dense
+ *           row-major layout with the vocabulary innermost.  The library never
+ *           allocates, never frees and never synchronizes; all work is enqueued on
+ *           `stream`, and outputs are valid once that stream reaches the call.
+ * Workspace. Each entry point takes a caller-owned device workspace of at least the
+ *           size its query function returns, aligned to 256 bytes.  It must be
+ *           zero-filled before its first use; every call leaves it zeroed again
+ *           (the counters it holds reset themselves), so one workspace serves any
+ *           number of calls issued in order on one stream.  Calls that overlap in
+ *           time must use different workspaces.
+ * Host status.  The return value reports only what the host can check before
+ *           launching: null pointers, sizes outside the documented limits, a
+ *           temperature outside its range, an unknown dtype, a workspace that is too
+ *           small or misaligned, and a HIP launch failure.  On any non-SPEC_OK
+ *           return nothing has been enqueued (except SPEC_EHIP, where a launch failed).
+ * Request status.  Data errors are reported per request in req_status[b] (SPEC_REQ_*).
+ *           A request with a non-zero status emits nothing: accepted_len[b] = -1 and
+ *           its out_tokens row is all -1 (the round is aborted without emitting, as
+ *           [Tiny] "Normative stochastic pseudocode" does on a NaN row or an empty
+ *           residual).  Checks apply to what the round actually reaches, in the
+ *           order it reaches it: row i, then draft token i, then q_i(x_i), then
+ *           uniform i, for i = 0, 1, ...
+ * Uniforms. The caller supplies every random number as fp32 in [0, 1) ([Tiny]
+ *           "Normative edge-case behavior": counter-based, per-purpose draws).  Given
+ *           the same inputs the outputs are bitwise reproducible.
+ * Exactness. Tokens are exact functions of the inputs except for uniforms that fall
+ *           within ~1e-6 of an acceptance threshold or of a CDF boundary, where fp32
+ *           rounding of the probabilities may decide either way.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+
+/* Limits checked on the host. */
+#define SPEC_MAX_BATCH  (1 << 22)   /* B */
+#define SPEC_MAX_GAMMA  63          /* gamma: draft tokens per request */
+#define SPEC_MAX_VOCAB  (1 << 28)   /* V */
+#define SPEC_MAX_NODES  4096        /* N: tree nodes per request */
+#define SPEC_MIN_TEMPERATURE 0x1p-20f
+#define SPEC_MAX_TEMPERATURE 0x1p+20f
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_EINVAL = 1,      /* null pointer, size out of range, bad temperature */
+  SPEC_EDTYPE = 2,      /* unknown spec_dtype */
+  SPEC_EWORKSPACE = 3,  /* workspace missing, too small or not 256-byte aligned */
+  SPEC_EHIP = 4         /* a kernel launch failed (hipGetLastError) */
+} spec_status;
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+/* Per-request status codes written to req_status[b]. */
+enum {
+  SPEC_REQ_OK = 0,
+  SPEC_REQ_NONFINITE = 1,       /* a reached logits row has NaN or +inf, or is all -inf */
+  SPEC_REQ_BADTOKEN = 2,        /* a reached draft token is outside [0, V) */
+  SPEC_REQ_BADUNIFORM = 3,      /* a consumed uniform is outside [0, 1) */
+  SPEC_REQ_QZERO = 4,           /* q_i(x_i) is not a positive finite number ([M7.1] §0x03D:
+                                   a token the draft gives no mass cannot be proposed) */
+  SPEC_REQ_RESIDUAL_EMPTY = 5,  /* terminal mass W is not positive and finite, or the q row
+                                   read at the rejected position has a negative or
+                                   non-finite entry ([Tiny] residual invariant) */
+  SPEC_REQ_BADTREE = 6          /* parents[0] != -1, a parents[v] outside [0, v), or a
+                                   non-root node token outside [0, V) ([M7.7] §0x0F) */
+};
+
+/* ------------------------------------------------------------------ chain ---
+ * Rejection-sampling verification of B independent draft chains.
+ *
+ * Defined by [M7.1] §0x03-§0x03H and §0x04 "Loop Pseudocode", [M16] "The Math:
+ * Speculative Sampling" and "Code: Verify a Draft", [Atlas] mechanism:
+ *   p_i = softmax(l_i / T) for rows i = 0..gamma  (temperature is applied to the
+ *         target logits only; q is used exactly as given);
+ *   for i = 0..gamma-1: accept x_i iff u_i < a_i = min(1, p_i(x_i) / q_i(x_i));
+ *         stop at the first rejection, A = its index (A = gamma if none);
+ *   terminal weights w = max(p_A - q_A, 0) if A < gamma ([M7.1] §0x03C), else
+ *         w = p_gamma (the bonus row, [M7.1] §0x03H);
+ *   terminal token k = first index (vocabulary order) whose running sum of w
+ *         exceeds u_gamma * sum(w);
+ *   emitted tokens: x_0..x_{A-1}, k  (A + 1 tokens, [M16]).
+ *
+ * target_logits  [B, gamma+1, V] in logit_dtype.  Row i < gamma scores draft token i;
+ *                row gamma is the bonus row ([M7.1] §0x04A, replayed-frontier layout).
+ * draft_probs    [B, gamma, V] in q_dtype: the distribution each draft token was drawn
+ *                from, after the drafter's processors.  Only q_i(x_i) for reached rows
+ *                and the full row q_A of a rejecting request are read.
+ * draft_tokens   [B, gamma] int32.
+ * uniforms       [B, gamma+1] fp32: u[b, i] for the accept test of draft i, u[b, gamma]
+ *                for the single terminal draw (correction or bonus).
+ * temperature    in [SPEC_MIN_TEMPERATURE, SPEC_MAX_TEMPERATURE].
+ * accepted_len   [B] int32 out: A in [0, gamma], or -1.
+ * out_tokens     [B, gamma+1] int32 out: A + 1 tokens, then -1.
+ * req_status     [B] int32 out: SPEC_REQ_*.
+ * stats          [B, gamma+1, 4] fp32 out, may be NULL.  For each reached row i < gamma:
+ *                (m_i, log Z_i, p_i(x_i), a_i), with m_i = max_x l_{i,x} / T and
+ *                Z_i = sum_x exp(l_{i,x} / T - m_i).  Row gamma: (m_gamma, log Z_gamma)
+ *                when the bonus row is reached, W = sum(w) in column 2, NaN in column 3.
+ *                Every other entry (and every entry of a failed request) is NaN.
+ * gamma may be 0 (a plain target draw from row 0); then draft_probs and draft_tokens
+ * may be NULL.  B may be 0 (nothing is enqueued).
+ */
+size_t spec_chain_workspace_bytes(int B, int gamma, int V);
+
+spec_status spec_verify_chain(const void* target_logits, int logit_dtype,
+                              const void* draft_probs, int q_dtype,
+                              const int32_t* draft_tokens, const float* uniforms,
+                              int B, int gamma, int V, float temperature,
+                              int32_t* accepted_len, int32_t* out_tokens, int32_t* req_status,
+                              float* stats, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* ----------------------------------------------------------------- greedy ---
+ * Argmax-match verification ([M7.1] §0x02D: longest-prefix validation is exact for
+ * greedy decoding; [Tiny] "Normative greedy pseudocode"):
+ *   t_i = argmax_x l_{i,x}, lowest index on ties;  A = first i < gamma with x_i != t_i,
+ *   else gamma;  emitted tokens x_0..x_{A-1}, t_A.
+ * target_logits [B, gamma+1, V]; draft_tokens [B, gamma]; outputs as for the chain.
+ * No temperature: a positive temperature does not move an argmax.
+ */
+size_t spec_greedy_workspace_bytes(int B, int gamma, int V);
+
+spec_status spec_verify_greedy(const void* target_logits, int logit_dtype,
+                               const int32_t* draft_tokens, int B, int gamma, int V,
+                               int32_t* accepted_len, int32_t* out_tokens, int32_t* req_status,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------- tree ---
+ * Tree verification by target-sample membership ([M7.7] §0x04B and §0x09: accept a
+ * candidate child when it equals the token the target samples; [M16] "Verify the
+ * Tree": walk down from the root until no child matches, then emit one target token).
+ *   v = 0 (the frontier root);
+ *   repeat: y = inverse-CDF draw of softmax(l_v / T) with u[b, v];
+ *           if a child c of v (parents[c] == v) has node_tokens[c] == y (the lowest
+ *           such c if siblings repeat a token): accept c, v = c;  else stop.
+ *   emitted tokens: tokens of the accepted nodes, then the last draw y.
+ * Row v of node_logits scores the children of node v ([M7.7] §0x02: a node's row
+ * predicts its children, never itself).  Only rows on the walked path are read.
+ *
+ * node_logits   [B, N, V]; node_tokens [B, N] int32 (node 0's entry is ignored);
+ * parents       [B, N] int32 with parents[0] = -1 and 0 <= parents[v] < v;
+ * uniforms      [B, N] fp32, u[b, v] used for the draw at node v;
+ * accepted_len  [B]: number of accepted non-root nodes (path length), or -1;
+ * out_tokens    [B, N]: accepted_len + 1 tokens, then -1;
+ * out_nodes     [B, N]: the accepted node ids in path order, then -1.
+ */
+size_t spec_tree_workspace_bytes(int B, int N, int V);
+
+spec_status spec_verify_tree(const void* node_logits, int logit_dtype,
+                             const int32_t* node_tokens, const int32_t* parents,
+                             const float* uniforms, int B, int N, int V, float temperature,
+                             int32_t* accepted_len, int32_t* out_tokens, int32_t* out_nodes,
+                             int32_t* req_status, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* ------------------------------------------------------------------ misc --- */
+const char* spec_status_string(int code);     /* static string, never NULL */
+const char* spec_req_status_string(int code); /* static string, never NULL */
+int spec_abi_version(void);                   /* SPEC_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

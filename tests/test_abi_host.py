@@ -1,0 +1,119 @@
+"""Host-side checks of libspec_verify.so that need no GPU.
+
+The library loads, exports every entry point include/spec_verify.h declares, and its
+host argument checks reject bad calls before anything is enqueued.  No call here
+reaches a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_rejection_sampling_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+OK, EINVAL, EDTYPE, EWORKSPACE = 0, 1, 2, 3
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x1000)       # never dereferenced: every call below fails on the host
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = sv.load_library()
+    names = declared_functions()
+    assert {"spec_verify_chain", "spec_verify_greedy", "spec_verify_tree"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared but not exported"
+
+
+def test_abi_version_and_strings():
+    lib = sv.load_library()
+    assert lib.spec_abi_version() == 1
+    for c in range(6):
+        assert lib.spec_status_string(c)
+    for c in range(8):
+        assert lib.spec_req_status_string(c)
+
+
+def test_workspace_sizes():
+    lib = sv.load_library()
+    n = lib.spec_chain_workspace_bytes(64, 5, 128256)
+    # summaries (8 B per 2048-element chunk per row) dominate: 64*6*63*8 B = 193536 B
+    assert 193536 <= n < 193536 + 64 * 64 * 16 + 8 * 256
+    assert lib.spec_chain_workspace_bytes(0, 5, 128256) == 0
+    assert lib.spec_chain_workspace_bytes(1, 64, 10) == 0      # gamma above the limit
+    assert lib.spec_chain_workspace_bytes(1, 5, 0) == 0
+    assert lib.spec_greedy_workspace_bytes(256, 8, 128256) > 0
+    assert lib.spec_tree_workspace_bytes(32, 63, 152064) > 0
+    assert lib.spec_tree_workspace_bytes(32, 5000, 152064) == 0  # N above the limit
+
+
+def _chain(lib, *, B=2, gamma=2, V=16, T=1.0, ldt=0, qdt=0, logits=FAKE, q=FAKE, tok=FAKE, u=FAKE,
+           acc=FAKE, out=FAKE, st=FAKE, ws=NULL, wsn=0):
+    return lib.spec_verify_chain(logits, ldt, q, qdt, tok, u, B, gamma, V, ctypes.c_float(T),
+                                 acc, out, st, NULL, ws, wsn, NULL)
+
+
+def test_chain_host_validation():
+    lib = sv.load_library()
+    assert _chain(lib, B=-1) == EINVAL
+    assert _chain(lib, gamma=-1) == EINVAL
+    assert _chain(lib, gamma=64) == EINVAL
+    assert _chain(lib, V=0) == EINVAL
+    for T in (0.0, -1.0, float("nan"), float("inf"), 1e-9, 1e9):
+        assert _chain(lib, T=T) == EINVAL
+    assert _chain(lib, ldt=7) == EDTYPE
+    assert _chain(lib, qdt=-1) == EDTYPE
+    assert _chain(lib, B=0, logits=NULL, q=NULL, tok=NULL, u=NULL, acc=NULL, out=NULL, st=NULL) == OK
+    assert _chain(lib, logits=NULL) == EINVAL
+    assert _chain(lib, u=NULL) == EINVAL
+    assert _chain(lib, q=NULL) == EINVAL
+    assert _chain(lib, gamma=0, q=NULL, tok=NULL) == EWORKSPACE    # gamma 0 needs no drafts
+    assert _chain(lib, ws=NULL, wsn=1 << 20) == EWORKSPACE
+    assert _chain(lib, ws=ctypes.c_void_p(0x1001), wsn=1 << 20) == EWORKSPACE   # misaligned
+    assert _chain(lib, ws=ctypes.c_void_p(0x10000), wsn=8) == EWORKSPACE        # too small
+
+
+def test_greedy_and_tree_host_validation():
+    lib = sv.load_library()
+    g = lambda **k: lib.spec_verify_greedy(k.get("l", FAKE), k.get("dt", 1), k.get("t", FAKE),
+                                            k.get("B", 2), k.get("G", 2), k.get("V", 16),
+                                            FAKE, FAKE, FAKE, k.get("ws", NULL), k.get("wsn", 0), NULL)
+    assert g(B=-1) == EINVAL and g(G=64) == EINVAL and g(V=0) == EINVAL
+    assert g(dt=3) == EDTYPE and g(l=NULL) == EINVAL and g(t=NULL) == EINVAL
+    assert g(G=0, t=NULL) == EWORKSPACE and g(B=0, l=NULL) == OK
+    t = lambda **k: lib.spec_verify_tree(k.get("l", FAKE), k.get("dt", 1), FAKE, k.get("par", FAKE),
+                                          FAKE, k.get("B", 2), k.get("N", 5), k.get("V", 16),
+                                          ctypes.c_float(k.get("T", 1.0)), FAKE, FAKE, FAKE, FAKE,
+                                          NULL, 0, NULL)
+    assert t(N=0) == EINVAL and t(N=4097) == EINVAL and t(T=0.0) == EINVAL
+    assert t(dt=2) == EDTYPE and t(par=NULL) == EINVAL and t(B=0, l=NULL) == OK
+    assert t() == EWORKSPACE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 3, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        sv.spec_verify_greedy(x, torch.zeros(2, 2, dtype=torch.int32))
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The package and its library never touch oracle/ (no CPU fallback)."""
+    pkg = os.path.join(ROOT, "exact_rejection_sampling_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            path = os.path.join(dirpath, f)
+            if f.endswith(".py"):
+                src = open(path).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", src, flags=re.M), path
+            elif f.endswith((".hip", ".h", ".cpp")):
+                assert "oracle" not in open(path).read().lower(), path
