@@ -99,10 +99,9 @@ spec_status spec_verify_chain(const void* target_logits, int logit_dtype, const 
   p.req_status = req_status;
   p.stats = stats;
   p.part = reinterpret_cast<float2*>(ws + L.part);
-  p.count1 = reinterpret_cast<unsigned*>(ws + L.count1);
+  p.counters = sv::request_counters(workspace);
   p.dec = reinterpret_cast<sv::ChainDecision*>(ws + L.dec);
   p.tmass = reinterpret_cast<double*>(ws + L.tmass);
-  p.count2 = reinterpret_cast<unsigned*>(ws + L.count2);
   p.B = B;
   p.G = gamma;
   p.R = gamma + 1;
@@ -137,8 +136,8 @@ spec_status spec_verify_greedy(const void* target_logits, int logit_dtype, const
   p.accepted_len = accepted_len;
   p.out_tokens = out_tokens;
   p.req_status = req_status;
-  p.part = reinterpret_cast<sv::GreedyPart*>(ws + L.part);
-  p.count = reinterpret_cast<unsigned*>(ws + L.count);
+  p.part = reinterpret_cast<unsigned long long*>(ws + L.part);
+  p.counters = sv::request_counters(workspace);
   p.B = B;
   p.G = gamma;
   p.R = gamma + 1;
@@ -176,7 +175,7 @@ spec_status spec_verify_tree(const void* node_logits, int logit_dtype, const int
   p.out_nodes = out_nodes;
   p.req_status = req_status;
   p.part = reinterpret_cast<float2*>(ws + L.part);
-  p.count = reinterpret_cast<unsigned*>(ws + L.count);
+  p.counters = sv::request_counters(workspace);
   p.B = B;
   p.N = N;
   p.V = V;

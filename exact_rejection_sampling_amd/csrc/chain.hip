@@ -55,12 +55,12 @@ __device__ void chain_decide(const ChainParams& p, int b) {
   for (int i = wave; i < p.R; i += kWavesPerBlock) {
     const float2* part = p.part + ((size_t)b * p.R + i) * p.P;
     float m = -INFINITY;
-    for (int j = lane; j < p.P; j += kWave) m = fmaxf(m, part[j].x);
+    for (int j = lane; j < p.P; j += kWave) m = fmaxf(m, fetch_f2(part + j).x);
     m = wave_max(m);
     const float r = m * c2;
     double z = 0.0;
     for (int j = lane; j < p.P; j += kWave) {
-      const float2 s = part[j];
+      const float2 s = fetch_f2(part + j);
       const float rj = s.x * c2;
       z += (double)s.y * exp2((double)rj - (double)r);
     }
@@ -74,6 +74,11 @@ __device__ void chain_decide(const ChainParams& p, int b) {
     }
   }
   __syncthreads();
+  // the summaries are consumed: return them to zero (every call leaves the workspace zeroed)
+  {
+    float2* part = p.part + (size_t)b * p.R * p.P;
+    for (int j = threadIdx.x; j < p.R * p.P; j += kBlock) part[j] = make_float2(0.0f, 0.0f);
+  }
   if (wave != 0) return;
 
   // lane i < G: draft position i, checked in the order a round reaches it
@@ -165,22 +170,18 @@ __global__ __launch_bounds__(kBlock) void chain_stats_kernel(ChainParams p) {
   if (chunk < p.P) {
     float m, z;
     chunk_summary<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, chunk, lane, p.c2, m, z);
-    if (lane == 0) {
-      p.part[rowid * p.P + chunk] = make_float2(m, z);
-      release_device();
-    }
+    if (lane == 0) publish_f2(p.part + rowid * p.P + chunk, make_float2(m, z));
   }
-  __syncthreads();
+  __syncthreads();   // every wave's summary store has completed
   __shared__ int s_last;
   if (threadIdx.x == 0) {
-    const unsigned prev = arrive(&p.count1[b]);
+    const unsigned prev = arrive(&p.counters[(size_t)b * kCounterSlots + 0]);
     s_last = (prev == (unsigned)(p.R * p.WG1 - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  acquire_device();
   chain_decide<DT>(p, b);
-  if (threadIdx.x == 0) reset_counter(&p.count1[b]);
+  if (threadIdx.x == 0) reset_counter(&p.counters[(size_t)b * kCounterSlots + 0]);
 }
 
 // Terminal weight of one element: p(x) = 2^(l c2 - r) / Z; residual rows subtract q and
@@ -231,11 +232,11 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
   const int per = (p.S2 + kBlock - 1) / kBlock;
   const int c_lo = min(tid * per, p.S2), c_hi = min(c_lo + per, p.S2);
   double mine = 0.0;
-  for (int c = c_lo; c < c_hi; ++c) mine += tm[c];
+  for (int c = c_lo; c < c_hi; ++c) mine += fetch_d(tm + c);
   double tot;
   const double excl = block_excl_scan_d(mine, s_scan, &tot);
   double run_end = excl;
-  for (int c = c_lo; c < c_hi; ++c) run_end += tm[c];
+  for (int c = c_lo; c < c_hi; ++c) run_end += fetch_d(tm + c);
   if (c_lo < c_hi && c_hi == p.S2) s_total = run_end;
   if (tid == 0) s_pick = 0x7fffffff;
   __syncthreads();
@@ -249,7 +250,7 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
   {
     double run = excl;
     for (int c = c_lo; c < c_hi; ++c) {
-      const double nxt = run + tm[c];
+      const double nxt = run + fetch_d(tm + c);
       if (nxt > t) {
         atomicMin(&s_pick, c);
         break;
@@ -264,7 +265,7 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
   __syncthreads();
   if (cstar >= c_lo && cstar < c_hi) {       // the owner of cstar records the mass before it
     double run = excl;
-    for (int c = c_lo; c < cstar; ++c) run += tm[c];
+    for (int c = c_lo; c < cstar; ++c) run += fetch_d(tm + c);
     s_before = run;
   }
   __syncthreads();
@@ -347,15 +348,20 @@ __device__ void chain_terminal_body(const ChainParams& p, int b, int c, const Ch
   __shared__ int s_last;
   if (tid == 0) {
     const double m = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
-    p.tmass[(size_t)b * p.S2 + c] = m;
-    const unsigned prev = arrive(&p.count2[b]);
+    publish_d(p.tmass + (size_t)b * p.S2 + c, m);
+    vmem_wait();
+    const unsigned prev = arrive(&p.counters[(size_t)b * kCounterSlots + 1]);
     s_last = (prev == (unsigned)(p.S2 - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  acquire_device();
   chain_select<DT, QT, VEC, RESID>(p, b, d, lrow, qrow);
-  if (tid == 0) reset_counter(&p.count2[b]);
+  __syncthreads();
+  for (int j = tid; j < p.S2; j += kBlock) p.tmass[(size_t)b * p.S2 + j] = 0.0;
+  if (tid == 0) {
+    p.dec[b] = ChainDecision{0, 0, 0.0f, 0.0f};
+    reset_counter(&p.counters[(size_t)b * kCounterSlots + 1]);
+  }
 }
 
 template <int DT, int QT, bool VEC>
@@ -363,7 +369,21 @@ __global__ __launch_bounds__(kBlock) void chain_terminal_kernel(ChainParams p) {
   const int b = blockIdx.x / p.S2;
   const int c = blockIdx.x % p.S2;
   const ChainDecision d = p.dec[b];
-  if (d.status != 0) return;            // failed in the statistics pass, outputs written
+  if (d.status != 0) {
+    // failed in the statistics pass (outputs already written): only count the arrival,
+    // so that the last block can clear the decision record
+    __shared__ int s_last;
+    if (threadIdx.x == 0) {
+      const unsigned prev = arrive(&p.counters[(size_t)b * kCounterSlots + 1]);
+      s_last = (prev == (unsigned)(p.S2 - 1));
+    }
+    __syncthreads();
+    if (s_last && threadIdx.x == 0) {
+      p.dec[b] = ChainDecision{0, 0, 0.0f, 0.0f};
+      reset_counter(&p.counters[(size_t)b * kCounterSlots + 1]);
+    }
+    return;
+  }
   if (d.A < p.G) chain_terminal_body<DT, QT, VEC, true>(p, b, c, d);
   else chain_terminal_body<DT, QT, VEC, false>(p, b, c, d);
 }

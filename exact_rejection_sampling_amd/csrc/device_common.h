@@ -218,18 +218,49 @@ __device__ __forceinline__ float scaled_exp(float l, float c2, float r) {
   return __builtin_amdgcn_exp2f(fmaf(l, c2, -r));
 }
 
-// ------------------------------------------------------------------ arrival counters
-// Release this thread's prior global writes at device scope, then count one arrival.
+// ------------------------------------------------------------------ cross-block traffic
+// Values that other blocks read within the same launch (chunk summaries, chunk masses)
+// are written and read with device-scope relaxed atomics: on this target those are
+// write-through stores and L2-bypassing loads, so they are coherent across the XCDs'
+// separate L2 caches without any cache-wide writeback or invalidate.  A block publishes
+// them by (1) storing with publish_*, (2) waiting for its own stores to complete
+// (__syncthreads, or vmem_wait() in a single thread), and (3) counting its arrival with a
+// relaxed device-scope add.  The block that sees the final count reads with fetch_*.
+__device__ __forceinline__ void publish_f2(float2* p, float2 v) {
+  const unsigned long long bits =
+      (static_cast<unsigned long long>(__float_as_uint(v.y)) << 32) | __float_as_uint(v.x);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), bits, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 fetch_f2(const float2* p) {
+  const unsigned long long bits = __hip_atomic_load(
+      reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<unsigned>(bits)),
+                     __uint_as_float(static_cast<unsigned>(bits >> 32)));
+}
+__device__ __forceinline__ void publish_d(double* p, double v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                     static_cast<unsigned long long>(__double_as_longlong(v)), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double fetch_d(const double* p) {
+  return __longlong_as_double(static_cast<long long>(__hip_atomic_load(
+      reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+}
+__device__ __forceinline__ void publish_u64(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long fetch_u64(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this thread's outstanding memory operations have completed (a
+// workgroup-scope release: no cache maintenance on this target).
+__device__ __forceinline__ void vmem_wait() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup"); }
+
+// Count one arrival; returns the count before this one.
 __device__ __forceinline__ unsigned arrive(unsigned* counter) {
-  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void acquire_device() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
-__device__ __forceinline__ void release_device() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void reset_counter(unsigned* counter) {

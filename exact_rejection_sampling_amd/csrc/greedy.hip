@@ -45,10 +45,18 @@ __device__ __forceinline__ GreedyPart greedy_chunk(const void* row, long V, long
     for (int k = 7; k >= 0; --k)
       if (v[j][k] == M) idx = static_cast<int>(base + static_cast<long>(j * kWave + lane) * kVec + k);
   GreedyPart g;
-  g.m = M;
+  g.m = wave_any(nan) ? __uint_as_float(0x7fc00000u) : M;   // NaN marks a chunk holding NaN
   g.idx = wave_min_i(idx);
-  g.nan = wave_any(nan) ? 1 : 0;
-  g.pad = 0;
+  return g;
+}
+
+__device__ __forceinline__ unsigned long long pack(const GreedyPart& g) {
+  return (static_cast<unsigned long long>(static_cast<unsigned>(g.idx)) << 32) | __float_as_uint(g.m);
+}
+__device__ __forceinline__ GreedyPart unpack(unsigned long long b) {
+  GreedyPart g;
+  g.m = __uint_as_float(static_cast<unsigned>(b));
+  g.idx = static_cast<int>(static_cast<unsigned>(b >> 32));
   return g;
 }
 
@@ -57,17 +65,20 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
   __shared__ int s_bad[SPEC_MAX_GAMMA + 1];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   for (int i = wave; i < p.R; i += kWavesPerBlock) {
-    const GreedyPart* part = p.part + ((size_t)b * p.R + i) * p.P;
+    const unsigned long long* part = p.part + ((size_t)b * p.R + i) * p.P;
     float m = -INFINITY;
     int nan = 0;
     for (int j = lane; j < p.P; j += kWave) {
-      m = fmaxf(m, part[j].m);
-      nan |= part[j].nan;
+      const GreedyPart g = unpack(fetch_u64(part + j));
+      m = fmaxf(m, g.m);
+      nan |= (g.m != g.m);
     }
     const float M = wave_max(m);
     int idx = 0x7fffffff;
-    for (int j = lane; j < p.P; j += kWave)
-      if (part[j].m == M) idx = min(idx, part[j].idx);
+    for (int j = lane; j < p.P; j += kWave) {
+      const GreedyPart g = unpack(fetch_u64(part + j));
+      if (g.m == M) idx = min(idx, g.idx);
+    }
     idx = wave_min_i(idx);
     const bool any_nan = wave_any(nan != 0);
     if (lane == 0) {
@@ -76,6 +87,10 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
     }
   }
   __syncthreads();
+  {
+    unsigned long long* part = p.part + (size_t)b * p.R * p.P;     // consumed: back to zero
+    for (int j = threadIdx.x; j < p.R * p.P; j += kBlock) part[j] = 0ull;
+  }
   if (wave != 0) return;
   const int G = p.G;
   int code = 0;
@@ -113,22 +128,18 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(GreedyParams p) {
   const int chunk = slice * kWavesPerBlock + wave;
   if (chunk < p.P) {
     const GreedyPart g = greedy_chunk<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, chunk, lane);
-    if (lane == 0) {
-      p.part[rowid * p.P + chunk] = g;
-      release_device();
-    }
+    if (lane == 0) publish_u64(p.part + rowid * p.P + chunk, pack(g));
   }
-  __syncthreads();
+  __syncthreads();   // every wave's summary store has completed
   __shared__ int s_last;
   if (threadIdx.x == 0) {
-    const unsigned prev = arrive(&p.count[b]);
+    const unsigned prev = arrive(&p.counters[(size_t)b * kCounterSlots + 0]);
     s_last = (prev == (unsigned)(p.R * p.WG1 - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  acquire_device();
   greedy_decide(p, b);
-  if (threadIdx.x == 0) reset_counter(&p.count[b]);
+  if (threadIdx.x == 0) reset_counter(&p.counters[(size_t)b * kCounterSlots + 0]);
 }
 
 template <int DT, bool VEC>

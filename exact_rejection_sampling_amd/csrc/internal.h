@@ -27,10 +27,9 @@ struct ChainParams {
   float* stats;              // [B, R, 4] or null
   // workspace
   float2* part;              // [B*R*P] wave-chunk summaries (raw max, Z)
-  unsigned* count1;          // [B] statistics-pass arrivals
+  unsigned* counters;        // per-request slots: [b*4 + 0] statistics, [b*4 + 1] terminal
   ChainDecision* dec;        // [B]
   double* tmass;             // [B*S2] terminal chunk masses
-  unsigned* count2;          // [B] terminal-pass arrivals
   int B, G, R, V;
   int P;                     // wave chunks per row = ceil(V / 2048)
   int WG1;                   // blocks per row in the statistics pass = ceil(P / 4)
@@ -43,11 +42,10 @@ struct ChainParams {
 constexpr int kTermSlabs = 2;                 // slabs per terminal chunk
 constexpr int kTermChunk = kTermSlabs * 2048;  // elements per terminal chunk
 
+// Greedy chunk summary, stored packed in 64 bits (idx << 32 | bits of m).
 struct GreedyPart {
-  float m;      // wave-chunk maximum
-  int32_t idx;  // lowest index attaining it (INT32_MAX if none)
-  int32_t nan;  // chunk holds a NaN
-  int32_t pad;
+  float m;      // wave-chunk maximum, or NaN if the chunk holds a NaN
+  int32_t idx;  // lowest index attaining it
 };
 
 struct GreedyParams {
@@ -56,8 +54,8 @@ struct GreedyParams {
   int32_t* accepted_len;
   int32_t* out_tokens;
   int32_t* req_status;
-  GreedyPart* part;          // [B*R*P]
-  unsigned* count;           // [B]
+  unsigned long long* part;  // [B*R*P] packed GreedyPart
+  unsigned* counters;        // per-request slots: [b*4 + 0] arrivals
   int B, G, R, V, P, WG1;
 };
 
@@ -71,49 +69,57 @@ struct TreeParams {
   int32_t* out_nodes;
   int32_t* req_status;
   float2* part;              // [B*P] summaries of the row being walked
-  unsigned* count;           // [B]
+  unsigned* counters;        // per-request slots: [b*4 + 0] arrivals
   int B, N, V, P, WG1;
   float c2;
 };
 
-// Workspace carving: each region starts on a 256-byte boundary.
+// Workspace carving: 256 bytes of global counters, kCounterSlots 32-bit counters per
+// request, then the data regions, each on a 256-byte boundary.  Every call returns all
+// of it to zero (counters are reset and intermediate results cleared by the blocks that
+// consume them), so a zero-filled workspace stays valid for any later call, of any
+// entry point and any sizes, issued in order on the same stream.
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+constexpr int kCounterSlots = 4;                 // per request
+constexpr size_t kGlobalCounterBytes = 256;
+inline size_t counter_bytes(long B) { return align256(kGlobalCounterBytes + sizeof(unsigned) * kCounterSlots * B); }
+inline unsigned* request_counters(void* ws) {
+  return reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kGlobalCounterBytes);
+}
+// slot s of request b: request_counters(ws)[b * kCounterSlots + s]
+
 struct ChainLayout {
-  size_t part, count1, dec, tmass, count2, total;
+  size_t part, dec, tmass, total;
 };
 inline ChainLayout chain_layout(long B, long G, long V) {
   const long R = G + 1, P = (V + 2047) / 2048, S2 = (V + kTermChunk - 1) / kTermChunk;
   ChainLayout L;
-  size_t o = 0;
+  size_t o = counter_bytes(B);
   L.part = o;   o = align256(o + sizeof(float2) * B * R * P);
-  L.count1 = o; o = align256(o + sizeof(unsigned) * B);
   L.dec = o;    o = align256(o + sizeof(ChainDecision) * B);
   L.tmass = o;  o = align256(o + sizeof(double) * B * S2);
-  L.count2 = o; o = align256(o + sizeof(unsigned) * B);
   L.total = o;
   return L;
 }
 
-struct GreedyLayout { size_t part, count, total; };
+struct GreedyLayout { size_t part, total; };
 inline GreedyLayout greedy_layout(long B, long G, long V) {
   const long R = G + 1, P = (V + 2047) / 2048;
   GreedyLayout L;
-  size_t o = 0;
-  L.part = o;  o = align256(o + sizeof(GreedyPart) * B * R * P);
-  L.count = o; o = align256(o + sizeof(unsigned) * B);
+  size_t o = counter_bytes(B);
+  L.part = o;  o = align256(o + sizeof(unsigned long long) * B * R * P);
   L.total = o;
   return L;
 }
 
-struct TreeLayout { size_t part, count, total; };
+struct TreeLayout { size_t part, total; };
 inline TreeLayout tree_layout(long B, long N, long V) {
   (void)N;
   const long P = (V + 2047) / 2048;
   TreeLayout L;
-  size_t o = 0;
+  size_t o = counter_bytes(B);
   L.part = o;  o = align256(o + sizeof(float2) * B * P);
-  L.count = o; o = align256(o + sizeof(unsigned) * B);
   L.total = o;
   return L;
 }

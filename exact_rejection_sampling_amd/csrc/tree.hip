@@ -54,7 +54,7 @@ __device__ int sample_row(const TreeParams& p, int b, const void* row, float uv,
   // reference exponent: fp32(max raw logit * c2), identical to the chunks' own r_j
   if (wave == 0) {
     float m = -INFINITY;
-    for (int j = lane; j < p.P; j += kWave) m = fmaxf(m, part[j].x);
+    for (int j = lane; j < p.P; j += kWave) m = fmaxf(m, fetch_f2(part + j).x);
     m = wave_max(m);
     if (lane == 0) s_r = m * c2;
   }
@@ -66,14 +66,14 @@ __device__ int sample_row(const TreeParams& p, int b, const void* row, float uv,
   const int c_lo = min(tid * per, p.P), c_hi = min(c_lo + per, p.P);
   double mine = 0.0;
   for (int c = c_lo; c < c_hi; ++c) {
-    const float2 s = part[c];
+    const float2 s = fetch_f2(part + c);
     mine += (double)s.y * exp2((double)(s.x * c2) - (double)R);
   }
   double tot;
   const double excl = block_excl_scan_d(mine, s_scan, &tot);
   double run_end = excl;
   for (int c = c_lo; c < c_hi; ++c) {
-    const float2 s = part[c];
+    const float2 s = fetch_f2(part + c);
     run_end += (double)s.y * exp2((double)(s.x * c2) - (double)R);
   }
   if (c_lo < c_hi && c_hi == p.P) s_total = run_end;
@@ -86,7 +86,7 @@ __device__ int sample_row(const TreeParams& p, int b, const void* row, float uv,
   {
     double run = excl;
     for (int c = c_lo; c < c_hi; ++c) {
-      const float2 s = part[c];
+      const float2 s = fetch_f2(part + c);
       const double nxt = run + (double)s.y * exp2((double)(s.x * c2) - (double)R);
       if (nxt > t) { atomicMin(&s_pick, c); break; }
       run = nxt;
@@ -100,7 +100,7 @@ __device__ int sample_row(const TreeParams& p, int b, const void* row, float uv,
   if (cstar >= c_lo && cstar < c_hi) {
     double run = excl;
     for (int c = c_lo; c < cstar; ++c) {
-      const float2 s = part[c];
+      const float2 s = fetch_f2(part + c);
       run += (double)s.y * exp2((double)(s.x * c2) - (double)R);
     }
     s_before = run;
@@ -110,7 +110,7 @@ __device__ int sample_row(const TreeParams& p, int b, const void* row, float uv,
   __syncthreads();
 
   // rescan chunk cstar (one slab) in the chunk's own units 2^(l c2 - r_c)
-  const float rc = part[cstar].x * c2;
+  const float rc = fetch_f2(part + cstar).x * c2;
   const double rem = (t - s_before) * exp2((double)R - (double)rc);
   const long e0 = (long)cstar * kWaveChunk + (long)tid * kVec;
   float v[8];
@@ -147,13 +147,9 @@ __device__ void summarize_row(const TreeParams& p, int b, const void* row) {
   for (int c = wave; c < p.P; c += kWavesPerBlock) {
     float m, z;
     chunk_summary<DT, VEC>(row, p.V, c, lane, p.c2, m, z);
-    if (lane == 0) {
-      p.part[(size_t)b * p.P + c] = make_float2(m, z);
-      release_device();
-    }
+    if (lane == 0) publish_f2(p.part + (size_t)b * p.P + c, make_float2(m, z));
   }
   __syncthreads();
-  acquire_device();
 }
 
 template <int DT, bool VEC>
@@ -222,22 +218,20 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
   if (chunk < p.P) {
     float m, z;
     chunk_summary<DT, VEC>(row_ptr<DT>(p.logits, (size_t)b * p.N, p.V), p.V, chunk, lane, p.c2, m, z);
-    if (lane == 0) {
-      p.part[(size_t)b * p.P + chunk] = make_float2(m, z);
-      release_device();
-    }
+    if (lane == 0) publish_f2(p.part + (size_t)b * p.P + chunk, make_float2(m, z));
   }
-  __syncthreads();
+  __syncthreads();   // every wave's summary store has completed
   __shared__ int s_last;
   if (threadIdx.x == 0) {
-    const unsigned prev = arrive(&p.count[b]);
+    const unsigned prev = arrive(&p.counters[(size_t)b * kCounterSlots + 0]);
     s_last = (prev == (unsigned)(p.WG1 - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  acquire_device();
   tree_walk<DT, VEC>(p, b);
-  if (threadIdx.x == 0) reset_counter(&p.count[b]);
+  __syncthreads();
+  for (int j = threadIdx.x; j < p.P; j += kBlock) p.part[(size_t)b * p.P + j] = make_float2(0.0f, 0.0f);
+  if (threadIdx.x == 0) reset_counter(&p.counters[(size_t)b * kCounterSlots + 0]);
 }
 
 template <int DT, bool VEC>

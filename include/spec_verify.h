@@ -22,10 +22,11 @@
  *           `stream`, and outputs are valid once that stream reaches the call.
  * Workspace. Each entry point takes a caller-owned device workspace of at least the
  *           size its query function returns, aligned to 256 bytes.  It must be
- *           zero-filled before its first use; every call leaves it zeroed again
- *           (the counters it holds reset themselves), so one workspace serves any
- *           number of calls issued in order on one stream.  Calls that overlap in
- *           time must use different workspaces.
+ *           zero-filled before its first use, and every call leaves it entirely
+ *           zero again (the blocks that consume counters and intermediate results
+ *           clear them), so one workspace serves any sequence of calls -- any entry
+ *           point, any sizes that fit it -- issued in order on one stream.  Calls
+ *           that overlap in time must use different workspaces.
  * Host status.  The return value reports only what the host can check before
  *           launching: null pointers, sizes outside the documented limits, a
  *           temperature outside its range, an unknown dtype, a workspace that is too

@@ -48,7 +48,7 @@ def test_workspace_sizes():
     n = lib.spec_chain_workspace_bytes(64, 5, 128256)
     # summaries (8 B per 2048-element chunk per row) dominate: 64*6*63*8 B = 193536 B
     assert 193536 <= n < 193536 + 64 * 64 * 16 + 8 * 256
-    assert lib.spec_chain_workspace_bytes(0, 5, 128256) == 0
+    assert lib.spec_chain_workspace_bytes(0, 5, 128256) == 256   # the counter header only
     assert lib.spec_chain_workspace_bytes(1, 64, 10) == 0      # gamma above the limit
     assert lib.spec_chain_workspace_bytes(1, 5, 0) == 0
     assert lib.spec_greedy_workspace_bytes(256, 8, 128256) > 0

@@ -242,3 +242,29 @@ def test_chi_square_million_trials():
                n_all=int(allacc.sum())))
     for pv in (p1, p2, p3, p4):
         assert pv > 1e-3
+
+
+def test_one_workspace_across_shapes_and_entry_points():
+    """Counters sit at fixed offsets: a single zero-filled workspace serves calls of any
+    size and any entry point issued in order on one stream."""
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    cases = [synth.make_chain(16, 5, 32000, seed=1, boost_frac=0.01),
+             synth.make_chain(8, 0, 1500, seed=2),
+             synth.make_chain(33, 3, 70001, seed=3, logit_dtype="f32"),
+             synth.make_chain(2, 63, 900, seed=4)]
+    from gpu_util import run_greedy
+    for rep in range(2):
+        for x in cases:
+            say(f"shared workspace chain B={x.B} gamma={x.gamma} V={x.V} rep={rep}")
+            out = to_np(sv.spec_verify_chain(t_logits(x.logits, x.logit_dtype), t_f32(x.q), t_i32(x.tokens),
+                                             t_f32(x.u), float(x.temperature), with_stats=True,
+                                             workspace_tensor=ws))
+            compare_chain(out, oracle_chain(x))
+            g = synth.make_greedy(x.B, x.gamma, x.V, seed=x.V)
+            say(f"shared workspace greedy B={g.B} gamma={g.gamma} V={g.V}")
+            gout = to_np(sv.spec_verify_greedy(t_logits(g.logits, g.logit_dtype), t_i32(g.tokens),
+                                               workspace_tensor=ws))
+            exp = oracle.verify_greedy(g.logits, g.tokens, g.logit_dtype)
+            np.testing.assert_array_equal(gout["out_tokens"], exp["out_tokens"])
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0              # the whole workspace is back at zero
