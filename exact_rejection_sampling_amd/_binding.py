@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
 SPEC_F32, SPEC_BF16 = 0, 1
 REQ_STATUS = {0: "OK", 1: "NONFINITE", 2: "BADTOKEN", 3: "BADUNIFORM", 4: "QZERO",
-              5: "RESIDUAL_EMPTY", 6: "BADTREE"}
+              5: "RESIDUAL_EMPTY", 6: "BADTREE", 7: "INTERNAL"}
 
 _lib = None
 _lock = threading.Lock()

@@ -22,12 +22,6 @@ bool sizes_ok(int B, int gamma, int V) {
          V <= SPEC_MAX_VOCAB;
 }
 int chunks(long V, long per) { return static_cast<int>((V + per - 1) / per); }
-// one block per (row, 8192-element slice) must fit the 1-D grid
-bool grid_ok(long rows, long V) {
-  const long slices = (V + 4 * 2048 - 1) / (4 * 2048);
-  return rows * slices <= 0x7fffffffL && rows * ((V + sv::kTermChunk - 1) / sv::kTermChunk) <= 0x7fffffffL;
-}
-
 }  // namespace
 
 extern "C" {
@@ -54,23 +48,25 @@ const char* spec_req_status_string(int code) {
     case SPEC_REQ_QZERO: return "draft probability of a proposed token is not positive";
     case SPEC_REQ_RESIDUAL_EMPTY: return "terminal mass not positive or q row invalid";
     case SPEC_REQ_BADTREE: return "invalid parent array or node token";
+    case SPEC_REQ_INTERNAL: return "internal wait bound reached (outputs invalid)";
     default: return "unknown request status";
   }
 }
 
 size_t spec_chain_workspace_bytes(int B, int gamma, int V) {
-  if (!sizes_ok(B, gamma, V)) return 0;
+  if (!sizes_ok(B, gamma, V) || !sv::grid_fits(sv::chain_blocks(B, gamma, V))) return 0;
   return sv::chain_layout(B, gamma, V).total;
 }
 
 size_t spec_greedy_workspace_bytes(int B, int gamma, int V) {
-  if (!sizes_ok(B, gamma, V)) return 0;
+  if (!sizes_ok(B, gamma, V) || !sv::grid_fits(sv::greedy_blocks(B, gamma, V))) return 0;
   return sv::greedy_layout(B, gamma, V).total;
 }
 
 size_t spec_tree_workspace_bytes(int B, int N, int V) {
   if (!(B >= 0 && B <= SPEC_MAX_BATCH && N >= 1 && N <= SPEC_MAX_NODES && V >= 1 && V <= SPEC_MAX_VOCAB))
     return 0;
+  if (!sv::grid_fits(sv::tree_blocks(B, V))) return 0;
   return sv::tree_layout(B, N, V).total;
 }
 
@@ -81,7 +77,7 @@ spec_status spec_verify_chain(const void* target_logits, int logit_dtype, const 
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!sizes_ok(B, gamma, V) || !temperature_ok(temperature)) return SPEC_EINVAL;
   if (!dtype_ok(logit_dtype) || !dtype_ok(q_dtype)) return SPEC_EDTYPE;
-  if (!grid_ok((long)B * (gamma + 1), V)) return SPEC_EINVAL;
+  if (!sv::grid_fits(sv::chain_blocks(B, gamma, V))) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
   if (!target_logits || !uniforms || !accepted_len || !out_tokens || !req_status) return SPEC_EINVAL;
   if (gamma > 0 && (!draft_probs || !draft_tokens)) return SPEC_EINVAL;
@@ -99,15 +95,20 @@ spec_status spec_verify_chain(const void* target_logits, int logit_dtype, const 
   p.req_status = req_status;
   p.stats = stats;
   p.part = reinterpret_cast<float2*>(ws + L.part);
+  p.global = reinterpret_cast<unsigned*>(ws);
   p.counters = sv::request_counters(workspace);
   p.dec = reinterpret_cast<sv::ChainDecision*>(ws + L.dec);
+  p.gath = reinterpret_cast<unsigned long long*>(ws + L.gath);
   p.tmass = reinterpret_cast<double*>(ws + L.tmass);
   p.B = B;
   p.G = gamma;
   p.R = gamma + 1;
   p.V = V;
-  p.P = chunks(V, sv::kWaveChunk);
-  p.WG1 = chunks(p.P, sv::kWavesPerBlock);
+  const sv::Slicing sl = sv::slicing((long)B * (gamma + 1), V, sv::kChainTargetBlocks);
+  p.P = sl.P;
+  p.CPW = sl.CPW;
+  p.SL = sl.SL;
+  p.PP = sl.PP;
   p.S2 = chunks(V, sv::kTermChunk);
   p.q_dtype = q_dtype;
   const double c2 = kLog2e / static_cast<double>(temperature);
@@ -123,7 +124,7 @@ spec_status spec_verify_greedy(const void* target_logits, int logit_dtype, const
                                hipStream_t stream) {
   if (!sizes_ok(B, gamma, V)) return SPEC_EINVAL;
   if (!dtype_ok(logit_dtype)) return SPEC_EDTYPE;
-  if (!grid_ok((long)B * (gamma + 1), V)) return SPEC_EINVAL;
+  if (!sv::grid_fits(sv::greedy_blocks(B, gamma, V))) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
   if (!target_logits || !accepted_len || !out_tokens || !req_status) return SPEC_EINVAL;
   if (gamma > 0 && !draft_tokens) return SPEC_EINVAL;
@@ -142,8 +143,11 @@ spec_status spec_verify_greedy(const void* target_logits, int logit_dtype, const
   p.G = gamma;
   p.R = gamma + 1;
   p.V = V;
-  p.P = chunks(V, sv::kWaveChunk);
-  p.WG1 = chunks(p.P, sv::kWavesPerBlock);
+  const sv::Slicing sl = sv::slicing((long)B * (gamma + 1), V);
+  p.P = sl.P;
+  p.CPW = sl.CPW;
+  p.SL = sl.SL;
+  p.PP = sl.PP;
   const bool vec = (V % 8 == 0) && aligned16(target_logits);
   return sv::launch_greedy(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
@@ -157,7 +161,7 @@ spec_status spec_verify_tree(const void* node_logits, int logit_dtype, const int
     return SPEC_EINVAL;
   if (!temperature_ok(temperature)) return SPEC_EINVAL;
   if (!dtype_ok(logit_dtype)) return SPEC_EDTYPE;
-  if (!grid_ok(B, V)) return SPEC_EINVAL;
+  if (!sv::grid_fits(sv::tree_blocks(B, V))) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
   if (!node_logits || !node_tokens || !parents || !uniforms || !accepted_len || !out_tokens ||
       !out_nodes || !req_status)
@@ -175,6 +179,7 @@ spec_status spec_verify_tree(const void* node_logits, int logit_dtype, const int
   p.out_nodes = out_nodes;
   p.req_status = req_status;
   p.part = reinterpret_cast<float2*>(ws + L.part);
+  p.part_deep = reinterpret_cast<float2*>(ws + L.part_deep);
   p.counters = sv::request_counters(workspace);
   p.B = B;
   p.N = N;

@@ -26,6 +26,10 @@ constexpr int kSlab = kBlock * kVec;                   // 2048
 
 enum : int { kF32 = 0, kBF16 = 1 };
 
+// Index of the calling wave in its block, as a wave-uniform (scalar) value: loop bounds and
+// branches derived from it then compile to scalar control flow.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / 64); }
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -149,7 +153,7 @@ __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 // Block-wide exclusive prefix (fp64) of one value per thread; returns the exclusive
 // prefix and writes the block total to *total.  `scratch` holds >= kWavesPerBlock doubles.
 __device__ __forceinline__ double block_excl_scan_d(double v, double* scratch, double* total) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   const double incl = wave_incl_scan_d(v, lane);
   double excl = __shfl_up(incl, 1, kWave);
   if (lane == 0) excl = 0.0;
@@ -167,49 +171,194 @@ __device__ __forceinline__ double block_excl_scan_d(double v, double* scratch, d
 }
 
 // ------------------------------------------------------------------ softmax pieces
-// Online-softmax summary of one wave chunk of a row: m = max of the raw logits, and
-// Z = sum_x 2^(l_x * c2 - r) with r = m * c2 (fp32), c2 = log2(e) / T.  The fma keeps
-// l_x * c2 - r exact before its single rounding, so the summary is relative to the
-// fp32 reference r that any later combine recomputes bit for bit as m * c2.
-//  * a chunk whose elements are all -inf gives (m, Z) = (-inf, 0) -- or Z = NaN if the
-//    "-inf" maximum hides NaN elements, since fmaxf drops NaN;
-//  * NaN or +inf elements make Z NaN (fma gives NaN, exp2 and the adds keep it).
+// Raw lane-vector storage for one wave chunk: 4 lane vectors of 8 elements.
+template <int DT> struct ChunkRegs;
+template <> struct ChunkRegs<kBF16> { u32x4 w[kStatVecs]; };
+template <> struct ChunkRegs<kF32> { f32x4 a[kStatVecs], b[kStatVecs]; };
+
+// Issue the loads of wave chunk `chunk` of a row (non-temporal: read once).  Lane L
+// holds lane vectors j*64 + L; vectors past the row end hold -inf.
 template <int DT, bool VEC>
-__device__ __forceinline__ void chunk_summary(const void* row, long V, long chunk, int lane,
-                                              float c2, float& m_out, float& z_out) {
-  float v[kStatVecs][8];
+__device__ __forceinline__ void chunk_load(const void* row, long V, long chunk, int lane, ChunkRegs<DT>& r) {
   const long base = chunk * kWaveChunk;
 #pragma unroll
-  for (int j = 0; j < kStatVecs; ++j)
-    load8<DT, VEC, true>(row, base + static_cast<long>(j * kWave + lane) * kVec, V, v[j], -INFINITY);
+  for (int j = 0; j < kStatVecs; ++j) {
+    const long e0 = base + static_cast<long>(j * kWave + lane) * kVec;
+    if constexpr (VEC) {
+      if constexpr (DT == kBF16) {
+        r.w[j] = e0 < V ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + e0))
+                        : u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+      } else {
+        const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(row) + e0);
+        const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        r.a[j] = e0 < V ? __builtin_nontemporal_load(p) : ninf;
+        r.b[j] = e0 < V ? __builtin_nontemporal_load(p + 1) : ninf;
+      }
+    } else {
+      float v[8];
+      load8<DT, false, false>(row, e0, V, v, -INFINITY);
+      if constexpr (DT == kBF16) {
+        // repack to bf16 bits (exact: the values came from bf16)
+        uint32_t t[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          t[k] = (__float_as_uint(v[2 * k]) >> 16) | (__float_as_uint(v[2 * k + 1]) & 0xffff0000u);
+        r.w[j] = u32x4{t[0], t[1], t[2], t[3]};
+      } else {
+        r.a[j] = f32x4{v[0], v[1], v[2], v[3]};
+        r.b[j] = f32x4{v[4], v[5], v[6], v[7]};
+      }
+    }
+  }
+}
+
+// Loads of a chunk known to lie entirely inside a 16-byte aligned row: unconditional, so
+// that the four loads issue back to back.
+template <int DT>
+__device__ __forceinline__ void chunk_load_full(const void* row, long chunk, int lane, ChunkRegs<DT>& r) {
+  const long base = chunk * kWaveChunk;
+#pragma unroll
+  for (int j = 0; j < kStatVecs; ++j) {
+    const long e0 = base + static_cast<long>(j * kWave + lane) * kVec;
+    if constexpr (DT == kBF16) {
+      r.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + e0));
+    } else {
+      const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(row) + e0);
+      r.a[j] = __builtin_nontemporal_load(p);
+      r.b[j] = __builtin_nontemporal_load(p + 1);
+    }
+  }
+}
+
+// One wave visits chunks first, first + stride, ... (n of them; chunks >= P do not exist)
+// of a row and calls f(regs, chunk) for each in order.  It works in batches of kBatch
+// chunks: a batch's loads all issue back to back, then the batch is reduced, so no load
+// registers live across iterations; the other waves of the CU keep HBM busy meanwhile.
+// Chunks entirely inside an aligned row use unconditional loads; a partial last chunk
+// (or an unaligned row) the checked loader.
+#ifndef SPEC_BATCH
+#define SPEC_BATCH 1
+#endif
+constexpr int kBatch = SPEC_BATCH;
+
+template <int DT, bool VEC, class F>
+__device__ __forceinline__ void stream_chunks(const void* row, long V, long P, long first, long stride, int n,
+                                              int lane, F&& f) {
+  const long p_full = VEC ? V / kWaveChunk : 0;
+  for (int k0 = 0; k0 < n; k0 += kBatch) {
+    if (first + k0 * stride >= P) break;
+    ChunkRegs<DT> r[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const long c = first + (k0 + k) * stride;
+      if (k0 + k < n && c < P) {
+        if (c < p_full) chunk_load_full<DT>(row, c, lane, r[k]);
+        else chunk_load<DT, VEC>(row, V, c, lane, r[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const long c = first + (k0 + k) * stride;
+      if (k0 + k < n && c < P) f(r[k], c);
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void chunk_values(const ChunkRegs<DT>& r, float (&v)[kStatVecs][8]) {
+#pragma unroll
+  for (int j = 0; j < kStatVecs; ++j) {
+    if constexpr (DT == kBF16) {
+      const u32x4 w = r.w[j];
+      v[j][0] = __uint_as_float(w.x << 16); v[j][1] = __uint_as_float(w.x & 0xffff0000u);
+      v[j][2] = __uint_as_float(w.y << 16); v[j][3] = __uint_as_float(w.y & 0xffff0000u);
+      v[j][4] = __uint_as_float(w.z << 16); v[j][5] = __uint_as_float(w.z & 0xffff0000u);
+      v[j][6] = __uint_as_float(w.w << 16); v[j][7] = __uint_as_float(w.w & 0xffff0000u);
+    } else {
+      v[j][0] = r.a[j].x; v[j][1] = r.a[j].y; v[j][2] = r.a[j].z; v[j][3] = r.a[j].w;
+      v[j][4] = r.b[j].x; v[j][5] = r.b[j].y; v[j][6] = r.b[j].z; v[j][7] = r.b[j].w;
+    }
+  }
+}
+
+// Per-lane online softmax state over the elements a lane has seen: m = max raw logit,
+// s = sum 2^(l * c2 - r) with r = m * c2 (fp32), nan = a NaN was seen.
+struct LaneSoftmax {
   float m = -INFINITY;
+  float s = 0.0f;
+  bool nan = false;
+};
+
+__device__ __forceinline__ void lane_softmax_update(LaneSoftmax& st, const float (&v)[kStatVecs][8], float c2) {
+  float cm = -INFINITY;
 #pragma unroll
   for (int j = 0; j < kStatVecs; ++j)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) m = fmaxf(m, v[j][k]);
-  m = wave_max(m);
-  float z;
-  if (m == -INFINITY) {
+    for (int k = 0; k < 8; ++k) cm = fmaxf(cm, v[j][k]);
+  if (cm > st.m) {                       // new maximum: rescale the running sum
+    if (st.m != -INFINITY) st.s *= __builtin_amdgcn_exp2f(st.m * c2 - cm * c2);
+    st.m = cm;
+  }
+  if (st.m == -INFINITY) {               // everything so far is -inf (or NaN)
     bool nan = false;
 #pragma unroll
     for (int j = 0; j < kStatVecs; ++j)
 #pragma unroll
       for (int k = 0; k < 8; ++k) nan |= (v[j][k] != v[j][k]);
-    z = wave_any(nan) ? NAN : 0.0f;
-  } else {
-    const float r = m * c2;
-    float s[kStatVecs];
-#pragma unroll
-    for (int j = 0; j < kStatVecs; ++j) {
-      float e[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) e[k] = __builtin_amdgcn_exp2f(fmaf(v[j][k], c2, -r));
-      s[j] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    }
-    z = wave_sum((s[0] + s[1]) + (s[2] + s[3]));
+    st.nan |= nan;
+    return;
   }
-  m_out = m;
+  const float r = st.m * c2;
+  float part[kStatVecs];
+#pragma unroll
+  for (int j = 0; j < kStatVecs; ++j) {
+    float e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = __builtin_amdgcn_exp2f(fmaf(v[j][k], c2, -r));
+    part[j] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  }
+  st.s += (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// Wave-wide merge of the lanes' states into (m, Z): m = max raw logit seen by the wave,
+// Z = sum 2^(l c2 - r), r = m * c2.  Z is NaN if any lane saw NaN or +inf; (m, Z) =
+// (-inf, 0) if every element was -inf.
+__device__ __forceinline__ void wave_softmax_merge(const LaneSoftmax& st, float c2, float& m_out, float& z_out) {
+  const float M = wave_max(st.m);
+  const bool nan = wave_any(st.nan);
+  float z;
+  if (M == -INFINITY) {
+    z = nan ? NAN : 0.0f;
+  } else {
+    const float R = M * c2;
+    const float term = st.m == -INFINITY ? (st.nan ? NAN : 0.0f)
+                                         : st.s * __builtin_amdgcn_exp2f(st.m * c2 - R);
+    z = wave_sum(term);
+    if (nan) z = NAN;
+  }
+  m_out = M;
   z_out = z;
+}
+
+// Online-softmax summary of the chunks a wave visits (see stream_chunks).
+template <int DT, bool VEC>
+__device__ __forceinline__ void wave_row_summary(const void* row, long V, long P, long first, long stride,
+                                                 int n, int lane, float c2, float& m_out, float& z_out) {
+  LaneSoftmax st;
+  stream_chunks<DT, VEC>(row, V, P, first, stride, n, lane, [&](const ChunkRegs<DT>& r, long) {
+    float v[kStatVecs][8];
+    chunk_values<DT>(r, v);
+    lane_softmax_update(st, v, c2);
+  });
+  wave_softmax_merge(st, c2, m_out, z_out);
+}
+
+// Single-chunk summary (one wave, one 2048-element chunk), used where a chunk must be
+// summarized exactly as a later rescan recomputes it.
+template <int DT, bool VEC>
+__device__ __forceinline__ void chunk_summary(const void* row, long V, long chunk, int lane,
+                                              float c2, float& m_out, float& z_out) {
+  wave_row_summary<DT, VEC>(row, V, chunk + 1, chunk, 1, 1, lane, c2, m_out, z_out);
 }
 
 // 2^(l * c2 - r): the same expression chunk_summary sums, for recomputation of single
@@ -219,39 +368,62 @@ __device__ __forceinline__ float scaled_exp(float l, float c2, float r) {
 }
 
 // ------------------------------------------------------------------ cross-block traffic
-// Values that other blocks read within the same launch (chunk summaries, chunk masses)
-// are written and read with device-scope relaxed atomics: on this target those are
-// write-through stores and L2-bypassing loads, so they are coherent across the XCDs'
-// separate L2 caches without any cache-wide writeback or invalidate.  A block publishes
-// them by (1) storing with publish_*, (2) waiting for its own stores to complete
-// (__syncthreads, or vmem_wait() in a single thread), and (3) counting its arrival with a
-// relaxed device-scope add.  The block that sees the final count reads with fetch_*.
-__device__ __forceinline__ void publish_f2(float2* p, float2 v) {
-  const unsigned long long bits =
-      (static_cast<unsigned long long>(__float_as_uint(v.y)) << 32) | __float_as_uint(v.x);
-  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), bits, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 fetch_f2(const float2* p) {
-  const unsigned long long bits = __hip_atomic_load(
-      reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float(static_cast<unsigned>(bits)),
-                     __uint_as_float(static_cast<unsigned>(bits >> 32)));
-}
-__device__ __forceinline__ void publish_d(double* p, double v) {
-  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
-                     static_cast<unsigned long long>(__double_as_longlong(v)), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ double fetch_d(const double* p) {
-  return __longlong_as_double(static_cast<long long>(__hip_atomic_load(
-      reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
-}
+// Values that other blocks read within the same launch (chunk summaries, chunk masses,
+// decisions) travel as single 64-bit words written and read with device-scope relaxed
+// atomics (write-through stores, L2-bypassing loads: coherent across the XCDs' separate
+// L2 caches without cache-wide writeback or invalidate).  Every such word is encoded so
+// that a published value is never all-zero bits, and every call returns the words it
+// used to zero.  A reader that has learned (through an arrival count) that a word was
+// published therefore re-reads it until it is non-zero: a store that is still on its way
+// is never mistaken for data.  The re-reading is bounded; a word that never arrives
+// reads as zero, which every consumer treats as invalid data.
+constexpr unsigned kSpinLimit = 1u << 22;
+
 __device__ __forceinline__ void publish_u64(unsigned long long* p, unsigned long long v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ unsigned long long fetch_u64(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Re-read until the word is published (non-zero), within the spin bound.
+__device__ __forceinline__ unsigned long long await_u64(const unsigned long long* p) {
+  unsigned long long v = fetch_u64(p);
+  for (unsigned spins = 0; v == 0ull && spins < kSpinLimit; ++spins) {
+    __builtin_amdgcn_s_sleep(1);
+    v = fetch_u64(p);
+  }
+  return v;
+}
+__device__ __forceinline__ void clear_u64(unsigned long long* p) { publish_u64(p, 0ull); }
+
+// (raw max m, sum Z) of a chunk range: never all-zero bits, because an empty range is
+// (-inf, 0) and a non-empty one has Z >= 1 (its maximum contributes 2^0) or NaN.
+__device__ __forceinline__ void publish_f2(float2* p, float2 v) {
+  publish_u64(reinterpret_cast<unsigned long long*>(p),
+              (static_cast<unsigned long long>(__float_as_uint(v.y)) << 32) | __float_as_uint(v.x));
+}
+__device__ __forceinline__ float2 await_f2(const float2* p) {
+  const unsigned long long bits = await_u64(reinterpret_cast<const unsigned long long*>(p));
+  return make_float2(__uint_as_float(static_cast<unsigned>(bits)),
+                     __uint_as_float(static_cast<unsigned>(bits >> 32)));
+}
+__device__ __forceinline__ void clear_f2(float2* p) { clear_u64(reinterpret_cast<unsigned long long*>(p)); }
+
+// A non-negative mass (or NaN) is stored negated, so that 0.0 travels as -0.0.
+__device__ __forceinline__ void publish_mass(double* p, double v) {
+  publish_u64(reinterpret_cast<unsigned long long*>(p),
+              static_cast<unsigned long long>(__double_as_longlong(-v)));
+}
+__device__ __forceinline__ double await_mass(const double* p) {
+  return -__longlong_as_double(static_cast<long long>(await_u64(reinterpret_cast<const unsigned long long*>(p))));
+}
+__device__ __forceinline__ void clear_mass(double* p) { clear_u64(reinterpret_cast<unsigned long long*>(p)); }
+
+// Write-through store of an output word that a later block of the same launch may
+// overwrite (after synchronizing on a flag): the later plain store then wins.
+__device__ __forceinline__ void store_wt(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait until this thread's outstanding memory operations have completed (a

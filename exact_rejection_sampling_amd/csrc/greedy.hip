@@ -20,63 +20,68 @@ namespace sv {
 
 namespace {
 
+// Argmax summary of the chunks a wave visits (see stream_chunks): per lane the maximum
+// and the lowest position holding it (positions rise with the chunk and, inside a chunk,
+// with j and e), then the wave's maximum and the lowest position among its lanes.
 template <int DT, bool VEC>
-__device__ __forceinline__ GreedyPart greedy_chunk(const void* row, long V, long chunk, int lane) {
-  float v[kStatVecs][8];
-  const long base = chunk * kWaveChunk;
-#pragma unroll
-  for (int j = 0; j < kStatVecs; ++j)
-    load8<DT, VEC, true>(row, base + static_cast<long>(j * kWave + lane) * kVec, V, v[j], -INFINITY);
+__device__ __forceinline__ GreedyPart wave_row_argmax(const void* row, long V, long P, long first,
+                                                      long stride, int n, int lane) {
   float m = -INFINITY;
-  bool nan = false;
-#pragma unroll
-  for (int j = 0; j < kStatVecs; ++j)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      m = fmaxf(m, v[j][k]);
-      nan |= (v[j][k] != v[j][k]);
-    }
-  const float M = wave_max(m);
-  // lowest position in this lane holding M: lane vectors ascend with j, elements with k
   int idx = 0x7fffffff;
+  bool nan = false;
+  stream_chunks<DT, VEC>(row, V, P, first, stride, n, lane, [&](const ChunkRegs<DT>& r, long c) {
+    float v[kStatVecs][8];
+    chunk_values<DT>(r, v);
+    const long base = c * kWaveChunk;
 #pragma unroll
-  for (int j = kStatVecs - 1; j >= 0; --j)
+    for (int j = 0; j < kStatVecs; ++j)
 #pragma unroll
-    for (int k = 7; k >= 0; --k)
-      if (v[j][k] == M) idx = static_cast<int>(base + static_cast<long>(j * kWave + lane) * kVec + k);
+      for (int e = 0; e < 8; ++e) {
+        const float x = v[j][e];
+        nan |= (x != x);
+        if (x > m) {
+          m = x;
+          idx = static_cast<int>(base + static_cast<long>(j * kWave + lane) * kVec + e);
+        }
+      }
+  });
+  const float M = wave_max(m);
   GreedyPart g;
-  g.m = wave_any(nan) ? __uint_as_float(0x7fc00000u) : M;   // NaN marks a chunk holding NaN
-  g.idx = wave_min_i(idx);
+  g.m = wave_any(nan) ? __uint_as_float(0x7fc00000u) : M;   // NaN marks a NaN-holding range
+  g.idx = wave_min_i(m == M ? idx : 0x7fffffff);
   return g;
 }
 
+// Packed summary: bits of m, and idx with its top bit flipped in the high word, so a
+// published summary is never all-zero bits (idx is non-negative).
 __device__ __forceinline__ unsigned long long pack(const GreedyPart& g) {
-  return (static_cast<unsigned long long>(static_cast<unsigned>(g.idx)) << 32) | __float_as_uint(g.m);
+  return (static_cast<unsigned long long>(static_cast<unsigned>(g.idx) ^ 0x80000000u) << 32) |
+         __float_as_uint(g.m);
 }
 __device__ __forceinline__ GreedyPart unpack(unsigned long long b) {
   GreedyPart g;
   g.m = __uint_as_float(static_cast<unsigned>(b));
-  g.idx = static_cast<int>(static_cast<unsigned>(b >> 32));
+  g.idx = static_cast<int>(static_cast<unsigned>(b >> 32) ^ 0x80000000u);
   return g;
 }
 
 __device__ void greedy_decide(const GreedyParams& p, int b) {
   __shared__ int s_arg[SPEC_MAX_GAMMA + 1];
   __shared__ int s_bad[SPEC_MAX_GAMMA + 1];
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   for (int i = wave; i < p.R; i += kWavesPerBlock) {
-    const unsigned long long* part = p.part + ((size_t)b * p.R + i) * p.P;
+    const unsigned long long* part = p.part + ((size_t)b * p.R + i) * p.PP;
     float m = -INFINITY;
     int nan = 0;
-    for (int j = lane; j < p.P; j += kWave) {
-      const GreedyPart g = unpack(fetch_u64(part + j));
+    for (int j = lane; j < p.PP; j += kWave) {
+      const GreedyPart g = unpack(await_u64(part + j));
       m = fmaxf(m, g.m);
       nan |= (g.m != g.m);
     }
     const float M = wave_max(m);
     int idx = 0x7fffffff;
-    for (int j = lane; j < p.P; j += kWave) {
-      const GreedyPart g = unpack(fetch_u64(part + j));
+    for (int j = lane; j < p.PP; j += kWave) {
+      const GreedyPart g = unpack(await_u64(part + j));
       if (g.m == M) idx = min(idx, g.idx);
     }
     idx = wave_min_i(idx);
@@ -88,8 +93,8 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
   }
   __syncthreads();
   {
-    unsigned long long* part = p.part + (size_t)b * p.R * p.P;     // consumed: back to zero
-    for (int j = threadIdx.x; j < p.R * p.P; j += kBlock) part[j] = 0ull;
+    unsigned long long* part = p.part + (size_t)b * p.R * p.PP;     // consumed: back to zero
+    for (int j = threadIdx.x; j < p.R * p.PP; j += kBlock) clear_u64(part + j);
   }
   if (wave != 0) return;
   const int G = p.G;
@@ -121,20 +126,21 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void greedy_kernel(GreedyParams p) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const size_t rowid = blockIdx.x / p.WG1;
-  const int slice = blockIdx.x % p.WG1;
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const size_t rowid = blockIdx.x / p.SL;
+  const int slice = blockIdx.x % p.SL;
   const int b = (int)(rowid / p.R);
-  const int chunk = slice * kWavesPerBlock + wave;
-  if (chunk < p.P) {
-    const GreedyPart g = greedy_chunk<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, chunk, lane);
-    if (lane == 0) publish_u64(p.part + rowid * p.P + chunk, pack(g));
+  {
+    const long first = (long)slice * kWavesPerBlock * p.CPW + wave;
+    const GreedyPart g = wave_row_argmax<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, p.P, first,
+                                                  kWavesPerBlock, p.CPW, lane);
+    if (lane == 0) publish_u64(p.part + rowid * p.PP + slice * kWavesPerBlock + wave, pack(g));
   }
   __syncthreads();   // every wave's summary store has completed
   __shared__ int s_last;
   if (threadIdx.x == 0) {
     const unsigned prev = arrive(&p.counters[(size_t)b * kCounterSlots + 0]);
-    s_last = (prev == (unsigned)(p.R * p.WG1 - 1));
+    s_last = (prev == (unsigned)(p.R * p.SL - 1));
   }
   __syncthreads();
   if (!s_last) return;
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(GreedyParams p) {
 
 template <int DT, bool VEC>
 hipError_t launch_typed(const GreedyParams& p, hipStream_t s) {
-  const unsigned g = (unsigned)((size_t)p.B * p.R * p.WG1);
+  const unsigned g = (unsigned)((size_t)p.B * p.R * p.SL);
   greedy_kernel<DT, VEC><<<dim3(g), dim3(kBlock), 0, s>>>(p);
   return hipGetLastError();
 }

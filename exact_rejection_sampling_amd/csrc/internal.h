@@ -26,13 +26,18 @@ struct ChainParams {
   int32_t* req_status;       // [B]
   float* stats;              // [B, R, 4] or null
   // workspace
-  float2* part;              // [B*R*P] wave-chunk summaries (raw max, Z)
-  unsigned* counters;        // per-request slots: [b*4 + 0] statistics, [b*4 + 1] terminal
+  unsigned* global;          // [0] next work ticket, [1] blocks that have left
+  float2* part;              // [B*R*PP] wave summaries (raw max, Z)
+  unsigned* counters;        // per-request slots: [b*4 + 0] statistics arrivals,
+                             // [b*4 + 1] terminal arrivals, [b*4 + 2] decision ready
   ChainDecision* dec;        // [B]
+  unsigned long long* gath;  // [B*G*3] draft token, its logit, its draft probability
   double* tmass;             // [B*S2] terminal chunk masses
   int B, G, R, V;
   int P;                     // wave chunks per row = ceil(V / 2048)
-  int WG1;                   // blocks per row in the statistics pass = ceil(P / 4)
+  int CPW;                   // wave chunks each wave streams per slice
+  int SL;                    // statistics slices (blocks) per row = ceil(P / (4 * CPW))
+  int PP;                    // summaries per row = 4 * SL (one per wave)
   int S2;                    // terminal chunks per row = ceil(V / kTermChunk)
   int q_dtype;
   float c2;                  // fp32(log2(e) / T)
@@ -54,10 +59,39 @@ struct GreedyParams {
   int32_t* accepted_len;
   int32_t* out_tokens;
   int32_t* req_status;
-  unsigned long long* part;  // [B*R*P] packed GreedyPart
+  unsigned long long* part;  // [B*R*PP] packed GreedyPart
   unsigned* counters;        // per-request slots: [b*4 + 0] arrivals
-  int B, G, R, V, P, WG1;
+  int B, G, R, V, P, CPW, SL, PP;
 };
+
+#ifdef SPEC_FORCE_CPW
+constexpr int kForceCPW = SPEC_FORCE_CPW;
+#else
+constexpr int kForceCPW = 0;
+#endif
+
+// Slicing of rows among blocks for the streaming passes: a block's 4 waves each stream
+// CPW wave chunks (interleaved, 4 KB apart for bf16), so a block covers 4*CPW chunks.
+// CPW grows with the total amount of work so that the grid stays near kTargetBlocks.
+#ifndef SPEC_TARGET_BLOCKS
+#define SPEC_TARGET_BLOCKS 2048
+#endif
+constexpr long kTargetBlocks = SPEC_TARGET_BLOCKS;
+constexpr int kMaxCPW = 16;
+struct Slicing { int P, CPW, SL, PP; };
+inline Slicing slicing(long rows, long V, long target_blocks = kTargetBlocks) {
+  Slicing s;
+  s.P = static_cast<int>((V + 2047) / 2048);
+  const long total = rows * s.P;
+  long cpw = (total + 4 * target_blocks - 1) / (4 * target_blocks);
+  if (cpw < 1) cpw = 1;
+  if (cpw > kMaxCPW) cpw = kMaxCPW;
+  if (kForceCPW > 0) cpw = kForceCPW;
+  s.CPW = static_cast<int>(cpw);
+  s.SL = static_cast<int>((s.P + 4 * cpw - 1) / (4 * cpw));
+  s.PP = 4 * s.SL;
+  return s;
+}
 
 struct TreeParams {
   const void* logits;        // [B, N, V]
@@ -68,7 +102,8 @@ struct TreeParams {
   int32_t* out_tokens;
   int32_t* out_nodes;
   int32_t* req_status;
-  float2* part;              // [B*P] summaries of the row being walked
+  float2* part;              // [B*P] root-row summaries, published across blocks
+  float2* part_deep;         // [B*P] summaries of deeper rows (walking block only)
   unsigned* counters;        // per-request slots: [b*4 + 0] arrivals
   int B, N, V, P, WG1;
   float c2;
@@ -90,14 +125,19 @@ inline unsigned* request_counters(void* ws) {
 // slot s of request b: request_counters(ws)[b * kCounterSlots + s]
 
 struct ChainLayout {
-  size_t part, dec, tmass, total;
+  size_t part, dec, gath, tmass, total;
 };
+// The chain's statistics pass uses finer slices than the other streaming passes: its
+// terminal items fill the statistics tail, which shrinks as the slices do.
+constexpr long kChainTargetBlocks = 4 * kTargetBlocks;
 inline ChainLayout chain_layout(long B, long G, long V) {
-  const long R = G + 1, P = (V + 2047) / 2048, S2 = (V + kTermChunk - 1) / kTermChunk;
+  const long R = G + 1, S2 = (V + kTermChunk - 1) / kTermChunk;
+  const long PP = slicing(B * R, V, kChainTargetBlocks).PP;
   ChainLayout L;
   size_t o = counter_bytes(B);
-  L.part = o;   o = align256(o + sizeof(float2) * B * R * P);
+  L.part = o;   o = align256(o + sizeof(float2) * B * R * PP);
   L.dec = o;    o = align256(o + sizeof(ChainDecision) * B);
+  L.gath = o;   o = align256(o + sizeof(unsigned long long) * 3 * B * G);
   L.tmass = o;  o = align256(o + sizeof(double) * B * S2);
   L.total = o;
   return L;
@@ -105,24 +145,42 @@ inline ChainLayout chain_layout(long B, long G, long V) {
 
 struct GreedyLayout { size_t part, total; };
 inline GreedyLayout greedy_layout(long B, long G, long V) {
-  const long R = G + 1, P = (V + 2047) / 2048;
+  const long R = G + 1;
+  const long PP = slicing(B * R, V).PP;
   GreedyLayout L;
   size_t o = counter_bytes(B);
-  L.part = o;  o = align256(o + sizeof(unsigned long long) * B * R * P);
+  L.part = o;  o = align256(o + sizeof(unsigned long long) * B * R * PP);
   L.total = o;
   return L;
 }
 
-struct TreeLayout { size_t part, total; };
+struct TreeLayout { size_t part, part_deep, total; };
 inline TreeLayout tree_layout(long B, long N, long V) {
   (void)N;
   const long P = (V + 2047) / 2048;
   TreeLayout L;
   size_t o = counter_bytes(B);
-  L.part = o;  o = align256(o + sizeof(float2) * B * P);
+  L.part = o;       o = align256(o + sizeof(float2) * B * P);
+  L.part_deep = o;  o = align256(o + sizeof(float2) * B * P);
   L.total = o;
   return L;
 }
+
+// Grid sizes of the launches.  A dispatch counts work-items in 32 bits, so a launch
+// holds at most floor((2^32 - 1) / kBlock) blocks; grid_fits says whether it does.
+inline unsigned long long chain_blocks(long B, long G, long V) {
+  const long R = G + 1, S2 = (V + kTermChunk - 1) / kTermChunk;
+  return (unsigned long long)B * ((unsigned long long)R * slicing(B * R, V, kChainTargetBlocks).SL + S2);
+}
+inline unsigned long long greedy_blocks(long B, long G, long V) {
+  const long R = G + 1;
+  return (unsigned long long)B * R * slicing(B * R, V).SL;
+}
+inline unsigned long long tree_blocks(long B, long V) {
+  const long P = (V + 2047) / 2048;
+  return (unsigned long long)B * ((P + kWavesPerBlock - 1) / kWavesPerBlock);
+}
+inline bool grid_fits(unsigned long long blocks) { return blocks <= 0xffffffffull / kBlock; }
 
 // Launchers (return hipGetLastError() after enqueueing).
 hipError_t launch_chain(const ChainParams& p, int logit_dtype, bool vec, hipStream_t s);

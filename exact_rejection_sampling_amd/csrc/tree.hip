@@ -36,10 +36,19 @@ __device__ void tree_fail(const TreeParams& p, int b, int code) {
   }
 }
 
+// Chunk summary c of the row being sampled.  PUBLISHED: written by other blocks (read
+// with bounded re-reads); otherwise written by this block itself (plain loads after a
+// barrier).
+template <int DT, bool VEC, bool PUBLISHED>
+__device__ __forceinline__ float2 summary(const float2* part, int c) {
+  if constexpr (PUBLISHED) return await_f2(part + c);
+  else return part[c];
+}
+
 // Block-wide: sample one token from softmax(row / T) given the row's chunk summaries.
-// Returns the token, or -1 (row not finite) / -2 (bad uniform) through *status.
-template <int DT, bool VEC>
-__device__ int sample_row(const TreeParams& p, int b, const void* row, float uv, int* status) {
+// Returns the token; a non-finite row or a bad uniform is reported through *status.
+template <int DT, bool VEC, bool PUBLISHED>
+__device__ int sample_row(const TreeParams& p, const float2* part, const void* row, float uv, int* status) {
   __shared__ double s_scan[kWavesPerBlock];
   __shared__ float s_r;
   __shared__ double s_z;
@@ -47,14 +56,13 @@ __device__ int sample_row(const TreeParams& p, int b, const void* row, float uv,
   __shared__ double s_before;
   __shared__ double s_total;
   __shared__ int s_last_pos;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const float2* part = p.part + (size_t)b * p.P;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   const float c2 = p.c2;
 
   // reference exponent: fp32(max raw logit * c2), identical to the chunks' own r_j
   if (wave == 0) {
     float m = -INFINITY;
-    for (int j = lane; j < p.P; j += kWave) m = fmaxf(m, fetch_f2(part + j).x);
+    for (int j = lane; j < p.P; j += kWave) m = fmaxf(m, summary<DT, VEC, PUBLISHED>(part, j).x);
     m = wave_max(m);
     if (lane == 0) s_r = m * c2;
   }
@@ -66,14 +74,14 @@ __device__ int sample_row(const TreeParams& p, int b, const void* row, float uv,
   const int c_lo = min(tid * per, p.P), c_hi = min(c_lo + per, p.P);
   double mine = 0.0;
   for (int c = c_lo; c < c_hi; ++c) {
-    const float2 s = fetch_f2(part + c);
+    const float2 s = summary<DT, VEC, PUBLISHED>(part, c);
     mine += (double)s.y * exp2((double)(s.x * c2) - (double)R);
   }
   double tot;
   const double excl = block_excl_scan_d(mine, s_scan, &tot);
   double run_end = excl;
   for (int c = c_lo; c < c_hi; ++c) {
-    const float2 s = fetch_f2(part + c);
+    const float2 s = summary<DT, VEC, PUBLISHED>(part, c);
     run_end += (double)s.y * exp2((double)(s.x * c2) - (double)R);
   }
   if (c_lo < c_hi && c_hi == p.P) s_total = run_end;
@@ -86,7 +94,7 @@ __device__ int sample_row(const TreeParams& p, int b, const void* row, float uv,
   {
     double run = excl;
     for (int c = c_lo; c < c_hi; ++c) {
-      const float2 s = fetch_f2(part + c);
+      const float2 s = summary<DT, VEC, PUBLISHED>(part, c);
       const double nxt = run + (double)s.y * exp2((double)(s.x * c2) - (double)R);
       if (nxt > t) { atomicMin(&s_pick, c); break; }
       run = nxt;
@@ -100,7 +108,7 @@ __device__ int sample_row(const TreeParams& p, int b, const void* row, float uv,
   if (cstar >= c_lo && cstar < c_hi) {
     double run = excl;
     for (int c = c_lo; c < cstar; ++c) {
-      const float2 s = fetch_f2(part + c);
+      const float2 s = summary<DT, VEC, PUBLISHED>(part, c);
       run += (double)s.y * exp2((double)(s.x * c2) - (double)R);
     }
     s_before = run;
@@ -110,7 +118,7 @@ __device__ int sample_row(const TreeParams& p, int b, const void* row, float uv,
   __syncthreads();
 
   // rescan chunk cstar (one slab) in the chunk's own units 2^(l c2 - r_c)
-  const float rc = fetch_f2(part + cstar).x * c2;
+  const float rc = summary<DT, VEC, PUBLISHED>(part, cstar).x * c2;
   const double rem = (t - s_before) * exp2((double)R - (double)rc);
   const long e0 = (long)cstar * kWaveChunk + (long)tid * kVec;
   float v[8];
@@ -140,14 +148,15 @@ __device__ int sample_row(const TreeParams& p, int b, const void* row, float uv,
   return y;
 }
 
-// Block-wide: summaries of one full row into p.part[b], by this block alone.
+// Block-wide: summaries of one full row into `part` (this request's private region for
+// rows below the root), written and read by this block alone.
 template <int DT, bool VEC>
-__device__ void summarize_row(const TreeParams& p, int b, const void* row) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+__device__ void summarize_row(const TreeParams& p, float2* part, const void* row) {
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   for (int c = wave; c < p.P; c += kWavesPerBlock) {
     float m, z;
     chunk_summary<DT, VEC>(row, p.V, c, lane, p.c2, m, z);
-    if (lane == 0) publish_f2(p.part + (size_t)b * p.P + c, make_float2(m, z));
+    if (lane == 0) part[c] = make_float2(m, z);
   }
   __syncthreads();
 }
@@ -171,10 +180,13 @@ __device__ void tree_walk(const TreeParams& p, int b) {
   if (s_bad) { tree_fail(p, b, SPEC_REQ_BADTREE); return; }
 
   int v = 0, depth = 0;
+  float2* deep = p.part_deep + (size_t)b * p.P;
   while (true) {
     const void* row = row_ptr<DT>(p.logits, (size_t)b * N + v, p.V);
     int status = 0;
-    const int y = sample_row<DT, VEC>(p, b, row, p.u[(size_t)b * N + v], &status);
+    const float uv = p.u[(size_t)b * N + v];
+    const int y = v == 0 ? sample_row<DT, VEC, true>(p, p.part + (size_t)b * p.P, row, uv, &status)
+                         : sample_row<DT, VEC, false>(p, deep, row, uv, &status);
     if (status != 0) { tree_fail(p, b, status); return; }
     if (tid == 0) s_child = kNoPick;
     __syncthreads();
@@ -205,13 +217,13 @@ __device__ void tree_walk(const TreeParams& p, int b) {
     }
     ++depth;
     v = child;
-    summarize_row<DT, VEC>(p, b, row_ptr<DT>(p.logits, (size_t)b * N + v, p.V));
+    summarize_row<DT, VEC>(p, deep, row_ptr<DT>(p.logits, (size_t)b * N + v, p.V));
   }
 }
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   const int b = blockIdx.x / p.WG1;
   const int slice = blockIdx.x % p.WG1;
   const int chunk = slice * kWavesPerBlock + wave;
@@ -230,7 +242,10 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
   if (!s_last) return;
   tree_walk<DT, VEC>(p, b);
   __syncthreads();
-  for (int j = threadIdx.x; j < p.P; j += kBlock) p.part[(size_t)b * p.P + j] = make_float2(0.0f, 0.0f);
+  for (int j = threadIdx.x; j < p.P; j += kBlock) {
+    clear_f2(p.part + (size_t)b * p.P + j);
+    p.part_deep[(size_t)b * p.P + j] = make_float2(0.0f, 0.0f);
+  }
   if (threadIdx.x == 0) reset_counter(&p.counters[(size_t)b * kCounterSlots + 0]);
 }
 

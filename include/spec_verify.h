@@ -30,7 +30,12 @@
  * Host status.  The return value reports only what the host can check before
  *           launching: null pointers, sizes outside the documented limits, a
  *           temperature outside its range, an unknown dtype, a workspace that is too
- *           small or misaligned, and a HIP launch failure.  On any non-SPEC_OK
+ *           small or misaligned, and a HIP launch failure.  Sizes are also refused
+ *           (SPEC_EINVAL, and a workspace query returns 0) when the launch would need
+ *           more than (2^32 - 1) / 256 = 16777215 blocks of 256 threads (a dispatch
+ *           counts work-items in 32 bits).  A launch has at least one block per row
+ *           (or tree request), so this happens once the rows near 2^24, or once the
+ *           logits near 2^40 elements.  On any non-SPEC_OK
  *           return nothing has been enqueued (except SPEC_EHIP, where a launch failed).
  * Request status.  Data errors are reported per request in req_status[b] (SPEC_REQ_*).
  *           A request with a non-zero status emits nothing: accepted_len[b] = -1 and
@@ -88,8 +93,10 @@ enum {
   SPEC_REQ_RESIDUAL_EMPTY = 5,  /* terminal mass W is not positive and finite, or the q row
                                    read at the rejected position has a negative or
                                    non-finite entry ([Tiny] residual invariant) */
-  SPEC_REQ_BADTREE = 6          /* parents[0] != -1, a parents[v] outside [0, v), or a
+  SPEC_REQ_BADTREE = 6,         /* parents[0] != -1, a parents[v] outside [0, v), or a
                                    non-root node token outside [0, V) ([M7.7] §0x0F) */
+  SPEC_REQ_INTERNAL = 7         /* an internal wait between blocks hit its bound (not
+                                   expected; the request's outputs are not valid) */
 };
 
 /* ------------------------------------------------------------------ chain ---

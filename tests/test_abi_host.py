@@ -46,8 +46,11 @@ def test_abi_version_and_strings():
 def test_workspace_sizes():
     lib = sv.load_library()
     n = lib.spec_chain_workspace_bytes(64, 5, 128256)
-    # summaries (8 B per 2048-element chunk per row) dominate: 64*6*63*8 B = 193536 B
-    assert 193536 <= n < 193536 + 64 * 64 * 16 + 8 * 256
+    # one 8-byte summary per wave (at most one per 2048-element chunk, the wave count
+    # rounded up to whole 4-wave blocks) per row, plus per-request decisions, gathered
+    # draft values (3 words per draft) and 4096-element chunk masses: well under a megabyte
+    rows, P, S2 = 64 * 6, (128256 + 2047) // 2048, (128256 + 4095) // 4096
+    assert rows * 4 * 8 <= n < rows * (P + 3) * 8 + 64 * (16 + 3 * 5 * 8 + S2 * 8) + 4096
     assert lib.spec_chain_workspace_bytes(0, 5, 128256) == 256   # the counter header only
     assert lib.spec_chain_workspace_bytes(1, 64, 10) == 0      # gamma above the limit
     assert lib.spec_chain_workspace_bytes(1, 5, 0) == 0
@@ -117,3 +120,15 @@ def test_product_path_does_not_import_the_oracle():
                 assert not re.search(r"^\s*(import|from)\s+oracle", src, flags=re.M), path
             elif f.endswith((".hip", ".h", ".cpp")):
                 assert "oracle" not in open(path).read().lower(), path
+
+
+def test_grid_limit():
+    # a dispatch counts work-items in 32 bits: at most 16777215 blocks of 256 threads
+    lib = sv.load_library()
+    big_rows = (1 << 22, 7, 16)        # 2^25 rows, one block each at least
+    assert lib.spec_chain_workspace_bytes(*big_rows) == 0
+    assert lib.spec_greedy_workspace_bytes(*big_rows) == 0
+    assert _chain(lib, B=1 << 22, gamma=7, V=16) == EINVAL
+    assert lib.spec_chain_workspace_bytes(1 << 20, 7, 16) > 0      # 2^23 rows fit
+    assert lib.spec_tree_workspace_bytes(1 << 22, 4, 1 << 20) == 0  # 2^22 * 128 blocks
+    assert lib.spec_tree_workspace_bytes(1 << 16, 4, 1 << 20) > 0
