@@ -168,7 +168,7 @@ spec_status spec_verify_greedy(const void* target_logits, int logit_dtype,
  *           if a child c of v (parents[c] == v) has node_tokens[c] == y (the lowest
  *           such c if siblings repeat a token): accept c, v = c;  else stop.
  *   emitted tokens: tokens of the accepted nodes, then the last draw y.
- * Row v of node_logits scores the children of node v ([M7.7] §0x02: a node's row
+ * Row v of node_logits scores the children of node v ([M7.7] §0x07E: a node's row
  * predicts its children, never itself).  Only rows on the walked path are read.
  *
  * node_logits   [B, N, V]; node_tokens [B, N] int32 (node 0's entry is ignored);

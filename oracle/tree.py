@@ -5,7 +5,7 @@ Test infrastructure only (see the package docstring).
 Inputs of one request: the candidate tree as a parent-index array (node 0 is the
 frontier root, parents[0] = -1, 0 <= parents[v] < v for v > 0 -- [M7.7] §0x0F
 "Implementation Assertions" requires -1 <= parent < row), one token per node, and
-one logits row per node.  Row v scores the children of node v: [M7.7] §0x02 (the
+one logits row per node.  Row v scores the children of node v: [M7.7] §0x07E (the
 distribution that scores a candidate comes from its parent's row; a root-level
 candidate is scored by the frontier row, which here is node 0's row).
 

@@ -122,7 +122,7 @@ def test_pages_worked_examples_on_gpu():
 
 
 def test_error_statuses():
-    B, G, V = 12, 3, 4100
+    B, G, V = 14, 3, 4100
     x = synth.make_chain(B, G, V, seed=9, logit_dtype="f32", sigma=2.0, noise=0.3, temperature=1.0)
     L = x.logits
     # 0: NaN in reached row 0
@@ -160,11 +160,17 @@ def test_error_statuses():
     L[10, 0, 5] = -np.inf
     x.q[10, 0, 200] = -0.25
     # 11: untouched
+    # 12: q(x_0) = 0 and a bad uniform at the same position: q is checked first
+    x.q[12, 0, x.tokens[12, 0]] = 0.0
+    x.u[12, 0] = 1.5
+    # 13: a bad uniform at position 0 wins over q(x_1) = 0 at position 1
+    x.u[13, 0] = 2.0
+    x.q[13, 1, x.tokens[13, 1]] = 0.0
     say("chain error statuses")
     got = run_chain(x)
     exp = oracle_chain(x)
     compare_chain(got, exp)
-    assert exp["status"].tolist() == [1, 1, 1, 2, 2, 4, 3, 3, 0, 5, 5, 0]
+    assert exp["status"].tolist() == [1, 1, 1, 2, 2, 4, 3, 3, 0, 5, 5, 0, 4, 3]
     assert (got["out_tokens"][got["req_status"] != 0] == -1).all()
     assert (got["accepted_len"][got["req_status"] != 0] == -1).all()
 

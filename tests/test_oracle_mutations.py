@@ -1,0 +1,117 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of `oracle/`, in a temporary directory, and runs
+the CPU pin suites (worked examples, closed forms, exact enumeration, stored regression
+outputs) against the copy in a fresh interpreter.  The case passes when the suite
+fails.  The real oracle is never modified.  The mistakes are the kind a reader of the
+pages could plausibly make: a flipped inequality, a dropped term, a transposed operand,
+an off-by-one row, a wrong uniform, a wrong tie rule.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_laws.py", "test_oracle_regression.py"]
+
+# (file under oracle/, text as it stands, the planted mistake)
+MUTANTS = {
+    # chain: [M7.1] §0x03A-§0x03H, [M16] "The Math: Speculative Sampling"
+    "accept_u_le_a": ("chain.py", "if not (u[i] < a):", "if not (u[i] <= a):"),
+    "ratio_inverted": ("chain.py", "a = min(1.0, px / qx)", "a = min(1.0, qx / max(px, 1e-300))"),
+    "no_clip_at_one": ("chain.py", "a = min(1.0, px / qx)", "a = px / qx if px < qx else 0.999"),
+    "residual_q_minus_p": ("chain.py", "w = np.maximum(p - qrow, 0.0)", "w = np.maximum(qrow - p, 0.0)"),
+    "residual_dropped": ("chain.py", "w = np.maximum(p - qrow, 0.0)", "w = p"),
+    "residual_unclipped": ("chain.py", "w = np.maximum(p - qrow, 0.0)", "w = np.abs(p - qrow)"),
+    "residual_next_row": ("chain.py", "p, _, _ = target_probs(L[A], temperature, check_backends=False)",
+                          "p, _, _ = target_probs(L[min(A + 1, gamma)], temperature, check_backends=False)"),
+    "residual_from_draft_row_0": ("chain.py", "qrow = Q[A]", "qrow = Q[0]"),
+    "bonus_from_row_0": ("chain.py", "p, m, Z = target_probs(L[gamma], temperature)",
+                         "p, m, Z = target_probs(L[0], temperature)"),
+    "no_stop_at_first_rejection": ("chain.py", "            A = i\n            break\n", "            A = i\n"),
+    "terminal_uses_rejecting_uniform": ("chain.py", "k, W, lo, hi = inverse_cdf(w, float(u[gamma]))",
+                                        "k, W, lo, hi = inverse_cdf(w, float(u[min(A, gamma)]))"),
+    "correction_not_emitted": ("chain.py", "res.tokens = [int(t) for t in x[:A]] + [k]",
+                               "res.tokens = [int(t) for t in x[:A]] + ([k] if A == gamma else [])"),
+    "uniform_checked_before_q": ("chain.py",
+                                 "        if not (np.isfinite(qx) and qx > 0.0):\n            return fail(QZERO)\n"
+                                 "        if not (0.0 <= u[i] < 1.0):\n            return fail(BADUNIFORM)\n",
+                                 "        if not (0.0 <= u[i] < 1.0):\n            return fail(BADUNIFORM)\n"
+                                 "        if not (np.isfinite(qx) and qx > 0.0):\n            return fail(QZERO)\n"),
+    "cdf_left_side": ("chain.py", 'k = int(np.searchsorted(c, u * W, side="right"))',
+                      'k = int(np.searchsorted(c, u * W, side="left"))'),
+    # numerics: decoding, temperature, softmax ([M7.1] §0x04F, §0x04J)
+    "temperature_multiplies": ("numerics.py", "s = logits_row / T", "s = logits_row * T"),
+    "softmax_drops_a_term": ("numerics.py", "    Z = float(np.sum(e))\n    return e / Z, m, Z",
+                             "    Z = float(np.sum(e[1:]))\n    return e / Z, m, Z"),
+    "bf16_wrong_shift": ("numerics.py", "* np.uint32(65536)", "* np.uint32(32768)"),
+    "posinf_row_valid": ("numerics.py", "if np.isnan(row).any() or np.isposinf(row).any():",
+                         "if np.isnan(row).any():"),
+    # greedy ([M7.1] §0x02D, [Tiny] "Normative greedy pseudocode")
+    "greedy_last_tie": ("greedy.py", "return int(np.flatnonzero(row == row.max())[0])",
+                        "return int(np.flatnonzero(row == row.max())[-1])"),
+    "greedy_no_correction": ("greedy.py", "return OK, i, [int(v) for v in x[:i]] + [t]",
+                             "return OK, i, [int(v) for v in x[:i]]"),
+    "greedy_bonus_row_off_by_one": ("greedy.py", "[first_argmax(L[gamma])]", "[first_argmax(L[gamma - 1])]"),
+    # tree ([M7.7] §0x07E, §0x09, §0x0F, §0x0AA)
+    "tree_any_node_with_token": ("tree.py", "if int(parents[c]) == v and int(node_tokens[c]) == y:",
+                                 "if int(node_tokens[c]) == y:"),
+    "tree_root_uniform_everywhere": ("tree.py", "uv = float(u[v])", "uv = float(u[0])"),
+    "tree_row_of_child": ("tree.py", "p, _, _ = target_probs(L[v], temperature)",
+                          "p, _, _ = target_probs(L[min(v + 1, N - 1)], temperature)"),
+    "tree_highest_index_child": ("tree.py", "for c in range(v + 1, N):", "for c in range(N - 1, v, -1):"),
+    "tree_accepts_self_parent": ("tree.py", "if not (0 <= pv < v):", "if not (0 <= pv <= v):"),
+    "tree_expectation_uses_child_row": ("tree.py",
+                                        "f[v] = f[int(parents[v])] * probs[int(parents[v]), int(node_tokens[v])]",
+                                        "f[v] = f[int(parents[v])] * probs[v, int(node_tokens[v])]"),
+    # laws ([M7.1] §0x05A-§0x05D, [Atlas] mechanism)
+    "expected_tokens_off_by_one": ("laws.py", "return (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)",
+                                   "return (1.0 - alpha ** gamma) / (1.0 - alpha)"),
+    "tv_without_half": ("laws.py", "return 0.5 * float(np.sum(np.abs(np.asarray(p) - np.asarray(q))))",
+                        "return float(np.sum(np.abs(np.asarray(p) - np.asarray(q))))"),
+}
+
+
+def _copy_tree(dst):
+    shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(dst, "oracle"),
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "synth"), os.path.join(dst, "synth"),
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    tdst = os.path.join(dst, "tests")
+    os.makedirs(tdst)
+    for f in PIN_FILES + ["conftest.py", "lawcheck.py"]:
+        shutil.copy(os.path.join(ROOT, "tests", f), tdst)
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), os.path.join(tdst, "golden"),
+                    ignore=shutil.ignore_patterns("__pycache__"))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    fname, before, after = MUTANTS[name]
+    _copy_tree(str(tmp_path))
+    path = tmp_path / "oracle" / fname
+    src = path.read_text()
+    assert src.count(before) == 1, f"mutation site for {name} not found exactly once"
+    path.write_text(src.replace(before, after))
+    env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
+    proc = subprocess.run(
+        [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu",
+         *[os.path.join("tests", f) for f in PIN_FILES]],
+        cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=600)
+    assert proc.returncode != 0, f"planted mistake {name!r} passed every pin:\n{proc.stdout[-2000:]}"
+    assert "passed" in proc.stdout or "failed" in proc.stdout, proc.stdout[-2000:] + proc.stderr[-2000:]
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """The copied suite itself is green, so a failure above is the planted mistake's doing."""
+    _copy_tree(str(tmp_path))
+    proc = subprocess.run(
+        [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", "-m", "not gpu",
+         *[os.path.join("tests", f) for f in PIN_FILES]],
+        cwd=str(tmp_path), env=dict(os.environ, PYTHONDONTWRITEBYTECODE="1"),
+        capture_output=True, text=True, timeout=600)
+    assert proc.returncode == 0, proc.stdout[-3000:] + proc.stderr[-2000:]

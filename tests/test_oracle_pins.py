@@ -303,6 +303,12 @@ def test_status_order_and_reached_semantics():
     # row order: a NaN row beats a bad token at the same position
     bad = L.copy(); bad[0, 0] = np.nan
     assert verify_chain_one(bad, Q, np.array([9, 2]), np.array([0.1, 0.1, 0.1]), 1.0).status == oracle.NONFINITE
+    # at one position the draft's q(x) is checked before its uniform (the draft token and
+    # its probability come with the proposal; the uniform is drawn by the verifier)
+    assert verify_chain_one(L, Qz, np.array([1, 2]), np.array([1.5, 0.1, 0.1]), 1.0).status == oracle.QZERO
+    # and an earlier position's error wins over a later one's
+    Qz1 = Q.copy(); Qz1[1, 2] = 0.0
+    assert verify_chain_one(L, Qz1, np.array([1, 2]), np.array([2.0, 0.1, 0.1]), 1.0).status == oracle.BADUNIFORM
     # unreached rows / tokens / uniforms do not matter: reject at draft 0 (p=0 there)
     p0 = np.array([0.0, 1.0, 0.0, 0.0])
     L2 = np.stack([logits_for(p0, 1.0), np.full(V, np.nan), np.full(V, np.nan)])
