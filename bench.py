@@ -41,27 +41,46 @@ def device_copies(make, per_copy_bytes, min_copies=3):
     return [make() for _ in range(n)]
 
 
-def time_calls(fn, sets, steps, warmup, stream):
-    """Runs fn(set) over rotating sets: warmup untimed, then `steps` timed calls.
+def time_calls(calls, steps, warmup, stream):
+    """Runs prepared calls round-robin: `warmup` untimed, then `steps` timed back to back.
 
-    Returns (total seconds between the first and last event, per-call durations in ms,
-    last outputs per set)."""
+    Returns (seconds between the events that bracket the timed steps, per-launch
+    durations in ms from a second pass of `steps` calls each bracketed by its own pair of
+    events on the same stream)."""
     import torch
     for i in range(warmup):
-        fn(sets[i % len(sets)])
+        calls[i % len(calls)]()
     torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        calls[i % len(calls)]()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    span_ms = t0.elapsed_time(t1)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
-        fn(sets[i % len(sets)])
+        calls[i % len(calls)]()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    span_ms = starts[0].elapsed_time(ends[-1])
-    return span_ms / 1e3, per, wall
+    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    return span_ms / 1e3, per
+
+
+def traffic_record(name):
+    """Per-launch HBM traffic from the committed rocprofv3 counter summary for kernel `name`,
+    or None when the kernel sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return rec if h.hexdigest() == rec["sources_sha256"] else None
 
 
 def bench_chain(args, torch, sv, synth):
@@ -77,18 +96,11 @@ def bench_chain(args, torch, sv, synth):
     del lt, qt
     stream = torch.cuda.current_stream()
     ws = torch.zeros(sv.chain_workspace_bytes(B, G, V) + 512, dtype=torch.uint8, device=dev)
-    outs = [dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
-                 out_tokens=torch.empty(B, G + 1, dtype=torch.int32, device=dev),
-                 req_status=torch.empty(B, dtype=torch.int32, device=dev)) for _ in sets]
-    idx = {id(s): k for k, s in enumerate(sets)}
-
-    def call(s):
-        sv.spec_verify_chain(s[0], s[1], s[2], s[3], float(x.temperature), workspace_tensor=ws,
-                             out=outs[idx[id(s)]])
-
-    span, per, wall = time_calls(call, sets, args.steps, args.warmup, stream)
-    acc = outs[0]["accepted_len"].cpu().numpy()
-    st = outs[0]["req_status"].cpu().numpy()
+    calls = [sv.prepare_chain(s[0], s[1], s[2], s[3], float(x.temperature), workspace_tensor=ws)
+             for s in sets]
+    span, per = time_calls(calls, args.steps, args.warmup, stream)
+    acc = calls[0].out["accepted_len"].cpu().numpy()
+    st = calls[0].out["req_status"].cpu().numpy()
     assert (st == 0).all(), "unexpected request errors in the benchmark workload"
     n_rej = int((acc < G).sum())
     logit_bytes = B * (G + 1) * V * 2
@@ -96,7 +108,7 @@ def bench_chain(args, torch, sv, synth):
     small = B * G * (4 + 4 + 2) + B * (G + 1) * 4 + B * (G + 2) * 4 * 2   # gathers, u, outputs
     alg_bytes = logit_bytes + q_bytes + small
     med_ms = float(np.median(per))
-    return dict(x=x, span=span, per=per, wall=wall, n_rej=n_rej, alg_bytes=alg_bytes,
+    return dict(x=x, span=span, per=per, n_rej=n_rej, alg_bytes=alg_bytes,
                 logit_bytes=logit_bytes, q_bytes=q_bytes, med_ms=med_ms, mean_ms=float(per.mean()),
                 positions=B * (G + 1), mean_acc=float(acc.mean()), copies=len(sets))
 
@@ -111,17 +123,15 @@ def bench_greedy(args, torch, sv, synth):
     del lt
     stream = torch.cuda.current_stream()
     ws = torch.zeros(sv.greedy_workspace_bytes(B, G, V) + 512, dtype=torch.uint8, device=dev)
-    out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
-               out_tokens=torch.empty(B, G + 1, dtype=torch.int32, device=dev),
-               req_status=torch.empty(B, dtype=torch.int32, device=dev))
-    span, per, wall = time_calls(lambda s: sv.spec_verify_greedy(s[0], s[1], workspace_tensor=ws, out=out),
-                                 sets, max(20, args.steps // 4), args.warmup, stream)
+    calls = [sv.prepare_greedy(s[0], s[1], workspace_tensor=ws) for s in sets]
+    span, per = time_calls(calls, max(20, args.steps // 4), args.warmup, stream)
     alg = B * (G + 1) * V * 2 + B * G * 4 + B * (G + 2) * 8
-    med = float(np.median(per))
-    del sets
+    mean = float(per.mean())
+    del sets, calls
     return dict(workload="greedy B=256 gamma=8 V=128256 bf16", positions_per_s=B * (G + 1) * len(per) / span,
-                median_us=med * 1e3, achieved_gbs=alg / (med * 1e-3) / 1e9,
-                frac=alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, alg_bytes=alg)
+                mean_launch_us=mean * 1e3, median_launch_us=float(np.median(per)) * 1e3,
+                achieved_gbs=alg / (mean * 1e-3) / 1e9, frac=alg / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                alg_bytes=alg, traffic=traffic_record("greedy_kernel_config4"))
 
 
 def bench_tree(args, torch, sv, synth):
@@ -136,22 +146,17 @@ def bench_tree(args, torch, sv, synth):
     del lt
     stream = torch.cuda.current_stream()
     ws = torch.zeros(sv.tree_workspace_bytes(B, N, V) + 512, dtype=torch.uint8, device=dev)
-    out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
-               out_tokens=torch.empty(B, N, dtype=torch.int32, device=dev),
-               out_nodes=torch.empty(B, N, dtype=torch.int32, device=dev),
-               req_status=torch.empty(B, dtype=torch.int32, device=dev))
-    span, per, wall = time_calls(
-        lambda s: sv.spec_verify_tree(s[0], s[1], s[2], s[3], float(x.temperature), workspace_tensor=ws, out=out),
-        sets, max(20, args.steps // 4), args.warmup, stream)
-    acc = out["accepted_len"].cpu().numpy()
+    calls = [sv.prepare_tree(s[0], s[1], s[2], s[3], float(x.temperature), workspace_tensor=ws) for s in sets]
+    span, per = time_calls(calls, max(20, args.steps // 4), args.warmup, stream)
+    acc = calls[0].out["accepted_len"].cpu().numpy()
     visited = int((acc + 1).sum())
     alg = visited * V * 2 + B * N * 12
-    med = float(np.median(per))
-    del sets
+    mean = float(per.mean())
+    del sets, calls
     return dict(workload="tree B=32 N=63 V=152064 bf16 T=1", nodes_per_s=B * N * len(per) / span,
-                median_us=med * 1e3, visited_rows=visited,
-                achieved_gbs_visited=alg / (med * 1e-3) / 1e9,
-                dense_equivalent_gbs=B * N * V * 2 / (med * 1e-3) / 1e9)
+                mean_launch_us=mean * 1e3, median_launch_us=float(np.median(per)) * 1e3,
+                visited_rows=visited, achieved_gbs_visited=alg / (mean * 1e-3) / 1e9,
+                dense_equivalent_gbs=B * N * V * 2 / (mean * 1e-3) / 1e9)
 
 
 _CPU_X = None   # the workload a forked oracle worker reads
@@ -231,6 +236,10 @@ def main():
     c = bench_chain(args, torch, sv, synth)
     value = c["positions"] * args.steps / c["span"]
     achieved = c["alg_bytes"] / (c["mean_ms"] * 1e-3) / 1e9     # per launch: one launch per call
+    # traffic: HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counters (scaled
+    # by what the counters read for device copies of known size), over the same launch time
+    trec = traffic_record("chain_kernel_config3")
+    traffic = None if trec is None else trec["bytes_per_launch"] / (c["mean_ms"] * 1e-3) / 1e9
     line = dict(
         metric="verified positions/s + achieved HBM GB/s (% peak), B=64 gamma=5 V=128256 bf16",
         value=value, unit="verified positions/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -240,12 +249,13 @@ def main():
                     B=64, gamma=5, V=128256, logits="bf16", q="fp32", temperature=0.8,
                     input_copies=c["copies"]),
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=achieved / HBM_PEAK_GBS, traffic=None,
+                      frac=achieved / HBM_PEAK_GBS, traffic=traffic,
                       kernel="chain_kernel (one launch per spec_verify_chain call)",
                       mean_launch_us=c["mean_ms"] * 1e3, median_launch_us=c["med_ms"] * 1e3,
                       p10_us=float(np.percentile(c["per"], 10)) * 1e3,
                       p90_us=float(np.percentile(c["per"], 90)) * 1e3,
                       alg_bytes_per_call=c["alg_bytes"], rejecting_requests=c["n_rej"],
+                      traffic_bytes_per_launch=None if trec is None else trec["bytes_per_launch"],
                       mean_accepted=c["mean_acc"]),
     )
     if not args.no_secondary:

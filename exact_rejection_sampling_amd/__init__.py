@@ -7,11 +7,17 @@ tensors in, torch tensors out, on the current CUDA (HIP) stream.
     spec_verify_chain   rejection-sampling verification of draft chains
     spec_verify_greedy  argmax-match verification
     spec_verify_tree    tree verification by target-sample membership
+
+prepare_chain / prepare_greedy / prepare_tree check and marshal the arguments once and
+return a callable that issues the same library call again (for loops that call the
+verifier many times on buffers refilled in place).
 """
-from ._binding import (REQ_STATUS, SpecError, chain_workspace_bytes, greedy_workspace_bytes,
-                       load_library, spec_verify_chain, spec_verify_greedy, spec_verify_tree,
+from ._binding import (REQ_STATUS, SpecError, PreparedCall, chain_workspace_bytes,
+                       greedy_workspace_bytes, load_library, prepare_chain, prepare_greedy,
+                       prepare_tree, spec_verify_chain, spec_verify_greedy, spec_verify_tree,
                        tree_workspace_bytes, LIB_PATH)
 
 __all__ = ["spec_verify_chain", "spec_verify_greedy", "spec_verify_tree", "load_library",
            "chain_workspace_bytes", "greedy_workspace_bytes", "tree_workspace_bytes",
+           "prepare_chain", "prepare_greedy", "prepare_tree", "PreparedCall",
            "SpecError", "REQ_STATUS", "LIB_PATH"]

@@ -129,17 +129,29 @@ def _aligned_ws(ws: torch.Tensor) -> tuple:
     return ctypes.c_void_p(base + off), ws.numel() - off
 
 
-def spec_verify_chain(target_logits: torch.Tensor, draft_probs: torch.Tensor,
-                      draft_tokens: torch.Tensor, uniforms: torch.Tensor, temperature: float,
-                      *, with_stats: bool = False, workspace_tensor: Optional[torch.Tensor] = None,
-                      out: Optional[dict] = None) -> dict:
-    """Chain verification by rejection sampling (C entry point spec_verify_chain).
+class PreparedCall:
+    """One library call with its arguments marshalled once.
 
-    target_logits [B, gamma+1, V] bf16/fp32; draft_probs [B, gamma, V] fp32/bf16;
-    draft_tokens [B, gamma] int32; uniforms [B, gamma+1] fp32; temperature > 0.
-    Returns {accepted_len [B], out_tokens [B, gamma+1], req_status [B], stats?} (int32 /
-    fp32 GPU tensors, valid once the current stream reaches the call).
+    Holds the tensors it points into (inputs, outputs, workspace) so their memory stays
+    alive, and the stream that was current when it was prepared.  Calling it enqueues the
+    same work again on that stream; it re-reads the tensors' *current contents*, so a caller
+    may refill the inputs in place between calls.
     """
+
+    __slots__ = ("_fn", "_args", "_keep", "out")
+
+    def __init__(self, fn, args, keep, out):
+        self._fn, self._args, self._keep, self.out = fn, args, keep, out
+
+    def __call__(self) -> dict:
+        code = self._fn(*self._args)
+        if code != 0:
+            _check(code)
+        return self.out
+
+
+def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature, with_stats,
+                workspace_tensor, out):
     lib = load_library()
     _need(target_logits, "target_logits")
     if target_logits.dim() != 3:
@@ -163,21 +175,39 @@ def spec_verify_chain(target_logits: torch.Tensor, draft_probs: torch.Tensor,
         raise SpecError(f"unsupported sizes B={B} gamma={G} V={V}")
     ws = workspace_tensor if workspace_tensor is not None else workspace("chain", need, dev, stream)
     wp, wn = _aligned_ws(ws)
-    _check(lib.spec_verify_chain(
-        _ptr(target_logits), lt, _ptr(draft_probs), qt, _ptr(draft_tokens), _ptr(uniforms),
-        B, G, V, ctypes.c_float(float(temperature)),
-        _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
-        _ptr(out.get("stats")), wp, wn, ctypes.c_void_p(stream.cuda_stream)))
+    args = (_ptr(target_logits), lt, _ptr(draft_probs), qt, _ptr(draft_tokens), _ptr(uniforms),
+            B, G, V, ctypes.c_float(float(temperature)),
+            _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
+            _ptr(out.get("stats")), wp, wn, ctypes.c_void_p(stream.cuda_stream))
+    keep = (target_logits, draft_probs, draft_tokens, uniforms, ws, stream)
+    return lib.spec_verify_chain, args, keep, out
+
+
+def spec_verify_chain(target_logits: torch.Tensor, draft_probs: torch.Tensor,
+                      draft_tokens: torch.Tensor, uniforms: torch.Tensor, temperature: float,
+                      *, with_stats: bool = False, workspace_tensor: Optional[torch.Tensor] = None,
+                      out: Optional[dict] = None) -> dict:
+    """Chain verification by rejection sampling (C entry point spec_verify_chain).
+
+    target_logits [B, gamma+1, V] bf16/fp32; draft_probs [B, gamma, V] fp32/bf16;
+    draft_tokens [B, gamma] int32; uniforms [B, gamma+1] fp32; temperature > 0.
+    Returns {accepted_len [B], out_tokens [B, gamma+1], req_status [B], stats?} (int32 /
+    fp32 GPU tensors, valid once the current stream reaches the call).
+    """
+    fn, args, _, out = _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
+                                   with_stats, workspace_tensor, out)
+    _check(fn(*args))
     return out
 
 
-def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor, *,
-                       workspace_tensor: Optional[torch.Tensor] = None,
-                       out: Optional[dict] = None) -> dict:
-    """Greedy argmax-match verification (C entry point spec_verify_greedy).
+def prepare_chain(target_logits, draft_probs, draft_tokens, uniforms, temperature, *,
+                  with_stats=False, workspace_tensor=None, out=None) -> PreparedCall:
+    """spec_verify_chain with its arguments checked and marshalled once (see PreparedCall)."""
+    return PreparedCall(*_chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
+                                     with_stats, workspace_tensor, out))
 
-    target_logits [B, gamma+1, V] bf16/fp32; draft_tokens [B, gamma] int32.
-    """
+
+def _greedy_args(target_logits, draft_tokens, workspace_tensor, out):
     lib = load_library()
     _need(target_logits, "target_logits")
     if target_logits.dim() != 3:
@@ -197,23 +227,31 @@ def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor, 
         raise SpecError(f"unsupported sizes B={B} gamma={G} V={V}")
     ws = workspace_tensor if workspace_tensor is not None else workspace("greedy", need, dev, stream)
     wp, wn = _aligned_ws(ws)
-    _check(lib.spec_verify_greedy(
-        _ptr(target_logits), lt, _ptr(draft_tokens), B, G, V,
-        _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
-        wp, wn, ctypes.c_void_p(stream.cuda_stream)))
+    args = (_ptr(target_logits), lt, _ptr(draft_tokens), B, G, V,
+            _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
+            wp, wn, ctypes.c_void_p(stream.cuda_stream))
+    keep = (target_logits, draft_tokens, ws, stream)
+    return lib.spec_verify_greedy, args, keep, out
+
+
+def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor, *,
+                       workspace_tensor: Optional[torch.Tensor] = None,
+                       out: Optional[dict] = None) -> dict:
+    """Greedy argmax-match verification (C entry point spec_verify_greedy).
+
+    target_logits [B, gamma+1, V] bf16/fp32; draft_tokens [B, gamma] int32.
+    """
+    fn, args, _, out = _greedy_args(target_logits, draft_tokens, workspace_tensor, out)
+    _check(fn(*args))
     return out
 
 
-def spec_verify_tree(node_logits: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor,
-                     uniforms: torch.Tensor, temperature: float, *,
-                     workspace_tensor: Optional[torch.Tensor] = None,
-                     out: Optional[dict] = None) -> dict:
-    """Tree verification by target-sample membership (C entry point spec_verify_tree).
+def prepare_greedy(target_logits, draft_tokens, *, workspace_tensor=None, out=None) -> PreparedCall:
+    """spec_verify_greedy with its arguments checked and marshalled once (see PreparedCall)."""
+    return PreparedCall(*_greedy_args(target_logits, draft_tokens, workspace_tensor, out))
 
-    node_logits [B, N, V] bf16/fp32 (row v scores the children of node v); node_tokens,
-    parents [B, N] int32 (parents[:, 0] = -1, 0 <= parents[v] < v); uniforms [B, N] fp32.
-    Returns {accepted_len [B], out_tokens [B, N], out_nodes [B, N], req_status [B]}.
-    """
+
+def _tree_args(node_logits, node_tokens, parents, uniforms, temperature, workspace_tensor, out):
     lib = load_library()
     _need(node_logits, "node_logits")
     if node_logits.dim() != 3:
@@ -235,12 +273,35 @@ def spec_verify_tree(node_logits: torch.Tensor, node_tokens: torch.Tensor, paren
         raise SpecError(f"unsupported sizes B={B} N={N} V={V}")
     ws = workspace_tensor if workspace_tensor is not None else workspace("tree", need, dev, stream)
     wp, wn = _aligned_ws(ws)
-    _check(lib.spec_verify_tree(
-        _ptr(node_logits), lt, _ptr(node_tokens), _ptr(parents), _ptr(uniforms),
-        B, N, V, ctypes.c_float(float(temperature)),
-        _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["out_nodes"]),
-        _ptr(out["req_status"]), wp, wn, ctypes.c_void_p(stream.cuda_stream)))
+    args = (_ptr(node_logits), lt, _ptr(node_tokens), _ptr(parents), _ptr(uniforms),
+            B, N, V, ctypes.c_float(float(temperature)),
+            _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["out_nodes"]),
+            _ptr(out["req_status"]), wp, wn, ctypes.c_void_p(stream.cuda_stream))
+    keep = (node_logits, node_tokens, parents, uniforms, ws, stream)
+    return lib.spec_verify_tree, args, keep, out
+
+
+def spec_verify_tree(node_logits: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor,
+                     uniforms: torch.Tensor, temperature: float, *,
+                     workspace_tensor: Optional[torch.Tensor] = None,
+                     out: Optional[dict] = None) -> dict:
+    """Tree verification by target-sample membership (C entry point spec_verify_tree).
+
+    node_logits [B, N, V] bf16/fp32 (row v scores the children of node v); node_tokens,
+    parents [B, N] int32 (parents[:, 0] = -1, 0 <= parents[v] < v); uniforms [B, N] fp32.
+    Returns {accepted_len [B], out_tokens [B, N], out_nodes [B, N], req_status [B]}.
+    """
+    fn, args, _, out = _tree_args(node_logits, node_tokens, parents, uniforms, temperature,
+                                  workspace_tensor, out)
+    _check(fn(*args))
     return out
+
+
+def prepare_tree(node_logits, node_tokens, parents, uniforms, temperature, *, workspace_tensor=None,
+                 out=None) -> PreparedCall:
+    """spec_verify_tree with its arguments checked and marshalled once (see PreparedCall)."""
+    return PreparedCall(*_tree_args(node_logits, node_tokens, parents, uniforms, temperature,
+                                    workspace_tensor, out))
 
 
 def chain_workspace_bytes(B: int, gamma: int, V: int) -> int:
