@@ -95,9 +95,6 @@ spec_status spec_verify_chain(const void* target_logits, int logit_dtype, const 
   p.req_status = req_status;
   p.stats = stats;
   p.part = reinterpret_cast<float2*>(ws + L.part);
-  p.global = reinterpret_cast<unsigned*>(ws);
-  p.counters = sv::request_counters(workspace);
-  p.dec = reinterpret_cast<sv::ChainDecision*>(ws + L.dec);
   p.gath = reinterpret_cast<unsigned long long*>(ws + L.gath);
   p.tmass = reinterpret_cast<double*>(ws + L.tmass);
   p.B = B;
@@ -108,7 +105,6 @@ spec_status spec_verify_chain(const void* target_logits, int logit_dtype, const 
   p.P = sl.P;
   p.CPW = sl.CPW;
   p.SL = sl.SL;
-  p.PP = sl.PP;
   p.S2 = chunks(V, sv::kTermChunk);
   p.q_dtype = q_dtype;
   const double c2 = kLog2e / static_cast<double>(temperature);

@@ -1,23 +1,28 @@
 // Chain verification by rejection sampling (spec_verify_chain).
 //
-// One launch, one block per work item, the item chosen by blockIdx.  The first B*(gamma+1)*SL
-// blocks are statistics items, request-major; the B*S2 blocks after them are terminal
-// items, also request-major:
+// One launch, one block per work item, the item chosen by blockIdx (block_item): B*(gamma+1)*SL
+// statistics items and B*S2 terminal items, each request's terminal items placed a fixed
+// lag of blocks after its statistics items:
 //  * statistics item (row, slice): the block's four waves stream a slice of one target
 //    row with 16-byte non-temporal loads, keep an online (max, sum of exponentials) per
-//    lane and publish one summary per wave.  The last item of a request to finish
-//    combines the summaries of all gamma+1 rows, runs the accept tests of the draft
-//    tokens in order and publishes the decision: the first rejection A (or gamma).
-//  * terminal item (request, 4096-element chunk): waits for the request's decision,
-//    then sums the terminal weights w = max(p_A - q_A, 0) (or p_gamma when every draft
-//    was accepted) over its chunk.  The last chunk to finish finds the chunk where the
-//    running mass passes u_gamma * W and rescans that chunk in vocabulary order.
-// Statistics items never wait for another block (the last arriver's reads of the other
-// summaries only bridge the time until their stores are visible).  Terminal items wait only
-// for statistics items, whose block indices are all lower; the hardware dispatches the
-// workgroups of a launch in index order, so those blocks are running or done, and every
-// wait ends.  The wait is bounded all the same: a decision that does not arrive within the
-// bound is reported as SPEC_REQ_INTERNAL rather than waited for.
+//    lane, merge lanes and waves, and publish one summary for the slice.  The block that
+//    streams a draft row's first slice also publishes the draft token, its logit and its
+//    draft probability.  A statistics item never waits and never counts arrivals.
+//  * terminal item (request, 4096-element chunk): reads every summary of its request as
+//    soon as it is published, combines them into each row's normalizer, runs the accept
+//    tests in order and so finds the first rejection A (or gamma) -- every terminal item of
+//    a request computes the same decision from the same words -- then sums the terminal
+//    weights w = max(p_A - q_A, 0) (or p_gamma when every draft was accepted) over its
+//    chunk and publishes the chunk's mass.  The request's last terminal item (its
+//    selector) waits for the other chunks' masses, finds the chunk where the running mass
+//    passes u_gamma * W, rescans that chunk in vocabulary order, writes the outputs and
+//    returns every workspace word the request used to zero.
+// Waits: a terminal item waits only for its request's statistics items, whose block
+// indices are all lower (see block_item), and a selector only for its request's other
+// terminal items, whose indices are lower too.  The hardware dispatches the workgroups of a launch in index order, so a
+// waiting block never holds a slot that one of the blocks it waits for still needs, and
+// every wait ends.  Each wait is bounded all the same: a word that does not arrive within
+// the bound makes the request report SPEC_REQ_INTERNAL rather than wait on.
 //
 // Method: [M7.1] "M7.1 - Speculative Decoding: Draft, Verify, Accept, Reject" §0x03A
 // (accept test), §0x03C (positive residual), §0x03G (stop at the first rejection),
@@ -35,48 +40,6 @@ constexpr double kLn2 = 0.69314718055994530942;
 
 __device__ __forceinline__ float gather_q(const ChainParams& p, size_t idx) {
   return p.q_dtype == kBF16 ? load_scalar<kBF16>(p.q, idx) : load_scalar<kF32>(p.q, idx);
-}
-
-__device__ void write_failed(const ChainParams& p, int b, int code) {
-  for (int i = threadIdx.x; i < p.R; i += blockDim.x) p.out_tokens[(size_t)b * p.R + i] = -1;
-  if (p.stats)
-    for (int i = threadIdx.x; i < p.R * 4; i += blockDim.x) p.stats[(size_t)b * p.R * 4 + i] = NAN;
-  if (threadIdx.x == 0) {
-    p.accepted_len[b] = -1;
-    p.req_status[b] = code;
-  }
-}
-
-constexpr int kSlotStats = 0, kSlotTerm = 1;
-
-__device__ __forceinline__ unsigned* slot(const ChainParams& p, int b, int k) {
-  return p.counters + (size_t)b * kCounterSlots + k;
-}
-
-// A request's decision as two self-validating words for the terminal items of the same
-// launch: word 0 = A | status << 32 with the top bit set; word 1 = r_ref | inv_z << 32,
-// where inv_z is positive (failed requests carry 1.0).
-__device__ __forceinline__ void publish_decision(const ChainParams& p, int b, const ChainDecision& d) {
-  unsigned long long* w = reinterpret_cast<unsigned long long*>(p.dec + b);
-  const float inv_z = d.status == 0 ? d.inv_z : 1.0f;
-  publish_u64(w + 1, (static_cast<unsigned long long>(__float_as_uint(inv_z)) << 32) |
-                         __float_as_uint(d.r_ref));
-  publish_u64(w, (1ull << 63) | (static_cast<unsigned long long>(static_cast<unsigned>(d.status)) << 32) |
-                     static_cast<unsigned>(d.A));
-}
-
-// Wait (bounded) for request b's decision; a decision that never arrives is reported
-// as an internal error.
-__device__ __forceinline__ ChainDecision await_decision(const ChainParams& p, int b) {
-  const unsigned long long* w = reinterpret_cast<const unsigned long long*>(p.dec + b);
-  const unsigned long long a = await_u64(w);
-  unsigned long long c = await_u64(w + 1);
-  for (unsigned spins = 0; (c >> 32) == 0ull && spins < kSpinLimit; ++spins) c = fetch_u64(w + 1);
-  if (!(a >> 63) || (c >> 32) == 0ull) return ChainDecision{-1, SPEC_REQ_INTERNAL, 0.0f, 0.0f};
-  return ChainDecision{static_cast<int32_t>(static_cast<unsigned>(a)),
-                       static_cast<int32_t>(static_cast<unsigned>(a >> 32) & 0x7fffffffu),
-                       __uint_as_float(static_cast<unsigned>(c)),
-                       __uint_as_float(static_cast<unsigned>(c >> 32))};
 }
 
 // Gather record of draft row i, published by the block that streams the row's first
@@ -106,28 +69,83 @@ __device__ __forceinline__ void gather_publish(const ChainParams& p, int b, int 
   publish_u64(g + 2, (1ull << 63) | qb);
 }
 
-constexpr int kDecideStage = 2048;                    // summaries the deciding block stages in LDS
+// Statistics item: slice `slice` of row i of request b.
+template <int DT, bool VEC>
+__device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
+  __shared__ float s_wm[kWavesPerBlock], s_wz[kWavesPerBlock];
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const size_t rowid = (size_t)b * p.R + i;
+  // the first slice of a draft row also fetches the draft token, its logit and its draft
+  // probability for the decision, overlapped with the streaming below
+  const bool gathers = slice == 0 && i < p.G && threadIdx.x == 0;
+  unsigned gx = 0, gl = 0, gq = 0;
+  if (gathers) gather_issue<DT>(p, b, i, gx, gl, gq);
+  // wave w streams chunks first + 4k of this slice (k < CPW)
+  const long first = (long)slice * kWavesPerBlock * p.CPW + wave;
+  float m, z;
+  wave_row_summary<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, p.P, first, kWavesPerBlock, p.CPW, lane,
+                            p.c2, m, z);
+  if (lane == 0) {
+    s_wm[wave] = m;
+    s_wz[wave] = z;
+  }
+  if (gathers) gather_publish(p, b, i, gx, gl, gq);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // the slice's summary: M = max of the waves' maxima, Z = sum of their sums rescaled
+    // to M (NaN if any wave saw NaN or +inf; (-inf, 0) if every element was -inf).  Z >= 1
+    // otherwise (the maximum contributes 2^0), so the published word is never zero.
+    float M = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      M = fmaxf(M, s_wm[w]);
+      nan |= (s_wz[w] != s_wz[w]);
+    }
+    float Z = 0.0f;
+    if (M != -INFINITY) {
+      const float R = M * p.c2;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w)
+        if (s_wm[w] != -INFINITY) Z += s_wz[w] * __builtin_amdgcn_exp2f(s_wm[w] * p.c2 - R);
+    }
+    if (nan) Z = NAN;
+    publish_f2(p.part + rowid * p.SL + slice, make_float2(M, Z));
+  }
+}
+
+// Summaries the terminal items stage in LDS when the request's rows have few slices.
+constexpr int kDecideStage = 1024;
 constexpr int kStagePerThread = kDecideStage / kBlock;
 
-// Last block of request b in the statistics pass: combine, accept scan, decision.  All of
-// its global reads (summaries, gathered draft values, uniforms) are issued together.
+// Per-row results of a terminal item's decision, kept for the selector's outputs.
+struct RowState {
+  float r[SPEC_MAX_GAMMA + 1];    // reference exponent per row
+  float m[SPEC_MAX_GAMMA + 1];    // raw max per row
+  double z[SPEC_MAX_GAMMA + 1];   // sum 2^(l c2 - r) per row
+  int bad[SPEC_MAX_GAMMA + 1];    // row is all -inf, or holds NaN / +inf
+  double px[SPEC_MAX_GAMMA];      // p_i(x_i) of the reached draft rows
+  double a[SPEC_MAX_GAMMA];       // a_i of the reached draft rows
+};
+
+// The decision of request b from its published summaries and gather records.  Every
+// terminal item of the request runs this on the same words and takes the same decision,
+// which it leaves in `s_dec` (shared; valid after the final barrier).
 template <int DT>
-__device__ void chain_decide(const ChainParams& p, int b) {
+__device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDecision& s_dec) {
   __shared__ float2 s_part[kDecideStage];
-  __shared__ float s_r[SPEC_MAX_GAMMA + 1];     // reference exponent per row
-  __shared__ float s_m[SPEC_MAX_GAMMA + 1];     // raw max per row
-  __shared__ double s_z[SPEC_MAX_GAMMA + 1];    // sum 2^(l c2 - r) per row
-  __shared__ int s_bad[SPEC_MAX_GAMMA + 1];
+  __shared__ int s_timeout;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   const float c2 = p.c2;
   const int G = p.G;
-  const int total = p.R * p.PP;
-  const float2* part_b = p.part + (size_t)b * p.R * p.PP;
+  const int total = p.R * p.SL;
+  const float2* part_b = p.part + (size_t)b * total;
   const bool staged = total <= kDecideStage;
+  if (tid == 0) s_timeout = 0;
 
   // wave 0, lane i < G: draft position i -- its gather record and uniform
   unsigned long long g[3] = {0ull, 0ull, 0ull};
-  float ui = 0.0f;
+  float ui = 0.0f, ut = 0.0f;
   if (wave == 0 && lane < G) {
     const unsigned long long* rec = gather_rec(p, b, lane);
     g[0] = fetch_u64(rec);
@@ -135,6 +153,8 @@ __device__ void chain_decide(const ChainParams& p, int b) {
     g[2] = fetch_u64(rec + 2);
     ui = p.u[(size_t)b * p.R + lane];
   }
+  if (wave == 0) ut = p.u[(size_t)b * p.R + G];
+  bool timeout = false;
   if (staged) {
     unsigned long long v[kStagePerThread];
 #pragma unroll
@@ -147,6 +167,7 @@ __device__ void chain_decide(const ChainParams& p, int b) {
       const int j = tid + k * kBlock;
       if (j < total) {
         if (v[k] == 0ull) v[k] = await_u64(reinterpret_cast<const unsigned long long*>(part_b + j));
+        timeout |= (v[k] == 0ull);
         s_part[j] = make_float2(__uint_as_float(static_cast<unsigned>(v[k])),
                                 __uint_as_float(static_cast<unsigned>(v[k] >> 32)));
       }
@@ -155,143 +176,86 @@ __device__ void chain_decide(const ChainParams& p, int b) {
   if (wave == 0 && lane < G) {
     const unsigned long long* rec = gather_rec(p, b, lane);
 #pragma unroll
-    for (int k = 0; k < 3; ++k)
+    for (int k = 0; k < 3; ++k) {
       if (g[k] == 0ull) g[k] = await_u64(rec + k);
+      timeout |= (g[k] == 0ull);
+    }
   }
-  __syncthreads();
+  __syncthreads();                        // s_timeout's reset precedes every report
+  if (timeout) s_timeout = 1;
 
   for (int i = wave; i < p.R; i += kWavesPerBlock) {
-    const float2* row_part = part_b + (size_t)i * p.PP;
+    const float2* row_part = part_b + (size_t)i * p.SL;
+    bool lost = false;
+    auto summary = [&](int j) {
+      if (staged) return s_part[i * p.SL + j];
+      const unsigned long long bits = await_u64(reinterpret_cast<const unsigned long long*>(row_part + j));
+      lost |= (bits == 0ull);
+      return make_float2(__uint_as_float(static_cast<unsigned>(bits)),
+                         __uint_as_float(static_cast<unsigned>(bits >> 32)));
+    };
     float m = -INFINITY;
-    for (int j = lane; j < p.PP; j += kWave)
-      m = fmaxf(m, staged ? s_part[i * p.PP + j].x : await_f2(row_part + j).x);
+    for (int j = lane; j < p.SL; j += kWave) m = fmaxf(m, summary(j).x);
     m = wave_max(m);
     const float r = m * c2;
     double z = 0.0;
-    for (int j = lane; j < p.PP; j += kWave) {
-      const float2 s = staged ? s_part[i * p.PP + j] : await_f2(row_part + j);
+    for (int j = lane; j < p.SL; j += kWave) {
+      const float2 s = summary(j);
       // 2^(r_j - r) <= 1; an all -inf row gives (-inf) - (-inf) = NaN, flagged below
       z += (double)s.y * (double)__builtin_amdgcn_exp2f(s.x * c2 - r);
     }
     z = wave_sum_d(z);
+    if (wave_any(lost) && lane == 0) s_timeout = 1;
     if (lane == 0) {
-      s_r[i] = r;
-      s_m[i] = m;
-      s_z[i] = z;
+      rs.r[i] = r;
+      rs.m[i] = m;
+      rs.z[i] = z;
       // all -inf, NaN or +inf anywhere: z is not a positive finite number
-      s_bad[i] = !(isfinite(z) && z > 0.0);
+      rs.bad[i] = !(isfinite(z) && z > 0.0);
     }
   }
   __syncthreads();
-  // the summaries and gather records are consumed: return them to zero (every call
-  // leaves the workspace zeroed)
-  for (int j = tid; j < total; j += kBlock) clear_f2(const_cast<float2*>(part_b) + j);
-  for (int j = tid; j < 3 * G; j += kBlock) clear_u64(gather_rec(p, b, 0) + j);
-  if (wave != 0) return;
-
-  // lane i < G: draft position i, checked in the order a round reaches it
-  int code = 0;
-  bool reject = false;
-  double px = NAN, a = NAN;
-  if (lane < G) {
-    const int x = static_cast<int>(static_cast<unsigned>(g[0]));
-    if (s_bad[lane]) {
-      code = SPEC_REQ_NONFINITE;
-    } else if (x < 0 || x >= p.V) {
-      code = SPEC_REQ_BADTOKEN;
-    } else {
-      const float qx = __uint_as_float(static_cast<unsigned>(g[2]));
-      if (!(isfinite(qx) && qx > 0.0f)) {
-        code = SPEC_REQ_QZERO;
-      } else if (!(ui >= 0.0f && ui < 1.0f)) {
-        code = SPEC_REQ_BADUNIFORM;
-      } else {
-        const float lx = __uint_as_float(static_cast<unsigned>(g[1]));
-        px = exp2((double)lx * (double)c2 - (double)s_r[lane]) / s_z[lane];
-        a = fmin(1.0, px / (double)qx);
-        reject = !((double)ui < a);
-      }
-    }
-  }
-  const unsigned long long stop = __ballot(lane < G && (code != 0 || reject));
-  int A = stop ? (__ffsll((long long)stop) - 1) : G;
-  int status = __shfl(code, A < G ? A : 0, kWave);
-  if (A == G) {
-    status = s_bad[G] ? SPEC_REQ_NONFINITE : 0;
-  }
-  if (status == 0) {
-    const float ut = p.u[(size_t)b * p.R + G];
-    if (!(ut >= 0.0f && ut < 1.0f)) status = SPEC_REQ_BADUNIFORM;
-  }
-
-  if (status != 0) {
-    // whole wave writes the failure record
-    for (int i = lane; i < p.R; i += kWave) p.out_tokens[(size_t)b * p.R + i] = -1;
-    if (p.stats)
-      for (int i = lane; i < p.R * 4; i += kWave) p.stats[(size_t)b * p.R * 4 + i] = NAN;
-    if (lane == 0) {
-      p.accepted_len[b] = -1;
-      p.req_status[b] = status;
-      publish_decision(p, b, ChainDecision{-1, status, 0.0f, 0.0f});
-    }
-    return;
-  }
-
-  if (p.stats) {
-    // Written through to memory before the decision is published: the terminal items'
-    // last block writes W (or, on failure, NaN over everything) afterwards.
-    float* st = p.stats + (size_t)b * p.R * 4;
-    // rows 0..A (< G) reached: (m, log Z, p(x), a); later draft rows NaN
+  if (wave == 0) {
+    // lane i < G: draft position i, checked in the order a round reaches it
+    int code = 0;
+    bool reject = false;
+    double px = NAN, a = NAN;
     if (lane < G) {
-      const bool reached = lane <= A;
-      const double m_nat = (double)s_m[lane] * p.inv_t;
-      const double logz = log(s_z[lane]) + (double)s_r[lane] * kLn2 - m_nat;
-      store_wt(st + lane * 4 + 0, reached ? (float)m_nat : NAN);
-      store_wt(st + lane * 4 + 1, reached ? (float)logz : NAN);
-      store_wt(st + lane * 4 + 2, reached ? (float)px : NAN);
-      store_wt(st + lane * 4 + 3, reached ? (float)a : NAN);
+      const int x = static_cast<int>(static_cast<unsigned>(g[0]));
+      if (rs.bad[lane]) {
+        code = SPEC_REQ_NONFINITE;
+      } else if (x < 0 || x >= p.V) {
+        code = SPEC_REQ_BADTOKEN;
+      } else {
+        const float qx = __uint_as_float(static_cast<unsigned>(g[2]));
+        if (!(isfinite(qx) && qx > 0.0f)) {
+          code = SPEC_REQ_QZERO;
+        } else if (!(ui >= 0.0f && ui < 1.0f)) {
+          code = SPEC_REQ_BADUNIFORM;
+        } else {
+          const float lx = __uint_as_float(static_cast<unsigned>(g[1]));
+          px = exp2((double)lx * (double)c2 - (double)rs.r[lane]) / rs.z[lane];
+          a = fmin(1.0, px / (double)qx);
+          reject = !((double)ui < a);
+        }
+      }
+      rs.px[lane] = px;
+      rs.a[lane] = a;
     }
+    const unsigned long long stop = __ballot(lane < G && (code != 0 || reject));
+    const int A = stop ? (__ffsll((long long)stop) - 1) : G;
+    int status = __shfl(code, A < G ? A : 0, kWave);
+    if (A == G) status = rs.bad[G] ? SPEC_REQ_NONFINITE : 0;
+    if (status == 0 && !(ut >= 0.0f && ut < 1.0f)) status = SPEC_REQ_BADUNIFORM;
+    if (s_timeout) status = SPEC_REQ_INTERNAL;
     if (lane == 0) {
-      const bool bonus = (A == G);
-      const double m_nat = (double)s_m[G] * p.inv_t;
-      const double logz = log(s_z[G]) + (double)s_r[G] * kLn2 - m_nat;
-      store_wt(st + G * 4 + 0, bonus ? (float)m_nat : NAN);
-      store_wt(st + G * 4 + 1, bonus ? (float)logz : NAN);
-      store_wt(st + G * 4 + 3, NAN);   // column 2 (W) belongs to the terminal items
+      s_dec.A = status == 0 ? A : -1;
+      s_dec.status = status;
+      s_dec.r_ref = status == 0 ? rs.r[A] : 0.0f;
+      s_dec.inv_z = status == 0 ? (float)(1.0 / rs.z[A]) : 0.0f;
     }
-  }
-  if (lane == 0) publish_decision(p, b, ChainDecision{A, 0, s_r[A], (float)(1.0 / s_z[A])});
-}
-
-// Statistics item: slice `slice` of row i of request b.
-template <int DT, bool VEC>
-__device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
-  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
-  const size_t rowid = (size_t)b * p.R + i;
-  // the first slice of a draft row also fetches the draft token, its logit and its draft
-  // probability for the decision, overlapped with the streaming below
-  const bool gathers = slice == 0 && i < p.G && threadIdx.x == 0;
-  unsigned gx = 0, gl = 0, gq = 0;
-  if (gathers) gather_issue<DT>(p, b, i, gx, gl, gq);
-  {
-    // wave w streams chunks first + 4k of this slice (k < CPW); always one summary per wave
-    const long first = (long)slice * kWavesPerBlock * p.CPW + wave;
-    float m, z;
-    wave_row_summary<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, p.P, first, kWavesPerBlock, p.CPW,
-                              lane, p.c2, m, z);
-    if (lane == 0) publish_f2(p.part + rowid * p.PP + slice * kWavesPerBlock + wave, make_float2(m, z));
-  }
-  if (gathers) gather_publish(p, b, i, gx, gl, gq);
-  __syncthreads();   // every wave's summary store has completed
-  __shared__ int s_last;
-  if (threadIdx.x == 0) {
-    const unsigned prev = arrive(slot(p, b, kSlotStats));
-    s_last = (prev == (unsigned)(p.R * p.SL - 1));
   }
   __syncthreads();
-  if (!s_last) return;
-  chain_decide<DT>(p, b);
-  if (threadIdx.x == 0) reset_counter(slot(p, b, kSlotStats));
 }
 
 // Terminal weight of one element: p(x) = 2^(l c2 - r) / Z; residual rows subtract q and
@@ -309,218 +273,321 @@ __device__ __forceinline__ float term_weight(float l, float qv, float c2, float 
   }
 }
 
+// The weights of this thread's 8 elements in each slab of terminal chunk c, both slabs'
+// loads issued together.
 template <int DT, int QT, bool VEC, bool RESID>
-__device__ __forceinline__ void term_load8(const void* lrow, const void* qrow, long e0, long V, float c2,
-                                           float r, float inv_z, float (&w)[8], bool& bad) {
-  float lv[8], qv[8];
-  load8<DT, VEC, false>(lrow, e0, V, lv, -INFINITY);
-  if constexpr (RESID) {
-    load8<QT, VEC, false>(qrow, e0, V, qv, 0.0f);
-  } else {
+__device__ __forceinline__ void term_chunk(const ChainParams& p, const void* lrow, const void* qrow, int c,
+                                           const ChainDecision& d, float (&w)[kTermSlabs][8], bool& bad) {
+  float lv[kTermSlabs][8], qv[kTermSlabs][8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) qv[k] = 0.0f;
+  for (int s = 0; s < kTermSlabs; ++s) {
+    const long e0 = ((long)c * kTermSlabs + s) * kSlab + (long)threadIdx.x * kVec;
+    load8<DT, VEC, false>(lrow, e0, p.V, lv[s], -INFINITY);
+    if constexpr (RESID) load8<QT, VEC, false>(qrow, e0, p.V, qv[s], 0.0f);
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) w[k] = term_weight<RESID>(lv[k], qv[k], c2, r, inv_z, bad);
+  for (int s = 0; s < kTermSlabs; ++s)
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      w[s][k] = term_weight<RESID>(lv[s][k], RESID ? qv[s][k] : 0.0f, p.c2, d.r_ref, d.inv_z, bad);
 }
 
-// Last block of request b in the terminal pass: pick the chunk, rescan it, emit.
+// Block sum (fp64) of this thread's weights; NaN if any thread saw a bad q entry.
+__device__ __forceinline__ double block_mass(const float (&w)[kTermSlabs][8], bool bad) {
+  __shared__ double s_red[kWavesPerBlock];
+  double acc = 0.0;
+#pragma unroll
+  for (int s = 0; s < kTermSlabs; ++s)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += (double)w[s][k];
+  if (bad) acc = NAN;
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const double ws = wave_sum_d(acc);
+  if (lane == 0) s_red[wave] = ws;
+  __syncthreads();
+  const double m = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+  __syncthreads();
+  return m;
+}
+
+// Chunk masses are read in runs of up to kMassRegs per thread and kept in registers;
+// longer runs (vocabularies beyond 8M) re-read the published words.
+constexpr int kMassRegs = 8;
+
+// The selector of request b: every other chunk's mass is awaited; then the chunk where the
+// running mass passes u_gamma * W is rescanned in vocabulary order and the outputs are
+// written.  `own` is the mass of chunk S2 - 1, which the selector computed itself.
 template <int DT, int QT, bool VEC, bool RESID>
-__device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d, const void* lrow,
-                             const void* qrow) {
+__device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d, const RowState& rs,
+                             double own, const void* lrow, const void* qrow) {
   __shared__ double s_scan[kWavesPerBlock];
-  __shared__ int s_pick;
-  __shared__ double s_before;
-  __shared__ double s_total;
-  const int tid = threadIdx.x;
+  __shared__ int s_imin[kWavesPerBlock];
+  __shared__ int s_timeout;
+  __shared__ double s_before, s_total;
+  const int tid = threadIdx.x, G = p.G;
   const double* tm = p.tmass + (size_t)b * p.S2;
+  const float ut = p.u[(size_t)b * p.R + G];
+  if (tid == 0) {
+    s_timeout = 0;
+    s_before = 0.0;
+  }
+  __syncthreads();
 
   // 1. running mass over the chunks in order: thread t owns a contiguous run of chunks
-  //    and extends the block-exclusive prefix sequentially over it.  W is the running
-  //    value after the last chunk, computed the same way, so u * W < W always finds a
-  //    chunk whose running value exceeds the target.
+  //    and extends the block-exclusive prefix over it.  W is the running value after the
+  //    last chunk, computed the same way, so u * W < W always finds a chunk whose running
+  //    value exceeds the target.
   const int per = (p.S2 + kBlock - 1) / kBlock;
   const int c_lo = min(tid * per, p.S2), c_hi = min(c_lo + per, p.S2);
+  double mv[kMassRegs];
+  bool lost = false;
+  auto mass_at = [&](int c) -> double {
+    if (c == p.S2 - 1) return own;
+    const unsigned long long bits = await_u64(reinterpret_cast<const unsigned long long*>(tm + c));
+    lost |= (bits == 0ull);
+    return -__longlong_as_double(static_cast<long long>(bits));
+  };
   double mine = 0.0;
-  for (int c = c_lo; c < c_hi; ++c) mine += await_mass(tm + c);
+#pragma unroll
+  for (int k = 0; k < kMassRegs; ++k) {
+    const int c = c_lo + k;
+    mv[k] = c < c_hi ? mass_at(c) : 0.0;
+    mine += mv[k];
+  }
+  for (int c = c_lo + kMassRegs; c < c_hi; ++c) mine += mass_at(c);
+  if (lost) s_timeout = 1;
   double tot;
   const double excl = block_excl_scan_d(mine, s_scan, &tot);
-  double run_end = excl;
-  for (int c = c_lo; c < c_hi; ++c) run_end += await_mass(tm + c);
-  if (c_lo < c_hi && c_hi == p.S2) s_total = run_end;
-  if (tid == 0) s_pick = 0x7fffffff;
+  if (c_lo < c_hi && c_hi == p.S2) s_total = excl + mine;
   __syncthreads();
   const double W = s_total;
-  const int G = p.G;
-  if (!(isfinite(W) && W > 0.0)) {
-    write_failed(p, b, SPEC_REQ_RESIDUAL_EMPTY);
-    return;
-  }
-  const double t = (double)p.u[(size_t)b * p.R + G] * W;
-  {
+  const bool failed = s_timeout || !(isfinite(W) && W > 0.0);   // uniform across the block
+  double t = 0.0;
+  int k = -1;
+  if (!failed) {
+    t = (double)ut * W;
+    int cand = 0x7fffffff;          // first chunk of this thread's run whose running value passes t
     double run = excl;
     for (int c = c_lo; c < c_hi; ++c) {
-      const double nxt = run + await_mass(tm + c);
+      const double mc = c - c_lo < kMassRegs ? mv[c - c_lo] : mass_at(c);
+      const double nxt = run + mc;
       if (nxt > t) {
-        atomicMin(&s_pick, c);
+        cand = c;
         break;
       }
       run = nxt;
     }
-  }
-  __syncthreads();
-  // a chunk is always found (t < W and the last running value is W); clamp regardless
-  const int cstar = s_pick == 0x7fffffff ? p.S2 - 1 : s_pick;
-  if (tid == 0) s_before = 0.0;
-  __syncthreads();
-  if (cstar >= c_lo && cstar < c_hi) {       // the owner of cstar records the mass before it
-    double run = excl;
-    for (int c = c_lo; c < cstar; ++c) run += await_mass(tm + c);
-    s_before = run;
-  }
-  __syncthreads();
-  if (tid == 0) s_pick = 0x7fffffff;
-  __syncthreads();
-  double rem = t - s_before;   // target mass inside chunk cstar
+    // a chunk is always found (t < W and the last running value is W); clamp regardless
+    int cstar = block_min_i(cand, s_imin);
+    if (cstar == 0x7fffffff) cstar = p.S2 - 1;
+    if (cstar >= c_lo && cstar < c_hi) {       // the owner of cstar records the mass before it
+      double before = excl;
+      for (int c = c_lo; c < cstar; ++c) before += c - c_lo < kMassRegs ? mv[c - c_lo] : mass_at(c);
+      s_before = before;
+    }
+    __syncthreads();
+    const double rem = t - s_before;   // target mass inside chunk cstar
 
-  // 2. rescan cstar in vocabulary order, slab by slab
-  const float c2 = p.c2, r = d.r_ref, inv_z = d.inv_z;
-  int last_pos = -1;
-  for (int s = 0; s < kTermSlabs; ++s) {
-    const long e0 = ((long)cstar * kTermSlabs + s) * kSlab + (long)tid * kVec;
-    float w[8];
+    // 2. rescan cstar in vocabulary order: slab 0 then slab 1, each thread's 8 elements
+    //    in order within a slab
+    float w[kTermSlabs][8];
     bool bad = false;
-    term_load8<DT, QT, VEC, RESID>(lrow, qrow, e0, p.V, c2, r, inv_z, w, bad);
-    double incl[8];
-    double acc = 0.0;
+    term_chunk<DT, QT, VEC, RESID>(p, lrow, qrow, cstar, d, w, bad);
+    double before_slab = 0.0;
+    int last_pos = -1, pick = 0x7fffffff;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      acc += (double)w[k];
-      incl[k] = acc;
-      if (w[k] > 0.0f) last_pos = (int)(e0 + k);
-    }
-    double slab_total;
-    const double off = block_excl_scan_d(acc, s_scan, &slab_total);
+    for (int s = 0; s < kTermSlabs; ++s) {
+      const long e0 = ((long)cstar * kTermSlabs + s) * kSlab + (long)tid * kVec;
+      double incl[8];
+      double acc = 0.0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (off + incl[k] > rem && w[k] > 0.0f) { atomicMin(&s_pick, (int)(e0 + k)); break; }
+      for (int j = 0; j < 8; ++j) {
+        acc += (double)w[s][j];
+        incl[j] = acc;
+        if (w[s][j] > 0.0f) last_pos = (int)(e0 + j);
+      }
+      double slab_total;
+      const double off = before_slab + block_excl_scan_d(acc, s_scan, &slab_total);
+      int cand = 0x7fffffff;
+#pragma unroll
+      for (int j = 7; j >= 0; --j)
+        if (off + incl[j] > rem && w[s][j] > 0.0f) cand = (int)(e0 + j);
+      pick = min(pick, cand);
+      before_slab += slab_total;
     }
-    __syncthreads();
-    if (s_pick != 0x7fffffff) break;
-    rem -= slab_total;
-    __syncthreads();
+    // the first position whose running value passes the target; rounding may leave the
+    // target just past the chunk's last positive weight: then take that weight
+    pick = block_min_i(pick, s_imin);
+    k = pick != 0x7fffffff ? pick : -block_min_i(-last_pos, s_imin);
   }
-  __shared__ int s_last_pos;
-  if (tid == 0) s_last_pos = -1;
-  __syncthreads();
-  if (s_pick == 0x7fffffff) atomicMax(&s_last_pos, last_pos);   // rounding left the target past the chunk
-  __syncthreads();
-  const int k = (s_pick != 0x7fffffff) ? s_pick : s_last_pos;
 
-  // 3. emit
+  // 3. outputs
   const int A = d.A;
+  const int status = s_timeout ? SPEC_REQ_INTERNAL : (failed ? SPEC_REQ_RESIDUAL_EMPTY : 0);
   for (int i = tid; i < p.R; i += kBlock) {
-    int v;
-    if (i < A) v = p.tokens[(size_t)b * G + i];
-    else if (i == A) v = k;
-    else v = -1;
+    int v = -1;
+    if (status == 0) {
+      if (i < A) v = p.tokens[(size_t)b * G + i];
+      else if (i == A) v = k;
+    }
     p.out_tokens[(size_t)b * p.R + i] = v;
   }
-  if (tid == 0) {
-    p.accepted_len[b] = A;
-    p.req_status[b] = 0;
-    if (p.stats) p.stats[((size_t)b * p.R + G) * 4 + 2] = (float)W;
-  }
-}
-
-// Every terminal item of request b has arrived: clear the request's workspace state.
-__device__ __forceinline__ void finish_request(const ChainParams& p, int b) {
-  unsigned long long* w = reinterpret_cast<unsigned long long*>(p.dec + b);
-  clear_u64(w);
-  clear_u64(w + 1);
-  reset_counter(slot(p, b, kSlotTerm));
-}
-
-template <int DT, int QT, bool VEC, bool RESID>
-__device__ void chain_terminal_body(const ChainParams& p, int b, int c, const ChainDecision& d) {
-  const int tid = threadIdx.x;
-  const int A = d.A;
-  const void* lrow = row_ptr<DT>(p.logits, (size_t)b * p.R + A, p.V);
-  const void* qrow = RESID ? row_ptr<QT>(p.q, (size_t)b * p.G + A, p.V) : nullptr;
-  double acc = 0.0;
-  bool bad = false;
-#pragma unroll
-  for (int s = 0; s < kTermSlabs; ++s) {
-    const long e0 = ((long)c * kTermSlabs + s) * kSlab + (long)tid * kVec;
-    float w[8];
-    term_load8<DT, QT, VEC, RESID>(lrow, qrow, e0, p.V, p.c2, d.r_ref, d.inv_z, w, bad);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc += (double)w[k];
-  }
-  if (bad) acc = NAN;
-  __shared__ double s_red[kWavesPerBlock];
-  const int lane = tid & (kWave - 1), wave = wave_id();
-  const double ws = wave_sum_d(acc);
-  if (lane == 0) s_red[wave] = ws;
-  __syncthreads();
-  __shared__ int s_last;
-  if (tid == 0) {
-    const double m = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
-    publish_mass(p.tmass + (size_t)b * p.S2 + c, m);
-    vmem_wait();
-    const unsigned prev = arrive(slot(p, b, kSlotTerm));
-    s_last = (prev == (unsigned)(p.S2 - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  chain_select<DT, QT, VEC, RESID>(p, b, d, lrow, qrow);
-  __syncthreads();
-  for (int j = tid; j < p.S2; j += kBlock) clear_mass(p.tmass + (size_t)b * p.S2 + j);
-  if (tid == 0) finish_request(p, b);
-}
-
-// Terminal item: chunk c of request b's terminal row.
-template <int DT, int QT, bool VEC>
-__device__ void terminal_item(const ChainParams& p, int b, int c) {
-  __shared__ ChainDecision s_dec;
-  if (threadIdx.x == 0) s_dec = await_decision(p, b);
-  __syncthreads();
-  const ChainDecision d = s_dec;
-  if (d.status != 0) {
-    // the request failed (its outputs are written): only count the arrival, so that
-    // the last item can clear the request's state
-    __shared__ int s_last;
-    if (threadIdx.x == 0) {
-      if (d.status == SPEC_REQ_INTERNAL) {   // wait bound hit: report instead of guessing
-        p.accepted_len[b] = -1;
-        p.req_status[b] = SPEC_REQ_INTERNAL;
+  if (p.stats) {
+    // rows 0..A (< G) reached: (m, log Z, p(x), a); row G: (m, log Z) when the bonus row
+    // is reached, W in column 2; everything else NaN, and everything on failure
+    float* st = p.stats + (size_t)b * p.R * 4;
+    for (int i = tid; i < p.R; i += kBlock) {
+      float v[4] = {NAN, NAN, NAN, NAN};
+      const bool reached = status == 0 && (i < G ? i <= A : A == G);
+      if (reached) {
+        const double m_nat = (double)rs.m[i] * p.inv_t;
+        v[0] = (float)m_nat;
+        v[1] = (float)(log(rs.z[i]) + (double)rs.r[i] * kLn2 - m_nat);
+        if (i < G) {
+          v[2] = (float)rs.px[i];
+          v[3] = (float)rs.a[i];
+        }
       }
-      const unsigned prev = arrive(slot(p, b, kSlotTerm));
-      s_last = (prev == (unsigned)(p.S2 - 1));
+      if (i == G && status == 0) v[2] = (float)W;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) st[i * 4 + c] = v[c];
     }
-    __syncthreads();
-    if (s_last && threadIdx.x == 0) finish_request(p, b);
+  }
+  if (tid == 0) {
+    p.accepted_len[b] = status == 0 ? A : -1;
+    p.req_status[b] = status;
+  }
+}
+
+// A failed request (the decision's status is not OK): the selector writes the failure
+// record once every other terminal item has signalled that it is done with the request.
+__device__ void chain_fail(const ChainParams& p, int b, int status) {
+  const int tid = threadIdx.x;
+  __shared__ int s_lost;
+  if (tid == 0) s_lost = 0;
+  __syncthreads();
+  const double* tm = p.tmass + (size_t)b * p.S2;
+  for (int c = tid; c < p.S2 - 1; c += kBlock)
+    if (await_u64(reinterpret_cast<const unsigned long long*>(tm + c)) == 0ull) s_lost = 1;
+  __syncthreads();
+  const int code = s_lost ? SPEC_REQ_INTERNAL : status;
+  for (int i = tid; i < p.R; i += kBlock) p.out_tokens[(size_t)b * p.R + i] = -1;
+  if (p.stats)
+    for (int i = tid; i < p.R * 4; i += kBlock) p.stats[(size_t)b * p.R * 4 + i] = NAN;
+  if (tid == 0) {
+    p.accepted_len[b] = -1;
+    p.req_status[b] = code;
+  }
+}
+
+// Every other terminal item of request b has published its chunk's mass, and so has
+// finished reading the request's summaries and gather records: return them all to zero.
+__device__ void chain_clear(const ChainParams& p, int b) {
+  const int tid = threadIdx.x;
+  float2* part_b = p.part + (size_t)b * p.R * p.SL;
+  for (int j = tid; j < p.R * p.SL; j += kBlock) clear_f2(part_b + j);
+  for (int j = tid; j < 3 * p.G; j += kBlock) clear_u64(gather_rec(p, b, 0) + j);
+  for (int j = tid; j < p.S2; j += kBlock) clear_mass(p.tmass + (size_t)b * p.S2 + j);
+}
+
+// Terminal item with a valid decision: chunk c of request b's terminal row; the last
+// chunk's item selects.
+template <int DT, int QT, bool VEC, bool RESID>
+__device__ void terminal_body(const ChainParams& p, int b, int c, const ChainDecision& d, const RowState& rs) {
+  const void* lrow = row_ptr<DT>(p.logits, (size_t)b * p.R + d.A, p.V);
+  const void* qrow = RESID ? row_ptr<QT>(p.q, (size_t)b * p.G + d.A, p.V) : nullptr;
+  float w[kTermSlabs][8];
+  bool bad = false;
+  term_chunk<DT, QT, VEC, RESID>(p, lrow, qrow, c, d, w, bad);
+  const double m = block_mass(w, bad);
+  if (c != p.S2 - 1) {
+    if (threadIdx.x == 0) publish_mass(p.tmass + (size_t)b * p.S2 + c, m);
     return;
   }
-  if (d.A < p.G) chain_terminal_body<DT, QT, VEC, true>(p, b, c, d);
-  else chain_terminal_body<DT, QT, VEC, false>(p, b, c, d);
+  chain_select<DT, QT, VEC, RESID>(p, b, d, rs, m, lrow, qrow);
+  __syncthreads();
+  chain_clear(p, b);
 }
 
-// Statistics items first, then terminal items, each request-major.
+template <int DT, int QT, bool VEC>
+__device__ void terminal_item(const ChainParams& p, int b, int c) {
+  __shared__ RowState s_rs;
+  __shared__ ChainDecision s_dec;
+  chain_decide<DT>(p, b, s_rs, s_dec);
+  const ChainDecision d = s_dec;
+  if (d.status != 0) {
+    if (c != p.S2 - 1) {
+      // no mass to contribute: a NaN marker says only that this item is done with the
+      // request's words
+      if (threadIdx.x == 0) publish_mass(p.tmass + (size_t)b * p.S2 + c, NAN);
+      return;
+    }
+    chain_fail(p, b, d.status);
+    __syncthreads();
+    chain_clear(p, b);
+    return;
+  }
+  if (d.A < p.G) terminal_body<DT, QT, VEC, true>(p, b, c, d, s_rs);
+  else terminal_body<DT, QT, VEC, false>(p, b, c, d, s_rs);
+}
+
+// Block order: groups g = 0 .. B + LAG - 1, group g holding the statistics items of
+// request g (if g < B) followed by the terminal items of request g - LAG (if g >= LAG), so a
+// request's terminal items follow its statistics items by LAG requests' worth of blocks.
+// LAG = B puts every statistics item first.
+struct Item { int terminal, b, idx; };
+__device__ __forceinline__ Item block_item(const ChainParams& p, long t) {
+  const long Sb = (long)p.R * p.SL, Tb = p.S2, L = p.LAG;
+  const long n1 = L * Sb, n2 = ((long)p.B - L) * (Sb + Tb);
+  Item it;
+  if (t < n1) {
+    it.terminal = 0; it.b = (int)(t / Sb); it.idx = (int)(t % Sb);
+  } else if (t < n1 + n2) {
+    const long u = t - n1, g = L + u / (Sb + Tb), o = u % (Sb + Tb);
+    if (o < Sb) { it.terminal = 0; it.b = (int)g; it.idx = (int)o; }
+    else { it.terminal = 1; it.b = (int)(g - L); it.idx = (int)(o - Sb); }
+  } else {
+    const long u = t - n1 - n2;
+    it.terminal = 1; it.b = (int)((long)p.B - L + u / Tb); it.idx = (int)(u % Tb);
+  }
+  return it;
+}
+
 template <int DT, int QT, bool VEC>
 __global__ __launch_bounds__(kBlock) void chain_kernel(ChainParams p) {
-  const long t = blockIdx.x, Sb = (long)p.R * p.SL, n_stats = (long)p.B * Sb;
-  if (t < n_stats) {
-    const int b = (int)(t / Sb), o = (int)(t % Sb);
-    stats_item<DT, VEC>(p, b, o / p.SL, o % p.SL);
-  } else {
-    const long u = t - n_stats;
-    terminal_item<DT, QT, VEC>(p, (int)(u / p.S2), (int)(u % p.S2));
-  }
+  const Item it = block_item(p, blockIdx.x);
+  if (it.terminal) terminal_item<DT, QT, VEC>(p, it.b, it.idx);
+  else stats_item<DT, VEC>(p, it.b, it.idx / p.SL, it.idx % p.SL);
 }
 
+// Lag between a request's statistics and terminal items, in rounds of resident blocks:
+// its terminal items start about that many block generations after its statistics
+// items, when their summaries are normally published.  0 puts every statistics item
+// first.
+#ifndef SPEC_CHAIN_LAG_TENTHS
+#define SPEC_CHAIN_LAG_TENTHS 20
+#endif
+constexpr long kLagTenths = SPEC_CHAIN_LAG_TENTHS;   // in tenths of a round
+
 template <int DT, int QT, bool VEC>
-hipError_t launch_typed(const ChainParams& p, hipStream_t s) {
+hipError_t launch_typed(ChainParams p, hipStream_t s) {
+  long lag = p.B;
+  if (kLagTenths > 0) {
+    static int s_resident[64] = {0};   // resident blocks per device ordinal; 0 = not queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (s_resident[dev] == 0) {
+      int per_cu = 0, cus = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel<DT, QT, VEC>, kBlock, 0) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipErrorInvalidValue;
+      s_resident[dev] = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
+    }
+    const long per_req = (long)p.R * p.SL + p.S2;
+    lag = (kLagTenths * s_resident[dev] / 10 + per_req - 1) / per_req;
+    if (lag > p.B) lag = p.B;
+  }
+  p.LAG = (int)lag;
   const unsigned long long blocks = (unsigned long long)p.B * ((unsigned long long)p.R * p.SL + p.S2);  // == chain_blocks
   chain_kernel<DT, QT, VEC><<<dim3((unsigned)blocks), dim3(kBlock), 0, s>>>(p);
   return hipGetLastError();

@@ -150,6 +150,21 @@ __device__ __forceinline__ double wave_incl_scan_d(double v, int lane) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
+// Block-wide minimum of one int per thread, returned to every thread: a DPP tree per
+// wave and one LDS word per wave (no contended LDS atomics).  `scratch` holds >=
+// kWavesPerBlock ints.  Contains two barriers.
+__device__ __forceinline__ int block_min_i(int v, int* scratch) {
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const int w = wave_min_i(v);
+  if (lane == 0) scratch[wave] = w;
+  __syncthreads();
+  int r = scratch[0];
+#pragma unroll
+  for (int k = 1; k < kWavesPerBlock; ++k) r = min(r, scratch[k]);
+  __syncthreads();
+  return r;
+}
+
 // Block-wide exclusive prefix (fp64) of one value per thread; returns the exclusive
 // prefix and writes the block total to *total.  `scratch` holds >= kWavesPerBlock doubles.
 __device__ __forceinline__ double block_excl_scan_d(double v, double* scratch, double* total) {

@@ -8,7 +8,8 @@
 
 namespace sv {
 
-// Per-request decision of the chain statistics pass, read by the terminal pass.
+// Per-request decision of the chain verifier: every terminal block of a request computes
+// it from the request's published summaries.
 struct ChainDecision {
   int32_t A;        // first rejected draft (gamma if all accepted); -1 on error
   int32_t status;   // SPEC_REQ_*
@@ -26,19 +27,15 @@ struct ChainParams {
   int32_t* req_status;       // [B]
   float* stats;              // [B, R, 4] or null
   // workspace
-  unsigned* global;          // [0] next work ticket, [1] blocks that have left
-  float2* part;              // [B*R*PP] wave summaries (raw max, Z)
-  unsigned* counters;        // per-request slots: [b*4 + 0] statistics arrivals,
-                             // [b*4 + 1] terminal arrivals, [b*4 + 2] decision ready
-  ChainDecision* dec;        // [B]
+  float2* part;              // [B*R*SL] block summaries (raw max, Z)
   unsigned long long* gath;  // [B*G*3] draft token, its logit, its draft probability
   double* tmass;             // [B*S2] terminal chunk masses
   int B, G, R, V;
   int P;                     // wave chunks per row = ceil(V / 2048)
   int CPW;                   // wave chunks each wave streams per slice
   int SL;                    // statistics slices (blocks) per row = ceil(P / (4 * CPW))
-  int PP;                    // summaries per row = 4 * SL (one per wave)
   int S2;                    // terminal chunks per row = ceil(V / kTermChunk)
+  int LAG;                   // requests between a request's statistics and terminal items
   int q_dtype;
   float c2;                  // fp32(log2(e) / T)
   double inv_t;              // 1 / T, T widened exactly from fp32
@@ -125,18 +122,21 @@ inline unsigned* request_counters(void* ws) {
 // slot s of request b: request_counters(ws)[b * kCounterSlots + s]
 
 struct ChainLayout {
-  size_t part, dec, gath, tmass, total;
+  size_t part, gath, tmass, total;
 };
 // The chain's statistics pass uses finer slices than the other streaming passes: its
 // terminal items fill the statistics tail, which shrinks as the slices do.
-constexpr long kChainTargetBlocks = 4 * kTargetBlocks;
+#ifndef SPEC_CHAIN_TARGET_BLOCKS
+#define SPEC_CHAIN_TARGET_BLOCKS 4096
+#endif
+constexpr long kChainTargetBlocks = SPEC_CHAIN_TARGET_BLOCKS;
+// The chain uses no counters: its regions start after the global header.
 inline ChainLayout chain_layout(long B, long G, long V) {
   const long R = G + 1, S2 = (V + kTermChunk - 1) / kTermChunk;
-  const long PP = slicing(B * R, V, kChainTargetBlocks).PP;
+  const long SL = slicing(B * R, V, kChainTargetBlocks).SL;
   ChainLayout L;
-  size_t o = counter_bytes(B);
-  L.part = o;   o = align256(o + sizeof(float2) * B * R * PP);
-  L.dec = o;    o = align256(o + sizeof(ChainDecision) * B);
+  size_t o = kGlobalCounterBytes;
+  L.part = o;   o = align256(o + sizeof(float2) * B * R * SL);
   L.gath = o;   o = align256(o + sizeof(unsigned long long) * 3 * B * G);
   L.tmass = o;  o = align256(o + sizeof(double) * B * S2);
   L.total = o;

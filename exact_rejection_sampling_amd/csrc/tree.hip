@@ -52,10 +52,9 @@ __device__ int sample_row(const TreeParams& p, const float2* part, const void* r
   __shared__ double s_scan[kWavesPerBlock];
   __shared__ float s_r;
   __shared__ double s_z;
-  __shared__ int s_pick;
+  __shared__ int s_imin[kWavesPerBlock];
   __shared__ double s_before;
   __shared__ double s_total;
-  __shared__ int s_last_pos;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   const float c2 = p.c2;
 
@@ -85,26 +84,25 @@ __device__ int sample_row(const TreeParams& p, const float2* part, const void* r
     run_end += (double)s.y * exp2((double)(s.x * c2) - (double)R);
   }
   if (c_lo < c_hi && c_hi == p.P) s_total = run_end;
-  if (tid == 0) s_pick = kNoPick;
   __syncthreads();
   const double Z = s_total;
   if (!(isfinite(Z) && Z > 0.0)) { *status = SPEC_REQ_NONFINITE; return -1; }
   if (!(uv >= 0.0f && uv < 1.0f)) { *status = SPEC_REQ_BADUNIFORM; return -1; }
   const double t = (double)uv * Z;
+  int cand = kNoPick;          // first chunk of this thread's run whose running value passes t
   {
     double run = excl;
     for (int c = c_lo; c < c_hi; ++c) {
       const float2 s = summary<DT, VEC, PUBLISHED>(part, c);
       const double nxt = run + (double)s.y * exp2((double)(s.x * c2) - (double)R);
-      if (nxt > t) { atomicMin(&s_pick, c); break; }
+      if (nxt > t) { cand = c; break; }
       run = nxt;
     }
   }
-  __syncthreads();
-  // a chunk is always found (t < Z and the last running value is Z); clamp regardless
-  const int cstar = s_pick == kNoPick ? p.P - 1 : s_pick;
   if (tid == 0) s_before = 0.0;
-  __syncthreads();
+  // a chunk is always found (t < Z and the last running value is Z); clamp regardless
+  int cstar = block_min_i(cand, s_imin);
+  if (cstar == kNoPick) cstar = p.P - 1;
   if (cstar >= c_lo && cstar < c_hi) {
     double run = excl;
     for (int c = c_lo; c < cstar; ++c) {
@@ -113,8 +111,6 @@ __device__ int sample_row(const TreeParams& p, const float2* part, const void* r
     }
     s_before = run;
   }
-  __syncthreads();
-  if (tid == 0) { s_pick = kNoPick; s_last_pos = -1; }
   __syncthreads();
 
   // rescan chunk cstar (one slab) in the chunk's own units 2^(l c2 - r_c)
@@ -136,14 +132,14 @@ __device__ int sample_row(const TreeParams& p, const float2* part, const void* r
   }
   double slab_total;
   const double off = block_excl_scan_d(acc, s_scan, &slab_total);
+  int pick = kNoPick;
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-    if (off + incl[k] > rem && e[k] > 0.0f) { atomicMin(&s_pick, (int)(e0 + k)); break; }
-  __syncthreads();
-  if (s_pick == kNoPick) atomicMax(&s_last_pos, last_pos);
-  __syncthreads();
-  const int y = (s_pick != kNoPick) ? s_pick : s_last_pos;
-  __syncthreads();
+  for (int k = 7; k >= 0; --k)
+    if (off + incl[k] > rem && e[k] > 0.0f) pick = (int)(e0 + k);
+  // the first position whose running value passes the target; rounding may leave the
+  // target just past the chunk's last positive weight: then take that weight
+  pick = block_min_i(pick, s_imin);
+  const int y = pick != kNoPick ? pick : -block_min_i(-last_pos, s_imin);
   *status = 0;
   return y;
 }
@@ -164,7 +160,7 @@ __device__ void summarize_row(const TreeParams& p, float2* part, const void* row
 template <int DT, bool VEC>
 __device__ void tree_walk(const TreeParams& p, int b) {
   __shared__ int s_bad;
-  __shared__ int s_child;
+  __shared__ int s_imin[kWavesPerBlock];
   const int tid = threadIdx.x;
   const int N = p.N;
   const int32_t* par = p.parents + (size_t)b * N;
@@ -188,13 +184,10 @@ __device__ void tree_walk(const TreeParams& p, int b) {
     const int y = v == 0 ? sample_row<DT, VEC, true>(p, p.part + (size_t)b * p.P, row, uv, &status)
                          : sample_row<DT, VEC, false>(p, deep, row, uv, &status);
     if (status != 0) { tree_fail(p, b, status); return; }
-    if (tid == 0) s_child = kNoPick;
-    __syncthreads();
+    int cand = kNoPick;           // this thread's lowest matching child (c rises)
     for (int c = v + 1 + tid; c < N; c += kBlock)
-      if (par[c] == v && tok[c] == y) atomicMin(&s_child, c);
-    __syncthreads();
-    const int child = s_child;
-    __syncthreads();
+      if (cand == kNoPick && par[c] == v && tok[c] == y) cand = c;
+    const int child = block_min_i(cand, s_imin);
     if (child == kNoPick) {
       for (int i = tid; i < N; i += kBlock) {
         if (i > depth) {
