@@ -175,13 +175,15 @@ spec_status spec_verify_tree(const void* node_logits, int logit_dtype, const int
   p.out_nodes = out_nodes;
   p.req_status = req_status;
   p.part = reinterpret_cast<float2*>(ws + L.part);
-  p.part_deep = reinterpret_cast<float2*>(ws + L.part_deep);
+  p.deep = reinterpret_cast<float2*>(ws + L.deep);
+  p.order = reinterpret_cast<unsigned long long*>(ws + L.order);
   p.counters = sv::request_counters(workspace);
   p.B = B;
   p.N = N;
   p.V = V;
   p.P = chunks(V, sv::kWaveChunk);
   p.WG1 = chunks(p.P, sv::kWavesPerBlock);
+  p.WH = chunks(p.P, sv::kTreeHelperChunks);
   p.c2 = static_cast<float>(kLog2e / static_cast<double>(temperature));
   const bool vec = (V % 8 == 0) && aligned16(node_logits);
   return sv::launch_tree(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;

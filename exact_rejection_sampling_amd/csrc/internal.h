@@ -100,11 +100,18 @@ struct TreeParams {
   int32_t* out_nodes;
   int32_t* req_status;
   float2* part;              // [B*P] root-row summaries, published across blocks
-  float2* part_deep;         // [B*P] summaries of deeper rows (walking block only)
-  unsigned* counters;        // per-request slots: [b*4 + 0] arrivals
-  int B, N, V, P, WG1;
+  float2* deep;              // [B*2*P] summaries of deeper rows from the helper blocks,
+                             // double-buffered by order generation
+  unsigned long long* order; // [B] the walking block's order to its helpers
+  unsigned* counters;        // per-request slots: [b*4 + 0] root arrivals, [b*4 + 1] helpers gone
+  int B, N, V, P, WG1, WH;
   float c2;
 };
+
+// Helper blocks of a tree request: each summarizes kTreeHelperChunks chunks of an ordered
+// row (its four waves two chunks each, loads in flight together).
+constexpr int kTreeHelperBatch = 2;
+constexpr int kTreeHelperChunks = 4 * kTreeHelperBatch;
 
 // Workspace carving: 256 bytes of global counters, kCounterSlots 32-bit counters per
 // request, then the data regions, each on a 256-byte boundary.  Every call returns all
@@ -154,14 +161,15 @@ inline GreedyLayout greedy_layout(long B, long G, long V) {
   return L;
 }
 
-struct TreeLayout { size_t part, part_deep, total; };
+struct TreeLayout { size_t part, deep, order, total; };
 inline TreeLayout tree_layout(long B, long N, long V) {
   (void)N;
   const long P = (V + 2047) / 2048;
   TreeLayout L;
   size_t o = counter_bytes(B);
-  L.part = o;       o = align256(o + sizeof(float2) * B * P);
-  L.part_deep = o;  o = align256(o + sizeof(float2) * B * P);
+  L.part = o;   o = align256(o + sizeof(float2) * B * P);
+  L.deep = o;   o = align256(o + sizeof(float2) * B * 2 * P);
+  L.order = o;  o = align256(o + sizeof(unsigned long long) * B);
   L.total = o;
   return L;
 }
@@ -178,7 +186,8 @@ inline unsigned long long greedy_blocks(long B, long G, long V) {
 }
 inline unsigned long long tree_blocks(long B, long V) {
   const long P = (V + 2047) / 2048;
-  return (unsigned long long)B * ((P + kWavesPerBlock - 1) / kWavesPerBlock);
+  return (unsigned long long)B * ((P + kWavesPerBlock - 1) / kWavesPerBlock +
+                                  (P + kTreeHelperChunks - 1) / kTreeHelperChunks);
 }
 inline bool grid_fits(unsigned long long blocks) { return blocks <= 0xffffffffull / kBlock; }
 

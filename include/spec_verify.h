@@ -96,7 +96,8 @@ enum {
   SPEC_REQ_BADTREE = 6,         /* parents[0] != -1, a parents[v] outside [0, v), or a
                                    non-root node token outside [0, V) ([M7.7] §0x0F) */
   SPEC_REQ_INTERNAL = 7         /* an internal wait between blocks hit its bound (not
-                                   expected; the request's outputs are not valid) */
+                                   expected; the request's outputs are not valid, and the
+                                   workspace must be zero-filled again before reuse) */
 };
 
 /* ------------------------------------------------------------------ chain ---
