@@ -134,16 +134,14 @@ spec_status spec_verify_greedy(const void* target_logits, int logit_dtype, const
   p.out_tokens = out_tokens;
   p.req_status = req_status;
   p.part = reinterpret_cast<unsigned long long*>(ws + L.part);
-  p.counters = sv::request_counters(workspace);
   p.B = B;
   p.G = gamma;
   p.R = gamma + 1;
   p.V = V;
-  const sv::Slicing sl = sv::slicing((long)B * (gamma + 1), V);
+  const sv::Slicing sl = sv::slicing((long)B * (gamma + 1), V, sv::kGreedyTargetBlocks);
   p.P = sl.P;
   p.CPW = sl.CPW;
   p.SL = sl.SL;
-  p.PP = sl.PP;
   const bool vec = (V % 8 == 0) && aligned16(target_logits);
   return sv::launch_greedy(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }

@@ -1,11 +1,21 @@
 // Greedy argmax-match verification (spec_verify_greedy).
 //
-// One kernel: each wave streams a 2048-element chunk of a target row and writes the
-// chunk's maximum, the lowest index attaining it, and whether the chunk holds a NaN.
-// The last block to finish a request combines the chunks of every row (max, then the
-// lowest index among the chunks holding it) and compares the argmaxes with the draft
-// tokens in order: the emitted tokens are the matching prefix plus the target argmax at
-// the first mismatch (or at the bonus row).
+// One launch, one block per work item, the item chosen by blockIdx (block_item): for each
+// request, (gamma+1)*SL streaming items and one decider, the decider placed a fixed lag of
+// blocks after its request's streaming items.
+//  * streaming item (row, slice): the block's four waves stream a slice of one target row
+//    with 16-byte non-temporal loads, keeping per lane the maximum and the lowest position
+//    holding it; lanes and waves merge, and the block publishes one summary for the slice
+//    (max, lowest index attaining it, NaN if the slice holds a NaN).  It never waits.
+//  * decider (request): reads every summary of its request as soon as it is published,
+//    combines each row's slices (the max, then the lowest index among the slices holding
+//    it), compares the argmaxes with the draft tokens in order and emits the matching
+//    prefix plus the target argmax at the first mismatch (or at the bonus row).  It then
+//    returns the summaries to zero.
+// Waits: a decider waits only for its request's streaming items, whose block indices are
+// all lower; the workgroups of a launch are dispatched in index order, so those blocks are
+// running or done and the wait ends.  It is bounded all the same: a summary that does not
+// arrive in time makes the request report SPEC_REQ_INTERNAL.
 //
 // Method: [M7.1] "M7.1 - Speculative Decoding: Draft, Verify, Accept, Reject" §0x02D
 // (longest-prefix validation is exact for greedy decoding); [Tiny] "Exact Speculative
@@ -65,43 +75,85 @@ __device__ __forceinline__ GreedyPart unpack(unsigned long long b) {
   return g;
 }
 
+// Streaming item: slice `slice` of row i of request b.
+template <int DT, bool VEC>
+__device__ void stream_item(const GreedyParams& p, int b, int i, int slice) {
+  __shared__ GreedyPart s_w[kWavesPerBlock];
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const size_t rowid = (size_t)b * p.R + i;
+  const long first = (long)slice * kWavesPerBlock * p.CPW + wave;
+  const GreedyPart g = wave_row_argmax<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, p.P, first,
+                                                kWavesPerBlock, p.CPW, lane);
+  if (lane == 0) s_w[wave] = g;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // the slice's maximum, then the lowest position among the waves holding it (waves
+    // visit interleaved chunks, so positions do not follow wave order); NaN if any wave
+    // saw one
+    float M = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      nan |= (s_w[w].m != s_w[w].m);
+      M = fmaxf(M, s_w[w].m);
+    }
+    int idx = 0x7fffffff;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w)
+      if (s_w[w].m == M) idx = min(idx, s_w[w].idx);
+    GreedyPart out;
+    out.m = nan ? __uint_as_float(0x7fc00000u) : M;
+    out.idx = idx;
+    publish_u64(p.part + rowid * p.SL + slice, pack(out));
+  }
+}
+
+// Decider of request b.
 __device__ void greedy_decide(const GreedyParams& p, int b) {
   __shared__ int s_arg[SPEC_MAX_GAMMA + 1];
   __shared__ int s_bad[SPEC_MAX_GAMMA + 1];
-  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  __shared__ int s_lost;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+  unsigned long long* part_b = p.part + (size_t)b * p.R * p.SL;
+  if (tid == 0) s_lost = 0;
+  // wave 0's draft tokens, fetched while the summaries are awaited
+  int x = 0;
+  if (wave == 0 && lane < p.G) x = p.tokens[(size_t)b * p.G + lane];
+  __syncthreads();
   for (int i = wave; i < p.R; i += kWavesPerBlock) {
-    const unsigned long long* part = p.part + ((size_t)b * p.R + i) * p.PP;
+    const unsigned long long* part = part_b + (size_t)i * p.SL;
     float m = -INFINITY;
-    int nan = 0;
-    for (int j = lane; j < p.PP; j += kWave) {
-      const GreedyPart g = unpack(await_u64(part + j));
-      m = fmaxf(m, g.m);
+    int idx = 0x7fffffff;
+    bool nan = false, lost = false;
+    // lane j takes slices j, j + 64, ...: slices rise with position, so a lane's lowest
+    // position at its own maximum is its first slice holding that maximum
+    for (int j = lane; j < p.SL; j += kWave) {
+      const unsigned long long bits = await_u64(part + j);
+      lost |= (bits == 0ull);
+      const GreedyPart g = unpack(bits);
       nan |= (g.m != g.m);
+      if (g.m > m) {
+        m = g.m;
+        idx = g.idx;
+      }
     }
     const float M = wave_max(m);
-    int idx = 0x7fffffff;
-    for (int j = lane; j < p.PP; j += kWave) {
-      const GreedyPart g = unpack(await_u64(part + j));
-      if (g.m == M) idx = min(idx, g.idx);
-    }
-    idx = wave_min_i(idx);
-    const bool any_nan = wave_any(nan != 0);
+    const int arg = wave_min_i(m == M ? idx : 0x7fffffff);
+    const bool any_nan = wave_any(nan);
+    if (wave_any(lost) && lane == 0) s_lost = 1;
     if (lane == 0) {
-      s_arg[i] = idx;
+      s_arg[i] = arg;
       s_bad[i] = any_nan || !(M > -INFINITY && M < INFINITY);
     }
   }
   __syncthreads();
-  {
-    unsigned long long* part = p.part + (size_t)b * p.R * p.PP;     // consumed: back to zero
-    for (int j = threadIdx.x; j < p.R * p.PP; j += kBlock) clear_u64(part + j);
-  }
+  // the summaries are consumed: return them to zero (every call leaves the workspace zeroed)
+  for (int j = tid; j < p.R * p.SL; j += kBlock) clear_u64(part_b + j);
   if (wave != 0) return;
   const int G = p.G;
   int code = 0;
   bool mismatch = false;
   if (lane < G) {
-    const int x = p.tokens[(size_t)b * G + lane];
     if (s_bad[lane]) code = SPEC_REQ_NONFINITE;
     else if (x < 0 || x >= p.V) code = SPEC_REQ_BADTOKEN;
     else mismatch = (x != s_arg[lane]);
@@ -110,6 +162,7 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
   const int A = stop ? (__ffsll((long long)stop) - 1) : G;
   int status = __shfl(code, A < G ? A : 0, kWave);
   if (A == G) status = s_bad[G] ? SPEC_REQ_NONFINITE : 0;
+  if (s_lost) status = SPEC_REQ_INTERNAL;
   for (int i = lane; i < p.R; i += kWave) {
     int v = -1;
     if (status == 0) {
@@ -124,34 +177,59 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
   }
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void greedy_kernel(GreedyParams p) {
-  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
-  const size_t rowid = blockIdx.x / p.SL;
-  const int slice = blockIdx.x % p.SL;
-  const int b = (int)(rowid / p.R);
-  {
-    const long first = (long)slice * kWavesPerBlock * p.CPW + wave;
-    const GreedyPart g = wave_row_argmax<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, p.P, first,
-                                                  kWavesPerBlock, p.CPW, lane);
-    if (lane == 0) publish_u64(p.part + rowid * p.PP + slice * kWavesPerBlock + wave, pack(g));
+// Block order: groups g = 0 .. B + LAG - 1, group g holding the streaming items of
+// request g (if g < B) followed by the decider of request g - LAG (if g >= LAG).
+struct Item { int decider, b, idx; };
+__device__ __forceinline__ Item block_item(const GreedyParams& p, long t) {
+  const long Sb = (long)p.R * p.SL, L = p.LAG;
+  const long n1 = L * Sb, n2 = ((long)p.B - L) * (Sb + 1);
+  Item it;
+  if (t < n1) {
+    it.decider = 0; it.b = (int)(t / Sb); it.idx = (int)(t % Sb);
+  } else if (t < n1 + n2) {
+    const long u = t - n1, g = L + u / (Sb + 1), o = u % (Sb + 1);
+    if (o < Sb) { it.decider = 0; it.b = (int)g; it.idx = (int)o; }
+    else { it.decider = 1; it.b = (int)(g - L); it.idx = 0; }
+  } else {
+    it.decider = 1; it.b = (int)((long)p.B - L + (t - n1 - n2)); it.idx = 0;
   }
-  __syncthreads();   // every wave's summary store has completed
-  __shared__ int s_last;
-  if (threadIdx.x == 0) {
-    const unsigned prev = arrive(&p.counters[(size_t)b * kCounterSlots + 0]);
-    s_last = (prev == (unsigned)(p.R * p.SL - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  greedy_decide(p, b);
-  if (threadIdx.x == 0) reset_counter(&p.counters[(size_t)b * kCounterSlots + 0]);
+  return it;
 }
 
 template <int DT, bool VEC>
-hipError_t launch_typed(const GreedyParams& p, hipStream_t s) {
-  const unsigned g = (unsigned)((size_t)p.B * p.R * p.SL);
-  greedy_kernel<DT, VEC><<<dim3(g), dim3(kBlock), 0, s>>>(p);
+__global__ __launch_bounds__(kBlock) void greedy_kernel(GreedyParams p) {
+  const Item it = block_item(p, blockIdx.x);
+  if (it.decider) greedy_decide(p, it.b);
+  else stream_item<DT, VEC>(p, it.b, it.idx / p.SL, it.idx % p.SL);
+}
+
+// Lag between a request's streaming items and its decider, in tenths of a round of
+// resident blocks: the decider starts about that many block generations later, when the
+// request's summaries are normally published.
+#ifndef SPEC_GREEDY_LAG_TENTHS
+#define SPEC_GREEDY_LAG_TENTHS 20
+#endif
+constexpr long kGreedyLagTenths = SPEC_GREEDY_LAG_TENTHS;
+
+template <int DT, bool VEC>
+hipError_t launch_typed(GreedyParams p, hipStream_t s) {
+  static int s_resident[64] = {0};   // resident blocks per device ordinal; 0 = not queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (s_resident[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, greedy_kernel<DT, VEC>, kBlock, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidValue;
+    s_resident[dev] = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
+  }
+  const long per_req = (long)p.R * p.SL + 1;
+  long lag = (kGreedyLagTenths * s_resident[dev] / 10 + per_req - 1) / per_req;
+  if (lag < 1) lag = 1;
+  if (lag > p.B) lag = p.B;
+  p.LAG = (int)lag;
+  const unsigned long long g = (unsigned long long)p.B * ((unsigned long long)p.R * p.SL + 1);  // == greedy_blocks
+  greedy_kernel<DT, VEC><<<dim3((unsigned)g), dim3(kBlock), 0, s>>>(p);
   return hipGetLastError();
 }
 

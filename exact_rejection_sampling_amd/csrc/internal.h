@@ -56,9 +56,9 @@ struct GreedyParams {
   int32_t* accepted_len;
   int32_t* out_tokens;
   int32_t* req_status;
-  unsigned long long* part;  // [B*R*PP] packed GreedyPart
-  unsigned* counters;        // per-request slots: [b*4 + 0] arrivals
-  int B, G, R, V, P, CPW, SL, PP;
+  unsigned long long* part;  // [B*R*SL] packed GreedyPart, one per slice
+  int B, G, R, V, P, CPW, SL;
+  int LAG;                   // requests between a request's streaming blocks and its decider
 };
 
 #ifdef SPEC_FORCE_CPW
@@ -151,12 +151,18 @@ inline ChainLayout chain_layout(long B, long G, long V) {
 }
 
 struct GreedyLayout { size_t part, total; };
+// Greedy slicing: finer than the default, since a streaming block no longer waits on
+// anything after it has streamed.
+#ifndef SPEC_GREEDY_TARGET_BLOCKS
+#define SPEC_GREEDY_TARGET_BLOCKS 16384
+#endif
+constexpr long kGreedyTargetBlocks = SPEC_GREEDY_TARGET_BLOCKS;
 inline GreedyLayout greedy_layout(long B, long G, long V) {
   const long R = G + 1;
-  const long PP = slicing(B * R, V).PP;
+  const long SL = slicing(B * R, V, kGreedyTargetBlocks).SL;
   GreedyLayout L;
-  size_t o = counter_bytes(B);
-  L.part = o;  o = align256(o + sizeof(unsigned long long) * B * R * PP);
+  size_t o = kGlobalCounterBytes;
+  L.part = o;  o = align256(o + sizeof(unsigned long long) * B * R * SL);
   L.total = o;
   return L;
 }
@@ -182,7 +188,7 @@ inline unsigned long long chain_blocks(long B, long G, long V) {
 }
 inline unsigned long long greedy_blocks(long B, long G, long V) {
   const long R = G + 1;
-  return (unsigned long long)B * R * slicing(B * R, V).SL;
+  return (unsigned long long)B * ((unsigned long long)R * slicing(B * R, V, kGreedyTargetBlocks).SL + 1);
 }
 inline unsigned long long tree_blocks(long B, long V) {
   const long P = (V + 2047) / 2048;
