@@ -126,12 +126,13 @@ def bench_greedy(args, torch, sv, synth):
     calls = [sv.prepare_greedy(s[0], s[1], workspace_tensor=ws) for s in sets]
     span, per = time_calls(calls, max(20, args.steps // 4), args.warmup, stream)
     alg = B * (G + 1) * V * 2 + B * G * 4 + B * (G + 2) * 8
-    mean = float(per.mean())
+    launch = span / len(per)       # seconds per launch over the timed region
     del sets, calls
+    trec = traffic_record("greedy_kernel_config4")
     return dict(workload="greedy B=256 gamma=8 V=128256 bf16", positions_per_s=B * (G + 1) * len(per) / span,
-                mean_launch_us=mean * 1e3, median_launch_us=float(np.median(per)) * 1e3,
-                achieved_gbs=alg / (mean * 1e-3) / 1e9, frac=alg / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                alg_bytes=alg, traffic=traffic_record("greedy_kernel_config4"))
+                launch_us=launch * 1e6, evented_launch_mean_us=float(per.mean()) * 1e3,
+                achieved_gbs=alg / launch / 1e9, frac=alg / launch / 1e9 / HBM_PEAK_GBS, alg_bytes=alg,
+                traffic_gbs=None if trec is None else trec["bytes_per_launch"] / launch / 1e9)
 
 
 def bench_tree(args, torch, sv, synth):
@@ -151,12 +152,12 @@ def bench_tree(args, torch, sv, synth):
     acc = calls[0].out["accepted_len"].cpu().numpy()
     visited = int((acc + 1).sum())
     alg = visited * V * 2 + B * N * 12
-    mean = float(per.mean())
+    launch = span / len(per)
     del sets, calls
     return dict(workload="tree B=32 N=63 V=152064 bf16 T=1", nodes_per_s=B * N * len(per) / span,
-                mean_launch_us=mean * 1e3, median_launch_us=float(np.median(per)) * 1e3,
-                visited_rows=visited, achieved_gbs_visited=alg / (mean * 1e-3) / 1e9,
-                dense_equivalent_gbs=B * N * V * 2 / (mean * 1e-3) / 1e9)
+                launch_us=launch * 1e6, evented_launch_mean_us=float(per.mean()) * 1e3,
+                visited_rows=visited, achieved_gbs_visited=alg / launch / 1e9,
+                dense_equivalent_gbs=B * N * V * 2 / launch / 1e9)
 
 
 _CPU_X = None   # the workload a forked oracle worker reads
@@ -235,11 +236,13 @@ def main():
     log("[bench] chain headline workload")
     c = bench_chain(args, torch, sv, synth)
     value = c["positions"] * args.steps / c["span"]
-    achieved = c["alg_bytes"] / (c["mean_ms"] * 1e-3) / 1e9     # per launch: one launch per call
+    # the timed region's average launch duration: one launch per call, back to back
+    launch_ms = c["span"] * 1e3 / args.steps
+    achieved = c["alg_bytes"] / (launch_ms * 1e-3) / 1e9
     # traffic: HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counters (scaled
     # by what the counters read for device copies of known size), over the same launch time
     trec = traffic_record("chain_kernel_config3")
-    traffic = None if trec is None else trec["bytes_per_launch"] / (c["mean_ms"] * 1e-3) / 1e9
+    traffic = None if trec is None else trec["bytes_per_launch"] / (launch_ms * 1e-3) / 1e9
     line = dict(
         metric="verified positions/s + achieved HBM GB/s (% peak), B=64 gamma=5 V=128256 bf16",
         value=value, unit="verified positions/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -251,7 +254,8 @@ def main():
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=traffic,
                       kernel="chain_kernel (one launch per spec_verify_chain call)",
-                      mean_launch_us=c["mean_ms"] * 1e3, median_launch_us=c["med_ms"] * 1e3,
+                      launch_us=launch_ms * 1e3,
+                      evented_launch_mean_us=c["mean_ms"] * 1e3, evented_launch_median_us=c["med_ms"] * 1e3,
                       p10_us=float(np.percentile(c["per"], 10)) * 1e3,
                       p90_us=float(np.percentile(c["per"], 90)) * 1e3,
                       alg_bytes_per_call=c["alg_bytes"], rejecting_requests=c["n_rej"],
