@@ -23,6 +23,7 @@ from .numerics import (NONFINITE, BADTOKEN, BADUNIFORM, QZERO, RESIDUAL_EMPTY, B
 from .chain import verify_chain, verify_chain_one, FLAG_WINDOW
 from .greedy import verify_greedy, verify_greedy_one
 from .tree import verify_tree, verify_tree_one, validate_tree, tree_expected_nodes
+from .tree_residual import verify_tree_residual, verify_tree_residual_one
 from . import laws
 
 __all__ = [
@@ -31,5 +32,6 @@ __all__ = [
     "verify_chain", "verify_chain_one", "FLAG_WINDOW",
     "verify_greedy", "verify_greedy_one",
     "verify_tree", "verify_tree_one", "validate_tree", "tree_expected_nodes",
+    "verify_tree_residual", "verify_tree_residual_one",
     "laws",
 ]

@@ -260,6 +260,55 @@ def make_tree(B: int, N: int, V: int, *, seed: int, logit_dtype: str = "bf16", s
                                 max_children=max_children, boost=boost))
 
 
+# ------------------------------------------------------------------ residual tree
+@dataclass
+class TreeResidualInputs:
+    B: int
+    N: int
+    V: int
+    temperature: np.float32
+    logit_dtype: str
+    logits: np.ndarray            # [B, N, V] target logits (row v scores v's children)
+    q: np.ndarray                 # [B, N, V] float32: row c = distribution node c was drawn from
+    node_tokens: np.ndarray       # [B, N] int32
+    parents: np.ndarray           # [B, N] int32
+    u_acc: np.ndarray             # [B, N] float32, entry c for the test of child c
+    u_draw: np.ndarray            # [B, N] float32, entry v for the terminal draw at v
+    meta: dict = field(default_factory=dict)
+
+
+def make_tree_residual(B: int, N: int, V: int, *, seed: int, logit_dtype: str = "bf16", sigma: float = 3.0,
+                       noise: float = 1.0, temperature: float = 1.0, max_depth: int = 3,
+                       max_children: int = 4, per_child: bool = False) -> TreeResidualInputs:
+    """Random candidate trees whose children are proposals of a stand-in drafter: the
+    drafter's distribution at node v is softmax(row_v + N(0, noise^2)) (stored fp32), and
+    v's children are drawn from it i.i.d. (with replacement, so siblings may repeat a
+    token); with per_child every child has a noise draw, a row and a token of its own."""
+    ss = np.random.SeedSequence(seed)
+    s_logit, s_tree, s_noise, s_pick, s_u = (np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(5))
+    lg = _normal_f32(s_logit, (B, N, V), sigma)
+    parents = np.stack([random_tree(s_tree, N, max_depth, max_children) for _ in range(B)])
+    q = np.zeros((B, N, V), dtype=np.float32)
+    node_tokens = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        for v in range(N):
+            kids = np.nonzero(parents[b] == v)[0]
+            if kids.size == 0:
+                continue
+            rows = 1 if not per_child else kids.size
+            z = lg[b, v].astype(np.float64)[None] + s_noise.standard_normal((rows, V)) * noise
+            qr = _drafter_softmax(z).astype(np.float32)
+            q[b, kids] = qr if per_child else qr[0]
+            node_tokens[b, kids] = _draw_from_rows(s_pick, q[b, kids])
+    stored = f32_to_bf16_bits(lg) if logit_dtype == "bf16" else lg
+    u_acc = uniforms(s_u, (B, N))
+    u_draw = uniforms(s_u, (B, N))
+    return TreeResidualInputs(B, N, V, np.float32(temperature), logit_dtype, stored, q, node_tokens,
+                              parents.astype(np.int32), u_acc, u_draw,
+                              meta=dict(seed=seed, sigma=sigma, noise=noise, max_depth=max_depth,
+                                        max_children=max_children, per_child=per_child))
+
+
 # --------------------------------------------------------------------------- configs
 CONFIGS = {
     # chain, correctness scale: fp32 logits ~ N(0, 2^2), drafter noise 0.5, T = 1
@@ -276,11 +325,15 @@ CONFIGS = {
     # tree, membership by target sample
     5: dict(kind="tree", B=32, N=63, V=152064, logit_dtype="bf16", sigma=3.0, noise=1.0,
             temperature=1.0, max_depth=6, max_children=4),
+    # multi-candidate tree with residual updates (not one of the pages' workloads): 31 nodes,
+    # depth <= 3, up to 4 children drawn i.i.d. from a noisy drafter, 32000-token vocabulary
+    6: dict(kind="tree_residual", B=32, N=31, V=32000, logit_dtype="bf16", sigma=3.0, noise=1.0,
+            temperature=1.0, max_depth=3, max_children=4),
 }
 
 
 def make_config(k: int, run: int = 0, **override):
-    """Inputs for workload k (1..5) with seed 1000*k + run; keyword overrides change the recipe."""
+    """Inputs for workload k (1..6) with seed 1000*k + run; keyword overrides change the recipe."""
     spec = dict(CONFIGS[k])
     spec.update(override)
     kind = spec.pop("kind")
@@ -291,4 +344,6 @@ def make_config(k: int, run: int = 0, **override):
         return make_greedy(seed=seed, **spec)
     if kind == "tree":
         return make_tree(seed=seed, **spec)
+    if kind == "tree_residual":
+        return make_tree_residual(seed=seed, **spec)
     raise ValueError(kind)

@@ -40,6 +40,15 @@ def main():
                           accepted_len=o["accepted_len"].tolist(),
                           out_tokens=o["out_tokens"].tolist(), out_nodes=o["out_nodes"].tolist(),
                           status=o["status"].tolist()))
+    for run in range(2):
+        x = synth.make_config(6, run, B=6, N=13, V=48, per_child=bool(run))
+        o = oracle.verify_tree_residual(x.logits, x.q, x.parents, x.node_tokens, x.u_acc, x.u_draw,
+                                        x.temperature, x.logit_dtype)
+        cases.append(dict(kind="tree_residual", config=6, run=run,
+                          override=dict(B=6, N=13, V=48, per_child=bool(run)),
+                          accepted_len=o["accepted_len"].tolist(),
+                          out_tokens=o["out_tokens"].tolist(), out_nodes=o["out_nodes"].tolist(),
+                          status=o["status"].tolist()))
     with open(OUT, "w") as f:
         json.dump(dict(note="written by tests/golden/make_golden.py from oracle/ outputs", cases=cases),
                   f, indent=1)

@@ -16,7 +16,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-PIN_FILES = ["test_oracle_pins.py", "test_oracle_laws.py", "test_oracle_regression.py"]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_laws.py", "test_oracle_regression.py",
+             "test_oracle_tree_residual.py"]
 
 # (file under oracle/, text as it stands, the planted mistake)
 MUTANTS = {
@@ -68,6 +69,17 @@ MUTANTS = {
     "tree_expectation_uses_child_row": ("tree.py",
                                         "f[v] = f[int(parents[v])] * probs[int(parents[v]), int(node_tokens[v])]",
                                         "f[v] = f[int(parents[v])] * probs[v, int(node_tokens[v])]"),
+    # residual-update tree ([M7.7] §0x08B, §0x09A)
+    "tree_residual_not_updated": ("tree_residual.py", "            res = g / W\n", "            res = res\n"),
+    "tree_residual_unnormalized": ("tree_residual.py", "            res = g / W\n", "            res = g\n"),
+    "tree_residual_unclipped": ("tree_residual.py", "            g = np.maximum(res - q, 0.0)",
+                                "            g = np.abs(res - q)"),
+    "tree_residual_tests_original_p": ("tree_residual.py", "            a = min(1.0, float(res[x]) / qx)",
+                                       "            a = min(1.0, float(target_probs(L[v], temperature)[0][x]) / qx)"),
+    "tree_residual_reverse_child_order": ("tree_residual.py", "        for c in range(v + 1, N):            # children",
+                                          "        for c in range(N - 1, v, -1):            # children"),
+    "tree_residual_draw_with_accept_uniform": ("tree_residual.py", "        ud = float(u_draw[v])",
+                                               "        ud = float(u_acc[v]) if v > 0 else float(u_draw[v])"),
     # laws ([M7.1] §0x05A-§0x05D, [Atlas] mechanism)
     "expected_tokens_off_by_one": ("laws.py", "return (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)",
                                    "return (1.0 - alpha ** gamma) / (1.0 - alpha)"),

@@ -19,6 +19,10 @@ def test_oracle_matches_stored_outputs():
             o = oracle.verify_chain(x.logits, x.q, x.tokens, x.u, x.temperature, x.logit_dtype)
         elif c["kind"] == "greedy":
             o = oracle.verify_greedy(x.logits, x.tokens, x.logit_dtype)
+        elif c["kind"] == "tree_residual":
+            o = oracle.verify_tree_residual(x.logits, x.q, x.parents, x.node_tokens, x.u_acc, x.u_draw,
+                                            x.temperature, x.logit_dtype)
+            assert o["out_nodes"].tolist() == c["out_nodes"]
         else:
             o = oracle.verify_tree(x.logits, x.parents, x.node_tokens, x.u, x.temperature, x.logit_dtype)
             assert o["out_nodes"].tolist() == c["out_nodes"]
