@@ -69,6 +69,29 @@ def time_calls(calls, steps, warmup, stream):
     return span_ms / 1e3, per
 
 
+def bench_tree_residual(args, torch, sv, synth):
+    x = synth.make_config(6, 0)
+    B, N, V = x.B, x.N, x.V
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    qt = torch.from_numpy(x.q).to(dev)
+    nt, pt = torch.from_numpy(x.node_tokens).to(dev), torch.from_numpy(x.parents).to(dev)
+    ua, ud = torch.from_numpy(x.u_acc).to(dev), torch.from_numpy(x.u_draw).to(dev)
+    sets = device_copies(lambda: (lt.clone(), qt.clone(), nt, pt, ua, ud), lt.numel() * 2 + qt.numel() * 4)
+    del lt, qt
+    stream = torch.cuda.current_stream()
+    ws = torch.zeros(sv.tree_residual_workspace_bytes(B, N, V) + 512, dtype=torch.uint8, device=dev)
+    calls = [sv.prepare_tree_residual(*s, float(x.temperature), workspace_tensor=ws) for s in sets]
+    span, per = time_calls(calls, max(100, args.steps // 2), args.warmup, stream)
+    acc = calls[0].out["accepted_len"].cpu().numpy()
+    launch = span / len(per)
+    del sets, calls
+    return dict(workload="tree with residual updates B=32 N=31 V=32000 bf16 logits, fp32 q, T=1",
+                nodes_per_s=B * N * len(per) / span, launch_us=launch * 1e6,
+                evented_launch_mean_us=float(per.mean()) * 1e3, mean_accepted=float(acc.mean()),
+                dense_equivalent_gbs=B * N * V * (2 + 4) / launch / 1e9)
+
+
 def traffic_record(name):
     """Per-launch HBM traffic from the committed rocprofv3 counter summary for kernel `name`,
     or None when the kernel sources have changed since the counters were taken."""
@@ -124,7 +147,7 @@ def bench_greedy(args, torch, sv, synth):
     stream = torch.cuda.current_stream()
     ws = torch.zeros(sv.greedy_workspace_bytes(B, G, V) + 512, dtype=torch.uint8, device=dev)
     calls = [sv.prepare_greedy(s[0], s[1], workspace_tensor=ws) for s in sets]
-    span, per = time_calls(calls, max(20, args.steps // 4), args.warmup, stream)
+    span, per = time_calls(calls, max(100, args.steps // 2), args.warmup, stream)
     alg = B * (G + 1) * V * 2 + B * G * 4 + B * (G + 2) * 8
     launch = span / len(per)       # seconds per launch over the timed region
     del sets, calls
@@ -148,7 +171,7 @@ def bench_tree(args, torch, sv, synth):
     stream = torch.cuda.current_stream()
     ws = torch.zeros(sv.tree_workspace_bytes(B, N, V) + 512, dtype=torch.uint8, device=dev)
     calls = [sv.prepare_tree(s[0], s[1], s[2], s[3], float(x.temperature), workspace_tensor=ws) for s in sets]
-    span, per = time_calls(calls, max(20, args.steps // 4), args.warmup, stream)
+    span, per = time_calls(calls, max(100, args.steps // 2), args.warmup, stream)
     acc = calls[0].out["accepted_len"].cpu().numpy()
     visited = int((acc + 1).sum())
     alg = visited * V * 2 + B * N * 12
@@ -268,6 +291,9 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] tree workload")
         line["secondary"]["tree"] = bench_tree(args, torch, sv, synth)
+        torch.cuda.empty_cache()
+        log("[bench] tree with residual updates")
+        line["secondary"]["tree_residual"] = bench_tree_residual(args, torch, sv, synth)
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

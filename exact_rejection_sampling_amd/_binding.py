@@ -43,6 +43,11 @@ _SIGNATURES = {
                                   _c_int, _c_int, _c_int, _c_float,
                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                   _c_void_p, _c_size_t, _c_void_p]),
+    "spec_tree_residual_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
+    "spec_verify_tree_residual": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                           _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_float,
+                                           _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                           _c_void_p, _c_size_t, _c_void_p]),
 }
 
 
@@ -302,6 +307,67 @@ def prepare_tree(node_logits, node_tokens, parents, uniforms, temperature, *, wo
     """spec_verify_tree with its arguments checked and marshalled once (see PreparedCall)."""
     return PreparedCall(*_tree_args(node_logits, node_tokens, parents, uniforms, temperature,
                                     workspace_tensor, out))
+
+
+def _tree_residual_args(node_logits, draft_probs, node_tokens, parents, accept_uniforms, draw_uniforms,
+                        temperature, workspace_tensor, out):
+    lib = load_library()
+    _need(node_logits, "node_logits")
+    if node_logits.dim() != 3:
+        raise ValueError("node_logits must be [B, N, V]")
+    B, N, V = node_logits.shape
+    dev = node_logits.device
+    _need(draft_probs, "draft_probs", shape=(B, N, V), device=dev)
+    _need(node_tokens, "node_tokens", dtype=torch.int32, shape=(B, N), device=dev)
+    _need(parents, "parents", dtype=torch.int32, shape=(B, N), device=dev)
+    _need(accept_uniforms, "accept_uniforms", dtype=torch.float32, shape=(B, N), device=dev)
+    _need(draw_uniforms, "draw_uniforms", dtype=torch.float32, shape=(B, N), device=dev)
+    lt, qt = _dtype_code(node_logits, "node_logits"), _dtype_code(draft_probs, "draft_probs")
+    if out is None:
+        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty(B, N, dtype=torch.int32, device=dev),
+                   out_nodes=torch.empty(B, N, dtype=torch.int32, device=dev),
+                   req_status=torch.empty(B, dtype=torch.int32, device=dev))
+    stream = torch.cuda.current_stream(dev)
+    need = lib.spec_tree_residual_workspace_bytes(B, N, V)
+    if need == 0 and B > 0:
+        raise SpecError(f"unsupported sizes B={B} N={N} V={V}")
+    ws = workspace_tensor if workspace_tensor is not None else workspace("tree_residual", need, dev, stream)
+    wp, wn = _aligned_ws(ws)
+    args = (_ptr(node_logits), lt, _ptr(draft_probs), qt, _ptr(node_tokens), _ptr(parents),
+            _ptr(accept_uniforms), _ptr(draw_uniforms), B, N, V, ctypes.c_float(float(temperature)),
+            _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["out_nodes"]),
+            _ptr(out["req_status"]), wp, wn, ctypes.c_void_p(stream.cuda_stream))
+    keep = (node_logits, draft_probs, node_tokens, parents, accept_uniforms, draw_uniforms, ws, stream)
+    return lib.spec_verify_tree_residual, args, keep, out
+
+
+def spec_verify_tree_residual(node_logits: torch.Tensor, draft_probs: torch.Tensor, node_tokens: torch.Tensor,
+                              parents: torch.Tensor, accept_uniforms: torch.Tensor, draw_uniforms: torch.Tensor,
+                              temperature: float, *, workspace_tensor: Optional[torch.Tensor] = None,
+                              out: Optional[dict] = None) -> dict:
+    """Multi-candidate tree verification with residual updates (C entry point
+    spec_verify_tree_residual).
+
+    node_logits [B, N, V] bf16/fp32; draft_probs [B, N, V] fp32/bf16 (row c: the distribution
+    node c's token was drawn from); node_tokens, parents [B, N] int32; accept_uniforms,
+    draw_uniforms [B, N] fp32.  Returns {accepted_len, out_tokens, out_nodes, req_status}.
+    """
+    fn, args, _, out = _tree_residual_args(node_logits, draft_probs, node_tokens, parents, accept_uniforms,
+                                           draw_uniforms, temperature, workspace_tensor, out)
+    _check(fn(*args))
+    return out
+
+
+def prepare_tree_residual(node_logits, draft_probs, node_tokens, parents, accept_uniforms, draw_uniforms,
+                          temperature, *, workspace_tensor=None, out=None) -> PreparedCall:
+    """spec_verify_tree_residual with its arguments checked and marshalled once."""
+    return PreparedCall(*_tree_residual_args(node_logits, draft_probs, node_tokens, parents, accept_uniforms,
+                                             draw_uniforms, temperature, workspace_tensor, out))
+
+
+def tree_residual_workspace_bytes(B: int, N: int, V: int) -> int:
+    return load_library().spec_tree_residual_workspace_bytes(B, N, V)
 
 
 def chain_workspace_bytes(B: int, gamma: int, V: int) -> int:

@@ -63,6 +63,16 @@ size_t spec_greedy_workspace_bytes(int B, int gamma, int V) {
   return sv::greedy_layout(B, gamma, V).total;
 }
 
+bool residual_sizes_ok(int B, int N, int V) {
+  return B >= 0 && B <= SPEC_MAX_BATCH && N >= 1 && N <= SPEC_MAX_NODES && V >= 1 &&
+         V <= sv::kTreeStage * 2048;
+}
+
+size_t spec_tree_residual_workspace_bytes(int B, int N, int V) {
+  if (!residual_sizes_ok(B, N, V) || !sv::grid_fits(sv::tree_blocks(B, V))) return 0;
+  return sv::tree_layout(B, N, V, true).total;
+}
+
 size_t spec_tree_workspace_bytes(int B, int N, int V) {
   if (!(B >= 0 && B <= SPEC_MAX_BATCH && N >= 1 && N <= SPEC_MAX_NODES && V >= 1 && V <= SPEC_MAX_VOCAB))
     return 0;
@@ -163,7 +173,7 @@ spec_status spec_verify_tree(const void* node_logits, int logit_dtype, const int
   const sv::TreeLayout L = sv::tree_layout(B, N, V);
   if (!workspace || workspace_bytes < L.total || !aligned256(workspace)) return SPEC_EWORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  sv::TreeParams p;
+  sv::TreeParams p{};
   p.logits = node_logits;
   p.node_tokens = node_tokens;
   p.parents = parents;
@@ -185,6 +195,52 @@ spec_status spec_verify_tree(const void* node_logits, int logit_dtype, const int
   p.c2 = static_cast<float>(kLog2e / static_cast<double>(temperature));
   const bool vec = (V % 8 == 0) && aligned16(node_logits);
   return sv::launch_tree(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+spec_status spec_verify_tree_residual(const void* node_logits, int logit_dtype, const void* draft_probs,
+                                      int q_dtype, const int32_t* node_tokens, const int32_t* parents,
+                                      const float* accept_uniforms, const float* draw_uniforms, int B, int N,
+                                      int V, float temperature, int32_t* accepted_len, int32_t* out_tokens,
+                                      int32_t* out_nodes, int32_t* req_status, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  if (!residual_sizes_ok(B, N, V)) return SPEC_EINVAL;
+  if (!temperature_ok(temperature)) return SPEC_EINVAL;
+  if (!dtype_ok(logit_dtype) || !dtype_ok(q_dtype)) return SPEC_EDTYPE;
+  if (!sv::grid_fits(sv::tree_blocks(B, V))) return SPEC_EINVAL;
+  if (B == 0) return SPEC_OK;
+  if (!node_logits || !draft_probs || !node_tokens || !parents || !accept_uniforms || !draw_uniforms ||
+      !accepted_len || !out_tokens || !out_nodes || !req_status)
+    return SPEC_EINVAL;
+  const sv::TreeLayout L = sv::tree_layout(B, N, V, true);
+  if (!workspace || workspace_bytes < L.total || !aligned256(workspace)) return SPEC_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  sv::TreeParams p{};
+  p.logits = node_logits;
+  p.node_tokens = node_tokens;
+  p.parents = parents;
+  p.u = accept_uniforms;
+  p.u_draw = draw_uniforms;
+  p.q = draft_probs;
+  p.q_dtype = q_dtype;
+  p.accepted_len = accepted_len;
+  p.out_tokens = out_tokens;
+  p.out_nodes = out_nodes;
+  p.req_status = req_status;
+  p.part = reinterpret_cast<float2*>(ws + L.part);
+  p.deep = reinterpret_cast<float2*>(ws + L.deep);
+  p.order = reinterpret_cast<unsigned long long*>(ws + L.order);
+  p.desc = reinterpret_cast<unsigned*>(ws + L.desc);
+  p.desc_words = 4 + 2 * N;
+  p.counters = sv::request_counters(workspace);
+  p.B = B;
+  p.N = N;
+  p.V = V;
+  p.P = chunks(V, sv::kWaveChunk);
+  p.WG1 = chunks(p.P, sv::kWavesPerBlock);
+  p.WH = chunks(p.P, sv::kTreeHelperChunks);
+  p.c2 = static_cast<float>(kLog2e / static_cast<double>(temperature));
+  const bool vec = (V % 8 == 0) && aligned16(node_logits) && aligned16(draft_probs);
+  return sv::launch_tree_residual(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
 }  // extern "C"

@@ -410,6 +410,13 @@ __device__ __forceinline__ unsigned long long await_u64(const unsigned long long
   return v;
 }
 __device__ __forceinline__ void clear_u64(unsigned long long* p) { publish_u64(p, 0ull); }
+// 32-bit words read by other blocks after an order that follows them (descriptors).
+__device__ __forceinline__ void publish_u32(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned fetch_u32(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // (raw max m, sum Z) of a chunk range: never all-zero bits, because an empty range is
 // (-inf, 0) and a non-empty one has Z >= 1 (its maximum contributes 2^0) or NaN.

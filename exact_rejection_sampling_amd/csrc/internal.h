@@ -106,7 +106,16 @@ struct TreeParams {
   unsigned* counters;        // per-request slots: [b*4 + 0] root arrivals, [b*4 + 1] helpers gone
   int B, N, V, P, WG1, WH;
   float c2;
+  // residual-update verifier only
+  const void* q;             // [B, N, V] proposal rows: row c = the distribution node c was drawn from
+  const float* u_draw;       // [B, N] terminal draw at node v (u holds the child accept uniforms)
+  unsigned* desc;            // [B * desc_words] residual-pass descriptors
+  int q_dtype, desc_words;   // desc_words = 4 + 2N
 };
+
+// Rows the residual-update tree verifier's walking block stages in LDS: at most this many
+// 2048-element chunks per row (V <= 2^21).
+constexpr int kTreeStage = 1024;
 
 // Helper blocks of a tree request: each summarizes kTreeHelperChunks chunks of an ordered
 // row (its four waves two chunks each, loads in flight together).
@@ -167,15 +176,15 @@ inline GreedyLayout greedy_layout(long B, long G, long V) {
   return L;
 }
 
-struct TreeLayout { size_t part, deep, order, total; };
-inline TreeLayout tree_layout(long B, long N, long V) {
-  (void)N;
+struct TreeLayout { size_t part, deep, order, desc, total; };
+inline TreeLayout tree_layout(long B, long N, long V, bool residual = false) {
   const long P = (V + 2047) / 2048;
   TreeLayout L;
   size_t o = counter_bytes(B);
   L.part = o;   o = align256(o + sizeof(float2) * B * P);
   L.deep = o;   o = align256(o + sizeof(float2) * B * 2 * P);
   L.order = o;  o = align256(o + sizeof(unsigned long long) * B);
+  L.desc = o;   if (residual) o = align256(o + sizeof(unsigned) * B * (4 + 2 * N));
   L.total = o;
   return L;
 }
@@ -201,5 +210,6 @@ inline bool grid_fits(unsigned long long blocks) { return blocks <= 0xfffffffful
 hipError_t launch_chain(const ChainParams& p, int logit_dtype, bool vec, hipStream_t s);
 hipError_t launch_greedy(const GreedyParams& p, int logit_dtype, bool vec, hipStream_t s);
 hipError_t launch_tree(const TreeParams& p, int logit_dtype, bool vec, hipStream_t s);
+hipError_t launch_tree_residual(const TreeParams& p, int logit_dtype, bool vec, hipStream_t s);
 
 }  // namespace sv

@@ -153,17 +153,90 @@ __device__ int sample_row(const TreeParams& p, const float2* part, const void* r
 }
 
 // Orders from a walking block to its request's helpers, one 64-bit word per request:
-// generation << 32 | code, code = row + 1 (summarize that row) or kTreeDone (leave).  A
-// generation is never 0, so a published order is never zero.
+// generation << 32 | code, code = row + 1 (summarize that row), kResidualPass | i (chunk
+// masses of the residual after i rejected children, residual-update verifier only) or
+// kTreeDone (leave).  A generation is never 0, so a published order is never zero.
 constexpr unsigned kTreeDone = 0xffffffffu;
+constexpr unsigned kResidualPass = 0x40000000u;
+
+// ------------------------------------------------------------ residual-update verifier
+// Descriptor of the residual passes at the current node v, written by the walker before
+// each pass order: [0] v, [1] bits of r (reference exponent of row v), [2] bits of 1/Z
+// (base 2), [4 + j] the j-th rejected child, [4 + N + j] bits of 1/W_j, W_j the mass of
+// the residual after j + 1 rejections.
+constexpr int kResidStage = 256;   // rejected children a helper keeps in LDS per pass
+
+// The unnormalized residual after i rejected children c_0..c_{i-1} at node v for the
+// eight elements [e0, e0 + 8): p(x) = 2^(l c2 - r) / Z, res_0 = p,
+// res_{j+1} = [res_j - q_{c_j}]_+ / W_j for j + 1 < i, and g = [res_{i-1} - q_{c_{i-1}}]_+.
+// One expression serves the helpers' chunk masses, the walker's single-element accept
+// tests and its rescan, so the three agree bit for bit.  bad: an entry of the last
+// rejected child's q row is negative or non-finite.
+template <int DT, int QT, bool VEC>
+__device__ __forceinline__ void residual8(const TreeParams& p, int b, const unsigned* d, int i, const int* s_kid,
+                                          const float* s_invw, const void* lrow, long e0, float r, float inv_z,
+                                          float (&g)[8], bool& bad) {
+  float l[8];
+  load8<DT, VEC, false>(lrow, e0, p.V, l, -INFINITY);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) g[k] = scaled_exp(l[k], p.c2, r) * inv_z;
+  for (int j = 0; j < i; ++j) {
+    const int kid = j < kResidStage && s_kid ? s_kid[j] : static_cast<int>(fetch_u32(d + 4 + j));
+    const float invw = j + 1 == i ? 1.0f
+                       : (j < kResidStage && s_invw ? s_invw[j] : __uint_as_float(fetch_u32(d + 4 + p.N + j)));
+    float q[8];
+    load8<QT, VEC, false>(row_ptr<QT>(p.q, (size_t)b * p.N + kid, p.V), e0, p.V, q, 0.0f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float t = g[k] - q[k];
+      const float pos = t > 0.0f ? t : 0.0f;
+      if (j + 1 == i) bad |= !(q[k] >= 0.0f && q[k] < INFINITY);
+      g[k] = j + 1 == i ? pos : pos * invw;
+    }
+  }
+}
+
+// Helper h's part of residual pass i: the chunk masses (fp64) of g over its chunks.
+template <int DT, int QT, bool VEC>
+__device__ void residual_pass(const TreeParams& p, int b, int h, unsigned gen, int i) {
+  __shared__ int s_kid[kResidStage];
+  __shared__ float s_invw[kResidStage];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+  const unsigned* d = p.desc + (size_t)b * p.desc_words;
+  const int v = static_cast<int>(fetch_u32(d));
+  const float r = __uint_as_float(fetch_u32(d + 1)), inv_z = __uint_as_float(fetch_u32(d + 2));
+  for (int j = tid; j < min(i, kResidStage); j += kBlock) {
+    s_kid[j] = static_cast<int>(fetch_u32(d + 4 + j));
+    s_invw[j] = __uint_as_float(fetch_u32(d + 4 + p.N + j));
+  }
+  __syncthreads();
+  const void* row = row_ptr<DT>(p.logits, (size_t)b * p.N + v, p.V);
+  double* dst = reinterpret_cast<double*>(p.deep + ((size_t)b * 2 + (gen & 1u)) * p.P);
+  for (int k = 0; k < kTreeHelperBatch; ++k) {
+    const int c = h * kTreeHelperChunks + k * kWavesPerBlock + wave;
+    if (c >= p.P) continue;
+    double acc = 0.0;
+    bool bad = false;
+    for (int jv = 0; jv < kStatVecs; ++jv) {
+      const long e0 = (long)c * kWaveChunk + static_cast<long>(jv * kWave + lane) * kVec;
+      float g[8];
+      residual8<DT, QT, VEC>(p, b, d, i, s_kid, s_invw, row, e0, r, inv_z, g, bad);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (double)g[e];
+    }
+    if (bad) acc = NAN;
+    const double m = wave_sum_d(acc);
+    if (lane == 0) publish_mass(dst + c, m);
+  }
+  __syncthreads();   // s_kid and s_invw are rewritten by the next pass
+}
 
 __device__ __forceinline__ void publish_order(const TreeParams& p, int b, unsigned gen, unsigned code) {
   publish_u64(p.order + b, (static_cast<unsigned long long>(gen) << 32) | code);
 }
 
-// Summaries of a row staged in LDS by the walker (rows of up to kTreeStage chunks;
-// longer rows are read from the workspace directly).
-constexpr int kTreeStage = 1024;
+// The walker stages a row's summaries in LDS when the row has at most kTreeStage chunks;
+// longer rows are read from the workspace directly.
 
 // Read the P published summaries at `src` into `dst` (LDS); sets *lost if one did not arrive.
 __device__ void stage_summaries(const float2* src, float2* dst, int P, int* lost) {
@@ -259,9 +332,258 @@ __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
   }
 }
 
+// Next child of v after `after` in index order (children have larger indices than their
+// parent), block-wide; kNoPick if there is none.
+__device__ __forceinline__ int next_child(const int32_t* par, int N, int v, int after, int* s_imin) {
+  int cand = kNoPick;
+  for (int c = after + 1 + threadIdx.x; c < N; c += kBlock)
+    if (cand == kNoPick && par[c] == v) cand = c;
+  return block_min_i(cand, s_imin);
+}
+
+// Running mass of the P chunk masses in `mass` (LDS), formed the same way wherever it is
+// needed: thread t owns a contiguous run of chunks and extends the block-exclusive prefix
+// over it.  Returns this thread's exclusive prefix; *total is the running value after the
+// last chunk (identical in every thread).
+__device__ double mass_prefix(const double* mass, int P, int c_lo, int c_hi, double* total) {
+  __shared__ double s_scan[kWavesPerBlock];
+  __shared__ double s_total;
+  double mine = 0.0;
+  for (int c = c_lo; c < c_hi; ++c) mine += mass[c];
+  double tot;
+  const double excl = block_excl_scan_d(mine, s_scan, &tot);
+  if (c_lo < c_hi && c_hi == P) s_total = excl + mine;
+  __syncthreads();
+  *total = s_total;
+  __syncthreads();
+  return excl;
+}
+
+// The terminal draw at node v after i >= 1 rejected children: inverse CDF of the residual
+// g with u, from the chunk masses of the last pass (in `mass`, total W) and a rescan of
+// the chunk holding the target.
+template <int DT, int QT, bool VEC>
+__device__ int residual_pick(const TreeParams& p, int b, const unsigned* d, int i, const void* row, float r,
+                             float inv_z, const double* mass, float u) {
+  __shared__ double s_scan[kWavesPerBlock];
+  __shared__ int s_imin[kWavesPerBlock];
+  __shared__ double s_before;
+  const int tid = threadIdx.x;
+  const int per = (p.P + kBlock - 1) / kBlock;
+  const int c_lo = min(tid * per, p.P), c_hi = min(c_lo + per, p.P);
+  double W;
+  const double excl = mass_prefix(mass, p.P, c_lo, c_hi, &W);
+  const double t = (double)u * W;
+  int cand = kNoPick;
+  {
+    double run = excl;
+    for (int c = c_lo; c < c_hi; ++c) {
+      const double nxt = run + mass[c];
+      if (nxt > t) { cand = c; break; }
+      run = nxt;
+    }
+  }
+  if (tid == 0) s_before = 0.0;
+  int cstar = block_min_i(cand, s_imin);   // a chunk is always found (t < W); clamp regardless
+  if (cstar == kNoPick) cstar = p.P - 1;
+  if (cstar >= c_lo && cstar < c_hi) {
+    double run = excl;
+    for (int c = c_lo; c < cstar; ++c) run += mass[c];
+    s_before = run;
+  }
+  __syncthreads();
+  const double rem = t - s_before;
+  const long e0 = (long)cstar * kWaveChunk + (long)tid * kVec;
+  float g[8];
+  bool bad = false;
+  residual8<DT, QT, VEC>(p, b, d, i, nullptr, nullptr, row, e0, r, inv_z, g, bad);
+  double incl[8];
+  double acc = 0.0;
+  int last_pos = -1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    acc += (double)g[k];
+    incl[k] = acc;
+    if (g[k] > 0.0f) last_pos = (int)(e0 + k);
+  }
+  double chunk_total;
+  const double off = block_excl_scan_d(acc, s_scan, &chunk_total);
+  int pick = kNoPick;
+#pragma unroll
+  for (int k = 7; k >= 0; --k)
+    if (off + incl[k] > rem && g[k] > 0.0f) pick = (int)(e0 + k);
+  pick = block_min_i(pick, s_imin);
+  return pick != kNoPick ? pick : -block_min_i(-last_pos, s_imin);
+}
+
+// Walk of request b by the last root block, residual-update verifier ([M7.7] §0x09A):
+// at node v the children are tested in index order against the current residual; an
+// accepted child becomes the next node (its row summarized by the helpers), a rejection
+// replaces the residual by [res - q_c]_+ / W (W from a helper pass), and a node whose
+// children are all rejected (or which has none) emits a draw of the residual.
+template <int DT, int QT, bool VEC>
+__device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
+  __shared__ int s_bad, s_lost, s_status, s_accept;
+  __shared__ int s_imin[kWavesPerBlock];
+  __shared__ float s_red[kWavesPerBlock];
+  __shared__ double s_scan[kWavesPerBlock];
+  __shared__ float2 s_sum[kTreeStage];
+  __shared__ double s_mass[kTreeStage];
+  __shared__ unsigned s_gen;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+  const int N = p.N, P = p.P;
+  const int32_t* par = p.parents + (size_t)b * N;
+  const int32_t* tok = p.node_tokens + (size_t)b * N;
+  unsigned* d = p.desc + (size_t)b * p.desc_words;
+
+  if (tid == 0) s_bad = (par[0] != -1);
+  __syncthreads();
+  for (int v = 1 + tid; v < N; v += kBlock) {
+    const int pv = par[v], tv = tok[v];
+    if (pv < 0 || pv >= v || tv < 0 || tv >= p.V) s_bad = 1;
+  }
+  __syncthreads();
+  if (s_bad) { tree_fail(p, b, SPEC_REQ_BADTREE); return; }
+
+  int v = 0, depth = 0;
+  while (true) {
+    const void* row = row_ptr<DT>(p.logits, (size_t)b * N + v, p.V);
+    // 1. the row's chunk summaries: the root items' or, below the root, the helpers'
+    if (tid == 0) s_lost = 0;
+    __syncthreads();
+    float2* src = v == 0 ? p.part + (size_t)b * P : p.deep + ((size_t)b * 2 + (gen & 1u)) * P;
+    stage_summaries(src, s_sum, P, &s_lost);
+    if (v != 0) {
+      for (int c = tid; c < P; c += kBlock) clear_f2(src + c);
+      vmem_wait();
+    }
+    if (s_lost) { tree_fail(p, b, SPEC_REQ_INTERNAL); return; }
+    // reference exponent r = fp32(max raw logit * c2) and Z = sum 2^(l c2 - r) in fp64
+    float m = -INFINITY;
+    for (int c = tid; c < P; c += kBlock) m = fmaxf(m, s_sum[c].x);
+    m = wave_max(m);
+    if (lane == 0) s_red[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float r = m * p.c2;
+    double zt = 0.0;
+    for (int c = tid; c < P; c += kBlock) zt += (double)s_sum[c].y * exp2((double)(s_sum[c].x * p.c2) - (double)r);
+    double Z;
+    block_excl_scan_d(zt, s_scan, &Z);
+    if (!(isfinite(Z) && Z > 0.0)) { tree_fail(p, b, SPEC_REQ_NONFINITE); return; }
+    const float inv_z = (float)(1.0 / Z);
+
+    // 2. the children, in index order
+    int i = 0, accepted = kNoPick;
+    int c = next_child(par, N, v, v, s_imin);
+    while (c != kNoPick) {
+      if (tid == 0) {
+        int st = 0, acc = 0;
+        const int x = tok[c];
+        const float qx = load_scalar<QT>(p.q, ((size_t)b * N + c) * p.V + x);
+        const float ua = p.u[(size_t)b * N + c];
+        if (!(isfinite(qx) && qx > 0.0f)) {
+          st = SPEC_REQ_QZERO;
+        } else if (!(ua >= 0.0f && ua < 1.0f)) {
+          st = SPEC_REQ_BADUNIFORM;
+        } else {
+          // residual at x after the i rejections so far, the same expression as residual8
+          float g = scaled_exp(load_scalar<DT>(row, x), p.c2, r) * inv_z;
+          for (int j = 0; j < i; ++j) {
+            const int kid = static_cast<int>(fetch_u32(d + 4 + j));
+            const float invw = __uint_as_float(fetch_u32(d + 4 + N + j));
+            const float t = g - load_scalar<QT>(p.q, ((size_t)b * N + kid) * p.V + x);
+            g = (t > 0.0f ? t : 0.0f) * invw;
+          }
+          const double a = fmin(1.0, (double)g / (double)qx);
+          acc = (double)ua < a;
+        }
+        s_status = st;
+        s_accept = acc;
+      }
+      __syncthreads();
+      if (s_status) { tree_fail(p, b, s_status); return; }
+      if (s_accept) { accepted = c; break; }
+      // rejected: the residual's chunk masses from a helper pass
+      if (tid == 0) {
+        if (i == 0) {
+          publish_u32(d, static_cast<unsigned>(v));
+          publish_u32(d + 1, __float_as_uint(r));
+          publish_u32(d + 2, __float_as_uint(inv_z));
+        }
+        publish_u32(d + 4 + i, static_cast<unsigned>(c));
+        vmem_wait();                      // the descriptor is complete before the order
+        publish_order(p, b, ++gen, kResidualPass | static_cast<unsigned>(i + 1));
+        s_gen = gen;
+        s_lost = 0;
+      }
+      ++i;
+      __syncthreads();
+      gen = s_gen;
+      double* mw = reinterpret_cast<double*>(p.deep + ((size_t)b * 2 + (gen & 1u)) * P);
+      for (int k = tid; k < P; k += kBlock) {
+        const unsigned long long bits = await_u64(reinterpret_cast<const unsigned long long*>(mw + k));
+        if (bits == 0ull) s_lost = 1;
+        s_mass[k] = -__longlong_as_double(static_cast<long long>(bits));
+        clear_u64(reinterpret_cast<unsigned long long*>(mw + k));
+      }
+      vmem_wait();                        // cleared before any later order reuses the words
+      __syncthreads();
+      if (s_lost) { tree_fail(p, b, SPEC_REQ_INTERNAL); return; }
+      const int per = (P + kBlock - 1) / kBlock;
+      const int c_lo = min(tid * per, P), c_hi = min(c_lo + per, P);
+      double W;
+      mass_prefix(s_mass, P, c_lo, c_hi, &W);
+      if (!(isfinite(W) && W > 0.0)) { tree_fail(p, b, SPEC_REQ_RESIDUAL_EMPTY); return; }
+      if (tid == 0) publish_u32(d + 4 + N + (i - 1), __float_as_uint((float)(1.0 / W)));
+      c = next_child(par, N, v, c, s_imin);
+    }
+    if (accepted != kNoPick) {
+      if (tid == 0) {
+        p.out_tokens[(size_t)b * N + depth] = tok[accepted];
+        p.out_nodes[(size_t)b * N + depth] = accepted;
+        vmem_wait();
+        publish_order(p, b, ++gen, static_cast<unsigned>(accepted) + 1u);   // summarize its row
+        s_gen = gen;
+      }
+      ++depth;
+      v = accepted;
+      __syncthreads();
+      gen = s_gen;
+      continue;
+    }
+
+    // 3. no child accepted: the terminal draw at v
+    const float ud = p.u_draw[(size_t)b * N + v];
+    if (!(ud >= 0.0f && ud < 1.0f)) { tree_fail(p, b, SPEC_REQ_BADUNIFORM); return; }
+    int y;
+    if (i == 0) {
+      int status = 0;
+      y = sample_row<DT, VEC, false>(p, s_sum, row, ud, &status);
+      if (status != 0) { tree_fail(p, b, status); return; }
+    } else {
+      y = residual_pick<DT, QT, VEC>(p, b, d, i, row, r, inv_z, s_mass, ud);
+    }
+    for (int k = tid; k < N; k += kBlock) {
+      if (k > depth) {
+        p.out_tokens[(size_t)b * N + k] = -1;
+        p.out_nodes[(size_t)b * N + k] = -1;
+      } else if (k == depth) {
+        p.out_tokens[(size_t)b * N + k] = y;
+        p.out_nodes[(size_t)b * N + k] = -1;
+      }
+    }
+    if (tid == 0) {
+      p.accepted_len[b] = depth;
+      p.req_status[b] = 0;
+    }
+    return;
+  }
+}
+
 // Helper h of request b: summarizes its chunks of every row the walker orders, until
 // dismissed; the last helper of the request to leave returns the order word to zero.
-template <int DT, bool VEC>
+template <int DT, int QT, bool VEC, bool RESID>
 __device__ void helper_item(const TreeParams& p, int b, int h) {
   __shared__ unsigned long long s_order;
   __shared__ int s_last;
@@ -283,6 +605,12 @@ __device__ void helper_item(const TreeParams& p, int b, int h) {
     const unsigned gen = static_cast<unsigned>(o >> 32), code = static_cast<unsigned>(o);
     if (o == 0ull || gen == last_gen || code == kTreeDone) break;   // dismissed (or the wait bound)
     last_gen = gen;
+    if constexpr (RESID) {
+      if (code & kResidualPass) {
+        residual_pass<DT, QT, VEC>(p, b, h, gen, static_cast<int>(code & ~kResidualPass));
+        continue;
+      }
+    }
     const void* row = row_ptr<DT>(p.logits, (size_t)b * p.N + (code - 1u), p.V);
     float2* dst = p.deep + ((size_t)b * 2 + (gen & 1u)) * p.P;
     ChunkRegs<DT> r[kTreeHelperBatch];
@@ -315,15 +643,16 @@ __device__ void helper_item(const TreeParams& p, int b, int h) {
   }
 }
 
-// Request b's blocks: WG1 root blocks, then WH helpers.
-template <int DT, bool VEC>
+// Request b's blocks: WG1 root blocks, then WH helpers.  RESID: the residual-update
+// verifier (q rows of type QT); otherwise membership (QT unused).
+template <int DT, int QT, bool VEC, bool RESID>
 __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   const int per_req = p.WG1 + p.WH;
   const int b = blockIdx.x / per_req;
   const int slice = blockIdx.x % per_req;
   if (slice >= p.WG1) {
-    helper_item<DT, VEC>(p, b, slice - p.WG1);
+    helper_item<DT, QT, VEC, RESID>(p, b, slice - p.WG1);
     return;
   }
   const int chunk = slice * kWavesPerBlock + wave;
@@ -341,25 +670,39 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
   __syncthreads();
   if (!s_last) return;
   unsigned gen = 0;
-  tree_walk<DT, VEC>(p, b, gen);
+  if constexpr (RESID) tree_walk_residual<DT, QT, VEC>(p, b, gen);
+  else tree_walk<DT, VEC>(p, b, gen);
   __syncthreads();
   if (threadIdx.x == 0) publish_order(p, b, gen + 1u, kTreeDone);   // dismiss the helpers
   for (int j = threadIdx.x; j < p.P; j += kBlock) clear_f2(p.part + (size_t)b * p.P + j);
+  if constexpr (RESID)   // no helper reads the descriptor once dismissed
+    for (int j = threadIdx.x; j < p.desc_words; j += kBlock) publish_u32(p.desc + (size_t)b * p.desc_words + j, 0u);
   if (threadIdx.x == 0) reset_counter(&p.counters[(size_t)b * kCounterSlots + 0]);
 }
 
-template <int DT, bool VEC>
+template <int DT, int QT, bool VEC, bool RESID>
 hipError_t launch_typed(const TreeParams& p, hipStream_t s) {
   const unsigned g = (unsigned)((size_t)p.B * (p.WG1 + p.WH));   // == tree_blocks
-  tree_kernel<DT, VEC><<<dim3(g), dim3(kBlock), 0, s>>>(p);
+  tree_kernel<DT, QT, VEC, RESID><<<dim3(g), dim3(kBlock), 0, s>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_tree(const TreeParams& p, int logit_dtype, bool vec, hipStream_t s) {
-  if (logit_dtype == kBF16) return vec ? launch_typed<kBF16, true>(p, s) : launch_typed<kBF16, false>(p, s);
-  return vec ? launch_typed<kF32, true>(p, s) : launch_typed<kF32, false>(p, s);
+  if (logit_dtype == kBF16)
+    return vec ? launch_typed<kBF16, kF32, true, false>(p, s) : launch_typed<kBF16, kF32, false, false>(p, s);
+  return vec ? launch_typed<kF32, kF32, true, false>(p, s) : launch_typed<kF32, kF32, false, false>(p, s);
+}
+
+hipError_t launch_tree_residual(const TreeParams& p, int logit_dtype, bool vec, hipStream_t s) {
+  const bool lb = logit_dtype == kBF16, qb = p.q_dtype == kBF16;
+  if (vec) {
+    if (lb) return qb ? launch_typed<kBF16, kBF16, true, true>(p, s) : launch_typed<kBF16, kF32, true, true>(p, s);
+    return qb ? launch_typed<kF32, kBF16, true, true>(p, s) : launch_typed<kF32, kF32, true, true>(p, s);
+  }
+  if (lb) return qb ? launch_typed<kBF16, kBF16, false, true>(p, s) : launch_typed<kBF16, kF32, false, true>(p, s);
+  return qb ? launch_typed<kF32, kBF16, false, true>(p, s) : launch_typed<kF32, kF32, false, true>(p, s);
 }
 
 }  // namespace sv

@@ -2,10 +2,11 @@
  * spec_verify.h -- C ABI of libspec_verify.so: batched target-side verification for
  * exact speculative decoding on AMD Instinct MI355X (gfx950).
  *
- * Three entry points, one per verification rule:
- *   spec_verify_chain   rejection-sampling verification of a draft chain
- *   spec_verify_greedy  argmax-match verification of a draft chain
- *   spec_verify_tree    tree verification by target-sample membership
+ * Four entry points, one per verification rule:
+ *   spec_verify_chain          rejection-sampling verification of a draft chain
+ *   spec_verify_greedy         argmax-match verification of a draft chain
+ *   spec_verify_tree           tree verification by target-sample membership
+ *   spec_verify_tree_residual  multi-candidate tree verification with residual updates
  *
  * Pages that define the operations (cited by title and section):
  *   [M7.1]  "M7.1 - Speculative Decoding: Draft, Verify, Accept, Reject"
@@ -187,6 +188,45 @@ spec_status spec_verify_tree(const void* node_logits, int logit_dtype,
                              int32_t* accepted_len, int32_t* out_tokens, int32_t* out_nodes,
                              int32_t* req_status, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/* -------------------------------------------------------- residual tree ---
+ * Multi-candidate tree verification with residual updates ([M7.7] §0x09A, "Stochastic
+ * residual update"; §0x08B: testing every candidate against the original target would
+ * duplicate mass).  Same tree layout as spec_verify_tree (node 0 = frontier root, row v of
+ * node_logits scores v's children), plus the proposal distribution of every node:
+ *   v = 0;
+ *   repeat: res = softmax(l_v / T);
+ *           for each child c of v in increasing index order (token x_c, drawn from q_c):
+ *               accept c iff u_acc[b, c] < min(1, res(x_c) / q_c(x_c)): emit x_c, v = c,
+ *               and continue the walk from c;
+ *               else res = [res - q_c]_+ / sum([res - q_c]_+);
+ *           no child accepted (or no children): emit the inverse-CDF draw of res with
+ *           u_draw[b, v] (vocabulary order, as spec_verify_chain) and stop.
+ * The emitted sequence follows the target's own law for any proposals ([M7.7] §0x09A).
+ *
+ * node_logits   [B, N, V] logit_dtype; draft_probs [B, N, V] q_dtype: row c (c >= 1) is the
+ *               distribution node c's token was drawn from (row 0 is not read; siblings
+ *               drawn i.i.d. repeat one row).  Only q_c(x_c) of tested children and the
+ *               full rows of rejected children are read.
+ * node_tokens, parents [B, N] int32 as for spec_verify_tree.
+ * accept_uniforms [B, N] fp32 (entry c for the test of child c; entry 0 is not read);
+ * draw_uniforms   [B, N] fp32 (entry v for the terminal draw at node v).
+ * Outputs as for spec_verify_tree.  Statuses: SPEC_REQ_BADTREE (checked first), then in
+ * reached order SPEC_REQ_NONFINITE (a row), SPEC_REQ_QZERO (q_c(x_c) not positive and
+ * finite), SPEC_REQ_BADUNIFORM, SPEC_REQ_RESIDUAL_EMPTY (a rejected child's q row has a
+ * negative or non-finite entry, or the residual has no mass).
+ * V is limited to 2^21 here (a row's 2048-element chunk masses are staged on chip).
+ */
+size_t spec_tree_residual_workspace_bytes(int B, int N, int V);
+
+spec_status spec_verify_tree_residual(const void* node_logits, int logit_dtype,
+                                      const void* draft_probs, int q_dtype,
+                                      const int32_t* node_tokens, const int32_t* parents,
+                                      const float* accept_uniforms, const float* draw_uniforms,
+                                      int B, int N, int V, float temperature,
+                                      int32_t* accepted_len, int32_t* out_tokens, int32_t* out_nodes,
+                                      int32_t* req_status, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /* ------------------------------------------------------------------ misc --- */
 const char* spec_status_string(int code);     /* static string, never NULL */

@@ -132,3 +132,19 @@ def test_grid_limit():
     assert lib.spec_chain_workspace_bytes(1 << 20, 7, 16) > 0      # 2^23 rows fit
     assert lib.spec_tree_workspace_bytes(1 << 22, 4, 1 << 20) == 0  # 2^22 * 128 blocks
     assert lib.spec_tree_workspace_bytes(1 << 16, 4, 1 << 20) > 0
+
+
+def test_tree_residual_host_validation():
+    lib = sv.load_library()
+    r = lambda **k: lib.spec_verify_tree_residual(
+        k.get("l", FAKE), k.get("dt", 1), k.get("q", FAKE), k.get("qdt", 0), FAKE, k.get("par", FAKE),
+        k.get("ua", FAKE), k.get("ud", FAKE), k.get("B", 2), k.get("N", 5), k.get("V", 16),
+        ctypes.c_float(k.get("T", 1.0)), FAKE, FAKE, FAKE, FAKE, k.get("ws", NULL), k.get("wsn", 0), NULL)
+    assert r(N=0) == EINVAL and r(N=4097) == EINVAL and r(T=float("nan")) == EINVAL
+    assert r(V=(1 << 21) + 1) == EINVAL and r(V=1 << 21) == EWORKSPACE   # chunk masses staged on chip
+    assert r(dt=2) == EDTYPE and r(qdt=5) == EDTYPE
+    assert r(q=NULL) == EINVAL and r(ud=NULL) == EINVAL and r(ua=NULL) == EINVAL
+    assert r(B=0, l=NULL) == OK and r() == EWORKSPACE
+    assert lib.spec_tree_residual_workspace_bytes(2, 5, (1 << 21) + 1) == 0
+    n = lib.spec_tree_residual_workspace_bytes(32, 31, 32000)
+    assert n > lib.spec_tree_workspace_bytes(32, 31, 32000)   # plus the pass descriptors
