@@ -21,7 +21,7 @@ values the pages print, closed forms, or brute-force enumeration; none is
 from .numerics import (NONFINITE, BADTOKEN, BADUNIFORM, QZERO, RESIDUAL_EMPTY, BADTREE, OK,
                        decode, softmax_maxshift, softmax_online, target_probs)
 from .chain import verify_chain, verify_chain_one, FLAG_WINDOW
-from .greedy import verify_greedy, verify_greedy_one
+from .greedy import verify_greedy, verify_greedy_one, verify_greedy_stop_one
 from .tree import verify_tree, verify_tree_one, validate_tree, tree_expected_nodes
 from .tree_residual import verify_tree_residual, verify_tree_residual_one
 from . import laws
@@ -30,7 +30,7 @@ __all__ = [
     "OK", "NONFINITE", "BADTOKEN", "BADUNIFORM", "QZERO", "RESIDUAL_EMPTY", "BADTREE",
     "decode", "softmax_maxshift", "softmax_online", "target_probs",
     "verify_chain", "verify_chain_one", "FLAG_WINDOW",
-    "verify_greedy", "verify_greedy_one",
+    "verify_greedy", "verify_greedy_one", "verify_greedy_stop_one",
     "verify_tree", "verify_tree_one", "validate_tree", "tree_expected_nodes",
     "verify_tree_residual", "verify_tree_residual_one",
     "laws",

@@ -54,6 +54,7 @@ class ChainResult:
     weights: Optional[np.ndarray] = None               # terminal weights w (unnormalized)
     cdf_lo: float = float("nan")                       # C_{k-1} at the chosen k
     cdf_hi: float = float("nan")                       # C_k at the chosen k
+    finish: int = 0                                    # 0 open, 1 stop token emitted, 2 budget reached
 
 
 def inverse_cdf(w: np.ndarray, u: float):
@@ -71,12 +72,22 @@ def inverse_cdf(w: np.ndarray, u: float):
 
 
 def verify_chain_one(L: np.ndarray, Q: np.ndarray, x: np.ndarray, u: np.ndarray,
-                     temperature: float) -> ChainResult:
+                     temperature: float, stop_tokens=(), budget=None) -> ChainResult:
     """Verify one request.
 
     L: [gamma+1, V] float64 target logits; Q: [gamma, V] float64 draft probabilities;
     x: [gamma] draft tokens; u: [gamma+1] uniforms (u[i] for the accept test of draft
     i, u[gamma] for the terminal draw -- [M7.1] §0x04J: one terminal draw per round).
+
+    Stopping ([M7.1] §0x05B "Round Progress Includes Correction Or Bonus", §0x06 "KV
+    Commit And Rollback": stopping is applied before publication): an accepted draft in
+    `stop_tokens` ends the round after itself, and so does the accepted draft that uses
+    up the remaining output `budget` (None: no limit); neither emits a correction or a
+    bonus, and no later draft is tested.  A correction or bonus that is a stop token, or
+    that uses up the budget, is emitted once and finishes the request.  A budget of 0
+    dispatches no round (nothing is emitted).  `finish`: 1 after a stop token, 2 when the
+    budget is reached (a stop token wins a tie), else 0; accepted_len counts the emitted
+    drafts.
     """
     gamma = int(len(x))
     V = int(L.shape[1])
@@ -87,7 +98,12 @@ def verify_chain_one(L: np.ndarray, Q: np.ndarray, x: np.ndarray, u: np.ndarray,
         return ChainResult(status=code, accepted_len=-1, tokens=[], flagged=res.flagged,
                            m=res.m, logZ=res.logZ, p_x=res.p_x, q_x=res.q_x, a=res.a)
 
+    stop = set(int(t) for t in stop_tokens)
+    H = None if budget is None else int(budget)
+    if H is not None and H <= 0:
+        return ChainResult(status=OK, accepted_len=0, tokens=[], finish=2)
     A = gamma
+    end = None                 # (emitted drafts, finish) when the round stops without a draw
     for i in range(gamma):
         if not row_is_valid(L[i]):
             return fail(NONFINITE)
@@ -112,6 +128,17 @@ def verify_chain_one(L: np.ndarray, Q: np.ndarray, x: np.ndarray, u: np.ndarray,
         if not (u[i] < a):          # first rejection: stop here
             A = i
             break
+        if int(x[i]) in stop:       # an accepted stop token ends the round
+            end = (i + 1, 1)
+            break
+        if H is not None and i + 1 == H:   # the remaining budget is used up
+            end = (i + 1, 2)
+            break
+
+    if end is not None:
+        res.accepted_len, res.finish = end
+        res.tokens = [int(t) for t in x[:end[0]]]
+        return res
 
     if A == gamma:
         if not row_is_valid(L[gamma]):
@@ -139,6 +166,7 @@ def verify_chain_one(L: np.ndarray, Q: np.ndarray, x: np.ndarray, u: np.ndarray,
 
     res.accepted_len = A
     res.tokens = [int(t) for t in x[:A]] + [k]
+    res.finish = 1 if k in stop else (2 if H is not None and A + 1 == H else 0)
     res.W = W
     res.weights = w
     res.cdf_lo, res.cdf_hi = lo, hi
@@ -146,7 +174,7 @@ def verify_chain_one(L: np.ndarray, Q: np.ndarray, x: np.ndarray, u: np.ndarray,
 
 
 def verify_chain(logits, q, tokens, u, temperature, logit_dtype="f32", q_dtype="f32",
-                 requests=None):
+                 requests=None, stop_tokens=(), budget=None):
     """Batched chain verification, one request at a time.
 
     logits [B, gamma+1, V] (raw bf16 bits or fp32), q [B, gamma, V], tokens [B, gamma],
@@ -169,13 +197,15 @@ def verify_chain(logits, q, tokens, u, temperature, logit_dtype="f32", q_dtype="
         out_tokens=np.full((n, R), -1, np.int32),
         status=np.zeros(n, np.int32),
         flagged=np.zeros(n, bool),
+        finish=np.zeros(n, np.int32),
         stats=np.full((n, R, 4), np.nan),
         results=[],
     )
     for j, b in enumerate(idx):
         L = decode(logits[b], logit_dtype)
         Q = decode(q[b], q_dtype) if gamma > 0 else np.zeros((0, V))
-        r = verify_chain_one(L, Q, np.asarray(tokens[b]), np.asarray(u[b]), temperature)
+        r = verify_chain_one(L, Q, np.asarray(tokens[b]), np.asarray(u[b]), temperature, stop_tokens,
+                             None if budget is None else int(budget[b]))
         out["results"].append(r)
         out["status"][j] = r.status
         out["flagged"][j] = r.flagged
@@ -183,10 +213,11 @@ def verify_chain(logits, q, tokens, u, temperature, logit_dtype="f32", q_dtype="
             continue
         out["accepted_len"][j] = r.accepted_len
         out["out_tokens"][j, :len(r.tokens)] = r.tokens
+        out["finish"][j] = r.finish
         st = out["stats"][j]
         for i in range(len(r.a)):
             st[i] = (r.m[i], r.logZ[i], r.p_x[i], r.a[i])
-        if r.accepted_len == gamma:
+        if len(r.m) > gamma:        # the bonus row was reached
             st[gamma, 0] = r.m[gamma]
             st[gamma, 1] = r.logZ[gamma]
         st[gamma, 2] = r.W

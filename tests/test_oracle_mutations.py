@@ -17,7 +17,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 PIN_FILES = ["test_oracle_pins.py", "test_oracle_laws.py", "test_oracle_regression.py",
-             "test_oracle_tree_residual.py"]
+             "test_oracle_tree_residual.py", "test_oracle_stop.py"]
 
 # (file under oracle/, text as it stands, the planted mistake)
 MUTANTS = {
@@ -55,9 +55,9 @@ MUTANTS = {
     # greedy ([M7.1] §0x02D, [Tiny] "Normative greedy pseudocode")
     "greedy_last_tie": ("greedy.py", "return int(np.flatnonzero(row == row.max())[0])",
                         "return int(np.flatnonzero(row == row.max())[-1])"),
-    "greedy_no_correction": ("greedy.py", "return OK, i, [int(v) for v in x[:i]] + [t]",
-                             "return OK, i, [int(v) for v in x[:i]]"),
-    "greedy_bonus_row_off_by_one": ("greedy.py", "[first_argmax(L[gamma])]", "[first_argmax(L[gamma - 1])]"),
+    "greedy_no_correction": ("greedy.py", "return OK, i, [int(v) for v in x[:i]] + [t], (",
+                             "return OK, i, [int(v) for v in x[:i]], ("),
+    "greedy_bonus_row_off_by_one": ("greedy.py", "t = first_argmax(L[gamma])", "t = first_argmax(L[gamma - 1])"),
     # tree ([M7.7] §0x07E, §0x09, §0x0F, §0x0AA)
     "tree_any_node_with_token": ("tree.py", "if int(parents[c]) == v and int(node_tokens[c]) == y:",
                                  "if int(node_tokens[c]) == y:"),
@@ -80,6 +80,25 @@ MUTANTS = {
                                           "        for c in range(N - 1, v, -1):            # children"),
     "tree_residual_draw_with_accept_uniform": ("tree_residual.py", "        ud = float(u_draw[v])",
                                                "        ud = float(u_acc[v]) if v > 0 else float(u_draw[v])"),
+    # stop tokens and output budget ([M7.1] §0x05B, §0x06)
+    "stop_token_not_ending_round": ("chain.py", "            end = (i + 1, 1)\n", "            pass\n"),
+    "stop_token_not_emitted": ("chain.py", "res.tokens = [int(t) for t in x[:end[0]]]",
+                               "res.tokens = [int(t) for t in x[:end[0] - 1]]"),
+    "budget_off_by_one": ("chain.py", "if H is not None and i + 1 == H:", "if H is not None and i == H:"),
+    "zero_budget_runs_a_round": ("chain.py", "if H is not None and H <= 0:", "if H is not None and H < 0:"),
+    "stop_checked_before_accept": ("chain.py",
+                                   "        if not (u[i] < a):          # first rejection: stop here\n"
+                                   "            A = i\n            break\n"
+                                   "        if int(x[i]) in stop:       # an accepted stop token ends the round\n"
+                                   "            end = (i + 1, 1)\n            break\n",
+                                   "        if int(x[i]) in stop:       # an accepted stop token ends the round\n"
+                                   "            end = (i + 1, 1)\n            break\n"
+                                   "        if not (u[i] < a):          # first rejection: stop here\n"
+                                   "            A = i\n            break\n"),
+    "budget_finish_off_by_one": ("chain.py", "(2 if H is not None and A + 1 == H else 0)",
+                                 "(2 if H is not None and A == H else 0)"),
+    "greedy_stop_ignored": ("greedy.py", "        if xi in stop:\n", "        if xi in stop and i + 1 == gamma:\n"),
+    "greedy_budget_off_by_one": ("greedy.py", "        if H == i + 1:\n", "        if H == i:\n"),
     # laws ([M7.1] §0x05A-§0x05D, [Atlas] mechanism)
     "expected_tokens_off_by_one": ("laws.py", "return (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)",
                                    "return (1.0 - alpha ** gamma) / (1.0 - alpha)"),
