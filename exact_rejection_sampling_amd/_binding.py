@@ -36,9 +36,18 @@ _SIGNATURES = {
                                    _c_int, _c_int, _c_int, _c_float,
                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                    _c_void_p, _c_size_t, _c_void_p]),
+    "spec_verify_chain_stop": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                        _c_int, _c_int, _c_int, _c_float,
+                                        _c_void_p, _c_int, _c_void_p,
+                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                        _c_void_p, _c_size_t, _c_void_p]),
     "spec_verify_greedy": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int,
                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
                                     _c_void_p]),
+    "spec_verify_greedy_stop": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int,
+                                         _c_void_p, _c_int, _c_void_p,
+                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_void_p, _c_size_t, _c_void_p]),
     "spec_verify_tree": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_void_p,
                                   _c_int, _c_int, _c_int, _c_float,
                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -155,8 +164,23 @@ class PreparedCall:
         return self.out
 
 
+SPEC_MAX_STOP = 256
+
+
+def _stop_args(stop_tokens, budget, B, dev):
+    """Checks the stop-token list [n] and the budget [B] (int32 GPU tensors, either None)."""
+    if stop_tokens is not None:
+        _need(stop_tokens, "stop_tokens", dtype=torch.int32, device=dev)
+        if stop_tokens.dim() != 1 or stop_tokens.numel() > SPEC_MAX_STOP:
+            raise ValueError(f"stop_tokens must be 1-D with at most {SPEC_MAX_STOP} entries")
+    if budget is not None:
+        _need(budget, "budget", dtype=torch.int32, shape=(B,), device=dev)
+    n = 0 if stop_tokens is None else int(stop_tokens.numel())
+    return n
+
+
 def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature, with_stats,
-                workspace_tensor, out):
+                workspace_tensor, out, stop_tokens=None, budget=None):
     lib = load_library()
     _need(target_logits, "target_logits")
     if target_logits.dim() != 3:
@@ -174,45 +198,58 @@ def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
                    req_status=torch.empty(B, dtype=torch.int32, device=dev))
         if with_stats:
             out["stats"] = torch.empty(B, R, 4, dtype=torch.float32, device=dev)
+    stopping = stop_tokens is not None or budget is not None
+    n_stop = _stop_args(stop_tokens, budget, B, dev)
+    if stopping and "finish" not in out:
+        out["finish"] = torch.empty(B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     need = lib.spec_chain_workspace_bytes(B, G, V)
     if need == 0 and B > 0:
         raise SpecError(f"unsupported sizes B={B} gamma={G} V={V}")
     ws = workspace_tensor if workspace_tensor is not None else workspace("chain", need, dev, stream)
     wp, wn = _aligned_ws(ws)
-    args = (_ptr(target_logits), lt, _ptr(draft_probs), qt, _ptr(draft_tokens), _ptr(uniforms),
-            B, G, V, ctypes.c_float(float(temperature)),
-            _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
-            _ptr(out.get("stats")), wp, wn, ctypes.c_void_p(stream.cuda_stream))
-    keep = (target_logits, draft_probs, draft_tokens, uniforms, ws, stream)
-    return lib.spec_verify_chain, args, keep, out
+    head = (_ptr(target_logits), lt, _ptr(draft_probs), qt, _ptr(draft_tokens), _ptr(uniforms),
+            B, G, V, ctypes.c_float(float(temperature)))
+    keep = (target_logits, draft_probs, draft_tokens, uniforms, ws, stream, stop_tokens, budget)
+    if not stopping:
+        args = head + (_ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
+                       _ptr(out.get("stats")), wp, wn, ctypes.c_void_p(stream.cuda_stream))
+        return lib.spec_verify_chain, args, keep, out
+    args = head + (_ptr(stop_tokens), n_stop, _ptr(budget),
+                   _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
+                   _ptr(out["finish"]), _ptr(out.get("stats")), wp, wn, ctypes.c_void_p(stream.cuda_stream))
+    return lib.spec_verify_chain_stop, args, keep, out
 
 
 def spec_verify_chain(target_logits: torch.Tensor, draft_probs: torch.Tensor,
                       draft_tokens: torch.Tensor, uniforms: torch.Tensor, temperature: float,
                       *, with_stats: bool = False, workspace_tensor: Optional[torch.Tensor] = None,
-                      out: Optional[dict] = None) -> dict:
-    """Chain verification by rejection sampling (C entry point spec_verify_chain).
+                      out: Optional[dict] = None, stop_tokens: Optional[torch.Tensor] = None,
+                      budget: Optional[torch.Tensor] = None) -> dict:
+    """Chain verification by rejection sampling (C entry point spec_verify_chain, or
+    spec_verify_chain_stop when stop_tokens or budget is given).
 
     target_logits [B, gamma+1, V] bf16/fp32; draft_probs [B, gamma, V] fp32/bf16;
-    draft_tokens [B, gamma] int32; uniforms [B, gamma+1] fp32; temperature > 0.
-    Returns {accepted_len [B], out_tokens [B, gamma+1], req_status [B], stats?} (int32 /
-    fp32 GPU tensors, valid once the current stream reaches the call).
+    draft_tokens [B, gamma] int32; uniforms [B, gamma+1] fp32; temperature > 0;
+    stop_tokens [n] int32 (n <= 256); budget [B] int32 remaining output budgets.
+    Returns {accepted_len [B], out_tokens [B, gamma+1], req_status [B], stats?, finish?}
+    (int32 / fp32 GPU tensors, valid once the current stream reaches the call).
     """
     fn, args, _, out = _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
-                                   with_stats, workspace_tensor, out)
+                                   with_stats, workspace_tensor, out, stop_tokens, budget)
     _check(fn(*args))
     return out
 
 
 def prepare_chain(target_logits, draft_probs, draft_tokens, uniforms, temperature, *,
-                  with_stats=False, workspace_tensor=None, out=None) -> PreparedCall:
+                  with_stats=False, workspace_tensor=None, out=None, stop_tokens=None,
+                  budget=None) -> PreparedCall:
     """spec_verify_chain with its arguments checked and marshalled once (see PreparedCall)."""
     return PreparedCall(*_chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
-                                     with_stats, workspace_tensor, out))
+                                     with_stats, workspace_tensor, out, stop_tokens, budget))
 
 
-def _greedy_args(target_logits, draft_tokens, workspace_tensor, out):
+def _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens=None, budget=None):
     lib = load_library()
     _need(target_logits, "target_logits")
     if target_logits.dim() != 3:
@@ -226,34 +263,47 @@ def _greedy_args(target_logits, draft_tokens, workspace_tensor, out):
         out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
                    out_tokens=torch.empty(B, R, dtype=torch.int32, device=dev),
                    req_status=torch.empty(B, dtype=torch.int32, device=dev))
+    stopping = stop_tokens is not None or budget is not None
+    n_stop = _stop_args(stop_tokens, budget, B, dev)
+    if stopping and "finish" not in out:
+        out["finish"] = torch.empty(B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     need = lib.spec_greedy_workspace_bytes(B, G, V)
     if need == 0 and B > 0:
         raise SpecError(f"unsupported sizes B={B} gamma={G} V={V}")
     ws = workspace_tensor if workspace_tensor is not None else workspace("greedy", need, dev, stream)
     wp, wn = _aligned_ws(ws)
-    args = (_ptr(target_logits), lt, _ptr(draft_tokens), B, G, V,
-            _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
-            wp, wn, ctypes.c_void_p(stream.cuda_stream))
-    keep = (target_logits, draft_tokens, ws, stream)
-    return lib.spec_verify_greedy, args, keep, out
+    keep = (target_logits, draft_tokens, ws, stream, stop_tokens, budget)
+    head = (_ptr(target_logits), lt, _ptr(draft_tokens), B, G, V)
+    if not stopping:
+        args = head + (_ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
+                       wp, wn, ctypes.c_void_p(stream.cuda_stream))
+        return lib.spec_verify_greedy, args, keep, out
+    args = head + (_ptr(stop_tokens), n_stop, _ptr(budget),
+                   _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
+                   _ptr(out["finish"]), wp, wn, ctypes.c_void_p(stream.cuda_stream))
+    return lib.spec_verify_greedy_stop, args, keep, out
 
 
 def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor, *,
                        workspace_tensor: Optional[torch.Tensor] = None,
-                       out: Optional[dict] = None) -> dict:
-    """Greedy argmax-match verification (C entry point spec_verify_greedy).
+                       out: Optional[dict] = None, stop_tokens: Optional[torch.Tensor] = None,
+                       budget: Optional[torch.Tensor] = None) -> dict:
+    """Greedy argmax-match verification (C entry point spec_verify_greedy, or
+    spec_verify_greedy_stop when stop_tokens or budget is given).
 
-    target_logits [B, gamma+1, V] bf16/fp32; draft_tokens [B, gamma] int32.
+    target_logits [B, gamma+1, V] bf16/fp32; draft_tokens [B, gamma] int32; stop_tokens,
+    budget as for spec_verify_chain.
     """
-    fn, args, _, out = _greedy_args(target_logits, draft_tokens, workspace_tensor, out)
+    fn, args, _, out = _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens, budget)
     _check(fn(*args))
     return out
 
 
-def prepare_greedy(target_logits, draft_tokens, *, workspace_tensor=None, out=None) -> PreparedCall:
+def prepare_greedy(target_logits, draft_tokens, *, workspace_tensor=None, out=None, stop_tokens=None,
+                   budget=None) -> PreparedCall:
     """spec_verify_greedy with its arguments checked and marshalled once (see PreparedCall)."""
-    return PreparedCall(*_greedy_args(target_logits, draft_tokens, workspace_tensor, out))
+    return PreparedCall(*_greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens, budget))
 
 
 def _tree_args(node_logits, node_tokens, parents, uniforms, temperature, workspace_tensor, out):

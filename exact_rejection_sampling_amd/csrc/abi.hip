@@ -22,6 +22,17 @@ bool sizes_ok(int B, int gamma, int V) {
          V <= SPEC_MAX_VOCAB;
 }
 int chunks(long V, long per) { return static_cast<int>((V + per - 1) / per); }
+bool stop_ok(const int32_t* stop_tokens, int n_stop) {
+  return n_stop >= 0 && n_stop <= SPEC_MAX_STOP && (n_stop == 0 || stop_tokens != nullptr);
+}
+sv::StopSpec stop_spec(const int32_t* stop_tokens, int n_stop, const int32_t* budget, int32_t* finish) {
+  sv::StopSpec st;
+  st.stop = n_stop > 0 ? stop_tokens : nullptr;
+  st.n_stop = n_stop;
+  st.budget = budget;
+  st.finish = finish;
+  return st;
+}
 }  // namespace
 
 extern "C" {
@@ -85,7 +96,19 @@ spec_status spec_verify_chain(const void* target_logits, int logit_dtype, const 
                               int gamma, int V, float temperature, int32_t* accepted_len,
                               int32_t* out_tokens, int32_t* req_status, float* stats,
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!sizes_ok(B, gamma, V) || !temperature_ok(temperature)) return SPEC_EINVAL;
+  return spec_verify_chain_stop(target_logits, logit_dtype, draft_probs, q_dtype, draft_tokens, uniforms, B,
+                                gamma, V, temperature, nullptr, 0, nullptr, accepted_len, out_tokens,
+                                req_status, nullptr, stats, workspace, workspace_bytes, stream);
+}
+
+spec_status spec_verify_chain_stop(const void* target_logits, int logit_dtype, const void* draft_probs,
+                                   int q_dtype, const int32_t* draft_tokens, const float* uniforms, int B,
+                                   int gamma, int V, float temperature, const int32_t* stop_tokens,
+                                   int n_stop, const int32_t* budget, int32_t* accepted_len,
+                                   int32_t* out_tokens, int32_t* req_status, int32_t* finish, float* stats,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!sizes_ok(B, gamma, V) || !temperature_ok(temperature) || !stop_ok(stop_tokens, n_stop))
+    return SPEC_EINVAL;
   if (!dtype_ok(logit_dtype) || !dtype_ok(q_dtype)) return SPEC_EDTYPE;
   if (!sv::grid_fits(sv::chain_blocks(B, gamma, V))) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
@@ -104,6 +127,7 @@ spec_status spec_verify_chain(const void* target_logits, int logit_dtype, const 
   p.out_tokens = out_tokens;
   p.req_status = req_status;
   p.stats = stats;
+  p.st = stop_spec(stop_tokens, n_stop, budget, finish);
   p.part = reinterpret_cast<float2*>(ws + L.part);
   p.gath = reinterpret_cast<unsigned long long*>(ws + L.gath);
   p.tmass = reinterpret_cast<double*>(ws + L.tmass);
@@ -128,7 +152,17 @@ spec_status spec_verify_greedy(const void* target_logits, int logit_dtype, const
                                int B, int gamma, int V, int32_t* accepted_len, int32_t* out_tokens,
                                int32_t* req_status, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
-  if (!sizes_ok(B, gamma, V)) return SPEC_EINVAL;
+  return spec_verify_greedy_stop(target_logits, logit_dtype, draft_tokens, B, gamma, V, nullptr, 0, nullptr,
+                                 accepted_len, out_tokens, req_status, nullptr, workspace, workspace_bytes,
+                                 stream);
+}
+
+spec_status spec_verify_greedy_stop(const void* target_logits, int logit_dtype, const int32_t* draft_tokens,
+                                    int B, int gamma, int V, const int32_t* stop_tokens, int n_stop,
+                                    const int32_t* budget, int32_t* accepted_len, int32_t* out_tokens,
+                                    int32_t* req_status, int32_t* finish, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  if (!sizes_ok(B, gamma, V) || !stop_ok(stop_tokens, n_stop)) return SPEC_EINVAL;
   if (!dtype_ok(logit_dtype)) return SPEC_EDTYPE;
   if (!sv::grid_fits(sv::greedy_blocks(B, gamma, V))) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
@@ -143,6 +177,7 @@ spec_status spec_verify_greedy(const void* target_logits, int logit_dtype, const
   p.accepted_len = accepted_len;
   p.out_tokens = out_tokens;
   p.req_status = req_status;
+  p.st = stop_spec(stop_tokens, n_stop, budget, finish);
   p.part = reinterpret_cast<unsigned long long*>(ws + L.part);
   p.B = B;
   p.G = gamma;

@@ -146,6 +146,7 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
   // wave 0, lane i < G: draft position i -- its gather record and uniform
   unsigned long long g[3] = {0ull, 0ull, 0ull};
   float ui = 0.0f, ut = 0.0f;
+  const int H = p.st.budget ? p.st.budget[b] : INT32_MAX;   // remaining output budget
   if (wave == 0 && lane < G) {
     const unsigned long long* rec = gather_rec(p, b, lane);
     g[0] = fetch_u64(rec);
@@ -216,8 +217,9 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
   }
   __syncthreads();
   if (wave == 0) {
-    // lane i < G: draft position i, checked in the order a round reaches it
-    int code = 0;
+    // lane i < G: draft position i, checked in the order a round reaches it; an accepted
+    // draft that is a stop token, or that uses up the budget, ends the round after itself
+    int code = 0, fin = 0;
     bool reject = false;
     double px = NAN, a = NAN;
     if (lane < G) {
@@ -237,22 +239,44 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
           px = exp2((double)lx * (double)c2 - (double)rs.r[lane]) / rs.z[lane];
           a = fmin(1.0, px / (double)qx);
           reject = !((double)ui < a);
+          if (!reject) {
+            if (p.st.n_stop > 0 && is_stop_token(p.st.stop, p.st.n_stop, x)) fin = SPEC_FINISH_STOP;
+            else if (lane + 1 == H) fin = SPEC_FINISH_BUDGET;
+          }
         }
       }
       rs.px[lane] = px;
       rs.a[lane] = a;
     }
-    const unsigned long long stop = __ballot(lane < G && (code != 0 || reject));
-    const int A = stop ? (__ffsll((long long)stop) - 1) : G;
-    int status = __shfl(code, A < G ? A : 0, kWave);
-    if (A == G) status = rs.bad[G] ? SPEC_REQ_NONFINITE : 0;
-    if (status == 0 && !(ut >= 0.0f && ut < 1.0f)) status = SPEC_REQ_BADUNIFORM;
+    const unsigned long long ev = __ballot(lane < G && (code != 0 || reject || fin != 0));
+    const int e = ev ? (__ffsll((long long)ev) - 1) : G;   // the first event
+    const int code_e = __shfl(code, e < G ? e : 0, kWave);
+    const int fin_e = __shfl(fin, e < G ? e : 0, kWave);
+    int A = e, status = 0, draw = 1, finish = 0;
+    if (e < G && fin_e != 0) {          // the round ends on draft e, with no draw
+      A = e + 1;
+      draw = 0;
+      finish = fin_e;
+    } else {
+      status = e < G ? code_e : (rs.bad[G] ? SPEC_REQ_NONFINITE : 0);
+      if (status == 0 && !(ut >= 0.0f && ut < 1.0f)) status = SPEC_REQ_BADUNIFORM;
+    }
+    if (H <= 0) {                       // no budget left: no round, nothing checked
+      A = 0;
+      status = 0;
+      draw = 0;
+      finish = SPEC_FINISH_BUDGET;
+    }
     if (s_timeout) status = SPEC_REQ_INTERNAL;
     if (lane == 0) {
+      const bool drawn = status == 0 && draw;
       s_dec.A = status == 0 ? A : -1;
       s_dec.status = status;
-      s_dec.r_ref = status == 0 ? rs.r[A] : 0.0f;
-      s_dec.inv_z = status == 0 ? (float)(1.0 / rs.z[A]) : 0.0f;
+      s_dec.draw = drawn ? 1 : 0;
+      s_dec.finish = finish;
+      s_dec.H = H;
+      s_dec.r_ref = drawn ? rs.r[A] : 0.0f;
+      s_dec.inv_z = drawn ? (float)(1.0 / rs.z[A]) : 0.0f;
     }
   }
   __syncthreads();
@@ -313,6 +337,21 @@ __device__ __forceinline__ double block_mass(const float (&w)[kTermSlabs][8], bo
 // Chunk masses are read in runs of up to kMassRegs per thread and kept in registers;
 // longer runs (vocabularies beyond 8M) re-read the published words.
 constexpr int kMassRegs = 8;
+
+// Statistics of row i: (m, log Z, p(x), a) of a reached draft row, (m, log Z, NaN, NaN)
+// of the reached bonus row, NaN otherwise.
+__device__ __forceinline__ void row_stats(const ChainParams& p, const RowState& rs, int i, bool reached,
+                                          float (&v)[4]) {
+  v[0] = v[1] = v[2] = v[3] = NAN;
+  if (!reached) return;
+  const double m_nat = (double)rs.m[i] * p.inv_t;
+  v[0] = (float)m_nat;
+  v[1] = (float)(log(rs.z[i]) + (double)rs.r[i] * kLn2 - m_nat);
+  if (i < p.G) {
+    v[2] = (float)rs.px[i];
+    v[3] = (float)rs.a[i];
+  }
+}
 
 // The selector of request b: every other chunk's mass is awaited; then the chunk where the
 // running mass passes u_gamma * W is rescanned in vocabulary order and the outputs are
@@ -424,6 +463,11 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
   // 3. outputs
   const int A = d.A;
   const int status = s_timeout ? SPEC_REQ_INTERNAL : (failed ? SPEC_REQ_RESIDUAL_EMPTY : 0);
+  // a terminal token that is a stop token, or that uses up the budget, finishes the request
+  int finish = 0;
+  if (p.st.n_stop > 0 && block_is_stop(p.st.stop, p.st.n_stop, k)) finish = SPEC_FINISH_STOP;
+  else if (A + 1 == d.H) finish = SPEC_FINISH_BUDGET;
+  if (status != 0) finish = 0;
   for (int i = tid; i < p.R; i += kBlock) {
     int v = -1;
     if (status == 0) {
@@ -437,17 +481,8 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
     // is reached, W in column 2; everything else NaN, and everything on failure
     float* st = p.stats + (size_t)b * p.R * 4;
     for (int i = tid; i < p.R; i += kBlock) {
-      float v[4] = {NAN, NAN, NAN, NAN};
-      const bool reached = status == 0 && (i < G ? i <= A : A == G);
-      if (reached) {
-        const double m_nat = (double)rs.m[i] * p.inv_t;
-        v[0] = (float)m_nat;
-        v[1] = (float)(log(rs.z[i]) + (double)rs.r[i] * kLn2 - m_nat);
-        if (i < G) {
-          v[2] = (float)rs.px[i];
-          v[3] = (float)rs.a[i];
-        }
-      }
+      float v[4];
+      row_stats(p, rs, i, status == 0 && (i < G ? i <= A : A == G), v);
       if (i == G && status == 0) v[2] = (float)W;
 #pragma unroll
       for (int c = 0; c < 4; ++c) st[i * 4 + c] = v[c];
@@ -456,12 +491,15 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
   if (tid == 0) {
     p.accepted_len[b] = status == 0 ? A : -1;
     p.req_status[b] = status;
+    if (p.st.finish) p.st.finish[b] = finish;
   }
 }
 
-// A failed request (the decision's status is not OK): the selector writes the failure
-// record once every other terminal item has signalled that it is done with the request.
-__device__ void chain_fail(const ChainParams& p, int b, int status) {
+// A request with no terminal draw -- a failed request, or a round that ended on an
+// accepted draft (a stop token, or the last token of the budget) or had no budget left:
+// the selector writes its record once every other terminal item has signalled that it is
+// done with the request.
+__device__ void chain_nodraw(const ChainParams& p, int b, const ChainDecision& d, const RowState& rs) {
   const int tid = threadIdx.x;
   __shared__ int s_lost;
   if (tid == 0) s_lost = 0;
@@ -470,13 +508,23 @@ __device__ void chain_fail(const ChainParams& p, int b, int status) {
   for (int c = tid; c < p.S2 - 1; c += kBlock)
     if (await_u64(reinterpret_cast<const unsigned long long*>(tm + c)) == 0ull) s_lost = 1;
   __syncthreads();
-  const int code = s_lost ? SPEC_REQ_INTERNAL : status;
-  for (int i = tid; i < p.R; i += kBlock) p.out_tokens[(size_t)b * p.R + i] = -1;
-  if (p.stats)
-    for (int i = tid; i < p.R * 4; i += kBlock) p.stats[(size_t)b * p.R * 4 + i] = NAN;
+  const int code = s_lost ? SPEC_REQ_INTERNAL : d.status;
+  const int A = code == 0 ? d.A : 0;   // drafts emitted; their rows are the ones tested
+  for (int i = tid; i < p.R; i += kBlock)
+    p.out_tokens[(size_t)b * p.R + i] = i < A ? p.tokens[(size_t)b * p.G + i] : -1;
+  if (p.stats) {
+    float* st = p.stats + (size_t)b * p.R * 4;
+    for (int i = tid; i < p.R; i += kBlock) {
+      float v[4];
+      row_stats(p, rs, i, i < A, v);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) st[i * 4 + c] = v[c];
+    }
+  }
   if (tid == 0) {
-    p.accepted_len[b] = -1;
+    p.accepted_len[b] = code == 0 ? A : -1;
     p.req_status[b] = code;
+    if (p.st.finish) p.st.finish[b] = code == 0 ? d.finish : 0;
   }
 }
 
@@ -515,14 +563,14 @@ __device__ void terminal_item(const ChainParams& p, int b, int c) {
   __shared__ ChainDecision s_dec;
   chain_decide<DT>(p, b, s_rs, s_dec);
   const ChainDecision d = s_dec;
-  if (d.status != 0) {
+  if (d.status != 0 || !d.draw) {
     if (c != p.S2 - 1) {
       // no mass to contribute: a NaN marker says only that this item is done with the
       // request's words
       if (threadIdx.x == 0) publish_mass(p.tmass + (size_t)b * p.S2 + c, NAN);
       return;
     }
-    chain_fail(p, b, d.status);
+    chain_nodraw(p, b, d, s_rs);
     __syncthreads();
     chain_clear(p, b);
     return;

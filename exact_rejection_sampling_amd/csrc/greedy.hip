@@ -116,9 +116,10 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   unsigned long long* part_b = p.part + (size_t)b * p.R * p.SL;
   if (tid == 0) s_lost = 0;
-  // wave 0's draft tokens, fetched while the summaries are awaited
+  // wave 0's draft tokens and the remaining budget, fetched while the summaries are awaited
   int x = 0;
   if (wave == 0 && lane < p.G) x = p.tokens[(size_t)b * p.G + lane];
+  const int H = p.st.budget ? p.st.budget[b] : INT32_MAX;
   __syncthreads();
   for (int i = wave; i < p.R; i += kWavesPerBlock) {
     const unsigned long long* part = part_b + (size_t)i * p.SL;
@@ -151,29 +152,60 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
   for (int j = tid; j < p.R * p.SL; j += kBlock) clear_u64(part_b + j);
   if (wave != 0) return;
   const int G = p.G;
-  int code = 0;
+  // lane i < G: draft position i; a matching draft that is a stop token, or that uses up
+  // the budget, ends the round after itself ([Tiny] "Normative greedy pseudocode")
+  int code = 0, fin = 0;
   bool mismatch = false;
   if (lane < G) {
-    if (s_bad[lane]) code = SPEC_REQ_NONFINITE;
-    else if (x < 0 || x >= p.V) code = SPEC_REQ_BADTOKEN;
-    else mismatch = (x != s_arg[lane]);
+    if (s_bad[lane]) {
+      code = SPEC_REQ_NONFINITE;
+    } else if (x < 0 || x >= p.V) {
+      code = SPEC_REQ_BADTOKEN;
+    } else {
+      mismatch = (x != s_arg[lane]);
+      if (!mismatch) {
+        if (p.st.n_stop > 0 && is_stop_token(p.st.stop, p.st.n_stop, x)) fin = SPEC_FINISH_STOP;
+        else if (lane + 1 == H) fin = SPEC_FINISH_BUDGET;
+      }
+    }
   }
-  const unsigned long long stop = __ballot(lane < G && (code != 0 || mismatch));
-  const int A = stop ? (__ffsll((long long)stop) - 1) : G;
-  int status = __shfl(code, A < G ? A : 0, kWave);
-  if (A == G) status = s_bad[G] ? SPEC_REQ_NONFINITE : 0;
+  const unsigned long long ev = __ballot(lane < G && (code != 0 || mismatch || fin != 0));
+  const int e = ev ? (__ffsll((long long)ev) - 1) : G;   // the first event
+  const int code_e = __shfl(code, e < G ? e : 0, kWave);
+  const int fin_e = __shfl(fin, e < G ? e : 0, kWave);
+  int A = e, status = 0, finish = 0;
+  bool draw = true;
+  if (e < G && fin_e != 0) {           // the round ends on draft e with no target token
+    A = e + 1;
+    draw = false;
+    finish = fin_e;
+  } else {
+    status = e < G ? code_e : (s_bad[G] ? SPEC_REQ_NONFINITE : 0);
+  }
+  if (H <= 0) {                        // no budget left: no round, nothing checked
+    A = 0;
+    status = 0;
+    draw = false;
+    finish = SPEC_FINISH_BUDGET;
+  }
   if (s_lost) status = SPEC_REQ_INTERNAL;
+  if (status == 0 && draw) {           // the target token at A
+    const int t = s_arg[A];
+    finish = (p.st.n_stop > 0 && is_stop_token(p.st.stop, p.st.n_stop, t)) ? SPEC_FINISH_STOP
+             : (A + 1 == H ? SPEC_FINISH_BUDGET : 0);
+  }
   for (int i = lane; i < p.R; i += kWave) {
     int v = -1;
     if (status == 0) {
       if (i < A) v = p.tokens[(size_t)b * G + i];
-      else if (i == A) v = s_arg[A];
+      else if (i == A && draw) v = s_arg[A];
     }
     p.out_tokens[(size_t)b * p.R + i] = v;
   }
   if (lane == 0) {
     p.accepted_len[b] = status == 0 ? A : -1;
     p.req_status[b] = status;
+    if (p.st.finish) p.st.finish[b] = status == 0 ? finish : 0;
   }
 }
 

@@ -11,10 +11,24 @@ namespace sv {
 // Per-request decision of the chain verifier: every terminal block of a request computes
 // it from the request's published summaries.
 struct ChainDecision {
-  int32_t A;        // first rejected draft (gamma if all accepted); -1 on error
+  int32_t A;        // emitted drafts: the first rejected draft (gamma if all accepted), or
+                    // the drafts up to the one that ended the round; -1 on error
   int32_t status;   // SPEC_REQ_*
+  int32_t draw;     // 1: a terminal token is drawn from row A; 0: the round ended on an
+                    // accepted draft (stop token or budget), or the budget was 0
+  int32_t finish;   // SPEC_FINISH_* of a round that ends without a draw
+  int32_t H;        // remaining output budget (INT32_MAX when none is given)
   float r_ref;      // reference exponent of the terminal row: fp32(max logit * c2)
   float inv_z;      // 1 / Z of the terminal row (Z relative to r_ref, base 2)
+};
+
+// Stop tokens and output budget of a round (spec_verify_*_stop); n_stop = 0 and a null
+// budget give the plain verifiers.
+struct StopSpec {
+  const int32_t* stop;       // [n_stop] stop tokens (entries outside [0, V) never match)
+  const int32_t* budget;     // [B] remaining output budget per request, or null
+  int32_t* finish;           // [B] out: SPEC_FINISH_*, or null
+  int n_stop;
 };
 
 struct ChainParams {
@@ -26,6 +40,7 @@ struct ChainParams {
   int32_t* out_tokens;       // [B, R]
   int32_t* req_status;       // [B]
   float* stats;              // [B, R, 4] or null
+  StopSpec st;
   // workspace
   float2* part;              // [B*R*SL] block summaries (raw max, Z)
   unsigned long long* gath;  // [B*G*3] draft token, its logit, its draft probability
@@ -56,6 +71,7 @@ struct GreedyParams {
   int32_t* accepted_len;
   int32_t* out_tokens;
   int32_t* req_status;
+  StopSpec st;
   unsigned long long* part;  // [B*R*SL] packed GreedyPart, one per slice
   int B, G, R, V, P, CPW, SL;
   int LAG;                   // requests between a request's streaming blocks and its decider

@@ -2,7 +2,8 @@
  * spec_verify.h -- C ABI of libspec_verify.so: batched target-side verification for
  * exact speculative decoding on AMD Instinct MI355X (gfx950).
  *
- * Four entry points, one per verification rule:
+ * Four verification rules, each one entry point (the chain and greedy rules also have a
+ * *_stop variant that applies stop tokens and an output budget inside the round):
  *   spec_verify_chain          rejection-sampling verification of a draft chain
  *   spec_verify_greedy         argmax-match verification of a draft chain
  *   spec_verify_tree           tree verification by target-sample membership
@@ -70,6 +71,7 @@ extern "C" {
 #define SPEC_MAX_GAMMA  63          /* gamma: draft tokens per request */
 #define SPEC_MAX_VOCAB  (1 << 28)   /* V */
 #define SPEC_MAX_NODES  4096        /* N: tree nodes per request */
+#define SPEC_MAX_STOP   256         /* n_stop: stop tokens of the *_stop entry points */
 #define SPEC_MIN_TEMPERATURE 0x1p-20f
 #define SPEC_MAX_TEMPERATURE 0x1p+20f
 
@@ -99,6 +101,14 @@ enum {
   SPEC_REQ_INTERNAL = 7         /* an internal wait between blocks hit its bound (not
                                    expected; the request's outputs are not valid, and the
                                    workspace must be zero-filled again before reuse) */
+};
+
+/* How a request's round ended (the finish output of the *_stop entry points). */
+enum {
+  SPEC_FINISH_NONE = 0,     /* the request goes on */
+  SPEC_FINISH_STOP = 1,     /* the last emitted token is a stop token */
+  SPEC_FINISH_BUDGET = 2    /* the emitted tokens used up the remaining budget (or it was
+                               already 0); a stop token wins a tie */
 };
 
 /* ------------------------------------------------------------------ chain ---
@@ -146,6 +156,37 @@ spec_status spec_verify_chain(const void* target_logits, int logit_dtype,
                               float* stats, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/* Chain verification with stop tokens and an output budget ([M7.1] §0x05B "Round
+ * Progress Includes Correction Or Bonus": progress is min(A + 1, H), H the distance to
+ * the first emitted stop token or the remaining budget; §0x06 "KV Commit And Rollback":
+ * stopping is applied before anything is published; [Tiny] "Normative stochastic
+ * pseudocode"):
+ *   budget[b] <= 0: no round -- nothing is read or checked, nothing is emitted,
+ *         accepted_len 0, finish SPEC_FINISH_BUDGET;
+ *   otherwise the tests run as in spec_verify_chain, and an ACCEPTED draft x_i that is a
+ *         stop token, or with i + 1 == budget[b], ends the round after itself: the
+ *         emitted tokens are x_0..x_i (accepted_len = i + 1), no terminal token is drawn,
+ *         and nothing after draft i is read or checked (row gamma and u_gamma included);
+ *   otherwise the terminal token is emitted as usual, and finish reports whether it is a
+ *         stop token, or whether A + 1 == budget[b].
+ * stop_tokens  [n_stop] int32 device array, 0 <= n_stop <= SPEC_MAX_STOP (may be NULL
+ *              when n_stop = 0); an entry outside [0, V) never matches.
+ * budget       [B] int32 device array of remaining output budgets, or NULL (no limit).
+ * finish       [B] int32 out (SPEC_FINISH_*; 0 for a failed request), or NULL.
+ * stats        rows tested by a round that ended on a draft keep their statistics; the
+ *              bonus row and W stay NaN.
+ * Every other argument is as for spec_verify_chain, whose workspace it uses; with
+ * n_stop = 0 and budget = NULL the outputs are those of spec_verify_chain.
+ */
+spec_status spec_verify_chain_stop(const void* target_logits, int logit_dtype,
+                                   const void* draft_probs, int q_dtype,
+                                   const int32_t* draft_tokens, const float* uniforms,
+                                   int B, int gamma, int V, float temperature,
+                                   const int32_t* stop_tokens, int n_stop, const int32_t* budget,
+                                   int32_t* accepted_len, int32_t* out_tokens, int32_t* req_status,
+                                   int32_t* finish, float* stats, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
 /* ----------------------------------------------------------------- greedy ---
  * Argmax-match verification ([M7.1] §0x02D: longest-prefix validation is exact for
  * greedy decoding; [Tiny] "Normative greedy pseudocode"):
@@ -160,6 +201,19 @@ spec_status spec_verify_greedy(const void* target_logits, int logit_dtype,
                                const int32_t* draft_tokens, int B, int gamma, int V,
                                int32_t* accepted_len, int32_t* out_tokens, int32_t* req_status,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Greedy verification with stop tokens and an output budget ([Tiny] "Normative greedy
+ * pseudocode": a matching draft that is an active stop token, or that uses up the
+ * remaining budget, ends the round after itself; a budget of 0 emits nothing).  The
+ * rules, stop_tokens, budget and finish are those of spec_verify_chain_stop; the
+ * workspace is that of spec_verify_greedy.
+ */
+spec_status spec_verify_greedy_stop(const void* target_logits, int logit_dtype,
+                                    const int32_t* draft_tokens, int B, int gamma, int V,
+                                    const int32_t* stop_tokens, int n_stop, const int32_t* budget,
+                                    int32_t* accepted_len, int32_t* out_tokens, int32_t* req_status,
+                                    int32_t* finish, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /* ------------------------------------------------------------------- tree ---
  * Tree verification by target-sample membership ([M7.7] §0x04B and §0x09: accept a

@@ -310,6 +310,26 @@ def make_tree_residual(B: int, N: int, V: int, *, seed: int, logit_dtype: str = 
 
 
 # --------------------------------------------------------------------------- configs
+def make_stop(tokens: np.ndarray, V: int, *, seed: int, n_stop: int = 4, from_drafts: int = 2,
+              budget_lo: int = 0, budget_hi: int = None):
+    """Stop-token list and per-request output budgets for a batch of draft chains.
+
+    `from_drafts` of the n_stop stop tokens are draft tokens picked at random positions
+    (so accepted stop tokens occur), the rest uniform on [0, V).  Budgets are uniform on
+    [budget_lo, budget_hi] (default gamma + 2, past the longest round).  Returns
+    (stop int32 [n_stop], budget int32 [B]).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, G = tokens.shape
+    picks = []
+    if G > 0 and from_drafts > 0:
+        picks = tokens[rng.integers(0, B, from_drafts), rng.integers(0, G, from_drafts)].tolist()
+    picks += rng.integers(0, V, max(0, n_stop - len(picks))).tolist()
+    hi = G + 2 if budget_hi is None else budget_hi
+    budget = rng.integers(budget_lo, hi + 1, B).astype(np.int32)
+    return np.asarray(picks[:n_stop], dtype=np.int32), budget
+
+
 CONFIGS = {
     # chain, correctness scale: fp32 logits ~ N(0, 2^2), drafter noise 0.5, T = 1
     1: dict(kind="chain", B=4, gamma=4, V=32, logit_dtype="f32", sigma=2.0, boost_frac=0.0,

@@ -148,3 +148,19 @@ def test_tree_residual_host_validation():
     assert lib.spec_tree_residual_workspace_bytes(2, 5, (1 << 21) + 1) == 0
     n = lib.spec_tree_residual_workspace_bytes(32, 31, 32000)
     assert n > lib.spec_tree_workspace_bytes(32, 31, 32000)   # plus the pass descriptors
+
+
+def test_stop_variants_host_validation():
+    lib = sv.load_library()
+    c = lambda **k: lib.spec_verify_chain_stop(
+        FAKE, 0, FAKE, 0, FAKE, FAKE, k.get("B", 2), 2, 16, ctypes.c_float(1.0),
+        k.get("stop", FAKE), k.get("n", 1), k.get("budget", NULL), FAKE, FAKE, FAKE, k.get("fin", NULL), NULL,
+        NULL, 0, NULL)
+    assert c(n=-1) == EINVAL and c(n=257) == EINVAL and c(stop=NULL) == EINVAL
+    assert c(n=0, stop=NULL) == EWORKSPACE and c(n=256) == EWORKSPACE   # only the workspace is missing
+    assert c(budget=FAKE, fin=FAKE) == EWORKSPACE and c(B=0) == OK
+    g = lambda **k: lib.spec_verify_greedy_stop(
+        FAKE, 1, FAKE, k.get("B", 2), 2, 16, k.get("stop", FAKE), k.get("n", 1), NULL, FAKE, FAKE, FAKE,
+        NULL, NULL, 0, NULL)
+    assert g(n=-1) == EINVAL and g(n=257) == EINVAL and g(stop=NULL) == EINVAL
+    assert g(n=0, stop=NULL) == EWORKSPACE and g(B=0) == OK
