@@ -17,7 +17,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 PIN_FILES = ["test_oracle_pins.py", "test_oracle_laws.py", "test_oracle_regression.py",
-             "test_oracle_tree_residual.py", "test_oracle_stop.py"]
+             "test_oracle_tree_residual.py", "test_oracle_stop.py", "test_oracle_tree_greedy.py"]
 
 # (file under oracle/, text as it stands, the planted mistake)
 MUTANTS = {
@@ -80,6 +80,16 @@ MUTANTS = {
                                           "        for c in range(N - 1, v, -1):            # children"),
     "tree_residual_draw_with_accept_uniform": ("tree_residual.py", "        ud = float(u_draw[v])",
                                                "        ud = float(u_acc[v]) if v > 0 else float(u_draw[v])"),
+    # greedy tree ([M16] "Verify the Tree -- and Why It's Exact")
+    "tree_greedy_last_tie": ("tree_greedy.py", "y = first_argmax(L[v])",
+                             "y = int(np.flatnonzero(L[v] == L[v].max())[-1])"),
+    "tree_greedy_child_row": ("tree_greedy.py", "y = first_argmax(L[v])", "y = first_argmax(L[min(v + 1, N - 1)])"),
+    "tree_greedy_no_bonus": ("tree_greedy.py", "tokens=[int(node_tokens[c]) for c in path] + [y])",
+                             "tokens=[int(node_tokens[c]) for c in path])"),
+    "tree_greedy_any_node": ("tree_greedy.py", "if int(parents[c]) == v and int(node_tokens[c]) == y:",
+                             "if int(node_tokens[c]) == y:"),
+    "tree_greedy_last_sibling": ("tree_greedy.py", "                nxt = c\n                break\n",
+                                 "                nxt = c\n"),
     # stop tokens and output budget ([M7.1] §0x05B, §0x06)
     "stop_token_not_ending_round": ("chain.py", "            end = (i + 1, 1)\n", "            pass\n"),
     "stop_token_not_emitted": ("chain.py", "res.tokens = [int(t) for t in x[:end[0]]]",
