@@ -4,23 +4,27 @@ The work runs in hand-written HIP kernels for gfx950 inside libspec_verify.so (C
 declared in include/spec_verify.h).  This package is the thin Python binding: torch
 tensors in, torch tensors out, on the current CUDA (HIP) stream.
 
-    spec_verify_chain   rejection-sampling verification of draft chains
-    spec_verify_greedy  argmax-match verification
-    spec_verify_tree    tree verification by target-sample membership
+    spec_verify_chain          rejection-sampling verification of draft chains
+                               (stop_tokens= / budget= apply stop tokens and an output
+                               budget inside the round)
+    spec_verify_greedy         argmax-match verification (same stop options)
+    spec_verify_tree           tree verification by target-sample membership
+    spec_verify_tree_greedy    its temperature-0 form (argmax membership)
     spec_verify_tree_residual  multi-candidate tree verification with residual updates
 
-prepare_chain / prepare_greedy / prepare_tree check and marshal the arguments once and
-return a callable that issues the same library call again (for loops that call the
-verifier many times on buffers refilled in place).
+prepare_* check and marshal the arguments once and return a callable that issues the
+same library call again (for loops that call the verifier many times on buffers refilled
+in place).
 """
 from ._binding import (REQ_STATUS, SpecError, PreparedCall, chain_workspace_bytes,
                        greedy_workspace_bytes, load_library, prepare_chain, prepare_greedy,
-                       prepare_tree, prepare_tree_residual, spec_verify_chain, spec_verify_greedy,
-                       spec_verify_tree, spec_verify_tree_residual, tree_residual_workspace_bytes,
-                       tree_workspace_bytes, LIB_PATH)
+                       prepare_tree, prepare_tree_greedy, prepare_tree_residual, spec_verify_chain,
+                       spec_verify_greedy, spec_verify_tree, spec_verify_tree_greedy,
+                       spec_verify_tree_residual, tree_residual_workspace_bytes, tree_workspace_bytes,
+                       LIB_PATH)
 
-__all__ = ["spec_verify_chain", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_residual",
-           "prepare_tree_residual", "tree_residual_workspace_bytes", "load_library",
-           "chain_workspace_bytes", "greedy_workspace_bytes", "tree_workspace_bytes",
-           "prepare_chain", "prepare_greedy", "prepare_tree", "PreparedCall",
+__all__ = ["spec_verify_chain", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_greedy",
+           "spec_verify_tree_residual", "prepare_tree_residual", "tree_residual_workspace_bytes",
+           "load_library", "chain_workspace_bytes", "greedy_workspace_bytes", "tree_workspace_bytes",
+           "prepare_chain", "prepare_greedy", "prepare_tree", "prepare_tree_greedy", "PreparedCall",
            "SpecError", "REQ_STATUS", "LIB_PATH"]

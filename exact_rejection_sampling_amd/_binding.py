@@ -52,6 +52,9 @@ _SIGNATURES = {
                                   _c_int, _c_int, _c_int, _c_float,
                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                   _c_void_p, _c_size_t, _c_void_p]),
+    "spec_verify_tree_greedy": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_int, _c_int, _c_int,
+                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_void_p, _c_size_t, _c_void_p]),
     "spec_tree_residual_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
     "spec_verify_tree_residual": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p,
                                            _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_float,
@@ -307,6 +310,7 @@ def prepare_greedy(target_logits, draft_tokens, *, workspace_tensor=None, out=No
 
 
 def _tree_args(node_logits, node_tokens, parents, uniforms, temperature, workspace_tensor, out):
+    """uniforms None: the greedy walk (spec_verify_tree_greedy; temperature unused)."""
     lib = load_library()
     _need(node_logits, "node_logits")
     if node_logits.dim() != 3:
@@ -315,7 +319,8 @@ def _tree_args(node_logits, node_tokens, parents, uniforms, temperature, workspa
     dev = node_logits.device
     _need(node_tokens, "node_tokens", dtype=torch.int32, shape=(B, N), device=dev)
     _need(parents, "parents", dtype=torch.int32, shape=(B, N), device=dev)
-    _need(uniforms, "uniforms", dtype=torch.float32, shape=(B, N), device=dev)
+    if uniforms is not None:
+        _need(uniforms, "uniforms", dtype=torch.float32, shape=(B, N), device=dev)
     lt = _dtype_code(node_logits, "node_logits")
     if out is None:
         out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
@@ -328,11 +333,14 @@ def _tree_args(node_logits, node_tokens, parents, uniforms, temperature, workspa
         raise SpecError(f"unsupported sizes B={B} N={N} V={V}")
     ws = workspace_tensor if workspace_tensor is not None else workspace("tree", need, dev, stream)
     wp, wn = _aligned_ws(ws)
-    args = (_ptr(node_logits), lt, _ptr(node_tokens), _ptr(parents), _ptr(uniforms),
-            B, N, V, ctypes.c_float(float(temperature)),
-            _ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["out_nodes"]),
-            _ptr(out["req_status"]), wp, wn, ctypes.c_void_p(stream.cuda_stream))
     keep = (node_logits, node_tokens, parents, uniforms, ws, stream)
+    outs = (_ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["out_nodes"]),
+            _ptr(out["req_status"]), wp, wn, ctypes.c_void_p(stream.cuda_stream))
+    if uniforms is None:
+        args = (_ptr(node_logits), lt, _ptr(node_tokens), _ptr(parents), B, N, V) + outs
+        return lib.spec_verify_tree_greedy, args, keep, out
+    args = (_ptr(node_logits), lt, _ptr(node_tokens), _ptr(parents), _ptr(uniforms),
+            B, N, V, ctypes.c_float(float(temperature))) + outs
     return lib.spec_verify_tree, args, keep, out
 
 
@@ -357,6 +365,23 @@ def prepare_tree(node_logits, node_tokens, parents, uniforms, temperature, *, wo
     """spec_verify_tree with its arguments checked and marshalled once (see PreparedCall)."""
     return PreparedCall(*_tree_args(node_logits, node_tokens, parents, uniforms, temperature,
                                     workspace_tensor, out))
+
+
+def spec_verify_tree_greedy(node_logits: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor, *,
+                            workspace_tensor: Optional[torch.Tensor] = None,
+                            out: Optional[dict] = None) -> dict:
+    """Greedy tree verification, the temperature-0 membership walk (C entry point
+    spec_verify_tree_greedy): the target's argmax (lowest index on ties) in place of its
+    sample.  Arguments and outputs as spec_verify_tree, without uniforms or temperature.
+    """
+    fn, args, _, out = _tree_args(node_logits, node_tokens, parents, None, 0.0, workspace_tensor, out)
+    _check(fn(*args))
+    return out
+
+
+def prepare_tree_greedy(node_logits, node_tokens, parents, *, workspace_tensor=None, out=None) -> PreparedCall:
+    """spec_verify_tree_greedy with its arguments checked and marshalled once (see PreparedCall)."""
+    return PreparedCall(*_tree_args(node_logits, node_tokens, parents, None, 0.0, workspace_tensor, out))
 
 
 def _tree_residual_args(node_logits, draft_probs, node_tokens, parents, accept_uniforms, draw_uniforms,

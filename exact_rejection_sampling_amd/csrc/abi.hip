@@ -232,6 +232,42 @@ spec_status spec_verify_tree(const void* node_logits, int logit_dtype, const int
   return sv::launch_tree(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
+spec_status spec_verify_tree_greedy(const void* node_logits, int logit_dtype, const int32_t* node_tokens,
+                                    const int32_t* parents, int B, int N, int V, int32_t* accepted_len,
+                                    int32_t* out_tokens, int32_t* out_nodes, int32_t* req_status,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!(B >= 0 && B <= SPEC_MAX_BATCH && N >= 1 && N <= SPEC_MAX_NODES && V >= 1 && V <= SPEC_MAX_VOCAB))
+    return SPEC_EINVAL;
+  if (!dtype_ok(logit_dtype)) return SPEC_EDTYPE;
+  if (!sv::grid_fits(sv::tree_blocks(B, V))) return SPEC_EINVAL;
+  if (B == 0) return SPEC_OK;
+  if (!node_logits || !node_tokens || !parents || !accepted_len || !out_tokens || !out_nodes || !req_status)
+    return SPEC_EINVAL;
+  const sv::TreeLayout L = sv::tree_layout(B, N, V);
+  if (!workspace || workspace_bytes < L.total || !aligned256(workspace)) return SPEC_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  sv::TreeParams p{};
+  p.logits = node_logits;
+  p.node_tokens = node_tokens;
+  p.parents = parents;
+  p.accepted_len = accepted_len;
+  p.out_tokens = out_tokens;
+  p.out_nodes = out_nodes;
+  p.req_status = req_status;
+  p.part = reinterpret_cast<float2*>(ws + L.part);
+  p.deep = reinterpret_cast<float2*>(ws + L.deep);
+  p.order = reinterpret_cast<unsigned long long*>(ws + L.order);
+  p.counters = sv::request_counters(workspace);
+  p.B = B;
+  p.N = N;
+  p.V = V;
+  p.P = chunks(V, sv::kWaveChunk);
+  p.WG1 = chunks(p.P, sv::kWavesPerBlock);
+  p.WH = chunks(p.P, sv::kTreeHelperChunks);
+  const bool vec = (V % 8 == 0) && aligned16(node_logits);
+  return sv::launch_tree_greedy(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
 spec_status spec_verify_tree_residual(const void* node_logits, int logit_dtype, const void* draft_probs,
                                       int q_dtype, const int32_t* node_tokens, const int32_t* parents,
                                       const float* accept_uniforms, const float* draw_uniforms, int B, int N,

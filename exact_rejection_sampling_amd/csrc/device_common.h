@@ -382,6 +382,59 @@ __device__ __forceinline__ float scaled_exp(float l, float c2, float r) {
   return __builtin_amdgcn_exp2f(fmaf(l, c2, -r));
 }
 
+// ------------------------------------------------------------------ argmax pieces
+// Per-lane argmax over one chunk's values (a lane's positions base + (j*64 + lane)*8 + e
+// rise with j and e): keeps the maximum and the lowest position holding it, notes NaN.
+__device__ __forceinline__ void lane_argmax_update(const float (&v)[kStatVecs][8], long base, int lane,
+                                                   float& m, int& idx, bool& nan) {
+#pragma unroll
+  for (int j = 0; j < kStatVecs; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = v[j][e];
+      nan |= (x != x);
+      if (x > m) {
+        m = x;
+        idx = static_cast<int>(base + static_cast<long>(j * kWave + lane) * kVec + e);
+      }
+    }
+}
+
+// Wave-wide merge: the maximum over the lanes and the lowest position among the lanes
+// holding it; the maximum reads NaN if any lane saw a NaN.
+__device__ __forceinline__ void wave_argmax_merge(float m, int idx, bool nan, float& m_out, int& idx_out) {
+  const float M = wave_max(m);
+  idx_out = wave_min_i(m == M ? idx : 0x7fffffff);
+  m_out = wave_any(nan) ? __uint_as_float(0x7fc00000u) : M;
+}
+
+// Argmax summary in one 64-bit word: bits of the maximum, and the position with its top
+// bit flipped in the high word, so a published summary is never all-zero bits.
+__device__ __forceinline__ unsigned long long pack_argmax(float m, int idx) {
+  return (static_cast<unsigned long long>(static_cast<unsigned>(idx) ^ 0x80000000u) << 32) | __float_as_uint(m);
+}
+__device__ __forceinline__ void unpack_argmax(unsigned long long b, float& m, int& idx) {
+  m = __uint_as_float(static_cast<unsigned>(b));
+  idx = static_cast<int>(static_cast<unsigned>(b >> 32) ^ 0x80000000u);
+}
+
+// Packed argmax summary of one 2048-element chunk of a row (one wave).
+template <int DT, bool VEC>
+__device__ __forceinline__ unsigned long long chunk_argmax(const void* row, long V, long chunk, int lane) {
+  float m = -INFINITY;
+  int idx = 0x7fffffff;
+  bool nan = false;
+  stream_chunks<DT, VEC>(row, V, chunk + 1, chunk, 1, 1, lane, [&](const ChunkRegs<DT>& r, long c) {
+    float v[kStatVecs][8];
+    chunk_values<DT>(r, v);
+    lane_argmax_update(v, c * kWaveChunk, lane, m, idx, nan);
+  });
+  float M;
+  int I;
+  wave_argmax_merge(m, idx, nan, M, I);
+  return pack_argmax(M, I);
+}
+
 // ------------------------------------------------------------------ cross-block traffic
 // Values that other blocks read within the same launch (chunk summaries, chunk masses,
 // decisions) travel as single 64-bit words written and read with device-scope relaxed

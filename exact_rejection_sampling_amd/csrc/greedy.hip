@@ -42,36 +42,17 @@ __device__ __forceinline__ GreedyPart wave_row_argmax(const void* row, long V, l
   stream_chunks<DT, VEC>(row, V, P, first, stride, n, lane, [&](const ChunkRegs<DT>& r, long c) {
     float v[kStatVecs][8];
     chunk_values<DT>(r, v);
-    const long base = c * kWaveChunk;
-#pragma unroll
-    for (int j = 0; j < kStatVecs; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = v[j][e];
-        nan |= (x != x);
-        if (x > m) {
-          m = x;
-          idx = static_cast<int>(base + static_cast<long>(j * kWave + lane) * kVec + e);
-        }
-      }
+    lane_argmax_update(v, c * kWaveChunk, lane, m, idx, nan);
   });
-  const float M = wave_max(m);
   GreedyPart g;
-  g.m = wave_any(nan) ? __uint_as_float(0x7fc00000u) : M;   // NaN marks a NaN-holding range
-  g.idx = wave_min_i(m == M ? idx : 0x7fffffff);
+  wave_argmax_merge(m, idx, nan, g.m, g.idx);   // NaN marks a NaN-holding range
   return g;
 }
 
-// Packed summary: bits of m, and idx with its top bit flipped in the high word, so a
-// published summary is never all-zero bits (idx is non-negative).
-__device__ __forceinline__ unsigned long long pack(const GreedyPart& g) {
-  return (static_cast<unsigned long long>(static_cast<unsigned>(g.idx) ^ 0x80000000u) << 32) |
-         __float_as_uint(g.m);
-}
+__device__ __forceinline__ unsigned long long pack(const GreedyPart& g) { return pack_argmax(g.m, g.idx); }
 __device__ __forceinline__ GreedyPart unpack(unsigned long long b) {
   GreedyPart g;
-  g.m = __uint_as_float(static_cast<unsigned>(b));
-  g.idx = static_cast<int>(static_cast<unsigned>(b >> 32) ^ 0x80000000u);
+  unpack_argmax(b, g.m, g.idx);
   return g;
 }
 

@@ -227,5 +227,6 @@ hipError_t launch_chain(const ChainParams& p, int logit_dtype, bool vec, hipStre
 hipError_t launch_greedy(const GreedyParams& p, int logit_dtype, bool vec, hipStream_t s);
 hipError_t launch_tree(const TreeParams& p, int logit_dtype, bool vec, hipStream_t s);
 hipError_t launch_tree_residual(const TreeParams& p, int logit_dtype, bool vec, hipStream_t s);
+hipError_t launch_tree_greedy(const TreeParams& p, int logit_dtype, bool vec, hipStream_t s);
 
 }  // namespace sv

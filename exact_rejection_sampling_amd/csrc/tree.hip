@@ -263,8 +263,58 @@ __device__ int sample_published(const TreeParams& p, const float2* src, const vo
   return sample_row<DT, VEC, true>(p, src, row, uv, status);
 }
 
+// The target's greedy token of a row from its P published argmax summaries at `src`
+// (greedy mode): the maximum, and the lowest position holding it.  A row holding NaN or
+// +inf, or entirely -inf, is reported through *status.
+__device__ int argmax_published(const TreeParams& p, const float2* src, int* status) {
+  __shared__ float s_m[kWavesPerBlock];
+  __shared__ int s_i[kWavesPerBlock];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+  const unsigned long long* words = reinterpret_cast<const unsigned long long*>(src);
+  float m = -INFINITY;
+  int idx = 0x7fffffff;
+  bool nan = false, lost = false;
+  for (int c = tid; c < p.P; c += kBlock) {      // a thread's chunks rise with c
+    const unsigned long long bits = await_u64(words + c);
+    lost |= (bits == 0ull);
+    float cm;
+    int ci;
+    unpack_argmax(bits, cm, ci);
+    nan |= (cm != cm);
+    if (cm > m) {
+      m = cm;
+      idx = ci;
+    }
+  }
+  float M;
+  int I;
+  wave_argmax_merge(m, idx, nan, M, I);
+  if (lane == 0) {
+    s_m[wave] = M;
+    s_i[wave] = I;
+  }
+  const bool any_lost = __syncthreads_or(lost) != 0;
+  float bm = -INFINITY;
+  bool bnan = false;
+#pragma unroll
+  for (int k = 0; k < kWavesPerBlock; ++k) {
+    bnan |= (s_m[k] != s_m[k]);
+    bm = fmaxf(bm, s_m[k]);
+  }
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < kWavesPerBlock; ++k)
+    if (s_m[k] == bm) bi = min(bi, s_i[k]);
+  __syncthreads();                               // s_m and s_i are rewritten by the next row
+  if (any_lost) { *status = SPEC_REQ_INTERNAL; return -1; }
+  if (bnan || !(bm > -INFINITY && bm < INFINITY)) { *status = SPEC_REQ_NONFINITE; return -1; }
+  *status = 0;
+  return bi;
+}
+
 // Walk of request b by the last root block.  `gen` counts the orders sent to the helpers.
-template <int DT, bool VEC>
+// ARGMAX: greedy mode, the target's argmax stands in for its sample (no uniforms).
+template <int DT, bool VEC, bool ARGMAX>
 __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
   __shared__ int s_bad;
   __shared__ int s_imin[kWavesPerBlock];
@@ -286,14 +336,16 @@ __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
   while (true) {
     const void* row = row_ptr<DT>(p.logits, (size_t)b * N + v, p.V);
     int status = 0;
-    const float uv = p.u[(size_t)b * N + v];
+    const float uv = ARGMAX ? 0.0f : p.u[(size_t)b * N + v];
     int y;
     if (v == 0) {
-      y = sample_published<DT, VEC>(p, p.part + (size_t)b * p.P, row, uv, &status);
+      if constexpr (ARGMAX) y = argmax_published(p, p.part + (size_t)b * p.P, &status);
+      else y = sample_published<DT, VEC>(p, p.part + (size_t)b * p.P, row, uv, &status);
     } else {
       // the helpers' summaries of this row; returned to zero once read
       float2* deep = p.deep + ((size_t)b * 2 + (gen & 1u)) * p.P;
-      y = sample_published<DT, VEC>(p, deep, row, uv, &status);
+      if constexpr (ARGMAX) y = argmax_published(p, deep, &status);
+      else y = sample_published<DT, VEC>(p, deep, row, uv, &status);
       for (int c = tid; c < p.P; c += kBlock) clear_f2(deep + c);
       vmem_wait();      // the clears are complete before any later order reuses the words
     }
@@ -583,7 +635,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
 
 // Helper h of request b: summarizes its chunks of every row the walker orders, until
 // dismissed; the last helper of the request to leave returns the order word to zero.
-template <int DT, int QT, bool VEC, bool RESID>
+template <int DT, int QT, bool VEC, bool RESID, bool ARGMAX>
 __device__ void helper_item(const TreeParams& p, int b, int h) {
   __shared__ unsigned long long s_order;
   __shared__ int s_last;
@@ -626,11 +678,22 @@ __device__ void helper_item(const TreeParams& p, int b, int h) {
         // the same per-chunk summary the root blocks form (one chunk per wave)
         float v[kStatVecs][8];
         chunk_values<DT>(r[k], v);
-        LaneSoftmax st;
-        lane_softmax_update(st, v, p.c2);
-        float m, z;
-        wave_softmax_merge(st, p.c2, m, z);
-        if (lane == 0) publish_f2(dst + c, make_float2(m, z));
+        if constexpr (ARGMAX) {
+          float m = -INFINITY;
+          int idx = 0x7fffffff;
+          bool nan = false;
+          lane_argmax_update(v, (long)c * kWaveChunk, lane, m, idx, nan);
+          float M;
+          int I;
+          wave_argmax_merge(m, idx, nan, M, I);
+          if (lane == 0) publish_u64(reinterpret_cast<unsigned long long*>(dst + c), pack_argmax(M, I));
+        } else {
+          LaneSoftmax st;
+          lane_softmax_update(st, v, p.c2);
+          float m, z;
+          wave_softmax_merge(st, p.c2, m, z);
+          if (lane == 0) publish_f2(dst + c, make_float2(m, z));
+        }
       }
     }
   }
@@ -644,22 +707,30 @@ __device__ void helper_item(const TreeParams& p, int b, int h) {
 }
 
 // Request b's blocks: WG1 root blocks, then WH helpers.  RESID: the residual-update
-// verifier (q rows of type QT); otherwise membership (QT unused).
-template <int DT, int QT, bool VEC, bool RESID>
+// verifier (q rows of type QT); ARGMAX: greedy membership (argmax summaries); otherwise
+// membership by target sample (QT unused).
+template <int DT, int QT, bool VEC, bool RESID, bool ARGMAX>
 __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
+  static_assert(!(RESID && ARGMAX), "the residual verifier samples");
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   const int per_req = p.WG1 + p.WH;
   const int b = blockIdx.x / per_req;
   const int slice = blockIdx.x % per_req;
   if (slice >= p.WG1) {
-    helper_item<DT, QT, VEC, RESID>(p, b, slice - p.WG1);
+    helper_item<DT, QT, VEC, RESID, ARGMAX>(p, b, slice - p.WG1);
     return;
   }
   const int chunk = slice * kWavesPerBlock + wave;
   if (chunk < p.P) {
-    float m, z;
-    chunk_summary<DT, VEC>(row_ptr<DT>(p.logits, (size_t)b * p.N, p.V), p.V, chunk, lane, p.c2, m, z);
-    if (lane == 0) publish_f2(p.part + (size_t)b * p.P + chunk, make_float2(m, z));
+    const void* row0 = row_ptr<DT>(p.logits, (size_t)b * p.N, p.V);
+    if constexpr (ARGMAX) {
+      const unsigned long long sum = chunk_argmax<DT, VEC>(row0, p.V, chunk, lane);
+      if (lane == 0) publish_u64(reinterpret_cast<unsigned long long*>(p.part + (size_t)b * p.P + chunk), sum);
+    } else {
+      float m, z;
+      chunk_summary<DT, VEC>(row0, p.V, chunk, lane, p.c2, m, z);
+      if (lane == 0) publish_f2(p.part + (size_t)b * p.P + chunk, make_float2(m, z));
+    }
   }
   __syncthreads();
   __shared__ int s_last;
@@ -671,7 +742,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
   if (!s_last) return;
   unsigned gen = 0;
   if constexpr (RESID) tree_walk_residual<DT, QT, VEC>(p, b, gen);
-  else tree_walk<DT, VEC>(p, b, gen);
+  else tree_walk<DT, VEC, ARGMAX>(p, b, gen);
   __syncthreads();
   if (threadIdx.x == 0) publish_order(p, b, gen + 1u, kTreeDone);   // dismiss the helpers
   for (int j = threadIdx.x; j < p.P; j += kBlock) clear_f2(p.part + (size_t)b * p.P + j);
@@ -680,10 +751,10 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
   if (threadIdx.x == 0) reset_counter(&p.counters[(size_t)b * kCounterSlots + 0]);
 }
 
-template <int DT, int QT, bool VEC, bool RESID>
+template <int DT, int QT, bool VEC, bool RESID, bool ARGMAX = false>
 hipError_t launch_typed(const TreeParams& p, hipStream_t s) {
   const unsigned g = (unsigned)((size_t)p.B * (p.WG1 + p.WH));   // == tree_blocks
-  tree_kernel<DT, QT, VEC, RESID><<<dim3(g), dim3(kBlock), 0, s>>>(p);
+  tree_kernel<DT, QT, VEC, RESID, ARGMAX><<<dim3(g), dim3(kBlock), 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -693,6 +764,12 @@ hipError_t launch_tree(const TreeParams& p, int logit_dtype, bool vec, hipStream
   if (logit_dtype == kBF16)
     return vec ? launch_typed<kBF16, kF32, true, false>(p, s) : launch_typed<kBF16, kF32, false, false>(p, s);
   return vec ? launch_typed<kF32, kF32, true, false>(p, s) : launch_typed<kF32, kF32, false, false>(p, s);
+}
+
+hipError_t launch_tree_greedy(const TreeParams& p, int logit_dtype, bool vec, hipStream_t s) {
+  if (logit_dtype == kBF16)
+    return vec ? launch_typed<kBF16, kF32, true, false, true>(p, s) : launch_typed<kBF16, kF32, false, false, true>(p, s);
+  return vec ? launch_typed<kF32, kF32, true, false, true>(p, s) : launch_typed<kF32, kF32, false, false, true>(p, s);
 }
 
 hipError_t launch_tree_residual(const TreeParams& p, int logit_dtype, bool vec, hipStream_t s) {

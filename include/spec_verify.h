@@ -6,7 +6,8 @@
  * *_stop variant that applies stop tokens and an output budget inside the round):
  *   spec_verify_chain          rejection-sampling verification of a draft chain
  *   spec_verify_greedy         argmax-match verification of a draft chain
- *   spec_verify_tree           tree verification by target-sample membership
+ *   spec_verify_tree           tree verification by target-sample membership (and
+ *                              spec_verify_tree_greedy, its temperature-0 form)
  *   spec_verify_tree_residual  multi-candidate tree verification with residual updates
  *
  * Pages that define the operations (cited by title and section):
@@ -242,6 +243,21 @@ spec_status spec_verify_tree(const void* node_logits, int logit_dtype,
                              int32_t* accepted_len, int32_t* out_tokens, int32_t* out_nodes,
                              int32_t* req_status, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/* Greedy tree verification, the temperature-0 form of spec_verify_tree ([M16] "Verify the
+ * Tree -- and Why It's Exact": follow the child whose token is the target's greedy next
+ * token; the output equals plain greedy decoding of the target):
+ *   y = argmax_x l_{v,x} (lowest index on ties) in place of the draw; the walk, the
+ *   outputs and the workspace (spec_tree_workspace_bytes) are those of spec_verify_tree.
+ * No uniforms and no temperature.  Request statuses: SPEC_REQ_BADTREE, then
+ * SPEC_REQ_NONFINITE for a reached row holding NaN or +inf, or entirely -inf.
+ */
+spec_status spec_verify_tree_greedy(const void* node_logits, int logit_dtype,
+                                    const int32_t* node_tokens, const int32_t* parents,
+                                    int B, int N, int V,
+                                    int32_t* accepted_len, int32_t* out_tokens, int32_t* out_nodes,
+                                    int32_t* req_status, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /* -------------------------------------------------------- residual tree ---
  * Multi-candidate tree verification with residual updates ([M7.7] §0x09A, "Stochastic

@@ -164,3 +164,13 @@ def test_stop_variants_host_validation():
         NULL, NULL, 0, NULL)
     assert g(n=-1) == EINVAL and g(n=257) == EINVAL and g(stop=NULL) == EINVAL
     assert g(n=0, stop=NULL) == EWORKSPACE and g(B=0) == OK
+
+
+def test_tree_greedy_host_validation():
+    lib = sv.load_library()
+    t = lambda **k: lib.spec_verify_tree_greedy(k.get("l", FAKE), k.get("dt", 1), FAKE, k.get("par", FAKE),
+                                                 k.get("B", 2), k.get("N", 5), k.get("V", 16),
+                                                 FAKE, FAKE, FAKE, FAKE, NULL, 0, NULL)
+    assert t(N=0) == EINVAL and t(N=4097) == EINVAL and t(V=0) == EINVAL
+    assert t(dt=2) == EDTYPE and t(par=NULL) == EINVAL and t(l=NULL) == EINVAL
+    assert t(B=0, l=NULL) == OK and t() == EWORKSPACE
