@@ -12,8 +12,9 @@ twice the 256 MB Infinity Cache, so every step streams from HBM.
 Prints ONE JSON line: throughput (verified positions/s) over K timed steps, the
 roofline of the verification kernel (one launch per call) from HIP events recorded on
 the stream it runs on, the oracle's CPU throughput on a bounded sample (measured first,
-before the GPU is touched), and secondary measurements of the greedy (B=256, gamma=8,
-V=128256) and tree (B=32, N=63, V=152064) workloads.
+before the GPU is touched), and secondary measurements: the greedy chain (B=256,
+gamma=8, V=128256), membership tree and greedy tree (B=32, N=63, V=152064), residual-update
+tree (B=32, N=31, V=32000) workloads, and the headline chain with stop tokens and budgets.
 """
 from __future__ import annotations
 
@@ -183,6 +184,56 @@ def bench_tree(args, torch, sv, synth):
                 dense_equivalent_gbs=B * N * V * 2 / launch / 1e9)
 
 
+def bench_tree_greedy(args, torch, sv, synth):
+    x = synth.make_config(5, 0)
+    B, N, V = x.B, x.N, x.V
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    nt = torch.from_numpy(x.node_tokens).to(dev)
+    pt = torch.from_numpy(x.parents).to(dev)
+    sets = device_copies(lambda: (lt.clone(), nt.clone(), pt.clone()), lt.numel() * 2)
+    del lt
+    stream = torch.cuda.current_stream()
+    ws = torch.zeros(sv.tree_workspace_bytes(B, N, V) + 512, dtype=torch.uint8, device=dev)
+    calls = [sv.prepare_tree_greedy(s[0], s[1], s[2], workspace_tensor=ws) for s in sets]
+    span, per = time_calls(calls, max(100, args.steps // 2), args.warmup, stream)
+    acc = calls[0].out["accepted_len"].cpu().numpy()
+    visited = int((acc + 1).sum())
+    alg = visited * V * 2 + B * N * 8
+    launch = span / len(per)
+    del sets, calls
+    return dict(workload="greedy tree B=32 N=63 V=152064 bf16", nodes_per_s=B * N * len(per) / span,
+                launch_us=launch * 1e6, evented_launch_mean_us=float(per.mean()) * 1e3,
+                visited_rows=visited, achieved_gbs_visited=alg / launch / 1e9,
+                dense_equivalent_gbs=B * N * V * 2 / launch / 1e9)
+
+
+def bench_chain_stop(args, torch, sv, synth):
+    """The headline chain workload through spec_verify_chain_stop: 64 stop tokens (48 of
+    them draft tokens), budgets uniform on [0, 7]."""
+    x = synth.make_config(3, 0)
+    stop, budget = synth.make_stop(x.tokens, x.V, seed=301, n_stop=64, from_drafts=48)
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    qt = torch.from_numpy(x.q).to(dev)
+    tt, ut = torch.from_numpy(x.tokens).to(dev), torch.from_numpy(x.u).to(dev)
+    st, bt = torch.from_numpy(stop).to(dev), torch.from_numpy(budget).to(dev)
+    sets = device_copies(lambda: (lt.clone(), qt.clone()), lt.numel() * 2 + qt.numel() * 4)
+    del lt, qt
+    stream = torch.cuda.current_stream()
+    ws = torch.zeros(sv.chain_workspace_bytes(x.B, x.gamma, x.V) + 512, dtype=torch.uint8, device=dev)
+    calls = [sv.prepare_chain(s[0], s[1], tt, ut, float(x.temperature), workspace_tensor=ws, stop_tokens=st,
+                              budget=bt) for s in sets]
+    span, per = time_calls(calls, max(100, args.steps // 2), args.warmup, stream)
+    fin = np.bincount(calls[0].out["finish"].cpu().numpy(), minlength=3)
+    launch = span / len(per)
+    del sets, calls
+    return dict(workload="chain B=64 gamma=5 V=128256 bf16 with 64 stop tokens and budgets 0..7",
+                positions_per_s=x.B * (x.gamma + 1) * len(per) / span, launch_us=launch * 1e6,
+                evented_launch_mean_us=float(per.mean()) * 1e3,
+                finish_counts=dict(open=int(fin[0]), stop=int(fin[1]), budget=int(fin[2])))
+
+
 _CPU_X = None   # the workload a forked oracle worker reads
 
 
@@ -294,6 +345,12 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] tree with residual updates")
         line["secondary"]["tree_residual"] = bench_tree_residual(args, torch, sv, synth)
+        torch.cuda.empty_cache()
+        log("[bench] greedy tree")
+        line["secondary"]["tree_greedy"] = bench_tree_greedy(args, torch, sv, synth)
+        torch.cuda.empty_cache()
+        log("[bench] chain with stop tokens and budgets")
+        line["secondary"]["chain_stop"] = bench_chain_stop(args, torch, sv, synth)
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -135,6 +135,8 @@ template <int DT>
 __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDecision& s_dec) {
   __shared__ float2 s_part[kDecideStage];
   __shared__ int s_timeout;
+  __shared__ int s_x[SPEC_MAX_GAMMA];           // the request's drafts, for the stop-token test
+  __shared__ unsigned s_hit[2];                 // bit i: draft i is a stop token
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   const float c2 = p.c2;
   const int G = p.G;
@@ -147,6 +149,14 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
   unsigned long long g[3] = {0ull, 0ull, 0ull};
   float ui = 0.0f, ut = 0.0f;
   const int H = p.st.budget ? p.st.budget[b] : INT32_MAX;   // remaining output budget
+  // stop tokens: thread t < n_stop holds entry t and tests it against every draft (in
+  // LDS) once the drafts are staged; a hit sets the draft's bit
+  const bool stops = p.st.n_stop > 0;
+  const int my_stop = stops && tid < p.st.n_stop ? p.st.stop[tid] : 0;
+  if (stops) {
+    if (tid < G) s_x[tid] = p.tokens[(size_t)b * G + tid];
+    if (tid < 2) s_hit[tid] = 0u;
+  }
   if (wave == 0 && lane < G) {
     const unsigned long long* rec = gather_rec(p, b, lane);
     g[0] = fetch_u64(rec);
@@ -184,6 +194,9 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
   }
   __syncthreads();                        // s_timeout's reset precedes every report
   if (timeout) s_timeout = 1;
+  if (stops && tid < p.st.n_stop)
+    for (int i = 0; i < G; ++i)
+      if (s_x[i] == my_stop) atomicOr(&s_hit[i >> 5], 1u << (i & 31));
 
   for (int i = wave; i < p.R; i += kWavesPerBlock) {
     const float2* row_part = part_b + (size_t)i * p.SL;
@@ -240,7 +253,7 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
           a = fmin(1.0, px / (double)qx);
           reject = !((double)ui < a);
           if (!reject) {
-            if (p.st.n_stop > 0 && is_stop_token(p.st.stop, p.st.n_stop, x)) fin = SPEC_FINISH_STOP;
+            if (stops && ((s_hit[lane >> 5] >> (lane & 31)) & 1u)) fin = SPEC_FINISH_STOP;
             else if (lane + 1 == H) fin = SPEC_FINISH_BUDGET;
           }
         }
@@ -366,6 +379,8 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
   const int tid = threadIdx.x, G = p.G;
   const double* tm = p.tmass + (size_t)b * p.S2;
   const float ut = p.u[(size_t)b * p.R + G];
+  // stop-token entry t, fetched while the masses are awaited (tested against the token)
+  const int my_stop = tid < p.st.n_stop ? p.st.stop[tid] : 0;
   if (tid == 0) {
     s_timeout = 0;
     s_before = 0.0;
@@ -465,7 +480,7 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
   const int status = s_timeout ? SPEC_REQ_INTERNAL : (failed ? SPEC_REQ_RESIDUAL_EMPTY : 0);
   // a terminal token that is a stop token, or that uses up the budget, finishes the request
   int finish = 0;
-  if (p.st.n_stop > 0 && block_is_stop(p.st.stop, p.st.n_stop, k)) finish = SPEC_FINISH_STOP;
+  if (p.st.n_stop > 0 && __syncthreads_or(tid < p.st.n_stop && my_stop == k)) finish = SPEC_FINISH_STOP;
   else if (A + 1 == d.H) finish = SPEC_FINISH_BUDGET;
   if (status != 0) finish = 0;
   for (int i = tid; i < p.R; i += kBlock) {

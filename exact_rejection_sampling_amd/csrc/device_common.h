@@ -505,20 +505,6 @@ __device__ __forceinline__ void store_wt(float* p, float v) {
 // workgroup-scope release: no cache maintenance on this target).
 __device__ __forceinline__ void vmem_wait() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup"); }
 
-// Whether `tok` is one of the n stop tokens (every lane of a wave reads the same words).
-__device__ __forceinline__ bool is_stop_token(const int32_t* stop, int n, int tok) {
-  bool hit = false;
-  for (int j = 0; j < n; ++j) hit |= (stop[j] == tok);
-  return hit;
-}
-
-// The same test by a whole block for a block-uniform token: thread t compares entry t
-// (n <= kBlock).  Every thread of the block must call it.
-__device__ __forceinline__ bool block_is_stop(const int32_t* stop, int n, int tok) {
-  const int t = threadIdx.x;
-  return __syncthreads_or(t < n && stop[t] == tok) != 0;
-}
-
 // Count one arrival; returns the count before this one.
 __device__ __forceinline__ unsigned arrive(unsigned* counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

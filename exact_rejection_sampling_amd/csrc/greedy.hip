@@ -94,6 +94,9 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
   __shared__ int s_arg[SPEC_MAX_GAMMA + 1];
   __shared__ int s_bad[SPEC_MAX_GAMMA + 1];
   __shared__ int s_lost;
+  __shared__ int s_x[SPEC_MAX_GAMMA];           // the drafts, for the stop-token test
+  __shared__ int s_stop[SPEC_MAX_STOP];         // the stop tokens, for the target token's test
+  __shared__ unsigned s_hit[2];                 // bit i: draft i is a stop token
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   unsigned long long* part_b = p.part + (size_t)b * p.R * p.SL;
   if (tid == 0) s_lost = 0;
@@ -101,7 +104,18 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
   int x = 0;
   if (wave == 0 && lane < p.G) x = p.tokens[(size_t)b * p.G + lane];
   const int H = p.st.budget ? p.st.budget[b] : INT32_MAX;
+  const bool stops = p.st.n_stop > 0;
+  const int my_stop = stops && tid < p.st.n_stop ? p.st.stop[tid] : 0;
+  if (stops) {
+    if (wave == 0 && lane < p.G) s_x[lane] = x;
+    if (tid < p.st.n_stop) s_stop[tid] = my_stop;
+    if (tid < 2) s_hit[tid] = 0u;
+  }
   __syncthreads();
+  // stop tokens: thread t < n_stop tests entry t against every draft
+  if (stops && tid < p.st.n_stop)
+    for (int i = 0; i < p.G; ++i)
+      if (s_x[i] == my_stop) atomicOr(&s_hit[i >> 5], 1u << (i & 31));
   for (int i = wave; i < p.R; i += kWavesPerBlock) {
     const unsigned long long* part = part_b + (size_t)i * p.SL;
     float m = -INFINITY;
@@ -145,7 +159,7 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
     } else {
       mismatch = (x != s_arg[lane]);
       if (!mismatch) {
-        if (p.st.n_stop > 0 && is_stop_token(p.st.stop, p.st.n_stop, x)) fin = SPEC_FINISH_STOP;
+        if (stops && ((s_hit[lane >> 5] >> (lane & 31)) & 1u)) fin = SPEC_FINISH_STOP;
         else if (lane + 1 == H) fin = SPEC_FINISH_BUDGET;
       }
     }
@@ -172,8 +186,9 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
   if (s_lost) status = SPEC_REQ_INTERNAL;
   if (status == 0 && draw) {           // the target token at A
     const int t = s_arg[A];
-    finish = (p.st.n_stop > 0 && is_stop_token(p.st.stop, p.st.n_stop, t)) ? SPEC_FINISH_STOP
-             : (A + 1 == H ? SPEC_FINISH_BUDGET : 0);
+    bool hit = false;
+    for (int j = lane; j < p.st.n_stop; j += kWave) hit |= (s_stop[j] == t);
+    finish = wave_any(hit) ? SPEC_FINISH_STOP : (A + 1 == H ? SPEC_FINISH_BUDGET : 0);
   }
   for (int i = lane; i < p.R; i += kWave) {
     int v = -1;
