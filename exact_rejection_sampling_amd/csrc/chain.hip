@@ -114,10 +114,6 @@ __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
   }
 }
 
-// Summaries the terminal items stage in LDS when the request's rows have few slices.
-constexpr int kDecideStage = 1024;
-constexpr int kStagePerThread = kDecideStage / kBlock;
-
 // Per-row results of a terminal item's decision, kept for the selector's outputs.
 struct RowState {
   float r[SPEC_MAX_GAMMA + 1];    // reference exponent per row
@@ -130,97 +126,99 @@ struct RowState {
 
 // The decision of request b from its published summaries and gather records.  Every
 // terminal item of the request runs this on the same words and takes the same decision,
-// which it leaves in `s_dec` (shared; valid after the final barrier).
+// which it leaves in `s_dec` (shared; valid after the final barrier).  Wave 0 does all of
+// it with no block barrier until the end: lane l holds the summaries of one (row, slice)
+// pair per pass -- rows in groups of S = 2^ceil(log2 SL) lanes (at most 64, lanes then
+// looping over slices) -- and a row's maximum and normalizer come from segmented DPP
+// reductions over its group.
+__device__ __forceinline__ int seg_lanes(int SL) {
+  int S = 1;
+  while (S < SL && S < kWave) S <<= 1;
+  return S;
+}
+
 template <int DT>
 __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDecision& s_dec) {
-  __shared__ float2 s_part[kDecideStage];
-  __shared__ int s_timeout;
-  __shared__ int s_x[SPEC_MAX_GAMMA];           // the request's drafts, for the stop-token test
-  __shared__ unsigned s_hit[2];                 // bit i: draft i is a stop token
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+  if (wave_id() != 0) {
+    __syncthreads();
+    return;
+  }
+  constexpr int kPre = 4;                       // slices per lane and pass kept in registers
+  const int lane = threadIdx.x & (kWave - 1);
   const float c2 = p.c2;
-  const int G = p.G;
-  const int total = p.R * p.SL;
-  const float2* part_b = p.part + (size_t)b * total;
-  const bool staged = total <= kDecideStage;
-  if (tid == 0) s_timeout = 0;
+  const int G = p.G, R = p.R, SL = p.SL;
+  const float2* part_b = p.part + (size_t)b * R * SL;
+  const auto* words = reinterpret_cast<const unsigned long long*>(part_b);
 
-  // wave 0, lane i < G: draft position i -- its gather record and uniform
+  // independent reads first: lane i < G's gather record and uniform, the terminal uniform,
+  // the budget, and lane l's stop entries l, l + 64, ...
   unsigned long long g[3] = {0ull, 0ull, 0ull};
-  float ui = 0.0f, ut = 0.0f;
-  const int H = p.st.budget ? p.st.budget[b] : INT32_MAX;   // remaining output budget
-  // stop tokens: thread t < n_stop holds entry t and tests it against every draft (in
-  // LDS) once the drafts are staged; a hit sets the draft's bit
-  const bool stops = p.st.n_stop > 0;
-  const int my_stop = stops && tid < p.st.n_stop ? p.st.stop[tid] : 0;
-  if (stops) {
-    if (tid < G) s_x[tid] = p.tokens[(size_t)b * G + tid];
-    if (tid < 2) s_hit[tid] = 0u;
-  }
-  if (wave == 0 && lane < G) {
+  float ui = 0.0f;
+  if (lane < G) {
     const unsigned long long* rec = gather_rec(p, b, lane);
-    g[0] = fetch_u64(rec);
-    g[1] = fetch_u64(rec + 1);
-    g[2] = fetch_u64(rec + 2);
-    ui = p.u[(size_t)b * p.R + lane];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) g[k] = fetch_u64(rec + k);
+    ui = p.u[(size_t)b * R + lane];
   }
-  if (wave == 0) ut = p.u[(size_t)b * p.R + G];
-  bool timeout = false;
-  if (staged) {
-    unsigned long long v[kStagePerThread];
+  const float ut = p.u[(size_t)b * R + G];
+  const int H = p.st.budget ? p.st.budget[b] : INT32_MAX;   // remaining output budget
+  const int n_stop = p.st.n_stop;
+  int stop_e[SPEC_MAX_STOP / kWave];
 #pragma unroll
-    for (int k = 0; k < kStagePerThread; ++k) {
-      const int j = tid + k * kBlock;
-      v[k] = j < total ? fetch_u64(reinterpret_cast<const unsigned long long*>(part_b + j)) : 1ull;
-    }
+  for (int k = 0; k < SPEC_MAX_STOP / kWave; ++k) {
+    const int j = lane + k * kWave;
+    stop_e[k] = j < n_stop ? p.st.stop[j] : 0;
+  }
+
+  const int S = seg_lanes(SL), rows_per_pass = kWave / S, tpl = (SL + S - 1) / S;
+  const int srow = lane / S, sj = lane & (S - 1);
+  bool lost = false;
+  for (int pass = 0; pass * rows_per_pass < R; ++pass) {
+    const int i = pass * rows_per_pass + srow;   // this lane's row
+    const bool rv = i < R;
+    auto slice_ok = [&](int t) { return rv && sj + S * t < SL; };
+    auto word = [&](int t) { return words + (size_t)i * SL + sj + S * t; };
+    unsigned long long v[kPre];
 #pragma unroll
-    for (int k = 0; k < kStagePerThread; ++k) {
-      const int j = tid + k * kBlock;
-      if (j < total) {
-        if (v[k] == 0ull) v[k] = await_u64(reinterpret_cast<const unsigned long long*>(part_b + j));
-        timeout |= (v[k] == 0ull);
-        s_part[j] = make_float2(__uint_as_float(static_cast<unsigned>(v[k])),
-                                __uint_as_float(static_cast<unsigned>(v[k] >> 32)));
+    for (int t = 0; t < kPre; ++t) v[t] = t < tpl && slice_ok(t) ? fetch_u64(word(t)) : 1ull;
+    // maximum over the row's slices
+    float m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kPre; ++t) {
+      if (t < tpl && slice_ok(t)) {
+        if (v[t] == 0ull) v[t] = await_u64(word(t));
+        lost |= (v[t] == 0ull);
+        m = fmaxf(m, __uint_as_float(static_cast<unsigned>(v[t])));
       }
     }
-  }
-  if (wave == 0 && lane < G) {
-    const unsigned long long* rec = gather_rec(p, b, lane);
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      if (g[k] == 0ull) g[k] = await_u64(rec + k);
-      timeout |= (g[k] == 0ull);
+    for (int t = kPre; t < tpl; ++t) {
+      if (slice_ok(t)) {
+        const unsigned long long w = await_u64(word(t));
+        lost |= (w == 0ull);
+        m = fmaxf(m, __uint_as_float(static_cast<unsigned>(w)));
+      }
     }
-  }
-  __syncthreads();                        // s_timeout's reset precedes every report
-  if (timeout) s_timeout = 1;
-  if (stops && tid < p.st.n_stop)
-    for (int i = 0; i < G; ++i)
-      if (s_x[i] == my_stop) atomicOr(&s_hit[i >> 5], 1u << (i & 31));
-
-  for (int i = wave; i < p.R; i += kWavesPerBlock) {
-    const float2* row_part = part_b + (size_t)i * p.SL;
-    bool lost = false;
-    auto summary = [&](int j) {
-      if (staged) return s_part[i * p.SL + j];
-      const unsigned long long bits = await_u64(reinterpret_cast<const unsigned long long*>(row_part + j));
-      lost |= (bits == 0ull);
-      return make_float2(__uint_as_float(static_cast<unsigned>(bits)),
-                         __uint_as_float(static_cast<unsigned>(bits >> 32)));
-    };
-    float m = -INFINITY;
-    for (int j = lane; j < p.SL; j += kWave) m = fmaxf(m, summary(j).x);
-    m = wave_max(m);
+    m = seg_max(m, S);
     const float r = m * c2;
+    // Z = sum_j Z_j 2^(r_j - r); an all -inf row gives (-inf) - (-inf) = NaN, flagged below
     double z = 0.0;
-    for (int j = lane; j < p.SL; j += kWave) {
-      const float2 s = summary(j);
-      // 2^(r_j - r) <= 1; an all -inf row gives (-inf) - (-inf) = NaN, flagged below
-      z += (double)s.y * (double)__builtin_amdgcn_exp2f(s.x * c2 - r);
+#pragma unroll
+    for (int t = 0; t < kPre; ++t) {
+      if (t < tpl && slice_ok(t)) {
+        const unsigned long long w = v[t];
+        z += (double)__uint_as_float(static_cast<unsigned>(w >> 32)) *
+             (double)__builtin_amdgcn_exp2f(__uint_as_float(static_cast<unsigned>(w)) * c2 - r);
+      }
     }
-    z = wave_sum_d(z);
-    if (wave_any(lost) && lane == 0) s_timeout = 1;
-    if (lane == 0) {
+    for (int t = kPre; t < tpl; ++t) {
+      if (slice_ok(t)) {
+        const unsigned long long w = fetch_u64(word(t));
+        z += (double)__uint_as_float(static_cast<unsigned>(w >> 32)) *
+             (double)__builtin_amdgcn_exp2f(__uint_as_float(static_cast<unsigned>(w)) * c2 - r);
+      }
+    }
+    z = seg_sum_d(z, S);
+    if (rv && sj == 0) {
       rs.r[i] = r;
       rs.m[i] = m;
       rs.z[i] = z;
@@ -228,69 +226,90 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
       rs.bad[i] = !(isfinite(z) && z > 0.0);
     }
   }
-  __syncthreads();
-  if (wave == 0) {
-    // lane i < G: draft position i, checked in the order a round reaches it; an accepted
-    // draft that is a stop token, or that uses up the budget, ends the round after itself
-    int code = 0, fin = 0;
-    bool reject = false;
-    double px = NAN, a = NAN;
-    if (lane < G) {
-      const int x = static_cast<int>(static_cast<unsigned>(g[0]));
-      if (rs.bad[lane]) {
-        code = SPEC_REQ_NONFINITE;
-      } else if (x < 0 || x >= p.V) {
-        code = SPEC_REQ_BADTOKEN;
+  if (lane < G) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      if (g[k] == 0ull) g[k] = await_u64(gather_rec(p, b, lane) + k);
+      lost |= (g[k] == 0ull);
+    }
+  }
+  const bool timeout = wave_any(lost);
+  // the row results travel through LDS within this wave: LDS operations of one wave complete
+  // in order, and the fence keeps the compiler from moving the reads above the writes
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  // stop tokens: bit i of `hits` is set when draft i is one of them
+  const int x = static_cast<int>(static_cast<unsigned>(g[0]));
+  unsigned long long hits = 0ull;
+  if (n_stop > 0) {
+    for (int i = 0; i < G; ++i) {
+      const int xi = __builtin_amdgcn_readlane(x, i);
+      bool h = false;
+#pragma unroll
+      for (int k = 0; k < SPEC_MAX_STOP / kWave; ++k) h |= (lane + k * kWave < n_stop) && stop_e[k] == xi;
+      if (wave_any(h)) hits |= 1ull << i;
+    }
+  }
+
+  // lane i < G: draft position i, checked in the order a round reaches it; an accepted
+  // draft that is a stop token, or that uses up the budget, ends the round after itself
+  int code = 0, fin = 0;
+  bool reject = false;
+  double px = NAN, a = NAN;
+  if (lane < G) {
+    if (rs.bad[lane]) {
+      code = SPEC_REQ_NONFINITE;
+    } else if (x < 0 || x >= p.V) {
+      code = SPEC_REQ_BADTOKEN;
+    } else {
+      const float qx = __uint_as_float(static_cast<unsigned>(g[2]));
+      if (!(isfinite(qx) && qx > 0.0f)) {
+        code = SPEC_REQ_QZERO;
+      } else if (!(ui >= 0.0f && ui < 1.0f)) {
+        code = SPEC_REQ_BADUNIFORM;
       } else {
-        const float qx = __uint_as_float(static_cast<unsigned>(g[2]));
-        if (!(isfinite(qx) && qx > 0.0f)) {
-          code = SPEC_REQ_QZERO;
-        } else if (!(ui >= 0.0f && ui < 1.0f)) {
-          code = SPEC_REQ_BADUNIFORM;
-        } else {
-          const float lx = __uint_as_float(static_cast<unsigned>(g[1]));
-          px = exp2((double)lx * (double)c2 - (double)rs.r[lane]) / rs.z[lane];
-          a = fmin(1.0, px / (double)qx);
-          reject = !((double)ui < a);
-          if (!reject) {
-            if (stops && ((s_hit[lane >> 5] >> (lane & 31)) & 1u)) fin = SPEC_FINISH_STOP;
-            else if (lane + 1 == H) fin = SPEC_FINISH_BUDGET;
-          }
+        const float lx = __uint_as_float(static_cast<unsigned>(g[1]));
+        px = exp2((double)lx * (double)c2 - (double)rs.r[lane]) / rs.z[lane];
+        a = fmin(1.0, px / (double)qx);
+        reject = !((double)ui < a);
+        if (!reject) {
+          if ((hits >> lane) & 1ull) fin = SPEC_FINISH_STOP;
+          else if (lane + 1 == H) fin = SPEC_FINISH_BUDGET;
         }
       }
-      rs.px[lane] = px;
-      rs.a[lane] = a;
     }
-    const unsigned long long ev = __ballot(lane < G && (code != 0 || reject || fin != 0));
-    const int e = ev ? (__ffsll((long long)ev) - 1) : G;   // the first event
-    const int code_e = __shfl(code, e < G ? e : 0, kWave);
-    const int fin_e = __shfl(fin, e < G ? e : 0, kWave);
-    int A = e, status = 0, draw = 1, finish = 0;
-    if (e < G && fin_e != 0) {          // the round ends on draft e, with no draw
-      A = e + 1;
-      draw = 0;
-      finish = fin_e;
-    } else {
-      status = e < G ? code_e : (rs.bad[G] ? SPEC_REQ_NONFINITE : 0);
-      if (status == 0 && !(ut >= 0.0f && ut < 1.0f)) status = SPEC_REQ_BADUNIFORM;
-    }
-    if (H <= 0) {                       // no budget left: no round, nothing checked
-      A = 0;
-      status = 0;
-      draw = 0;
-      finish = SPEC_FINISH_BUDGET;
-    }
-    if (s_timeout) status = SPEC_REQ_INTERNAL;
-    if (lane == 0) {
-      const bool drawn = status == 0 && draw;
-      s_dec.A = status == 0 ? A : -1;
-      s_dec.status = status;
-      s_dec.draw = drawn ? 1 : 0;
-      s_dec.finish = finish;
-      s_dec.H = H;
-      s_dec.r_ref = drawn ? rs.r[A] : 0.0f;
-      s_dec.inv_z = drawn ? (float)(1.0 / rs.z[A]) : 0.0f;
-    }
+    rs.px[lane] = px;
+    rs.a[lane] = a;
+  }
+  const unsigned long long ev = __ballot(lane < G && (code != 0 || reject || fin != 0));
+  const int e = ev ? (__ffsll((long long)ev) - 1) : G;   // the first event
+  const int code_e = __shfl(code, e < G ? e : 0, kWave);
+  const int fin_e = __shfl(fin, e < G ? e : 0, kWave);
+  int A = e, status = 0, draw = 1, finish = 0;
+  if (e < G && fin_e != 0) {          // the round ends on draft e, with no draw
+    A = e + 1;
+    draw = 0;
+    finish = fin_e;
+  } else {
+    status = e < G ? code_e : (rs.bad[G] ? SPEC_REQ_NONFINITE : 0);
+    if (status == 0 && !(ut >= 0.0f && ut < 1.0f)) status = SPEC_REQ_BADUNIFORM;
+  }
+  if (H <= 0) {                       // no budget left: no round, nothing checked
+    A = 0;
+    status = 0;
+    draw = 0;
+    finish = SPEC_FINISH_BUDGET;
+  }
+  if (timeout) status = SPEC_REQ_INTERNAL;
+  if (lane == 0) {
+    const bool drawn = status == 0 && draw;
+    s_dec.A = status == 0 ? A : -1;
+    s_dec.status = status;
+    s_dec.draw = drawn ? 1 : 0;
+    s_dec.finish = finish;
+    s_dec.H = H;
+    s_dec.r_ref = drawn ? rs.r[A] : 0.0f;
+    s_dec.inv_z = drawn ? (float)(1.0 / rs.z[A]) : 0.0f;
   }
   __syncthreads();
 }
@@ -632,6 +651,16 @@ __global__ __launch_bounds__(kBlock) void chain_kernel(ChainParams p) {
 #endif
 constexpr long kLagTenths = SPEC_CHAIN_LAG_TENTHS;   // in tenths of a round
 
+// Blocks resident per CU: 0 leaves it to the register count; k > 0 reserves LDS so that
+// at most k blocks share a CU (fewer loads in flight: shorter queues, so the decision's
+// dependent reads come back sooner).
+#ifndef SPEC_CHAIN_BLOCKS_PER_CU
+#define SPEC_CHAIN_BLOCKS_PER_CU 0
+#endif
+constexpr int kBlocksPerCU = SPEC_CHAIN_BLOCKS_PER_CU;
+constexpr size_t kLdsPerCU = 160 * 1024;
+constexpr size_t chain_dyn_lds() { return kBlocksPerCU > 0 ? kLdsPerCU / kBlocksPerCU - 12 * 1024 : 0; }
+
 template <int DT, int QT, bool VEC>
 hipError_t launch_typed(ChainParams p, hipStream_t s) {
   long lag = p.B;
@@ -641,7 +670,7 @@ hipError_t launch_typed(ChainParams p, hipStream_t s) {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     if (s_resident[dev] == 0) {
       int per_cu = 0, cus = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel<DT, QT, VEC>, kBlock, 0) != hipSuccess ||
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel<DT, QT, VEC>, kBlock, chain_dyn_lds()) != hipSuccess ||
           hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipErrorInvalidValue;
       s_resident[dev] = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
@@ -652,7 +681,7 @@ hipError_t launch_typed(ChainParams p, hipStream_t s) {
   }
   p.LAG = (int)lag;
   const unsigned long long blocks = (unsigned long long)p.B * ((unsigned long long)p.R * p.SL + p.S2);  // == chain_blocks
-  chain_kernel<DT, QT, VEC><<<dim3((unsigned)blocks), dim3(kBlock), 0, s>>>(p);
+  chain_kernel<DT, QT, VEC><<<dim3((unsigned)blocks), dim3(kBlock), chain_dyn_lds(), s>>>(p);
   return hipGetLastError();
 }
 

@@ -131,24 +131,75 @@ __device__ __forceinline__ int wave_min_i(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Butterfly sum in fp64: every lane ends with the same bits.
+// fp64 DPP move: both halves through the same DPP pattern; lanes a step does not write
+// keep `ident`.
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ double dpp_d(double ident, double v) {
+  const long long iv = __double_as_longlong(v), ii = __double_as_longlong(ident);
+  const int lo = dpp_i<CTRL, ROWMASK>(static_cast<int>(ii), static_cast<int>(iv));
+  const int hi = dpp_i<CTRL, ROWMASK>(static_cast<int>(ii >> 32), static_cast<int>(iv >> 32));
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const long long iv = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(iv), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(iv >> 32), lane);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+
+// fp64 sum over the wave (DPP tree, read from lane 63): every lane ends with the same bits.
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  v += dpp_d<0xb1>(0.0, v);         // quad_perm [1,0,3,2]
+  v += dpp_d<0x4e>(0.0, v);         // quad_perm [2,3,0,1]
+  v += dpp_d<0x141>(0.0, v);        // row_half_mirror
+  v += dpp_d<0x140>(0.0, v);        // row_mirror
+  v += dpp_d<0x142, 0xa>(0.0, v);   // row_bcast:15 into rows 1, 3
+  v += dpp_d<0x143, 0xc>(0.0, v);   // row_bcast:31 into rows 2, 3
+  return readlane_d(v, 63);
+}
+
+// Inclusive prefix sum in fp64 over the lanes of a wave: shifts within rows of 16, then
+// each row adds the running total of the rows before it.
+__device__ __forceinline__ double wave_incl_scan_d(double v, int /*lane*/) {
+  v += dpp_d<0x111>(0.0, v);        // row_shr:1
+  v += dpp_d<0x112>(0.0, v);        // row_shr:2
+  v += dpp_d<0x114>(0.0, v);        // row_shr:4
+  v += dpp_d<0x118>(0.0, v);        // row_shr:8
+  v += dpp_d<0x142, 0xa>(0.0, v);   // row_bcast:15 into rows 1, 3
+  v += dpp_d<0x143, 0xc>(0.0, v);   // row_bcast:31 into rows 2, 3
   return v;
 }
 
-// Inclusive prefix sum in fp64 over the lanes of a wave.
-__device__ __forceinline__ double wave_incl_scan_d(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    double t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
+// The previous lane's value (0 in lane 0).
+__device__ __forceinline__ double wave_shr1_d(double v) { return dpp_d<0x138>(0.0, v); }   // wave_shr:1
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
+
+// Segmented reductions over groups of S consecutive lanes (S a power of two, 1..64, the
+// same in every lane): every lane of a group ends with the group's result.  DPP within
+// rows of 16 lanes (quad swaps, half-row and row mirrors: each step adds the partner
+// half's partial exactly once), xor shuffles across rows.  Call with every lane active.
+__device__ __forceinline__ float seg_max(float v, int S) {
+  const float I = -INFINITY;
+  if (S > 1) v = fmaxf(v, dpp_f<0xb1>(I, v));
+  if (S > 2) v = fmaxf(v, dpp_f<0x4e>(I, v));
+  if (S > 4) v = fmaxf(v, dpp_f<0x141>(I, v));
+  if (S > 8) v = fmaxf(v, dpp_f<0x140>(I, v));
+  if (S > 16) v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  if (S > 32) v = fmaxf(v, __shfl_xor(v, 32, kWave));
+  return v;
+}
+
+__device__ __forceinline__ double seg_sum_d(double v, int S) {
+  if (S > 1) v += dpp_d<0xb1>(0.0, v);
+  if (S > 2) v += dpp_d<0x4e>(0.0, v);
+  if (S > 4) v += dpp_d<0x141>(0.0, v);
+  if (S > 8) v += dpp_d<0x140>(0.0, v);
+  if (S > 16) v += __shfl_xor(v, 16, kWave);
+  if (S > 32) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
 
 // Block-wide minimum of one int per thread, returned to every thread: a DPP tree per
 // wave and one LDS word per wave (no contended LDS atomics).  `scratch` holds >=
@@ -170,8 +221,7 @@ __device__ __forceinline__ int block_min_i(int v, int* scratch) {
 __device__ __forceinline__ double block_excl_scan_d(double v, double* scratch, double* total) {
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   const double incl = wave_incl_scan_d(v, lane);
-  double excl = __shfl_up(incl, 1, kWave);
-  if (lane == 0) excl = 0.0;
+  const double excl = wave_shr1_d(incl);
   if (lane == kWave - 1) scratch[wave] = incl;
   __syncthreads();
   double off = 0.0, tot = 0.0;
