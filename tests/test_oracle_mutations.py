@@ -17,7 +17,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 PIN_FILES = ["test_oracle_pins.py", "test_oracle_laws.py", "test_oracle_regression.py",
-             "test_oracle_tree_residual.py", "test_oracle_stop.py", "test_oracle_tree_greedy.py"]
+             "test_oracle_tree_residual.py", "test_oracle_stop.py", "test_oracle_tree_greedy.py",
+             "test_oracle_processors.py"]
 
 # (file under oracle/, text as it stands, the planted mistake)
 MUTANTS = {
@@ -90,6 +91,15 @@ MUTANTS = {
                              "if int(node_tokens[c]) == y:"),
     "tree_greedy_last_sibling": ("tree_greedy.py", "                nxt = c\n                break\n",
                                  "                nxt = c\n"),
+    # target logit processors ([Tiny] grammar mask, exactness tests; [M7.1] §0x04G, §0x06J)
+    "topk_drops_boundary_ties": ("processors.py", "keep &= s >= kth", "keep &= s > kth"),
+    "topk_off_by_one": ("processors.py", "[::-1][top_k - 1]", "[::-1][min(top_k, len(s) - 1)]"),
+    "topp_counts_own_mass": ("processors.py", "np.flatnonzero(excl < target)", "np.flatnonzero(incl < target)"),
+    "bias_after_temperature": ("processors.py", "s = (l32 + b32).astype(np.float64)",
+                               "s = (l32 + b32 * np.float32(temperature)).astype(np.float64)"),
+    "masked_fault_hidden": ("processors.py", "    out[fault] = s[fault]\n", ""),
+    "mask_ignored_by_truncation": ("processors.py", "        keep &= np.asarray(allowed, dtype=bool)\n",
+                                   "        pass\n"),
     # stop tokens and output budget ([M7.1] §0x05B, §0x06)
     "stop_token_not_ending_round": ("chain.py", "            end = (i + 1, 1)\n", "            pass\n"),
     "stop_token_not_emitted": ("chain.py", "res.tokens = [int(t) for t in x[:end[0]]]",
