@@ -44,6 +44,12 @@ _SIGNATURES = {
     "spec_verify_greedy": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int,
                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t,
                                     _c_void_p]),
+    "spec_verify_chain_ex": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                      _c_int, _c_int, _c_int, _c_float, _c_void_p,
+                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                      _c_void_p, _c_size_t, _c_void_p]),
+    "spec_verify_greedy_ex": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
+                                       _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     "spec_verify_greedy_stop": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int,
                                          _c_void_p, _c_int, _c_void_p,
                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -61,6 +67,14 @@ _SIGNATURES = {
                                            _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                            _c_void_p, _c_size_t, _c_void_p]),
 }
+
+
+class SpecOptions(ctypes.Structure):
+    """spec_verify_options: stop tokens, budget, finish and target logit processors (device
+    pointers, NULL = off)."""
+    _fields_ = [("stop_tokens", _c_void_p), ("n_stop", ctypes.c_int32), ("budget", _c_void_p),
+                ("finish", _c_void_p), ("bias", _c_void_p), ("allowed", _c_void_p), ("top_k", _c_void_p),
+                ("top_p", _c_void_p)]
 
 
 class SpecError(RuntimeError):
@@ -182,8 +196,33 @@ def _stop_args(stop_tokens, budget, B, dev):
     return n
 
 
+def _proc_args(bias, allowed, top_k, top_p, B, R, V, dev):
+    """Checks the processor tensors: bias [V] fp32, allowed [B, R, ceil(V/32)] int32/uint32
+    bit words, top_k [B] int32, top_p [B] fp32 (each None = off)."""
+    if bias is not None:
+        _need(bias, "bias", dtype=torch.float32, shape=(V,), device=dev)
+    if allowed is not None:
+        if allowed.dtype not in (torch.int32, torch.uint32):
+            raise TypeError("allowed must be int32 or uint32 bit words")
+        _need(allowed, "allowed", shape=(B, R, (V + 31) // 32), device=dev)
+    if top_k is not None:
+        _need(top_k, "top_k", dtype=torch.int32, shape=(B,), device=dev)
+    if top_p is not None:
+        _need(top_p, "top_p", dtype=torch.float32, shape=(B,), device=dev)
+
+
+def _options(stop_tokens, budget, finish, bias=None, allowed=None, top_k=None, top_p=None) -> SpecOptions:
+    o = SpecOptions()
+    o.stop_tokens = _ptr(stop_tokens)
+    o.n_stop = 0 if stop_tokens is None else int(stop_tokens.numel())
+    o.budget, o.finish = _ptr(budget), _ptr(finish)
+    o.bias, o.allowed, o.top_k, o.top_p = _ptr(bias), _ptr(allowed), _ptr(top_k), _ptr(top_p)
+    return o
+
+
 def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature, with_stats,
-                workspace_tensor, out, stop_tokens=None, budget=None):
+                workspace_tensor, out, stop_tokens=None, budget=None, bias=None, allowed=None, top_k=None,
+                top_p=None):
     lib = load_library()
     _need(target_logits, "target_logits")
     if target_logits.dim() != 3:
@@ -203,6 +242,8 @@ def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
             out["stats"] = torch.empty(B, R, 4, dtype=torch.float32, device=dev)
     stopping = stop_tokens is not None or budget is not None
     n_stop = _stop_args(stop_tokens, budget, B, dev)
+    processing = any(t is not None for t in (bias, allowed, top_k, top_p))
+    _proc_args(bias, allowed, top_k, top_p, B, R, V, dev)
     if stopping and "finish" not in out:
         out["finish"] = torch.empty(B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -213,7 +254,13 @@ def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
     wp, wn = _aligned_ws(ws)
     head = (_ptr(target_logits), lt, _ptr(draft_probs), qt, _ptr(draft_tokens), _ptr(uniforms),
             B, G, V, ctypes.c_float(float(temperature)))
-    keep = (target_logits, draft_probs, draft_tokens, uniforms, ws, stream, stop_tokens, budget)
+    keep = (target_logits, draft_probs, draft_tokens, uniforms, ws, stream, stop_tokens, budget, bias, allowed,
+            top_k, top_p)
+    if processing:
+        opt = _options(stop_tokens, budget, out.get("finish"), bias, allowed, top_k, top_p)
+        args = head + (ctypes.byref(opt), _ptr(out["accepted_len"]), _ptr(out["out_tokens"]),
+                       _ptr(out["req_status"]), _ptr(out.get("stats")), wp, wn, ctypes.c_void_p(stream.cuda_stream))
+        return lib.spec_verify_chain_ex, args, keep + (opt,), out
     if not stopping:
         args = head + (_ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
                        _ptr(out.get("stats")), wp, wn, ctypes.c_void_p(stream.cuda_stream))
@@ -228,31 +275,39 @@ def spec_verify_chain(target_logits: torch.Tensor, draft_probs: torch.Tensor,
                       draft_tokens: torch.Tensor, uniforms: torch.Tensor, temperature: float,
                       *, with_stats: bool = False, workspace_tensor: Optional[torch.Tensor] = None,
                       out: Optional[dict] = None, stop_tokens: Optional[torch.Tensor] = None,
-                      budget: Optional[torch.Tensor] = None) -> dict:
-    """Chain verification by rejection sampling (C entry point spec_verify_chain, or
-    spec_verify_chain_stop when stop_tokens or budget is given).
+                      budget: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                      allowed: Optional[torch.Tensor] = None, top_k: Optional[torch.Tensor] = None,
+                      top_p: Optional[torch.Tensor] = None) -> dict:
+    """Chain verification by rejection sampling (C entry point spec_verify_chain;
+    spec_verify_chain_stop when stop_tokens or budget is given; spec_verify_chain_ex when a
+    processor is given).
 
     target_logits [B, gamma+1, V] bf16/fp32; draft_probs [B, gamma, V] fp32/bf16;
     draft_tokens [B, gamma] int32; uniforms [B, gamma+1] fp32; temperature > 0;
-    stop_tokens [n] int32 (n <= 256); budget [B] int32 remaining output budgets.
+    stop_tokens [n] int32 (n <= 256); budget [B] int32 remaining output budgets;
+    processors: bias [V] fp32, allowed [B, gamma+1, ceil(V/32)] int32 bit words,
+    top_k [B] int32, top_p [B] fp32.
     Returns {accepted_len [B], out_tokens [B, gamma+1], req_status [B], stats?, finish?}
     (int32 / fp32 GPU tensors, valid once the current stream reaches the call).
     """
     fn, args, _, out = _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
-                                   with_stats, workspace_tensor, out, stop_tokens, budget)
+                                   with_stats, workspace_tensor, out, stop_tokens, budget, bias, allowed,
+                                   top_k, top_p)
     _check(fn(*args))
     return out
 
 
 def prepare_chain(target_logits, draft_probs, draft_tokens, uniforms, temperature, *,
                   with_stats=False, workspace_tensor=None, out=None, stop_tokens=None,
-                  budget=None) -> PreparedCall:
+                  budget=None, bias=None, allowed=None, top_k=None, top_p=None) -> PreparedCall:
     """spec_verify_chain with its arguments checked and marshalled once (see PreparedCall)."""
     return PreparedCall(*_chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
-                                     with_stats, workspace_tensor, out, stop_tokens, budget))
+                                     with_stats, workspace_tensor, out, stop_tokens, budget, bias, allowed,
+                                     top_k, top_p))
 
 
-def _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens=None, budget=None):
+def _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens=None, budget=None, bias=None,
+                 allowed=None):
     lib = load_library()
     _need(target_logits, "target_logits")
     if target_logits.dim() != 3:
@@ -268,6 +323,8 @@ def _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens
                    req_status=torch.empty(B, dtype=torch.int32, device=dev))
     stopping = stop_tokens is not None or budget is not None
     n_stop = _stop_args(stop_tokens, budget, B, dev)
+    processing = bias is not None or allowed is not None
+    _proc_args(bias, allowed, None, None, B, R, V, dev)
     if stopping and "finish" not in out:
         out["finish"] = torch.empty(B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -276,8 +333,13 @@ def _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens
         raise SpecError(f"unsupported sizes B={B} gamma={G} V={V}")
     ws = workspace_tensor if workspace_tensor is not None else workspace("greedy", need, dev, stream)
     wp, wn = _aligned_ws(ws)
-    keep = (target_logits, draft_tokens, ws, stream, stop_tokens, budget)
+    keep = (target_logits, draft_tokens, ws, stream, stop_tokens, budget, bias, allowed)
     head = (_ptr(target_logits), lt, _ptr(draft_tokens), B, G, V)
+    if processing:
+        opt = _options(stop_tokens, budget, out.get("finish"), bias, allowed)
+        args = head + (ctypes.byref(opt), _ptr(out["accepted_len"]), _ptr(out["out_tokens"]),
+                       _ptr(out["req_status"]), wp, wn, ctypes.c_void_p(stream.cuda_stream))
+        return lib.spec_verify_greedy_ex, args, keep + (opt,), out
     if not stopping:
         args = head + (_ptr(out["accepted_len"]), _ptr(out["out_tokens"]), _ptr(out["req_status"]),
                        wp, wn, ctypes.c_void_p(stream.cuda_stream))
@@ -291,22 +353,26 @@ def _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens
 def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor, *,
                        workspace_tensor: Optional[torch.Tensor] = None,
                        out: Optional[dict] = None, stop_tokens: Optional[torch.Tensor] = None,
-                       budget: Optional[torch.Tensor] = None) -> dict:
-    """Greedy argmax-match verification (C entry point spec_verify_greedy, or
-    spec_verify_greedy_stop when stop_tokens or budget is given).
+                       budget: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                       allowed: Optional[torch.Tensor] = None) -> dict:
+    """Greedy argmax-match verification (C entry point spec_verify_greedy;
+    spec_verify_greedy_stop when stop_tokens or budget is given; spec_verify_greedy_ex when
+    bias or allowed is given).
 
     target_logits [B, gamma+1, V] bf16/fp32; draft_tokens [B, gamma] int32; stop_tokens,
-    budget as for spec_verify_chain.
+    budget, bias, allowed as for spec_verify_chain.
     """
-    fn, args, _, out = _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens, budget)
+    fn, args, _, out = _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens, budget, bias,
+                                    allowed)
     _check(fn(*args))
     return out
 
 
 def prepare_greedy(target_logits, draft_tokens, *, workspace_tensor=None, out=None, stop_tokens=None,
-                   budget=None) -> PreparedCall:
+                   budget=None, bias=None, allowed=None) -> PreparedCall:
     """spec_verify_greedy with its arguments checked and marshalled once (see PreparedCall)."""
-    return PreparedCall(*_greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens, budget))
+    return PreparedCall(*_greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens, budget,
+                                      bias, allowed))
 
 
 def _tree_args(node_logits, node_tokens, parents, uniforms, temperature, workspace_tensor, out):

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspec_verify.so")
-SOURCES = ["abi.hip", "chain.hip", "greedy.hip", "tree.hip"]
+SOURCES = ["abi.hip", "chain.hip", "greedy.hip", "tree.hip", "proc.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

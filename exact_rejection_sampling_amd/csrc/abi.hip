@@ -25,6 +25,15 @@ int chunks(long V, long per) { return static_cast<int>((V + per - 1) / per); }
 bool stop_ok(const int32_t* stop_tokens, int n_stop) {
   return n_stop >= 0 && n_stop <= SPEC_MAX_STOP && (n_stop == 0 || stop_tokens != nullptr);
 }
+sv::ProcSpec proc_spec(const spec_verify_options& o, int V, const float* thresh) {
+  sv::ProcSpec pr{};
+  pr.bias = o.bias;
+  pr.allowed = o.allowed;
+  pr.thresh = thresh;
+  pr.W = (V + 31) / 32;
+  pr.on = o.bias || o.allowed || thresh;
+  return pr;
+}
 sv::StopSpec stop_spec(const int32_t* stop_tokens, int n_stop, const int32_t* budget, int32_t* finish) {
   sv::StopSpec st;
   st.stop = n_stop > 0 ? stop_tokens : nullptr;
@@ -96,9 +105,9 @@ spec_status spec_verify_chain(const void* target_logits, int logit_dtype, const 
                               int gamma, int V, float temperature, int32_t* accepted_len,
                               int32_t* out_tokens, int32_t* req_status, float* stats,
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return spec_verify_chain_stop(target_logits, logit_dtype, draft_probs, q_dtype, draft_tokens, uniforms, B,
-                                gamma, V, temperature, nullptr, 0, nullptr, accepted_len, out_tokens,
-                                req_status, nullptr, stats, workspace, workspace_bytes, stream);
+  return spec_verify_chain_ex(target_logits, logit_dtype, draft_probs, q_dtype, draft_tokens, uniforms, B, gamma,
+                              V, temperature, nullptr, accepted_len, out_tokens, req_status, stats, workspace,
+                              workspace_bytes, stream);
 }
 
 spec_status spec_verify_chain_stop(const void* target_logits, int logit_dtype, const void* draft_probs,
@@ -107,7 +116,23 @@ spec_status spec_verify_chain_stop(const void* target_logits, int logit_dtype, c
                                    int n_stop, const int32_t* budget, int32_t* accepted_len,
                                    int32_t* out_tokens, int32_t* req_status, int32_t* finish, float* stats,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!sizes_ok(B, gamma, V) || !temperature_ok(temperature) || !stop_ok(stop_tokens, n_stop))
+  spec_verify_options o = {};
+  o.stop_tokens = stop_tokens;
+  o.n_stop = n_stop;
+  o.budget = budget;
+  o.finish = finish;
+  return spec_verify_chain_ex(target_logits, logit_dtype, draft_probs, q_dtype, draft_tokens, uniforms, B, gamma,
+                              V, temperature, &o, accepted_len, out_tokens, req_status, stats, workspace,
+                              workspace_bytes, stream);
+}
+
+spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, const void* draft_probs,
+                                 int q_dtype, const int32_t* draft_tokens, const float* uniforms, int B,
+                                 int gamma, int V, float temperature, const spec_verify_options* opt,
+                                 int32_t* accepted_len, int32_t* out_tokens, int32_t* req_status, float* stats,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const spec_verify_options o = opt ? *opt : spec_verify_options{};
+  if (!sizes_ok(B, gamma, V) || !temperature_ok(temperature) || !stop_ok(o.stop_tokens, o.n_stop))
     return SPEC_EINVAL;
   if (!dtype_ok(logit_dtype) || !dtype_ok(q_dtype)) return SPEC_EDTYPE;
   if (!sv::grid_fits(sv::chain_blocks(B, gamma, V))) return SPEC_EINVAL;
@@ -127,7 +152,10 @@ spec_status spec_verify_chain_stop(const void* target_logits, int logit_dtype, c
   p.out_tokens = out_tokens;
   p.req_status = req_status;
   p.stats = stats;
-  p.st = stop_spec(stop_tokens, n_stop, budget, finish);
+  p.st = stop_spec(o.stop_tokens, o.n_stop, o.budget, o.finish);
+  const bool truncate = o.top_k || o.top_p;
+  p.pr = proc_spec(o, V, truncate ? reinterpret_cast<float*>(ws + L.thresh) : nullptr);
+  p.thresh_ws = truncate ? reinterpret_cast<float*>(ws + L.thresh) : nullptr;
   p.part = reinterpret_cast<float2*>(ws + L.part);
   p.gath = reinterpret_cast<unsigned long long*>(ws + L.gath);
   p.tmass = reinterpret_cast<double*>(ws + L.tmass);
@@ -144,7 +172,23 @@ spec_status spec_verify_chain_stop(const void* target_logits, int logit_dtype, c
   const double c2 = kLog2e / static_cast<double>(temperature);
   p.c2 = static_cast<float>(c2);
   p.inv_t = 1.0 / static_cast<double>(temperature);
-  const bool vec = (V % 8 == 0) && aligned16(target_logits) && (gamma == 0 || aligned16(draft_probs));
+  const bool vec = (V % 8 == 0) && aligned16(target_logits) && (gamma == 0 || aligned16(draft_probs)) &&
+                   (!o.bias || aligned16(o.bias));
+  if (truncate) {
+    sv::ThreshParams t{};
+    t.logits = target_logits;
+    t.bias = o.bias;
+    t.allowed = o.allowed;
+    t.top_k = o.top_k;
+    t.top_p = o.top_p;
+    t.thresh = p.thresh_ws;
+    t.rows = B * (gamma + 1);
+    t.R = gamma + 1;
+    t.V = V;
+    t.W = p.pr.W;
+    t.c2 = p.c2;
+    if (sv::launch_thresholds(t, logit_dtype, vec, stream) != hipSuccess) return SPEC_EHIP;
+  }
   return sv::launch_chain(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
@@ -152,9 +196,8 @@ spec_status spec_verify_greedy(const void* target_logits, int logit_dtype, const
                                int B, int gamma, int V, int32_t* accepted_len, int32_t* out_tokens,
                                int32_t* req_status, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
-  return spec_verify_greedy_stop(target_logits, logit_dtype, draft_tokens, B, gamma, V, nullptr, 0, nullptr,
-                                 accepted_len, out_tokens, req_status, nullptr, workspace, workspace_bytes,
-                                 stream);
+  return spec_verify_greedy_ex(target_logits, logit_dtype, draft_tokens, B, gamma, V, nullptr, accepted_len,
+                               out_tokens, req_status, workspace, workspace_bytes, stream);
 }
 
 spec_status spec_verify_greedy_stop(const void* target_logits, int logit_dtype, const int32_t* draft_tokens,
@@ -162,7 +205,21 @@ spec_status spec_verify_greedy_stop(const void* target_logits, int logit_dtype, 
                                     const int32_t* budget, int32_t* accepted_len, int32_t* out_tokens,
                                     int32_t* req_status, int32_t* finish, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream) {
-  if (!sizes_ok(B, gamma, V) || !stop_ok(stop_tokens, n_stop)) return SPEC_EINVAL;
+  spec_verify_options o = {};
+  o.stop_tokens = stop_tokens;
+  o.n_stop = n_stop;
+  o.budget = budget;
+  o.finish = finish;
+  return spec_verify_greedy_ex(target_logits, logit_dtype, draft_tokens, B, gamma, V, &o, accepted_len,
+                               out_tokens, req_status, workspace, workspace_bytes, stream);
+}
+
+spec_status spec_verify_greedy_ex(const void* target_logits, int logit_dtype, const int32_t* draft_tokens,
+                                  int B, int gamma, int V, const spec_verify_options* opt, int32_t* accepted_len,
+                                  int32_t* out_tokens, int32_t* req_status, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  const spec_verify_options o = opt ? *opt : spec_verify_options{};
+  if (!sizes_ok(B, gamma, V) || !stop_ok(o.stop_tokens, o.n_stop)) return SPEC_EINVAL;
   if (!dtype_ok(logit_dtype)) return SPEC_EDTYPE;
   if (!sv::grid_fits(sv::greedy_blocks(B, gamma, V))) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
@@ -177,7 +234,8 @@ spec_status spec_verify_greedy_stop(const void* target_logits, int logit_dtype, 
   p.accepted_len = accepted_len;
   p.out_tokens = out_tokens;
   p.req_status = req_status;
-  p.st = stop_spec(stop_tokens, n_stop, budget, finish);
+  p.st = stop_spec(o.stop_tokens, o.n_stop, o.budget, o.finish);
+  p.pr = proc_spec(o, V, nullptr);   // top-k and top-p keep the maximum: no effect on an argmax
   p.part = reinterpret_cast<unsigned long long*>(ws + L.part);
   p.B = B;
   p.G = gamma;
@@ -187,7 +245,7 @@ spec_status spec_verify_greedy_stop(const void* target_logits, int logit_dtype, 
   p.P = sl.P;
   p.CPW = sl.CPW;
   p.SL = sl.SL;
-  const bool vec = (V % 8 == 0) && aligned16(target_logits);
+  const bool vec = (V % 8 == 0) && aligned16(target_logits) && (!o.bias || aligned16(o.bias));
   return sv::launch_greedy(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 

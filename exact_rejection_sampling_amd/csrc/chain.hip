@@ -30,6 +30,7 @@
 // "Module 16: Speculative Decoding", "The Math: Speculative Sampling" (u < min(1, p/q)).
 #include "device_common.h"
 #include "internal.h"
+#include "proc.h"
 #include "spec_verify.h"
 
 namespace sv {
@@ -49,14 +50,17 @@ __device__ __forceinline__ unsigned long long* gather_rec(const ChainParams& p, 
   return p.gath + ((size_t)b * p.G + i) * 3;
 }
 
-template <int DT>
+template <int DT, bool PROC>
 __device__ __forceinline__ void gather_issue(const ChainParams& p, int b, int i, unsigned& x, unsigned& lb,
                                              unsigned& qb) {
   const int t = p.tokens[(size_t)b * p.G + i];
   x = static_cast<unsigned>(t);
   lb = qb = 0u;
   if (t >= 0 && t < p.V) {
-    lb = __float_as_uint(load_scalar<DT>(p.logits, ((size_t)b * p.R + i) * p.V + t));
+    const size_t rowid = (size_t)b * p.R + i;
+    float l = load_scalar<DT>(p.logits, rowid * p.V + t);
+    if constexpr (PROC) l = proc1(p.pr, rowid, row_tau(p.pr, rowid), t, l);
+    lb = __float_as_uint(l);
     qb = __float_as_uint(gather_q(p, ((size_t)b * p.G + i) * p.V + t));
   }
 }
@@ -69,8 +73,28 @@ __device__ __forceinline__ void gather_publish(const ChainParams& p, int b, int 
   publish_u64(g + 2, (1ull << 63) | qb);
 }
 
-// Statistics item: slice `slice` of row i of request b.
+// Online-softmax summary of the chunks a wave visits, the processors applied to every
+// element first.
 template <int DT, bool VEC>
+__device__ __forceinline__ void wave_row_summary_proc(const ChainParams& p, size_t rowid, long first, int lane,
+                                                      float& m_out, float& z_out) {
+  const float tau = row_tau(p.pr, rowid);
+  LaneSoftmax st;
+  stream_chunks<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, p.P, first, kWavesPerBlock, p.CPW, lane,
+                         [&](const ChunkRegs<DT>& r, long c) {
+                           float v[kStatVecs][8];
+                           chunk_values<DT>(r, v);
+#pragma unroll
+                           for (int j = 0; j < kStatVecs; ++j)
+                             proc8<VEC>(p.pr, rowid, tau, c * kWaveChunk + static_cast<long>(j * kWave + lane) * kVec,
+                                        p.V, v[j]);
+                           lane_softmax_update(st, v, p.c2);
+                         });
+  wave_softmax_merge(st, p.c2, m_out, z_out);
+}
+
+// Statistics item: slice `slice` of row i of request b.
+template <int DT, bool VEC, bool PROC>
 __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
   __shared__ float s_wm[kWavesPerBlock], s_wz[kWavesPerBlock];
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
@@ -79,12 +103,15 @@ __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
   // probability for the decision, overlapped with the streaming below
   const bool gathers = slice == 0 && i < p.G && threadIdx.x == 0;
   unsigned gx = 0, gl = 0, gq = 0;
-  if (gathers) gather_issue<DT>(p, b, i, gx, gl, gq);
+  if (gathers) gather_issue<DT, PROC>(p, b, i, gx, gl, gq);
   // wave w streams chunks first + 4k of this slice (k < CPW)
   const long first = (long)slice * kWavesPerBlock * p.CPW + wave;
   float m, z;
-  wave_row_summary<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, p.P, first, kWavesPerBlock, p.CPW, lane,
-                            p.c2, m, z);
+  if constexpr (PROC)
+    wave_row_summary_proc<DT, VEC>(p, rowid, first, lane, m, z);
+  else
+    wave_row_summary<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, p.P, first, kWavesPerBlock, p.CPW, lane,
+                              p.c2, m, z);
   if (lane == 0) {
     s_wm[wave] = m;
     s_wz[wave] = z;
@@ -162,6 +189,7 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
   }
   const float ut = p.u[(size_t)b * R + G];
   const int H = p.st.budget ? p.st.budget[b] : INT32_MAX;   // remaining output budget
+  const float tau_lane = lane < R ? row_tau(p.pr, (size_t)b * R + lane) : -INFINITY;   // keep thresholds
   const int n_stop = p.st.n_stop;
   int stop_e[SPEC_MAX_STOP / kWave];
 #pragma unroll
@@ -301,8 +329,10 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
     finish = SPEC_FINISH_BUDGET;
   }
   if (timeout) status = SPEC_REQ_INTERNAL;
+  const float tau_a = __shfl(tau_lane, A < R ? A : 0, kWave);
   if (lane == 0) {
     const bool drawn = status == 0 && draw;
+    s_dec.tau = tau_a;
     s_dec.A = status == 0 ? A : -1;
     s_dec.status = status;
     s_dec.draw = drawn ? 1 : 0;
@@ -331,15 +361,21 @@ __device__ __forceinline__ float term_weight(float l, float qv, float c2, float 
 
 // The weights of this thread's 8 elements in each slab of terminal chunk c, both slabs'
 // loads issued together.
-template <int DT, int QT, bool VEC, bool RESID>
+template <int DT, int QT, bool VEC, bool RESID, bool PROC>
 __device__ __forceinline__ void term_chunk(const ChainParams& p, const void* lrow, const void* qrow, int c,
-                                           const ChainDecision& d, float (&w)[kTermSlabs][8], bool& bad) {
+                                           const ChainDecision& d, size_t rowid, float (&w)[kTermSlabs][8],
+                                           bool& bad) {
   float lv[kTermSlabs][8], qv[kTermSlabs][8];
 #pragma unroll
   for (int s = 0; s < kTermSlabs; ++s) {
     const long e0 = ((long)c * kTermSlabs + s) * kSlab + (long)threadIdx.x * kVec;
     load8<DT, VEC, false>(lrow, e0, p.V, lv[s], -INFINITY);
     if constexpr (RESID) load8<QT, VEC, false>(qrow, e0, p.V, qv[s], 0.0f);
+  }
+  if constexpr (PROC) {
+#pragma unroll
+    for (int s = 0; s < kTermSlabs; ++s)
+      proc8<VEC>(p.pr, rowid, d.tau, ((long)c * kTermSlabs + s) * kSlab + (long)threadIdx.x * kVec, p.V, lv[s]);
   }
 #pragma unroll
   for (int s = 0; s < kTermSlabs; ++s)
@@ -388,7 +424,7 @@ __device__ __forceinline__ void row_stats(const ChainParams& p, const RowState& 
 // The selector of request b: every other chunk's mass is awaited; then the chunk where the
 // running mass passes u_gamma * W is rescanned in vocabulary order and the outputs are
 // written.  `own` is the mass of chunk S2 - 1, which the selector computed itself.
-template <int DT, int QT, bool VEC, bool RESID>
+template <int DT, int QT, bool VEC, bool RESID, bool PROC>
 __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d, const RowState& rs,
                              double own, const void* lrow, const void* qrow) {
   __shared__ double s_scan[kWavesPerBlock];
@@ -465,7 +501,7 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
     //    in order within a slab
     float w[kTermSlabs][8];
     bool bad = false;
-    term_chunk<DT, QT, VEC, RESID>(p, lrow, qrow, cstar, d, w, bad);
+    term_chunk<DT, QT, VEC, RESID, PROC>(p, lrow, qrow, cstar, d, (size_t)b * p.R + d.A, w, bad);
     double before_slab = 0.0;
     int last_pos = -1, pick = 0x7fffffff;
 #pragma unroll
@@ -570,28 +606,30 @@ __device__ void chain_clear(const ChainParams& p, int b) {
   for (int j = tid; j < p.R * p.SL; j += kBlock) clear_f2(part_b + j);
   for (int j = tid; j < 3 * p.G; j += kBlock) clear_u64(gather_rec(p, b, 0) + j);
   for (int j = tid; j < p.S2; j += kBlock) clear_mass(p.tmass + (size_t)b * p.S2 + j);
+  if (p.thresh_ws)   // written by the threshold pass, read by this request's blocks only
+    for (int j = tid; j < p.R; j += kBlock) store_wt(p.thresh_ws + (size_t)b * p.R + j, 0.0f);
 }
 
 // Terminal item with a valid decision: chunk c of request b's terminal row; the last
 // chunk's item selects.
-template <int DT, int QT, bool VEC, bool RESID>
+template <int DT, int QT, bool VEC, bool RESID, bool PROC>
 __device__ void terminal_body(const ChainParams& p, int b, int c, const ChainDecision& d, const RowState& rs) {
   const void* lrow = row_ptr<DT>(p.logits, (size_t)b * p.R + d.A, p.V);
   const void* qrow = RESID ? row_ptr<QT>(p.q, (size_t)b * p.G + d.A, p.V) : nullptr;
   float w[kTermSlabs][8];
   bool bad = false;
-  term_chunk<DT, QT, VEC, RESID>(p, lrow, qrow, c, d, w, bad);
+  term_chunk<DT, QT, VEC, RESID, PROC>(p, lrow, qrow, c, d, (size_t)b * p.R + d.A, w, bad);
   const double m = block_mass(w, bad);
   if (c != p.S2 - 1) {
     if (threadIdx.x == 0) publish_mass(p.tmass + (size_t)b * p.S2 + c, m);
     return;
   }
-  chain_select<DT, QT, VEC, RESID>(p, b, d, rs, m, lrow, qrow);
+  chain_select<DT, QT, VEC, RESID, PROC>(p, b, d, rs, m, lrow, qrow);
   __syncthreads();
   chain_clear(p, b);
 }
 
-template <int DT, int QT, bool VEC>
+template <int DT, int QT, bool VEC, bool PROC>
 __device__ void terminal_item(const ChainParams& p, int b, int c) {
   __shared__ RowState s_rs;
   __shared__ ChainDecision s_dec;
@@ -609,8 +647,8 @@ __device__ void terminal_item(const ChainParams& p, int b, int c) {
     chain_clear(p, b);
     return;
   }
-  if (d.A < p.G) terminal_body<DT, QT, VEC, true>(p, b, c, d, s_rs);
-  else terminal_body<DT, QT, VEC, false>(p, b, c, d, s_rs);
+  if (d.A < p.G) terminal_body<DT, QT, VEC, true, PROC>(p, b, c, d, s_rs);
+  else terminal_body<DT, QT, VEC, false, PROC>(p, b, c, d, s_rs);
 }
 
 // Block order: groups g = 0 .. B + LAG - 1, group g holding the statistics items of
@@ -635,11 +673,19 @@ __device__ __forceinline__ Item block_item(const ChainParams& p, long t) {
   return it;
 }
 
-template <int DT, int QT, bool VEC>
+template <int DT, int QT, bool VEC, bool PROC>
+// Waves per SIMD the register allocation must allow (0: whatever the code needs).
+#ifndef SPEC_CHAIN_WAVES_PER_EU
+#define SPEC_CHAIN_WAVES_PER_EU 0
+#endif
+#if SPEC_CHAIN_WAVES_PER_EU > 0
+__global__ __launch_bounds__(kBlock, SPEC_CHAIN_WAVES_PER_EU) void chain_kernel(ChainParams p) {
+#else
 __global__ __launch_bounds__(kBlock) void chain_kernel(ChainParams p) {
+#endif
   const Item it = block_item(p, blockIdx.x);
-  if (it.terminal) terminal_item<DT, QT, VEC>(p, it.b, it.idx);
-  else stats_item<DT, VEC>(p, it.b, it.idx / p.SL, it.idx % p.SL);
+  if (it.terminal) terminal_item<DT, QT, VEC, PROC>(p, it.b, it.idx);
+  else stats_item<DT, VEC, PROC>(p, it.b, it.idx / p.SL, it.idx % p.SL);
 }
 
 // Lag between a request's statistics and terminal items, in rounds of resident blocks:
@@ -661,7 +707,7 @@ constexpr int kBlocksPerCU = SPEC_CHAIN_BLOCKS_PER_CU;
 constexpr size_t kLdsPerCU = 160 * 1024;
 constexpr size_t chain_dyn_lds() { return kBlocksPerCU > 0 ? kLdsPerCU / kBlocksPerCU - 12 * 1024 : 0; }
 
-template <int DT, int QT, bool VEC>
+template <int DT, int QT, bool VEC, bool PROC>
 hipError_t launch_typed(ChainParams p, hipStream_t s) {
   long lag = p.B;
   if (kLagTenths > 0) {
@@ -670,7 +716,7 @@ hipError_t launch_typed(ChainParams p, hipStream_t s) {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     if (s_resident[dev] == 0) {
       int per_cu = 0, cus = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel<DT, QT, VEC>, kBlock, chain_dyn_lds()) != hipSuccess ||
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel<DT, QT, VEC, PROC>, kBlock, chain_dyn_lds()) != hipSuccess ||
           hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return hipErrorInvalidValue;
       s_resident[dev] = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
@@ -681,20 +727,25 @@ hipError_t launch_typed(ChainParams p, hipStream_t s) {
   }
   p.LAG = (int)lag;
   const unsigned long long blocks = (unsigned long long)p.B * ((unsigned long long)p.R * p.SL + p.S2);  // == chain_blocks
-  chain_kernel<DT, QT, VEC><<<dim3((unsigned)blocks), dim3(kBlock), chain_dyn_lds(), s>>>(p);
+  chain_kernel<DT, QT, VEC, PROC><<<dim3((unsigned)blocks), dim3(kBlock), chain_dyn_lds(), s>>>(p);
   return hipGetLastError();
+}
+
+template <bool PROC>
+hipError_t launch_dispatch(const ChainParams& p, int logit_dtype, bool vec, hipStream_t s) {
+  const bool lb = logit_dtype == kBF16, qb = p.q_dtype == kBF16;
+  if (vec) {
+    if (lb) return qb ? launch_typed<kBF16, kBF16, true, PROC>(p, s) : launch_typed<kBF16, kF32, true, PROC>(p, s);
+    return qb ? launch_typed<kF32, kBF16, true, PROC>(p, s) : launch_typed<kF32, kF32, true, PROC>(p, s);
+  }
+  if (lb) return qb ? launch_typed<kBF16, kBF16, false, PROC>(p, s) : launch_typed<kBF16, kF32, false, PROC>(p, s);
+  return qb ? launch_typed<kF32, kBF16, false, PROC>(p, s) : launch_typed<kF32, kF32, false, PROC>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_chain(const ChainParams& p, int logit_dtype, bool vec, hipStream_t s) {
-  const bool lb = logit_dtype == kBF16, qb = p.q_dtype == kBF16;
-  if (vec) {
-    if (lb) return qb ? launch_typed<kBF16, kBF16, true>(p, s) : launch_typed<kBF16, kF32, true>(p, s);
-    return qb ? launch_typed<kF32, kBF16, true>(p, s) : launch_typed<kF32, kF32, true>(p, s);
-  }
-  if (lb) return qb ? launch_typed<kBF16, kBF16, false>(p, s) : launch_typed<kBF16, kF32, false>(p, s);
-  return qb ? launch_typed<kF32, kBF16, false>(p, s) : launch_typed<kF32, kF32, false>(p, s);
+  return p.pr.on ? launch_dispatch<true>(p, logit_dtype, vec, s) : launch_dispatch<false>(p, logit_dtype, vec, s);
 }
 
 }  // namespace sv

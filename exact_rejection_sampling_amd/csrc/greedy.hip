@@ -24,6 +24,7 @@
 // mismatch).
 #include "device_common.h"
 #include "internal.h"
+#include "proc.h"
 #include "spec_verify.h"
 
 namespace sv {
@@ -33,15 +34,22 @@ namespace {
 // Argmax summary of the chunks a wave visits (see stream_chunks): per lane the maximum
 // and the lowest position holding it (positions rise with the chunk and, inside a chunk,
 // with j and e), then the wave's maximum and the lowest position among its lanes.
-template <int DT, bool VEC>
-__device__ __forceinline__ GreedyPart wave_row_argmax(const void* row, long V, long P, long first,
-                                                      long stride, int n, int lane) {
+// PROC: the processors (bias, allowed set) are applied to every element of row `rowid`
+// first; truncations keep the maximum, so they never move an argmax and are not applied.
+template <int DT, bool VEC, bool PROC>
+__device__ __forceinline__ GreedyPart wave_row_argmax(const ProcSpec& pr, size_t rowid, const void* row, long V,
+                                                      long P, long first, long stride, int n, int lane) {
   float m = -INFINITY;
   int idx = 0x7fffffff;
   bool nan = false;
   stream_chunks<DT, VEC>(row, V, P, first, stride, n, lane, [&](const ChunkRegs<DT>& r, long c) {
     float v[kStatVecs][8];
     chunk_values<DT>(r, v);
+    if constexpr (PROC) {
+#pragma unroll
+      for (int j = 0; j < kStatVecs; ++j)
+        proc8<VEC>(pr, rowid, -INFINITY, c * kWaveChunk + static_cast<long>(j * kWave + lane) * kVec, V, v[j]);
+    }
     lane_argmax_update(v, c * kWaveChunk, lane, m, idx, nan);
   });
   GreedyPart g;
@@ -57,14 +65,14 @@ __device__ __forceinline__ GreedyPart unpack(unsigned long long b) {
 }
 
 // Streaming item: slice `slice` of row i of request b.
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool PROC>
 __device__ void stream_item(const GreedyParams& p, int b, int i, int slice) {
   __shared__ GreedyPart s_w[kWavesPerBlock];
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   const size_t rowid = (size_t)b * p.R + i;
   const long first = (long)slice * kWavesPerBlock * p.CPW + wave;
-  const GreedyPart g = wave_row_argmax<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, p.P, first,
-                                                kWavesPerBlock, p.CPW, lane);
+  const GreedyPart g = wave_row_argmax<DT, VEC, PROC>(p.pr, rowid, row_ptr<DT>(p.logits, rowid, p.V), p.V, p.P,
+                                                      first, kWavesPerBlock, p.CPW, lane);
   if (lane == 0) s_w[wave] = g;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -224,11 +232,11 @@ __device__ __forceinline__ Item block_item(const GreedyParams& p, long t) {
   return it;
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool PROC>
 __global__ __launch_bounds__(kBlock) void greedy_kernel(GreedyParams p) {
   const Item it = block_item(p, blockIdx.x);
   if (it.decider) greedy_decide(p, it.b);
-  else stream_item<DT, VEC>(p, it.b, it.idx / p.SL, it.idx % p.SL);
+  else stream_item<DT, VEC, PROC>(p, it.b, it.idx / p.SL, it.idx % p.SL);
 }
 
 // Lag between a request's streaming items and its decider, in tenths of a round of
@@ -239,14 +247,14 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(GreedyParams p) {
 #endif
 constexpr long kGreedyLagTenths = SPEC_GREEDY_LAG_TENTHS;
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool PROC>
 hipError_t launch_typed(GreedyParams p, hipStream_t s) {
   static int s_resident[64] = {0};   // resident blocks per device ordinal; 0 = not queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (s_resident[dev] == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, greedy_kernel<DT, VEC>, kBlock, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, greedy_kernel<DT, VEC, PROC>, kBlock, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return hipErrorInvalidValue;
     s_resident[dev] = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
@@ -257,15 +265,19 @@ hipError_t launch_typed(GreedyParams p, hipStream_t s) {
   if (lag > p.B) lag = p.B;
   p.LAG = (int)lag;
   const unsigned long long g = (unsigned long long)p.B * ((unsigned long long)p.R * p.SL + 1);  // == greedy_blocks
-  greedy_kernel<DT, VEC><<<dim3((unsigned)g), dim3(kBlock), 0, s>>>(p);
+  greedy_kernel<DT, VEC, PROC><<<dim3((unsigned)g), dim3(kBlock), 0, s>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_greedy(const GreedyParams& p, int logit_dtype, bool vec, hipStream_t s) {
-  if (logit_dtype == kBF16) return vec ? launch_typed<kBF16, true>(p, s) : launch_typed<kBF16, false>(p, s);
-  return vec ? launch_typed<kF32, true>(p, s) : launch_typed<kF32, false>(p, s);
+  if (p.pr.on) {
+    if (logit_dtype == kBF16) return vec ? launch_typed<kBF16, true, true>(p, s) : launch_typed<kBF16, false, true>(p, s);
+    return vec ? launch_typed<kF32, true, true>(p, s) : launch_typed<kF32, false, true>(p, s);
+  }
+  if (logit_dtype == kBF16) return vec ? launch_typed<kBF16, true, false>(p, s) : launch_typed<kBF16, false, false>(p, s);
+  return vec ? launch_typed<kF32, true, false>(p, s) : launch_typed<kF32, false, false>(p, s);
 }
 
 }  // namespace sv

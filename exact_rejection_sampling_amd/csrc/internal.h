@@ -20,6 +20,7 @@ struct ChainDecision {
   int32_t H;        // remaining output budget (INT32_MAX when none is given)
   float r_ref;      // reference exponent of the terminal row: fp32(max logit * c2)
   float inv_z;      // 1 / Z of the terminal row (Z relative to r_ref, base 2)
+  float tau;        // keep threshold of the terminal row (processors; -inf otherwise)
 };
 
 // Stop tokens and output budget of a round (spec_verify_*_stop); n_stop = 0 and a null
@@ -29,6 +30,17 @@ struct StopSpec {
   const int32_t* budget;     // [B] remaining output budget per request, or null
   int32_t* finish;           // [B] out: SPEC_FINISH_*, or null
   int n_stop;
+};
+
+// Target logit processors (spec_verify_*_ex): s = l + bias (fp32), then tokens outside the
+// allowed set or below the row's keep threshold are removed (-inf).  NaN and +inf stay,
+// so a faulty row still reads as invalid.  With `on` false every row is used as is.
+struct ProcSpec {
+  const float* bias;         // [V] additive bias, or null
+  const uint32_t* allowed;   // [rows, W] allowed-token bitmask (bit x % 32 of word x / 32), or null
+  const float* thresh;       // [rows] keep threshold from the top-k / top-p pass, or null
+  int W;                     // words per mask row = ceil(V / 32)
+  bool on;
 };
 
 struct ChainParams {
@@ -41,6 +53,8 @@ struct ChainParams {
   int32_t* req_status;       // [B]
   float* stats;              // [B, R, 4] or null
   StopSpec st;
+  ProcSpec pr;
+  float* thresh_ws;          // the workspace's threshold words (cleared by the selectors), or null
   // workspace
   float2* part;              // [B*R*SL] block summaries (raw max, Z)
   unsigned long long* gath;  // [B*G*3] draft token, its logit, its draft probability
@@ -56,7 +70,10 @@ struct ChainParams {
   double inv_t;              // 1 / T, T widened exactly from fp32
 };
 
-constexpr int kTermSlabs = 2;                 // slabs per terminal chunk
+#ifndef SPEC_TERM_SLABS
+#define SPEC_TERM_SLABS 2
+#endif
+constexpr int kTermSlabs = SPEC_TERM_SLABS;   // 2048-element slabs per terminal chunk
 constexpr int kTermChunk = kTermSlabs * 2048;  // elements per terminal chunk
 
 // Greedy chunk summary, stored packed in 64 bits (idx << 32 | bits of m).
@@ -72,6 +89,7 @@ struct GreedyParams {
   int32_t* out_tokens;
   int32_t* req_status;
   StopSpec st;
+  ProcSpec pr;               // bias and mask (truncations never move an argmax)
   unsigned long long* part;  // [B*R*SL] packed GreedyPart, one per slice
   int B, G, R, V, P, CPW, SL;
   int LAG;                   // requests between a request's streaming blocks and its decider
@@ -154,7 +172,7 @@ inline unsigned* request_counters(void* ws) {
 // slot s of request b: request_counters(ws)[b * kCounterSlots + s]
 
 struct ChainLayout {
-  size_t part, gath, tmass, total;
+  size_t part, gath, tmass, thresh, total;
 };
 // The chain's statistics pass uses finer slices than the other streaming passes: its
 // terminal items fill the statistics tail, which shrinks as the slices do.
@@ -171,9 +189,23 @@ inline ChainLayout chain_layout(long B, long G, long V) {
   L.part = o;   o = align256(o + sizeof(float2) * B * R * SL);
   L.gath = o;   o = align256(o + sizeof(unsigned long long) * 3 * B * G);
   L.tmass = o;  o = align256(o + sizeof(double) * B * S2);
+  L.thresh = o; o = align256(o + sizeof(float) * B * R);
   L.total = o;
   return L;
 }
+
+// Per-row keep thresholds for top-k / top-p (one block per row): written into `thresh`.
+struct ThreshParams {
+  const void* logits;        // [rows, V]
+  const float* bias;
+  const uint32_t* allowed;   // [rows, W] or null
+  const int32_t* top_k;      // [B] or null (0: off)
+  const float* top_p;        // [B] or null (>= 1: off)
+  float* thresh;             // [rows] out: -inf when nothing is truncated
+  int rows, R, V, W;
+  float c2;                  // fp32(log2(e) / T)
+};
+hipError_t launch_thresholds(const ThreshParams& p, int logit_dtype, bool vec, hipStream_t s);
 
 struct GreedyLayout { size_t part, total; };
 // Greedy slicing: finer than the default, since a streaming block no longer waits on

@@ -3,7 +3,8 @@
  * exact speculative decoding on AMD Instinct MI355X (gfx950).
  *
  * Four verification rules, each one entry point (the chain and greedy rules also have a
- * *_stop variant that applies stop tokens and an output budget inside the round):
+ * *_stop variant that applies stop tokens and an output budget inside the round, and an
+ * *_ex variant that adds target logit processors -- bias, grammar mask, top-k, top-p):
  *   spec_verify_chain          rejection-sampling verification of a draft chain
  *   spec_verify_greedy         argmax-match verification of a draft chain
  *   spec_verify_tree           tree verification by target-sample membership (and
@@ -188,6 +189,47 @@ spec_status spec_verify_chain_stop(const void* target_logits, int logit_dtype,
                                    int32_t* finish, float* stats, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
+/* Options of spec_verify_chain_ex and spec_verify_greedy_ex: stop tokens, an output
+ * budget, and target logit processors.  Every pointer is a device pointer or NULL (that
+ * option off); a zero-initialized struct (or a NULL options pointer) gives the plain call.
+ *
+ * Processors ([M7.1] §0x06J: the verified p_i is the processed row, not the raw softmax;
+ * §0x04G: ordered temperature and additive-bias processors; [Tiny] "Grammar and
+ * deterministic opportunities": a grammar mask renormalizes over the valid tokens):
+ *   s_x = l_x + bias_x in fp32;  p is proportional to exp(s_x / T) over the kept tokens;
+ *   a token is kept when it is allowed, and s_x is at least the k-th largest allowed s
+ *   (top-k, ties kept), and the probability mass (over the tokens left so far) of the tokens
+ *   with strictly larger s is below top_p (top-p: the smallest tie-closed set of top tokens
+ *   whose mass reaches top_p).  NaN or +inf in l + bias anywhere in a reached row makes the
+ *   request SPEC_REQ_NONFINITE, masked or not; so does a reached row with no kept token.
+ *   Top-k and top-p run a threshold pass over every row first (a second launch, about 17
+ *   reads of each row from cache); bias and the mask are applied where the verifier reads
+ *   logits, at no extra pass.  The greedy verifier applies bias and the mask (truncations
+ *   never move the argmax) and ignores top_k and top_p.
+ */
+typedef struct {
+  const int32_t* stop_tokens;   /* [n_stop] stop tokens (as for spec_verify_chain_stop) */
+  int32_t n_stop;               /* 0 .. SPEC_MAX_STOP */
+  const int32_t* budget;        /* [B] remaining output budgets */
+  int32_t* finish;              /* [B] out: SPEC_FINISH_* */
+  const float* bias;            /* [V] additive logit bias, fp32 */
+  const uint32_t* allowed;      /* [B, gamma+1, ceil(V/32)] allowed-token bitmask of each
+                                   row: bit x % 32 of word x / 32 set = token x allowed */
+  const int32_t* top_k;         /* [B] top-k per request; 0 (or negative): off */
+  const float* top_p;           /* [B] top-p per request; outside (0, 1): off */
+} spec_verify_options;
+
+/* Chain verification with options (spec_verify_options); every other argument and the
+ * workspace are those of spec_verify_chain, whose outputs it gives for opt = NULL. */
+spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype,
+                                 const void* draft_probs, int q_dtype,
+                                 const int32_t* draft_tokens, const float* uniforms,
+                                 int B, int gamma, int V, float temperature,
+                                 const spec_verify_options* opt,
+                                 int32_t* accepted_len, int32_t* out_tokens, int32_t* req_status,
+                                 float* stats, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 /* ----------------------------------------------------------------- greedy ---
  * Argmax-match verification ([M7.1] §0x02D: longest-prefix validation is exact for
  * greedy decoding; [Tiny] "Normative greedy pseudocode"):
@@ -215,6 +257,14 @@ spec_status spec_verify_greedy_stop(const void* target_logits, int logit_dtype,
                                     int32_t* accepted_len, int32_t* out_tokens, int32_t* req_status,
                                     int32_t* finish, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/* Greedy verification with options (stop tokens, budget, bias and mask; top_k and top_p
+ * are ignored); the workspace is that of spec_verify_greedy. */
+spec_status spec_verify_greedy_ex(const void* target_logits, int logit_dtype,
+                                  const int32_t* draft_tokens, int B, int gamma, int V,
+                                  const spec_verify_options* opt,
+                                  int32_t* accepted_len, int32_t* out_tokens, int32_t* req_status,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------- tree ---
  * Tree verification by target-sample membership ([M7.7] §0x04B and §0x09: accept a

@@ -35,8 +35,9 @@ import numpy as np
 from .numerics import decode
 
 # A top-p boundary is flagged when a mass that decides it lies within this fraction of the
-# row's total of the target p * Z (fp32 exponentials on the GPU may decide it either way).
-TOP_P_FLAG = 1e-6
+# row's total of the target p * Z: fp32 exponentials with an fp32 log2(e)/T factor put
+# relative errors of up to about (s_max - s) * 1e-7 on a weight, which may decide it either way.
+TOP_P_FLAG = 1e-5
 
 
 def unpack_mask(words: np.ndarray, V: int) -> np.ndarray:
@@ -71,8 +72,9 @@ def process_row(l_row: np.ndarray, temperature: float, bias=None, allowed=None, 
         w = np.exp((vals - vals.max()) / T)
         Z = float(w.sum())
         target = top_p * Z
-        uniq = np.unique(vals)[::-1]                       # distinct values, largest first
-        mass_at = np.array([w[vals == v].sum() for v in uniq])
+        uniq, inv = np.unique(vals, return_inverse=True)   # distinct values, ascending
+        mass_at = np.bincount(inv, weights=w)[::-1]        # their masses, largest value first
+        uniq = uniq[::-1]
         incl = np.cumsum(mass_at)                          # mass of tokens with s >= v
         excl = incl - mass_at                              # mass of tokens with s >  v
         j = int(np.flatnonzero(excl < target).max())       # smallest value still needed

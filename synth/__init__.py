@@ -330,6 +330,27 @@ def make_stop(tokens: np.ndarray, V: int, *, seed: int, n_stop: int = 4, from_dr
     return np.asarray(picks[:n_stop], dtype=np.int32), budget
 
 
+def make_processors(B: int, R: int, V: int, *, seed: int, bias_sigma: float = 1.0, allowed_frac: float = 0.9,
+                    top_k=(0, 1, 20, 1000), top_p=(1.0, 0.5, 0.9, 0.99), with_bias=True, with_mask=True,
+                    with_top_k=True, with_top_p=True):
+    """Target logit processor inputs: an fp32 bias row [V] ~ N(0, bias_sigma^2); an allowed-token
+    bitmask per row [B, R, ceil(V/32)] (uint32 words; each token allowed with probability
+    allowed_frac, independently per row); per-request top-k and top-p drawn from the given
+    choices.  Disabled parts are None."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    bias = rng.normal(0.0, bias_sigma, V).astype(np.float32) if with_bias else None
+    words = None
+    if with_mask:
+        W = (V + 31) // 32
+        allowed = rng.random((B, R, W * 32)) < allowed_frac
+        allowed[..., V:] = False
+        weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))
+        words = (allowed.reshape(B, R, W, 32).astype(np.uint64) * weights).sum(-1).astype(np.uint32)
+    k = rng.choice(np.asarray(top_k, np.int32), B).astype(np.int32) if with_top_k else None
+    p = rng.choice(np.asarray(top_p, np.float32), B).astype(np.float32) if with_top_p else None
+    return bias, words, k, p
+
+
 CONFIGS = {
     # chain, correctness scale: fp32 logits ~ N(0, 2^2), drafter noise 0.5, T = 1
     1: dict(kind="chain", B=4, gamma=4, V=32, logit_dtype="f32", sigma=2.0, boost_frac=0.0,

@@ -174,3 +174,16 @@ def test_tree_greedy_host_validation():
     assert t(N=0) == EINVAL and t(N=4097) == EINVAL and t(V=0) == EINVAL
     assert t(dt=2) == EDTYPE and t(par=NULL) == EINVAL and t(l=NULL) == EINVAL
     assert t(B=0, l=NULL) == OK and t() == EWORKSPACE
+
+
+def test_options_entry_points_host_validation():
+    lib = sv.load_library()
+    from exact_rejection_sampling_amd._binding import SpecOptions
+    bad = SpecOptions()
+    bad.n_stop = 300
+    c = lambda opt, **k: lib.spec_verify_chain_ex(FAKE, 0, FAKE, 0, FAKE, FAKE, k.get("B", 2), 2, 16,
+                                                  ctypes.c_float(1.0), opt, FAKE, FAKE, FAKE, NULL, NULL, 0, NULL)
+    assert c(None) == EWORKSPACE and c(ctypes.byref(SpecOptions())) == EWORKSPACE
+    assert c(ctypes.byref(bad)) == EINVAL and c(None, B=0) == OK
+    g = lambda opt: lib.spec_verify_greedy_ex(FAKE, 1, FAKE, 2, 2, 16, opt, FAKE, FAKE, FAKE, NULL, 0, NULL)
+    assert g(None) == EWORKSPACE and g(ctypes.byref(bad)) == EINVAL

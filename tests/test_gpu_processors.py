@@ -1,0 +1,150 @@
+"""GPU parity of the target logit processors (spec_verify_chain_ex, spec_verify_greedy_ex)
+against the oracle: the oracle processes every row (bias, mask, top-k, top-p) and runs the
+unchanged verifier on the processed rows.  Statuses exact; tokens, lengths and finish codes
+exact outside flagged requests (accept/CDF windows, and top-p boundaries within 1e-5 of
+the target mass); statistics within the tolerances of tests/gpu_util.py.
+
+[M7.1] §0x06J (p is the processed row), §0x04G (temperature and additive bias); [Tiny]
+"Grammar and deterministic opportunities" (q_G) and "Exactness tests" item 6.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import exact_rejection_sampling_amd as sv
+from gpu_util import DEV, say, compare_chain, compare_exact, t_logits, t_f32, t_i32, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def t_words(w):
+    return None if w is None else torch.from_numpy(np.ascontiguousarray(w).view(np.int32)).to(DEV)
+
+
+def run_chain_proc(x, bias, words, top_k, top_p, stop=None, budget=None, workspace_tensor=None):
+    out = sv.spec_verify_chain(t_logits(x.logits, x.logit_dtype), t_f32(x.q), t_i32(x.tokens), t_f32(x.u),
+                               float(x.temperature), with_stats=True,
+                               bias=None if bias is None else t_f32(bias), allowed=t_words(words),
+                               top_k=None if top_k is None else t_i32(top_k),
+                               top_p=None if top_p is None else t_f32(top_p),
+                               stop_tokens=None if stop is None else t_i32(stop),
+                               budget=None if budget is None else t_i32(budget), workspace_tensor=workspace_tensor)
+    return to_np(out)
+
+
+def oracle_chain_proc(x, bias, words, top_k, top_p, stop=(), budget=None):
+    L, pflag = oracle.process_rows(x.logits, x.logit_dtype, x.temperature, bias, words, top_k, top_p)
+    exp = oracle.verify_chain(L, x.q, x.tokens, x.u, x.temperature, "f64", stop_tokens=list(stop), budget=budget)
+    exp["flagged"] = exp["flagged"] | pflag
+    return exp
+
+
+def check(x, bias, words, top_k, top_p, stop=None, budget=None):
+    got = run_chain_proc(x, bias, words, top_k, top_p, stop, budget)
+    exp = oracle_chain_proc(x, bias, words, top_k, top_p, () if stop is None else stop.tolist(), budget)
+    s = compare_chain(got, exp)
+    # the comparison must cover most requests: flags are for rare near-ties only
+    assert (~exp["flagged"]).sum() >= (len(exp["flagged"]) + 1) // 2, exp["flagged"].sum()
+    if stop is not None or budget is not None:
+        keep = ~exp["flagged"]
+        np.testing.assert_array_equal(got["finish"][keep], exp["finish"][keep])
+    return got, exp, s
+
+
+def test_headline_shape_all_processors():
+    """B=64, gamma=5, V=128256 bf16, T=0.8; fp32 bias, 90%-allowed masks per row, top-k in
+    {0, 1, 20, 1000}, top-p in {1, 0.5, 0.9, 0.99} per request."""
+    x = synth.make_config(3, 0)
+    bias, words, k, p = synth.make_processors(x.B, x.gamma + 1, x.V, seed=11)
+    say("chain_ex config3 bias+mask+top-k+top-p")
+    got, exp, s = check(x, bias, words, k, p)
+    print(s, "accepted", np.bincount(got["accepted_len"][got["req_status"] == 0], minlength=6).tolist())
+
+
+@pytest.mark.parametrize("which", ["bias", "mask", "top_k", "top_p"])
+def test_each_processor_alone(which):
+    x = synth.make_chain(24, 4, 20003, seed=300, logit_dtype="bf16", sigma=2.0, noise=0.5, temperature=0.9)
+    bias, words, k, p = synth.make_processors(x.B, x.gamma + 1, x.V, seed=12, top_k=(1, 5, 300, 19000),
+                                              top_p=(0.3, 0.8, 0.95, 0.999), with_bias=which == "bias",
+                                              with_mask=which == "mask", with_top_k=which == "top_k",
+                                              with_top_p=which == "top_p")
+    say(f"chain_ex {which} alone V=20003")
+    print(check(x, bias, words, k, p)[2])
+
+
+@pytest.mark.parametrize("V,dt,gamma", [(1, "f32", 2), (7, "bf16", 3), (33, "f32", 4), (2049, "bf16", 5),
+                                        (8193, "f32", 8), (65536, "bf16", 3)])
+def test_ragged_with_every_processor(V, dt, gamma):
+    x = synth.make_chain(12, gamma, V, seed=310 + V, logit_dtype=dt, sigma=2.0, noise=0.5, temperature=1.1)
+    bias, words, k, p = synth.make_processors(x.B, gamma + 1, V, seed=13 + V, allowed_frac=0.7,
+                                              top_k=(0, 1, 3, 100), top_p=(1.0, 0.2, 0.7, 0.97))
+    say(f"chain_ex ragged V={V} {dt} gamma={gamma}")
+    check(x, bias, words, k, p)
+
+
+def test_top_k_one_and_ties():
+    """top-k = 1 keeps only the maximum (all of its ties): with coarse logits the maximum is
+    often shared, and the draw is among the tied tokens."""
+    B, G, V = 16, 3, 5000
+    rng = np.random.default_rng(14)
+    vals = np.round(rng.normal(0, 1, (B, G + 1, V)) * 2) / 2
+    x = synth.make_chain(B, G, V, seed=15, logit_dtype="f32", noise=0.5)
+    x.logits = vals.astype(np.float32)
+    say("chain_ex top-k 1 with ties")
+    check(x, None, None, np.ones(B, np.int32), None)
+
+
+def test_statuses_with_processors():
+    B, G, V = 8, 3, 3000
+    x = synth.make_chain(B, G, V, seed=16, logit_dtype="f32", sigma=2.0, noise=0.3)
+    bias, words, _, _ = synth.make_processors(B, G + 1, V, seed=17, with_top_k=False, with_top_p=False)
+    words = words.copy()
+    words[0, 0, :] = 0                                    # 0: row 0 entirely masked -> no valid token
+    x.logits[1, 0, 5] = np.nan                            # 1: NaN in row 0 ...
+    words[1, 0, 0] &= ~np.uint32(1 << 5)                  # ... at a masked position: still invalid
+    words[2, 0, x.tokens[2, 0] // 32] &= ~np.uint32(1 << (x.tokens[2, 0] % 32))   # 2: draft 0 masked: rejected
+    bias = bias.copy()
+    bias[x.tokens[3, 0]] = -np.inf                        # 3: draft 0 banned by the bias
+    say("chain_ex statuses")
+    got, exp, _ = check(x, bias, words, None, None)
+    assert exp["status"].tolist()[:2] == [oracle.NONFINITE, oracle.NONFINITE]
+    assert exp["accepted_len"][2] == 0 and exp["accepted_len"][3] == 0
+
+
+def test_processors_with_stops_and_workspace_reuse():
+    x = synth.make_config(2, 3)
+    bias, words, k, p = synth.make_processors(x.B, x.gamma + 1, x.V, seed=18)
+    stop, budget = synth.make_stop(x.tokens, x.V, seed=19, n_stop=32, from_drafts=32)
+    ws = torch.zeros(sv.chain_workspace_bytes(x.B, x.gamma, x.V) + 512, dtype=torch.uint8, device=DEV)
+    say("chain_ex processors + stops, workspace reuse")
+    a = run_chain_proc(x, bias, words, k, p, stop, budget, workspace_tensor=ws)
+    b = run_chain_proc(x, bias, words, k, p, stop, budget, workspace_tensor=ws)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    check(x, bias, words, k, p, stop, budget)
+
+
+def test_no_processor_options_match_the_plain_call():
+    x = synth.make_config(2, 4)
+    say("chain_ex with disabled processors vs spec_verify_chain")
+    got = run_chain_proc(x, None, None, np.zeros(x.B, np.int32), np.ones(x.B, np.float32))
+    plain = to_np(sv.spec_verify_chain(t_logits(x.logits, x.logit_dtype), t_f32(x.q), t_i32(x.tokens),
+                                       t_f32(x.u), float(x.temperature), with_stats=True))
+    for key in ("accepted_len", "out_tokens", "req_status"):
+        np.testing.assert_array_equal(got[key], plain[key], err_msg=key)
+
+
+def test_greedy_with_bias_and_mask():
+    x = synth.make_config(4, 1, B=64)
+    bias, words, _, _ = synth.make_processors(x.B, x.gamma + 1, x.V, seed=20, bias_sigma=0.5,
+                                              with_top_k=False, with_top_p=False)
+    say("greedy_ex bias+mask B=64 gamma=8 V=128256")
+    got = to_np(sv.spec_verify_greedy(t_logits(x.logits, x.logit_dtype), t_i32(x.tokens), bias=t_f32(bias),
+                                      allowed=t_words(words)))
+    L, _ = oracle.process_rows(x.logits, x.logit_dtype, 1.0, bias, words)
+    exp = oracle.verify_greedy(L, x.tokens, "f64")
+    compare_exact(got, exp, ["accepted_len", "out_tokens"])
