@@ -14,7 +14,8 @@ roofline of the verification kernel (one launch per call) from HIP events record
 the stream it runs on, the oracle's CPU throughput on a bounded sample (measured first,
 before the GPU is touched), and secondary measurements: the greedy chain (B=256,
 gamma=8, V=128256), membership tree and greedy tree (B=32, N=63, V=152064), residual-update
-tree (B=32, N=31, V=32000) workloads, and the headline chain with stop tokens and budgets.
+tree (B=32, N=31, V=32000) workloads, and the headline chain with stop tokens and budgets and
+with target logit processors.
 """
 from __future__ import annotations
 
@@ -234,6 +235,36 @@ def bench_chain_stop(args, torch, sv, synth):
                 finish_counts=dict(open=int(fin[0]), stop=int(fin[1]), budget=int(fin[2])))
 
 
+def bench_chain_proc(args, torch, sv, synth, truncate):
+    """The headline chain workload through spec_verify_chain_ex with target logit processors:
+    fp32 bias and 90%-allowed masks per row, plus (truncate) top-k in {0, 1, 20, 1000} and
+    top-p in {1, 0.5, 0.9, 0.99} per request, which add the threshold pre-pass."""
+    x = synth.make_config(3, 0)
+    bias, words, k, p = synth.make_processors(x.B, x.gamma + 1, x.V, seed=11, with_top_k=truncate,
+                                              with_top_p=truncate)
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    qt = torch.from_numpy(x.q).to(dev)
+    tt, ut = torch.from_numpy(x.tokens).to(dev), torch.from_numpy(x.u).to(dev)
+    bt = torch.from_numpy(bias).to(dev)
+    wt = torch.from_numpy(words.view(np.int32)).to(dev)
+    kt = None if k is None else torch.from_numpy(k).to(dev)
+    pt = None if p is None else torch.from_numpy(p).to(dev)
+    sets = device_copies(lambda: (lt.clone(), qt.clone()), lt.numel() * 2 + qt.numel() * 4)
+    del lt, qt
+    stream = torch.cuda.current_stream()
+    ws = torch.zeros(sv.chain_workspace_bytes(x.B, x.gamma, x.V) + 512, dtype=torch.uint8, device=dev)
+    calls = [sv.prepare_chain(s[0], s[1], tt, ut, float(x.temperature), workspace_tensor=ws, bias=bt, allowed=wt,
+                              top_k=kt, top_p=pt) for s in sets]
+    span, per = time_calls(calls, max(100, args.steps // 2), args.warmup, stream)
+    launch = span / len(per)
+    del sets, calls
+    what = "bias, masks, top-k, top-p (threshold pass + verification)" if truncate else "bias and masks"
+    return dict(workload=f"chain B=64 gamma=5 V=128256 bf16 with {what}",
+                positions_per_s=x.B * (x.gamma + 1) * len(per) / span, us_per_call=launch * 1e6,
+                evented_call_mean_us=float(per.mean()) * 1e3)
+
+
 _CPU_X = None   # the workload a forked oracle worker reads
 
 
@@ -351,6 +382,12 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] chain with stop tokens and budgets")
         line["secondary"]["chain_stop"] = bench_chain_stop(args, torch, sv, synth)
+        torch.cuda.empty_cache()
+        log("[bench] chain with bias and masks")
+        line["secondary"]["chain_bias_mask"] = bench_chain_proc(args, torch, sv, synth, False)
+        torch.cuda.empty_cache()
+        log("[bench] chain with every processor")
+        line["secondary"]["chain_processors"] = bench_chain_proc(args, torch, sv, synth, True)
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

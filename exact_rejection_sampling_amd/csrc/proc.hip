@@ -7,11 +7,12 @@
 //  * top-p (0 < p < 1): among the candidates with key >= tau_k, with weights
 //    w = 2^((s - max) * c2), tau_p = the largest key t whose mass {key >= t} reaches
 //    p * (total mass): the smallest tie-closed set of top tokens whose probability reaches p.
-// Both are found by 16-way bisection over the key range: a pass streams the row once and
-// accumulates, per thread and in registers, the count (or fp64 mass) of candidates at or
-// above each of 16 boundaries; one block reduction, in a fixed order, picks the
-// sub-interval.  Eight passes resolve a 32-bit key; there are no atomics and the result is
-// the same on every run.  The row's threshold is the larger of the two, or -inf.
+// Both are found by radix selection over the bits in which the row's candidate keys differ,
+// 12 bits per pass: a pass streams the row once and adds each candidate whose higher bits
+// match the prefix found so far into one of 4096 LDS bins -- a count (top-k) or a mass in
+// fixed point, 2^-32 of the largest weight, rounded to nearest (top-p).  Integer sums do not
+// depend on the order of the additions, so the result is the same on every run.  The row's
+// threshold is the larger of the two, or -inf.
 //
 // Method: [M7.1] "M7.1 - Speculative Decoding: Draft, Verify, Accept, Reject" §0x06J (the
 // verified p is the row after top-k and top-p); [Tiny] "Exact Speculative and Assisted
@@ -24,8 +25,6 @@
 namespace sv {
 
 namespace {
-
-constexpr int kWays = 16;
 
 __device__ __forceinline__ unsigned key_of(float s) {
   if (s == 0.0f) s = 0.0f;                       // -0 and +0 are one value
@@ -53,80 +52,111 @@ __device__ __forceinline__ unsigned cand8(const ThreshParams& p, const void* lro
   return ok;
 }
 
-// Block-wide fp64 sums of 16 per-thread accumulators (fixed order: DPP tree per wave, waves
-// in index order).  Every thread receives the totals.
-__device__ void block_sums16(double (&acc)[kWays], double* scratch /* [kWavesPerBlock * kWays] */) {
+// 1024 threads (16 waves) per row: enough waves per SIMD to hide the per-element chain.
+constexpr int kTB = 1024;
+constexpr int kTW = kTB / kWave;
+constexpr int kDigit = 12;
+constexpr int kBins = 1 << kDigit;
+constexpr int kBinsPerThread = kBins / kTB;
+
+struct RadixLds {
+  unsigned long long bin[kBins];        // counts, or masses in fixed point
+  double scan[kTW];
+  int digit;
+  double f_above;
+};
+
+// Block-wide exclusive prefix (fp64) over the kTB threads; *total gets the block sum.
+__device__ double tb_excl_scan(double v, double* scratch, double* total) {
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const double incl = wave_incl_scan_d(v, lane);
+  const double excl = wave_shr1_d(incl);
+  if (lane == kWave - 1) scratch[wave] = incl;
+  __syncthreads();
+  double off = 0.0, tot = 0.0;
 #pragma unroll
-  for (int j = 0; j < kWays; ++j) {
-    const double t = wave_sum_d(acc[j]);
-    if (lane == 0) scratch[wave * kWays + j] = t;
+  for (int w = 0; w < kTW; ++w) {
+    if (w < wave) off += scratch[w];
+    tot += scratch[w];
   }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kWays; ++j) {
-    double t = 0.0;
-#pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) t += scratch[w * kWays + j];
-    acc[j] = t;
-  }
-  __syncthreads();
+  *total = tot;
+  return off + excl;
 }
 
-// 16-way bisection for the largest key t in [lo, hi] with F(t) >= target, where F(t) is
-// the count (MASS false) or the mass (MASS true) of candidates with key >= t, and
-// F(lo) >= target.  The target is target_of(F(lo)), F(lo) coming from the first pass.
-template <int DT, bool VEC, bool MASS, class TargetOf>
-__device__ unsigned bisect(const ThreshParams& p, const void* lrow, size_t row, unsigned lo, unsigned hi, float M,
-                           TargetOf target_of, double* scratch) {
-  double target = 0.0;
-  bool first = true;
-  while (lo < hi) {
-    const unsigned long long width = ((unsigned long long)(hi - lo) + kWays) / kWays;   // ceil((hi-lo+1)/16)
-    unsigned bnd[kWays];
-#pragma unroll
-    for (int j = 0; j < kWays; ++j) {
-      const unsigned long long b = (unsigned long long)lo + (unsigned long long)j * width;
-      bnd[j] = b > hi ? 0xffffffffu : static_cast<unsigned>(b);   // past hi: never reached below
-    }
-    double acc[kWays];
-#pragma unroll
-    for (int j = 0; j < kWays; ++j) acc[j] = 0.0;
-    for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kBlock * kVec) {
+// Radix selection of the largest key t >= klo with F(t) >= target, where F(t) is the count
+// (MASS false) or the fixed-point mass (MASS true; weights scaled by `fix`) of the
+// candidates with key >= t; keys below klo are ignored.  [klo, khi] bounds the keys; the
+// bits above their highest differing bit are shared.  `param` is the count target k, or the
+// fraction p of the total mass F(klo) that the target is.  Every value stays an integer
+// below 2^53, so the fp64 scans are exact.
+template <int DT, bool VEC, bool MASS>
+__device__ unsigned radix_select(const ThreshParams& p, const void* lrow, size_t row, unsigned klo, unsigned khi,
+                                 double param, float M, double fix, RadixLds& L) {
+  const int tid = threadIdx.x;
+  const int nb = (klo == khi) ? 0 : 32 - __clz(klo ^ khi);   // the varying low bits
+  unsigned prefix = nb == 32 ? 0u : (klo >> nb);             // the digits chosen so far
+  double above = 0.0;                                        // F just above the prefix's range
+  double target = MASS ? -1.0 : param;
+  for (int done = 0; done < nb;) {
+    const int width = min(kDigit, nb - done), shift = nb - done - width;
+    for (int j = tid; j < kBins; j += kTB) L.bin[j] = 0ull;
+    __syncthreads();
+    for (long e0 = (long)tid * kVec; e0 < p.V; e0 += (long)kTB * kVec) {
       float s[8];
       const unsigned ok = cand8<DT, VEC>(p, lrow, row, e0, s);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (!((ok >> e) & 1u)) continue;
         const unsigned k = key_of(s[e]);
-        if (k < lo) continue;
-        const double w = MASS ? (double)__builtin_amdgcn_exp2f((s[e] - M) * p.c2) : 1.0;
-#pragma unroll
-        for (int j = 0; j < kWays; ++j)
-          if (k >= bnd[j] && (j == 0 || (unsigned long long)lo + (unsigned long long)j * width <= hi)) acc[j] += w;
+        if (k < klo) continue;
+        const unsigned high = shift + width == 32 ? 0u : (k >> (shift + width));
+        if (high != prefix) continue;
+        unsigned long long v = 1ull;
+        if constexpr (MASS) v = __double2ull_rn((double)__builtin_amdgcn_exp2f((s[e] - M) * p.c2) * fix);
+        atomicAdd(&L.bin[(k >> shift) & ((1u << width) - 1u)], v);
       }
     }
-    block_sums16(acc, scratch);
-    if (first) {
-      target = target_of(acc[0]);
-      first = false;
-    }
-    int jbest = 0;
+    __syncthreads();
+    // thread t owns kBinsPerThread consecutive digits, highest digits to thread 0
+    const int d_hi = (1 << width) - 1 - tid * kBinsPerThread;
+    double run = 0.0;
 #pragma unroll
-    for (int j = 1; j < kWays; ++j)
-      if ((unsigned long long)lo + (unsigned long long)j * width <= hi && acc[j] >= target) jbest = j;
-    const unsigned long long nlo = (unsigned long long)lo + (unsigned long long)jbest * width;
-    const unsigned long long nhi = nlo + width - 1;
-    lo = static_cast<unsigned>(nlo);
-    hi = nhi < hi ? static_cast<unsigned>(nhi) : hi;
+    for (int i = 0; i < kBinsPerThread; ++i)
+      if (d_hi - i >= 0) run += (double)L.bin[d_hi - i];
+    double tot;
+    const double before = tb_excl_scan(run, L.scan, &tot);   // F of the digits above this run
+    if (target < 0.0) target = param * (above + tot);             // MASS: p * total mass
+    if (tid == 0) L.digit = -1;
+    __syncthreads();
+    // the largest digit whose F reaches the target: the first hit going down; only one
+    // thread's run holds it (F rises as the digit falls)
+    double f = above + before;
+    for (int i = 0; i < kBinsPerThread; ++i) {
+      const int d = d_hi - i;
+      if (d < 0) break;
+      const double b = (double)L.bin[d];
+      if (f < target && f + b >= target) {
+        L.digit = d;
+        L.f_above = f;
+      }
+      f += b;
+    }
+    __syncthreads();
+    const int d = L.digit;
+    above = L.f_above;
+    __syncthreads();
+    prefix = (prefix << width) | static_cast<unsigned>(d < 0 ? 0 : d);
+    done += width;
   }
-  return lo;
+  return nb == 0 ? klo : prefix;
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void thresh_kernel(ThreshParams p) {
-  __shared__ double s_scratch[kWavesPerBlock * kWays];
-  __shared__ float s_m[kWavesPerBlock], s_mn[kWavesPerBlock];
+__global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
+  __shared__ double s_scratch[kTW];
+  __shared__ RadixLds s_radix;
+  __shared__ float s_m[kTW], s_mn[kTW];
   __shared__ int s_fault;
   const size_t row = blockIdx.x;
   const int b = static_cast<int>(row / p.R);
@@ -146,7 +176,7 @@ __global__ __launch_bounds__(kBlock) void thresh_kernel(ThreshParams p) {
   float m = -INFINITY, mn = INFINITY;
   double cnt = 0.0;
   bool fault = false;
-  for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kBlock * kVec) {
+  for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kTB * kVec) {
     float s[8];
     const unsigned ok = cand8<DT, VEC>(p, lrow, row, e0, s);
 #pragma unroll
@@ -172,7 +202,7 @@ __global__ __launch_bounds__(kBlock) void thresh_kernel(ThreshParams p) {
   float M = -INFINITY, MN = INFINITY;
   double C = 0.0;
 #pragma unroll
-  for (int w = 0; w < kWavesPerBlock; ++w) {
+  for (int w = 0; w < kTW; ++w) {
     M = fmaxf(M, s_m[w]);
     MN = fminf(MN, s_mn[w]);
     C += s_scratch[w];
@@ -180,15 +210,16 @@ __global__ __launch_bounds__(kBlock) void thresh_kernel(ThreshParams p) {
   __syncthreads();
   float tau = -INFINITY;
   if (!s_fault && C > 0.0) {
-    unsigned lo = key_of(MN), hi = key_of(M);
+    unsigned lo = key_of(MN);
+    const unsigned hi = key_of(M);
     if (use_k && (double)k < C) {
-      const double kk = (double)k;
-      lo = bisect<DT, VEC, false>(p, lrow, row, lo, hi, M, [kk](double) { return kk; }, s_scratch);
+      lo = radix_select<DT, VEC, false>(p, lrow, row, lo, hi, (double)k, M, 1.0, s_radix);
       tau = value_of(lo);
     }
     if (use_p) {
-      const double pp = (double)tp;
-      const unsigned t = bisect<DT, VEC, true>(p, lrow, row, lo, hi, M, [pp](double z) { return pp * z; }, s_scratch);
+      // the largest scale that keeps every sum of fixed-point weights (each <= 1) below 2^53
+      const double fix = ldexp(1.0, 52 - (64 - __clzll(static_cast<unsigned long long>(C))));
+      const unsigned t = radix_select<DT, VEC, true>(p, lrow, row, lo, hi, (double)tp, M, fix, s_radix);
       tau = value_of(t);
     }
   }
@@ -197,7 +228,7 @@ __global__ __launch_bounds__(kBlock) void thresh_kernel(ThreshParams p) {
 
 template <int DT, bool VEC>
 hipError_t launch_typed(const ThreshParams& p, hipStream_t s) {
-  thresh_kernel<DT, VEC><<<dim3((unsigned)p.rows), dim3(kBlock), 0, s>>>(p);
+  thresh_kernel<DT, VEC><<<dim3((unsigned)p.rows), dim3(kTB), 0, s>>>(p);
   return hipGetLastError();
 }
 
