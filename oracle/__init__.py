@@ -25,7 +25,7 @@ from .greedy import verify_greedy, verify_greedy_one, verify_greedy_stop_one
 from .tree import verify_tree, verify_tree_one, validate_tree, tree_expected_nodes
 from .tree_residual import verify_tree_residual, verify_tree_residual_one
 from .tree_greedy import verify_tree_greedy, verify_tree_greedy_one
-from .processors import process_row, process_rows, unpack_mask
+from .processors import process_row, process_rows, unpack_mask, densify_sparse_q
 from . import laws
 
 __all__ = [
@@ -36,6 +36,6 @@ __all__ = [
     "verify_tree", "verify_tree_one", "validate_tree", "tree_expected_nodes",
     "verify_tree_residual", "verify_tree_residual_one",
     "verify_tree_greedy", "verify_tree_greedy_one",
-    "process_row", "process_rows", "unpack_mask",
+    "process_row", "process_rows", "unpack_mask", "densify_sparse_q",
     "laws",
 ]

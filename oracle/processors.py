@@ -103,3 +103,22 @@ def process_rows(logits, logit_dtype, temperature, bias=None, mask_words=None, t
             out[b, i], f = process_row(L[i], temperature, bias, None if allowed is None else allowed[b, i], k, p)
             flagged[b] |= f
     return out, flagged
+
+
+def densify_sparse_q(index: np.ndarray, values: np.ndarray, V: int) -> np.ndarray:
+    """Sparse draft rows -> dense rows.  [Tiny] "Logit and residual scratch": a sparse top-k
+    representation is exact only when the omitted proposal probabilities are known to be
+    zero, so every token not listed gets q = 0; entries that share an index add up.
+    index, values: [..., K] (int indices in [0, V), fp32 values)."""
+    index = np.asarray(index)
+    if ((index < 0) | (index >= V)).any():
+        raise ValueError("sparse q index outside [0, V)")
+    vals = np.asarray(values, dtype=np.float32).astype(np.float64)
+    lead = index.shape[:-1]
+    out = np.zeros(lead + (V,))
+    flat_out = out.reshape(-1, V)
+    flat_idx = index.reshape(-1, index.shape[-1])
+    flat_val = vals.reshape(-1, vals.shape[-1])
+    for r in range(flat_out.shape[0]):
+        np.add.at(flat_out[r], flat_idx[r], flat_val[r])
+    return out

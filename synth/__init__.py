@@ -277,13 +277,31 @@ class TreeResidualInputs:
     meta: dict = field(default_factory=dict)
 
 
+def without_replacement_row(q0: np.ndarray, drawn) -> np.ndarray:
+    """The proposal after removing the tokens already drawn at a parent: q0 with those
+    tokens zeroed and renormalized, or, when no draft mass is left, the uniform distribution
+    over the tokens not yet drawn ([M7.7] §0x0AB, Sequoia's proposal process)."""
+    r = np.asarray(q0, dtype=np.float64).copy()
+    r[list(drawn)] = 0.0
+    tot = r.sum()
+    if tot > 0.0:
+        return r / tot
+    u = np.ones_like(r)
+    u[list(drawn)] = 0.0
+    return u / u.sum()
+
+
 def make_tree_residual(B: int, N: int, V: int, *, seed: int, logit_dtype: str = "bf16", sigma: float = 3.0,
                        noise: float = 1.0, temperature: float = 1.0, max_depth: int = 3,
-                       max_children: int = 4, per_child: bool = False) -> TreeResidualInputs:
+                       max_children: int = 4, per_child: bool = False,
+                       without_replacement: bool = False) -> TreeResidualInputs:
     """Random candidate trees whose children are proposals of a stand-in drafter: the
     drafter's distribution at node v is softmax(row_v + N(0, noise^2)) (stored fp32), and
     v's children are drawn from it i.i.d. (with replacement, so siblings may repeat a
-    token); with per_child every child has a noise draw, a row and a token of its own."""
+    token); with per_child every child has a noise draw, a row and a token of its own; with
+    without_replacement the children of v are drawn one after another, each from the
+    drafter's row with the earlier siblings' tokens removed (without_replacement_row), and
+    that row, stored fp32, is the child's proposal row."""
     ss = np.random.SeedSequence(seed)
     s_logit, s_tree, s_noise, s_pick, s_u = (np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(5))
     lg = _normal_f32(s_logit, (B, N, V), sigma)
@@ -298,6 +316,13 @@ def make_tree_residual(B: int, N: int, V: int, *, seed: int, logit_dtype: str = 
             rows = 1 if not per_child else kids.size
             z = lg[b, v].astype(np.float64)[None] + s_noise.standard_normal((rows, V)) * noise
             qr = _drafter_softmax(z).astype(np.float32)
+            if without_replacement:
+                drawn = []
+                for c in kids:
+                    q[b, c] = without_replacement_row(qr[0], drawn).astype(np.float32)
+                    node_tokens[b, c] = _draw_from_rows(s_pick, q[b, c][None])[0]
+                    drawn.append(int(node_tokens[b, c]))
+                continue
             q[b, kids] = qr if per_child else qr[0]
             node_tokens[b, kids] = _draw_from_rows(s_pick, q[b, kids])
     stored = f32_to_bf16_bits(lg) if logit_dtype == "bf16" else lg

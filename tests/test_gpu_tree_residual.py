@@ -164,3 +164,19 @@ def test_pages_example_law_million_requests():
     chi2, pval = sst.chisquare(counts, p * B)
     print("counts", counts.tolist(), "p-value", pval)
     assert pval > 1e-3
+
+
+@pytest.mark.parametrize("V,noise", [(32000, 1.0), (3000, 0.1), (50, 0.5)])
+def test_without_replacement_siblings(V, noise):
+    """[M7.7] §0x0AB (Sequoia): each child drawn from the drafter's row with the earlier
+    siblings' tokens removed (uniform over the unsampled tokens once the draft mass is used
+    up) and verified against that row; siblings never repeat a token."""
+    x = synth.make_tree_residual(32, 31, V, seed=130 + V, sigma=2.0, noise=noise, max_depth=3, max_children=4,
+                                 without_replacement=True)
+    for b in range(x.B):
+        for v in range(x.N):
+            kids = np.nonzero(x.parents[b] == v)[0]
+            assert len(set(x.node_tokens[b, kids].tolist())) == len(kids)
+    say(f"tree_residual without replacement V={V} noise={noise}")
+    got, exp = check(x)
+    print("accepted", np.bincount(got["accepted_len"][got["req_status"] == 0]).tolist())

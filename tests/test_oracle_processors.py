@@ -186,3 +186,79 @@ def test_process_rows_batches_like_rows():
             ref, _ = process_row(L[b, i].astype(np.float64), 0.7, bias, allowed[b, i],
                                  [3, 0, 50][b], [0.9, 0.5, 1.0][b])
             assert np.array_equal(out[b, i], ref)
+
+
+def test_sparse_q_rows_are_zero_outside_the_support():
+    from oracle.processors import densify_sparse_q
+    idx = np.array([[3, 0, 7], [1, 1, 2]])
+    val = np.array([[0.5, 0.25, 0.25], [0.25, 0.25, 0.5]], np.float32)
+    q = densify_sparse_q(idx, val, 8)
+    assert q[0].tolist() == [0.25, 0, 0, 0.5, 0, 0, 0, 0.25]
+    assert q[1].tolist() == [0, 0.5, 0.5, 0, 0, 0, 0, 0]          # a repeated index adds up
+    with pytest.raises(ValueError):
+        densify_sparse_q(np.array([[8]]), np.array([[1.0]]), 8)
+
+
+@pytest.mark.parametrize("K", [1, 2])
+def test_top_k_drafter_with_sparse_q_is_exact_and_hidden_mass_is_not(K):
+    """[Tiny] "Logit and residual scratch": with a top-K drafter (mass outside the K listed
+    tokens truly zero) the verifier on the sparse rows emits the target law; if the drafter
+    proposes from its full distribution but only K entries reach the verifier (omitted
+    probabilities not zero), the law is wrong."""
+    rng = np.random.default_rng(30 + K)
+    V, G, T = 3, 2, 1.0
+    p_of = lambda pre, t={}: t.setdefault(pre, rng.dirichlet(np.ones(V)))
+    full = {}
+
+    def q_full(pre):
+        if pre not in full:
+            full[pre] = rng.dirichlet(np.ones(V))
+        return full[pre]
+
+    def topk(row):
+        keep = np.argsort(-row, kind="stable")[:K]
+        out = np.zeros(V)
+        out[keep] = row[keep]
+        return out / out.sum()
+    joint, _ = chain_joint(p_of, lambda pre: topk(q_full(pre)), V, G, T)
+    assert max_joint_gap(joint, target_joint(p_of, V, G + 1)) < 1e-12
+    # drafts from the full q, verified against the truncated (renormalized) rows
+    from lawcheck import _midpoints  # noqa: F401  (same enumeration, mismatched rows)
+    joint_bad = mismatched_chain_joint(p_of, q_full, lambda pre: topk(q_full(pre)), V, G, T)
+    assert max_joint_gap(joint_bad, target_joint(p_of, V, G + 1)) > 1e-3
+
+
+def mismatched_chain_joint(p_of, q_draw, q_verify, V, G, T):
+    """Emitted law when drafts come from q_draw but the verifier is given q_verify rows
+    (accept probability min(1, p / q_verify), residual [p - q_verify]_+)."""
+    from collections import defaultdict
+    joint = defaultdict(float)
+    for x in itertools.product(range(V), repeat=G):
+        w = float(np.prod([q_draw(x[:i])[x[i]] for i in range(G)]))
+        if w == 0.0:
+            continue
+
+        def walk(i, mass):
+            if i == G:
+                for k, pk in enumerate(p_of(x)):
+                    joint[x + (k,)] += mass * pk
+                return
+            p, qv = p_of(x[:i]), q_verify(x[:i])
+            a = 0.0 if qv[x[i]] == 0 else min(1.0, p[x[i]] / qv[x[i]])
+            walk(i + 1, mass * a)
+            if a < 1.0:
+                res = np.maximum(p - qv, 0.0)
+                res = res / res.sum()
+                for k, rk in enumerate(res):
+                    seq = x[:i] + (k,)
+                    # complete to G + 1 tokens with target draws
+                    stack = [(seq, mass * (1 - a) * rk)]
+                    while stack:
+                        s_, m_ = stack.pop()
+                        if len(s_) == G + 1:
+                            joint[s_] += m_
+                            continue
+                        for t, pt in enumerate(p_of(s_)):
+                            stack.append((s_ + (t,), m_ * pt))
+        walk(0, w)
+    return joint

@@ -29,12 +29,15 @@ def _paths(parents, tokens):
     return paths
 
 
-def residual_walk_law(p_of, q_of, parents, V, T, horizon, retest_original=False):
+def residual_walk_law(p_of, q_of, parents, V, T, horizon, retest_original=False, verify_rows=None):
     """Joint law of the emitted tokens (completed to `horizon`) over the proposals (node c's
-    token drawn from q_of(c, tokens of its ancestors)) and the walk's uniforms.
+    token drawn from q_of(c, tokens of its ancestors, tokens of its earlier siblings)) and
+    the walk's uniforms.
 
     retest_original: weight the branches as if every child were tested against the
     original p (the wrong procedure of [M7.7] §0x08B); the oracle is then not consulted.
+    verify_rows: rows given to the verifier instead of the proposal rows (a proposal /
+    verifier mismatch, [M7.7] §0x0AB); called like q_of.
     """
     N = len(parents)
     children = {v: [c for c in range(v + 1, N) if parents[c] == v] for v in range(N)}
@@ -42,8 +45,12 @@ def residual_walk_law(p_of, q_of, parents, V, T, horizon, retest_original=False)
     for toks in itertools.product(range(V), repeat=N - 1):
         tokens = (0,) + toks
         paths = _paths(parents, tokens)
-        qrows = [np.zeros(V)] + [np.asarray(q_of(c, paths[parents[c]]), np.float64) for c in range(1, N)]
+        sibs = [tuple(tokens[s] for s in children[parents[c]] if s < c) if c else () for c in range(N)]
+        qrows = [np.zeros(V)] + [np.asarray(q_of(c, paths[parents[c]], sibs[c]), np.float64) for c in range(1, N)]
         w_prop = float(np.prod([qrows[c][tokens[c]] for c in range(1, N)]))
+        if verify_rows is not None:
+            qrows = [np.zeros(V)] + [np.asarray(verify_rows(c, paths[parents[c]], sibs[c]), np.float64)
+                                     for c in range(1, N)]
         if w_prop == 0.0:
             continue
         L = np.stack([logits_for(p_of(paths[v]), T) for v in range(N)])
@@ -93,7 +100,7 @@ def test_pages_example_two_iid_proposals():
     p = np.array([0.5, 0.3, 0.2])
     q = np.array([0.4, 0.4, 0.2])
     p_of = lambda pre: p if len(pre) == 0 else np.full(3, 1 / 3)
-    q_of = lambda c, pre: q
+    q_of = lambda c, pre, sib: q
     parents = [-1, 0, 0]
     first = lambda joint: np.array([sum(v for s, v in joint.items() if s[0] == k) for k in range(3)])
     joint = residual_walk_law(p_of, q_of, parents, 3, 1.0, 2)
@@ -116,9 +123,9 @@ def test_pages_degenerate_example_duplicated_mass():
     for k in (2, 3):
         parents = [-1] + [0] * k
         first1 = lambda joint: sum(v for s, v in joint.items() if s[0] == 1)
-        joint = residual_walk_law(p_of, lambda c, pre: q, parents, 2, 1.0, 2)
+        joint = residual_walk_law(p_of, lambda c, pre, sib: q, parents, 2, 1.0, 2)
         assert abs(first1(joint) - 0.5) < 1e-12
-        wrong = residual_walk_law(p_of, lambda c, pre: q, parents, 2, 1.0, 2, retest_original=True)
+        wrong = residual_walk_law(p_of, lambda c, pre, sib: q, parents, 2, 1.0, 2, retest_original=True)
         # at least 1 - 2^-k (the pages' bound); all-rejected rounds add 2^-k * p(1)
         assert first1(wrong) >= 1 - 0.5 ** k
         assert abs(first1(wrong) - (1 - 0.5 ** k + 0.5 ** k * 0.5)) < 1e-12
@@ -129,7 +136,7 @@ def test_law_depth_one(V, k, iid):
     rng = np.random.default_rng(40 * V + k + (0 if iid else 7))
     p_of = prefix_table(rng, V, 2)
     qs = [rng.dirichlet(np.ones(V)) for _ in range(k + 1)]
-    q_of = (lambda c, pre: qs[0]) if iid else (lambda c, pre: qs[c])
+    q_of = (lambda c, pre, sib: qs[0]) if iid else (lambda c, pre, sib: qs[c])
     parents = [-1] + [0] * k
     joint = residual_walk_law(p_of, q_of, parents, V, 0.9, 2)
     assert max_joint_gap(joint, target_joint(p_of, V, 2)) < 1e-12
@@ -142,7 +149,7 @@ def test_law_depth_two(shape):
     p_of = prefix_table(rng, V, 3)
     q_tab = {}
 
-    def q_of(c, pre):
+    def q_of(c, pre, sib):
         # each parent's children drawn i.i.d. from a proposal that depends on the prefix
         if pre not in q_tab:
             q_tab[pre] = rng.dirichlet(np.ones(V))
@@ -210,3 +217,39 @@ def test_leaf_root_is_a_plain_target_draw():
         r = verify_tree_residual_one(L, np.zeros((1, 4)), np.array([-1]), np.array([0]), np.array([0.5]),
                                      np.array([u]), 0.7)
         assert r["tokens"] == [int(np.searchsorted(np.cumsum(p), u, side="right"))]
+
+
+@pytest.mark.parametrize("V,k", [(2, 2), (3, 2), (3, 3), (4, 3)])
+def test_law_without_replacement_proposals(V, k):
+    """[M7.7] §0x0AB (Sequoia): siblings drawn without replacement, each from the draft row
+    with the earlier siblings' tokens removed (uniform over the unsampled tokens once the
+    draft mass is used up); verified with those rows, the emitted law is the target's."""
+    from synth import without_replacement_row
+    rng = np.random.default_rng(60 + 10 * V + k)
+    p_of = prefix_table(rng, V, 2)
+    q0 = rng.dirichlet(np.ones(V))
+    if V >= 3:
+        q0[rng.integers(V)] = 0.0                      # a token the draft never proposes first
+        q0 /= q0.sum()
+    q_of = lambda c, pre, sib: without_replacement_row(q0, sib)
+    parents = [-1] + [0] * k
+    joint = residual_walk_law(p_of, q_of, parents, V, 1.0, 2)
+    assert max_joint_gap(joint, target_joint(p_of, V, 2)) < 1e-12
+
+
+def test_without_replacement_with_iid_rows_is_wrong():
+    """[M7.7] §0x0AB: without-replacement sampling changes the proposal law, so the verifier
+    for i.i.d. samples (every sibling tested against the drafter's original row) is not
+    exact for it."""
+    from synth import without_replacement_row
+    p = np.array([0.2, 0.5, 0.3])
+    q0 = np.array([0.6, 0.3, 0.1])
+    p_of = lambda pre: p if len(pre) == 0 else np.full(3, 1 / 3)
+    parents = [-1, 0, 0]
+    first = lambda joint: np.array([sum(v for s, v in joint.items() if s[0] == t) for t in range(3)])
+    right = residual_walk_law(p_of, lambda c, pre, sib: without_replacement_row(q0, sib), parents, 3, 1.0, 2)
+    assert np.allclose(first(right), p, atol=1e-12)
+    wrong = residual_walk_law(p_of, lambda c, pre, sib: without_replacement_row(q0, sib), parents, 3, 1.0, 2,
+                              verify_rows=lambda c, pre, sib: q0)
+    assert abs(first(wrong).sum() - 1.0) < 1e-12
+    assert np.abs(first(wrong) - p).max() > 0.01, first(wrong)
