@@ -74,7 +74,7 @@ class SpecOptions(ctypes.Structure):
     pointers, NULL = off)."""
     _fields_ = [("stop_tokens", _c_void_p), ("n_stop", ctypes.c_int32), ("budget", _c_void_p),
                 ("finish", _c_void_p), ("bias", _c_void_p), ("allowed", _c_void_p), ("top_k", _c_void_p),
-                ("top_p", _c_void_p)]
+                ("top_p", _c_void_p), ("q_index", _c_void_p), ("q_k", ctypes.c_int32)]
 
 
 class SpecError(RuntimeError):
@@ -211,8 +211,11 @@ def _proc_args(bias, allowed, top_k, top_p, B, R, V, dev):
         _need(top_p, "top_p", dtype=torch.float32, shape=(B,), device=dev)
 
 
-def _options(stop_tokens, budget, finish, bias=None, allowed=None, top_k=None, top_p=None) -> SpecOptions:
+def _options(stop_tokens, budget, finish, bias=None, allowed=None, top_k=None, top_p=None,
+             q_index=None) -> SpecOptions:
     o = SpecOptions()
+    o.q_index = _ptr(q_index)
+    o.q_k = 0 if q_index is None else int(q_index.shape[-1])
     o.stop_tokens = _ptr(stop_tokens)
     o.n_stop = 0 if stop_tokens is None else int(stop_tokens.numel())
     o.budget, o.finish = _ptr(budget), _ptr(finish)
@@ -222,7 +225,7 @@ def _options(stop_tokens, budget, finish, bias=None, allowed=None, top_k=None, t
 
 def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature, with_stats,
                 workspace_tensor, out, stop_tokens=None, budget=None, bias=None, allowed=None, top_k=None,
-                top_p=None):
+                top_p=None, q_index=None):
     lib = load_library()
     _need(target_logits, "target_logits")
     if target_logits.dim() != 3:
@@ -230,7 +233,13 @@ def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
     B, R, V = target_logits.shape
     G = R - 1
     dev = target_logits.device
-    _need(draft_probs, "draft_probs", shape=(B, G, V), device=dev)
+    if q_index is None:
+        _need(draft_probs, "draft_probs", shape=(B, G, V), device=dev)
+    else:
+        _need(q_index, "q_index", dtype=torch.int32, device=dev)
+        if q_index.dim() != 3 or tuple(q_index.shape[:2]) != (B, G):
+            raise ValueError("q_index must be [B, gamma, K]")
+        _need(draft_probs, "draft_probs", dtype=torch.float32, shape=tuple(q_index.shape), device=dev)
     _need(draft_tokens, "draft_tokens", dtype=torch.int32, shape=(B, G), device=dev)
     _need(uniforms, "uniforms", dtype=torch.float32, shape=(B, R), device=dev)
     lt, qt = _dtype_code(target_logits, "target_logits"), _dtype_code(draft_probs, "draft_probs")
@@ -242,7 +251,7 @@ def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
             out["stats"] = torch.empty(B, R, 4, dtype=torch.float32, device=dev)
     stopping = stop_tokens is not None or budget is not None
     n_stop = _stop_args(stop_tokens, budget, B, dev)
-    processing = any(t is not None for t in (bias, allowed, top_k, top_p))
+    processing = any(t is not None for t in (bias, allowed, top_k, top_p, q_index))
     _proc_args(bias, allowed, top_k, top_p, B, R, V, dev)
     if stopping and "finish" not in out:
         out["finish"] = torch.empty(B, dtype=torch.int32, device=dev)
@@ -255,9 +264,9 @@ def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
     head = (_ptr(target_logits), lt, _ptr(draft_probs), qt, _ptr(draft_tokens), _ptr(uniforms),
             B, G, V, ctypes.c_float(float(temperature)))
     keep = (target_logits, draft_probs, draft_tokens, uniforms, ws, stream, stop_tokens, budget, bias, allowed,
-            top_k, top_p)
+            top_k, top_p, q_index)
     if processing:
-        opt = _options(stop_tokens, budget, out.get("finish"), bias, allowed, top_k, top_p)
+        opt = _options(stop_tokens, budget, out.get("finish"), bias, allowed, top_k, top_p, q_index)
         args = head + (ctypes.byref(opt), _ptr(out["accepted_len"]), _ptr(out["out_tokens"]),
                        _ptr(out["req_status"]), _ptr(out.get("stats")), wp, wn, ctypes.c_void_p(stream.cuda_stream))
         return lib.spec_verify_chain_ex, args, keep + (opt,), out
@@ -277,7 +286,7 @@ def spec_verify_chain(target_logits: torch.Tensor, draft_probs: torch.Tensor,
                       out: Optional[dict] = None, stop_tokens: Optional[torch.Tensor] = None,
                       budget: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
                       allowed: Optional[torch.Tensor] = None, top_k: Optional[torch.Tensor] = None,
-                      top_p: Optional[torch.Tensor] = None) -> dict:
+                      top_p: Optional[torch.Tensor] = None, q_index: Optional[torch.Tensor] = None) -> dict:
     """Chain verification by rejection sampling (C entry point spec_verify_chain;
     spec_verify_chain_stop when stop_tokens or budget is given; spec_verify_chain_ex when a
     processor is given).
@@ -286,24 +295,25 @@ def spec_verify_chain(target_logits: torch.Tensor, draft_probs: torch.Tensor,
     draft_tokens [B, gamma] int32; uniforms [B, gamma+1] fp32; temperature > 0;
     stop_tokens [n] int32 (n <= 256); budget [B] int32 remaining output budgets;
     processors: bias [V] fp32, allowed [B, gamma+1, ceil(V/32)] int32 bit words,
-    top_k [B] int32, top_p [B] fp32.
+    top_k [B] int32, top_p [B] fp32; sparse draft rows: q_index [B, gamma, K] int32 with
+    draft_probs [B, gamma, K] fp32 values (every token not listed has q = 0).
     Returns {accepted_len [B], out_tokens [B, gamma+1], req_status [B], stats?, finish?}
     (int32 / fp32 GPU tensors, valid once the current stream reaches the call).
     """
     fn, args, _, out = _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
                                    with_stats, workspace_tensor, out, stop_tokens, budget, bias, allowed,
-                                   top_k, top_p)
+                                   top_k, top_p, q_index)
     _check(fn(*args))
     return out
 
 
 def prepare_chain(target_logits, draft_probs, draft_tokens, uniforms, temperature, *,
                   with_stats=False, workspace_tensor=None, out=None, stop_tokens=None,
-                  budget=None, bias=None, allowed=None, top_k=None, top_p=None) -> PreparedCall:
+                  budget=None, bias=None, allowed=None, top_k=None, top_p=None, q_index=None) -> PreparedCall:
     """spec_verify_chain with its arguments checked and marshalled once (see PreparedCall)."""
     return PreparedCall(*_chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
                                      with_stats, workspace_tensor, out, stop_tokens, budget, bias, allowed,
-                                     top_k, top_p))
+                                     top_k, top_p, q_index))
 
 
 def _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens=None, budget=None, bias=None,

@@ -134,7 +134,9 @@ spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, con
   const spec_verify_options o = opt ? *opt : spec_verify_options{};
   if (!sizes_ok(B, gamma, V) || !temperature_ok(temperature) || !stop_ok(o.stop_tokens, o.n_stop))
     return SPEC_EINVAL;
+  if (o.q_index && !(o.q_k >= 1 && o.q_k <= SPEC_MAX_SPARSE_K)) return SPEC_EINVAL;
   if (!dtype_ok(logit_dtype) || !dtype_ok(q_dtype)) return SPEC_EDTYPE;
+  if (o.q_index && q_dtype != SPEC_F32) return SPEC_EDTYPE;
   if (!sv::grid_fits(sv::chain_blocks(B, gamma, V))) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
   if (!target_logits || !uniforms || !accepted_len || !out_tokens || !req_status) return SPEC_EINVAL;
@@ -156,6 +158,8 @@ spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, con
   const bool truncate = o.top_k || o.top_p;
   p.pr = proc_spec(o, V, truncate ? reinterpret_cast<float*>(ws + L.thresh) : nullptr);
   p.thresh_ws = truncate ? reinterpret_cast<float*>(ws + L.thresh) : nullptr;
+  p.q_index = gamma > 0 ? o.q_index : nullptr;
+  p.q_k = o.q_k;
   p.part = reinterpret_cast<float2*>(ws + L.part);
   p.gath = reinterpret_cast<unsigned long long*>(ws + L.gath);
   p.tmass = reinterpret_cast<double*>(ws + L.tmass);
@@ -172,8 +176,8 @@ spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, con
   const double c2 = kLog2e / static_cast<double>(temperature);
   p.c2 = static_cast<float>(c2);
   p.inv_t = 1.0 / static_cast<double>(temperature);
-  const bool vec = (V % 8 == 0) && aligned16(target_logits) && (gamma == 0 || aligned16(draft_probs)) &&
-                   (!o.bias || aligned16(o.bias));
+  const bool vec = (V % 8 == 0) && aligned16(target_logits) &&
+                   (gamma == 0 || p.q_index || aligned16(draft_probs)) && (!o.bias || aligned16(o.bias));
   if (truncate) {
     sv::ThreshParams t{};
     t.logits = target_logits;

@@ -50,7 +50,7 @@ __device__ __forceinline__ unsigned long long* gather_rec(const ChainParams& p, 
   return p.gath + ((size_t)b * p.G + i) * 3;
 }
 
-template <int DT, bool PROC>
+template <int DT, int QT, bool PROC>
 __device__ __forceinline__ void gather_issue(const ChainParams& p, int b, int i, unsigned& x, unsigned& lb,
                                              unsigned& qb) {
   const int t = p.tokens[(size_t)b * p.G + i];
@@ -61,8 +61,26 @@ __device__ __forceinline__ void gather_issue(const ChainParams& p, int b, int i,
     float l = load_scalar<DT>(p.logits, rowid * p.V + t);
     if constexpr (PROC) l = proc1(p.pr, rowid, row_tau(p.pr, rowid), t, l);
     lb = __float_as_uint(l);
-    qb = __float_as_uint(gather_q(p, ((size_t)b * p.G + i) * p.V + t));
+    if constexpr (QT != kSparseQ) qb = __float_as_uint(gather_q(p, ((size_t)b * p.G + i) * p.V + t));
   }
+}
+
+// q_i(x) of a sparse draft row, block-wide: the sum of the values listed at index x (each
+// thread sums its share of the entries in order, then a fixed-order block sum); every
+// thread receives it.  Contains two barriers.
+__device__ float sparse_q_lookup(const ChainParams& p, int b, int i, int x, float* scratch) {
+  const size_t base = ((size_t)b * p.G + i) * p.q_k;
+  const float* val = static_cast<const float*>(p.q) + base;
+  const int32_t* idx = p.q_index + base;
+  float acc = 0.0f;
+  for (int j = threadIdx.x; j < p.q_k; j += kBlock)
+    if (idx[j] == x) acc += val[j];
+  const float w = wave_sum(acc);
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[wave_id()] = w;
+  __syncthreads();
+  const float t = (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
+  __syncthreads();
+  return t;
 }
 
 __device__ __forceinline__ void gather_publish(const ChainParams& p, int b, int i, unsigned x, unsigned lb,
@@ -94,7 +112,7 @@ __device__ __forceinline__ void wave_row_summary_proc(const ChainParams& p, size
 }
 
 // Statistics item: slice `slice` of row i of request b.
-template <int DT, bool VEC, bool PROC>
+template <int DT, int QT, bool VEC, bool PROC>
 __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
   __shared__ float s_wm[kWavesPerBlock], s_wz[kWavesPerBlock];
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
@@ -103,7 +121,7 @@ __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
   // probability for the decision, overlapped with the streaming below
   const bool gathers = slice == 0 && i < p.G && threadIdx.x == 0;
   unsigned gx = 0, gl = 0, gq = 0;
-  if (gathers) gather_issue<DT, PROC>(p, b, i, gx, gl, gq);
+  if (gathers) gather_issue<DT, QT, PROC>(p, b, i, gx, gl, gq);
   // wave w streams chunks first + 4k of this slice (k < CPW)
   const long first = (long)slice * kWavesPerBlock * p.CPW + wave;
   float m, z;
@@ -115,6 +133,14 @@ __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
   if (lane == 0) {
     s_wm[wave] = m;
     s_wz[wave] = z;
+  }
+  if constexpr (QT == kSparseQ) {
+    if (slice == 0 && i < p.G) {        // block-uniform: the whole block searches the row
+      __shared__ float s_q[kWavesPerBlock];
+      const int t = p.tokens[(size_t)b * p.G + i];
+      const float qx = sparse_q_lookup(p, b, i, t, s_q);
+      if (gathers && t >= 0 && t < p.V) gq = __float_as_uint(qx);
+    }
   }
   if (gathers) gather_publish(p, b, i, gx, gl, gq);
   __syncthreads();
@@ -370,7 +396,34 @@ __device__ __forceinline__ void term_chunk(const ChainParams& p, const void* lro
   for (int s = 0; s < kTermSlabs; ++s) {
     const long e0 = ((long)c * kTermSlabs + s) * kSlab + (long)threadIdx.x * kVec;
     load8<DT, VEC, false>(lrow, e0, p.V, lv[s], -INFINITY);
-    if constexpr (RESID) load8<QT, VEC, false>(qrow, e0, p.V, qv[s], 0.0f);
+    if constexpr (RESID && QT != kSparseQ) load8<QT, VEC, false>(qrow, e0, p.V, qv[s], 0.0f);
+  }
+  if constexpr (RESID && QT == kSparseQ) {
+    // the chunk of the sparse row, densified in LDS: listed values added at their indices
+    // (an entry with an index outside [0, V) makes the row invalid, like a negative value)
+    __shared__ float s_qd[kTermChunk];
+    __shared__ int s_qbad;
+    const int tid = threadIdx.x;
+    for (int j = tid; j < kTermChunk; j += kBlock) s_qd[j] = 0.0f;
+    if (tid == 0) s_qbad = 0;
+    __syncthreads();
+    const size_t base = ((rowid / p.R) * p.G + d.A) * p.q_k;
+    const float* val = static_cast<const float*>(p.q) + base;
+    const int32_t* idx = p.q_index + base;
+    const long lo = (long)c * kTermChunk;
+    for (int j = tid; j < p.q_k; j += kBlock) {
+      const int x = idx[j];
+      const float v = val[j];
+      if (x < 0 || x >= p.V || !(v >= 0.0f && v < INFINITY)) s_qbad = 1;
+      else if (x >= lo && x < lo + kTermChunk) atomicAdd(&s_qd[x - lo], v);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kTermSlabs; ++s)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qv[s][k] = s_qd[s * kSlab + tid * kVec + k];
+    bad |= (s_qbad != 0);
+    __syncthreads();                    // s_qd is reused by the next call
   }
   if constexpr (PROC) {
 #pragma unroll
@@ -615,7 +668,8 @@ __device__ void chain_clear(const ChainParams& p, int b) {
 template <int DT, int QT, bool VEC, bool RESID, bool PROC>
 __device__ void terminal_body(const ChainParams& p, int b, int c, const ChainDecision& d, const RowState& rs) {
   const void* lrow = row_ptr<DT>(p.logits, (size_t)b * p.R + d.A, p.V);
-  const void* qrow = RESID ? row_ptr<QT>(p.q, (size_t)b * p.G + d.A, p.V) : nullptr;
+  const void* qrow = nullptr;
+  if constexpr (RESID && QT != kSparseQ) qrow = row_ptr<QT>(p.q, (size_t)b * p.G + d.A, p.V);
   float w[kTermSlabs][8];
   bool bad = false;
   term_chunk<DT, QT, VEC, RESID, PROC>(p, lrow, qrow, c, d, (size_t)b * p.R + d.A, w, bad);
@@ -685,7 +739,7 @@ __global__ __launch_bounds__(kBlock) void chain_kernel(ChainParams p) {
 #endif
   const Item it = block_item(p, blockIdx.x);
   if (it.terminal) terminal_item<DT, QT, VEC, PROC>(p, it.b, it.idx);
-  else stats_item<DT, VEC, PROC>(p, it.b, it.idx / p.SL, it.idx % p.SL);
+  else stats_item<DT, QT, VEC, PROC>(p, it.b, it.idx / p.SL, it.idx % p.SL);
 }
 
 // Lag between a request's statistics and terminal items, in rounds of resident blocks:
@@ -734,6 +788,10 @@ hipError_t launch_typed(ChainParams p, hipStream_t s) {
 template <bool PROC>
 hipError_t launch_dispatch(const ChainParams& p, int logit_dtype, bool vec, hipStream_t s) {
   const bool lb = logit_dtype == kBF16, qb = p.q_dtype == kBF16;
+  if (p.q_index) {
+    if (vec) return lb ? launch_typed<kBF16, kSparseQ, true, PROC>(p, s) : launch_typed<kF32, kSparseQ, true, PROC>(p, s);
+    return lb ? launch_typed<kBF16, kSparseQ, false, PROC>(p, s) : launch_typed<kF32, kSparseQ, false, PROC>(p, s);
+  }
   if (vec) {
     if (lb) return qb ? launch_typed<kBF16, kBF16, true, PROC>(p, s) : launch_typed<kBF16, kF32, true, PROC>(p, s);
     return qb ? launch_typed<kF32, kBF16, true, PROC>(p, s) : launch_typed<kF32, kF32, true, PROC>(p, s);

@@ -25,6 +25,8 @@ constexpr int kWaveChunk = kWave * kStatVecs * kVec;   // 2048
 constexpr int kSlab = kBlock * kVec;                   // 2048
 
 enum : int { kF32 = 0, kBF16 = 1 };
+// Draft rows given sparsely: K fp32 values at K listed token indices, zero elsewhere.
+constexpr int kSparseQ = 2;
 
 // Index of the calling wave in its block, as a wave-uniform (scalar) value: loop bounds and
 // branches derived from it then compile to scalar control flow.

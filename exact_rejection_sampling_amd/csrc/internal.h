@@ -55,6 +55,8 @@ struct ChainParams {
   StopSpec st;
   ProcSpec pr;
   float* thresh_ws;          // the workspace's threshold words (cleared by the selectors), or null
+  const int32_t* q_index;    // [B, G, q_k] token indices of sparse draft rows (q then holds
+  int q_k;                   //   [B, G, q_k] fp32 values), or null for dense rows
   // workspace
   float2* part;              // [B*R*SL] block summaries (raw max, Z)
   unsigned long long* gath;  // [B*G*3] draft token, its logit, its draft probability

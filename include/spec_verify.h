@@ -74,6 +74,7 @@ extern "C" {
 #define SPEC_MAX_VOCAB  (1 << 28)   /* V */
 #define SPEC_MAX_NODES  4096        /* N: tree nodes per request */
 #define SPEC_MAX_STOP   256         /* n_stop: stop tokens of the *_stop entry points */
+#define SPEC_MAX_SPARSE_K 65536     /* q_k: entries of a sparse draft row */
 #define SPEC_MIN_TEMPERATURE 0x1p-20f
 #define SPEC_MAX_TEMPERATURE 0x1p+20f
 
@@ -202,6 +203,11 @@ spec_status spec_verify_chain_stop(const void* target_logits, int logit_dtype,
  *   with strictly larger s is below top_p (top-p: the smallest tie-closed set of top tokens
  *   whose mass reaches top_p).  NaN or +inf in l + bias anywhere in a reached row makes the
  *   request SPEC_REQ_NONFINITE, masked or not; so does a reached row with no kept token.
+ *   Sparse draft rows ([Tiny] "Logit and residual scratch": exact only when the omitted
+ *   proposal probabilities are known to be zero): q_i(x) is the sum of the values listed at
+ *   index x (0 if none); the residual uses the row densified the same way.  An entry whose
+ *   index is outside [0, V), or whose value is negative or not finite, makes the row
+ *   invalid when it is read as a whole (SPEC_REQ_RESIDUAL_EMPTY at a rejection there).
  *   Top-k and top-p run a threshold pass over every row first (a second launch, about 17
  *   reads of each row from cache); bias and the mask are applied where the verifier reads
  *   logits, at no extra pass.  The greedy verifier applies bias and the mask (truncations
@@ -217,6 +223,10 @@ typedef struct {
                                    row: bit x % 32 of word x / 32 set = token x allowed */
   const int32_t* top_k;         /* [B] top-k per request; 0 (or negative): off */
   const float* top_p;           /* [B] top-p per request; outside (0, 1): off */
+  const int32_t* q_index;       /* chain only: [B, gamma, q_k] token indices of sparse draft
+                                   rows; draft_probs then holds [B, gamma, q_k] fp32 values
+                                   (q_dtype SPEC_F32) and every token not listed has q = 0 */
+  int32_t q_k;                  /* 1 .. SPEC_MAX_SPARSE_K when q_index is given */
 } spec_verify_options;
 
 /* Chain verification with options (spec_verify_options); every other argument and the

@@ -355,6 +355,26 @@ def make_stop(tokens: np.ndarray, V: int, *, seed: int, n_stop: int = 4, from_dr
     return np.asarray(picks[:n_stop], dtype=np.int32), budget
 
 
+def make_chain_sparse(B: int, gamma: int, V: int, K: int, *, seed: int, **chain_kw):
+    """A top-K drafter: the chain recipe's draft rows truncated to their K largest entries
+    and renormalized (fp32), the draft tokens drawn again from the truncated rows.  Returns
+    (ChainInputs whose q holds the dense truncated rows, index [B, gamma, K] int32,
+    values [B, gamma, K] fp32) -- the sparse form lists each row's K tokens in increasing
+    index order."""
+    x = make_chain(B, gamma, V, seed=seed, **chain_kw)
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    K = min(K, V)
+    idx = np.sort(np.argpartition(-x.q, K - 1, axis=-1)[..., :K], axis=-1).astype(np.int32)
+    vals = np.take_along_axis(x.q, idx, -1).astype(np.float64)
+    vals = (vals / vals.sum(-1, keepdims=True)).astype(np.float32)
+    dense = np.zeros_like(x.q)
+    np.put_along_axis(dense, idx, vals, -1)
+    x.q = dense
+    if gamma > 0:
+        x.tokens = _draw_from_rows(rng, dense)
+    return x, idx, vals
+
+
 def make_processors(B: int, R: int, V: int, *, seed: int, bias_sigma: float = 1.0, allowed_frac: float = 0.9,
                     top_k=(0, 1, 20, 1000), top_p=(1.0, 0.5, 0.9, 0.99), with_bias=True, with_mask=True,
                     with_top_k=True, with_top_p=True):
