@@ -160,6 +160,35 @@ def bench_greedy(args, torch, sv, synth):
                 traffic_gbs=None if trec is None else trec["bytes_per_launch"] / launch / 1e9)
 
 
+def bench_greedy_lazy(args, torch, sv, synth, k):
+    """The greedy workload with lazy rows (spec_verify_greedy_ex, lazy_rows = k): rows read in
+    groups of k, a group only when every draft before it matched."""
+    x = synth.make_config(4, 0)
+    B, G, V = x.B, x.gamma, x.V
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    tt = torch.from_numpy(x.tokens).to(dev)
+    sets = device_copies(lambda: (lt.clone(),), lt.numel() * 2)
+    del lt
+    stream = torch.cuda.current_stream()
+    ws = torch.zeros(sv.greedy_workspace_bytes(B, G, V) + 512, dtype=torch.uint8, device=dev)
+    calls = [sv.prepare_greedy(s[0], tt, workspace_tensor=ws, lazy_rows=k) for s in sets]
+    span, per = time_calls(calls, max(100, args.steps // 2), args.warmup, stream)
+    acc = calls[0].out["accepted_len"].cpu().numpy()
+    assert (calls[0].out["req_status"].cpu().numpy() == 0).all()
+    launch = span / len(per)
+    R = G + 1
+    needed = int((acc + 1).sum())
+    read = int(np.minimum(R, -(-(acc + 1) // k) * k).sum())
+    alg = needed * V * 2 + B * G * 4 + B * (G + 2) * 8
+    del sets, calls
+    return dict(workload=f"greedy B=256 gamma=8 V=128256 bf16, lazy rows in groups of {k}",
+                positions_per_s=B * R * len(per) / span, us_per_call=launch * 1e6,
+                evented_call_mean_us=float(per.mean()) * 1e3, rows_needed=needed, rows_read=read,
+                rows_dense=B * R, alg_bytes_per_call=alg, alg_gbs=alg / launch / 1e9,
+                alg_frac=alg / launch / 1e9 / HBM_PEAK_GBS)
+
+
 def bench_tree(args, torch, sv, synth):
     x = synth.make_config(5, 0)
     B, N, V = x.B, x.N, x.V
@@ -263,6 +292,45 @@ def bench_chain_proc(args, torch, sv, synth, truncate):
     return dict(workload=f"chain B=64 gamma=5 V=128256 bf16 with {what}",
                 positions_per_s=x.B * (x.gamma + 1) * len(per) / span, us_per_call=launch * 1e6,
                 evented_call_mean_us=float(per.mean()) * 1e3)
+
+
+def bench_chain_lazy(args, torch, sv, synth, k, fp32=False):
+    """The headline chain workload (fp32: its fp32-logit variant at T = 1), with lazy rows
+    when k >= 1 (spec_verify_chain_ex, lazy_rows = k: rows read in groups of k, a group only
+    when every draft before it was accepted), or every row read (k = 0)."""
+    x = synth.make_config(3, 0, logit_dtype="f32", temperature=1.0) if fp32 else synth.make_config(3, 0)
+    B, G, V = x.B, x.gamma, x.V
+    dev = "cuda:0"
+    if fp32:
+        lt = torch.from_numpy(x.logits).to(dev)
+    else:
+        lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    qt = torch.from_numpy(x.q).to(dev)
+    tt, ut = torch.from_numpy(x.tokens).to(dev), torch.from_numpy(x.u).to(dev)
+    sl = lt.element_size()
+    sets = device_copies(lambda: (lt.clone(), qt.clone()), lt.numel() * sl + qt.numel() * 4)
+    del lt, qt
+    stream = torch.cuda.current_stream()
+    ws = torch.zeros(sv.chain_workspace_bytes(B, G, V) + 512, dtype=torch.uint8, device=dev)
+    calls = [sv.prepare_chain(s[0], s[1], tt, ut, float(x.temperature), workspace_tensor=ws, lazy_rows=k)
+             for s in sets]
+    span, per = time_calls(calls, args.steps, args.warmup, stream)
+    acc = calls[0].out["accepted_len"].cpu().numpy()
+    assert (calls[0].out["req_status"].cpu().numpy() == 0).all()
+    launch = span / len(per)
+    R = G + 1
+    needed = int((acc + 1).sum()) if k else B * R                  # rows 0..A of every request
+    read = int(np.minimum(R, -(-(acc + 1) // k) * k).sum()) if k else B * R   # whole groups
+    n_rej = int((acc < G).sum())
+    alg = needed * V * sl + n_rej * V * 4 + B * G * 10 + B * R * 4 + B * (G + 2) * 8
+    del sets, calls
+    what = f"lazy rows in groups of {k}" if k else "every row read"
+    dt = "fp32 logits, T=1" if fp32 else "bf16 logits, T=0.8"
+    return dict(workload=f"chain B=64 gamma=5 V=128256 {dt}, {what}",
+                positions_per_s=B * R * len(per) / span, us_per_call=launch * 1e6,
+                evented_call_mean_us=float(per.mean()) * 1e3, rows_needed=needed, rows_read=read,
+                rows_dense=B * R, alg_bytes_per_call=alg, alg_gbs=alg / launch / 1e9,
+                alg_frac=alg / launch / 1e9 / HBM_PEAK_GBS)
 
 
 _CPU_X = None   # the workload a forked oracle worker reads
@@ -388,6 +456,18 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] chain with every processor")
         line["secondary"]["chain_processors"] = bench_chain_proc(args, torch, sv, synth, True)
+        for k in (3, 2):
+            torch.cuda.empty_cache()
+            log(f"[bench] chain with lazy rows, groups of {k}")
+            line["secondary"][f"chain_lazy{k}"] = bench_chain_lazy(args, torch, sv, synth, k)
+        for k in (0, 3):
+            torch.cuda.empty_cache()
+            log(f"[bench] chain, fp32 logits, lazy rows {k}")
+            line["secondary"][f"chain_f32_lazy{k}"] = bench_chain_lazy(args, torch, sv, synth, k, fp32=True)
+        for k in (3, 2, 1):
+            torch.cuda.empty_cache()
+            log(f"[bench] greedy with lazy rows, groups of {k}")
+            line["secondary"][f"greedy_lazy{k}"] = bench_greedy_lazy(args, torch, sv, synth, k)
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

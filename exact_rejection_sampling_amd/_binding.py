@@ -74,7 +74,8 @@ class SpecOptions(ctypes.Structure):
     pointers, NULL = off)."""
     _fields_ = [("stop_tokens", _c_void_p), ("n_stop", ctypes.c_int32), ("budget", _c_void_p),
                 ("finish", _c_void_p), ("bias", _c_void_p), ("allowed", _c_void_p), ("top_k", _c_void_p),
-                ("top_p", _c_void_p), ("q_index", _c_void_p), ("q_k", ctypes.c_int32)]
+                ("top_p", _c_void_p), ("q_index", _c_void_p), ("q_k", ctypes.c_int32),
+                ("lazy_rows", ctypes.c_int32)]
 
 
 class SpecError(RuntimeError):
@@ -212,8 +213,9 @@ def _proc_args(bias, allowed, top_k, top_p, B, R, V, dev):
 
 
 def _options(stop_tokens, budget, finish, bias=None, allowed=None, top_k=None, top_p=None,
-             q_index=None) -> SpecOptions:
+             q_index=None, lazy_rows=0) -> SpecOptions:
     o = SpecOptions()
+    o.lazy_rows = int(lazy_rows)
     o.q_index = _ptr(q_index)
     o.q_k = 0 if q_index is None else int(q_index.shape[-1])
     o.stop_tokens = _ptr(stop_tokens)
@@ -225,8 +227,10 @@ def _options(stop_tokens, budget, finish, bias=None, allowed=None, top_k=None, t
 
 def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature, with_stats,
                 workspace_tensor, out, stop_tokens=None, budget=None, bias=None, allowed=None, top_k=None,
-                top_p=None, q_index=None):
+                top_p=None, q_index=None, lazy_rows=0):
     lib = load_library()
+    if int(lazy_rows) < 0:
+        raise ValueError("lazy_rows must be >= 0")
     _need(target_logits, "target_logits")
     if target_logits.dim() != 3:
         raise ValueError("target_logits must be [B, gamma+1, V]")
@@ -251,7 +255,7 @@ def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
             out["stats"] = torch.empty(B, R, 4, dtype=torch.float32, device=dev)
     stopping = stop_tokens is not None or budget is not None
     n_stop = _stop_args(stop_tokens, budget, B, dev)
-    processing = any(t is not None for t in (bias, allowed, top_k, top_p, q_index))
+    processing = any(t is not None for t in (bias, allowed, top_k, top_p, q_index)) or int(lazy_rows) > 0
     _proc_args(bias, allowed, top_k, top_p, B, R, V, dev)
     if stopping and "finish" not in out:
         out["finish"] = torch.empty(B, dtype=torch.int32, device=dev)
@@ -266,7 +270,7 @@ def _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
     keep = (target_logits, draft_probs, draft_tokens, uniforms, ws, stream, stop_tokens, budget, bias, allowed,
             top_k, top_p, q_index)
     if processing:
-        opt = _options(stop_tokens, budget, out.get("finish"), bias, allowed, top_k, top_p, q_index)
+        opt = _options(stop_tokens, budget, out.get("finish"), bias, allowed, top_k, top_p, q_index, lazy_rows)
         args = head + (ctypes.byref(opt), _ptr(out["accepted_len"]), _ptr(out["out_tokens"]),
                        _ptr(out["req_status"]), _ptr(out.get("stats")), wp, wn, ctypes.c_void_p(stream.cuda_stream))
         return lib.spec_verify_chain_ex, args, keep + (opt,), out
@@ -286,7 +290,8 @@ def spec_verify_chain(target_logits: torch.Tensor, draft_probs: torch.Tensor,
                       out: Optional[dict] = None, stop_tokens: Optional[torch.Tensor] = None,
                       budget: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
                       allowed: Optional[torch.Tensor] = None, top_k: Optional[torch.Tensor] = None,
-                      top_p: Optional[torch.Tensor] = None, q_index: Optional[torch.Tensor] = None) -> dict:
+                      top_p: Optional[torch.Tensor] = None, q_index: Optional[torch.Tensor] = None,
+                      lazy_rows: int = 0) -> dict:
     """Chain verification by rejection sampling (C entry point spec_verify_chain;
     spec_verify_chain_stop when stop_tokens or budget is given; spec_verify_chain_ex when a
     processor is given).
@@ -296,29 +301,33 @@ def spec_verify_chain(target_logits: torch.Tensor, draft_probs: torch.Tensor,
     stop_tokens [n] int32 (n <= 256); budget [B] int32 remaining output budgets;
     processors: bias [V] fp32, allowed [B, gamma+1, ceil(V/32)] int32 bit words,
     top_k [B] int32, top_p [B] fp32; sparse draft rows: q_index [B, gamma, K] int32 with
-    draft_probs [B, gamma, K] fp32 values (every token not listed has q = 0).
+    draft_probs [B, gamma, K] fp32 values (every token not listed has q = 0); lazy_rows k >= 1:
+    rows read in groups of k, a group only when every draft before it was accepted.
     Returns {accepted_len [B], out_tokens [B, gamma+1], req_status [B], stats?, finish?}
     (int32 / fp32 GPU tensors, valid once the current stream reaches the call).
     """
     fn, args, _, out = _chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
                                    with_stats, workspace_tensor, out, stop_tokens, budget, bias, allowed,
-                                   top_k, top_p, q_index)
+                                   top_k, top_p, q_index, lazy_rows)
     _check(fn(*args))
     return out
 
 
 def prepare_chain(target_logits, draft_probs, draft_tokens, uniforms, temperature, *,
                   with_stats=False, workspace_tensor=None, out=None, stop_tokens=None,
-                  budget=None, bias=None, allowed=None, top_k=None, top_p=None, q_index=None) -> PreparedCall:
+                  budget=None, bias=None, allowed=None, top_k=None, top_p=None, q_index=None,
+                  lazy_rows=0) -> PreparedCall:
     """spec_verify_chain with its arguments checked and marshalled once (see PreparedCall)."""
     return PreparedCall(*_chain_args(target_logits, draft_probs, draft_tokens, uniforms, temperature,
                                      with_stats, workspace_tensor, out, stop_tokens, budget, bias, allowed,
-                                     top_k, top_p, q_index))
+                                     top_k, top_p, q_index, lazy_rows))
 
 
 def _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens=None, budget=None, bias=None,
-                 allowed=None):
+                 allowed=None, lazy_rows=0):
     lib = load_library()
+    if int(lazy_rows) < 0:
+        raise ValueError("lazy_rows must be >= 0")
     _need(target_logits, "target_logits")
     if target_logits.dim() != 3:
         raise ValueError("target_logits must be [B, gamma+1, V]")
@@ -333,7 +342,7 @@ def _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens
                    req_status=torch.empty(B, dtype=torch.int32, device=dev))
     stopping = stop_tokens is not None or budget is not None
     n_stop = _stop_args(stop_tokens, budget, B, dev)
-    processing = bias is not None or allowed is not None
+    processing = bias is not None or allowed is not None or int(lazy_rows) > 0
     _proc_args(bias, allowed, None, None, B, R, V, dev)
     if stopping and "finish" not in out:
         out["finish"] = torch.empty(B, dtype=torch.int32, device=dev)
@@ -346,7 +355,7 @@ def _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens
     keep = (target_logits, draft_tokens, ws, stream, stop_tokens, budget, bias, allowed)
     head = (_ptr(target_logits), lt, _ptr(draft_tokens), B, G, V)
     if processing:
-        opt = _options(stop_tokens, budget, out.get("finish"), bias, allowed)
+        opt = _options(stop_tokens, budget, out.get("finish"), bias, allowed, lazy_rows=lazy_rows)
         args = head + (ctypes.byref(opt), _ptr(out["accepted_len"]), _ptr(out["out_tokens"]),
                        _ptr(out["req_status"]), wp, wn, ctypes.c_void_p(stream.cuda_stream))
         return lib.spec_verify_greedy_ex, args, keep + (opt,), out
@@ -364,25 +373,25 @@ def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor, 
                        workspace_tensor: Optional[torch.Tensor] = None,
                        out: Optional[dict] = None, stop_tokens: Optional[torch.Tensor] = None,
                        budget: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
-                       allowed: Optional[torch.Tensor] = None) -> dict:
+                       allowed: Optional[torch.Tensor] = None, lazy_rows: int = 0) -> dict:
     """Greedy argmax-match verification (C entry point spec_verify_greedy;
     spec_verify_greedy_stop when stop_tokens or budget is given; spec_verify_greedy_ex when
-    bias or allowed is given).
+    bias, allowed or lazy_rows is given).
 
     target_logits [B, gamma+1, V] bf16/fp32; draft_tokens [B, gamma] int32; stop_tokens,
-    budget, bias, allowed as for spec_verify_chain.
+    budget, bias, allowed, lazy_rows as for spec_verify_chain.
     """
     fn, args, _, out = _greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens, budget, bias,
-                                    allowed)
+                                    allowed, lazy_rows)
     _check(fn(*args))
     return out
 
 
 def prepare_greedy(target_logits, draft_tokens, *, workspace_tensor=None, out=None, stop_tokens=None,
-                   budget=None, bias=None, allowed=None) -> PreparedCall:
+                   budget=None, bias=None, allowed=None, lazy_rows=0) -> PreparedCall:
     """spec_verify_greedy with its arguments checked and marshalled once (see PreparedCall)."""
     return PreparedCall(*_greedy_args(target_logits, draft_tokens, workspace_tensor, out, stop_tokens, budget,
-                                      bias, allowed))
+                                      bias, allowed, lazy_rows))
 
 
 def _tree_args(node_logits, node_tokens, parents, uniforms, temperature, workspace_tensor, out):

@@ -135,6 +135,7 @@ spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, con
   if (!sizes_ok(B, gamma, V) || !temperature_ok(temperature) || !stop_ok(o.stop_tokens, o.n_stop))
     return SPEC_EINVAL;
   if (o.q_index && !(o.q_k >= 1 && o.q_k <= SPEC_MAX_SPARSE_K)) return SPEC_EINVAL;
+  if (o.lazy_rows < 0) return SPEC_EINVAL;
   if (!dtype_ok(logit_dtype) || !dtype_ok(q_dtype)) return SPEC_EDTYPE;
   if (o.q_index && q_dtype != SPEC_F32) return SPEC_EDTYPE;
   if (!sv::grid_fits(sv::chain_blocks(B, gamma, V))) return SPEC_EINVAL;
@@ -172,6 +173,9 @@ spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, con
   p.CPW = sl.CPW;
   p.SL = sl.SL;
   p.S2 = chunks(V, sv::kTermChunk);
+  p.LK = (o.lazy_rows >= 1 && o.lazy_rows < gamma + 1) ? o.lazy_rows : gamma + 1;
+  p.J = (gamma + 1 + p.LK - 1) / p.LK;
+  p.LAG = 0;
   p.q_dtype = q_dtype;
   const double c2 = kLog2e / static_cast<double>(temperature);
   p.c2 = static_cast<float>(c2);
@@ -223,7 +227,7 @@ spec_status spec_verify_greedy_ex(const void* target_logits, int logit_dtype, co
                                   int32_t* out_tokens, int32_t* req_status, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
   const spec_verify_options o = opt ? *opt : spec_verify_options{};
-  if (!sizes_ok(B, gamma, V) || !stop_ok(o.stop_tokens, o.n_stop)) return SPEC_EINVAL;
+  if (!sizes_ok(B, gamma, V) || !stop_ok(o.stop_tokens, o.n_stop) || o.lazy_rows < 0) return SPEC_EINVAL;
   if (!dtype_ok(logit_dtype)) return SPEC_EDTYPE;
   if (!sv::grid_fits(sv::greedy_blocks(B, gamma, V))) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
@@ -249,6 +253,8 @@ spec_status spec_verify_greedy_ex(const void* target_logits, int logit_dtype, co
   p.P = sl.P;
   p.CPW = sl.CPW;
   p.SL = sl.SL;
+  p.LK = (o.lazy_rows >= 1 && o.lazy_rows < gamma + 1) ? o.lazy_rows : gamma + 1;
+  p.J = (gamma + 1 + p.LK - 1) / p.LK;
   const bool vec = (V % 8 == 0) && aligned16(target_logits) && (!o.bias || aligned16(o.bias));
   return sv::launch_greedy(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }

@@ -111,7 +111,27 @@ __device__ __forceinline__ void wave_row_summary_proc(const ChainParams& p, size
   wave_softmax_merge(st, p.c2, m_out, z_out);
 }
 
+// Per-row results of a terminal item's decision, kept for the selector's outputs.
+struct RowState {
+  float r[SPEC_MAX_GAMMA + 1];    // reference exponent per row
+  float m[SPEC_MAX_GAMMA + 1];    // raw max per row
+  double z[SPEC_MAX_GAMMA + 1];   // sum 2^(l c2 - r) per row
+  int bad[SPEC_MAX_GAMMA + 1];    // row is all -inf, or holds NaN / +inf
+  double px[SPEC_MAX_GAMMA];      // p_i(x_i) of the reached draft rows
+  double a[SPEC_MAX_GAMMA];       // a_i of the reached draft rows
+};
+
 // Statistics item: slice `slice` of row i of request b.
+// Lazy rows: an item of a row the round never reaches publishes an empty-range summary
+// (-inf, 0) and a zero gather record, which say only that the item is done; the decision
+// never uses them, because an earlier event ends the round.
+__device__ __forceinline__ void stats_skip(const ChainParams& p, int b, int i, int slice) {
+  if (threadIdx.x == 0) {
+    publish_f2(p.part + ((size_t)b * p.R + i) * p.SL + slice, make_float2(-INFINITY, 0.0f));
+    if (slice == 0 && i < p.G) gather_publish(p, b, i, 0u, 0u, 0u);
+  }
+}
+
 template <int DT, int QT, bool VEC, bool PROC>
 __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
   __shared__ float s_wm[kWavesPerBlock], s_wz[kWavesPerBlock];
@@ -167,15 +187,6 @@ __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
   }
 }
 
-// Per-row results of a terminal item's decision, kept for the selector's outputs.
-struct RowState {
-  float r[SPEC_MAX_GAMMA + 1];    // reference exponent per row
-  float m[SPEC_MAX_GAMMA + 1];    // raw max per row
-  double z[SPEC_MAX_GAMMA + 1];   // sum 2^(l c2 - r) per row
-  int bad[SPEC_MAX_GAMMA + 1];    // row is all -inf, or holds NaN / +inf
-  double px[SPEC_MAX_GAMMA];      // p_i(x_i) of the reached draft rows
-  double a[SPEC_MAX_GAMMA];       // a_i of the reached draft rows
-};
 
 // The decision of request b from its published summaries and gather records.  Every
 // terminal item of the request runs this on the same words and takes the same decision,
@@ -183,7 +194,9 @@ struct RowState {
 // it with no block barrier until the end: lane l holds the summaries of one (row, slice)
 // pair per pass -- rows in groups of S = 2^ceil(log2 SL) lanes (at most 64, lanes then
 // looping over slices) -- and a row's maximum and normalizer come from segmented DPP
-// reductions over its group.
+// reductions over its group.  With [lo, nr) != [0, R) only rows lo..nr-1 and drafts lo..nr-1
+// are read (the gate of a lazy row group): then only `ev`, `H` and an INTERNAL status are
+// meaningful.
 __device__ __forceinline__ int seg_lanes(int SL) {
   int S = 1;
   while (S < SL && S < kWave) S <<= 1;
@@ -191,7 +204,7 @@ __device__ __forceinline__ int seg_lanes(int SL) {
 }
 
 template <int DT>
-__device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDecision& s_dec) {
+__device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDecision& s_dec, int lo, int nr) {
   if (wave_id() != 0) {
     __syncthreads();
     return;
@@ -200,6 +213,7 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
   const int lane = threadIdx.x & (kWave - 1);
   const float c2 = p.c2;
   const int G = p.G, R = p.R, SL = p.SL;
+  const int nd = min(G, nr);                    // drafts decided
   const float2* part_b = p.part + (size_t)b * R * SL;
   const auto* words = reinterpret_cast<const unsigned long long*>(part_b);
 
@@ -207,7 +221,8 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
   // the budget, and lane l's stop entries l, l + 64, ...
   unsigned long long g[3] = {0ull, 0ull, 0ull};
   float ui = 0.0f;
-  if (lane < G) {
+  const bool dl = lane >= lo && lane < nd;      // this lane's draft is decided
+  if (dl) {
     const unsigned long long* rec = gather_rec(p, b, lane);
 #pragma unroll
     for (int k = 0; k < 3; ++k) g[k] = fetch_u64(rec + k);
@@ -227,9 +242,9 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
   const int S = seg_lanes(SL), rows_per_pass = kWave / S, tpl = (SL + S - 1) / S;
   const int srow = lane / S, sj = lane & (S - 1);
   bool lost = false;
-  for (int pass = 0; pass * rows_per_pass < R; ++pass) {
+  for (int pass = lo / rows_per_pass; pass * rows_per_pass < nr; ++pass) {
     const int i = pass * rows_per_pass + srow;   // this lane's row
-    const bool rv = i < R;
+    const bool rv = i >= lo && i < nr;
     auto slice_ok = [&](int t) { return rv && sj + S * t < SL; };
     auto word = [&](int t) { return words + (size_t)i * SL + sj + S * t; };
     unsigned long long v[kPre];
@@ -280,7 +295,7 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
       rs.bad[i] = !(isfinite(z) && z > 0.0);
     }
   }
-  if (lane < G) {
+  if (dl) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       if (g[k] == 0ull) g[k] = await_u64(gather_rec(p, b, lane) + k);
@@ -296,7 +311,7 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
   const int x = static_cast<int>(static_cast<unsigned>(g[0]));
   unsigned long long hits = 0ull;
   if (n_stop > 0) {
-    for (int i = 0; i < G; ++i) {
+    for (int i = lo; i < nd; ++i) {
       const int xi = __builtin_amdgcn_readlane(x, i);
       bool h = false;
 #pragma unroll
@@ -310,7 +325,7 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
   int code = 0, fin = 0;
   bool reject = false;
   double px = NAN, a = NAN;
-  if (lane < G) {
+  if (dl) {
     if (rs.bad[lane]) {
       code = SPEC_REQ_NONFINITE;
     } else if (x < 0 || x >= p.V) {
@@ -335,7 +350,7 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
     rs.px[lane] = px;
     rs.a[lane] = a;
   }
-  const unsigned long long ev = __ballot(lane < G && (code != 0 || reject || fin != 0));
+  const unsigned long long ev = __ballot(dl && (code != 0 || reject || fin != 0));
   const int e = ev ? (__ffsll((long long)ev) - 1) : G;   // the first event
   const int code_e = __shfl(code, e < G ? e : 0, kWave);
   const int fin_e = __shfl(fin, e < G ? e : 0, kWave);
@@ -345,7 +360,7 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
     draw = 0;
     finish = fin_e;
   } else {
-    status = e < G ? code_e : (rs.bad[G] ? SPEC_REQ_NONFINITE : 0);
+    status = e < G ? code_e : (nr > G && rs.bad[G] ? SPEC_REQ_NONFINITE : 0);
     if (status == 0 && !(ut >= 0.0f && ut < 1.0f)) status = SPEC_REQ_BADUNIFORM;
   }
   if (H <= 0) {                       // no budget left: no round, nothing checked
@@ -357,7 +372,8 @@ __device__ void chain_decide(const ChainParams& p, int b, RowState& rs, ChainDec
   if (timeout) status = SPEC_REQ_INTERNAL;
   const float tau_a = __shfl(tau_lane, A < R ? A : 0, kWave);
   if (lane == 0) {
-    const bool drawn = status == 0 && draw;
+    const bool drawn = status == 0 && draw && A < nr;
+    s_dec.ev = e;
     s_dec.tau = tau_a;
     s_dec.A = status == 0 ? A : -1;
     s_dec.status = status;
@@ -683,11 +699,9 @@ __device__ void terminal_body(const ChainParams& p, int b, int c, const ChainDec
   chain_clear(p, b);
 }
 
+// Terminal item with the request's decision taken (chain_decide over every row).
 template <int DT, int QT, bool VEC, bool PROC>
-__device__ void terminal_item(const ChainParams& p, int b, int c) {
-  __shared__ RowState s_rs;
-  __shared__ ChainDecision s_dec;
-  chain_decide<DT>(p, b, s_rs, s_dec);
+__device__ void terminal_item(const ChainParams& p, int b, int c, RowState& s_rs, ChainDecision& s_dec) {
   const ChainDecision d = s_dec;
   if (d.status != 0 || !d.draw) {
     if (c != p.S2 - 1) {
@@ -705,25 +719,49 @@ __device__ void terminal_item(const ChainParams& p, int b, int c) {
   else terminal_body<DT, QT, VEC, false, PROC>(p, b, c, d, s_rs);
 }
 
-// Block order: groups g = 0 .. B + LAG - 1, group g holding the statistics items of
-// request g (if g < B) followed by the terminal items of request g - LAG (if g >= LAG), so a
-// request's terminal items follow its statistics items by LAG requests' worth of blocks.
-// LAG = B puts every statistics item first.
+// Block order: groups g = 0 .. B + L - 1, group g holding the Sb statistics items of
+// request g (if g < B) followed by the Tb terminal items of request g - L (if g >= L), so a
+// request's terminal items follow its statistics items by L requests' worth of blocks.
+// L = B puts every statistics item first.  32-bit arithmetic: a grid holds fewer than
+// 2^24 blocks.
 struct Item { int terminal, b, idx; };
-__device__ __forceinline__ Item block_item(const ChainParams& p, long t) {
-  const long Sb = (long)p.R * p.SL, Tb = p.S2, L = p.LAG;
-  const long n1 = L * Sb, n2 = ((long)p.B - L) * (Sb + Tb);
+__host__ __device__ __forceinline__ Item tail_item(unsigned t, unsigned B, unsigned Sb, unsigned Tb, unsigned L) {
+  const unsigned n1 = L * Sb, n2 = (B - L) * (Sb + Tb);
   Item it;
   if (t < n1) {
-    it.terminal = 0; it.b = (int)(t / Sb); it.idx = (int)(t % Sb);
+    it.terminal = 0; it.b = (int)(t / Sb); it.idx = (int)(t - (unsigned)it.b * Sb);
   } else if (t < n1 + n2) {
-    const long u = t - n1, g = L + u / (Sb + Tb), o = u % (Sb + Tb);
-    if (o < Sb) { it.terminal = 0; it.b = (int)g; it.idx = (int)o; }
-    else { it.terminal = 1; it.b = (int)(g - L); it.idx = (int)(o - Sb); }
+    const unsigned u = t - n1, k = u / (Sb + Tb), o = u - k * (Sb + Tb);
+    if (o < Sb) { it.terminal = 0; it.b = (int)(L + k); it.idx = (int)o; }
+    else { it.terminal = 1; it.b = (int)k; it.idx = (int)(o - Sb); }
   } else {
-    const long u = t - n1 - n2;
-    it.terminal = 1; it.b = (int)((long)p.B - L + u / Tb); it.idx = (int)(u % Tb);
+    const unsigned u = t - n1 - n2, k = u / Tb;
+    it.terminal = 1; it.b = (int)(B - L + k); it.idx = (int)(u - k * Tb);
   }
+  return it;
+}
+
+__host__ __device__ __forceinline__ Item block_item(const ChainParams& p, unsigned t) {
+  return tail_item(t, p.B, (unsigned)(p.R * p.SL), p.S2, p.LAG);
+}
+
+// Lazy-rows order: row group j (rows [j LK, (j + 1) LK)) of every request, for j = 0 .. J-2
+// in turn, then the last group interleaved with the terminal items as above.  A group's
+// items thus follow every item of the request's earlier groups.  (Interleaving the earlier
+// groups with lags as well measured slower: their gates and the terminal items then hold
+// slots that the first group's stream needs.)
+__host__ __device__ __forceinline__ Item lazy_item(const ChainParams& p, unsigned t) {
+  const unsigned B = p.B, SL = p.SL, LK = p.LK, J = p.J;
+  const unsigned nG = LK * SL, layer = B * nG, early = (J - 1) * layer;
+  Item it;
+  if (t < early) {
+    const unsigned j = t / layer, u = t - j * layer, b = u / nG;
+    it.terminal = 0; it.b = (int)b; it.idx = (int)(j * nG + (u - b * nG));
+    return it;
+  }
+  const unsigned first = (J - 1) * LK;   // the last group's first row
+  it = tail_item(t - early, B, ((unsigned)p.R - first) * SL, p.S2, p.LAG);
+  if (!it.terminal) it.idx += (int)(first * SL);
   return it;
 }
 
@@ -737,9 +775,36 @@ __global__ __launch_bounds__(kBlock, SPEC_CHAIN_WAVES_PER_EU) void chain_kernel(
 #else
 __global__ __launch_bounds__(kBlock) void chain_kernel(ChainParams p) {
 #endif
-  const Item it = block_item(p, blockIdx.x);
-  if (it.terminal) terminal_item<DT, QT, VEC, PROC>(p, it.b, it.idx);
-  else stats_item<DT, QT, VEC, PROC>(p, it.b, it.idx / p.SL, it.idx % p.SL);
+  __shared__ RowState s_rs;
+  __shared__ ChainDecision s_dec;
+  const Item it = p.J > 1 ? lazy_item(p, blockIdx.x) : block_item(p, blockIdx.x);
+  const int row = it.idx / p.SL;
+  // the rows whose words this block's decision reads: every row for a terminal item; for
+  // a lazy row group after the first, the rows of the group before it (whether the round
+  // reaches this group)
+  // (a group is reached when the group before it was and none of that group's drafts ends
+  // the round: a skipped group's words read as all -inf rows, an event at its first draft)
+  int lo = 0, nr = 0;
+  bool reached = true;
+  if (it.terminal) {
+    nr = p.R;
+  } else if (p.J > 1) {
+    const int first = (row / p.LK) * p.LK;
+    if (first == 0) reached = p.st.budget == nullptr || p.st.budget[it.b] > 0;
+    else { lo = first - p.LK; nr = first; }
+  }
+  if (nr > 0) chain_decide<DT>(p, it.b, s_rs, s_dec, lo, nr);   // one call site: inlined once
+  if (it.terminal) {
+    terminal_item<DT, QT, VEC, PROC>(p, it.b, it.idx, s_rs, s_dec);
+    return;
+  }
+  if (nr > 0) {
+    // a gate that timed out answers yes, so that no row the terminal items may need is skipped
+    const ChainDecision d = s_dec;
+    reached = d.status == SPEC_REQ_INTERNAL || (d.ev >= nr && d.H > 0);
+  }
+  if (reached) stats_item<DT, QT, VEC, PROC>(p, it.b, row, it.idx % p.SL);
+  else stats_skip(p, it.b, row, it.idx % p.SL);
 }
 
 // Lag between a request's statistics and terminal items, in rounds of resident blocks:
@@ -750,6 +815,12 @@ __global__ __launch_bounds__(kBlock) void chain_kernel(ChainParams p) {
 #define SPEC_CHAIN_LAG_TENTHS 20
 #endif
 constexpr long kLagTenths = SPEC_CHAIN_LAG_TENTHS;   // in tenths of a round
+// Lazy rows: lag between a request's last row group and its terminal items, in tenths of
+// a round.
+#ifndef SPEC_LAZY_LAG_TENTHS
+#define SPEC_LAZY_LAG_TENTHS 10
+#endif
+constexpr long kLazyLagTenths = SPEC_LAZY_LAG_TENTHS;
 
 // Blocks resident per CU: 0 leaves it to the register count; k > 0 reserves LDS so that
 // at most k blocks share a CU (fewer loads in flight: shorter queues, so the decision's
@@ -761,25 +832,28 @@ constexpr int kBlocksPerCU = SPEC_CHAIN_BLOCKS_PER_CU;
 constexpr size_t kLdsPerCU = 160 * 1024;
 constexpr size_t chain_dyn_lds() { return kBlocksPerCU > 0 ? kLdsPerCU / kBlocksPerCU - 12 * 1024 : 0; }
 
+// A lag of `tenths` tenths of a round of resident blocks, in requests (at most B); a
+// non-positive setting gives B (every earlier layer first).
+inline long lag_requests(long tenths, long resident, long per_req, long B) {
+  if (tenths <= 0) return B;
+  const long lag = (tenths * resident / 10 + per_req - 1) / per_req;
+  return lag > B ? B : lag;
+}
+
 template <int DT, int QT, bool VEC, bool PROC>
 hipError_t launch_typed(ChainParams p, hipStream_t s) {
-  long lag = p.B;
-  if (kLagTenths > 0) {
-    static int s_resident[64] = {0};   // resident blocks per device ordinal; 0 = not queried
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (s_resident[dev] == 0) {
-      int per_cu = 0, cus = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel<DT, QT, VEC, PROC>, kBlock, chain_dyn_lds()) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return hipErrorInvalidValue;
-      s_resident[dev] = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
-    }
-    const long per_req = (long)p.R * p.SL + p.S2;
-    lag = (kLagTenths * s_resident[dev] / 10 + per_req - 1) / per_req;
-    if (lag > p.B) lag = p.B;
+  static int s_resident[64] = {0};   // resident blocks per device ordinal; 0 = not queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (s_resident[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel<DT, QT, VEC, PROC>, kBlock, chain_dyn_lds()) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidValue;
+    s_resident[dev] = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
   }
-  p.LAG = (int)lag;
+  const long per_req = (long)p.R * p.SL + p.S2;
+  p.LAG = (int)lag_requests(p.J > 1 ? kLazyLagTenths : kLagTenths, s_resident[dev], per_req, p.B);
   const unsigned long long blocks = (unsigned long long)p.B * ((unsigned long long)p.R * p.SL + p.S2);  // == chain_blocks
   chain_kernel<DT, QT, VEC, PROC><<<dim3((unsigned)blocks), dim3(kBlock), chain_dyn_lds(), s>>>(p);
   return hipGetLastError();

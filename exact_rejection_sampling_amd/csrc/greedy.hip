@@ -97,34 +97,43 @@ __device__ void stream_item(const GreedyParams& p, int b, int i, int slice) {
   }
 }
 
-// Decider of request b.
-__device__ void greedy_decide(const GreedyParams& p, int b) {
+// Decision of request b over rows [lo, nr) and drafts [lo, min(nr, gamma)).  The decider
+// of the request reads every row (lo = 0, nr = gamma + 1), writes the outputs and returns
+// the summaries to zero.  With nr < gamma + 1 it is the gate of a lazy row group (rows
+// [nr, ...)): it returns, block-uniformly, whether the round reaches row nr -- the rows
+// [lo, nr) were read (a skipped group's summaries read as NaN rows, an event at its first
+// draft) and none of their drafts ends the round -- and changes nothing.  A gate whose
+// words did not arrive answers yes, so that no row the decider may need is skipped.
+__device__ bool greedy_decide(const GreedyParams& p, int b, int lo, int nr) {
   __shared__ int s_arg[SPEC_MAX_GAMMA + 1];
   __shared__ int s_bad[SPEC_MAX_GAMMA + 1];
   __shared__ int s_lost;
   __shared__ int s_x[SPEC_MAX_GAMMA];           // the drafts, for the stop-token test
   __shared__ int s_stop[SPEC_MAX_STOP];         // the stop tokens, for the target token's test
   __shared__ unsigned s_hit[2];                 // bit i: draft i is a stop token
+  __shared__ int s_reach;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+  const bool gate = nr < p.R;
+  const int G = p.G, nd = min(G, nr);
   unsigned long long* part_b = p.part + (size_t)b * p.R * p.SL;
   if (tid == 0) s_lost = 0;
   // wave 0's draft tokens and the remaining budget, fetched while the summaries are awaited
   int x = 0;
-  if (wave == 0 && lane < p.G) x = p.tokens[(size_t)b * p.G + lane];
+  if (wave == 0 && lane < G) x = p.tokens[(size_t)b * G + lane];
   const int H = p.st.budget ? p.st.budget[b] : INT32_MAX;
   const bool stops = p.st.n_stop > 0;
   const int my_stop = stops && tid < p.st.n_stop ? p.st.stop[tid] : 0;
   if (stops) {
-    if (wave == 0 && lane < p.G) s_x[lane] = x;
+    if (wave == 0 && lane < G) s_x[lane] = x;
     if (tid < p.st.n_stop) s_stop[tid] = my_stop;
     if (tid < 2) s_hit[tid] = 0u;
   }
   __syncthreads();
-  // stop tokens: thread t < n_stop tests entry t against every draft
+  // stop tokens: thread t < n_stop tests entry t against every decided draft
   if (stops && tid < p.st.n_stop)
-    for (int i = 0; i < p.G; ++i)
+    for (int i = lo; i < nd; ++i)
       if (s_x[i] == my_stop) atomicOr(&s_hit[i >> 5], 1u << (i & 31));
-  for (int i = wave; i < p.R; i += kWavesPerBlock) {
+  for (int i = lo + wave; i < nr; i += kWavesPerBlock) {
     const unsigned long long* part = part_b + (size_t)i * p.SL;
     float m = -INFINITY;
     int idx = 0x7fffffff;
@@ -152,14 +161,14 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
   }
   __syncthreads();
   // the summaries are consumed: return them to zero (every call leaves the workspace zeroed)
-  for (int j = tid; j < p.R * p.SL; j += kBlock) clear_u64(part_b + j);
-  if (wave != 0) return;
-  const int G = p.G;
-  // lane i < G: draft position i; a matching draft that is a stop token, or that uses up
-  // the budget, ends the round after itself ([Tiny] "Normative greedy pseudocode")
+  if (!gate)
+    for (int j = tid; j < p.R * p.SL; j += kBlock) clear_u64(part_b + j);
+  // lane i in [lo, nd): draft position i; a matching draft that is a stop token, or that
+  // uses up the budget, ends the round after itself ([Tiny] "Normative greedy pseudocode")
   int code = 0, fin = 0;
   bool mismatch = false;
-  if (lane < G) {
+  const bool dl = wave == 0 && lane >= lo && lane < nd;
+  if (dl) {
     if (s_bad[lane]) {
       code = SPEC_REQ_NONFINITE;
     } else if (x < 0 || x >= p.V) {
@@ -172,8 +181,14 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
       }
     }
   }
-  const unsigned long long ev = __ballot(lane < G && (code != 0 || mismatch || fin != 0));
+  const unsigned long long ev = __ballot(dl && (code != 0 || mismatch || fin != 0));
   const int e = ev ? (__ffsll((long long)ev) - 1) : G;   // the first event
+  if (gate) {
+    if (tid == 0) s_reach = s_lost || (e >= nr && H > 0);
+    __syncthreads();
+    return s_reach != 0;
+  }
+  if (wave != 0) return false;
   const int code_e = __shfl(code, e < G ? e : 0, kWave);
   const int fin_e = __shfl(fin, e < G ? e : 0, kWave);
   int A = e, status = 0, finish = 0;
@@ -211,32 +226,73 @@ __device__ void greedy_decide(const GreedyParams& p, int b) {
     p.req_status[b] = status;
     if (p.st.finish) p.st.finish[b] = status == 0 ? finish : 0;
   }
+  return false;
 }
 
-// Block order: groups g = 0 .. B + LAG - 1, group g holding the streaming items of
-// request g (if g < B) followed by the decider of request g - LAG (if g >= LAG).
+// Block order: groups g = 0 .. B + L - 1, group g holding the Sb streaming items of
+// request g (if g < B) followed by the decider of request g - L (if g >= L).  32-bit
+// arithmetic: a grid holds fewer than 2^24 blocks.
 struct Item { int decider, b, idx; };
-__device__ __forceinline__ Item block_item(const GreedyParams& p, long t) {
-  const long Sb = (long)p.R * p.SL, L = p.LAG;
-  const long n1 = L * Sb, n2 = ((long)p.B - L) * (Sb + 1);
+__host__ __device__ __forceinline__ Item tail_item(unsigned t, unsigned B, unsigned Sb, unsigned L) {
+  const unsigned n1 = L * Sb, n2 = (B - L) * (Sb + 1);
   Item it;
   if (t < n1) {
-    it.decider = 0; it.b = (int)(t / Sb); it.idx = (int)(t % Sb);
+    it.decider = 0; it.b = (int)(t / Sb); it.idx = (int)(t - (unsigned)it.b * Sb);
   } else if (t < n1 + n2) {
-    const long u = t - n1, g = L + u / (Sb + 1), o = u % (Sb + 1);
-    if (o < Sb) { it.decider = 0; it.b = (int)g; it.idx = (int)o; }
-    else { it.decider = 1; it.b = (int)(g - L); it.idx = 0; }
+    const unsigned u = t - n1, k = u / (Sb + 1), o = u - k * (Sb + 1);
+    if (o < Sb) { it.decider = 0; it.b = (int)(L + k); it.idx = (int)o; }
+    else { it.decider = 1; it.b = (int)k; it.idx = 0; }
   } else {
-    it.decider = 1; it.b = (int)((long)p.B - L + (t - n1 - n2)); it.idx = 0;
+    it.decider = 1; it.b = (int)(B - L + (t - n1 - n2)); it.idx = 0;
   }
+  return it;
+}
+
+// Lazy rows: row group j (rows [j LK, (j + 1) LK)) of every request, for j = 0 .. J-2 in
+// turn, then the last group interleaved with the deciders as above; with J = 1 this is the
+// order above.  A group's items follow every item of the request's earlier groups.
+__host__ __device__ __forceinline__ Item block_item(const GreedyParams& p, unsigned t) {
+  const unsigned B = p.B, SL = p.SL, LK = p.LK, J = p.J;
+  const unsigned nG = LK * SL, layer = B * nG, early = (J - 1) * layer;
+  Item it;
+  if (t < early) {
+    const unsigned j = t / layer, u = t - j * layer, b = u / nG;
+    it.decider = 0; it.b = (int)b; it.idx = (int)(j * nG + (u - b * nG));
+    return it;
+  }
+  const unsigned first = (J - 1) * LK;   // the last group's first row
+  it = tail_item(t - early, B, ((unsigned)p.R - first) * SL, p.LAG);
+  if (!it.decider) it.idx += (int)(first * SL);
   return it;
 }
 
 template <int DT, bool VEC, bool PROC>
 __global__ __launch_bounds__(kBlock) void greedy_kernel(GreedyParams p) {
   const Item it = block_item(p, blockIdx.x);
-  if (it.decider) greedy_decide(p, it.b);
-  else stream_item<DT, VEC, PROC>(p, it.b, it.idx / p.SL, it.idx % p.SL);
+  const int row = it.idx / p.SL;
+  // the rows a decision reads: every row for a decider; for a lazy row group after the
+  // first, the rows of the group before it (whether the round reaches this group)
+  int lo = 0, nr = 0;
+  bool reached = true;
+  if (it.decider) {
+    nr = p.R;
+  } else if (p.J > 1) {
+    const int first = (row / p.LK) * p.LK;
+    if (first == 0) reached = p.st.budget == nullptr || p.st.budget[it.b] > 0;
+    else { lo = first - p.LK; nr = first; }
+  }
+  if (nr > 0) {
+    const bool r = greedy_decide(p, it.b, lo, nr);   // one call site: inlined once
+    if (it.decider) return;
+    reached = r;
+  }
+  if (reached) {
+    stream_item<DT, VEC, PROC>(p, it.b, row, it.idx % p.SL);
+  } else if (threadIdx.x == 0) {
+    // a row the round never reaches: a NaN summary, which the decision never uses (an
+    // earlier event ends the round), says only that this item is done
+    publish_u64(p.part + ((size_t)it.b * p.R + row) * p.SL + it.idx % p.SL, pack_argmax(__uint_as_float(0x7fc00000u), 0));
+  }
 }
 
 // Lag between a request's streaming items and its decider, in tenths of a round of

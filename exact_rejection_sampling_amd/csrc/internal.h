@@ -21,6 +21,8 @@ struct ChainDecision {
   float r_ref;      // reference exponent of the terminal row: fp32(max logit * c2)
   float inv_z;      // 1 / Z of the terminal row (Z relative to r_ref, base 2)
   float tau;        // keep threshold of the terminal row (processors; -inf otherwise)
+  int32_t ev;       // first event (error, rejection, stop, budget) among the drafts read
+                    // (gamma if none)
 };
 
 // Stop tokens and output budget of a round (spec_verify_*_stop); n_stop = 0 and a null
@@ -67,6 +69,9 @@ struct ChainParams {
   int SL;                    // statistics slices (blocks) per row = ceil(P / (4 * CPW))
   int S2;                    // terminal chunks per row = ceil(V / kTermChunk)
   int LAG;                   // requests between a request's statistics and terminal items
+  // lazy rows: rows are read in groups of LK (J groups; J = 1: every row read); group j > 0
+  // of a request is read only when its drafts before row j * LK were all accepted
+  int LK, J;
   int q_dtype;
   float c2;                  // fp32(log2(e) / T)
   double inv_t;              // 1 / T, T widened exactly from fp32
@@ -95,6 +100,7 @@ struct GreedyParams {
   unsigned long long* part;  // [B*R*SL] packed GreedyPart, one per slice
   int B, G, R, V, P, CPW, SL;
   int LAG;                   // requests between a request's streaming blocks and its decider
+  int LK, J;                 // lazy rows: groups of LK rows, J groups (as for the chain)
 };
 
 #ifdef SPEC_FORCE_CPW

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 1
+#define SPEC_ABI_VERSION 2
 
 /* Limits checked on the host. */
 #define SPEC_MAX_BATCH  (1 << 22)   /* B */
@@ -212,6 +212,13 @@ spec_status spec_verify_chain_stop(const void* target_logits, int logit_dtype,
  *   reads of each row from cache); bias and the mask are applied where the verifier reads
  *   logits, at no extra pass.  The greedy verifier applies bias and the mask (truncations
  *   never move the argmax) and ignores top_k and top_p.
+ * Lazy rows ([M7.1] §0x03G: the round stops at the first rejection, and every later row
+ * is discarded): with lazy_rows = k >= 1, rows 0..k-1 of every request are read (none when
+ * the budget is 0), and rows jk..jk+k-1 (j >= 1) only when drafts 0..jk-1 were all
+ * accepted without a stop or budget end (greedy: matched the target argmax).  The outputs
+ * equal those of lazy_rows = 0 (statistics are only reported for reached rows either way);
+ * fewer bytes are read when rejections come early, at the cost of one dependent wait per
+ * group.  Negative values are SPEC_EINVAL; k >= gamma + 1 is one group (every row).
  */
 typedef struct {
   const int32_t* stop_tokens;   /* [n_stop] stop tokens (as for spec_verify_chain_stop) */
@@ -227,6 +234,9 @@ typedef struct {
                                    rows; draft_probs then holds [B, gamma, q_k] fp32 values
                                    (q_dtype SPEC_F32) and every token not listed has q = 0 */
   int32_t q_k;                  /* 1 .. SPEC_MAX_SPARSE_K when q_index is given */
+  int32_t lazy_rows;            /* 0 reads every row; k >= 1 reads the rows in groups of
+                                   k, a group only when every draft before it was
+                                   accepted (see above) */
 } spec_verify_options;
 
 /* Chain verification with options (spec_verify_options); every other argument and the
@@ -268,8 +278,8 @@ spec_status spec_verify_greedy_stop(const void* target_logits, int logit_dtype,
                                     int32_t* finish, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
-/* Greedy verification with options (stop tokens, budget, bias and mask; top_k and top_p
- * are ignored); the workspace is that of spec_verify_greedy. */
+/* Greedy verification with options (stop tokens, budget, bias and mask, lazy rows; top_k,
+ * top_p and q_index are ignored); the workspace is that of spec_verify_greedy. */
 spec_status spec_verify_greedy_ex(const void* target_logits, int logit_dtype,
                                   const int32_t* draft_tokens, int B, int gamma, int V,
                                   const spec_verify_options* opt,

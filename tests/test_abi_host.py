@@ -36,7 +36,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_abi_version_and_strings():
     lib = sv.load_library()
-    assert lib.spec_abi_version() == 1
+    assert lib.spec_abi_version() == 2
     for c in range(6):
         assert lib.spec_status_string(c)
     for c in range(8):
@@ -187,3 +187,12 @@ def test_options_entry_points_host_validation():
     assert c(ctypes.byref(bad)) == EINVAL and c(None, B=0) == OK
     g = lambda opt: lib.spec_verify_greedy_ex(FAKE, 1, FAKE, 2, 2, 16, opt, FAKE, FAKE, FAKE, NULL, 0, NULL)
     assert g(None) == EWORKSPACE and g(ctypes.byref(bad)) == EINVAL
+    sparse = SpecOptions()
+    sparse.q_index, sparse.q_k = FAKE, 0
+    assert c(ctypes.byref(sparse)) == EINVAL
+    lazy = SpecOptions()
+    lazy.lazy_rows = -1
+    assert c(ctypes.byref(lazy)) == EINVAL
+    for k in (1, 3, 100):
+        lazy.lazy_rows = k
+        assert c(ctypes.byref(lazy)) == EWORKSPACE
