@@ -818,7 +818,7 @@ constexpr long kLagTenths = SPEC_CHAIN_LAG_TENTHS;   // in tenths of a round
 // Lazy rows: lag between a request's last row group and its terminal items, in tenths of
 // a round.
 #ifndef SPEC_LAZY_LAG_TENTHS
-#define SPEC_LAZY_LAG_TENTHS 10
+#define SPEC_LAZY_LAG_TENTHS 20
 #endif
 constexpr long kLazyLagTenths = SPEC_LAZY_LAG_TENTHS;
 
