@@ -387,6 +387,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary", default="all",
+                    help="comma-separated secondary lines to run (greedy, tree, tree_residual, tree_greedy, "
+                         "chain_stop, chain_bias_mask, chain_processors, chain_lazy, chain_f32, greedy_lazy), or all")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -436,38 +439,36 @@ def main():
                       mean_accepted=c["mean_acc"]),
     )
     if not args.no_secondary:
-        log("[bench] greedy workload")
-        line["secondary"] = dict(greedy=bench_greedy(args, torch, sv, synth))
-        torch.cuda.empty_cache()
-        log("[bench] tree workload")
-        line["secondary"]["tree"] = bench_tree(args, torch, sv, synth)
-        torch.cuda.empty_cache()
-        log("[bench] tree with residual updates")
-        line["secondary"]["tree_residual"] = bench_tree_residual(args, torch, sv, synth)
-        torch.cuda.empty_cache()
-        log("[bench] greedy tree")
-        line["secondary"]["tree_greedy"] = bench_tree_greedy(args, torch, sv, synth)
-        torch.cuda.empty_cache()
-        log("[bench] chain with stop tokens and budgets")
-        line["secondary"]["chain_stop"] = bench_chain_stop(args, torch, sv, synth)
-        torch.cuda.empty_cache()
-        log("[bench] chain with bias and masks")
-        line["secondary"]["chain_bias_mask"] = bench_chain_proc(args, torch, sv, synth, False)
-        torch.cuda.empty_cache()
-        log("[bench] chain with every processor")
-        line["secondary"]["chain_processors"] = bench_chain_proc(args, torch, sv, synth, True)
+        want = None if args.secondary == "all" else set(args.secondary.split(","))
+        sec = line["secondary"] = {}
+
+        def run(name, key, what, fn):
+            if want is not None and name not in want:
+                return
+            torch.cuda.empty_cache()
+            log(f"[bench] {what}")
+            sec[key] = fn()
+
+        run("greedy", "greedy", "greedy workload", lambda: bench_greedy(args, torch, sv, synth))
+        run("tree", "tree", "tree workload", lambda: bench_tree(args, torch, sv, synth))
+        run("tree_residual", "tree_residual", "tree with residual updates",
+            lambda: bench_tree_residual(args, torch, sv, synth))
+        run("tree_greedy", "tree_greedy", "greedy tree", lambda: bench_tree_greedy(args, torch, sv, synth))
+        run("chain_stop", "chain_stop", "chain with stop tokens and budgets",
+            lambda: bench_chain_stop(args, torch, sv, synth))
+        run("chain_bias_mask", "chain_bias_mask", "chain with bias and masks",
+            lambda: bench_chain_proc(args, torch, sv, synth, False))
+        run("chain_processors", "chain_processors", "chain with every processor",
+            lambda: bench_chain_proc(args, torch, sv, synth, True))
         for k in (3, 2):
-            torch.cuda.empty_cache()
-            log(f"[bench] chain with lazy rows, groups of {k}")
-            line["secondary"][f"chain_lazy{k}"] = bench_chain_lazy(args, torch, sv, synth, k)
+            run("chain_lazy", f"chain_lazy{k}", f"chain with lazy rows, groups of {k}",
+                lambda: bench_chain_lazy(args, torch, sv, synth, k))
         for k in (0, 3):
-            torch.cuda.empty_cache()
-            log(f"[bench] chain, fp32 logits, lazy rows {k}")
-            line["secondary"][f"chain_f32_lazy{k}"] = bench_chain_lazy(args, torch, sv, synth, k, fp32=True)
+            run("chain_f32", f"chain_f32_lazy{k}", f"chain, fp32 logits, lazy rows {k}",
+                lambda: bench_chain_lazy(args, torch, sv, synth, k, fp32=True))
         for k in (3, 2, 1):
-            torch.cuda.empty_cache()
-            log(f"[bench] greedy with lazy rows, groups of {k}")
-            line["secondary"][f"greedy_lazy{k}"] = bench_greedy_lazy(args, torch, sv, synth, k)
+            run("greedy_lazy", f"greedy_lazy{k}", f"greedy with lazy rows, groups of {k}",
+                lambda: bench_greedy_lazy(args, torch, sv, synth, k))
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
