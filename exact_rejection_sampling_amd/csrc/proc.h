@@ -20,30 +20,45 @@ __device__ __forceinline__ float proc_elem(float l, float b, bool allowed, float
   return (allowed && s >= tau) ? s : -INFINITY;
 }
 
-// Processors over this lane's 8 elements [e0, e0 + 8) of row `row` (e0 a multiple of 8, so
-// the 8 mask bits lie in one word).  Elements at or past V are left as they are.
-template <bool VEC>
-__device__ __forceinline__ void proc8(const ProcSpec& pr, size_t row, float tau, long e0, long V, float (&v)[8]) {
+// The processor inputs of 8 elements [e0, e0 + 8) of row `row` (e0 a multiple of 8, so the
+// 8 mask bits lie in one word): the bias values and the allowed bits.
+struct Proc8In {
   float b[8];
+  unsigned bits;
+};
+template <bool VEC>
+__device__ __forceinline__ void proc8_load(const ProcSpec& pr, size_t row, long e0, long V, Proc8In& in) {
   if (pr.bias) {
     if (VEC && e0 + 8 <= V) {
       const f32x4 lo = *reinterpret_cast<const f32x4*>(pr.bias + e0);
       const f32x4 hi = *reinterpret_cast<const f32x4*>(pr.bias + e0 + 4);
-      b[0] = lo.x; b[1] = lo.y; b[2] = lo.z; b[3] = lo.w;
-      b[4] = hi.x; b[5] = hi.y; b[6] = hi.z; b[7] = hi.w;
+      in.b[0] = lo.x; in.b[1] = lo.y; in.b[2] = lo.z; in.b[3] = lo.w;
+      in.b[4] = hi.x; in.b[5] = hi.y; in.b[6] = hi.z; in.b[7] = hi.w;
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = e0 + j < V ? pr.bias[e0 + j] : 0.0f;
+      for (int j = 0; j < 8; ++j) in.b[j] = e0 + j < V ? pr.bias[e0 + j] : 0.0f;
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = 0.0f;
+    for (int j = 0; j < 8; ++j) in.b[j] = 0.0f;
   }
-  unsigned bits = 0xffu;
-  if (pr.allowed && e0 < V) bits = (pr.allowed[row * pr.W + (e0 >> 5)] >> (e0 & 31)) & 0xffu;
+  in.bits = 0xffu;
+  if (pr.allowed && e0 < V) in.bits = (pr.allowed[row * pr.W + (e0 >> 5)] >> (e0 & 31)) & 0xffu;
+}
+
+// Processors applied to 8 loaded logits; elements at or past V are left as they are.
+__device__ __forceinline__ void proc8_apply(const Proc8In& in, float tau, long e0, long V, float (&v)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    if (e0 + j < V) v[j] = proc_elem(v[j], b[j], (bits >> j) & 1u, tau);
+    if (e0 + j < V) v[j] = proc_elem(v[j], in.b[j], (in.bits >> j) & 1u, tau);
+}
+
+// Processors over this lane's 8 elements [e0, e0 + 8) of row `row`.
+template <bool VEC>
+__device__ __forceinline__ void proc8(const ProcSpec& pr, size_t row, float tau, long e0, long V, float (&v)[8]) {
+  Proc8In in;
+  proc8_load<VEC>(pr, row, e0, V, in);
+  proc8_apply(in, tau, e0, V, v);
 }
 
 // The processed value of one element x of row `row`.

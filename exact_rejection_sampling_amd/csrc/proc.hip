@@ -7,12 +7,16 @@
 //  * top-p (0 < p < 1): among the candidates with key >= tau_k, with weights
 //    w = 2^((s - max) * c2), tau_p = the largest key t whose mass {key >= t} reaches
 //    p * (total mass): the smallest tie-closed set of top tokens whose probability reaches p.
-// Both are found by radix selection over the bits in which the row's candidate keys differ,
-// 12 bits per pass: a pass streams the row once and adds each candidate whose higher bits
-// match the prefix found so far into one of 4096 LDS bins -- a count (top-k) or a mass in
-// fixed point, 2^-32 of the largest weight, rounded to nearest (top-p).  Integer sums do not
-// depend on the order of the additions, so the result is the same on every run.  The row's
-// threshold is the larger of the two, or -inf.
+// Counts are integers and masses are fixed-point integers (each weight scaled by the
+// largest power of two that keeps every sum below 2^53, rounded to nearest), so every sum is
+// exact and the result does not depend on the order of the additions.  Usual path, three
+// or four passes over the row: (0) the candidates' max, min and count; (1) counts and
+// masses in 4096 LDS bins linear in s over [min, max]; then for each selection the bin
+// where the count or mass from the top reaches its target, (2) a pass that collects that
+// bin's candidates into LDS, and an exact resolution among them.  A bin with more than
+// 2048 candidates (values piled on a few points) falls back to radix selection over the
+// bits in which the candidate keys differ, 12 bits per pass.  The row's threshold is tau_p
+// when top-p is on (it is at least tau_k), else tau_k, or -inf.
 //
 // Method: [M7.1] "M7.1 - Speculative Decoding: Draft, Verify, Accept, Reject" §0x06J (the
 // verified p is the row after top-k and top-p); [Tiny] "Exact Speculative and Assisted
@@ -35,21 +39,86 @@ __device__ __forceinline__ float value_of(unsigned k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// The candidates of this thread's 8 elements at e0: processed values (mask applied, no
-// threshold), validity bits.
+// Elements per thread and loop step: kU vectors of 8, kTB * 8 elements apart, whose loads
+// (logits, bias, mask words) are all issued before any is used -- one memory latency per
+// step instead of one per vector.  (Three or four vectors exceed the 128 registers a
+// 1024-thread block allows and spill.)
+constexpr int kU = 2;
+
+// The candidates of this thread's kU vectors at e0, e0 + stride, ...: processed values
+// (bias and mask applied, no threshold) and validity bits.
 template <int DT, bool VEC>
-__device__ __forceinline__ unsigned cand8(const ThreshParams& p, const void* lrow, size_t row, long e0, float (&s)[8]) {
-  load8<DT, VEC, false>(lrow, e0, p.V, s, -INFINITY);
-  ProcSpec pr{};
-  pr.bias = p.bias;
-  pr.allowed = p.allowed;
-  pr.W = p.W;
-  proc8<VEC>(pr, row, -INFINITY, e0, p.V, s);
-  unsigned ok = 0u;
+__device__ __forceinline__ void cand_batch(const ThreshParams& p, const void* lrow, size_t row, long e0, long stride,
+                                           float (&s)[kU][8], unsigned (&ok)[kU]) {
+  Proc8In in[kU];
+  if (VEC && e0 + (kU - 1) * stride + 8 <= p.V) {
+    // every vector inside the row: raw loads only (the bias and mask branches are uniform),
+    // then the arithmetic
+    u32x4 w[kU];
+    f32x4 f[kU][2], bl[kU], bh[kU];
+    unsigned mw[kU];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (e0 + j < p.V && s[j] > -INFINITY && s[j] < INFINITY) ok |= 1u << j;   // false for NaN
-  return ok;
+    for (int u = 0; u < kU; ++u) {
+      const long e = e0 + u * stride;
+      if constexpr (DT == kBF16) {
+        w[u] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(lrow) + e);
+      } else {
+        f[u][0] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(lrow) + e);
+        f[u][1] = *(reinterpret_cast<const f32x4*>(static_cast<const float*>(lrow) + e) + 1);
+      }
+    }
+    if (p.bias) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        bl[u] = *reinterpret_cast<const f32x4*>(p.bias + e0 + u * stride);
+        bh[u] = *reinterpret_cast<const f32x4*>(p.bias + e0 + u * stride + 4);
+      }
+    }
+    if (p.allowed) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) mw[u] = p.allowed[row * p.W + ((e0 + u * stride) >> 5)];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if constexpr (DT == kBF16) {
+        s[u][0] = __uint_as_float(w[u].x << 16); s[u][1] = __uint_as_float(w[u].x & 0xffff0000u);
+        s[u][2] = __uint_as_float(w[u].y << 16); s[u][3] = __uint_as_float(w[u].y & 0xffff0000u);
+        s[u][4] = __uint_as_float(w[u].z << 16); s[u][5] = __uint_as_float(w[u].z & 0xffff0000u);
+        s[u][6] = __uint_as_float(w[u].w << 16); s[u][7] = __uint_as_float(w[u].w & 0xffff0000u);
+      } else {
+        s[u][0] = f[u][0].x; s[u][1] = f[u][0].y; s[u][2] = f[u][0].z; s[u][3] = f[u][0].w;
+        s[u][4] = f[u][1].x; s[u][5] = f[u][1].y; s[u][6] = f[u][1].z; s[u][7] = f[u][1].w;
+      }
+      if (p.bias) {
+        in[u].b[0] = bl[u].x; in[u].b[1] = bl[u].y; in[u].b[2] = bl[u].z; in[u].b[3] = bl[u].w;
+        in[u].b[4] = bh[u].x; in[u].b[5] = bh[u].y; in[u].b[6] = bh[u].z; in[u].b[7] = bh[u].w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) in[u].b[j] = 0.0f;
+      }
+      const long e = e0 + u * stride;
+      in[u].bits = p.allowed ? (mw[u] >> (e & 31)) & 0xffu : 0xffu;
+    }
+  } else {
+    ProcSpec pr{};
+    pr.bias = p.bias;
+    pr.allowed = p.allowed;
+    pr.W = p.W;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) load8<DT, VEC, false>(lrow, e0 + u * stride, p.V, s[u], -INFINITY);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) proc8_load<VEC>(pr, row, e0 + u * stride, p.V, in[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const long e = e0 + u * stride;
+    proc8_apply(in[u], -INFINITY, e, p.V, s[u]);
+    unsigned m = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (e + j < p.V && s[u][j] > -INFINITY && s[u][j] < INFINITY) m |= 1u << j;   // false for NaN
+    ok[u] = m;
+  }
 }
 
 // 1024 threads (16 waves) per row: enough waves per SIMD to hide the per-element chain.
@@ -102,20 +171,23 @@ __device__ unsigned radix_select(const ThreshParams& p, const void* lrow, size_t
     const int width = min(kDigit, nb - done), shift = nb - done - width;
     for (int j = tid; j < kBins; j += kTB) L.bin[j] = 0ull;
     __syncthreads();
-    for (long e0 = (long)tid * kVec; e0 < p.V; e0 += (long)kTB * kVec) {
-      float s[8];
-      const unsigned ok = cand8<DT, VEC>(p, lrow, row, e0, s);
+    for (long e0 = (long)tid * kVec; e0 < p.V; e0 += (long)kTB * kVec * kU) {
+      float s[kU][8];
+      unsigned ok[kU];
+      cand_batch<DT, VEC>(p, lrow, row, e0, (long)kTB * kVec, s, ok);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (!((ok >> e) & 1u)) continue;
-        const unsigned k = key_of(s[e]);
-        if (k < klo) continue;
-        const unsigned high = shift + width == 32 ? 0u : (k >> (shift + width));
-        if (high != prefix) continue;
-        unsigned long long v = 1ull;
-        if constexpr (MASS) v = __double2ull_rn((double)__builtin_amdgcn_exp2f((s[e] - M) * p.c2) * fix);
-        atomicAdd(&L.bin[(k >> shift) & ((1u << width) - 1u)], v);
-      }
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (!((ok[u] >> e) & 1u)) continue;
+          const unsigned k = key_of(s[u][e]);
+          if (k < klo) continue;
+          const unsigned high = shift + width == 32 ? 0u : (k >> (shift + width));
+          if (high != prefix) continue;
+          unsigned long long v = 1ull;
+          if constexpr (MASS) v = __double2ull_rn((double)__builtin_amdgcn_exp2f((s[u][e] - M) * p.c2) * fix);   // fixed_weight
+          atomicAdd(&L.bin[(k >> shift) & ((1u << width) - 1u)], v);
+        }
     }
     __syncthreads();
     // thread t owns kBinsPerThread consecutive digits, highest digits to thread 0
@@ -152,12 +224,143 @@ __device__ unsigned radix_select(const ThreshParams& p, const void* lrow, size_t
   return nb == 0 ? klo : prefix;
 }
 
+// ------------------------------------------------------------------ value-bin selection
+// The usual path: one pass adds every candidate into one of kBins bins linear in its value
+// over [min, max] (counts, and fixed-point masses for top-p); the bin where the count or
+// mass from the top reaches the target holds the threshold, and a second pass collects that
+// bin's candidates into LDS, where the threshold is resolved exactly.  Linear bins spread a
+// row's values evenly, so the LDS adds rarely collide (the first radix digit of the keys
+// piles most of a row into a few dozen bins).  bin(s) is monotone in s, ties share a bin,
+// and every count and mass is an integer sum, so the result is the radix selection's.  A
+// bin with more than kCap candidates falls back to the radix selection.
+constexpr int kCap = 2048;
+
+struct BinLds {
+  unsigned cnt[kBins];
+  unsigned long long mass[kBins];
+};
+union SelectLds {
+  BinLds bins;
+  RadixLds radix;
+};
+struct Collected {
+  float v[kCap];
+  unsigned long long w[kCap];
+  int n;
+};
+
+struct ValueBins {
+  float lo, scale;
+  __device__ __forceinline__ int of(float s) const {
+    return static_cast<int>(fminf((s - lo) * scale, static_cast<float>(kBins - 1)));
+  }
+};
+
+// Block-wide fp64 sum (every thread receives it).
+__device__ __forceinline__ double block_sum_d(double v, double* scratch) {
+  double tot;
+  tb_excl_scan(v, scratch, &tot);
+  return tot;
+}
+
+__device__ __forceinline__ unsigned long long fixed_weight(float s, float M, float c2, double fix) {
+  return __double2ull_rn((double)__builtin_amdgcn_exp2f((s - M) * c2) * fix);
+}
+
+// The largest bin d whose F(d) = above + sum of val over bins >= d reaches `target` (block-
+// wide; -1 if none): returns d and, in *f_above, F(d + 1).  Thread t owns kBinsPerThread
+// consecutive bins, the highest to thread 0.
+template <class Val>
+__device__ int find_bin(Val val, double above, double target, double* scratch, int* s_d, double* s_f, double* f_above) {
+  const int tid = threadIdx.x;
+  const int d_hi = kBins - 1 - tid * kBinsPerThread;
+  double run = 0.0;
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) run += val(d_hi - i);
+  double tot;
+  const double before = tb_excl_scan(run, scratch, &tot);
+  if (tid == 0) *s_d = -1;
+  __syncthreads();
+  double f = above + before;
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) {
+    const double v = val(d_hi - i);
+    if (f < target && f + v >= target) {   // one thread's run holds the crossing
+      *s_d = d_hi - i;
+      *s_f = f;
+    }
+    f += v;
+  }
+  __syncthreads();
+  const int d = *s_d;
+  *f_above = *s_f;
+  __syncthreads();
+  return d;
+}
+
+// Collects the candidates of bin d with their weights (fixed-point masses when fix > 0);
+// returns the number found (which may exceed kCap: then only kCap are stored).
+template <int DT, bool VEC>
+__device__ int collect(const ThreshParams& p, const void* lrow, size_t row, const ValueBins& vb, int d, float M,
+                       double fix, Collected& L) {
+  if (threadIdx.x == 0) L.n = 0;
+  __syncthreads();
+  for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kTB * kVec * kU) {
+    float s[kU][8];
+    unsigned ok[kU];
+    cand_batch<DT, VEC>(p, lrow, row, e0, (long)kTB * kVec, s, ok);
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (!((ok[u] >> e) & 1u)) continue;
+        if (vb.of(s[u][e]) != d) continue;
+        const int i = atomicAdd(&L.n, 1);
+        if (i < kCap) {
+          L.v[i] = s[u][e];
+          L.w[i] = fix > 0.0 ? fixed_weight(s[u][e], M, p.c2, fix) : 1ull;
+        }
+      }
+  }
+  __syncthreads();
+  const int n = L.n;
+  __syncthreads();
+  return n;
+}
+
+// Among the n collected candidates (one bin) with value >= floor_v: the largest value t with
+// above + the sum of w (mass) or the count over those with value >= t reaching `target`
+// (-inf if none).  Ties share their sum, so the threshold never splits them.
+__device__ float resolve(const Collected& L, int n, float floor_v, bool mass, double above, double target,
+                         float* scratch) {
+  float best = -INFINITY;
+  for (int i = threadIdx.x; i < n; i += kTB) {
+    const float t = L.v[i];
+    if (t < floor_v) continue;
+    double f = above;
+    for (int j = 0; j < n; ++j)
+      if (L.v[j] >= t) f += mass ? (double)L.w[j] : 1.0;
+    if (f >= target) best = fmaxf(best, t);
+  }
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const float wb = wave_max(best);
+  if (lane == 0) scratch[wave] = wb;
+  __syncthreads();
+  float r = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kTW; ++w) r = fmaxf(r, scratch[w]);
+  __syncthreads();
+  return r;
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
   __shared__ double s_scratch[kTW];
-  __shared__ RadixLds s_radix;
+  __shared__ SelectLds s_sel;
+  __shared__ Collected s_col;
   __shared__ float s_m[kTW], s_mn[kTW];
-  __shared__ int s_fault;
+  __shared__ int s_fault, s_d;
+  __shared__ double s_f;
   const size_t row = blockIdx.x;
   const int b = static_cast<int>(row / p.R);
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
@@ -176,18 +379,22 @@ __global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
   float m = -INFINITY, mn = INFINITY;
   double cnt = 0.0;
   bool fault = false;
-  for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kTB * kVec) {
-    float s[8];
-    const unsigned ok = cand8<DT, VEC>(p, lrow, row, e0, s);
+  for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kTB * kVec * kU) {
+    float s[kU][8];
+    unsigned ok[kU];
+    cand_batch<DT, VEC>(p, lrow, row, e0, (long)kTB * kVec, s, ok);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (e0 + e < p.V && (s[e] != s[e] || s[e] == INFINITY)) fault = true;
-      if ((ok >> e) & 1u) {
-        m = fmaxf(m, s[e]);
-        mn = fminf(mn, s[e]);
-        cnt += 1.0;
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const long x = e0 + (long)u * kTB * kVec + e;
+        if (x < p.V && (s[u][e] != s[u][e] || s[u][e] == INFINITY)) fault = true;
+        if ((ok[u] >> e) & 1u) {
+          m = fmaxf(m, s[u][e]);
+          mn = fminf(mn, s[u][e]);
+          cnt += 1.0;
+        }
       }
-    }
   }
   if (fault) s_fault = 1;
   const float wm = wave_max(m);
@@ -210,17 +417,91 @@ __global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
   __syncthreads();
   float tau = -INFINITY;
   if (!s_fault && C > 0.0) {
-    unsigned lo = key_of(MN);
-    const unsigned hi = key_of(M);
-    if (use_k && (double)k < C) {
-      lo = radix_select<DT, VEC, false>(p, lrow, row, lo, hi, (double)k, M, 1.0, s_radix);
-      tau = value_of(lo);
+    const bool sel_k = use_k && (double)k < C;
+    // the largest scale that keeps every sum of fixed-point weights (each <= 1) below 2^53
+    const double fix = use_p ? ldexp(1.0, 52 - (64 - __clzll(static_cast<unsigned long long>(C)))) : 0.0;
+    ValueBins vb;
+    vb.lo = MN;
+    vb.scale = static_cast<float>(kBins) / (M - MN);
+    bool fast = M > MN && isfinite(M - MN) && isfinite(vb.scale) && vb.scale > 0.0f;
+    float tau_k = -INFINITY;
+    if (M == MN) {
+      tau = M;                                   // one distinct value: every selection keeps it
+    } else if (fast) {
+      BinLds& L = s_sel.bins;
+      for (int j = threadIdx.x; j < kBins; j += kTB) {
+        L.cnt[j] = 0u;
+        L.mass[j] = 0ull;
+      }
+      __syncthreads();
+      // pass 1: counts and masses per value bin
+      for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kTB * kVec * kU) {
+        float s[kU][8];
+        unsigned ok[kU];
+        cand_batch<DT, VEC>(p, lrow, row, e0, (long)kTB * kVec, s, ok);
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (!((ok[u] >> e) & 1u)) continue;
+            const int d = vb.of(s[u][e]);
+            if (sel_k) atomicAdd(&L.cnt[d], 1u);
+            if (use_p) atomicAdd(&L.mass[d], fixed_weight(s[u][e], M, p.c2, fix));
+          }
+      }
+      __syncthreads();
+      int dk = -1, n = 0;
+      double fk = 0.0;
+      if (sel_k) {
+        dk = find_bin([&](int d) { return d >= 0 ? (double)L.cnt[d] : 0.0; }, 0.0, (double)k, s_scratch, &s_d, &s_f, &fk);
+        if (dk >= 0) n = collect<DT, VEC>(p, lrow, row, vb, dk, M, fix, s_col);
+        if (dk < 0 || n > kCap) fast = false;
+        else tau_k = resolve(s_col, n, -INFINITY, false, fk, (double)k, s_m);
+        tau = tau_k;
+      }
+      if (fast && use_p) {
+        // survivors of top-k: every candidate above bin dk, and those of bin dk at or above
+        // tau_k (collected); their total mass fixes the target
+        double part = 0.0, total = 0.0;
+        if (sel_k)
+          for (int i = threadIdx.x; i < n; i += kTB)
+            if (s_col.v[i] >= tau_k) part += (double)s_col.w[i];
+        part = block_sum_d(part, s_scratch);
+        auto valp = [&](int d) -> double {
+          if (d < 0 || (sel_k && d < dk)) return 0.0;
+          return (sel_k && d == dk) ? part : (double)L.mass[d];
+        };
+        {
+          double t = 0.0;
+          for (int d = threadIdx.x; d < kBins; d += kTB) t += valp(d);
+          total = block_sum_d(t, s_scratch);
+        }
+        const double target = (double)tp * total;
+        double fp = 0.0;
+        const int dp = find_bin(valp, 0.0, target, s_scratch, &s_d, &s_f, &fp);
+        if (dp < 0) {
+          fast = false;
+        } else if (sel_k && dp == dk) {
+          tau = resolve(s_col, n, tau_k, true, fp, target, s_m);
+        } else {
+          const int n2 = collect<DT, VEC>(p, lrow, row, vb, dp, M, fix, s_col);
+          if (n2 > kCap) fast = false;
+          else tau = resolve(s_col, n2, -INFINITY, true, fp, target, s_m);
+        }
+      }
     }
-    if (use_p) {
-      // the largest scale that keeps every sum of fixed-point weights (each <= 1) below 2^53
-      const double fix = ldexp(1.0, 52 - (64 - __clzll(static_cast<unsigned long long>(C))));
-      const unsigned t = radix_select<DT, VEC, true>(p, lrow, row, lo, hi, (double)tp, M, fix, s_radix);
-      tau = value_of(t);
+    if (!fast) {
+      // radix selection (also for rows whose values cannot be binned)
+      unsigned lo = key_of(MN);
+      const unsigned hi = key_of(M);
+      if (sel_k) {
+        lo = radix_select<DT, VEC, false>(p, lrow, row, lo, hi, (double)k, M, 1.0, s_sel.radix);
+        tau = value_of(lo);
+      }
+      if (use_p) {
+        const unsigned t = radix_select<DT, VEC, true>(p, lrow, row, lo, hi, (double)tp, M, fix, s_sel.radix);
+        tau = value_of(t);
+      }
     }
   }
   if (threadIdx.x == 0) p.thresh[row] = tau;

@@ -148,3 +148,18 @@ def test_greedy_with_bias_and_mask():
     L, _ = oracle.process_rows(x.logits, x.logit_dtype, 1.0, bias, words)
     exp = oracle.verify_greedy(L, x.tokens, "f64")
     compare_exact(got, exp, ["accepted_len", "out_tokens"])
+
+
+@pytest.mark.parametrize("V", [5000, 65536])
+def test_truncations_on_piled_values(V):
+    """Logits on a coarse grid (a few dozen distinct values): with V = 65536 the bin holding
+    a threshold has thousands of candidates, so the selection takes its radix fallback; with
+    V = 5000 it resolves the bin directly.  Both must give the oracle's thresholds."""
+    B, G = 12, 2
+    rng = np.random.default_rng(21 + V)
+    x = synth.make_chain(B, G, V, seed=22 + V, logit_dtype="f32", noise=0.5)
+    x.logits = (np.round(rng.normal(0, 1, (B, G + 1, V)) * 4) / 4).astype(np.float32)
+    k = np.array([1, 20, 1000, 0] * 3, np.int32)
+    p = np.array([1.0, 0.5, 0.9, 0.99, 0.3, 1.0] * 2, np.float32)
+    say(f"chain_ex truncations on piled values V={V}")
+    check(x, None, None, k, p)
