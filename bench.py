@@ -394,7 +394,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps(dict(error="this build measures one GPU only; run with --gpus 1")))
+        print(json.dumps(dict(error="this benchmark runs on one GPU only; run with --gpus 1")))
         sys.exit(2)
 
     import torch
