@@ -333,6 +333,42 @@ def bench_chain_lazy(args, torch, sv, synth, k, fp32=False):
                 alg_frac=alg / launch / 1e9 / HBM_PEAK_GBS)
 
 
+def bench_sweep(args, torch, sv, synth):
+    """Bandwidth sweep of the chain verifier: config 3's recipe (gamma = 5, V = 128256) with
+    bf16 logits at T = 0.8 and fp32 logits at T = 1, over batch sizes B (the first B requests
+    of a 256-request batch); one JSON line per point with the time per call and the achieved
+    GB/s on the algorithmic bytes (every row once plus each rejecting request's fp32 q row)."""
+    dev = "cuda:0"
+    sizes = (8, 16, 32, 64, 128, 256)
+    for fp32 in (False, True):
+        # the largest batch once; smaller ones are its first B requests (requests are independent)
+        x = synth.make_config(3, 0, B=sizes[-1], **(dict(logit_dtype="f32", temperature=1.0) if fp32 else {}))
+        G, V = x.gamma, x.V
+        for B in sizes:
+            if fp32:
+                lt = torch.from_numpy(x.logits[:B]).to(dev)
+            else:
+                lt = torch.from_numpy(x.logits[:B].view(np.int16)).to(dev).view(torch.bfloat16)
+            qt = torch.from_numpy(x.q[:B]).to(dev)
+            tt, ut = torch.from_numpy(x.tokens[:B]).to(dev), torch.from_numpy(x.u[:B]).to(dev)
+            sl = lt.element_size()
+            sets = device_copies(lambda: (lt.clone(), qt.clone()), lt.numel() * sl + qt.numel() * 4)
+            del lt, qt
+            ws = torch.zeros(sv.chain_workspace_bytes(B, G, V) + 512, dtype=torch.uint8, device=dev)
+            calls = [sv.prepare_chain(s_[0], s_[1], tt, ut, float(x.temperature), workspace_tensor=ws) for s_ in sets]
+            span, per = time_calls(calls, args.steps, args.warmup, torch.cuda.current_stream())
+            acc = calls[0].out["accepted_len"].cpu().numpy()
+            n_rej = int((acc < G).sum())
+            alg = B * (G + 1) * V * sl + n_rej * V * 4 + B * G * 10 + B * (G + 1) * 4 + B * (G + 2) * 8
+            launch = span / len(per)
+            print(json.dumps(dict(sweep="chain", logits="fp32" if fp32 else "bf16", B=B, gamma=G, V=V,
+                                  us_per_call=launch * 1e6, alg_bytes=alg, alg_gbs=alg / launch / 1e9,
+                                  frac=alg / launch / 1e9 / HBM_PEAK_GBS,
+                                  positions_per_s=B * (G + 1) / launch)), flush=True)
+            del sets, calls, ws
+            torch.cuda.empty_cache()
+
+
 _CPU_X = None   # the workload a forked oracle worker reads
 
 
@@ -392,6 +428,8 @@ def main():
                          "chain_stop, chain_bias_mask, chain_processors, chain_lazy, chain_f32, greedy_lazy), or all")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="print the chain bandwidth sweep over batch sizes (one JSON line per point) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps(dict(error="this benchmark runs on one GPU only; run with --gpus 1")))
@@ -401,13 +439,16 @@ def main():
     import exact_rejection_sampling_amd as sv
     import synth
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and not args.sweep:
         log("[bench] oracle CPU baseline")
         cpu = cpu_baseline(synth.make_config(3, 0), args.cpu_seconds)
     if not torch.cuda.is_available():
         print(json.dumps(dict(error="no GPU visible")))
         sys.exit(1)
     sv.load_library()
+    if args.sweep:
+        bench_sweep(args, torch, sv, synth)
+        return
 
     log("[bench] chain headline workload")
     c = bench_chain(args, torch, sv, synth)
