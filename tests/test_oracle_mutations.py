@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 PIN_FILES = ["test_oracle_pins.py", "test_oracle_laws.py", "test_oracle_regression.py",
              "test_oracle_tree_residual.py", "test_oracle_stop.py", "test_oracle_tree_greedy.py",
-             "test_oracle_processors.py"]
+             "test_oracle_processors.py", "test_oracle_lazy.py"]
 
 # (file under oracle/, text as it stands, the planted mistake)
 MUTANTS = {
@@ -35,6 +35,14 @@ MUTANTS = {
     "bonus_from_row_0": ("chain.py", "p, m, Z = target_probs(L[gamma], temperature)",
                          "p, m, Z = target_probs(L[0], temperature)"),
     "no_stop_at_first_rejection": ("chain.py", "            A = i\n            break\n", "            A = i\n"),
+    # rows past the first rejection read as if they mattered ([M7.1] §0x03G)
+    "chain_validates_every_row": ("chain.py", "    A = gamma\n    end = None",
+                                  "    if not all(row_is_valid(L[j]) for j in range(gamma + 1)):\n"
+                                  "        return fail(NONFINITE)\n    A = gamma\n    end = None"),
+    "greedy_validates_every_row": ("greedy.py", "    for i in range(gamma):\n        if not row_is_valid(L[i]):",
+                                   "    if not all(row_is_valid(L[j]) for j in range(gamma + 1)):\n"
+                                   "        return NONFINITE, -1, [], 0\n"
+                                   "    for i in range(gamma):\n        if not row_is_valid(L[i]):"),
     "terminal_uses_rejecting_uniform": ("chain.py", "k, W, lo, hi = inverse_cdf(w, float(u[gamma]))",
                                         "k, W, lo, hi = inverse_cdf(w, float(u[min(A, gamma)]))"),
     "correction_not_emitted": ("chain.py", "res.tokens = [int(t) for t in x[:A]] + [k]",
