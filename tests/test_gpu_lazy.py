@@ -206,3 +206,17 @@ def test_greedy_bad_rows_stops_budgets_and_workspace_reuse():
     compare_exact(c, e2, ["accepted_len", "out_tokens"])
     assert c["req_status"][early[0]] == 0 and c["req_status"][early[1]] == 0
     assert c["req_status"][late[0]] == oracle.NONFINITE
+
+
+def test_greedy_lazy_with_bias_and_mask():
+    """Gates decide on processed rows too: lazy greedy with bias and masks equals the
+    every-row call with them, and the oracle on the processed rows."""
+    x = synth.make_greedy(48, 6, 20000, seed=620, logit_dtype="bf16", match_prob=0.75)
+    bias, words, _, _ = synth.make_processors(x.B, x.gamma + 1, x.V, seed=621, bias_sigma=0.5,
+                                              with_top_k=False, with_top_p=False)
+    kw = dict(bias=t_f32(bias), allowed=torch.from_numpy(words.view(np.int32)).to(DEV))
+    say("greedy lazy k=2 with bias and masks")
+    got = run_greedy(x, 2, **kw)
+    same(got, run_greedy(x, 0, **kw), GKEYS)
+    L, _ = oracle.process_rows(x.logits, x.logit_dtype, 1.0, bias, words)
+    compare_exact(got, oracle.verify_greedy(L, x.tokens, "f64"), ["accepted_len", "out_tokens"])
