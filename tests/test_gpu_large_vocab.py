@@ -3,8 +3,9 @@ tree's limit V = 2^21), where the kernels take the paths that only long rows rea
 than 64 statistics slices per row (each decision lane loops over slices), more than 2048
 terminal chunks per row (the selector re-reads chunk masses beyond the 8 it keeps in
 registers), tree rows of more than 1024 chunks (the walker reads the row's summaries from
-the workspace instead of staging them in LDS), and hundreds of helper blocks per row.
-Same comparisons as the workload-size tests."""
+the workspace instead of staging them in LDS), and hundreds of helper blocks per row; and
+trees at the node limit N = 4096, and a residual-update node with more rejected children
+than a helper keeps in LDS.  Same comparisons as the workload-size tests."""
 import numpy as np
 import pytest
 
@@ -72,3 +73,43 @@ def test_residual_tree_at_its_vocabulary_limit():
                                       x.temperature, x.logit_dtype)
     compare_exact(got, exp, TREE_KEYS, flagged=exp["flagged"])
     print("accepted", got["accepted_len"].tolist())
+
+
+def test_trees_with_the_most_nodes():
+    """N = 4096 nodes (the limit), random trees of depth <= 40: the membership walks and the
+    child searches over thousands of nodes."""
+    x = synth.make_tree(3, 4096, 512, seed=705, logit_dtype="f32", max_depth=40, max_children=6, boost=12.0)
+    say("tree B=3 N=4096 V=512")
+    exp = oracle.verify_tree(x.logits, x.parents, x.node_tokens, x.u, x.temperature, x.logit_dtype)
+    compare_exact(run_tree(x), exp, TREE_KEYS, flagged=exp["flagged"])
+    say("tree_greedy B=3 N=4096 V=512")
+    got = to_np(sv.spec_verify_tree_greedy(t_logits(x.logits, x.logit_dtype), t_i32(x.node_tokens),
+                                           t_i32(x.parents)))
+    compare_exact(got, oracle.verify_tree_greedy(x.logits, x.parents, x.node_tokens, x.logit_dtype), TREE_KEYS)
+    print("accepted", exp["accepted_len"].tolist(), got["accepted_len"].tolist())
+
+
+def test_residual_tree_with_hundreds_of_rejected_siblings():
+    """A root with 300 children, every one proposing a token the target almost never takes
+    (the target's mass sits on tokens 0..9, the drafter's on 10..511): all 300 are rejected,
+    so the residual carries 300 updates -- past the 256 rejected children a helper keeps in
+    LDS -- before the final draw."""
+    B, N, V = 2, 301, 512
+    rng = np.random.default_rng(706)
+    logits = rng.normal(0, 1, (B, N, V)).astype(np.float32)
+    logits[:, 0, :10] += 20.0
+    q = np.zeros((B, N, V), np.float32)
+    q[:, 1:, 10:] = np.float32(1.0 / (V - 10))
+    parents = np.zeros((B, N), np.int32)
+    parents[:, 0] = -1
+    tokens = np.zeros((B, N), np.int32)
+    tokens[:, 1:] = rng.integers(10, V, (B, N - 1))
+    u_acc = rng.random((B, N), dtype=np.float32)
+    u_draw = rng.random((B, N), dtype=np.float32)
+    exp = oracle.verify_tree_residual(logits, q, parents, tokens, u_acc, u_draw, 1.0, "f32")
+    assert (exp["accepted_len"] == 0).all() and (exp["status"] == 0).all()
+    say("tree_residual B=2 star of 300 rejected children V=512")
+    got = to_np(sv.spec_verify_tree_residual(t_f32(logits), t_f32(q), t_i32(tokens), t_i32(parents), t_f32(u_acc),
+                                             t_f32(u_draw), 1.0))
+    compare_exact(got, exp, TREE_KEYS, flagged=exp["flagged"])
+    assert (got["out_tokens"][:, 0] < 10).all()
