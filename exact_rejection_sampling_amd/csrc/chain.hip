@@ -481,9 +481,11 @@ __device__ __forceinline__ void row_stats(const ChainParams& p, const RowState& 
                                           float (&v)[4]) {
   v[0] = v[1] = v[2] = v[3] = NAN;
   if (!reached) return;
-  const double m_nat = (double)rs.m[i] * p.inv_t;
-  v[0] = (float)m_nat;
-  v[1] = (float)(log(rs.z[i]) + (double)rs.r[i] * kLn2 - m_nat);
+  v[0] = (float)((double)rs.m[i] * p.inv_t);
+  // log Z = log sum 2^((l - m) c2) = log z + (r - m c2) ln 2: relative to the row's own
+  // maximum, so that the fp32 rounding of c2 enters only through (l - m) (written as
+  // log z + r ln 2 - m / T it would add m (c2 ln 2 - 1/T), about 1e-4 at m / T = 1800)
+  v[1] = (float)(log(rs.z[i]) + ((double)rs.r[i] - (double)rs.m[i] * (double)p.c2) * kLn2);
   if (i < p.G) {
     v[2] = (float)rs.px[i];
     v[3] = (float)rs.a[i];

@@ -274,3 +274,15 @@ def test_one_workspace_across_shapes_and_entry_points():
             np.testing.assert_array_equal(gout["out_tokens"], exp["out_tokens"])
     torch.cuda.synchronize()
     assert int(ws.count_nonzero()) == 0              # the whole workspace is back at zero
+
+
+@pytest.mark.parametrize("T", [0.01, 0.05, 20.0, 1000.0])
+def test_extreme_temperatures(T):
+    """Near-greedy and near-uniform targets: at T = 0.01 most p(x) underflow (fp32 on the
+    GPU, fp64 in the oracle: both far below any uniform), at T = 1000 the rows are almost
+    flat; tokens, lengths and statistics still match outside flagged draws."""
+    x = synth.make_chain(32, 4, 20000, seed=90 + int(T * 100), logit_dtype="bf16", sigma=3.0, boost_frac=0.01,
+                         noise=1.0, temperature=T)
+    say(f"chain T={T}")
+    got = run_chain(x)
+    print(compare_chain(got, oracle_chain(x)), np.bincount(got["accepted_len"][got["req_status"] == 0]).tolist())
