@@ -102,3 +102,12 @@ def test_repeatable():
     a, b = run_tree(x), run_tree(x)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+@pytest.mark.parametrize("T", [0.01, 100.0])
+def test_extreme_temperatures(T):
+    x = synth.make_tree(8, 31, 20000, seed=int(T * 10) + 5, logit_dtype="bf16", temperature=T, max_depth=4,
+                        max_children=4, boost=6.0)
+    say(f"tree T={T}")
+    got, exp = check(x)
+    print("accepted", got["accepted_len"].tolist(), "flagged", int(exp["flagged"].sum()))

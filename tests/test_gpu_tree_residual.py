@@ -185,3 +185,12 @@ def test_without_replacement_siblings(V, noise):
     say(f"tree_residual without replacement V={V} noise={noise}")
     got, exp = check(x)
     print("accepted", np.bincount(got["accepted_len"][got["req_status"] == 0]).tolist())
+
+
+@pytest.mark.parametrize("T", [0.01, 100.0])
+def test_extreme_temperatures(T):
+    x = synth.make_tree_residual(8, 31, 20000, seed=int(T * 10) + 7, sigma=2.0, noise=0.5, temperature=T,
+                                 max_depth=3, max_children=4)
+    say(f"tree_residual T={T}")
+    got, exp = check(x)
+    print("accepted", got["accepted_len"].tolist(), "flagged", int(exp["flagged"].sum()))
