@@ -108,3 +108,13 @@ def test_workspace_returns_to_zero_with_processors():
                               q_dtype="f64")
     exp["flagged"] |= pflag
     compare_chain(a, exp)
+
+
+def test_the_largest_sparse_rows():
+    """K = 65536 entries per row (the limit) at V = 128256: every terminal item scans all of
+    them to fill its chunk, and the gather sums a token's entries block-wide."""
+    x, idx, vals = synth.make_chain_sparse(4, 3, 128256, 65536, seed=3500, logit_dtype="bf16", sigma=3.0,
+                                           boost_frac=0.01, noise=1.0, temperature=0.8)
+    say("chain sparse q K=65536 V=128256")
+    got = run_sparse(x, idx, vals)
+    print(compare_chain(got, oracle_sparse(x, idx, vals)), got["accepted_len"].tolist())
