@@ -7,7 +7,14 @@
 //    row with 16-byte non-temporal loads, keep an online (max, sum of exponentials) per
 //    lane, merge lanes and waves, and publish one summary for the slice.  The block that
 //    streams a draft row's first slice also publishes the draft token, its logit and its
-//    draft probability.  A statistics item never waits and never counts arrivals.
+//    draft probability.  A statistics item never counts arrivals, and waits only as
+//    the gate of a lazy row group (below).
+//  * lazy rows (lazy_rows = LK): the rows come in groups of LK, ordered group by group
+//    (lazy_item).  An item of a group after the first first takes the request's decision
+//    over the previous group's published words; if the round never reaches its group it
+//    publishes a marker (an empty-range summary, a zero gather record) instead of
+//    streaming.  Markers read as invalid rows, so they only ever follow an earlier event
+//    and never change the decision.
 //  * terminal item (request, 4096-element chunk): reads every summary of its request as
 //    soon as it is published, combines them into each row's normalizer, runs the accept
 //    tests in order and so finds the first rejection A (or gamma) -- every terminal item of
@@ -18,8 +25,9 @@
 //    passes u_gamma * W, rescans that chunk in vocabulary order, writes the outputs and
 //    returns every workspace word the request used to zero.
 // Waits: a terminal item waits only for its request's statistics items, whose block
-// indices are all lower (see block_item), and a selector only for its request's other
-// terminal items, whose indices are lower too.  The hardware dispatches the workgroups of a launch in index order, so a
+// indices are all lower (see block_item), a lazy gate only for the previous group's items
+// (lower, see lazy_item), and a selector only for its request's other terminal items,
+// whose indices are lower too.  The hardware dispatches the workgroups of a launch in index order, so a
 // waiting block never holds a slot that one of the blocks it waits for still needs, and
 // every wait ends.  Each wait is bounded all the same: a word that does not arrive within
 // the bound makes the request report SPEC_REQ_INTERNAL rather than wait on.
@@ -782,10 +790,10 @@ __global__ __launch_bounds__(kBlock) void chain_kernel(ChainParams p) {
   const Item it = p.J > 1 ? lazy_item(p, blockIdx.x) : block_item(p, blockIdx.x);
   const int row = it.idx / p.SL;
   // the rows whose words this block's decision reads: every row for a terminal item; for
-  // a lazy row group after the first, the rows of the group before it (whether the round
-  // reaches this group)
-  // (a group is reached when the group before it was and none of that group's drafts ends
-  // the round: a skipped group's words read as all -inf rows, an event at its first draft)
+  // a lazy row group after the first, the rows of the group before it, which decide whether
+  // the round reaches this group (it does when the group before it was reached and none
+  // of that group's drafts ends the round; a skipped group's markers read as invalid rows,
+  // an event at its first draft)
   int lo = 0, nr = 0;
   bool reached = true;
   if (it.terminal) {

@@ -6,14 +6,18 @@
 //  * streaming item (row, slice): the block's four waves stream a slice of one target row
 //    with 16-byte non-temporal loads, keeping per lane the maximum and the lowest position
 //    holding it; lanes and waves merge, and the block publishes one summary for the slice
-//    (max, lowest index attaining it, NaN if the slice holds a NaN).  It never waits.
+//    (max, lowest index attaining it, NaN if the slice holds a NaN).  It waits only as
+//    the gate of a lazy row group: with lazy_rows = LK the rows come in groups of LK,
+//    ordered group by group, and an item of a later group first decides, from the
+//    previous group's summaries, whether the round reaches it; if not it publishes a NaN
+//    summary instead of streaming (it reads as an invalid row, after an earlier event).
 //  * decider (request): reads every summary of its request as soon as it is published,
 //    combines each row's slices (the max, then the lowest index among the slices holding
 //    it), compares the argmaxes with the draft tokens in order and emits the matching
 //    prefix plus the target argmax at the first mismatch (or at the bonus row).  It then
 //    returns the summaries to zero.
-// Waits: a decider waits only for its request's streaming items, whose block indices are
-// all lower; the workgroups of a launch are dispatched in index order, so those blocks are
+// Waits: a decider waits only for its request's streaming items, and a lazy gate only for
+// the previous group's items, whose block indices are all lower; the workgroups of a launch are dispatched in index order, so those blocks are
 // running or done and the wait ends.  It is bounded all the same: a summary that does not
 // arrive in time makes the request report SPEC_REQ_INTERNAL.
 //
