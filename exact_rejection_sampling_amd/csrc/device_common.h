@@ -54,6 +54,58 @@ __device__ __forceinline__ const void* row_ptr(const void* base, size_t row, siz
   return static_cast<const char*>(base) + row * V * Elt<DT>::bytes;
 }
 
+// Eight consecutive elements [e0, e0 + 8) of a row whose address is only element-aligned
+// (V % 8 != 0, or an offset base): the whole 16-byte granules holding them are loaded and
+// the wanted bytes shifted out.  A granule never crosses a page and each one loaded holds
+// at least one wanted byte, so it lies in mapped memory; the bytes around the wanted ones
+// are never used.  The misalignment is the row's own (e0 * element size is a multiple of
+// 16), the same for every lane, so the shift is uniform.
+template <int DT>
+__device__ __forceinline__ void load8_granules(const void* row, long e0, float (&v)[8]) {
+  constexpr unsigned kBytes = DT == kBF16 ? 2u : 4u;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(row) + static_cast<uintptr_t>(e0) * kBytes;
+  const uintptr_t a0 = addr & ~static_cast<uintptr_t>(15);
+  const unsigned off = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(addr - a0));
+  const u32x4* g = reinterpret_cast<const u32x4*>(a0);
+  constexpr int kGran = DT == kBF16 ? 2 : 3;    // granules spanned when misaligned
+  uint32_t w[4 * kGran + 1];
+  const u32x4 g0 = g[0];
+  w[0] = g0.x; w[1] = g0.y; w[2] = g0.z; w[3] = g0.w;
+#pragma unroll
+  for (int k = 1; k < kGran; ++k) {
+    u32x4 gk = u32x4{0u, 0u, 0u, 0u};
+    if (off != 0u) gk = g[k];                   // off = 0: granule 0 (and 1 for fp32) suffice
+    if (DT != kBF16 && k == 1) gk = g[1];
+    w[4 * k] = gk.x; w[4 * k + 1] = gk.y; w[4 * k + 2] = gk.z; w[4 * k + 3] = gk.w;
+  }
+  w[4 * kGran] = 0u;
+  constexpr int kOut = DT == kBF16 ? 4 : 8;     // dwords wanted
+  uint32_t o[kOut];
+  const unsigned sh = off & 3u;                 // bytes within a dword (bf16: 0 or 2)
+  // the first wanted dword is w[off / 4]; a uniform switch keeps every index constant
+  switch (off >> 2) {
+#define SPEC_G(D)                                                                        \
+  case D:                                                                                \
+    _Pragma("unroll") for (int j = 0; j < kOut; ++j) o[j] = __builtin_amdgcn_alignbyte(w[D + j + 1], w[D + j], sh); \
+    break;
+    SPEC_G(0)
+    SPEC_G(1)
+    SPEC_G(2)
+    SPEC_G(3)
+#undef SPEC_G
+  }
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(o[k] << 16);
+      v[2 * k + 1] = __uint_as_float(o[k] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __uint_as_float(o[k]);
+  }
+}
+
 // Eight consecutive elements [e0, e0 + 8) of a row of V elements, e0 % 8 == 0.
 // Positions >= V read as `fill`.  VEC: the row is 16-byte aligned and V % 8 == 0, so the
 // group is either entirely inside or entirely past the row.  NT: streaming (non-temporal)
@@ -82,6 +134,8 @@ __device__ __forceinline__ void load8(const void* row, long e0, long V, float (&
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
       v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
+  } else if (e0 + 8 <= V) {
+    load8_granules<DT>(row, e0, v);
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = (e0 + k < V) ? load_scalar<DT>(row, e0 + k) : fill;
