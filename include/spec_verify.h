@@ -24,6 +24,11 @@
  *           row-major layout with the vocabulary innermost.  The library never
  *           allocates, never frees and never synchronizes; all work is enqueued on
  *           `stream`, and outputs are valid once that stream reaches the call.
+ * Graphs.   A call enqueues kernel launches only (one, or two with top-k / top-p), so
+ *           it may be captured in a HIP graph and replayed: each replay reads the
+ *           buffers' contents at replay time.  Make one eager call with the same
+ *           sizes and dtypes before capturing: the first launch of a kernel
+ *           configuration on a device queries its occupancy.
  * Workspace. Each entry point takes a caller-owned device workspace of at least the
  *           size its query function returns, aligned to 256 bytes.  It must be
  *           zero-filled before its first use, and every call leaves it entirely
