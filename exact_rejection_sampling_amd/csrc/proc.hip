@@ -13,7 +13,8 @@
 // or four passes over the row: (0) the candidates' max, min and count; (1) counts and
 // masses in 4096 LDS bins linear in s over [min, max]; then for each selection the bin
 // where the count or mass from the top reaches its target, (2) a pass that collects that
-// bin's candidates into LDS, and an exact resolution among them.  A bin with more than
+// bin's candidates into LDS, and an exact resolution among them.  With both selections on,
+// one collecting pass serves both whenever the top-p bin is fixed before tau_k is.  A bin with more than
 // 2048 candidates (values piled on a few points) falls back to radix selection over the
 // bits in which the candidate keys differ, 12 bits per pass.  The row's threshold is tau_p
 // when top-p is on (it is at least tau_k), else tau_k, or -inf.
@@ -160,7 +161,7 @@ __device__ double tb_excl_scan(double v, double* scratch, double* total) {
 // fraction p of the total mass F(klo) that the target is.  Every value stays an integer
 // below 2^53, so the fp64 scans are exact.
 template <int DT, bool VEC, bool MASS>
-__device__ unsigned radix_select(const ThreshParams& p, const void* lrow, size_t row, unsigned klo, unsigned khi,
+__device__ __forceinline__ unsigned radix_select(const ThreshParams& p, const void* lrow, size_t row, unsigned klo, unsigned khi,
                                  double param, float M, double fix, RadixLds& L) {
   const int tid = threadIdx.x;
   const int nb = (klo == khi) ? 0 : 32 - __clz(klo ^ khi);   // the varying low bits
@@ -271,7 +272,7 @@ __device__ __forceinline__ unsigned long long fixed_weight(float s, float M, flo
 // wide; -1 if none): returns d and, in *f_above, F(d + 1).  Thread t owns kBinsPerThread
 // consecutive bins, the highest to thread 0.
 template <class Val>
-__device__ int find_bin(Val val, double above, double target, double* scratch, int* s_d, double* s_f, double* f_above) {
+__device__ __forceinline__ int find_bin(Val val, double above, double target, double* scratch, int* s_d, double* s_f, double* f_above) {
   const int tid = threadIdx.x;
   const int d_hi = kBins - 1 - tid * kBinsPerThread;
   double run = 0.0;
@@ -301,7 +302,7 @@ __device__ int find_bin(Val val, double above, double target, double* scratch, i
 // Collects the candidates of bin d with their weights (fixed-point masses when fix > 0);
 // returns the number found (which may exceed kCap: then only kCap are stored).
 template <int DT, bool VEC>
-__device__ int collect(const ThreshParams& p, const void* lrow, size_t row, const ValueBins& vb, int d, float M,
+__device__ __forceinline__ int collect(const ThreshParams& p, const void* lrow, size_t row, const ValueBins& vb, int d, float M,
                        double fix, Collected& L) {
   if (threadIdx.x == 0) L.n = 0;
   __syncthreads();
@@ -328,10 +329,46 @@ __device__ int collect(const ThreshParams& p, const void* lrow, size_t row, cons
   return n;
 }
 
+// collect() for two bins in one pass: d1's candidates into L1, d2's into L2; returns the
+// count of d1 and leaves d2's in *n2.
+template <int DT, bool VEC>
+__device__ __forceinline__ int collect2(const ThreshParams& p, const void* lrow, size_t row, const ValueBins& vb, int d1, int d2,
+                        float M, double fix, Collected& L1, Collected& L2, int* n2) {
+  if (threadIdx.x == 0) {
+    L1.n = 0;
+    L2.n = 0;
+  }
+  __syncthreads();
+  for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kTB * kVec * kU) {
+    float s[kU][8];
+    unsigned ok[kU];
+    cand_batch<DT, VEC>(p, lrow, row, e0, (long)kTB * kVec, s, ok);
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (!((ok[u] >> e) & 1u)) continue;
+        const int d = vb.of(s[u][e]);
+        if (d != d1 && d != d2) continue;
+        Collected& L = d == d1 ? L1 : L2;
+        const int i = atomicAdd(&L.n, 1);
+        if (i < kCap) {
+          L.v[i] = s[u][e];
+          L.w[i] = fixed_weight(s[u][e], M, p.c2, fix);
+        }
+      }
+  }
+  __syncthreads();
+  const int n = L1.n;
+  *n2 = L2.n;
+  __syncthreads();
+  return n;
+}
+
 // Among the n collected candidates (one bin) with value >= floor_v: the largest value t with
 // above + the sum of w (mass) or the count over those with value >= t reaching `target`
 // (-inf if none).  Ties share their sum, so the threshold never splits them.
-__device__ float resolve(const Collected& L, int n, float floor_v, bool mass, double above, double target,
+__device__ __forceinline__ float resolve(const Collected& L, int n, float floor_v, bool mass, double above, double target,
                          float* scratch) {
   float best = -INFINITY;
   for (int i = threadIdx.x; i < n; i += kTB) {
@@ -357,7 +394,7 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
   __shared__ double s_scratch[kTW];
   __shared__ SelectLds s_sel;
-  __shared__ Collected s_col;
+  __shared__ Collected s_col, s_col2;
   __shared__ float s_m[kTW], s_mn[kTW];
   __shared__ int s_fault, s_d;
   __shared__ double s_f;
@@ -450,11 +487,32 @@ __global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
           }
       }
       __syncthreads();
-      int dk = -1, n = 0;
+      int dk = -1, n = 0, dpf = -1, n2 = 0;
       double fk = 0.0;
       if (sel_k) {
         dk = find_bin([&](int d) { return d >= 0 ? (double)L.cnt[d] : 0.0; }, 0.0, (double)k, s_scratch, &s_d, &s_f, &fk);
-        if (dk >= 0) n = collect<DT, VEC>(p, lrow, row, vb, dk, M, fix, s_col);
+        if (dk >= 0 && use_p) {
+          // The top-p target is p * (A + part), A the mass of the bins above dk and part the
+          // mass of bin dk's survivors (0 <= part <= mass[dk], known only after tau_k).  When
+          // the targets for both ends fall in the same bin above dk, that bin is collected in
+          // the same pass as dk (every mass is an exact integer, so the true target lies
+          // between the two).
+          double A = 0.0;
+          for (int d = threadIdx.x; d < kBins; d += kTB)
+            if (d > dk) A += (double)L.mass[d];
+          A = block_sum_d(A, s_scratch);
+          const double mdk = (double)L.mass[dk];
+          double f0 = 0.0, f1 = 0.0;
+          const int d0 = find_bin([&](int d) { return d > dk ? (double)L.mass[d] : 0.0; }, 0.0, (double)tp * A,
+                                  s_scratch, &s_d, &s_f, &f0);
+          const int d1 = find_bin([&](int d) { return d > dk ? (double)L.mass[d] : (d == dk ? mdk : 0.0); }, 0.0,
+                                  (double)tp * (A + mdk), s_scratch, &s_d, &s_f, &f1);
+          if (d0 > dk && d1 == d0) dpf = d0;
+        }
+        if (dk >= 0) {
+          if (dpf >= 0) n = collect2<DT, VEC>(p, lrow, row, vb, dk, dpf, M, fix, s_col, s_col2, &n2);
+          else n = collect<DT, VEC>(p, lrow, row, vb, dk, M, fix, s_col);
+        }
         if (dk < 0 || n > kCap) fast = false;
         else tau_k = resolve(s_col, n, -INFINITY, false, fk, (double)k, s_m);
         tau = tau_k;
@@ -483,6 +541,9 @@ __global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
           fast = false;
         } else if (sel_k && dp == dk) {
           tau = resolve(s_col, n, tau_k, true, fp, target, s_m);
+        } else if (dp == dpf) {          // collected with bin dk
+          if (n2 > kCap) fast = false;
+          else tau = resolve(s_col2, n2, -INFINITY, true, fp, target, s_m);
         } else {
           const int n2 = collect<DT, VEC>(p, lrow, row, vb, dp, M, fix, s_col);
           if (n2 > kCap) fast = false;

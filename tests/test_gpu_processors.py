@@ -63,6 +63,20 @@ def test_headline_shape_all_processors():
     print(s, "accepted", np.bincount(got["accepted_len"][got["req_status"] == 0], minlength=6).tolist())
 
 
+@pytest.mark.parametrize("k,tp", [(1000, 0.5), (200, 0.3), (20, 0.9)])
+def test_top_k_and_top_p_bins_collected_together(k, tp):
+    """Both truncations on every request, on peaked rows (1% of entries boosted by +8): the
+    top-p bin usually lies above the top-k bin, and both bins' candidates are then collected
+    in one pass over the row; the result must equal the oracle's."""
+    x = synth.make_chain(32, 4, 32000, seed=int(k * 10 + tp * 100), logit_dtype="bf16", sigma=2.5,
+                         boost_frac=0.01, boost=8.0, noise=1.0, temperature=0.8)
+    bias, words, _, _ = synth.make_processors(x.B, x.gamma + 1, x.V, seed=k, with_top_k=False, with_top_p=False)
+    kk = np.full(x.B, k, np.int32)
+    pp = np.full(x.B, tp, np.float32)
+    say(f"chain_ex top-k {k} and top-p {tp} on every request")
+    check(x, bias, words, kk, pp)
+
+
 @pytest.mark.parametrize("which", ["bias", "mask", "top_k", "top_p"])
 def test_each_processor_alone(which):
     x = synth.make_chain(24, 4, 20003, seed=300, logit_dtype="bf16", sigma=2.0, noise=0.5, temperature=0.9)
