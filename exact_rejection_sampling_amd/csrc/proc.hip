@@ -90,16 +90,23 @@ __device__ __forceinline__ void cand_batch(const ThreshParams& p, const void* lr
         s[u][0] = f[u][0].x; s[u][1] = f[u][0].y; s[u][2] = f[u][0].z; s[u][3] = f[u][0].w;
         s[u][4] = f[u][1].x; s[u][5] = f[u][1].y; s[u][6] = f[u][1].z; s[u][7] = f[u][1].w;
       }
-      if (p.bias) {
-        in[u].b[0] = bl[u].x; in[u].b[1] = bl[u].y; in[u].b[2] = bl[u].z; in[u].b[3] = bl[u].w;
-        in[u].b[4] = bh[u].x; in[u].b[5] = bh[u].y; in[u].b[6] = bh[u].z; in[u].b[7] = bh[u].w;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) in[u].b[j] = 0.0f;
-      }
+      // s = l + b in fp32 (b = 0 without a bias, as the verifier computes it); a candidate is
+      // an allowed token with a finite s.  Masked tokens keep their raw value here: every
+      // use of s other than the NaN / +inf fault test is guarded by the candidate bits.
+      const float b[8] = {p.bias ? bl[u].x : 0.0f, p.bias ? bl[u].y : 0.0f, p.bias ? bl[u].z : 0.0f,
+                          p.bias ? bl[u].w : 0.0f, p.bias ? bh[u].x : 0.0f, p.bias ? bh[u].y : 0.0f,
+                          p.bias ? bh[u].z : 0.0f, p.bias ? bh[u].w : 0.0f};
       const long e = e0 + u * stride;
-      in[u].bits = p.allowed ? (mw[u] >> (e & 31)) & 0xffu : 0xffu;
+      const unsigned bits = p.allowed ? (mw[u] >> (e & 31)) & 0xffu : 0xffu;
+      unsigned m = 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        s[u][j] += b[j];
+        if (__builtin_isfinite(s[u][j])) m |= 1u << j;
+      }
+      ok[u] = m & bits;
     }
+    return;
   } else {
     ProcSpec pr{};
     pr.bias = p.bias;
@@ -136,6 +143,18 @@ struct RadixLds {
   double f_above;
 };
 
+// The weight 2^((s - M) c2) in fixed point with 2^fe units, rounded to the nearest integer
+// (ties to even).  w * 2^fe is exact in fp32 (a power-of-two scaling of a value in [0, 1],
+// fe <= 52), so rounding it in fp32 and splitting it into two exact 32-bit halves gives
+// the same integer as rounding the product in fp64.
+__device__ __forceinline__ unsigned long long fixed_weight(float s, float M, float c2, int fe) {
+  const float w = __builtin_amdgcn_exp2f((s - M) * c2);
+  const float v = rintf(ldexpf(w, fe));
+  const float hi = truncf(v * 0x1p-32f);
+  const float lo = fmaf(hi, -0x1p32f, v);
+  return (static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) | static_cast<unsigned>(lo);
+}
+
 // Block-wide exclusive prefix (fp64) over the kTB threads; *total gets the block sum.
 __device__ double tb_excl_scan(double v, double* scratch, double* total) {
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
@@ -155,14 +174,14 @@ __device__ double tb_excl_scan(double v, double* scratch, double* total) {
 }
 
 // Radix selection of the largest key t >= klo with F(t) >= target, where F(t) is the count
-// (MASS false) or the fixed-point mass (MASS true; weights scaled by `fix`) of the
+// (MASS false) or the fixed-point mass (MASS true; weights in units of 2^-fe) of the
 // candidates with key >= t; keys below klo are ignored.  [klo, khi] bounds the keys; the
 // bits above their highest differing bit are shared.  `param` is the count target k, or the
 // fraction p of the total mass F(klo) that the target is.  Every value stays an integer
 // below 2^53, so the fp64 scans are exact.
 template <int DT, bool VEC, bool MASS>
 __device__ __forceinline__ unsigned radix_select(const ThreshParams& p, const void* lrow, size_t row, unsigned klo, unsigned khi,
-                                 double param, float M, double fix, RadixLds& L) {
+                                 double param, float M, int fe, RadixLds& L) {
   const int tid = threadIdx.x;
   const int nb = (klo == khi) ? 0 : 32 - __clz(klo ^ khi);   // the varying low bits
   unsigned prefix = nb == 32 ? 0u : (klo >> nb);             // the digits chosen so far
@@ -186,7 +205,7 @@ __device__ __forceinline__ unsigned radix_select(const ThreshParams& p, const vo
           const unsigned high = shift + width == 32 ? 0u : (k >> (shift + width));
           if (high != prefix) continue;
           unsigned long long v = 1ull;
-          if constexpr (MASS) v = __double2ull_rn((double)__builtin_amdgcn_exp2f((s[u][e] - M) * p.c2) * fix);   // fixed_weight
+          if constexpr (MASS) v = fixed_weight(s[u][e], M, p.c2, fe);
           atomicAdd(&L.bin[(k >> shift) & ((1u << width) - 1u)], v);
         }
     }
@@ -264,10 +283,6 @@ __device__ __forceinline__ double block_sum_d(double v, double* scratch) {
   return tot;
 }
 
-__device__ __forceinline__ unsigned long long fixed_weight(float s, float M, float c2, double fix) {
-  return __double2ull_rn((double)__builtin_amdgcn_exp2f((s - M) * c2) * fix);
-}
-
 // The largest bin d whose F(d) = above + sum of val over bins >= d reaches `target` (block-
 // wide; -1 if none): returns d and, in *f_above, F(d + 1).  Thread t owns kBinsPerThread
 // consecutive bins, the highest to thread 0.
@@ -299,11 +314,11 @@ __device__ __forceinline__ int find_bin(Val val, double above, double target, do
   return d;
 }
 
-// Collects the candidates of bin d with their weights (fixed-point masses when fix > 0);
+// Collects the candidates of bin d with their weights (fixed-point masses when fe >= 0);
 // returns the number found (which may exceed kCap: then only kCap are stored).
 template <int DT, bool VEC>
 __device__ __forceinline__ int collect(const ThreshParams& p, const void* lrow, size_t row, const ValueBins& vb, int d, float M,
-                       double fix, Collected& L) {
+                       int fe, Collected& L) {
   if (threadIdx.x == 0) L.n = 0;
   __syncthreads();
   for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kTB * kVec * kU) {
@@ -319,7 +334,7 @@ __device__ __forceinline__ int collect(const ThreshParams& p, const void* lrow, 
         const int i = atomicAdd(&L.n, 1);
         if (i < kCap) {
           L.v[i] = s[u][e];
-          L.w[i] = fix > 0.0 ? fixed_weight(s[u][e], M, p.c2, fix) : 1ull;
+          L.w[i] = fe >= 0 ? fixed_weight(s[u][e], M, p.c2, fe) : 1ull;
         }
       }
   }
@@ -333,7 +348,7 @@ __device__ __forceinline__ int collect(const ThreshParams& p, const void* lrow, 
 // count of d1 and leaves d2's in *n2.
 template <int DT, bool VEC>
 __device__ __forceinline__ int collect2(const ThreshParams& p, const void* lrow, size_t row, const ValueBins& vb, int d1, int d2,
-                        float M, double fix, Collected& L1, Collected& L2, int* n2) {
+                        float M, int fe, Collected& L1, Collected& L2, int* n2) {
   if (threadIdx.x == 0) {
     L1.n = 0;
     L2.n = 0;
@@ -354,7 +369,7 @@ __device__ __forceinline__ int collect2(const ThreshParams& p, const void* lrow,
         const int i = atomicAdd(&L.n, 1);
         if (i < kCap) {
           L.v[i] = s[u][e];
-          L.w[i] = fixed_weight(s[u][e], M, p.c2, fix);
+          L.w[i] = fixed_weight(s[u][e], M, p.c2, fe);
         }
       }
   }
@@ -414,29 +429,28 @@ __global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
   // pass 0: the candidates' maximum, minimum and count; NaN / +inf anywhere makes the row
   // invalid for the verifier, and then no threshold is needed
   float m = -INFINITY, mn = INFINITY;
-  double cnt = 0.0;
+  unsigned cnt = 0u;
   bool fault = false;
   for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kTB * kVec * kU) {
     float s[kU][8];
     unsigned ok[kU];
     cand_batch<DT, VEC>(p, lrow, row, e0, (long)kTB * kVec, s, ok);
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
+    for (int u = 0; u < kU; ++u) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const long x = e0 + (long)u * kTB * kVec + e;
-        if (x < p.V && (s[u][e] != s[u][e] || s[u][e] == INFINITY)) fault = true;
-        if ((ok[u] >> e) & 1u) {
-          m = fmaxf(m, s[u][e]);
-          mn = fminf(mn, s[u][e]);
-          cnt += 1.0;
-        }
+        fault |= !(s[u][e] < INFINITY);      // NaN or +inf; positions past the row read as -inf
+        const bool c = (ok[u] >> e) & 1u;
+        m = fmaxf(m, c ? s[u][e] : -INFINITY);
+        mn = fminf(mn, c ? s[u][e] : INFINITY);
       }
+      cnt += __popc(ok[u]);
+    }
   }
   if (fault) s_fault = 1;
   const float wm = wave_max(m);
   const float wmn = -wave_max(-mn);
-  const double wc = wave_sum_d(cnt);
+  const double wc = wave_sum_d(static_cast<double>(cnt));
   if (lane == 0) {
     s_m[wave] = wm;
     s_mn[wave] = wmn;
@@ -456,7 +470,7 @@ __global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
   if (!s_fault && C > 0.0) {
     const bool sel_k = use_k && (double)k < C;
     // the largest scale that keeps every sum of fixed-point weights (each <= 1) below 2^53
-    const double fix = use_p ? ldexp(1.0, 52 - (64 - __clzll(static_cast<unsigned long long>(C)))) : 0.0;
+    const int fe = use_p ? 52 - (64 - __clzll(static_cast<unsigned long long>(C))) : -1;
     ValueBins vb;
     vb.lo = MN;
     vb.scale = static_cast<float>(kBins) / (M - MN);
@@ -483,7 +497,7 @@ __global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
             if (!((ok[u] >> e) & 1u)) continue;
             const int d = vb.of(s[u][e]);
             if (sel_k) atomicAdd(&L.cnt[d], 1u);
-            if (use_p) atomicAdd(&L.mass[d], fixed_weight(s[u][e], M, p.c2, fix));
+            if (use_p) atomicAdd(&L.mass[d], fixed_weight(s[u][e], M, p.c2, fe));
           }
       }
       __syncthreads();
@@ -510,8 +524,8 @@ __global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
           if (d0 > dk && d1 == d0) dpf = d0;
         }
         if (dk >= 0) {
-          if (dpf >= 0) n = collect2<DT, VEC>(p, lrow, row, vb, dk, dpf, M, fix, s_col, s_col2, &n2);
-          else n = collect<DT, VEC>(p, lrow, row, vb, dk, M, fix, s_col);
+          if (dpf >= 0) n = collect2<DT, VEC>(p, lrow, row, vb, dk, dpf, M, fe, s_col, s_col2, &n2);
+          else n = collect<DT, VEC>(p, lrow, row, vb, dk, M, fe, s_col);
         }
         if (dk < 0 || n > kCap) fast = false;
         else tau_k = resolve(s_col, n, -INFINITY, false, fk, (double)k, s_m);
@@ -545,7 +559,7 @@ __global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
           if (n2 > kCap) fast = false;
           else tau = resolve(s_col2, n2, -INFINITY, true, fp, target, s_m);
         } else {
-          const int n2 = collect<DT, VEC>(p, lrow, row, vb, dp, M, fix, s_col);
+          const int n2 = collect<DT, VEC>(p, lrow, row, vb, dp, M, fe, s_col);
           if (n2 > kCap) fast = false;
           else tau = resolve(s_col, n2, -INFINITY, true, fp, target, s_m);
         }
@@ -556,11 +570,11 @@ __global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
       unsigned lo = key_of(MN);
       const unsigned hi = key_of(M);
       if (sel_k) {
-        lo = radix_select<DT, VEC, false>(p, lrow, row, lo, hi, (double)k, M, 1.0, s_sel.radix);
+        lo = radix_select<DT, VEC, false>(p, lrow, row, lo, hi, (double)k, M, -1, s_sel.radix);
         tau = value_of(lo);
       }
       if (use_p) {
-        const unsigned t = radix_select<DT, VEC, true>(p, lrow, row, lo, hi, (double)tp, M, fix, s_sel.radix);
+        const unsigned t = radix_select<DT, VEC, true>(p, lrow, row, lo, hi, (double)tp, M, fe, s_sel.radix);
         tau = value_of(t);
       }
     }
