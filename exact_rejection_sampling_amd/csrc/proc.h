@@ -16,8 +16,8 @@ namespace sv {
 // and +inf pass through, so a faulty row stays invalid whatever the mask.
 __device__ __forceinline__ float proc_elem(float l, float b, bool allowed, float tau) {
   const float s = l + b;
-  if (s != s || s == INFINITY) return s;
-  return (allowed && s >= tau) ? s : -INFINITY;
+  // NaN and +inf pass through (!(s < inf) holds for exactly those two)
+  return (!(s < INFINITY) || (allowed && s >= tau)) ? s : -INFINITY;
 }
 
 // The processor inputs of 8 elements [e0, e0 + 8) of row `row` (e0 a multiple of 8, so the
@@ -47,10 +47,14 @@ __device__ __forceinline__ void proc8_load(const ProcSpec& pr, size_t row, long 
 }
 
 // Processors applied to 8 loaded logits; elements at or past V are left as they are.
+// VEC (V % 8 == 0): the 8 positions are all inside the row or all past it, and a vector
+// past it holds -inf with a zero bias, which the transform leaves at -inf, so no position
+// needs a bounds test.
+template <bool VEC>
 __device__ __forceinline__ void proc8_apply(const Proc8In& in, float tau, long e0, long V, float (&v)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    if (e0 + j < V) v[j] = proc_elem(v[j], in.b[j], (in.bits >> j) & 1u, tau);
+    if (VEC || e0 + j < V) v[j] = proc_elem(v[j], in.b[j], (in.bits >> j) & 1u, tau);
 }
 
 // Processors over this lane's 8 elements [e0, e0 + 8) of row `row`.
@@ -58,7 +62,7 @@ template <bool VEC>
 __device__ __forceinline__ void proc8(const ProcSpec& pr, size_t row, float tau, long e0, long V, float (&v)[8]) {
   Proc8In in;
   proc8_load<VEC>(pr, row, e0, V, in);
-  proc8_apply(in, tau, e0, V, v);
+  proc8_apply<VEC>(in, tau, e0, V, v);
 }
 
 // The processed value of one element x of row `row`.

@@ -120,7 +120,7 @@ __device__ __forceinline__ void cand_batch(const ThreshParams& p, const void* lr
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const long e = e0 + u * stride;
-    proc8_apply(in[u], -INFINITY, e, p.V, s[u]);
+    proc8_apply<VEC>(in[u], -INFINITY, e, p.V, s[u]);
     unsigned m = 0u;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
