@@ -77,6 +77,19 @@ def test_top_k_and_top_p_bins_collected_together(k, tp):
     check(x, bias, words, kk, pp)
 
 
+@pytest.mark.parametrize("V,T", [(40, 0.05), (40, 50.0), (3000, 0.05), (3000, 50.0), (100000, 20.0)])
+def test_top_p_weight_scales(V, T):
+    """Top-p masses are fixed-point integers with a scale set by the candidate count (up to
+    2^51 units per weight when few tokens are candidates).  Small vocabularies and extreme
+    temperatures (weights close to 1, or all but the top ones close to 0) reach the widest
+    integers and the most rounding; results must equal the oracle's."""
+    x = synth.make_chain(24, 3, V, seed=V + int(T * 100), logit_dtype="f32", sigma=2.0, noise=0.8, temperature=T)
+    bias, words, k, p = synth.make_processors(x.B, x.gamma + 1, x.V, seed=V, top_k=(0, 5, 30),
+                                              top_p=(0.3, 0.7, 0.95))
+    say(f"chain_ex top-p weight scales V={V} T={T}")
+    check(x, bias, words, k, p)
+
+
 @pytest.mark.parametrize("which", ["bias", "mask", "top_k", "top_p"])
 def test_each_processor_alone(which):
     x = synth.make_chain(24, 4, 20003, seed=300, logit_dtype="bf16", sigma=2.0, noise=0.5, temperature=0.9)
