@@ -1,6 +1,6 @@
 // Keep thresholds of top-k and top-p (the pre-pass of spec_verify_chain_ex).
 //
-// One block per row.  A token is a candidate when it is allowed and s = l + b (fp32) is
+// One 512-thread block per row.  A token is a candidate when it is allowed and s = l + b (fp32) is
 // finite; a candidate's key is an order-preserving map of s to 32 bits.
 //  * top-k (k >= 1, fewer than k candidates: off): tau_k = the k-th largest key, with
 //    multiplicity -- the largest key t with #{candidates with key >= t} >= k.
@@ -15,7 +15,7 @@
 // where the count or mass from the top reaches its target, (2) a pass that collects that
 // bin's candidates into LDS, and an exact resolution among them.  With both selections on,
 // one collecting pass serves both whenever the top-p bin is fixed before tau_k is.  A bin with more than
-// 2048 candidates (values piled on a few points) falls back to radix selection over the
+// 1024 candidates (values piled on a few points) falls back to radix selection over the
 // bits in which the candidate keys differ, 12 bits per pass.  The row's threshold is tau_p
 // when top-p is on (it is at least tau_k), else tau_k, or -inf.
 //
@@ -42,8 +42,9 @@ __device__ __forceinline__ float value_of(unsigned k) {
 
 // Elements per thread and loop step: kU vectors of 8, kTB * 8 elements apart, whose loads
 // (logits, bias, mask words) are all issued before any is used -- one memory latency per
-// step instead of one per vector.  (Three or four vectors exceed the 128 registers a
-// 1024-thread block allows and spill.)
+// step instead of one per vector.  (Deeper batches fit the 128 registers per thread but
+// measured slower: the pass is bound by its per-element arithmetic and LDS atomics as much
+// as by memory latency.)
 constexpr int kU = 2;
 
 // The candidates of this thread's kU vectors at e0, e0 + stride, ...: processed values
@@ -129,8 +130,13 @@ __device__ __forceinline__ void cand_batch(const ThreshParams& p, const void* lr
   }
 }
 
-// 1024 threads (16 waves) per row: enough waves per SIMD to hide the per-element chain.
-constexpr int kTB = 1024;
+// 512 threads (8 waves) per row, at most 128 registers and about 73 KB of LDS, so that two
+// blocks share a CU and a batch's rows (384 at the headline shape) run in one round on 256
+// CUs rather than two (measured 4% faster than one 1024-thread block per CU).
+#ifndef SPEC_THRESH_TB
+#define SPEC_THRESH_TB 512
+#endif
+constexpr int kTB = SPEC_THRESH_TB;
 constexpr int kTW = kTB / kWave;
 constexpr int kDigit = 12;
 constexpr int kBins = 1 << kDigit;
@@ -253,7 +259,7 @@ __device__ __forceinline__ unsigned radix_select(const ThreshParams& p, const vo
 // piles most of a row into a few dozen bins).  bin(s) is monotone in s, ties share a bin,
 // and every count and mass is an integer sum, so the result is the radix selection's.  A
 // bin with more than kCap candidates falls back to the radix selection.
-constexpr int kCap = 2048;
+constexpr int kCap = kTB >= 1024 ? 2048 : 1024;
 
 struct BinLds {
   unsigned cnt[kBins];
@@ -406,7 +412,7 @@ __device__ __forceinline__ float resolve(const Collected& L, int n, float floor_
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kTB) void thresh_kernel(ThreshParams p) {
+__global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(ThreshParams p) {
   __shared__ double s_scratch[kTW];
   __shared__ SelectLds s_sel;
   __shared__ Collected s_col, s_col2;
