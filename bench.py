@@ -264,6 +264,36 @@ def bench_chain_stop(args, torch, sv, synth):
                 finish_counts=dict(open=int(fin[0]), stop=int(fin[1]), budget=int(fin[2])))
 
 
+def bench_chain_sparse(args, torch, sv, synth):
+    """The headline chain workload with a top-K drafter (K = 64): draft rows given as K
+    (index, value) pairs, so a rejecting request reads 8 K bytes of its q row instead of 4 V.
+    Algorithmic bytes: every target row once, the K pairs of each rejecting request's row."""
+    K = 64
+    spec = dict(synth.CONFIGS[3])
+    spec.pop("kind")
+    B, G, V = spec.pop("B"), spec.pop("gamma"), spec.pop("V")
+    x, idx, vals = synth.make_chain_sparse(B, G, V, K, seed=0, **spec)
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    it, vt = torch.from_numpy(idx).to(dev), torch.from_numpy(vals).to(dev)
+    tt, ut = torch.from_numpy(x.tokens).to(dev), torch.from_numpy(x.u).to(dev)
+    sets = device_copies(lambda: lt.clone(), lt.numel() * 2)
+    del lt
+    stream = torch.cuda.current_stream()
+    ws = torch.zeros(sv.chain_workspace_bytes(B, G, V) + 512, dtype=torch.uint8, device=dev)
+    calls = [sv.prepare_chain(s, vt, tt, ut, float(x.temperature), workspace_tensor=ws, q_index=it) for s in sets]
+    span, per = time_calls(calls, max(100, args.steps // 2), args.warmup, stream)
+    acc = calls[0].out["accepted_len"].cpu().numpy()
+    n_rej = int((acc < G).sum())
+    alg = B * (G + 1) * V * 2 + n_rej * K * 8 + B * G * 10 + B * (G + 1) * 4
+    launch = span / len(per)
+    del sets, calls
+    return dict(workload=f"chain B={B} gamma={G} V={V} bf16 logits, sparse draft rows K={K}, T={spec['temperature']}",
+                positions_per_s=B * (G + 1) * len(per) / span, us_per_call=launch * 1e6,
+                evented_call_mean_us=float(per.mean()) * 1e3, rejecting_requests=n_rej, alg_bytes_per_call=alg,
+                alg_gbs=alg / launch / 1e9, alg_frac=alg / launch / 1e9 / HBM_PEAK_GBS)
+
+
 def bench_chain_proc(args, torch, sv, synth, truncate):
     """The headline chain workload through spec_verify_chain_ex with target logit processors:
     fp32 bias and 90%-allowed masks per row, plus (truncate) top-k in {0, 1, 20, 1000} and
@@ -442,7 +472,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary", default="all",
                     help="comma-separated secondary lines to run (greedy, tree, tree_residual, tree_greedy, "
-                         "chain_stop, chain_bias_mask, chain_processors, chain_lazy, chain_f32, greedy_lazy), or all")
+                         "chain_stop, chain_bias_mask, chain_processors, chain_sparse, chain_lazy, chain_f32, greedy_lazy), or all")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true",
@@ -519,6 +549,8 @@ def main():
             lambda: bench_chain_proc(args, torch, sv, synth, False))
         run("chain_processors", "chain_processors", "chain with every processor",
             lambda: bench_chain_proc(args, torch, sv, synth, True))
+        run("chain_sparse", "chain_sparse", "chain with sparse draft rows",
+            lambda: bench_chain_sparse(args, torch, sv, synth))
         for k in (3, 2):
             run("chain_lazy", f"chain_lazy{k}", f"chain with lazy rows, groups of {k}",
                 lambda: bench_chain_lazy(args, torch, sv, synth, k))

@@ -76,12 +76,15 @@ __device__ __forceinline__ void gather_issue(const ChainParams& p, int b, int i,
 // q_i(x) of a sparse draft row, block-wide: the sum of the values listed at index x (each
 // thread sums its share of the entries in order, then a fixed-order block sum); every
 // thread receives it.  Contains two barriers.
-__device__ float sparse_q_lookup(const ChainParams& p, int b, int i, int x, float* scratch) {
+// The thread's first entry (x0, v0; has0 when it exists) was loaded by the caller before
+// streaming the row.
+__device__ float sparse_q_lookup(const ChainParams& p, int b, int i, int x, float* scratch, bool has0, int x0,
+                                 float v0) {
   const size_t base = ((size_t)b * p.G + i) * p.q_k;
   const float* val = static_cast<const float*>(p.q) + base;
   const int32_t* idx = p.q_index + base;
-  float acc = 0.0f;
-  for (int j = threadIdx.x; j < p.q_k; j += kBlock)
+  float acc = (has0 && x0 == x) ? v0 : 0.0f;
+  for (int j = threadIdx.x + kBlock; j < p.q_k; j += kBlock)
     if (idx[j] == x) acc += val[j];
   const float w = wave_sum(acc);
   if ((threadIdx.x & (kWave - 1)) == 0) scratch[wave_id()] = w;
@@ -150,6 +153,22 @@ __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
   const bool gathers = slice == 0 && i < p.G && threadIdx.x == 0;
   unsigned gx = 0, gl = 0, gq = 0;
   if (gathers) gather_issue<DT, QT, PROC>(p, b, i, gx, gl, gq);
+  // sparse draft rows: the draft token and this thread's first entry are loaded before the
+  // stream too, so the lookup after it costs no further memory round trip
+  int sp_t = 0, sp_x0 = 0;
+  float sp_v0 = 0.0f;
+  bool sp_has0 = false;
+  if constexpr (QT == kSparseQ) {
+    if (slice == 0 && i < p.G) {
+      sp_t = p.tokens[(size_t)b * p.G + i];
+      const size_t base = ((size_t)b * p.G + i) * p.q_k;
+      sp_has0 = (int)threadIdx.x < p.q_k;
+      if (sp_has0) {
+        sp_x0 = p.q_index[base + threadIdx.x];
+        sp_v0 = static_cast<const float*>(p.q)[base + threadIdx.x];
+      }
+    }
+  }
   // wave w streams chunks first + 4k of this slice (k < CPW)
   const long first = (long)slice * kWavesPerBlock * p.CPW + wave;
   float m, z;
@@ -165,9 +184,8 @@ __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
   if constexpr (QT == kSparseQ) {
     if (slice == 0 && i < p.G) {        // block-uniform: the whole block searches the row
       __shared__ float s_q[kWavesPerBlock];
-      const int t = p.tokens[(size_t)b * p.G + i];
-      const float qx = sparse_q_lookup(p, b, i, t, s_q);
-      if (gathers && t >= 0 && t < p.V) gq = __float_as_uint(qx);
+      const float qx = sparse_q_lookup(p, b, i, sp_t, s_q, sp_has0, sp_x0, sp_v0);
+      if (gathers && sp_t >= 0 && sp_t < p.V) gq = __float_as_uint(qx);
     }
   }
   if (gathers) gather_publish(p, b, i, gx, gl, gq);
@@ -428,19 +446,28 @@ __device__ __forceinline__ void term_chunk(const ChainParams& p, const void* lro
     __shared__ float s_qd[kTermChunk];
     __shared__ int s_qbad;
     const int tid = threadIdx.x;
-    for (int j = tid; j < kTermChunk; j += kBlock) s_qd[j] = 0.0f;
-    if (tid == 0) s_qbad = 0;
-    __syncthreads();
     const size_t base = ((rowid / p.R) * p.G + d.A) * p.q_k;
     const float* val = static_cast<const float*>(p.q) + base;
     const int32_t* idx = p.q_index + base;
     const long lo = (long)c * kTermChunk;
-    for (int j = tid; j < p.q_k; j += kBlock) {
-      const int x = idx[j];
-      const float v = val[j];
+    // this thread's first entry is loaded before the barrier, together with the logits
+    // (the barrier waits for both), so the row costs one memory round trip, not two
+    const bool has0 = tid < p.q_k;
+    int x0 = 0;
+    float v0 = 0.0f;
+    if (has0) {
+      x0 = idx[tid];
+      v0 = val[tid];
+    }
+    for (int j = tid; j < kTermChunk; j += kBlock) s_qd[j] = 0.0f;
+    if (tid == 0) s_qbad = 0;
+    __syncthreads();
+    auto add = [&](int x, float v) {
       if (x < 0 || x >= p.V || !(v >= 0.0f && v < INFINITY)) s_qbad = 1;
       else if (x >= lo && x < lo + kTermChunk) atomicAdd(&s_qd[x - lo], v);
-    }
+    };
+    if (has0) add(x0, v0);
+    for (int j = tid + kBlock; j < p.q_k; j += kBlock) add(idx[j], val[j]);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < kTermSlabs; ++s)
