@@ -607,9 +607,14 @@ __device__ __forceinline__ void store_wt(float* p, float v) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait until this thread's outstanding memory operations have completed (a
-// workgroup-scope release: no cache maintenance on this target).
-__device__ __forceinline__ void vmem_wait() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup"); }
+// Wait until every vector memory operation this thread has issued has completed.  A
+// write-through store (publish_*, clear_*) has then reached the level every XCD reads
+// from, so any store this thread issues afterwards becomes visible to other blocks after
+// it.  This is the ordering point of a handoff: data words, vmem_wait(), then the word
+// that tells the reader to look.  (A workgroup-scope release fence would not do: with a
+// workgroup confined to one CU it compiles to no wait at all.)  The "memory" clobber keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void vmem_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Count one arrival; returns the count before this one.
 __device__ __forceinline__ unsigned arrive(unsigned* counter) {

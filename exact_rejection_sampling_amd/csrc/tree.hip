@@ -162,9 +162,17 @@ constexpr unsigned kResidualPass = 0x40000000u;
 // ------------------------------------------------------------ residual-update verifier
 // Descriptor of the residual passes at the current node v, written by the walker before
 // each pass order: [0] v, [1] bits of r (reference exponent of row v), [2] bits of 1/Z
-// (base 2), [4 + j] the j-th rejected child, [4 + N + j] bits of 1/W_j, W_j the mass of
-// the residual after j + 1 rejections.
+// (base 2), [3] the generation of the pass order it is complete for, [4 + j] the j-th
+// rejected child, [4 + N + j] bits of 1/W_j, W_j the mass of the residual after j + 1
+// rejections.  The walker (one thread) writes every word through, waits for those stores
+// to complete (vmem_wait), then writes word 3 and the order.  A helper that sees the order
+// re-reads word 3 until it holds the order's generation before it reads the rest, so it
+// never reads a descriptor older than its order, whichever store arrives first.
 constexpr int kResidStage = 256;   // rejected children a helper keeps in LDS per pass
+// A chunk-mass word meaning "the helper's descriptor never became current": the walker
+// reports SPEC_REQ_INTERNAL on it.  (A published mass is a negated fp64 value; this is a
+// NaN bit pattern that no negated mass takes.)
+constexpr unsigned long long kLostMassWord = 0x7ff4000000000001ull;
 
 // The unnormalized residual after i rejected children c_0..c_{i-1} at node v for the
 // eight elements [e0, e0 + 8): p(x) = 2^(l c2 - r) / Z, res_0 = p,
@@ -201,8 +209,26 @@ template <int DT, int QT, bool VEC>
 __device__ void residual_pass(const TreeParams& p, int b, int h, unsigned gen, int i) {
   __shared__ int s_kid[kResidStage];
   __shared__ float s_invw[kResidStage];
+  __shared__ int s_current;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   const unsigned* d = p.desc + (size_t)b * p.desc_words;
+  if (tid == 0) {
+    unsigned tag = fetch_u32(d + 3);
+    for (unsigned spins = 0; tag != gen && spins < kSpinLimit; ++spins) {
+      __builtin_amdgcn_s_sleep(1);
+      tag = fetch_u32(d + 3);
+    }
+    s_current = tag == gen;
+  }
+  __syncthreads();
+  if (!s_current) {   // the wait bound: say so in every chunk mass this helper owns
+    double* dst = reinterpret_cast<double*>(p.deep + ((size_t)b * 2 + (gen & 1u)) * p.P);
+    for (int k = tid; k < kTreeHelperChunks; k += kBlock) {
+      const int c = h * kTreeHelperChunks + k;
+      if (c < p.P) publish_u64(reinterpret_cast<unsigned long long*>(dst + c), kLostMassWord);
+    }
+    return;
+  }
   const int v = static_cast<int>(fetch_u32(d));
   const float r = __uint_as_float(fetch_u32(d + 1)), inv_z = __uint_as_float(fetch_u32(d + 2));
   for (int j = tid; j < min(i, kResidStage); j += kBlock) {
@@ -564,7 +590,8 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
           publish_u32(d + 2, __float_as_uint(inv_z));
         }
         publish_u32(d + 4 + i, static_cast<unsigned>(c));
-        vmem_wait();                      // the descriptor is complete before the order
+        vmem_wait();                      // every descriptor word has completed: then its tag
+        publish_u32(d + 3, gen + 1u);
         publish_order(p, b, ++gen, kResidualPass | static_cast<unsigned>(i + 1));
         s_gen = gen;
         s_lost = 0;
@@ -575,7 +602,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
       double* mw = reinterpret_cast<double*>(p.deep + ((size_t)b * 2 + (gen & 1u)) * P);
       for (int k = tid; k < P; k += kBlock) {
         const unsigned long long bits = await_u64(reinterpret_cast<const unsigned long long*>(mw + k));
-        if (bits == 0ull) s_lost = 1;
+        if (bits == 0ull || bits == kLostMassWord) s_lost = 1;
         s_mass[k] = -__longlong_as_double(static_cast<long long>(bits));
         clear_u64(reinterpret_cast<unsigned long long*>(mw + k));
       }
