@@ -164,6 +164,7 @@ spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, con
   p.part = reinterpret_cast<float2*>(ws + L.part);
   p.gath = reinterpret_cast<unsigned long long*>(ws + L.gath);
   p.tmass = reinterpret_cast<double*>(ws + L.tmass);
+  p.xmass = reinterpret_cast<double*>(ws + L.xmass);
   p.B = B;
   p.G = gamma;
   p.R = gamma + 1;
@@ -180,6 +181,7 @@ spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, con
   const double c2 = kLog2e / static_cast<double>(temperature);
   p.c2 = static_cast<float>(c2);
   p.inv_t = 1.0 / static_cast<double>(temperature);
+  p.c2d = kLog2e / static_cast<double>(temperature);
   const bool vec = (V % 8 == 0) && aligned16(target_logits) &&
                    (gamma == 0 || p.q_index || aligned16(draft_probs)) && (!o.bias || aligned16(o.bias));
   if (truncate) {

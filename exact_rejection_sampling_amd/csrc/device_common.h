@@ -488,6 +488,30 @@ __device__ __forceinline__ float scaled_exp(float l, float c2, float r) {
   return __builtin_amdgcn_exp2f(fmaf(l, c2, -r));
 }
 
+// 2^t in fp64 with a relative error below 4e-13 for -1020 <= t <= 1 (0 below, and for
+// -inf).  t = k + f with k the nearest integer, so |f| <= 1/2; 2^f = e^(f ln 2) is the
+// Taylor series of the exponential to degree 10 (coefficients (ln 2)^i / i!; the first
+// omitted term is below 3.1e-13 at |f| = 1/2), evaluated by Horner's rule; then the
+// exponent is added.  Used where a residual row's weights must carry more precision than
+// the hardware fp32 exp2 gives: a residual mass W scales every rounding error by 1/W.
+__device__ __forceinline__ double exp2_acc(double t) {
+  if (!(t >= -1020.0)) return 0.0;
+  const double k = __builtin_rint(t);
+  const double f = t - k;
+  double s = 0x1.e4cf5158b8ecap-28;             // (ln 2)^10 / 10!
+  s = fma(s, f, 0x1.b5253d395e7c4p-24);         // (ln 2)^9 / 9!
+  s = fma(s, f, 0x1.62c0223a5c824p-20);
+  s = fma(s, f, 0x1.ffcbfc588b0c7p-17);
+  s = fma(s, f, 0x1.430912f86c787p-13);
+  s = fma(s, f, 0x1.5d87fe78a6731p-10);
+  s = fma(s, f, 0x1.3b2ab6fba4e77p-7);
+  s = fma(s, f, 0x1.c6b08d704a0c0p-5);
+  s = fma(s, f, 0x1.ebfbdff82c58fp-3);
+  s = fma(s, f, 0x1.62e42fefa39efp-1);          // ln 2
+  s = fma(s, f, 1.0);
+  return ldexp(s, static_cast<int>(k));
+}
+
 // ------------------------------------------------------------------ argmax pieces
 // Per-lane argmax over one chunk's values (a lane's positions base + (j*64 + lane)*8 + e
 // rise with j and e): keeps the maximum and the lowest position holding it, notes NaN.

@@ -63,6 +63,8 @@ struct ChainParams {
   float2* part;              // [B*R*SL] block summaries (raw max, Z)
   unsigned long long* gath;  // [B*G*3] draft token, its logit, its draft probability
   double* tmass;             // [B*S2] terminal chunk masses
+  double* xmass;             // [B*S2*3] exact pass: per chunk residual mass, positive-set
+                             // e-mass, e-mass (see chain.hip, chain_exact_kernel)
   int B, G, R, V;
   int P;                     // wave chunks per row = ceil(V / 2048)
   int CPW;                   // wave chunks each wave streams per slice
@@ -75,6 +77,7 @@ struct ChainParams {
   int q_dtype;
   float c2;                  // fp32(log2(e) / T)
   double inv_t;              // 1 / T, T widened exactly from fp32
+  double c2d;                // log2(e) / T in fp64 (the exact pass's exponent slope)
 };
 
 #ifndef SPEC_TERM_SLABS
@@ -180,7 +183,7 @@ inline unsigned* request_counters(void* ws) {
 // slot s of request b: request_counters(ws)[b * kCounterSlots + s]
 
 struct ChainLayout {
-  size_t part, gath, tmass, thresh, total;
+  size_t part, gath, tmass, thresh, xmass, total;
 };
 // The chain's statistics pass uses finer slices than the other streaming passes: its
 // terminal items fill the statistics tail, which shrinks as the slices do.
@@ -198,6 +201,7 @@ inline ChainLayout chain_layout(long B, long G, long V) {
   L.gath = o;   o = align256(o + sizeof(unsigned long long) * 3 * B * G);
   L.tmass = o;  o = align256(o + sizeof(double) * B * S2);
   L.thresh = o; o = align256(o + sizeof(float) * B * R);
+  L.xmass = o;  o = align256(o + sizeof(double) * 3 * B * S2);
   L.total = o;
   return L;
 }

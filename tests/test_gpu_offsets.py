@@ -51,7 +51,7 @@ def test_chain_processors():
     L, pflag = oracle.process_rows(x.logits, "bf16", x.temperature, bias, words, k, p)
     exp = oracle.verify_chain(L, x.q, x.tokens, x.u, x.temperature, "f64")
     exp["flagged"] = exp["flagged"] | pflag
-    print(compare_chain(to_np(out), exp))
+    print(compare_chain(to_np(out), exp, max_flag_frac=0.5))   # top-p windows: see test_gpu_processors
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])

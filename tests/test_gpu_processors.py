@@ -44,9 +44,9 @@ def oracle_chain_proc(x, bias, words, top_k, top_p, stop=(), budget=None):
 def check(x, bias, words, top_k, top_p, stop=None, budget=None):
     got = run_chain_proc(x, bias, words, top_k, top_p, stop, budget)
     exp = oracle_chain_proc(x, bias, words, top_k, top_p, () if stop is None else stop.tolist(), budget)
-    s = compare_chain(got, exp)
-    # the comparison must cover most requests: flags are for rare near-ties only
-    assert (~exp["flagged"]).sum() >= (len(exp["flagged"]) + 1) // 2, exp["flagged"].sum()
+    # flags also cover top-p boundaries within TOP_P_FLAG of the target mass, which the
+    # chain's flag expectation does not include: a fixed allowance, at most half the batch
+    s = compare_chain(got, exp, max_flag_frac=0.5)
     if stop is not None or budget is not None:
         keep = ~exp["flagged"]
         np.testing.assert_array_equal(got["finish"][keep], exp["finish"][keep])
