@@ -399,6 +399,266 @@ def bench_sweep(args, torch, sv, synth):
             torch.cuda.empty_cache()
 
 
+TRACE_WORDS = 8          # words per block record of the timeline-trace build
+TRACE_KERNELS = 4        # kernel slots: 0 chain, 1 chain exact redraw, 2 tree, 3 residual tree
+TICK_US = 0.01           # s_memrealtime runs at 100 MHz
+
+
+def _trace_records(buf, cap):
+    """The trace buffer as {slot: (tag fields, stamps in us)} for the blocks that wrote a tag."""
+    a = buf.cpu().numpy().view(np.uint64).reshape(TRACE_KERNELS, cap, TRACE_WORDS)
+    out = {}
+    for k in range(TRACE_KERNELS):
+        r = a[k][(a[k][:, 0] >> np.uint64(63)) == 1]
+        tag = r[:, 0]
+        out[k] = dict(kind=((tag >> np.uint64(56)) & np.uint64(0x7f)).astype(int),
+                      b=((tag >> np.uint64(24)) & np.uint64(0xffffffff)).astype(int),
+                      idx=(tag & np.uint64(0xffffff)).astype(int),
+                      t=r[:, 1:].astype(np.int64))
+    return out
+
+
+def _med(v):
+    v = np.asarray(v, dtype=float)
+    v = v[np.isfinite(v)]
+    return float(np.median(v)) if v.size else float("nan")
+
+
+def timeline_chain(args, torch, sv, synth, lib):
+    """Per-block timeline of the headline chain call from the trace build: when the statistics
+    stream ends, and each selector's steps (decision, own chunk mass, every mass in, rescan,
+    outputs, workspace cleared), then the exact-redraw kernel.  Prints a markdown summary."""
+    import ctypes
+    x = synth.make_config(3, 0)
+    B, G, V = x.B, x.gamma, x.V
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    qt = torch.from_numpy(x.q).to(dev)
+    tt, ut = torch.from_numpy(x.tokens).to(dev), torch.from_numpy(x.u).to(dev)
+    sets = device_copies(lambda: (lt.clone(), qt.clone()), lt.numel() * 2 + qt.numel() * 4)
+    del lt, qt
+    ws = torch.zeros(sv.chain_workspace_bytes(B, G, V) + 512, dtype=torch.uint8, device=dev)
+    calls = [sv.prepare_chain(s_[0], s_[1], tt, ut, float(x.temperature), workspace_tensor=ws) for s_ in sets]
+    stream = torch.cuda.current_stream()
+    cap = 8192
+    buf = torch.zeros(TRACE_KERNELS * cap * TRACE_WORDS, dtype=torch.int64, device=dev)
+    assert lib.spec_trace_set(ctypes.c_void_p(0), 0) == 0
+    span_off, _ = time_calls(calls, args.steps, args.warmup, stream)
+    assert lib.spec_trace_set(ctypes.c_void_p(buf.data_ptr()), cap) == 0
+    span_on, _ = time_calls(calls, args.steps, args.warmup, stream)
+    rows = []
+    for rep in range(args.timeline_calls):
+        buf.zero_()
+        torch.cuda.synchronize()
+        calls[rep % len(calls)]()
+        torch.cuda.synchronize()
+        rec = _trace_records(buf, cap)
+        c, e = rec[0], rec[1]
+        t = c["t"].astype(float)
+        t[t == 0] = np.nan
+        base = np.nanmin(t[:, 0])
+        t = (t - base) * TICK_US
+        kind, b = c["kind"], c["b"]
+        S, L = kind == 0, kind == 3
+        chain_end = np.nanmax(t)
+        stats_done = np.array([np.nanmax(t[S & (b == r), 1]) for r in range(B)])
+        sel = {r: t[L & (b == r)][0] for r in range(B)}
+        steps = np.array([[sel[r][1] - sel[r][0],                 # start -> decided
+                           sel[r][2] - sel[r][1],                 # decided -> own chunk mass
+                           sel[r][3] - sel[r][2],                 # own mass -> every mass in
+                           sel[r][4] - sel[r][3],                 # masses in -> rescan done
+                           sel[r][5] - sel[r][4],                 # rescan -> outputs written
+                           sel[r][6] - sel[r][5]] for r in range(B)])
+        sel_end = np.array([sel[r][6] for r in range(B)])
+        last = int(np.argmax(sel_end))
+        et = e["t"].astype(float)
+        et[et == 0] = np.nan
+        et = (et - base) * TICK_US
+        k3_start, k3_end = np.nanmin(et[:, 0]), np.nanmax(et)
+        rows.append(dict(chain_end=chain_end, stream_end=float(np.nanmax(t[S, 1])),
+                         stats_item=_med(t[S, 2] - t[S, 0]), last_req_stats=float(stats_done.max()),
+                         sel_start_last=float(sel[last][0]), sel_end_last=float(sel_end[last]),
+                         steps_med=np.median(steps, axis=0), steps_last=steps[last],
+                         after_stats_last=float(sel_end[last] - stats_done[last]),
+                         k3_gap=float(k3_start - chain_end), k3_span=float(k3_end - k3_start),
+                         k3_exact=int((e["kind"] == 5).sum()), total=float(k3_end)))
+    assert lib.spec_trace_set(ctypes.c_void_p(0), 0) == 0
+    g = lambda k: _med([r_[k] for r_ in rows])
+    sm = np.median(np.array([r_["steps_med"] for r_ in rows]), axis=0)
+    sl = np.median(np.array([r_["steps_last"] for r_ in rows]), axis=0)
+    names = ["dispatch -> decision", "decision -> own chunk mass", "own mass -> every mass in",
+             "masses in -> rescan done", "rescan -> outputs written", "outputs -> workspace cleared"]
+    print(f"## chain_kernel timeline: B={B} gamma={G} V={V} bf16 logits, fp32 q, T={x.temperature}")
+    print()
+    print(f"Trace build, {args.timeline_calls} traced calls; medians over calls. Times in us from the "
+          f"first block's start (s_memrealtime, 10 ns ticks). Calls of the trace build: "
+          f"{span_off / args.steps * 1e6:.1f} us with tracing off, {span_on / args.steps * 1e6:.1f} us on "
+          f"(event span / {args.steps} back-to-back calls).")
+    print()
+    print("| event | us |")
+    print("|---|---|")
+    print(f"| median statistics item (start -> published) | {g('stats_item'):.2f} |")
+    print(f"| statistics stream ends (last item's stream done) | {g('stream_end'):.2f} |")
+    print(f"| last-finishing request: its statistics done | {g('last_req_stats'):.2f} |")
+    print(f"| last-finishing request: selector dispatched | {g('sel_start_last'):.2f} |")
+    print(f"| last-finishing request: selector done | {g('sel_end_last'):.2f} |")
+    print(f"| chain kernel's last stamp | {g('chain_end'):.2f} |")
+    print(f"| exact-redraw kernel: first block starts after the chain's last stamp | {g('k3_gap'):.2f} |")
+    print(f"| exact-redraw kernel: first start -> last stamp | {g('k3_span'):.2f} |")
+    print(f"| call: first start -> last stamp | {g('total'):.2f} |")
+    print()
+    print("| selector step | median over the requests | request that finishes last |")
+    print("|---|---|---|")
+    for n_, a_, b_ in zip(names, sm, sl):
+        print(f"| {n_} | {a_:.2f} | {b_:.2f} |")
+    print()
+    print(f"Last-finishing request: {g('after_stats_last'):.2f} us from its statistics' end to its selector's end; "
+          f"exact redraws per call: {g('k3_exact'):.0f} blocks.")
+
+
+def _traced_calls(args, torch, lib, calls, cap, slot):
+    """Times `calls` with tracing off and on, then runs args.timeline_calls traced calls one at
+    a time; returns (us per call off, us per call on, [records of kernel slot `slot`, base])."""
+    import ctypes
+    stream = torch.cuda.current_stream()
+    buf = torch.zeros(TRACE_KERNELS * cap * TRACE_WORDS, dtype=torch.int64, device="cuda:0")
+    assert lib.spec_trace_set(ctypes.c_void_p(0), 0) == 0
+    span_off, per = time_calls(calls, args.steps, args.warmup, stream)
+    assert lib.spec_trace_set(ctypes.c_void_p(buf.data_ptr()), cap) == 0
+    span_on, _ = time_calls(calls, args.steps, args.warmup, stream)
+    out = []
+    for rep in range(args.timeline_calls):
+        buf.zero_()
+        torch.cuda.synchronize()
+        calls[rep % len(calls)]()
+        torch.cuda.synchronize()
+        r = _trace_records(buf, cap)[slot]
+        t = r["t"].astype(float)
+        t[t == 0] = np.nan
+        base = np.nanmin(t[:, 0])
+        r["t"] = (t - base) * TICK_US
+        out.append(r)
+    assert lib.spec_trace_set(ctypes.c_void_p(0), 0) == 0
+    return span_off / args.steps * 1e6, span_on / args.steps * 1e6, out
+
+
+def timeline_tree(args, torch, sv, synth, lib):
+    """Per-hop timeline of the membership tree (B=32, N=63, V=152064): for each hop of each
+    request's walk, the wait for the row's summaries (the root stream at hop 0, the helpers'
+    round trip after that), the sample (chunk select and rescan), and the child search plus
+    the next order."""
+    x = synth.make_config(5, 0)
+    B, N, V = x.B, x.N, x.V
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    nt, pt, ut = (torch.from_numpy(a).to(dev) for a in (x.node_tokens, x.parents, x.u))
+    sets = device_copies(lambda: (lt.clone(), nt, pt, ut), lt.numel() * 2)
+    del lt
+    ws = torch.zeros(sv.tree_workspace_bytes(B, N, V) + 512, dtype=torch.uint8, device=dev)
+    calls = [sv.prepare_tree(s_[0], s_[1], s_[2], s_[3], float(x.temperature), workspace_tensor=ws) for s_ in sets]
+    off, on, recs = _traced_calls(args, torch, lib, calls, 8192, 2)
+    per_hop = {}
+    ends, root_ends, walk_starts = [], [], []
+    for r in recs:
+        t, kind, b = r["t"], r["kind"], r["b"]
+        node = kind == 8
+        root = kind == 0
+        root_ends.append(np.nanmax(t[(kind == 0) | (kind == 2), 1]))
+        walk_starts.append(_med(t[kind == 2, 1]))
+        ends.append(np.nanmax(t))
+        for req in range(B):
+            h = t[node & (b == req)]
+            h = h[np.argsort(h[:, 0])]
+            for j in range(len(h)):
+                wait = h[j, 1] - (h[j - 1, 3] if j else h[j, 0])
+                per_hop.setdefault(j, []).append((wait, h[j, 2] - h[j, 1], h[j, 3] - h[j, 2], h[j, 3]))
+    print(f"## tree_kernel timeline (membership): B={B} N={N} V={V} bf16 logits, T={x.temperature}")
+    print()
+    print(f"Trace build, {args.timeline_calls} traced calls; times in us from the first block's start. "
+          f"Calls of the trace build: {off:.1f} us with tracing off, {on:.1f} us on.")
+    print()
+    print(f"Root stream: the last root chunk summary published at {_med(root_ends):.2f} us (median over "
+          f"calls); the call's last stamp at {_med(ends):.2f} us.")
+    print()
+    print("| hop | walks reaching it | wait for the row's summaries | sample (select + rescan) | "
+          "child search + order | hop done at (median) |")
+    print("|---|---|---|---|---|---|")
+    for j in sorted(per_hop):
+        a = np.array(per_hop[j])
+        what = "root row (stream)" if j == 0 else "helpers' round trip"
+        print(f"| {j} | {len(a) // max(1, args.timeline_calls)} | {_med(a[:, 0]):.2f} ({what}) | "
+              f"{_med(a[:, 1]):.2f} | {_med(a[:, 2]):.2f} | {_med(a[:, 3]):.2f} |")
+
+
+def timeline_tree_residual(args, torch, sv, synth, lib):
+    """Per-hop timeline of the residual-update tree (B=32, N=31, V=32000): node visits (wait for
+    the row's summaries, normalizer) and residual passes (order -> every chunk mass in -> W)."""
+    x = synth.make_config(6, 0)
+    B, N, V = x.B, x.N, x.V
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    qt = torch.from_numpy(x.q).to(dev)
+    nt, pt = torch.from_numpy(x.node_tokens).to(dev), torch.from_numpy(x.parents).to(dev)
+    ua, ud = torch.from_numpy(x.u_acc).to(dev), torch.from_numpy(x.u_draw).to(dev)
+    sets = device_copies(lambda: (lt.clone(), qt.clone(), nt, pt, ua, ud), lt.numel() * 2 + qt.numel() * 4)
+    del lt, qt
+    ws = torch.zeros(sv.tree_residual_workspace_bytes(B, N, V) + 512, dtype=torch.uint8, device=dev)
+    calls = [sv.prepare_tree_residual(*s_, float(x.temperature), workspace_tensor=ws) for s_ in sets]
+    off, on, recs = _traced_calls(args, torch, lib, calls, 8192, 3)
+    node_wait, node_z, node_root, pass_in, pass_w, tests, draws, accept_order = [], [], [], [], [], [], [], []
+    n_nodes, n_pass, ends, walk_ends = [], [], [], []
+    for r in recs:
+        t, kind, b = r["t"], r["kind"], r["b"]
+        ends.append(np.nanmax(t))
+        walk_ends.append(_med([np.nanmax(t[(kind >= 8) & (b == q)]) for q in range(B)]))
+        n_nodes.append((kind == 8).sum() / B)
+        n_pass.append((kind == 9).sum() / B)
+        for req in range(B):
+            sel = (kind >= 8) & (b == req)
+            ev = sorted(zip(t[sel, 0], kind[sel], map(tuple, t[sel])), key=lambda e: e[0])
+            prev_order = None   # when the order for the current node's row was published
+            k = 0
+            while k < len(ev):
+                s_ = ev[k][2]           # a node visit: slots top, staged, Z, child order, draw
+                if prev_order is None:
+                    node_root.append(s_[1])
+                else:
+                    node_wait.append(s_[1] - prev_order)
+                node_z.append(s_[2] - s_[1])
+                last = s_[2]
+                k += 1
+                while k < len(ev) and ev[k][1] == 9:   # its residual passes: order, masses in, W
+                    p_ = ev[k][2]
+                    tests.append(p_[0] - last)
+                    pass_in.append(p_[1] - p_[0])
+                    pass_w.append(p_[2] - p_[1])
+                    last = p_[2]
+                    k += 1
+                if np.isfinite(s_[3]):
+                    accept_order.append(s_[3] - last)
+                    prev_order = s_[3]
+                if np.isfinite(s_[4]):
+                    draws.append(s_[4] - last)
+    print(f"## tree_kernel timeline (residual-update): B={B} N={N} V={V} bf16 logits, fp32 q, T={x.temperature}")
+    print()
+    print(f"Trace build, {args.timeline_calls} traced calls; times in us. Calls of the trace build: "
+          f"{off:.1f} us with tracing off, {on:.1f} us on. Per request: {_med(n_nodes):.1f} node visits and "
+          f"{_med(n_pass):.1f} residual passes (medians over calls); median walk ends at {_med(walk_ends):.2f} us, "
+          f"the call's last stamp at {_med(ends):.2f} us.")
+    print()
+    print("| step | count per call | median us |")
+    print("|---|---|---|")
+    nc = max(1, args.timeline_calls)
+    print(f"| root row: summaries in (from the first block's start) | {len(node_root) // nc} | {_med(node_root):.2f} |")
+    print(f"| node below the root: order for its row -> summaries in (helpers' round trip) | {len(node_wait) // nc} | {_med(node_wait):.2f} |")
+    print(f"| summaries in -> normalizer Z | {len(node_z) // nc} | {_med(node_z):.2f} |")
+    print(f"| accept test of a child (after Z or the last pass) -> pass order | {len(tests) // nc} | {_med(tests):.2f} |")
+    print(f"| residual pass: order -> every chunk mass in (helpers' round trip) | {len(pass_in) // nc} | {_med(pass_in):.2f} |")
+    print(f"| residual pass: masses in -> W published | {len(pass_w) // nc} | {_med(pass_w):.2f} |")
+    print(f"| accepted child: accept test -> its row's order published | {len(accept_order) // nc} | {_med(accept_order):.2f} |")
+    print(f"| terminal draw (after Z or the last W) -> token | {len(draws) // nc} | {_med(draws):.2f} |")
+
+
 class _CachedSynth:
     """The synth module with make_config memoized, so that the lines that share a workload
     generate its inputs once (they only read them)."""
@@ -477,6 +737,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true",
                     help="print the chain bandwidth sweep over batch sizes (one JSON line per point) instead")
+    ap.add_argument("--timeline", choices=["chain", "tree", "tree_residual"],
+                    help="print a per-block timeline summary (markdown) of one workload instead, from the "
+                         "trace build (python -m exact_rejection_sampling_amd.build --trace)")
+    ap.add_argument("--timeline-calls", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps(dict(error="this benchmark runs on one GPU only; run with --gpus 1")))
@@ -487,12 +751,18 @@ def main():
     import synth as synth_module
     synth = _CachedSynth(synth_module)
     cpu = None
-    if not args.no_cpu and not args.sweep:
+    if not args.no_cpu and not args.sweep and not args.timeline:
         log("[bench] oracle CPU baseline")
         cpu = cpu_baseline(synth.make_config(3, 0), args.cpu_seconds)
     if not torch.cuda.is_available():
         print(json.dumps(dict(error="no GPU visible")))
         sys.exit(1)
+    if args.timeline:
+        from exact_rejection_sampling_amd import build as _build
+        lib = sv.load_library(_build.TRACE_LIB, install=True)
+        fn = dict(chain=timeline_chain, tree=timeline_tree, tree_residual=timeline_tree_residual)[args.timeline]
+        fn(args, torch, sv, synth, lib)
+        return
     sv.load_library()
     if args.sweep:
         bench_sweep(args, torch, sv, synth)

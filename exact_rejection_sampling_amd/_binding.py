@@ -27,6 +27,7 @@ _c_void_p, _c_int, _c_float, _c_size_t = ctypes.c_void_p, ctypes.c_int, ctypes.c
 
 _SIGNATURES = {
     "spec_abi_version": (_c_int, []),
+    "spec_trace_set": (_c_int, [_c_void_p, _c_size_t]),
     "spec_status_string": (ctypes.c_char_p, [_c_int]),
     "spec_req_status_string": (ctypes.c_char_p, [_c_int]),
     "spec_chain_workspace_bytes": (_c_size_t, [_c_int, _c_int, _c_int]),
@@ -82,8 +83,11 @@ class SpecError(RuntimeError):
     """A host-side error status returned by the library."""
 
 
-def load_library(path: Optional[str] = None) -> ctypes.CDLL:
-    """Load (once) and return the shared library; raises if it has not been built."""
+def load_library(path: Optional[str] = None, install: bool = False) -> ctypes.CDLL:
+    """Load (once) and return the shared library; raises if it has not been built.
+
+    With a path, that library is loaded instead (for instance the timeline-trace build); with
+    install=True it also becomes the one every later call of this module uses."""
     global _lib
     with _lock:
         if _lib is not None and path is None:
@@ -98,7 +102,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
-        if path is None:
+        if path is None or install:
             _lib = lib
         return lib
 

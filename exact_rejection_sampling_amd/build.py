@@ -51,23 +51,33 @@ def _run(cmd, verbose):
         print(out)
 
 
-def build_library(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every HIP source for gfx950 and link the shared library; returns its path."""
+TRACE_LIB = os.path.join(PKG, "libspec_verify_trace.so")
+
+
+def build_library(verbose: bool = False, jobs: int = 4, trace: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link the shared library; returns its path.
+
+    trace=True builds the timeline-trace variant instead (-DSPEC_TRACE, objects under
+    _build/trace, library libspec_verify_trace.so): the same kernels with per-block
+    real-time stamps, for profiling only (spec_trace_set in include/spec_verify.h)."""
     cc = hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    build = os.path.join(BUILD, "trace") if trace else BUILD
+    lib = TRACE_LIB if trace else LIB
+    extra = ["-DSPEC_TRACE=1"] if trace else []
+    os.makedirs(build, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(build, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build_library(verbose="-v" in sys.argv))
+    print(build_library(verbose="-v" in sys.argv, trace="--trace" in sys.argv))

@@ -7,6 +7,10 @@
 #include "internal.h"
 #include "spec_verify.h"
 
+#ifdef SPEC_TRACE
+namespace sv { TraceSink g_trace_sink{}; }
+#endif
+
 namespace {
 
 constexpr double kLog2e = 1.44269504088896340736;
@@ -47,6 +51,19 @@ sv::StopSpec stop_spec(const int32_t* stop_tokens, int n_stop, const int32_t* bu
 extern "C" {
 
 int spec_abi_version(void) { return SPEC_ABI_VERSION; }
+
+spec_status spec_trace_set(void* buffer, size_t records_per_kernel) {
+#ifdef SPEC_TRACE
+  if (buffer && records_per_kernel == 0) return SPEC_EINVAL;
+  sv::g_trace_sink.buf = static_cast<unsigned long long*>(buffer);
+  sv::g_trace_sink.cap = buffer ? records_per_kernel : 0;
+  return SPEC_OK;
+#else
+  (void)buffer;
+  (void)records_per_kernel;
+  return SPEC_EINVAL;
+#endif
+}
 
 const char* spec_status_string(int code) {
   switch (code) {
@@ -199,6 +216,7 @@ spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, con
     t.c2 = p.c2;
     if (sv::launch_thresholds(t, logit_dtype, vec, stream) != hipSuccess) return SPEC_EHIP;
   }
+  SPEC_TRACE_FILL(p);
   return sv::launch_chain(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
@@ -299,6 +317,7 @@ spec_status spec_verify_tree(const void* node_logits, int logit_dtype, const int
   p.WH = chunks(p.P, sv::kTreeHelperChunks);
   p.c2 = static_cast<float>(kLog2e / static_cast<double>(temperature));
   const bool vec = (V % 8 == 0) && aligned16(node_logits);
+  SPEC_TRACE_FILL(p);
   return sv::launch_tree(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
@@ -335,6 +354,7 @@ spec_status spec_verify_tree_greedy(const void* node_logits, int logit_dtype, co
   p.WG1 = chunks(p.P, sv::kWavesPerBlock);
   p.WH = chunks(p.P, sv::kTreeHelperChunks);
   const bool vec = (V % 8 == 0) && aligned16(node_logits);
+  SPEC_TRACE_FILL(p);
   return sv::launch_tree_greedy(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
@@ -381,6 +401,7 @@ spec_status spec_verify_tree_residual(const void* node_logits, int logit_dtype, 
   p.WH = chunks(p.P, sv::kTreeHelperChunks);
   p.c2 = static_cast<float>(kLog2e / static_cast<double>(temperature));
   const bool vec = (V % 8 == 0) && aligned16(node_logits) && aligned16(draft_probs);
+  SPEC_TRACE_FILL(p);
   return sv::launch_tree_residual(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 

@@ -47,6 +47,10 @@ namespace {
 
 constexpr double kLn2 = 0.69314718055994530942;
 
+// Item kinds in a trace record's tag (trace builds only).
+enum : int { kTraceStats = 0, kTraceSkipped = 1, kTraceTerminal = 2, kTraceSelector = 3,
+             kTraceExactIdle = 4, kTraceExact = 5 };
+
 __device__ __forceinline__ float gather_q(const ChainParams& p, size_t idx) {
   return p.q_dtype == kBF16 ? load_scalar<kBF16>(p.q, idx) : load_scalar<kF32>(p.q, idx);
 }
@@ -190,6 +194,7 @@ __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
   }
   if (gathers) gather_publish(p, b, i, gx, gl, gq);
   __syncthreads();
+  SPEC_STAMP(p, 0, 2);
   if (threadIdx.x == 0) {
     // the slice's summary: M = max of the waves' maxima, Z = sum of their sums rescaled
     // to M (NaN if any wave saw NaN or +inf; (-inf, 0) if every element was -inf).  Z >= 1
@@ -590,6 +595,7 @@ __device__ bool chain_select(const ChainParams& p, int b, const ChainDecision& d
   __syncthreads();
   const double W = s_total;
   const bool failed = s_timeout || !(isfinite(W) && W > 0.0);   // uniform across the block
+  SPEC_STAMP(p, 0, 4);
   double t = 0.0;
   int k = -1;
   if (!failed) {
@@ -648,6 +654,7 @@ __device__ bool chain_select(const ChainParams& p, int b, const ChainDecision& d
     pick = block_min_i(pick, s_imin);
     k = pick != 0x7fffffff ? pick : -block_min_i(-last_pos, s_imin);
   }
+  SPEC_STAMP(p, 0, 5);
 
   // 3. outputs
   const int A = d.A;
@@ -682,6 +689,7 @@ __device__ bool chain_select(const ChainParams& p, int b, const ChainDecision& d
     p.req_status[b] = status;
     if (p.st.finish) p.st.finish[b] = finish;
   }
+  SPEC_STAMP(p, 0, 6);
   return RESID && status == 0 && W < kExactBelow;
 }
 
@@ -751,6 +759,7 @@ __device__ void terminal_body(const ChainParams& p, int b, int c, const ChainDec
   bool bad = false;
   term_chunk<DT, QT, VEC, RESID, PROC>(p, lrow, qrow, c, d, (size_t)b * p.R + d.A, w, bad);
   const double m = block_mass(w, bad);
+  SPEC_STAMP(p, 0, 3);
   if (c != p.S2 - 1) {
     if (threadIdx.x == 0) publish_mass(p.tmass + (size_t)b * p.S2 + c, m);
     return;
@@ -758,6 +767,7 @@ __device__ void terminal_body(const ChainParams& p, int b, int c, const ChainDec
   const bool exact = chain_select<DT, QT, VEC, RESID, PROC>(p, b, d, rs, m, lrow, qrow);
   __syncthreads();
   chain_clear(p, b, exact ? &d : nullptr);
+  SPEC_STAMP(p, 0, 7);
 }
 
 // Terminal item with the request's decision taken (chain_decide over every row).
@@ -827,8 +837,10 @@ __global__ __launch_bounds__(kBlock) void chain_exact_kernel(ChainParams p) {
   __shared__ int s_lost;
   __shared__ double s_before, s_total;
   const int b = blockIdx.x / p.S2, c = blockIdx.x % p.S2;
+  SPEC_STAMP(p, 1, 1);
   unsigned* rec = reinterpret_cast<unsigned*>(p.part + (size_t)b * p.R * p.SL);
   const unsigned pend = rec[0];
+  SPEC_TAG(p, 1, SPEC_TRACE_TAG(pend ? kTraceExact : kTraceExactIdle, b, c));
   if (pend == 0u) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   ChainDecision d{};
@@ -877,6 +889,7 @@ __global__ __launch_bounds__(kBlock) void chain_exact_kernel(ChainParams p) {
   if (c != p.S2 - 1) {
     if (tid == 0)
       for (int k = 0; k < 3; ++k) publish_mass(xmass_word(p, b, c, k), own[k]);
+    SPEC_STAMP(p, 1, 3);
     return;
   }
 
@@ -988,6 +1001,7 @@ __global__ __launch_bounds__(kBlock) void chain_exact_kernel(ChainParams p) {
   __syncthreads();
   for (int j = tid; j < 3 * p.S2; j += kBlock) clear_mass(p.xmass + (size_t)b * p.S2 * 3 + j);
   if (tid < 4) rec[tid] = 0u;
+  SPEC_STAMP(p, 1, 3);
 }
 
 // Block order: groups g = 0 .. B + L - 1, group g holding the Sb statistics items of
@@ -1048,6 +1062,7 @@ __global__ __launch_bounds__(kBlock) void chain_kernel(ChainParams p) {
 #endif
   __shared__ RowState s_rs;
   __shared__ ChainDecision s_dec;
+  SPEC_STAMP(p, 0, 1);
   const Item it = p.J > 1 ? lazy_item(p, blockIdx.x) : block_item(p, blockIdx.x);
   const int row = it.idx / p.SL;
   // the rows whose words this block's decision reads: every row for a terminal item; for
@@ -1066,6 +1081,8 @@ __global__ __launch_bounds__(kBlock) void chain_kernel(ChainParams p) {
   }
   if (nr > 0) chain_decide<DT>(p, it.b, s_rs, s_dec, lo, nr);   // one call site: inlined once
   if (it.terminal) {
+    SPEC_STAMP(p, 0, 2);
+    SPEC_TAG(p, 0, SPEC_TRACE_TAG(it.idx == p.S2 - 1 ? kTraceSelector : kTraceTerminal, it.b, it.idx));
     terminal_item<DT, QT, VEC, PROC>(p, it.b, it.idx, s_rs, s_dec);
     return;
   }
@@ -1074,8 +1091,10 @@ __global__ __launch_bounds__(kBlock) void chain_kernel(ChainParams p) {
     const ChainDecision d = s_dec;
     reached = d.status == SPEC_REQ_INTERNAL || (d.ev >= nr && d.H > 0);
   }
+  SPEC_TAG(p, 0, SPEC_TRACE_TAG(reached ? kTraceStats : kTraceSkipped, it.b, it.idx));
   if (reached) stats_item<DT, QT, VEC, PROC>(p, it.b, row, it.idx % p.SL);
   else stats_skip(p, it.b, row, it.idx % p.SL);
+  SPEC_STAMP(p, 0, 3);
 }
 
 // Lag between a request's statistics and terminal items, in rounds of resident blocks:

@@ -8,6 +8,46 @@
 
 namespace sv {
 
+// ------------------------------------------------------------ timeline trace
+// In a library built with -DSPEC_TRACE (exact_rejection_sampling_amd.build --trace), thread
+// 0 of every block of a traced kernel writes a tag and up to 7 stamps of the 100 MHz
+// real-time counter (s_memrealtime) into the buffer that spec_trace_set installs: the
+// record of block x of kernel slot k is words [(k * cap + x) * 8, + 8), and blocks at or
+// past `cap` write nothing.  Other builds compile every mark to nothing and carry no trace
+// member in their kernel arguments.
+#ifdef SPEC_TRACE
+struct TraceSink {
+  unsigned long long* buf;   // [kTraceKernels * cap * 8] words, or null (tracing off)
+  unsigned long long cap;    // records per kernel slot
+};
+constexpr int kTraceKernels = 4;   // slots: 0 chain, 1 chain exact redraw, 2 tree, 3 tree residual
+extern TraceSink g_trace_sink;     // host copy, set by spec_trace_set
+#define SPEC_TRACE_MEMBER TraceSink trace{};
+__device__ __forceinline__ void trace_word(const TraceSink& t, int k, unsigned long long rec, int slot,
+                                           unsigned long long v) {
+  if (threadIdx.x == 0 && t.buf && rec < t.cap) t.buf[((unsigned long long)k * t.cap + rec) * 8 + slot] = v;
+}
+#define SPEC_STAMP(P, K, SLOT) ::sv::trace_word((P).trace, (K), blockIdx.x, (SLOT), __builtin_amdgcn_s_memrealtime())
+#define SPEC_TAG(P, K, TAG) ::sv::trace_word((P).trace, (K), blockIdx.x, 0, (TAG))
+// the same into record REC instead of the block's own (per-event records)
+#define SPEC_STAMP_AT(P, K, REC, SLOT) \
+  ::sv::trace_word((P).trace, (K), (REC), (SLOT), __builtin_amdgcn_s_memrealtime())
+#define SPEC_TAG_AT(P, K, REC, TAG) ::sv::trace_word((P).trace, (K), (REC), 0, (TAG))
+#define SPEC_TRACE_FILL(P) ((P).trace = ::sv::g_trace_sink)
+#else
+#define SPEC_TRACE_MEMBER
+#define SPEC_STAMP(P, K, SLOT) ((void)0)
+#define SPEC_TAG(P, K, TAG) ((void)0)
+#define SPEC_STAMP_AT(P, K, REC, SLOT) ((void)0)
+#define SPEC_TAG_AT(P, K, REC, TAG) ((void)0)
+#define SPEC_TRACE_FILL(P) ((void)0)
+#endif
+// A record's tag: bit 63 set, the item kind in bits 56..62, the request in bits 24..55
+// and the item's index within the request in bits 0..23.
+#define SPEC_TRACE_TAG(KIND, B, IDX) \
+  ((1ull << 63) | ((unsigned long long)(KIND) << 56) | ((unsigned long long)(unsigned)(B) << 24) | \
+   (unsigned long long)((IDX) & 0xffffff))
+
 // Per-request decision of the chain verifier: every terminal block of a request computes
 // it from the request's published summaries.
 struct ChainDecision {
@@ -78,6 +118,7 @@ struct ChainParams {
   float c2;                  // fp32(log2(e) / T)
   double inv_t;              // 1 / T, T widened exactly from fp32
   double c2d;                // log2(e) / T in fp64 (the exact pass's exponent slope)
+  SPEC_TRACE_MEMBER
 };
 
 #ifndef SPEC_TERM_SLABS
@@ -156,6 +197,7 @@ struct TreeParams {
   const float* u_draw;       // [B, N] terminal draw at node v (u holds the child accept uniforms)
   unsigned* desc;            // [B * desc_words] residual-pass descriptors
   int q_dtype, desc_words;   // desc_words = 4 + 2N
+  SPEC_TRACE_MEMBER
 };
 
 // Rows the residual-update tree verifier's walking block stages in LDS: at most this many

@@ -33,6 +33,17 @@ namespace {
 
 constexpr int kNoPick = 0x7fffffff;
 
+// Trace records (trace builds only): kernel slot 2 (membership and greedy trees) or 3
+// (residual-update tree).  Each block tags its own record as a root block, a helper or, for
+// the root block that walks, the walker; the walker also writes one record per hop (a node
+// visited, or a residual pass) at record B * (WG1 + WH) + b * kTraceHops + hop.
+enum : int { kTraceRoot = 0, kTraceHelper = 1, kTraceWalker = 2, kTraceNode = 8, kTracePass = 9 };
+constexpr int kTraceHops = 128;
+__device__ __forceinline__ unsigned long long hop_record(const TreeParams& p, int b, int hop) {
+  return (unsigned long long)p.B * (p.WG1 + p.WH) + (unsigned long long)b * kTraceHops +
+         (unsigned long long)min(hop, kTraceHops - 1);
+}
+
 __device__ void tree_fail(const TreeParams& p, int b, int code) {
   for (int i = threadIdx.x; i < p.N; i += blockDim.x) {
     p.out_tokens[(size_t)b * p.N + i] = -1;
@@ -276,13 +287,15 @@ __device__ void stage_summaries(const float2* src, float2* dst, int P, int* lost
 
 // One target sample from row `row` whose P chunk summaries are published at `src`.
 template <int DT, bool VEC>
-__device__ int sample_published(const TreeParams& p, const float2* src, const void* row, float uv, int* status) {
+__device__ int sample_published(const TreeParams& p, const float2* src, const void* row, float uv, int* status,
+                                unsigned long long trec) {
   __shared__ float2 s_sum[kTreeStage];
   __shared__ int s_lost;
   if (threadIdx.x == 0) s_lost = 0;
   __syncthreads();
   if (p.P <= kTreeStage) {
     stage_summaries(src, s_sum, p.P, &s_lost);
+    SPEC_STAMP_AT(p, 2, trec, 2);
     if (s_lost) { *status = SPEC_REQ_INTERNAL; return -1; }
     return sample_row<DT, VEC, false>(p, s_sum, row, uv, status);
   }
@@ -360,21 +373,25 @@ __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
 
   int v = 0, depth = 0;
   while (true) {
+    const unsigned long long trec = hop_record(p, b, depth);
+    SPEC_TAG_AT(p, 2, trec, SPEC_TRACE_TAG(kTraceNode, b, v));
+    SPEC_STAMP_AT(p, 2, trec, 1);
     const void* row = row_ptr<DT>(p.logits, (size_t)b * N + v, p.V);
     int status = 0;
     const float uv = ARGMAX ? 0.0f : p.u[(size_t)b * N + v];
     int y;
     if (v == 0) {
       if constexpr (ARGMAX) y = argmax_published(p, p.part + (size_t)b * p.P, &status);
-      else y = sample_published<DT, VEC>(p, p.part + (size_t)b * p.P, row, uv, &status);
+      else y = sample_published<DT, VEC>(p, p.part + (size_t)b * p.P, row, uv, &status, trec);
     } else {
       // the helpers' summaries of this row; returned to zero once read
       float2* deep = p.deep + ((size_t)b * 2 + (gen & 1u)) * p.P;
       if constexpr (ARGMAX) y = argmax_published(p, deep, &status);
-      else y = sample_published<DT, VEC>(p, deep, row, uv, &status);
+      else y = sample_published<DT, VEC>(p, deep, row, uv, &status, trec);
       for (int c = tid; c < p.P; c += kBlock) clear_f2(deep + c);
       vmem_wait();      // the clears are complete before any later order reuses the words
     }
+    SPEC_STAMP_AT(p, 2, trec, 3);
     if (status != 0) { tree_fail(p, b, status); return; }
     int cand = kNoPick;           // this thread's lowest matching child (c rises)
     for (int c = v + 1 + tid; c < N; c += kBlock)
@@ -394,6 +411,7 @@ __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
         p.accepted_len[b] = depth;
         p.req_status[b] = 0;
       }
+      SPEC_STAMP_AT(p, 2, trec, 4);
       return;
     }
     if (tid == 0) {
@@ -401,6 +419,7 @@ __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
       p.out_nodes[(size_t)b * N + depth] = child;
       publish_order(p, b, ++gen, static_cast<unsigned>(child) + 1u);   // summarize the child's row
     }
+    SPEC_STAMP_AT(p, 2, trec, 4);
     ++depth;
     v = child;
     __shared__ unsigned s_gen;
@@ -523,14 +542,18 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
   __syncthreads();
   if (s_bad) { tree_fail(p, b, SPEC_REQ_BADTREE); return; }
 
-  int v = 0, depth = 0;
+  int v = 0, depth = 0, hop = 0;
   while (true) {
+    const unsigned long long trec = hop_record(p, b, hop++);
+    SPEC_TAG_AT(p, 3, trec, SPEC_TRACE_TAG(kTraceNode, b, v));
+    SPEC_STAMP_AT(p, 3, trec, 1);
     const void* row = row_ptr<DT>(p.logits, (size_t)b * N + v, p.V);
     // 1. the row's chunk summaries: the root items' or, below the root, the helpers'
     if (tid == 0) s_lost = 0;
     __syncthreads();
     float2* src = v == 0 ? p.part + (size_t)b * P : p.deep + ((size_t)b * 2 + (gen & 1u)) * P;
     stage_summaries(src, s_sum, P, &s_lost);
+    SPEC_STAMP_AT(p, 3, trec, 2);
     if (v != 0) {
       for (int c = tid; c < P; c += kBlock) clear_f2(src + c);
       vmem_wait();
@@ -550,6 +573,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
     block_excl_scan_d(zt, s_scan, &Z);
     if (!(isfinite(Z) && Z > 0.0)) { tree_fail(p, b, SPEC_REQ_NONFINITE); return; }
     const float inv_z = (float)(1.0 / Z);
+    SPEC_STAMP_AT(p, 3, trec, 3);
 
     // 2. the children, in index order
     int i = 0, accepted = kNoPick;
@@ -596,6 +620,9 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
         s_gen = gen;
         s_lost = 0;
       }
+      const unsigned long long prec = hop_record(p, b, hop++);
+      SPEC_TAG_AT(p, 3, prec, SPEC_TRACE_TAG(kTracePass, b, i));
+      SPEC_STAMP_AT(p, 3, prec, 1);
       ++i;
       __syncthreads();
       gen = s_gen;
@@ -608,6 +635,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
       }
       vmem_wait();                        // cleared before any later order reuses the words
       __syncthreads();
+      SPEC_STAMP_AT(p, 3, prec, 2);
       if (s_lost) { tree_fail(p, b, SPEC_REQ_INTERNAL); return; }
       const int per = (P + kBlock - 1) / kBlock;
       const int c_lo = min(tid * per, P), c_hi = min(c_lo + per, P);
@@ -615,6 +643,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
       mass_prefix(s_mass, P, c_lo, c_hi, &W);
       if (!(isfinite(W) && W > 0.0)) { tree_fail(p, b, SPEC_REQ_RESIDUAL_EMPTY); return; }
       if (tid == 0) publish_u32(d + 4 + N + (i - 1), __float_as_uint((float)(1.0 / W)));
+      SPEC_STAMP_AT(p, 3, prec, 3);
       c = next_child(par, N, v, c, s_imin);
     }
     if (accepted != kNoPick) {
@@ -625,6 +654,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
         publish_order(p, b, ++gen, static_cast<unsigned>(accepted) + 1u);   // summarize its row
         s_gen = gen;
       }
+      SPEC_STAMP_AT(p, 3, trec, 4);
       ++depth;
       v = accepted;
       __syncthreads();
@@ -643,6 +673,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
     } else {
       y = residual_pick<DT, QT, VEC>(p, b, d, i, row, r, inv_z, s_mass, ud);
     }
+    SPEC_STAMP_AT(p, 3, trec, 5);
     for (int k = tid; k < N; k += kBlock) {
       if (k > depth) {
         p.out_tokens[(size_t)b * N + k] = -1;
@@ -683,6 +714,7 @@ __device__ void helper_item(const TreeParams& p, int b, int h) {
     __syncthreads();                      // every thread has read s_order before it changes
     const unsigned gen = static_cast<unsigned>(o >> 32), code = static_cast<unsigned>(o);
     if (o == 0ull || gen == last_gen || code == kTreeDone) break;   // dismissed (or the wait bound)
+    if (last_gen == 0) SPEC_STAMP(p, RESID ? 3 : 2, 2);   // first order
     last_gen = gen;
     if constexpr (RESID) {
       if (code & kResidualPass) {
@@ -743,10 +775,15 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
   const int per_req = p.WG1 + p.WH;
   const int b = blockIdx.x / per_req;
   const int slice = blockIdx.x % per_req;
+  constexpr int K = RESID ? 3 : 2;   // trace slot
+  SPEC_STAMP(p, K, 1);
   if (slice >= p.WG1) {
+    SPEC_TAG(p, K, SPEC_TRACE_TAG(kTraceHelper, b, slice - p.WG1));
     helper_item<DT, QT, VEC, RESID, ARGMAX>(p, b, slice - p.WG1);
+    SPEC_STAMP(p, K, 3);
     return;
   }
+  SPEC_TAG(p, K, SPEC_TRACE_TAG(kTraceRoot, b, slice));
   const int chunk = slice * kWavesPerBlock + wave;
   if (chunk < p.P) {
     const void* row0 = row_ptr<DT>(p.logits, (size_t)b * p.N, p.V);
@@ -760,6 +797,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
     }
   }
   __syncthreads();
+  SPEC_STAMP(p, K, 2);
   __shared__ int s_last;
   if (threadIdx.x == 0) {
     const unsigned prev = arrive(&p.counters[(size_t)b * kCounterSlots + 0]);
@@ -767,6 +805,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
   }
   __syncthreads();
   if (!s_last) return;
+  SPEC_TAG(p, K, SPEC_TRACE_TAG(kTraceWalker, b, slice));
   unsigned gen = 0;
   if constexpr (RESID) tree_walk_residual<DT, QT, VEC>(p, b, gen);
   else tree_walk<DT, VEC, ARGMAX>(p, b, gen);
@@ -776,6 +815,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
   if constexpr (RESID)   // no helper reads the descriptor once dismissed
     for (int j = threadIdx.x; j < p.desc_words; j += kBlock) publish_u32(p.desc + (size_t)b * p.desc_words + j, 0u);
   if (threadIdx.x == 0) reset_counter(&p.counters[(size_t)b * kCounterSlots + 0]);
+  SPEC_STAMP(p, K, 3);
 }
 
 template <int DT, int QT, bool VEC, bool RESID, bool ARGMAX = false>

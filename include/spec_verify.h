@@ -378,6 +378,18 @@ const char* spec_status_string(int code);     /* static string, never NULL */
 const char* spec_req_status_string(int code); /* static string, never NULL */
 int spec_abi_version(void);                   /* SPEC_ABI_VERSION */
 
+/* Timeline trace, for profiling (not for the calls' results).  In a library built with
+ * tracing (python -m exact_rejection_sampling_amd.build --trace, which writes
+ * libspec_verify_trace.so), every later call records, for each block of its kernels, a tag
+ * and stamps of the GPU's 100 MHz real-time counter into `buffer`: a device allocation of
+ * 4 * records_per_kernel * 8 uint64 words, which the caller owns and keeps alive while traced
+ * calls run; block x of kernel slot k (0 chain, 1 chain exact redraw, 2 tree, 3 residual tree)
+ * writes words [(k * records_per_kernel + x) * 8, + 8) with plain stores on the call's stream,
+ * and blocks at or past records_per_kernel write nothing.  buffer == NULL turns tracing off.
+ * Returns SPEC_EINVAL in a library built without tracing, or for a non-null buffer with
+ * records_per_kernel == 0.  Not thread-safe: set it while no call is being issued. */
+spec_status spec_trace_set(void* buffer, size_t records_per_kernel);
+
 #ifdef __cplusplus
 }
 #endif

@@ -196,3 +196,10 @@ def test_options_entry_points_host_validation():
     for k in (1, 3, 100):
         lazy.lazy_rows = k
         assert c(ctypes.byref(lazy)) == EWORKSPACE
+
+
+def test_trace_setter_refuses_outside_trace_builds():
+    """spec_trace_set is exported by every build; only the trace build accepts a buffer."""
+    lib = sv.load_library()
+    assert lib.spec_trace_set(FAKE, 16) == EINVAL
+    assert lib.spec_trace_set(NULL, 0) == EINVAL
