@@ -106,7 +106,7 @@ bool residual_sizes_ok(int B, int N, int V) {
 }
 
 size_t spec_tree_residual_workspace_bytes(int B, int N, int V) {
-  if (!residual_sizes_ok(B, N, V) || !sv::grid_fits(sv::tree_blocks(B, V))) return 0;
+  if (!residual_sizes_ok(B, N, V) || !sv::grid_fits(sv::tree_blocks(B, V, true))) return 0;
   return sv::tree_layout(B, N, V, true).total;
 }
 
@@ -367,7 +367,7 @@ spec_status spec_verify_tree_residual(const void* node_logits, int logit_dtype, 
   if (!residual_sizes_ok(B, N, V)) return SPEC_EINVAL;
   if (!temperature_ok(temperature)) return SPEC_EINVAL;
   if (!dtype_ok(logit_dtype) || !dtype_ok(q_dtype)) return SPEC_EDTYPE;
-  if (!sv::grid_fits(sv::tree_blocks(B, V))) return SPEC_EINVAL;
+  if (!sv::grid_fits(sv::tree_blocks(B, V, true))) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
   if (!node_logits || !draft_probs || !node_tokens || !parents || !accept_uniforms || !draw_uniforms ||
       !accepted_len || !out_tokens || !out_nodes || !req_status)
@@ -390,15 +390,15 @@ spec_status spec_verify_tree_residual(const void* node_logits, int logit_dtype, 
   p.part = reinterpret_cast<float2*>(ws + L.part);
   p.deep = reinterpret_cast<float2*>(ws + L.deep);
   p.order = reinterpret_cast<unsigned long long*>(ws + L.order);
-  p.desc = reinterpret_cast<unsigned*>(ws + L.desc);
-  p.desc_words = 4 + 2 * N;
+  p.desc = reinterpret_cast<unsigned long long*>(ws + L.desc);
+  p.desc_words = 3 + 2 * N;
   p.counters = sv::request_counters(workspace);
   p.B = B;
   p.N = N;
   p.V = V;
   p.P = chunks(V, sv::kWaveChunk);
   p.WG1 = chunks(p.P, sv::kWavesPerBlock);
-  p.WH = chunks(p.P, sv::kTreeHelperChunks);
+  p.WH = (int)sv::tree_helpers(p.P, true);
   p.c2 = static_cast<float>(kLog2e / static_cast<double>(temperature));
   const bool vec = (V % 8 == 0) && aligned16(node_logits) && aligned16(draft_probs);
   SPEC_TRACE_FILL(p);

@@ -195,8 +195,8 @@ struct TreeParams {
   // residual-update verifier only
   const void* q;             // [B, N, V] proposal rows: row c = the distribution node c was drawn from
   const float* u_draw;       // [B, N] terminal draw at node v (u holds the child accept uniforms)
-  unsigned* desc;            // [B * desc_words] residual-pass descriptors
-  int q_dtype, desc_words;   // desc_words = 4 + 2N
+  unsigned long long* desc;  // [B * desc_words] residual-pass descriptors (tagged 64-bit words)
+  int q_dtype, desc_words;   // desc_words = 3 + 2N
   SPEC_TRACE_MEMBER
 };
 
@@ -208,6 +208,15 @@ constexpr int kTreeStage = 1024;
 // row (its four waves two chunks each, loads in flight together).
 constexpr int kTreeHelperBatch = 2;
 constexpr int kTreeHelperChunks = 4 * kTreeHelperBatch;
+// The residual-update tree's helpers take one chunk per wave: a residual pass reads the row
+// and every rejected child's q row at each element, so fewer chunks per wave means fewer
+// dependent rounds of loads per pass.
+constexpr int kResidHelperBatch = 1;
+constexpr int kResidHelperChunks = 4 * kResidHelperBatch;
+inline long tree_helpers(long P, bool residual) {
+  const long per = residual ? kResidHelperChunks : kTreeHelperChunks;
+  return (P + per - 1) / per;
+}
 
 // Workspace carving: 256 bytes of global counters, kCounterSlots 32-bit counters per
 // request, then the data regions, each on a 256-byte boundary.  Every call returns all
@@ -286,7 +295,7 @@ inline TreeLayout tree_layout(long B, long N, long V, bool residual = false) {
   L.part = o;   o = align256(o + sizeof(float2) * B * P);
   L.deep = o;   o = align256(o + sizeof(float2) * B * 2 * P);
   L.order = o;  o = align256(o + sizeof(unsigned long long) * B);
-  L.desc = o;   if (residual) o = align256(o + sizeof(unsigned) * B * (4 + 2 * N));
+  L.desc = o;   if (residual) o = align256(o + sizeof(unsigned long long) * B * (3 + 2 * N));
   L.total = o;
   return L;
 }
@@ -301,10 +310,9 @@ inline unsigned long long greedy_blocks(long B, long G, long V) {
   const long R = G + 1;
   return (unsigned long long)B * ((unsigned long long)R * slicing(B * R, V, kGreedyTargetBlocks).SL + 1);
 }
-inline unsigned long long tree_blocks(long B, long V) {
+inline unsigned long long tree_blocks(long B, long V, bool residual = false) {
   const long P = (V + 2047) / 2048;
-  return (unsigned long long)B * ((P + kWavesPerBlock - 1) / kWavesPerBlock +
-                                  (P + kTreeHelperChunks - 1) / kTreeHelperChunks);
+  return (unsigned long long)B * ((P + kWavesPerBlock - 1) / kWavesPerBlock + tree_helpers(P, residual));
 }
 inline bool grid_fits(unsigned long long blocks) { return blocks <= 0xffffffffull / kBlock; }
 

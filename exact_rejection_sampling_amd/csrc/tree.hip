@@ -171,101 +171,140 @@ constexpr unsigned kTreeDone = 0xffffffffu;
 constexpr unsigned kResidualPass = 0x40000000u;
 
 // ------------------------------------------------------------ residual-update verifier
-// Descriptor of the residual passes at the current node v, written by the walker before
-// each pass order: [0] v, [1] bits of r (reference exponent of row v), [2] bits of 1/Z
-// (base 2), [3] the generation of the pass order it is complete for, [4 + j] the j-th
-// rejected child, [4 + N + j] bits of 1/W_j, W_j the mass of the residual after j + 1
-// rejections.  The walker (one thread) writes every word through, waits for those stores
-// to complete (vmem_wait), then writes word 3 and the order.  A helper that sees the order
-// re-reads word 3 until it holds the order's generation before it reads the rest, so it
-// never reads a descriptor older than its order, whichever store arrives first.
+// Descriptor of the residual passes at the current node v: 64-bit words, each tag << 32 |
+// value, written through by the walker (one thread) before the pass order that first needs
+// it: [0] v, [1] bits of r (reference exponent of row v), [2] bits of 1/Z (base 2), [3 + j]
+// the j-th rejected child, [3 + N + j] bits of 1/W_j, W_j the mass of the residual after
+// j + 1 rejections.  A node's pass orders carry consecutive generations g1, g1 + 1, ...
+// (nothing else is ordered between them), so pass i (order generation g) has g1 = g - i + 1,
+// and the tag of words 0..2 is g1 and that of child j and of 1/W_j is g1 + j.  Every word
+// thus validates itself: a helper re-reads a word until its tag is the one the order
+// implies, in whatever order the stores arrive, and no store of the walker needs to wait
+// for another.  Generations only grow within a call and the walker zeroes the descriptor
+// before the call ends, so no stale word carries a current tag.
 constexpr int kResidStage = 256;   // rejected children a helper keeps in LDS per pass
+__device__ __forceinline__ unsigned long long desc_word(unsigned tag, unsigned v) {
+  return (static_cast<unsigned long long>(tag) << 32) | v;
+}
+__device__ __forceinline__ unsigned desc_value(unsigned long long w) { return static_cast<unsigned>(w); }
 // A chunk-mass word meaning "the helper's descriptor never became current": the walker
 // reports SPEC_REQ_INTERNAL on it.  (A published mass is a negated fp64 value; this is a
 // NaN bit pattern that no negated mass takes.)
 constexpr unsigned long long kLostMassWord = 0x7ff4000000000001ull;
 
-// The unnormalized residual after i rejected children c_0..c_{i-1} at node v for the
-// eight elements [e0, e0 + 8): p(x) = 2^(l c2 - r) / Z, res_0 = p,
+// The unnormalized residual after i rejected children c_0..c_{i-1} at node v, for NV
+// vectors of eight elements [e0 + n * step, + 8): p(x) = 2^(l c2 - r) / Z, res_0 = p,
 // res_{j+1} = [res_j - q_{c_j}]_+ / W_j for j + 1 < i, and g = [res_{i-1} - q_{c_{i-1}}]_+.
 // One expression serves the helpers' chunk masses, the walker's single-element accept
-// tests and its rescan, so the three agree bit for bit.  bad: an entry of the last
-// rejected child's q row is negative or non-finite.
-template <int DT, int QT, bool VEC>
-__device__ __forceinline__ void residual8(const TreeParams& p, int b, const unsigned* d, int i, const int* s_kid,
-                                          const float* s_invw, const void* lrow, long e0, float r, float inv_z,
-                                          float (&g)[8], bool& bad) {
-  float l[8];
-  load8<DT, VEC, false>(lrow, e0, p.V, l, -INFINITY);
+// tests and its rescan, so the three agree bit for bit.  The NV vectors' loads of each row
+// are issued together, and the first rejected child's q row is fetched with the logits,
+// so a call costs max(1, i) dependent memory round trips.  The children and their 1/W come
+// from LDS (s_kid, s_invw: the first kResidStage of them) or else from the descriptor.
+// bad: an entry of the last rejected child's q row is negative or non-finite.
+template <int DT, int QT, bool VEC, int NV>
+__device__ __forceinline__ void residualN(const TreeParams& p, int b, const unsigned long long* d, int i,
+                                          const int* s_kid,
+                                          const float* s_invw, const void* lrow, long e0, long step, float r,
+                                          float inv_z, float (&g)[NV][8], bool& bad) {
+  auto kid_of = [&](int j) {
+    return j < kResidStage && s_kid ? s_kid[j] : static_cast<int>(desc_value(fetch_u64(d + 3 + j)));
+  };
+  float l[NV][8], q[NV][8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) g[k] = scaled_exp(l[k], p.c2, r) * inv_z;
+  for (int n = 0; n < NV; ++n) load8<DT, VEC, false>(lrow, e0 + n * step, p.V, l[n], -INFINITY);
+  if (i > 0) {
+    const void* q0 = row_ptr<QT>(p.q, (size_t)b * p.N + kid_of(0), p.V);
+#pragma unroll
+    for (int n = 0; n < NV; ++n) load8<QT, VEC, false>(q0, e0 + n * step, p.V, q[n], 0.0f);
+  }
+#pragma unroll
+  for (int n = 0; n < NV; ++n)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) g[n][k] = scaled_exp(l[n][k], p.c2, r) * inv_z;
   for (int j = 0; j < i; ++j) {
-    const int kid = j < kResidStage && s_kid ? s_kid[j] : static_cast<int>(fetch_u32(d + 4 + j));
     const float invw = j + 1 == i ? 1.0f
-                       : (j < kResidStage && s_invw ? s_invw[j] : __uint_as_float(fetch_u32(d + 4 + p.N + j)));
-    float q[8];
-    load8<QT, VEC, false>(row_ptr<QT>(p.q, (size_t)b * p.N + kid, p.V), e0, p.V, q, 0.0f);
+                       : (j < kResidStage && s_invw ? s_invw[j] : __uint_as_float(desc_value(fetch_u64(d + 3 + p.N + j))));
+    if (j > 0) {
+      const void* qj = row_ptr<QT>(p.q, (size_t)b * p.N + kid_of(j), p.V);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float t = g[k] - q[k];
-      const float pos = t > 0.0f ? t : 0.0f;
-      if (j + 1 == i) bad |= !(q[k] >= 0.0f && q[k] < INFINITY);
-      g[k] = j + 1 == i ? pos : pos * invw;
+      for (int n = 0; n < NV; ++n) load8<QT, VEC, false>(qj, e0 + n * step, p.V, q[n], 0.0f);
     }
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float t = g[n][k] - q[n][k];
+        const float pos = t > 0.0f ? t : 0.0f;
+        if (j + 1 == i) bad |= !(q[n][k] >= 0.0f && q[n][k] < INFINITY);
+        g[n][k] = j + 1 == i ? pos : pos * invw;
+      }
   }
 }
 
-// Helper h's part of residual pass i: the chunk masses (fp64) of g over its chunks.
+// Helper h's part of residual pass i (order generation gen): the chunk masses (fp64) of g
+// over its chunks.  The descriptor words the pass needs -- v, r, 1/Z, the i rejected
+// children and the i - 1 values 1/W_j -- are read together, one thread each, and each is
+// re-read until it carries the tag the order implies (bounded).
 template <int DT, int QT, bool VEC>
 __device__ void residual_pass(const TreeParams& p, int b, int h, unsigned gen, int i) {
   __shared__ int s_kid[kResidStage];
   __shared__ float s_invw[kResidStage];
-  __shared__ int s_current;
+  __shared__ unsigned s_head[3];
+  __shared__ int s_stale;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
-  const unsigned* d = p.desc + (size_t)b * p.desc_words;
-  if (tid == 0) {
-    unsigned tag = fetch_u32(d + 3);
-    for (unsigned spins = 0; tag != gen && spins < kSpinLimit; ++spins) {
+  const unsigned long long* d = p.desc + (size_t)b * p.desc_words;
+  const unsigned g1 = gen - static_cast<unsigned>(i) + 1u;   // the node's first pass order
+  if (tid == 0) s_stale = 0;
+  __syncthreads();
+  const int nwords = 2 + 2 * i;   // 3 head words, i children, i - 1 values 1/W_j
+  for (int k = tid; k < nwords; k += kBlock) {
+    const int j = k < 3 ? 0 : (k < 3 + i ? k - 3 : k - 3 - i);
+    const int idx = k < 3 ? k : (k < 3 + i ? 3 + j : 3 + p.N + j);
+    const unsigned tag = g1 + static_cast<unsigned>(j);
+    unsigned long long w = fetch_u64(d + idx);
+    for (unsigned spins = 0; static_cast<unsigned>(w >> 32) != tag && spins < kSpinLimit; ++spins) {
       __builtin_amdgcn_s_sleep(1);
-      tag = fetch_u32(d + 3);
+      w = fetch_u64(d + idx);
     }
-    s_current = tag == gen;
+    if (static_cast<unsigned>(w >> 32) != tag) s_stale = 1;
+    const unsigned val = desc_value(w);
+    if (k < 3) s_head[k] = val;
+    else if (k < 3 + i) { if (j < kResidStage) s_kid[j] = static_cast<int>(val); }
+    else if (j < kResidStage) s_invw[j] = __uint_as_float(val);
   }
   __syncthreads();
-  if (!s_current) {   // the wait bound: say so in every chunk mass this helper owns
-    double* dst = reinterpret_cast<double*>(p.deep + ((size_t)b * 2 + (gen & 1u)) * p.P);
-    for (int k = tid; k < kTreeHelperChunks; k += kBlock) {
-      const int c = h * kTreeHelperChunks + k;
+  double* dst = reinterpret_cast<double*>(p.deep + ((size_t)b * 2 + (gen & 1u)) * p.P);
+  if (s_stale) {   // the wait bound: say so in every chunk mass this helper owns
+    for (int k = tid; k < kResidHelperChunks; k += kBlock) {
+      const int c = h * kResidHelperChunks + k;
       if (c < p.P) publish_u64(reinterpret_cast<unsigned long long*>(dst + c), kLostMassWord);
     }
+    __syncthreads();
     return;
   }
-  const int v = static_cast<int>(fetch_u32(d));
-  const float r = __uint_as_float(fetch_u32(d + 1)), inv_z = __uint_as_float(fetch_u32(d + 2));
-  for (int j = tid; j < min(i, kResidStage); j += kBlock) {
-    s_kid[j] = static_cast<int>(fetch_u32(d + 4 + j));
-    s_invw[j] = __uint_as_float(fetch_u32(d + 4 + p.N + j));
-  }
-  __syncthreads();
+  // every word of the pass has been validated, so re-reads of children past kResidStage
+  // (residualN) return the same values: the walker writes each word once per node visit
+  const int v = static_cast<int>(s_head[0]);
+  const float r = __uint_as_float(s_head[1]), inv_z = __uint_as_float(s_head[2]);
   const void* row = row_ptr<DT>(p.logits, (size_t)b * p.N + v, p.V);
-  double* dst = reinterpret_cast<double*>(p.deep + ((size_t)b * 2 + (gen & 1u)) * p.P);
-  for (int k = 0; k < kTreeHelperBatch; ++k) {
-    const int c = h * kTreeHelperChunks + k * kWavesPerBlock + wave;
+  for (int k = 0; k < kResidHelperBatch; ++k) {
+    const int c = h * kResidHelperChunks + k * kWavesPerBlock + wave;
     if (c >= p.P) continue;
     double acc = 0.0;
     bool bad = false;
-    for (int jv = 0; jv < kStatVecs; ++jv) {
-      const long e0 = (long)c * kWaveChunk + static_cast<long>(jv * kWave + lane) * kVec;
-      float g[8];
-      residual8<DT, QT, VEC>(p, b, d, i, s_kid, s_invw, row, e0, r, inv_z, g, bad);
+    float g[kStatVecs][8];
+    residualN<DT, QT, VEC, kStatVecs>(p, b, d, i, s_kid, s_invw, row,
+                                      (long)c * kWaveChunk + static_cast<long>(lane) * kVec, (long)kWave * kVec,
+                                      r, inv_z, g, bad);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += (double)g[e];
-    }
+    for (int jv = 0; jv < kStatVecs; ++jv)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (double)g[jv][e];
     if (bad) acc = NAN;
     const double m = wave_sum_d(acc);
     if (lane == 0) publish_mass(dst + c, m);
   }
-  __syncthreads();   // s_kid and s_invw are rewritten by the next pass
+  __syncthreads();   // s_kid, s_invw and s_head are rewritten by the next pass
 }
 
 __device__ __forceinline__ void publish_order(const TreeParams& p, int b, unsigned gen, unsigned code) {
@@ -351,25 +390,43 @@ __device__ int argmax_published(const TreeParams& p, const float2* src, int* sta
   return bi;
 }
 
+// Validation of a request's tree ([M7.7] §0x0F: parents[0] = -1, 0 <= parents[v] < v, and
+// non-root tokens in [0, V)), split so that its loads overlap the walker's first staging:
+// tree_check_issue loads node 1 + t (and thread 0 parents[0]) into registers,
+// tree_check_done compares them (and any nodes past the first kBlock + 1, directly).
+// Block-wide; returns true when the tree is bad.
+struct TreeCheck { int pv, tv, p0; };
+__device__ __forceinline__ TreeCheck tree_check_issue(const int32_t* par, const int32_t* tok, int N) {
+  const int v = 1 + threadIdx.x;
+  TreeCheck k{0, 0, -1};
+  if (v < N) {
+    k.pv = par[v];
+    k.tv = tok[v];
+  }
+  if (threadIdx.x == 0) k.p0 = par[0];
+  return k;
+}
+__device__ bool tree_check_done(const int32_t* par, const int32_t* tok, int N, int V, const TreeCheck& k) {
+  const int v = 1 + threadIdx.x;
+  bool bad = (v < N && (k.pv < 0 || k.pv >= v || k.tv < 0 || k.tv >= V)) || (threadIdx.x == 0 && k.p0 != -1);
+  for (int w = 1 + kBlock + threadIdx.x; w < N; w += kBlock) {
+    const int pw = par[w], tw = tok[w];
+    bad |= pw < 0 || pw >= w || tw < 0 || tw >= V;
+  }
+  return __syncthreads_or(bad) != 0;
+}
+
 // Walk of request b by the last root block.  `gen` counts the orders sent to the helpers.
 // ARGMAX: greedy mode, the target's argmax stands in for its sample (no uniforms).
 template <int DT, bool VEC, bool ARGMAX>
 __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
-  __shared__ int s_bad;
   __shared__ int s_imin[kWavesPerBlock];
   const int tid = threadIdx.x;
   const int N = p.N;
   const int32_t* par = p.parents + (size_t)b * N;
   const int32_t* tok = p.node_tokens + (size_t)b * N;
-
-  if (tid == 0) s_bad = (par[0] != -1);
-  __syncthreads();
-  for (int v = 1 + tid; v < N; v += kBlock) {
-    const int pv = par[v], tv = tok[v];
-    if (pv < 0 || pv >= v || tv < 0 || tv >= p.V) s_bad = 1;
-  }
-  __syncthreads();
-  if (s_bad) { tree_fail(p, b, SPEC_REQ_BADTREE); return; }
+  // the tree's validation: loads now, verdict after the root's sample (before any status)
+  const TreeCheck check = tree_check_issue(par, tok, N);
 
   int v = 0, depth = 0;
   while (true) {
@@ -392,6 +449,7 @@ __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
       vmem_wait();      // the clears are complete before any later order reuses the words
     }
     SPEC_STAMP_AT(p, 2, trec, 3);
+    if (v == 0 && tree_check_done(par, tok, N, p.V, check)) { tree_fail(p, b, SPEC_REQ_BADTREE); return; }
     if (status != 0) { tree_fail(p, b, status); return; }
     int cand = kNoPick;           // this thread's lowest matching child (c rises)
     for (int c = v + 1 + tid; c < N; c += kBlock)
@@ -460,8 +518,9 @@ __device__ double mass_prefix(const double* mass, int P, int c_lo, int c_hi, dou
 // g with u, from the chunk masses of the last pass (in `mass`, total W) and a rescan of
 // the chunk holding the target.
 template <int DT, int QT, bool VEC>
-__device__ int residual_pick(const TreeParams& p, int b, const unsigned* d, int i, const void* row, float r,
-                             float inv_z, const double* mass, float u) {
+__device__ int residual_pick(const TreeParams& p, int b, const unsigned long long* d, int i, const int* s_kid,
+                             const float* s_invw, const void* row, float r, float inv_z, const double* mass,
+                             float u) {
   __shared__ double s_scan[kWavesPerBlock];
   __shared__ int s_imin[kWavesPerBlock];
   __shared__ double s_before;
@@ -491,9 +550,10 @@ __device__ int residual_pick(const TreeParams& p, int b, const unsigned* d, int 
   __syncthreads();
   const double rem = t - s_before;
   const long e0 = (long)cstar * kWaveChunk + (long)tid * kVec;
-  float g[8];
+  float gv[1][8];
   bool bad = false;
-  residual8<DT, QT, VEC>(p, b, d, i, nullptr, nullptr, row, e0, r, inv_z, g, bad);
+  residualN<DT, QT, VEC, 1>(p, b, d, i, s_kid, s_invw, row, e0, 0, r, inv_z, gv, bad);
+  const float (&g)[8] = gv[0];
   double incl[8];
   double acc = 0.0;
   int last_pos = -1;
@@ -520,27 +580,26 @@ __device__ int residual_pick(const TreeParams& p, int b, const unsigned* d, int 
 // children are all rejected (or which has none) emits a draw of the residual.
 template <int DT, int QT, bool VEC>
 __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
-  __shared__ int s_bad, s_lost, s_status, s_accept;
+  __shared__ int s_lost, s_status, s_accept;
   __shared__ int s_imin[kWavesPerBlock];
   __shared__ float s_red[kWavesPerBlock];
   __shared__ double s_scan[kWavesPerBlock];
   __shared__ float2 s_sum[kTreeStage];
   __shared__ double s_mass[kTreeStage];
   __shared__ unsigned s_gen;
+  // the node's rejected children, the 1/W of their residuals and their q values at the child
+  // under test (the first kResidStage; the descriptor holds them all)
+  __shared__ int s_kid[kResidStage];
+  __shared__ float s_invw[kResidStage];
+  __shared__ float s_qx[kResidStage];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   const int N = p.N, P = p.P;
   const int32_t* par = p.parents + (size_t)b * N;
   const int32_t* tok = p.node_tokens + (size_t)b * N;
-  unsigned* d = p.desc + (size_t)b * p.desc_words;
-
-  if (tid == 0) s_bad = (par[0] != -1);
-  __syncthreads();
-  for (int v = 1 + tid; v < N; v += kBlock) {
-    const int pv = par[v], tv = tok[v];
-    if (pv < 0 || pv >= v || tv < 0 || tv >= p.V) s_bad = 1;
-  }
-  __syncthreads();
-  if (s_bad) { tree_fail(p, b, SPEC_REQ_BADTREE); return; }
+  unsigned long long* d = p.desc + (size_t)b * p.desc_words;
+  unsigned g1 = 0;   // thread 0: the generation of the current node's first pass order
+  // the tree's validation: loads now, verdict once the root's summaries are staged
+  const TreeCheck check = tree_check_issue(par, tok, N);
 
   int v = 0, depth = 0, hop = 0;
   while (true) {
@@ -554,6 +613,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
     float2* src = v == 0 ? p.part + (size_t)b * P : p.deep + ((size_t)b * 2 + (gen & 1u)) * P;
     stage_summaries(src, s_sum, P, &s_lost);
     SPEC_STAMP_AT(p, 3, trec, 2);
+    if (v == 0 && tree_check_done(par, tok, N, p.V, check)) { tree_fail(p, b, SPEC_REQ_BADTREE); return; }
     if (v != 0) {
       for (int c = tid; c < P; c += kBlock) clear_f2(src + c);
       vmem_wait();
@@ -579,22 +639,33 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
     int i = 0, accepted = kNoPick;
     int c = next_child(par, N, v, v, s_imin);
     while (c != kNoPick) {
+      // the accept test's loads, issued together: thread 0 the child's q(x), u and the row's
+      // logit at x; thread 1 + j the q value at x of rejected child j
+      const int x = tok[c];
+      float qx = 0.0f, ua = 0.0f, lx = 0.0f;
+      if (tid == 0) {
+        qx = load_scalar<QT>(p.q, ((size_t)b * N + c) * p.V + x);
+        ua = p.u[(size_t)b * N + c];
+        lx = load_scalar<DT>(row, x);
+      } else if (tid - 1 < min(i, kResidStage)) {
+        s_qx[tid - 1] = load_scalar<QT>(p.q, ((size_t)b * N + s_kid[tid - 1]) * p.V + x);
+      }
+      __syncthreads();
       if (tid == 0) {
         int st = 0, acc = 0;
-        const int x = tok[c];
-        const float qx = load_scalar<QT>(p.q, ((size_t)b * N + c) * p.V + x);
-        const float ua = p.u[(size_t)b * N + c];
         if (!(isfinite(qx) && qx > 0.0f)) {
           st = SPEC_REQ_QZERO;
         } else if (!(ua >= 0.0f && ua < 1.0f)) {
           st = SPEC_REQ_BADUNIFORM;
         } else {
-          // residual at x after the i rejections so far, the same expression as residual8
-          float g = scaled_exp(load_scalar<DT>(row, x), p.c2, r) * inv_z;
+          // residual at x after the i rejections so far, the same expression as residualN
+          float g = scaled_exp(lx, p.c2, r) * inv_z;
           for (int j = 0; j < i; ++j) {
-            const int kid = static_cast<int>(fetch_u32(d + 4 + j));
-            const float invw = __uint_as_float(fetch_u32(d + 4 + N + j));
-            const float t = g - load_scalar<QT>(p.q, ((size_t)b * N + kid) * p.V + x);
+            const float qj = j < kResidStage
+                                 ? s_qx[j]
+                                 : load_scalar<QT>(p.q, ((size_t)b * N + static_cast<int>(desc_value(fetch_u64(d + 3 + j)))) * p.V + x);
+            const float invw = j < kResidStage ? s_invw[j] : __uint_as_float(desc_value(fetch_u64(d + 3 + N + j)));
+            const float t = g - qj;
             g = (t > 0.0f ? t : 0.0f) * invw;
           }
           const double a = fmin(1.0, (double)g / (double)qx);
@@ -608,14 +679,15 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
       if (s_accept) { accepted = c; break; }
       // rejected: the residual's chunk masses from a helper pass
       if (tid == 0) {
+        const unsigned tag = gen + 1u;    // this pass order's generation, g1 + i
         if (i == 0) {
-          publish_u32(d, static_cast<unsigned>(v));
-          publish_u32(d + 1, __float_as_uint(r));
-          publish_u32(d + 2, __float_as_uint(inv_z));
+          g1 = tag;
+          publish_u64(d, desc_word(g1, static_cast<unsigned>(v)));
+          publish_u64(d + 1, desc_word(g1, __float_as_uint(r)));
+          publish_u64(d + 2, desc_word(g1, __float_as_uint(inv_z)));
         }
-        publish_u32(d + 4 + i, static_cast<unsigned>(c));
-        vmem_wait();                      // every descriptor word has completed: then its tag
-        publish_u32(d + 3, gen + 1u);
+        publish_u64(d + 3 + i, desc_word(tag, static_cast<unsigned>(c)));
+        if (i < kResidStage) s_kid[i] = c;
         publish_order(p, b, ++gen, kResidualPass | static_cast<unsigned>(i + 1));
         s_gen = gen;
         s_lost = 0;
@@ -642,7 +714,11 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
       double W;
       mass_prefix(s_mass, P, c_lo, c_hi, &W);
       if (!(isfinite(W) && W > 0.0)) { tree_fail(p, b, SPEC_REQ_RESIDUAL_EMPTY); return; }
-      if (tid == 0) publish_u32(d + 4 + N + (i - 1), __float_as_uint((float)(1.0 / W)));
+      if (tid == 0) {
+        const float invw = (float)(1.0 / W);
+        publish_u64(d + 3 + N + (i - 1), desc_word(gen, __float_as_uint(invw)));   // tag g1 + i - 1
+        if (i - 1 < kResidStage) s_invw[i - 1] = invw;
+      }
       SPEC_STAMP_AT(p, 3, prec, 3);
       c = next_child(par, N, v, c, s_imin);
     }
@@ -650,7 +726,6 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
       if (tid == 0) {
         p.out_tokens[(size_t)b * N + depth] = tok[accepted];
         p.out_nodes[(size_t)b * N + depth] = accepted;
-        vmem_wait();
         publish_order(p, b, ++gen, static_cast<unsigned>(accepted) + 1u);   // summarize its row
         s_gen = gen;
       }
@@ -671,7 +746,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
       y = sample_row<DT, VEC, false>(p, s_sum, row, ud, &status);
       if (status != 0) { tree_fail(p, b, status); return; }
     } else {
-      y = residual_pick<DT, QT, VEC>(p, b, d, i, row, r, inv_z, s_mass, ud);
+      y = residual_pick<DT, QT, VEC>(p, b, d, i, s_kid, s_invw, row, r, inv_z, s_mass, ud);
     }
     SPEC_STAMP_AT(p, 3, trec, 5);
     for (int k = tid; k < N; k += kBlock) {
@@ -724,15 +799,17 @@ __device__ void helper_item(const TreeParams& p, int b, int h) {
     }
     const void* row = row_ptr<DT>(p.logits, (size_t)b * p.N + (code - 1u), p.V);
     float2* dst = p.deep + ((size_t)b * 2 + (gen & 1u)) * p.P;
-    ChunkRegs<DT> r[kTreeHelperBatch];
+    constexpr int HB = RESID ? kResidHelperBatch : kTreeHelperBatch;     // chunks per wave
+    constexpr int HC = RESID ? kResidHelperChunks : kTreeHelperChunks;   // chunks per helper
+    ChunkRegs<DT> r[HB];
 #pragma unroll
-    for (int k = 0; k < kTreeHelperBatch; ++k) {
-      const int c = h * kTreeHelperChunks + k * kWavesPerBlock + wave;
+    for (int k = 0; k < HB; ++k) {
+      const int c = h * HC + k * kWavesPerBlock + wave;
       if (c < p.P) chunk_load<DT, VEC>(row, p.V, c, lane, r[k]);
     }
 #pragma unroll
-    for (int k = 0; k < kTreeHelperBatch; ++k) {
-      const int c = h * kTreeHelperChunks + k * kWavesPerBlock + wave;
+    for (int k = 0; k < HB; ++k) {
+      const int c = h * HC + k * kWavesPerBlock + wave;
       if (c < p.P) {
         // the same per-chunk summary the root blocks form (one chunk per wave)
         float v[kStatVecs][8];
@@ -813,7 +890,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
   if (threadIdx.x == 0) publish_order(p, b, gen + 1u, kTreeDone);   // dismiss the helpers
   for (int j = threadIdx.x; j < p.P; j += kBlock) clear_f2(p.part + (size_t)b * p.P + j);
   if constexpr (RESID)   // no helper reads the descriptor once dismissed
-    for (int j = threadIdx.x; j < p.desc_words; j += kBlock) publish_u32(p.desc + (size_t)b * p.desc_words + j, 0u);
+    for (int j = threadIdx.x; j < p.desc_words; j += kBlock) publish_u64(p.desc + (size_t)b * p.desc_words + j, 0ull);
   if (threadIdx.x == 0) reset_counter(&p.counters[(size_t)b * kCounterSlots + 0]);
   SPEC_STAMP(p, K, 3);
 }
