@@ -141,22 +141,45 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
 
 
-_WS_CACHE = {}
+_WS_CACHE = {}   # (kind, device index, stream handle) -> (workspace tensor, stream)
 
 
 def workspace(kind: str, size: int, device: torch.device, stream: torch.cuda.Stream) -> torch.Tensor:
     """A zero-initialised workspace of at least `size` bytes, kept per (kind, device, stream).
 
     Calls on one stream run in order and leave the workspace zeroed, so it is reused;
-    calls on different streams get different workspaces.
+    calls on different streams get different workspaces.  After a call reports
+    SPEC_REQ_INTERNAL, reset_workspaces() zero-fills them again.
     """
     key = (kind, device.index, stream.cuda_stream)
-    ws = _WS_CACHE.get(key)
+    ent = _WS_CACHE.get(key)
+    ws = None if ent is None else ent[0]
     if ws is None or ws.numel() < size:
         with torch.cuda.stream(stream):
             ws = torch.zeros(max(size, 256) + 256, dtype=torch.uint8, device=device)
-        _WS_CACHE[key] = ws
+        _WS_CACHE[key] = (ws, stream)
     return ws
+
+
+def reset_workspaces(device=None) -> int:
+    """Zero-fills the workspaces this module has cached (all of them, or those on `device`),
+    each with a fill on the stream it serves; returns how many were reset.
+
+    A wait between blocks that gives up (status SPEC_REQ_INTERNAL) may leave a published
+    word behind.  A chain call repairs its own workspace; a greedy or tree call marks it
+    dirty, and every later call on it then reports SPEC_REQ_INTERNAL for all its requests
+    until the workspace is zero-filled: this does that for the cached ones (a caller-owned
+    workspace_tensor is the caller's to zero).  Not for use during graph capture.
+    """
+    want = None if device is None else torch.device(device).index
+    n = 0
+    for (kind, dev_index, _), (ws, stream) in list(_WS_CACHE.items()):
+        if want is not None and dev_index != want:
+            continue
+        with torch.cuda.stream(stream):
+            ws.zero_()
+        n += 1
+    return n
 
 
 def _aligned_ws(ws: torch.Tensor) -> tuple:

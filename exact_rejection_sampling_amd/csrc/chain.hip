@@ -825,6 +825,31 @@ __device__ __forceinline__ double exact_w(float l, float q, double c2d, double r
   return t > 0.0 ? t : 0.0;
 }
 
+// Request b fails with `status`: no tokens, NaN statistics (block-wide).
+__device__ void chain_fail(const ChainParams& p, int b, int status) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < p.R; i += kBlock) p.out_tokens[(size_t)b * p.R + i] = -1;
+  if (p.stats)
+    for (int i = tid; i < 4 * p.R; i += kBlock) p.stats[(size_t)b * p.R * 4 + i] = NAN;
+  if (tid == 0) {
+    p.accepted_len[b] = -1;
+    p.req_status[b] = status;
+    if (p.st.finish) p.st.finish[b] = 0;
+  }
+}
+
+// Every workspace word of request b back to zero (block-wide).
+__device__ void chain_scrub(const ChainParams& p, int b) {
+  const int tid = threadIdx.x;
+  float2* part_b = p.part + (size_t)b * p.R * p.SL;
+  for (int j = tid; j < p.R * p.SL; j += kBlock) clear_f2(part_b + j);
+  for (int j = tid; j < 3 * p.G; j += kBlock) clear_u64(gather_rec(p, b, 0) + j);
+  for (int j = tid; j < p.S2; j += kBlock) clear_mass(p.tmass + (size_t)b * p.S2 + j);
+  for (int j = tid; j < 3 * p.S2; j += kBlock) clear_mass(p.xmass + (size_t)b * p.S2 * 3 + j);
+  if (p.thresh_ws)
+    for (int j = tid; j < p.R; j += kBlock) store_wt(p.thresh_ws + (size_t)b * p.R + j, 0.0f);
+}
+
 __device__ __forceinline__ double* xmass_word(const ChainParams& p, int b, int c, int k) {
   return p.xmass + ((size_t)b * p.S2 + c) * 3 + k;
 }
@@ -840,7 +865,21 @@ __global__ __launch_bounds__(kBlock) void chain_exact_kernel(ChainParams p) {
   SPEC_STAMP(p, 1, 1);
   unsigned* rec = reinterpret_cast<unsigned*>(p.part + (size_t)b * p.R * p.SL);
   const unsigned pend = rec[0];
+  const int chain_status = p.req_status[b];
+  const unsigned dirty = fetch_u32(dirty_word(p.part));
   SPEC_TAG(p, 1, SPEC_TRACE_TAG(pend ? kTraceExact : kTraceExactIdle, b, c));
+  if (dirty != 0u || chain_status == SPEC_REQ_INTERNAL) {
+    // A wait of the chain kernel gave up on this request: a word published after its
+    // consumer cleared it may be left over.  Every block of the chain kernel has finished
+    // now, so zeroing the request's words here leaves them clean for later calls.  On a
+    // dirty workspace (a wait of an earlier call gave up) no result of this call can be
+    // trusted: every request fails.
+    if (c == 0) {
+      if (dirty != 0u) chain_fail(p, b, SPEC_REQ_INTERNAL);
+      chain_scrub(p, b);
+    }
+    return;
+  }
   if (pend == 0u) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   ChainDecision d{};
@@ -988,14 +1027,9 @@ __global__ __launch_bounds__(kBlock) void chain_exact_kernel(ChainParams p) {
       if (p.st.finish) p.st.finish[b] = finish;
     }
   } else {
-    for (int i = tid; i < p.R; i += kBlock) p.out_tokens[(size_t)b * p.R + i] = -1;
-    if (p.stats)
-      for (int i = tid; i < 4 * p.R; i += kBlock) p.stats[(size_t)b * p.R * 4 + i] = NAN;
-    if (tid == 0) {
-      p.accepted_len[b] = -1;
-      p.req_status[b] = status;
-      if (p.st.finish) p.st.finish[b] = 0;
-    }
+    chain_fail(p, b, status);
+    // this kernel's own words may arrive after the clear below: nothing follows to repair it
+    if (status == SPEC_REQ_INTERNAL && tid == 0) publish_u32(dirty_word(p.part), 1u);
   }
   // every other block of the request has published its sums, and so has read the record
   __syncthreads();
@@ -1147,7 +1181,8 @@ hipError_t launch_typed(ChainParams p, hipStream_t s) {
   const unsigned long long blocks = (unsigned long long)p.B * ((unsigned long long)p.R * p.SL + p.S2);  // == chain_blocks
   chain_kernel<DT, QT, VEC, PROC><<<dim3((unsigned)blocks), dim3(kBlock), chain_dyn_lds(), s>>>(p);
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.G == 0) return e;   // with no drafts there is no residual
+  if (e != hipSuccess) return e;
+  // the exact redraws of small residuals, and the scrub of requests whose waits gave up
   chain_exact_kernel<DT, QT, VEC, PROC><<<dim3((unsigned)((size_t)p.B * p.S2)), dim3(kBlock), 0, s>>>(p);
   return hipGetLastError();
 }

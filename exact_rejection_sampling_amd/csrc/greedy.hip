@@ -121,6 +121,8 @@ __device__ bool greedy_decide(const GreedyParams& p, int b, int lo, int nr) {
   const int G = p.G, nd = min(G, nr);
   unsigned long long* part_b = p.part + (size_t)b * p.R * p.SL;
   if (tid == 0) s_lost = 0;
+  // the workspace's dirty word (a wait of an earlier call gave up), checked with the summaries
+  const unsigned dirty = tid == 0 ? fetch_u32(dirty_word(p.part)) : 0u;
   // wave 0's draft tokens and the remaining budget, fetched while the summaries are awaited
   int x = 0;
   if (wave == 0 && lane < G) x = p.tokens[(size_t)b * G + lane];
@@ -163,6 +165,7 @@ __device__ bool greedy_decide(const GreedyParams& p, int b, int lo, int nr) {
       s_bad[i] = any_nan || !(M > -INFINITY && M < INFINITY);
     }
   }
+  if (dirty) s_lost = 1;
   __syncthreads();
   // the summaries are consumed: return them to zero (every call leaves the workspace zeroed)
   if (!gate)
@@ -229,6 +232,8 @@ __device__ bool greedy_decide(const GreedyParams& p, int b, int lo, int nr) {
     p.accepted_len[b] = status == 0 ? A : -1;
     p.req_status[b] = status;
     if (p.st.finish) p.st.finish[b] = status == 0 ? finish : 0;
+    // a summary may arrive after the clear above: the workspace is no longer known to be zero
+    if (status == SPEC_REQ_INTERNAL) publish_u32(dirty_word(p.part), 1u);
   }
   return false;
 }

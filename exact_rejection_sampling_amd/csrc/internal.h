@@ -227,6 +227,16 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 
 constexpr int kCounterSlots = 4;                 // per request
 constexpr size_t kGlobalCounterBytes = 256;
+// Word 0 of the global header is the workspace's dirty word: a greedy or tree wait that gave
+// up sets it (a word published after its consumer cleared it may be left anywhere), and from
+// then on every call on the workspace reports SPEC_REQ_INTERNAL for all its requests until
+// the caller zero-fills the workspace.  (A chain call repairs its own give-ups instead: the
+// exact-redraw kernel that follows it zeroes those requests' words.)  Every layout starts
+// its first region right after the header, so a kernel finds the word from that region.
+__host__ __device__ __forceinline__ unsigned* dirty_word(const void* first_region) {
+  return reinterpret_cast<unsigned*>(const_cast<char*>(static_cast<const char*>(first_region)) -
+                                     kGlobalCounterBytes);
+}
 inline size_t counter_bytes(long B) { return align256(kGlobalCounterBytes + sizeof(unsigned) * kCounterSlots * B); }
 inline unsigned* request_counters(void* ws) {
   return reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kGlobalCounterBytes);

@@ -44,6 +44,7 @@ __device__ __forceinline__ unsigned long long hop_record(const TreeParams& p, in
          (unsigned long long)min(hop, kTraceHops - 1);
 }
 
+// A failed request.  SPEC_REQ_INTERNAL (a wait that gave up) also marks the workspace dirty.
 __device__ void tree_fail(const TreeParams& p, int b, int code) {
   for (int i = threadIdx.x; i < p.N; i += blockDim.x) {
     p.out_tokens[(size_t)b * p.N + i] = -1;
@@ -52,6 +53,7 @@ __device__ void tree_fail(const TreeParams& p, int b, int code) {
   if (threadIdx.x == 0) {
     p.accepted_len[b] = -1;
     p.req_status[b] = code;
+    if (code == SPEC_REQ_INTERNAL) publish_u32(dirty_word(p.counters), 1u);
   }
 }
 
@@ -391,29 +393,35 @@ __device__ int argmax_published(const TreeParams& p, const float2* src, int* sta
 }
 
 // Validation of a request's tree ([M7.7] §0x0F: parents[0] = -1, 0 <= parents[v] < v, and
-// non-root tokens in [0, V)), split so that its loads overlap the walker's first staging:
-// tree_check_issue loads node 1 + t (and thread 0 parents[0]) into registers,
-// tree_check_done compares them (and any nodes past the first kBlock + 1, directly).
-// Block-wide; returns true when the tree is bad.
-struct TreeCheck { int pv, tv, p0; };
-__device__ __forceinline__ TreeCheck tree_check_issue(const int32_t* par, const int32_t* tok, int N) {
+// non-root tokens in [0, V)) and of the workspace (its dirty word), split so that the loads
+// overlap the walker's first staging: tree_check_issue loads node 1 + t (and thread 0
+// parents[0] and the dirty word) into registers, tree_check_done compares them (and any
+// nodes past the first kBlock + 1, directly).  Block-wide; returns 0, SPEC_REQ_INTERNAL (a
+// dirty workspace) or SPEC_REQ_BADTREE.
+struct TreeCheck { int pv, tv, p0; unsigned dirty; };
+__device__ __forceinline__ TreeCheck tree_check_issue(const TreeParams& p, const int32_t* par, const int32_t* tok,
+                                                      int N) {
   const int v = 1 + threadIdx.x;
-  TreeCheck k{0, 0, -1};
+  TreeCheck k{0, 0, -1, 0u};
   if (v < N) {
     k.pv = par[v];
     k.tv = tok[v];
   }
-  if (threadIdx.x == 0) k.p0 = par[0];
+  if (threadIdx.x == 0) {
+    k.p0 = par[0];
+    k.dirty = fetch_u32(dirty_word(p.counters));
+  }
   return k;
 }
-__device__ bool tree_check_done(const int32_t* par, const int32_t* tok, int N, int V, const TreeCheck& k) {
+__device__ int tree_check_done(const int32_t* par, const int32_t* tok, int N, int V, const TreeCheck& k) {
   const int v = 1 + threadIdx.x;
   bool bad = (v < N && (k.pv < 0 || k.pv >= v || k.tv < 0 || k.tv >= V)) || (threadIdx.x == 0 && k.p0 != -1);
   for (int w = 1 + kBlock + threadIdx.x; w < N; w += kBlock) {
     const int pw = par[w], tw = tok[w];
     bad |= pw < 0 || pw >= w || tw < 0 || tw >= V;
   }
-  return __syncthreads_or(bad) != 0;
+  if (__syncthreads_or(threadIdx.x == 0 && k.dirty != 0u)) return SPEC_REQ_INTERNAL;
+  return __syncthreads_or(bad) ? SPEC_REQ_BADTREE : 0;
 }
 
 // Walk of request b by the last root block.  `gen` counts the orders sent to the helpers.
@@ -426,7 +434,7 @@ __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
   const int32_t* par = p.parents + (size_t)b * N;
   const int32_t* tok = p.node_tokens + (size_t)b * N;
   // the tree's validation: loads now, verdict after the root's sample (before any status)
-  const TreeCheck check = tree_check_issue(par, tok, N);
+  const TreeCheck check = tree_check_issue(p, par, tok, N);
 
   int v = 0, depth = 0;
   while (true) {
@@ -449,7 +457,10 @@ __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
       vmem_wait();      // the clears are complete before any later order reuses the words
     }
     SPEC_STAMP_AT(p, 2, trec, 3);
-    if (v == 0 && tree_check_done(par, tok, N, p.V, check)) { tree_fail(p, b, SPEC_REQ_BADTREE); return; }
+    if (v == 0) {
+      const int code = tree_check_done(par, tok, N, p.V, check);
+      if (code != 0) { tree_fail(p, b, code); return; }
+    }
     if (status != 0) { tree_fail(p, b, status); return; }
     int cand = kNoPick;           // this thread's lowest matching child (c rises)
     for (int c = v + 1 + tid; c < N; c += kBlock)
@@ -599,7 +610,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
   unsigned long long* d = p.desc + (size_t)b * p.desc_words;
   unsigned g1 = 0;   // thread 0: the generation of the current node's first pass order
   // the tree's validation: loads now, verdict once the root's summaries are staged
-  const TreeCheck check = tree_check_issue(par, tok, N);
+  const TreeCheck check = tree_check_issue(p, par, tok, N);
 
   int v = 0, depth = 0, hop = 0;
   while (true) {
@@ -613,7 +624,10 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
     float2* src = v == 0 ? p.part + (size_t)b * P : p.deep + ((size_t)b * 2 + (gen & 1u)) * P;
     stage_summaries(src, s_sum, P, &s_lost);
     SPEC_STAMP_AT(p, 3, trec, 2);
-    if (v == 0 && tree_check_done(par, tok, N, p.V, check)) { tree_fail(p, b, SPEC_REQ_BADTREE); return; }
+    if (v == 0) {
+      const int code = tree_check_done(par, tok, N, p.V, check);
+      if (code != 0) { tree_fail(p, b, code); return; }
+    }
     if (v != 0) {
       for (int c = tid; c < P; c += kBlock) clear_f2(src + c);
       vmem_wait();

@@ -107,8 +107,13 @@ enum {
   SPEC_REQ_BADTREE = 6,         /* parents[0] != -1, a parents[v] outside [0, v), or a
                                    non-root node token outside [0, V) ([M7.7] §0x0F) */
   SPEC_REQ_INTERNAL = 7         /* an internal wait between blocks hit its bound (not
-                                   expected; the request's outputs are not valid, and the
-                                   workspace must be zero-filled again before reuse) */
+                                   expected; the request's outputs are not valid).  A word
+                                   published late may be left in the workspace: a chain
+                                   call zeroes its failed requests' words itself; a greedy
+                                   or tree call marks the workspace dirty (word 0), and
+                                   every later call on a dirty workspace, of any entry
+                                   point, reports SPEC_REQ_INTERNAL for all its requests
+                                   until the caller zero-fills the workspace */
 };
 
 /* How a request's round ended (the finish output of the *_stop entry points). */
