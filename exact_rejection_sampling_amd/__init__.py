@@ -21,10 +21,11 @@ from ._binding import (REQ_STATUS, SpecError, PreparedCall, chain_workspace_byte
                        prepare_tree, prepare_tree_greedy, prepare_tree_residual, spec_verify_chain,
                        spec_verify_greedy, spec_verify_tree, spec_verify_tree_greedy,
                        spec_verify_tree_residual, tree_residual_workspace_bytes, tree_workspace_bytes,
-                       reset_workspaces, LIB_PATH)
+                       reset_workspaces, spec_verify_chain_static, LIB_PATH)
 
 __all__ = ["spec_verify_chain", "spec_verify_greedy", "spec_verify_tree", "spec_verify_tree_greedy",
            "spec_verify_tree_residual", "prepare_tree_residual", "tree_residual_workspace_bytes",
            "load_library", "chain_workspace_bytes", "greedy_workspace_bytes", "tree_workspace_bytes",
            "prepare_chain", "prepare_greedy", "prepare_tree", "prepare_tree_greedy", "PreparedCall",
-           "SpecError", "REQ_STATUS", "LIB_PATH", "reset_workspaces"]
+           "SpecError", "REQ_STATUS", "LIB_PATH", "reset_workspaces",
+           "spec_verify_chain_static"]

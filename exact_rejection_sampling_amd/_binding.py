@@ -37,6 +37,9 @@ _SIGNATURES = {
                                    _c_int, _c_int, _c_int, _c_float,
                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                    _c_void_p, _c_size_t, _c_void_p]),
+    "spec_verify_chain_static": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                          _c_int, _c_int, _c_int, _c_float,
+                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "spec_verify_chain_stop": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, _c_void_p, _c_void_p,
                                         _c_int, _c_int, _c_int, _c_float,
                                         _c_void_p, _c_int, _c_void_p,
@@ -337,6 +340,40 @@ def spec_verify_chain(target_logits: torch.Tensor, draft_probs: torch.Tensor,
                                    with_stats, workspace_tensor, out, stop_tokens, budget, bias, allowed,
                                    top_k, top_p, q_index, lazy_rows)
     _check(fn(*args))
+    return out
+
+
+def spec_verify_chain_static(target_logits: torch.Tensor, draft_probs: torch.Tensor,
+                             draft_tokens: torch.Tensor, uniforms: torch.Tensor, temperature: float,
+                             *, with_stats: bool = False, out: Optional[dict] = None) -> dict:
+    """spec_verify_chain without a workspace (C entry point spec_verify_chain_static): the
+    library's per-GPU static scratch stands in for it, so nothing is allocated when `out`
+    is given.  Same arguments, results and errors as spec_verify_chain's plain form."""
+    lib = load_library()
+    _need(target_logits, "target_logits")
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, gamma+1, V]")
+    B, R, V = target_logits.shape
+    G = R - 1
+    dev = target_logits.device
+    _need(draft_probs, "draft_probs", shape=(B, G, V), device=dev)
+    _need(draft_tokens, "draft_tokens", dtype=torch.int32, shape=(B, G), device=dev)
+    _need(uniforms, "uniforms", dtype=torch.float32, shape=(B, R), device=dev)
+    lt, qt = _dtype_code(target_logits, "target_logits"), _dtype_code(draft_probs, "draft_probs")
+    if out is None:
+        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty(B, R, dtype=torch.int32, device=dev),
+                   req_status=torch.empty(B, dtype=torch.int32, device=dev))
+        if with_stats:
+            out["stats"] = torch.empty(B, R, 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    code = lib.spec_verify_chain_static(_ptr(target_logits), lt, _ptr(draft_probs), qt, _ptr(draft_tokens),
+                                        _ptr(uniforms), B, G, V, ctypes.c_float(float(temperature)),
+                                        _ptr(out["accepted_len"]), _ptr(out["out_tokens"]),
+                                        _ptr(out["req_status"]), _ptr(out.get("stats")),
+                                        ctypes.c_void_p(stream.cuda_stream))
+    if code != 0:
+        _check(code)
     return out
 
 

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 #include "spec_verify.h"
@@ -48,6 +50,37 @@ sv::StopSpec stop_spec(const int32_t* stop_tokens, int n_stop, const int32_t* bu
 }
 }  // namespace
 
+// ------------------------------------------------------------ no-allocation chain call
+// Device scratch of spec_verify_chain_static: a file-scope array that each GPU holds for the
+// life of the process.  In host code its name stands for no device address; the entry
+// point looks the address up once per device (hipGetSymbolAddress, with that device
+// current) and passes only that pointer on.
+constexpr size_t kStaticScratchBytes = SPEC_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch address, looked up on its first use; null on failure.
+void* device_scratch(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// Zero-fill of n 64-bit words (a kernel rather than a memset node, so the call can be
+// captured in a graph).
+__global__ __launch_bounds__(256) void zero_words(unsigned long long* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0ull;
+}
+}  // namespace
+
 extern "C" {
 
 int spec_abi_version(void) { return SPEC_ABI_VERSION; }
@@ -72,6 +105,7 @@ const char* spec_status_string(int code) {
     case SPEC_EDTYPE: return "unknown dtype";
     case SPEC_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case SPEC_EHIP: return "HIP kernel launch failed";
+    case SPEC_ESCRATCH: return "sizes need more device scratch than spec_verify_chain_static holds";
     default: return "unknown status";
   }
 }
@@ -403,6 +437,29 @@ spec_status spec_verify_tree_residual(const void* node_logits, int logit_dtype, 
   const bool vec = (V % 8 == 0) && aligned16(node_logits) && aligned16(draft_probs);
   SPEC_TRACE_FILL(p);
   return sv::launch_tree_residual(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+spec_status spec_verify_chain_static(const void* target_logits, int logit_dtype, const void* draft_probs,
+                                     int q_dtype, const int32_t* draft_tokens, const float* uniforms, int B,
+                                     int gamma, int V, float temperature, int32_t* accepted_len,
+                                     int32_t* out_tokens, int32_t* req_status, float* stats, hipStream_t stream) {
+  const size_t need = spec_chain_workspace_bytes(B, gamma, V);
+  if (need == 0) return SPEC_EINVAL;
+  if (need > kStaticScratchBytes) return SPEC_ESCRATCH;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPEC_EHIP;
+  void* ptr = device_scratch(dev);
+  if (!ptr) return SPEC_EHIP;
+  if (B > 0) {
+    // every call leaves its words zeroed, but a call that failed (or one that raced on the
+    // same GPU) may not have: clear what this call uses
+    const size_t words = need / 8, blocks = (words + 255) / 256;
+    zero_words<<<dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream>>>(
+        static_cast<unsigned long long*>(ptr), words);
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+  }
+  return spec_verify_chain(target_logits, logit_dtype, draft_probs, q_dtype, draft_tokens, uniforms, B, gamma, V,
+                           temperature, accepted_len, out_tokens, req_status, stats, ptr, need, stream);
 }
 
 }  // extern "C"

@@ -88,7 +88,8 @@ typedef enum {
   SPEC_EINVAL = 1,      /* null pointer, size out of range, bad temperature */
   SPEC_EDTYPE = 2,      /* unknown spec_dtype */
   SPEC_EWORKSPACE = 3,  /* workspace missing, too small or not 256-byte aligned */
-  SPEC_EHIP = 4         /* a kernel launch failed (hipGetLastError) */
+  SPEC_EHIP = 4,        /* a kernel launch failed (hipGetLastError) */
+  SPEC_ESCRATCH = 5     /* spec_verify_chain_static: the sizes need more than its scratch */
 } spec_status;
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
@@ -168,6 +169,23 @@ spec_status spec_verify_chain(const void* target_logits, int logit_dtype,
                               int32_t* accepted_len, int32_t* out_tokens, int32_t* req_status,
                               float* stats, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): spec_verify_chain with the same
+ * arguments, results and errors, minus the workspace, which it takes from a device array
+ * of SPEC_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on until the
+ * process ends.  It calls no allocating routine.  Sizes whose spec_chain_workspace_bytes
+ * exceeds SPEC_STATIC_SCRATCH_BYTES return SPEC_ESCRATCH; invalid sizes SPEC_EINVAL.  Each
+ * call first zero-fills the part of the array it uses (a kernel on `stream`), so a failed
+ * call leaves nothing behind.  All calls on one GPU share its array: calls that may overlap
+ * on one GPU (different streams without ordering) race and must not be issued. */
+#define SPEC_STATIC_SCRATCH_BYTES (4u << 20)
+spec_status spec_verify_chain_static(const void* target_logits, int logit_dtype,
+                                     const void* draft_probs, int q_dtype,
+                                     const int32_t* draft_tokens, const float* uniforms,
+                                     int B, int gamma, int V, float temperature,
+                                     int32_t* accepted_len, int32_t* out_tokens,
+                                     int32_t* req_status, float* stats, hipStream_t stream);
 
 /* Chain verification with stop tokens and an output budget ([M7.1] §0x05B "Round
  * Progress Includes Correction Or Bonus": progress is min(A + 1, H), H the distance to

@@ -203,3 +203,17 @@ def test_trace_setter_refuses_outside_trace_builds():
     lib = sv.load_library()
     assert lib.spec_trace_set(FAKE, 16) == EINVAL
     assert lib.spec_trace_set(NULL, 0) == EINVAL
+
+
+def test_static_scratch_entry_rejects_sizes_past_its_scratch():
+    """spec_verify_chain_static checks sizes before it touches a device: sizes whose
+    workspace exceeds SPEC_STATIC_SCRATCH_BYTES get SPEC_ESCRATCH, invalid ones EINVAL."""
+    lib = sv.load_library()
+    ESCRATCH = 5
+    big = lib.spec_chain_workspace_bytes(8192, 5, 128256)
+    assert big > (4 << 20)
+    args = (FAKE, 1, FAKE, 0, FAKE, FAKE)
+    tail = (ctypes.c_float(1.0), FAKE, FAKE, FAKE, NULL, NULL)
+    assert lib.spec_verify_chain_static(*args, 8192, 5, 128256, *tail) == ESCRATCH
+    assert lib.spec_verify_chain_static(*args, 4, 64, 128, *tail) == EINVAL     # gamma above the limit
+    assert lib.spec_status_string(ESCRATCH)
