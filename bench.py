@@ -399,7 +399,7 @@ def bench_sweep(args, torch, sv, synth):
             torch.cuda.empty_cache()
 
 
-TRACE_WORDS = 8          # words per block record of the timeline-trace build
+TRACE_WORDS = 16         # words per record of the timeline-trace build
 TRACE_KERNELS = 4        # kernel slots: 0 chain, 1 chain exact redraw, 2 tree, 3 residual tree
 TICK_US = 0.01           # s_memrealtime runs at 100 MHz
 
@@ -460,6 +460,15 @@ def timeline_chain(args, torch, sv, synth, lib):
         t = (t - base) * TICK_US
         kind, b = c["kind"], c["b"]
         S, L = kind == 0, kind == 3
+        if L.sum() != B:
+            raw = buf.cpu().numpy().view(np.uint64).reshape(TRACE_KERNELS, cap, TRACE_WORDS)
+            if os.environ.get("SPEC_TRACE_DUMP"):
+                np.save(os.environ["SPEC_TRACE_DUMP"], raw)
+            nz = np.nonzero(raw[0][:, 0])[0]
+            raise RuntimeError(f"trace records: {len(kind)} blocks, kinds {np.bincount(kind).tolist()}, "
+                               f"selectors for requests {np.unique(b[L]).tolist()}; tagged records "
+                               f"{nz.min()}..{nz.max()} ({nz.size}); slot-1 records tagged "
+                               f"{np.count_nonzero(raw[1][:, 0])}")
         chain_end = np.nanmax(t)
         stats_done = np.array([np.nanmax(t[S & (b == r), 1]) for r in range(B)])
         sel = {r: t[L & (b == r)][0] for r in range(B)}
@@ -469,6 +478,13 @@ def timeline_chain(args, torch, sv, synth, lib):
                            sel[r][4] - sel[r][3],                 # masses in -> rescan done
                            sel[r][5] - sel[r][4],                 # rescan -> outputs written
                            sel[r][6] - sel[r][5]] for r in range(B)])
+        sub = np.array([[sel[r][7] - sel[r][0],                   # start -> rows combined
+                         sel[r][8] - sel[r][7],                   # -> gather records in
+                         sel[r][9] - sel[r][8],                   # -> decided
+                         sel[r][1] - sel[r][9],                   # -> past the block barrier
+                         sel[r][10] - sel[r][3],                  # masses in -> chunk picked
+                         sel[r][11] - sel[r][10],                 # -> chunk reloaded
+                         sel[r][4] - sel[r][11]] for r in range(B)])   # -> rescan scans done
         sel_end = np.array([sel[r][6] for r in range(B)])
         last = int(np.argmax(sel_end))
         et = e["t"].astype(float)
@@ -479,6 +495,7 @@ def timeline_chain(args, torch, sv, synth, lib):
                          stats_item=_med(t[S, 2] - t[S, 0]), last_req_stats=float(stats_done.max()),
                          sel_start_last=float(sel[last][0]), sel_end_last=float(sel_end[last]),
                          steps_med=np.median(steps, axis=0), steps_last=steps[last],
+                         sub_med=np.nanmedian(sub, axis=0), sub_last=sub[last],
                          after_stats_last=float(sel_end[last] - stats_done[last]),
                          k3_gap=float(k3_start - chain_end), k3_span=float(k3_end - k3_start),
                          k3_exact=int((e["kind"] == 5).sum()), total=float(k3_end)))
@@ -510,6 +527,16 @@ def timeline_chain(args, torch, sv, synth, lib):
     print("| selector step | median over the requests | request that finishes last |")
     print("|---|---|---|")
     for n_, a_, b_ in zip(names, sm, sl):
+        print(f"| {n_} | {a_:.2f} | {b_:.2f} |")
+    print()
+    sub_names = ["dispatch -> summaries in, rows combined", "-> gather records in", "-> decision taken",
+                 "-> past the block barrier", "masses in -> chunk picked", "chunk picked -> chunk reloaded",
+                 "chunk reloaded -> rescan scans done"]
+    sbm = np.median(np.array([r_["sub_med"] for r_ in rows]), axis=0)
+    sbl = np.median(np.array([r_["sub_last"] for r_ in rows]), axis=0)
+    print("| selector sub-step | median over the requests | request that finishes last |")
+    print("|---|---|---|")
+    for n_, a_, b_ in zip(sub_names, sbm, sbl):
         print(f"| {n_} | {a_:.2f} | {b_:.2f} |")
     print()
     print(f"Last-finishing request: {g('after_stats_last'):.2f} us from its statistics' end to its selector's end; "

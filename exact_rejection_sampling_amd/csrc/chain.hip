@@ -326,6 +326,7 @@ __device__ __forceinline__ void chain_decide(const ChainParams& p, int b, RowSta
       rs.bad[i] = !(isfinite(z) && z > 0.0);
     }
   }
+  SPEC_STAMP(p, 0, 8);   // summaries in, rows combined
   if (dl) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
@@ -334,6 +335,7 @@ __device__ __forceinline__ void chain_decide(const ChainParams& p, int b, RowSta
     }
   }
   const bool timeout = wave_any(lost);
+  SPEC_STAMP(p, 0, 9);   // gather records in
   // the row results travel through LDS within this wave: LDS operations of one wave complete
   // in order, and the fence keeps the compiler from moving the reads above the writes
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -414,6 +416,7 @@ __device__ __forceinline__ void chain_decide(const ChainParams& p, int b, RowSta
     s_dec.r_ref = drawn ? rs.r[A] : 0.0f;
     s_dec.inv_z = drawn ? (float)(1.0 / rs.z[A]) : 0.0f;
   }
+  SPEC_STAMP(p, 0, 10);  // decided (before the block barrier)
   __syncthreads();
 }
 
@@ -545,14 +548,42 @@ __device__ __forceinline__ void row_stats(const ChainParams& p, const RowState& 
   }
 }
 
+// Every other terminal item of request b has published its chunk's mass, and so has
+// finished reading the request's summaries and gather records: return them to zero.  xd:
+// the decision of a draw that the exact kernel redoes, whose record then takes the
+// request's first two summary words (R * SL >= 2 whenever there is a residual); the exact
+// kernel clears them.
+__device__ void chain_clear_summaries(const ChainParams& p, int b, const ChainDecision* xd) {
+  const int tid = threadIdx.x;
+  float2* part_b = p.part + (size_t)b * p.R * p.SL;
+  for (int j = tid; j < p.R * p.SL; j += kBlock) {
+    if (xd && j < 2) {
+      const unsigned lo = j == 0 ? static_cast<unsigned>(xd->A + 1) : __float_as_uint(xd->inv_z);
+      const unsigned hi = j == 0 ? __float_as_uint(xd->r_ref) : __float_as_uint(xd->tau);
+      publish_u64(reinterpret_cast<unsigned long long*>(part_b + j), (unsigned long long)hi << 32 | lo);
+    } else {
+      clear_f2(part_b + j);
+    }
+  }
+  for (int j = tid; j < 3 * p.G; j += kBlock) clear_u64(gather_rec(p, b, 0) + j);
+  if (p.thresh_ws)   // written by the threshold pass, read by this request's blocks only
+    for (int j = tid; j < p.R; j += kBlock) store_wt(p.thresh_ws + (size_t)b * p.R + j, 0.0f);
+}
+// ... and the chunk masses, once the selector has read them for the last time.
+__device__ void chain_clear_masses(const ChainParams& p, int b) {
+  for (int j = threadIdx.x; j < p.S2; j += kBlock) clear_mass(p.tmass + (size_t)b * p.S2 + j);
+}
+
 // The selector of request b: every other chunk's mass is awaited; then the chunk where the
 // running mass passes u_gamma * W is rescanned in vocabulary order and the outputs are
 // written.  `own` is the mass of chunk S2 - 1, which the selector computed itself.
 template <int DT, int QT, bool VEC, bool RESID, bool PROC>
-__device__ bool chain_select(const ChainParams& p, int b, const ChainDecision& d, const RowState& rs,
+__device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d, const RowState& rs,
                              double own, const void* lrow, const void* qrow) {
   __shared__ double s_scan[kWavesPerBlock];
+  __shared__ double s_scan2[2 * kWavesPerBlock];
   __shared__ int s_imin[kWavesPerBlock];
+  __shared__ int s_imin2[2 * kWavesPerBlock];
   __shared__ int s_timeout;
   __shared__ double s_before, s_total;
   const int tid = threadIdx.x, G = p.G;
@@ -596,8 +627,13 @@ __device__ bool chain_select(const ChainParams& p, int b, const ChainDecision& d
   const double W = s_total;
   const bool failed = s_timeout || !(isfinite(W) && W > 0.0);   // uniform across the block
   SPEC_STAMP(p, 0, 4);
+  // every other terminal item is done with the request's words: clear them now, so that the
+  // clears complete under the rescan
+  const bool exact = RESID && !failed && W < kExactBelow;
+  chain_clear_summaries(p, b, exact ? &d : nullptr);
   double t = 0.0;
   int k = -1;
+  if (failed) chain_clear_masses(p, b);
   if (!failed) {
     t = (double)ut * W;
     int cand = 0x7fffffff;          // first chunk of this thread's run whose running value passes t
@@ -621,38 +657,47 @@ __device__ bool chain_select(const ChainParams& p, int b, const ChainDecision& d
     }
     __syncthreads();
     const double rem = t - s_before;   // target mass inside chunk cstar
+    chain_clear_masses(p, b);          // every thread has read its masses for the last time
+    SPEC_STAMP(p, 0, 11);   // chunk picked
 
     // 2. rescan cstar in vocabulary order: slab 0 then slab 1, each thread's 8 elements
     //    in order within a slab
     float w[kTermSlabs][8];
     bool bad = false;
     term_chunk<DT, QT, VEC, RESID, PROC>(p, lrow, qrow, cstar, d, (size_t)b * p.R + d.A, w, bad);
-    double before_slab = 0.0;
+    SPEC_STAMP(p, 0, 12);   // chunk reloaded, weights formed
+    static_assert(kTermSlabs == 2, "the rescan scans two slabs in one pass");
+    double incl[kTermSlabs][8], acc[kTermSlabs];
     int last_pos = -1, pick = 0x7fffffff;
 #pragma unroll
     for (int s = 0; s < kTermSlabs; ++s) {
       const long e0 = ((long)cstar * kTermSlabs + s) * kSlab + (long)tid * kVec;
-      double incl[8];
-      double acc = 0.0;
+      acc[s] = 0.0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        acc += (double)w[s][j];
-        incl[j] = acc;
+        acc[s] += (double)w[s][j];
+        incl[s][j] = acc[s];
         if (w[s][j] > 0.0f) last_pos = (int)(e0 + j);
       }
-      double slab_total;
-      const double off = before_slab + block_excl_scan_d(acc, s_scan, &slab_total);
+    }
+    // slab 0 then slab 1 in vocabulary order: one pass for both slabs' block prefixes
+    double off[kTermSlabs], slab_total[kTermSlabs];
+    block_excl_scan_d2(acc[0], acc[1], s_scan2, &off[0], &off[1], &slab_total[0], &slab_total[1]);
+    off[1] += 0.0 + slab_total[0];
+#pragma unroll
+    for (int s = 0; s < kTermSlabs; ++s) {
+      const long e0 = ((long)cstar * kTermSlabs + s) * kSlab + (long)tid * kVec;
       int cand = 0x7fffffff;
 #pragma unroll
       for (int j = 7; j >= 0; --j)
-        if (off + incl[j] > rem && w[s][j] > 0.0f) cand = (int)(e0 + j);
+        if (off[s] + incl[s][j] > rem && w[s][j] > 0.0f) cand = (int)(e0 + j);
       pick = min(pick, cand);
-      before_slab += slab_total;
     }
     // the first position whose running value passes the target; rounding may leave the
     // target just past the chunk's last positive weight: then take that weight
-    pick = block_min_i(pick, s_imin);
-    k = pick != 0x7fffffff ? pick : -block_min_i(-last_pos, s_imin);
+    int last_any;
+    pick = block_min_max_i(pick, last_pos, s_imin2, &last_any);
+    k = pick != 0x7fffffff ? pick : last_any;
   }
   SPEC_STAMP(p, 0, 5);
 
@@ -690,7 +735,6 @@ __device__ bool chain_select(const ChainParams& p, int b, const ChainDecision& d
     if (p.st.finish) p.st.finish[b] = finish;
   }
   SPEC_STAMP(p, 0, 6);
-  return RESID && status == 0 && W < kExactBelow;
 }
 
 // A request with no terminal draw -- a failed request, or a round that ended on an
@@ -726,28 +770,6 @@ __device__ void chain_nodraw(const ChainParams& p, int b, const ChainDecision& d
   }
 }
 
-// Every other terminal item of request b has published its chunk's mass, and so has
-// finished reading the request's summaries and gather records: return them all to zero.
-__device__ void chain_clear(const ChainParams& p, int b, const ChainDecision* xd = nullptr) {
-  const int tid = threadIdx.x;
-  float2* part_b = p.part + (size_t)b * p.R * p.SL;
-  for (int j = tid; j < p.R * p.SL; j += kBlock) {
-    if (xd && j < 2) {
-      // the exact-draw record takes the request's first two summary words (R * SL >= 2
-      // whenever there is a residual); the exact kernel clears them
-      const unsigned lo = j == 0 ? static_cast<unsigned>(xd->A + 1) : __float_as_uint(xd->inv_z);
-      const unsigned hi = j == 0 ? __float_as_uint(xd->r_ref) : __float_as_uint(xd->tau);
-      publish_u64(reinterpret_cast<unsigned long long*>(part_b + j), (unsigned long long)hi << 32 | lo);
-    } else {
-      clear_f2(part_b + j);
-    }
-  }
-  for (int j = tid; j < 3 * p.G; j += kBlock) clear_u64(gather_rec(p, b, 0) + j);
-  for (int j = tid; j < p.S2; j += kBlock) clear_mass(p.tmass + (size_t)b * p.S2 + j);
-  if (p.thresh_ws)   // written by the threshold pass, read by this request's blocks only
-    for (int j = tid; j < p.R; j += kBlock) store_wt(p.thresh_ws + (size_t)b * p.R + j, 0.0f);
-}
-
 // Terminal item with a valid decision: chunk c of request b's terminal row; the last
 // chunk's item selects.
 template <int DT, int QT, bool VEC, bool RESID, bool PROC>
@@ -764,9 +786,7 @@ __device__ void terminal_body(const ChainParams& p, int b, int c, const ChainDec
     if (threadIdx.x == 0) publish_mass(p.tmass + (size_t)b * p.S2 + c, m);
     return;
   }
-  const bool exact = chain_select<DT, QT, VEC, RESID, PROC>(p, b, d, rs, m, lrow, qrow);
-  __syncthreads();
-  chain_clear(p, b, exact ? &d : nullptr);
+  chain_select<DT, QT, VEC, RESID, PROC>(p, b, d, rs, m, lrow, qrow);
   SPEC_STAMP(p, 0, 7);
 }
 
@@ -783,7 +803,8 @@ __device__ void terminal_item(const ChainParams& p, int b, int c, RowState& s_rs
     }
     chain_nodraw(p, b, d, s_rs);
     __syncthreads();
-    chain_clear(p, b);
+    chain_clear_summaries(p, b, nullptr);
+    chain_clear_masses(p, b);
     return;
   }
   if (d.A < p.G) terminal_body<DT, QT, VEC, true, PROC>(p, b, c, d, s_rs);

@@ -291,6 +291,56 @@ __device__ __forceinline__ double block_excl_scan_d(double v, double* scratch, d
   return off + excl;
 }
 
+// Two independent block-wide exclusive prefixes in one pass (the same sums, in the same
+// order, as two calls of block_excl_scan_d); `scratch` holds >= 2 * kWavesPerBlock doubles.
+__device__ __forceinline__ void block_excl_scan_d2(double a, double b, double* scratch, double* excl_a,
+                                                   double* excl_b, double* total_a, double* total_b) {
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const double ia = wave_incl_scan_d(a, lane), ib = wave_incl_scan_d(b, lane);
+  const double ea = wave_shr1_d(ia), eb = wave_shr1_d(ib);
+  if (lane == kWave - 1) {
+    scratch[wave] = ia;
+    scratch[kWavesPerBlock + wave] = ib;
+  }
+  __syncthreads();
+  double oa = 0.0, ta = 0.0, ob = 0.0, tb = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) {
+    if (w < wave) {
+      oa += scratch[w];
+      ob += scratch[kWavesPerBlock + w];
+    }
+    ta += scratch[w];
+    tb += scratch[kWavesPerBlock + w];
+  }
+  __syncthreads();
+  *excl_a = oa + ea;
+  *excl_b = ob + eb;
+  *total_a = ta;
+  *total_b = tb;
+}
+
+// Block-wide minimum of `mn` and maximum of `mx` in one pass; `scratch` holds >= 2 *
+// kWavesPerBlock ints.
+__device__ __forceinline__ int block_min_max_i(int mn, int mx, int* scratch, int* max_out) {
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const int wmn = wave_min_i(mn), wmx = -wave_min_i(-mx);
+  if (lane == 0) {
+    scratch[wave] = wmn;
+    scratch[kWavesPerBlock + wave] = wmx;
+  }
+  __syncthreads();
+  int r = scratch[0], q = scratch[kWavesPerBlock];
+#pragma unroll
+  for (int k = 1; k < kWavesPerBlock; ++k) {
+    r = min(r, scratch[k]);
+    q = max(q, scratch[kWavesPerBlock + k]);
+  }
+  __syncthreads();
+  *max_out = q;
+  return r;
+}
+
 // ------------------------------------------------------------------ softmax pieces
 // Raw lane-vector storage for one wave chunk: 4 lane vectors of 8 elements.
 template <int DT> struct ChunkRegs;

@@ -10,22 +10,23 @@ namespace sv {
 
 // ------------------------------------------------------------ timeline trace
 // In a library built with -DSPEC_TRACE (exact_rejection_sampling_amd.build --trace), thread
-// 0 of every block of a traced kernel writes a tag and up to 7 stamps of the 100 MHz
+// 0 of every block of a traced kernel writes a tag and up to 15 stamps of the 100 MHz
 // real-time counter (s_memrealtime) into the buffer that spec_trace_set installs: the
-// record of block x of kernel slot k is words [(k * cap + x) * 8, + 8), and blocks at or
+// record of block x of kernel slot k is words [(k * cap + x) * 16, + 16), and blocks at or
 // past `cap` write nothing.  Other builds compile every mark to nothing and carry no trace
 // member in their kernel arguments.
 #ifdef SPEC_TRACE
 struct TraceSink {
-  unsigned long long* buf;   // [kTraceKernels * cap * 8] words, or null (tracing off)
+  unsigned long long* buf;   // [kTraceKernels * cap * kTraceWords] words, or null (tracing off)
   unsigned long long cap;    // records per kernel slot
 };
 constexpr int kTraceKernels = 4;   // slots: 0 chain, 1 chain exact redraw, 2 tree, 3 tree residual
+constexpr int kTraceWords = 16;    // words per record: the tag, then stamps
 extern TraceSink g_trace_sink;     // host copy, set by spec_trace_set
 #define SPEC_TRACE_MEMBER TraceSink trace{};
 __device__ __forceinline__ void trace_word(const TraceSink& t, int k, unsigned long long rec, int slot,
                                            unsigned long long v) {
-  if (threadIdx.x == 0 && t.buf && rec < t.cap) t.buf[((unsigned long long)k * t.cap + rec) * 8 + slot] = v;
+  if (threadIdx.x == 0 && t.buf && rec < t.cap) t.buf[((unsigned long long)k * t.cap + rec) * kTraceWords + slot] = v;
 }
 #define SPEC_STAMP(P, K, SLOT) ::sv::trace_word((P).trace, (K), blockIdx.x, (SLOT), __builtin_amdgcn_s_memrealtime())
 #define SPEC_TAG(P, K, TAG) ::sv::trace_word((P).trace, (K), blockIdx.x, 0, (TAG))
