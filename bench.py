@@ -400,7 +400,7 @@ def bench_sweep(args, torch, sv, synth):
 
 
 TRACE_WORDS = 16         # words per record of the timeline-trace build
-TRACE_KERNELS = 4        # kernel slots: 0 chain, 1 chain exact redraw, 2 tree, 3 residual tree
+TRACE_KERNELS = 5        # kernel slots: 0 chain, 1 exact redraw, 2 tree, 3 residual tree, 4 thresholds
 TICK_US = 0.01           # s_memrealtime runs at 100 MHz
 
 
@@ -560,6 +560,7 @@ def _traced_calls(args, torch, lib, calls, cap, slot):
         calls[rep % len(calls)]()
         torch.cuda.synchronize()
         r = _trace_records(buf, cap)[slot]
+        r["raw"] = r["t"].copy()
         t = r["t"].astype(float)
         t[t == 0] = np.nan
         base = np.nanmin(t[:, 0])
@@ -686,6 +687,64 @@ def timeline_tree_residual(args, torch, sv, synth, lib):
     print(f"| terminal draw (after Z or the last W) -> token | {len(draws) // nc} | {_med(draws):.2f} |")
 
 
+def timeline_thresh(args, torch, sv, synth, lib):
+    """Per-row timeline of the top-k / top-p threshold pass on the processors workload (B=64,
+    gamma=5, V=128256 bf16 with bias, masks, top-k in {0, 1, 20, 1000} and top-p in {1, 0.5,
+    0.9, 0.99}): each row's phases and the slowest rows."""
+    x = synth.make_config(3, 0)
+    bias, words, k, p = synth.make_processors(x.B, x.gamma + 1, x.V, seed=11)
+    dev = "cuda:0"
+    lt = torch.from_numpy(x.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    qt = torch.from_numpy(x.q).to(dev)
+    tt, ut = torch.from_numpy(x.tokens).to(dev), torch.from_numpy(x.u).to(dev)
+    bt, wt = torch.from_numpy(bias).to(dev), torch.from_numpy(words.view(np.int32)).to(dev)
+    kt, pt = torch.from_numpy(k).to(dev), torch.from_numpy(p).to(dev)
+    sets = device_copies(lambda: (lt.clone(), qt.clone()), lt.numel() * 2 + qt.numel() * 4)
+    del lt, qt
+    ws = torch.zeros(sv.chain_workspace_bytes(x.B, x.gamma, x.V) + 512, dtype=torch.uint8, device=dev)
+    calls = [sv.prepare_chain(s_[0], s_[1], tt, ut, float(x.temperature), workspace_tensor=ws, bias=bt, allowed=wt,
+                              top_k=kt, top_p=pt) for s_ in sets]
+    off, on, recs = _traced_calls(args, torch, lib, calls, 8192, 4)
+    rows = []
+    for r in recs:
+        t, kind, kk = r["t"], r["kind"], r["idx"]
+        raw = r["raw"].astype(np.uint64)
+        for i in range(len(kind)):
+            tp = float(np.array([raw[i, 8] & np.uint64(0xffffffff)], dtype=np.uint64).astype(np.uint32).view(np.float32)[0])
+            n1 = int(raw[i, 9] & np.uint64(0xffffffff))
+            rows.append(dict(kind=int(kind[i]), k=int(kk[i]), p=tp, n=n1, radix=int(raw[i, 10]),
+                             dur=t[i, 6] - t[i, 0], p0=t[i, 1] - t[i, 0],
+                             p1=t[i, 2] - t[i, 1], col=t[i, 3] - t[i, 2], res=t[i, 4] - t[i, 3],
+                             topp=t[i, 5] - t[i, 4], rest=t[i, 6] - t[i, 5], start=t[i, 0], end=t[i, 6]))
+    print(f"## thresh_kernel timeline: B={x.B} rows of gamma+1={x.gamma + 1}, V={x.V} bf16, bias, masks, top-k, top-p")
+    print()
+    print(f"Trace build, {args.timeline_calls} traced calls; per row (block) times in us. Calls of the trace build: "
+          f"{off:.1f} us with tracing off, {on:.1f} us on (the whole processed chain call).")
+    print()
+    print("| rows (top-k, top-p) | count per call | median duration | max duration | pass 0 | pass 1 (bins) | "
+          "collect | resolve top-k | top-p | radix / end |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    nc = max(1, args.timeline_calls)
+    for kval in sorted(set(r_["k"] for r_ in rows if r_["kind"] != 0)):
+        for pval in sorted(set(r_["p"] for r_ in rows if r_["kind"] != 0 and r_["k"] == kval)):
+            sel = [r_ for r_ in rows if r_["kind"] != 0 and r_["k"] == kval and r_["p"] == pval]
+            if not sel:
+                continue
+            f = lambda key: _med([r_[key] for r_ in sel])
+            nrad = sum(r_["radix"] for r_ in sel)
+            print(f"| k={kval}, p={pval:g} | {len(sel) // nc} | {f('dur'):.2f} | {max(r_['dur'] for r_ in sel):.2f} | "
+                  f"{f('p0'):.2f} | {f('p1'):.2f} | {f('col'):.2f} | {f('res'):.2f} | {f('topp'):.2f} | "
+                  f"{f('rest'):.2f}{' (radix in %d)' % nrad if nrad else ''} |")
+    slow = sorted(rows, key=lambda r_: -r_["dur"] if np.isfinite(r_["dur"]) else 0)[:8]
+    print()
+    print("Slowest rows: " + "; ".join(f"k={r_['k']} p={r_['p']:g} {r_['dur']:.1f} us (collected {r_['n']}"
+                                      f"{', radix' if r_['radix'] else ''})" for r_ in slow))
+    ends = [r_["end"] for r_ in rows if np.isfinite(r_["end"])]
+    print()
+    print(f"Last row ends at {np.percentile(ends, 100):.2f} us (p90 {np.percentile(ends, 90):.2f}, "
+          f"median {np.median(ends):.2f}) after the first row's start.")
+
+
 class _CachedSynth:
     """The synth module with make_config memoized, so that the lines that share a workload
     generate its inputs once (they only read them)."""
@@ -723,8 +782,9 @@ def _oracle_worker(args):
 
 def cpu_baseline(x, budget_s):
     """The float64 oracle, as it stands, on requests of the headline workload: one process on
-    one core, then a pool of forked processes over requests on up to 16 host cores, each for
-    about budget_s.  Runs before anything touches the GPU, so the fork is of a plain CPU
+    one core, then a pool of forked processes over requests, one per core this process may
+    run on up to 16 (a one-GPU machine's CPU share), each for about budget_s; nproc and the
+    affinity count are reported beside the pool size.  Runs before anything touches the GPU, so the fork is of a plain CPU
     process."""
     import multiprocessing as mp
     global _CPU_X
@@ -737,6 +797,7 @@ def cpu_baseline(x, budget_s):
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
         avail = os.cpu_count() or 1
+    # one worker per core this process may run on, up to 16: a one-GPU machine's CPU share
     workers = max(1, min(16, avail))
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(workers) as pool:
@@ -744,6 +805,7 @@ def cpu_baseline(x, budget_s):
     elp = time.perf_counter() - t0
     n = sum(counts)
     return dict(value=n * (G + 1) / elp, unit="verified positions/s", cores=workers, kind="oracle",
+                nproc=os.cpu_count(), affinity_cores=avail,
                 sample=f"{n} requests of the chain B=64 gamma=5 V=128256 bf16 workload (its 64 requests "
                        f"cycled), float64 NumPy oracle, {workers} forked processes for {elp:.1f} s "
                        f"wall including pool start-up",
@@ -764,7 +826,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true",
                     help="print the chain bandwidth sweep over batch sizes (one JSON line per point) instead")
-    ap.add_argument("--timeline", choices=["chain", "tree", "tree_residual"],
+    ap.add_argument("--timeline", choices=["chain", "tree", "tree_residual", "thresh"],
                     help="print a per-block timeline summary (markdown) of one workload instead, from the "
                          "trace build (python -m exact_rejection_sampling_amd.build --trace)")
     ap.add_argument("--timeline-calls", type=int, default=5)
@@ -787,7 +849,8 @@ def main():
     if args.timeline:
         from exact_rejection_sampling_amd import build as _build
         lib = sv.load_library(_build.TRACE_LIB, install=True)
-        fn = dict(chain=timeline_chain, tree=timeline_tree, tree_residual=timeline_tree_residual)[args.timeline]
+        fn = dict(chain=timeline_chain, tree=timeline_tree, tree_residual=timeline_tree_residual,
+                  thresh=timeline_thresh)[args.timeline]
         fn(args, torch, sv, synth, lib)
         return
     sv.load_library()

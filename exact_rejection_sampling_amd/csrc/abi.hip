@@ -248,6 +248,7 @@ spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, con
     t.V = V;
     t.W = p.pr.W;
     t.c2 = p.c2;
+    SPEC_TRACE_FILL(t);
     if (sv::launch_thresholds(t, logit_dtype, vec, stream) != hipSuccess) return SPEC_EHIP;
   }
   SPEC_TRACE_FILL(p);

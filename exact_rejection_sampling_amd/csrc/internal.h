@@ -20,7 +20,8 @@ struct TraceSink {
   unsigned long long* buf;   // [kTraceKernels * cap * kTraceWords] words, or null (tracing off)
   unsigned long long cap;    // records per kernel slot
 };
-constexpr int kTraceKernels = 4;   // slots: 0 chain, 1 chain exact redraw, 2 tree, 3 tree residual
+constexpr int kTraceKernels = 5;   // slots: 0 chain, 1 chain exact redraw, 2 tree, 3 tree residual,
+                                   // 4 top-k / top-p thresholds
 constexpr int kTraceWords = 16;    // words per record: the tag, then stamps
 extern TraceSink g_trace_sink;     // host copy, set by spec_trace_set
 #define SPEC_TRACE_MEMBER TraceSink trace{};
@@ -35,6 +36,7 @@ __device__ __forceinline__ void trace_word(const TraceSink& t, int k, unsigned l
   ::sv::trace_word((P).trace, (K), (REC), (SLOT), __builtin_amdgcn_s_memrealtime())
 #define SPEC_TAG_AT(P, K, REC, TAG) ::sv::trace_word((P).trace, (K), (REC), 0, (TAG))
 #define SPEC_TRACE_FILL(P) ((P).trace = ::sv::g_trace_sink)
+#define SPEC_TRACE_ONLY(X) X
 #else
 #define SPEC_TRACE_MEMBER
 #define SPEC_STAMP(P, K, SLOT) ((void)0)
@@ -42,6 +44,7 @@ __device__ __forceinline__ void trace_word(const TraceSink& t, int k, unsigned l
 #define SPEC_STAMP_AT(P, K, REC, SLOT) ((void)0)
 #define SPEC_TAG_AT(P, K, REC, TAG) ((void)0)
 #define SPEC_TRACE_FILL(P) ((void)0)
+#define SPEC_TRACE_ONLY(X) ((void)0)
 #endif
 // A record's tag: bit 63 set, the item kind in bits 56..62, the request in bits 24..55
 // and the item's index within the request in bits 0..23.
@@ -278,6 +281,7 @@ struct ThreshParams {
   float* thresh;             // [rows] out: -inf when nothing is truncated
   int rows, R, V, W;
   float c2;                  // fp32(log2(e) / T)
+  SPEC_TRACE_MEMBER
 };
 hipError_t launch_thresholds(const ThreshParams& p, int logit_dtype, bool vec, hipStream_t s);
 

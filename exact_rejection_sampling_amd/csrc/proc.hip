@@ -7,17 +7,21 @@
 //  * top-p (0 < p < 1): among the candidates with key >= tau_k, with weights
 //    w = 2^((s - max) * c2), tau_p = the largest key t whose mass {key >= t} reaches
 //    p * (total mass): the smallest tie-closed set of top tokens whose probability reaches p.
-// Counts are integers and masses are fixed-point integers (each weight scaled by the
-// largest power of two that keeps every sum below 2^53, rounded to nearest), so every sum is
-// exact and the result does not depend on the order of the additions.  Usual path, three
-// or four passes over the row: (0) the candidates' max, min and count; (1) counts and
-// masses in 4096 LDS bins linear in s over [min, max]; then for each selection the bin
-// where the count or mass from the top reaches its target, (2) a pass that collects that
-// bin's candidates into LDS, and an exact resolution among them.  With both selections on,
-// one collecting pass serves both whenever the top-p bin is fixed before tau_k is.  A bin with more than
-// 1024 candidates (values piled on a few points) falls back to radix selection over the
-// bits in which the candidate keys differ, 12 bits per pass.  The row's threshold is tau_p
-// when top-p is on (it is at least tau_k), else tau_k, or -inf.
+// Counts are integers; masses are fp64 sums of fp32 weights 2^((s - ref) c2) (ref a value of
+// the row, which cancels in every ratio), whose rounding (about 1e-16 relative per add) is
+// far inside the 1e-5 window in which the oracle flags a top-p decision.  Usual path, two
+// or three passes over the row: a sample of the row (one batch per thread, spread over it)
+// fixes the range of 4096 LDS bins linear in s; (1) one pass adds every candidate's count
+// and weight to its bin (values outside the range go to the end bins) and finds the row's
+// max, min and count; then for each selection the bin where the count or mass from the top
+// reaches its target, (2) a pass that collects that bin's candidates into LDS, and an exact
+// resolution among them.  With both selections on, one collecting pass serves both
+// whenever the top-p bin is fixed before tau_k is.  Top-1 keeps the maximum's ties whatever
+// top-p is.  A bin with more than 1024 candidates (values piled on a few points) falls back
+// to radix selection over the bits in which the candidate keys differ, 12 bits per pass,
+// with fixed-point masses (each weight scaled by the largest power of two that keeps every
+// sum below 2^53).  The row's threshold is tau_p when top-p is on (it is at least tau_k),
+// else tau_k, or -inf.
 //
 // Method: [M7.1] "M7.1 - Speculative Decoding: Draft, Verify, Accept, Reject" §0x06J (the
 // verified p is the row after top-k and top-p); [Tiny] "Exact Speculative and Assisted
@@ -45,7 +49,10 @@ __device__ __forceinline__ float value_of(unsigned k) {
 // step instead of one per vector.  (Deeper batches fit the 128 registers per thread but
 // measured slower: the pass is bound by its per-element arithmetic and LDS atomics as much
 // as by memory latency.)
-constexpr int kU = 2;
+#ifndef SPEC_THRESH_U
+#define SPEC_THRESH_U 2
+#endif
+constexpr int kU = SPEC_THRESH_U;
 
 // The candidates of this thread's kU vectors at e0, e0 + stride, ...: processed values
 // (bias and mask applied, no threshold) and validity bits.
@@ -263,7 +270,7 @@ constexpr int kCap = kTB >= 1024 ? 2048 : 1024;
 
 struct BinLds {
   unsigned cnt[kBins];
-  unsigned long long mass[kBins];
+  double mass[kBins];                   // fp64 sums of fp32 weights relative to the bins' reference
 };
 union SelectLds {
   BinLds bins;
@@ -271,16 +278,24 @@ union SelectLds {
 };
 struct Collected {
   float v[kCap];
-  unsigned long long w[kCap];
+  double w[kCap];                       // the weights, relative to the bins' reference (or 1)
   int n;
 };
 
+// Bins linear in the value over [lo, lo + kBins / scale]; values outside fall into the end
+// bins, so bin(s) stays monotone in s and ties share a bin.
 struct ValueBins {
   float lo, scale;
   __device__ __forceinline__ int of(float s) const {
-    return static_cast<int>(fminf((s - lo) * scale, static_cast<float>(kBins - 1)));
+    return static_cast<int>(fminf(fmaxf((s - lo) * scale, 0.0f), static_cast<float>(kBins - 1)));
   }
 };
+
+// A candidate's top-p weight relative to the reference value ref: 2^((s - ref) c2) in fp32,
+// accumulated in fp64.  The reference cancels in every mass ratio.
+__device__ __forceinline__ double rel_weight(float s, float ref, float c2) {
+  return (double)__builtin_amdgcn_exp2f((s - ref) * c2);
+}
 
 // Block-wide fp64 sum (every thread receives it).
 __device__ __forceinline__ double block_sum_d(double v, double* scratch) {
@@ -323,8 +338,8 @@ __device__ __forceinline__ int find_bin(Val val, double above, double target, do
 // Collects the candidates of bin d with their weights (fixed-point masses when fe >= 0);
 // returns the number found (which may exceed kCap: then only kCap are stored).
 template <int DT, bool VEC>
-__device__ __forceinline__ int collect(const ThreshParams& p, const void* lrow, size_t row, const ValueBins& vb, int d, float M,
-                       int fe, Collected& L) {
+__device__ __forceinline__ int collect(const ThreshParams& p, const void* lrow, size_t row, const ValueBins& vb, int d, float ref,
+                       bool weights, Collected& L) {
   if (threadIdx.x == 0) L.n = 0;
   __syncthreads();
   for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kTB * kVec * kU) {
@@ -336,11 +351,11 @@ __device__ __forceinline__ int collect(const ThreshParams& p, const void* lrow, 
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (!((ok[u] >> e) & 1u)) continue;
-        if (vb.of(s[u][e]) != d) continue;
+        if (s[u][e] < vb.lo || vb.of(s[u][e]) != d) continue;   // below the bins: in none
         const int i = atomicAdd(&L.n, 1);
         if (i < kCap) {
           L.v[i] = s[u][e];
-          L.w[i] = fe >= 0 ? fixed_weight(s[u][e], M, p.c2, fe) : 1ull;
+          L.w[i] = weights ? rel_weight(s[u][e], ref, p.c2) : 1.0;
         }
       }
   }
@@ -354,7 +369,7 @@ __device__ __forceinline__ int collect(const ThreshParams& p, const void* lrow, 
 // count of d1 and leaves d2's in *n2.
 template <int DT, bool VEC>
 __device__ __forceinline__ int collect2(const ThreshParams& p, const void* lrow, size_t row, const ValueBins& vb, int d1, int d2,
-                        float M, int fe, Collected& L1, Collected& L2, int* n2) {
+                        float ref, Collected& L1, Collected& L2, int* n2) {
   if (threadIdx.x == 0) {
     L1.n = 0;
     L2.n = 0;
@@ -368,14 +383,14 @@ __device__ __forceinline__ int collect2(const ThreshParams& p, const void* lrow,
     for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if (!((ok[u] >> e) & 1u)) continue;
+        if (!((ok[u] >> e) & 1u) || s[u][e] < vb.lo) continue;
         const int d = vb.of(s[u][e]);
         if (d != d1 && d != d2) continue;
         Collected& L = d == d1 ? L1 : L2;
         const int i = atomicAdd(&L.n, 1);
         if (i < kCap) {
           L.v[i] = s[u][e];
-          L.w[i] = fixed_weight(s[u][e], M, p.c2, fe);
+          L.w[i] = rel_weight(s[u][e], ref, p.c2);
         }
       }
   }
@@ -397,7 +412,7 @@ __device__ __forceinline__ float resolve(const Collected& L, int n, float floor_
     if (t < floor_v) continue;
     double f = above;
     for (int j = 0; j < n; ++j)
-      if (L.v[j] >= t) f += mass ? (double)L.w[j] : 1.0;
+      if (L.v[j] >= t) f += mass ? L.w[j] : 1.0;
     if (f >= target) best = fmaxf(best, t);
   }
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
@@ -420,11 +435,14 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
   __shared__ int s_fault, s_d;
   __shared__ double s_f;
   const size_t row = blockIdx.x;
+  SPEC_STAMP(p, 4, 1);
   const int b = static_cast<int>(row / p.R);
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   const int k = p.top_k ? p.top_k[b] : 0;
   const float tp = p.top_p ? p.top_p[b] : 1.0f;
   const bool use_k = k >= 1, use_p = tp > 0.0f && tp < 1.0f;   // false for NaN
+  SPEC_TAG(p, 4, SPEC_TRACE_TAG((use_k ? 1 : 0) | (use_p ? 2 : 0), row, k));
+  SPEC_TRACE_ONLY(trace_word(p.trace, 4, blockIdx.x, 9, __float_as_uint(tp)));
   if (!use_k && !use_p) {
     if (threadIdx.x == 0) p.thresh[row] = -INFINITY;
     return;
@@ -432,12 +450,73 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
   const void* lrow = row_ptr<DT>(p.logits, row, p.V);
   if (threadIdx.x == 0) s_fault = 0;
   __syncthreads();
-  // pass 0: the candidates' maximum, minimum and count; NaN / +inf anywhere makes the row
-  // invalid for the verifier, and then no threshold is needed
+  // The bins' range comes from a sample: one batch per thread, the threads' batches spread
+  // over the row.  The pass that follows counts and weighs every candidate into bins over
+  // that range (values outside it fall into the end bins) and finds the row's true maximum,
+  // minimum and count, and any NaN / +inf (which makes the row invalid for the verifier,
+  // and then no threshold is needed) on the way.
+  const long step = (long)kTB * kVec * kU;
+  const long iters = (p.V + step - 1) / step;
+  {
+    float sm = -INFINITY, smn = INFINITY;
+    const long e0 = (long)threadIdx.x * kVec + (long)(threadIdx.x % iters) * step;
+    if (e0 < p.V) {
+      float s[kU][8];
+      unsigned ok[kU];
+      cand_batch<DT, VEC>(p, lrow, row, e0, (long)kTB * kVec, s, ok);
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool c = (ok[u] >> e) & 1u;
+          sm = fmaxf(sm, c ? s[u][e] : -INFINITY);
+          smn = fminf(smn, c ? s[u][e] : INFINITY);
+        }
+    }
+    const float wm = wave_max(sm), wmn = -wave_max(-smn);
+    if (lane == 0) {
+      s_m[wave] = wm;
+      s_mn[wave] = wmn;
+    }
+  }
+  __syncthreads();
+  float SM = -INFINITY, SMN = INFINITY;
+#pragma unroll
+  for (int w = 0; w < kTW; ++w) {
+    SM = fmaxf(SM, s_m[w]);
+    SMN = fminf(SMN, s_mn[w]);
+  }
+  __syncthreads();
+  // Only values near the top can hold a threshold: the bins cover [lo, SM] with lo the
+  // sample's minimum or, if higher, the cut SM - cut / c2, below which a weight is under
+  // 2^-cut.  Top-p keeps a set whose mass reaches p of the total, and the candidates below
+  // the cut weigh less than V 2^-cut <= (1 - p) / 8 of a total of at least 1 (the sample's
+  // maximum weighs 1), so its threshold lies above the cut; the k-th largest for top-k lies
+  // there whenever at least k candidates do.  Candidates below lo go to two running sums
+  // (count and weight) instead of the bins; a row whose threshold falls below lo after all
+  // takes the radix selection.
+  const float q1 = use_p ? 1.0f - tp : 1.0f;
+  const float cut = fmaxf(24.0f, ceilf(log2f(8.0f * static_cast<float>(p.V) / q1)));
+  ValueBins vb;
+  vb.lo = fmaxf(SMN, SM - cut / p.c2);
+  vb.scale = static_cast<float>(kBins) / (SM - vb.lo);
+  // (top-1 keeps the maximum's ties whatever top-p is: no bins needed)
+  const bool binned = !(use_k && k == 1) && SM > vb.lo && isfinite(SM - vb.lo) && isfinite(vb.scale) &&
+                      vb.scale > 0.0f;
+  const float ref = SM;                 // the weights' reference value
+  BinLds& L = s_sel.bins;
+  if (binned) {
+    for (int j = threadIdx.x; j < kBins; j += kTB) {
+      L.cnt[j] = 0u;
+      L.mass[j] = 0.0;
+    }
+  }
+  __syncthreads();
   float m = -INFINITY, mn = INFINITY;
   unsigned cnt = 0u;
+  double low_mass = 0.0;
   bool fault = false;
-  for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kTB * kVec * kU) {
+  for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += step) {
     float s[kU][8];
     unsigned ok[kU];
     cand_batch<DT, VEC>(p, lrow, row, e0, (long)kTB * kVec, s, ok);
@@ -449,6 +528,15 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
         const bool c = (ok[u] >> e) & 1u;
         m = fmaxf(m, c ? s[u][e] : -INFINITY);
         mn = fminf(mn, c ? s[u][e] : INFINITY);
+        if (binned && c) {
+          if (s[u][e] >= vb.lo) {
+            const int d = vb.of(s[u][e]);
+            if (use_k) atomicAdd(&L.cnt[d], 1u);
+            if (use_p) atomicAdd(&L.mass[d], rel_weight(s[u][e], ref, p.c2));
+          } else {
+            if (use_p) low_mass += rel_weight(s[u][e], ref, p.c2);
+          }
+        }
       }
       cnt += __popc(ok[u]);
     }
@@ -472,51 +560,35 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
     C += s_scratch[w];
   }
   __syncthreads();
+  // the weight of the candidates below the bins
+  const double W_low = use_p ? block_sum_d(low_mass, s_scratch) : 0.0;
+  SPEC_STAMP(p, 4, 2);   // sample and fused pass done
+  SPEC_STAMP(p, 4, 3);
   float tau = -INFINITY;
   if (!s_fault && C > 0.0) {
     const bool sel_k = use_k && (double)k < C;
-    // the largest scale that keeps every sum of fixed-point weights (each <= 1) below 2^53
+    // the radix fallback's fixed point: the largest scale that keeps every sum of weights
+    // (each <= 1) below 2^53
     const int fe = use_p ? 52 - (64 - __clzll(static_cast<unsigned long long>(C))) : -1;
-    ValueBins vb;
-    vb.lo = MN;
-    vb.scale = static_cast<float>(kBins) / (M - MN);
-    bool fast = M > MN && isfinite(M - MN) && isfinite(vb.scale) && vb.scale > 0.0f;
+    // a candidate far above the sample's maximum would overflow its fp32 weight
+    bool fast = binned && (!use_p || (M - ref) * p.c2 < 64.0f);
     float tau_k = -INFINITY;
-    if (M == MN) {
-      tau = M;                                   // one distinct value: every selection keeps it
+    if (M == MN || (sel_k && k == 1)) {
+      // one distinct value, or top-1: the kept set is the maximum's ties whatever top-p is
+      tau = M;
+      fast = true;
     } else if (fast) {
-      BinLds& L = s_sel.bins;
-      for (int j = threadIdx.x; j < kBins; j += kTB) {
-        L.cnt[j] = 0u;
-        L.mass[j] = 0ull;
-      }
-      __syncthreads();
-      // pass 1: counts and masses per value bin
-      for (long e0 = (long)threadIdx.x * kVec; e0 < p.V; e0 += (long)kTB * kVec * kU) {
-        float s[kU][8];
-        unsigned ok[kU];
-        cand_batch<DT, VEC>(p, lrow, row, e0, (long)kTB * kVec, s, ok);
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (!((ok[u] >> e) & 1u)) continue;
-            const int d = vb.of(s[u][e]);
-            if (sel_k) atomicAdd(&L.cnt[d], 1u);
-            if (use_p) atomicAdd(&L.mass[d], fixed_weight(s[u][e], M, p.c2, fe));
-          }
-      }
-      __syncthreads();
       int dk = -1, n = 0, dpf = -1, n2 = 0;
       double fk = 0.0;
       if (sel_k) {
+        // (dk < 0 when fewer than k candidates lie in the bins: then the radix selection)
         dk = find_bin([&](int d) { return d >= 0 ? (double)L.cnt[d] : 0.0; }, 0.0, (double)k, s_scratch, &s_d, &s_f, &fk);
         if (dk >= 0 && use_p) {
           // The top-p target is p * (A + part), A the mass of the bins above dk and part the
           // mass of bin dk's survivors (0 <= part <= mass[dk], known only after tau_k).  When
           // the targets for both ends fall in the same bin above dk, that bin is collected in
-          // the same pass as dk (every mass is an exact integer, so the true target lies
-          // between the two).
+          // the same pass as dk (the running mass is monotone in the bin, so the true
+          // target's bin lies between the two).
           double A = 0.0;
           for (int d = threadIdx.x; d < kBins; d += kTB)
             if (d > dk) A += (double)L.mass[d];
@@ -530,12 +602,15 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
           if (d0 > dk && d1 == d0) dpf = d0;
         }
         if (dk >= 0) {
-          if (dpf >= 0) n = collect2<DT, VEC>(p, lrow, row, vb, dk, dpf, M, fe, s_col, s_col2, &n2);
-          else n = collect<DT, VEC>(p, lrow, row, vb, dk, M, fe, s_col);
+          if (dpf >= 0) n = collect2<DT, VEC>(p, lrow, row, vb, dk, dpf, ref, s_col, s_col2, &n2);
+          else n = collect<DT, VEC>(p, lrow, row, vb, dk, ref, use_p, s_col);
         }
+        SPEC_STAMP(p, 4, 4);   // collected
+        SPEC_TRACE_ONLY(trace_word(p.trace, 4, blockIdx.x, 10, (unsigned)n | ((unsigned long long)n2 << 32)));
         if (dk < 0 || n > kCap) fast = false;
         else tau_k = resolve(s_col, n, -INFINITY, false, fk, (double)k, s_m);
         tau = tau_k;
+        SPEC_STAMP(p, 4, 5);   // top-k resolved
       }
       if (fast && use_p) {
         // survivors of top-k: every candidate above bin dk, and those of bin dk at or above
@@ -543,7 +618,7 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
         double part = 0.0, total = 0.0;
         if (sel_k)
           for (int i = threadIdx.x; i < n; i += kTB)
-            if (s_col.v[i] >= tau_k) part += (double)s_col.w[i];
+            if (s_col.v[i] >= tau_k) part += s_col.w[i];
         part = block_sum_d(part, s_scratch);
         auto valp = [&](int d) -> double {
           if (d < 0 || (sel_k && d < dk)) return 0.0;
@@ -552,7 +627,8 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
         {
           double t = 0.0;
           for (int d = threadIdx.x; d < kBins; d += kTB) t += valp(d);
-          total = block_sum_d(t, s_scratch);
+          // without top-k every candidate survives, those below the bins too
+          total = block_sum_d(t, s_scratch) + (sel_k ? 0.0 : W_low);
         }
         const double target = (double)tp * total;
         double fp = 0.0;
@@ -565,13 +641,15 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
           if (n2 > kCap) fast = false;
           else tau = resolve(s_col2, n2, -INFINITY, true, fp, target, s_m);
         } else {
-          const int n2 = collect<DT, VEC>(p, lrow, row, vb, dp, M, fe, s_col);
+          const int n2 = collect<DT, VEC>(p, lrow, row, vb, dp, ref, true, s_col);
           if (n2 > kCap) fast = false;
           else tau = resolve(s_col, n2, -INFINITY, true, fp, target, s_m);
         }
       }
     }
+    SPEC_STAMP(p, 4, 6);   // binned path done
     if (!fast) {
+      SPEC_TRACE_ONLY(trace_word(p.trace, 4, blockIdx.x, 11, 1ull));   // radix path taken
       // radix selection (also for rows whose values cannot be binned)
       unsigned lo = key_of(MN);
       const unsigned hi = key_of(M);
@@ -586,6 +664,7 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
     }
   }
   if (threadIdx.x == 0) p.thresh[row] = tau;
+  SPEC_STAMP(p, 4, 7);
 }
 
 template <int DT, bool VEC>

@@ -405,8 +405,9 @@ int spec_abi_version(void);                   /* SPEC_ABI_VERSION */
  * tracing (python -m exact_rejection_sampling_amd.build --trace, which writes
  * libspec_verify_trace.so), every later call records, for each block of its kernels, a tag
  * and stamps of the GPU's 100 MHz real-time counter into `buffer`: a device allocation of
- * 4 * records_per_kernel * 16 uint64 words, which the caller owns and keeps alive while traced
- * calls run; block x of kernel slot k (0 chain, 1 chain exact redraw, 2 tree, 3 residual tree)
+ * 5 * records_per_kernel * 16 uint64 words, which the caller owns and keeps alive while traced
+ * calls run; block x of kernel slot k (0 chain, 1 chain exact redraw, 2 tree, 3 residual tree,
+ * 4 the top-k / top-p threshold pass)
  * writes words [(k * records_per_kernel + x) * 16, + 16) with plain stores on the call's stream,
  * and blocks at or past records_per_kernel write nothing.  buffer == NULL turns tracing off.
  * Returns SPEC_EINVAL in a library built without tracing, or for a non-null buffer with
