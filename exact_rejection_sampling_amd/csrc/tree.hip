@@ -1,9 +1,11 @@
 // Tree verification by target-sample membership (spec_verify_tree).
 //
-// One kernel.  Each request owns ceil(V / 8192) root blocks followed by ceil(V / 16384)
-// helper blocks, adjacent in block order.  The root blocks stream the frontier row (node 0)
-// together, one 2048-element chunk per wave, and publish the chunks' online-softmax
-// summaries.  The last root block to finish walks the tree:
+// One kernel.  Each request owns ceil(V / 8192) root blocks followed by its helper blocks
+// (ceil(V / 16384); ceil(V / 8192) for the residual-update tree), adjacent in block order.
+// The root blocks stream the frontier row (node 0) together, one 2048-element chunk per
+// wave, and publish the chunks' online-softmax summaries.  The request's first root block,
+// once its own chunks are summarized, walks the tree, reading the other summaries as they
+// are published:
 //   * combine the summaries of the current node's row into (reference, Z) and the chunk
 //     masses, pick the chunk where the running mass passes u_v * Z, rescan that chunk in
 //     vocabulary order to get the target sample y;
@@ -11,12 +13,11 @@
 //     blocks to summarize the child's row (each helper streams 8 chunks of it); otherwise
 //     y is the terminal token and the helpers are dismissed.
 // Only rows on the walked path are read.  Waits: the helpers wait for their walker, a
-// lower-numbered block; the walker waits for its helpers, which follow its request's root
-// blocks directly.  The workgroups of a launch are dispatched in index order, so the only
-// helpers a walker can wait for before they are dispatched belong to the request being
-// dispatched, and every other waiting block's partners are running; every wait ends, and
-// each is bounded all the same (a word that does not arrive in time is reported as
-// SPEC_REQ_INTERNAL).
+// lower-numbered block; the walker waits for its request's other root blocks and helpers,
+// which follow it directly.  Each XCD dispatches the workgroups it is given in index order,
+// so once every earlier request has finished, all of a request's workgroups are dispatched
+// (a request needs a few slots per XCD) and every wait among them ends; each is bounded all
+// the same (a word that does not arrive in time is reported as SPEC_REQ_INTERNAL).
 //
 // Method: [M7.7] "M7.7 - Draft Sources, Dependent Heads, and Hardware-Aware Trees"
 // §0x07E (a node's row scores its children), §0x04B and §0x09 (accept the candidate that
@@ -889,13 +890,9 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
   }
   __syncthreads();
   SPEC_STAMP(p, K, 2);
-  __shared__ int s_last;
-  if (threadIdx.x == 0) {
-    const unsigned prev = arrive(&p.counters[(size_t)b * kCounterSlots + 0]);
-    s_last = (prev == (unsigned)(p.WG1 - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
+  // the request's first root block walks: it reads the other root blocks' summaries as
+  // they are published (every summary word validates itself), so no arrival count is kept
+  if (slice != 0) return;
   SPEC_TAG(p, K, SPEC_TRACE_TAG(kTraceWalker, b, slice));
   unsigned gen = 0;
   if constexpr (RESID) tree_walk_residual<DT, QT, VEC>(p, b, gen);
@@ -905,7 +902,6 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams p) {
   for (int j = threadIdx.x; j < p.P; j += kBlock) clear_f2(p.part + (size_t)b * p.P + j);
   if constexpr (RESID)   // no helper reads the descriptor once dismissed
     for (int j = threadIdx.x; j < p.desc_words; j += kBlock) publish_u64(p.desc + (size_t)b * p.desc_words + j, 0ull);
-  if (threadIdx.x == 0) reset_counter(&p.counters[(size_t)b * kCounterSlots + 0]);
   SPEC_STAMP(p, K, 3);
 }
 
