@@ -9,7 +9,7 @@
 //    p * (total mass): the smallest tie-closed set of top tokens whose probability reaches p.
 // Counts are integers; masses are fp64 sums of fp32 weights 2^((s - ref) c2) (ref a value of
 // the row, which cancels in every ratio), whose rounding (about 1e-16 relative per add) is
-// far inside the 1e-5 window in which the oracle flags a top-p decision.  Usual path, two
+// far inside the 1e-5 relative window around a top-p boundary that parity tests exclude.  Usual path, two
 // or three passes over the row: a sample of the row (one batch per thread, spread over it)
 // fixes the range of 4096 LDS bins linear in s; (1) one pass adds every candidate's count
 // and weight to its bin (values outside the range go to the end bins) and finds the row's
