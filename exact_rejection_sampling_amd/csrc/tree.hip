@@ -190,6 +190,15 @@ __device__ __forceinline__ unsigned long long desc_word(unsigned tag, unsigned v
   return (static_cast<unsigned long long>(tag) << 32) | v;
 }
 __device__ __forceinline__ unsigned desc_value(unsigned long long w) { return static_cast<unsigned>(w); }
+// A descriptor word re-read until it carries `tag` (bounded: the last read is returned).
+__device__ __forceinline__ unsigned long long await_desc(const unsigned long long* w, unsigned tag) {
+  unsigned long long v = fetch_u64(w);
+  for (unsigned spins = 0; static_cast<unsigned>(v >> 32) != tag && spins < kSpinLimit; ++spins) {
+    __builtin_amdgcn_s_sleep(1);
+    v = fetch_u64(w);
+  }
+  return v;
+}
 // A chunk-mass word meaning "the helper's descriptor never became current": the walker
 // reports SPEC_REQ_INTERNAL on it.  (A published mass is a negated fp64 value; this is a
 // NaN bit pattern that no negated mass takes.)
@@ -655,15 +664,20 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
     int c = next_child(par, N, v, v, s_imin);
     while (c != kNoPick) {
       // the accept test's loads, issued together: thread 0 the child's q(x), u and the row's
-      // logit at x; thread 1 + j the q value at x of rejected child j
+      // logit at x; threads 1 .. kBlock - 1 the q values at x of the staged rejected children
+      // j = tid - 1 and j = tid - 1 + (kBlock - 1) (kResidStage > kBlock - 1: one thread
+      // alone would leave the last staged child's value unloaded)
       const int x = tok[c];
       float qx = 0.0f, ua = 0.0f, lx = 0.0f;
       if (tid == 0) {
         qx = load_scalar<QT>(p.q, ((size_t)b * N + c) * p.V + x);
         ua = p.u[(size_t)b * N + c];
         lx = load_scalar<DT>(row, x);
-      } else if (tid - 1 < min(i, kResidStage)) {
-        s_qx[tid - 1] = load_scalar<QT>(p.q, ((size_t)b * N + s_kid[tid - 1]) * p.V + x);
+      } else {
+        static_assert(kResidStage <= 2 * (kBlock - 1), "two staged children per thread at most");
+        const int ns = min(i, kResidStage);
+        for (int j = tid - 1; j < ns; j += kBlock - 1)
+          s_qx[j] = load_scalar<QT>(p.q, ((size_t)b * N + s_kid[j]) * p.V + x);
       }
       __syncthreads();
       if (tid == 0) {
@@ -675,16 +689,28 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
         } else {
           // residual at x after the i rejections so far, the same expression as residualN
           float g = scaled_exp(lx, p.c2, r) * inv_z;
+          bool stale = false;
           for (int j = 0; j < i; ++j) {
-            const float qj = j < kResidStage
-                                 ? s_qx[j]
-                                 : load_scalar<QT>(p.q, ((size_t)b * N + static_cast<int>(desc_value(fetch_u64(d + 3 + j)))) * p.V + x);
-            const float invw = j < kResidStage ? s_invw[j] : __uint_as_float(desc_value(fetch_u64(d + 3 + N + j)));
+            float qj, invw;
+            if (j < kResidStage) {
+              qj = s_qx[j];
+              invw = s_invw[j];
+            } else {
+              // this thread wrote both words (tag g1 + j), the 1/W word just before this test:
+              // a read that can pass the write-through store is re-read until it is current
+              const unsigned tag = g1 + static_cast<unsigned>(j);
+              const unsigned long long wk = await_desc(d + 3 + j, tag);
+              const unsigned long long ww = await_desc(d + 3 + N + j, tag);
+              stale |= static_cast<unsigned>(wk >> 32) != tag || static_cast<unsigned>(ww >> 32) != tag;
+              qj = load_scalar<QT>(p.q, ((size_t)b * N + static_cast<int>(desc_value(wk))) * p.V + x);
+              invw = __uint_as_float(desc_value(ww));
+            }
             const float t = g - qj;
             g = (t > 0.0f ? t : 0.0f) * invw;
           }
           const double a = fmin(1.0, (double)g / (double)qx);
           acc = (double)ua < a;
+          if (stale) st = SPEC_REQ_INTERNAL;
         }
         s_status = st;
         s_accept = acc;
