@@ -420,6 +420,13 @@ __device__ __forceinline__ void chain_decide(const ChainParams& p, int b, RowSta
   __syncthreads();
 }
 
+// An empty asm on an element's input keeps the compiler from widening every element of a
+// chunk to fp64 at once.
+__device__ __forceinline__ float pin(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Terminal weight of one element: p(x) = 2^(l c2 - r) / Z; residual rows subtract q and
 // clamp at zero.  A negative or non-finite q entry poisons the mass with NaN.
 template <bool RESID>
@@ -667,31 +674,35 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
     term_chunk<DT, QT, VEC, RESID, PROC>(p, lrow, qrow, cstar, d, (size_t)b * p.R + d.A, w, bad);
     SPEC_STAMP(p, 0, 12);   // chunk reloaded, weights formed
     static_assert(kTermSlabs == 2, "the rescan scans two slabs in one pass");
-    double incl[kTermSlabs][8], acc[kTermSlabs];
-    int last_pos = -1, pick = 0x7fffffff;
+    double acc[kTermSlabs];
+    unsigned pos_mask[kTermSlabs];
 #pragma unroll
     for (int s = 0; s < kTermSlabs; ++s) {
-      const long e0 = ((long)cstar * kTermSlabs + s) * kSlab + (long)tid * kVec;
       acc[s] = 0.0;
+      pos_mask[s] = 0u;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         acc[s] += (double)w[s][j];
-        incl[s][j] = acc[s];
-        if (w[s][j] > 0.0f) last_pos = (int)(e0 + j);
+        pos_mask[s] |= (w[s][j] > 0.0f ? 1u : 0u) << j;
       }
     }
-    // slab 0 then slab 1 in vocabulary order: one pass for both slabs' block prefixes
     double off[kTermSlabs], slab_total[kTermSlabs];
     block_excl_scan_d2(acc[0], acc[1], s_scan2, &off[0], &off[1], &slab_total[0], &slab_total[1]);
     off[1] += 0.0 + slab_total[0];
+    int last_pos = -1, pick = 0x7fffffff;
 #pragma unroll
     for (int s = 0; s < kTermSlabs; ++s) {
-      const long e0 = ((long)cstar * kTermSlabs + s) * kSlab + (long)tid * kVec;
-      int cand = 0x7fffffff;
+      const int e0 = (int)(((long)cstar * kTermSlabs + s) * kSlab + (long)tid * kVec);
+      unsigned hit = 0u;
+      double run = 0.0;
 #pragma unroll
-      for (int j = 7; j >= 0; --j)
-        if (off[s] + incl[s][j] > rem && w[s][j] > 0.0f) cand = (int)(e0 + j);
-      pick = min(pick, cand);
+      for (int j = 0; j < 8; ++j) {
+        run += (double)pin(w[s][j]);
+        hit |= (off[s] + run > rem ? 1u : 0u) << j;
+      }
+      hit &= pos_mask[s];
+      if (hit) pick = min(pick, e0 + __builtin_ctz(hit));
+      if (pos_mask[s]) last_pos = max(last_pos, e0 + 31 - __builtin_clz(pos_mask[s]));
     }
     // the first position whose running value passes the target; rounding may leave the
     // target just past the chunk's last positive weight: then take that weight
@@ -831,13 +842,6 @@ __device__ void terminal_item(const ChainParams& p, int b, int c, RowState& s_rs
 // the weights at 1/Z, and overwrites the request's token, W and finish.  Blocks of requests
 // without a record return at once.  It is a kernel of its own so that its fp64 registers
 // do not lower the chain kernel's occupancy.
-
-// An empty asm on an element's input keeps the compiler from widening every element of a
-// chunk to fp64 at once.
-__device__ __forceinline__ float pin(float x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
 
 // One element's exact weight at 1/Z = iz; e(x) is returned too.
 __device__ __forceinline__ double exact_w(float l, float q, double c2d, double r, double iz, double& e) {
@@ -1157,7 +1161,7 @@ __global__ __launch_bounds__(kBlock) void chain_kernel(ChainParams p) {
 // items, when their summaries are normally published.  0 puts every statistics item
 // first.
 #ifndef SPEC_CHAIN_LAG_TENTHS
-#define SPEC_CHAIN_LAG_TENTHS 20
+#define SPEC_CHAIN_LAG_TENTHS 16
 #endif
 constexpr long kLagTenths = SPEC_CHAIN_LAG_TENTHS;   // in tenths of a round
 // Lazy rows: lag between a request's last row group and its terminal items, in tenths of

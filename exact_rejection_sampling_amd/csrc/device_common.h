@@ -108,37 +108,43 @@ __device__ __forceinline__ void load8_granules(const void* row, long e0, float (
 
 // Eight consecutive elements [e0, e0 + 8) of a row of V elements, e0 % 8 == 0.
 // Positions >= V read as `fill`.  VEC: the row is 16-byte aligned and V % 8 == 0, so the
-// group is either entirely inside or entirely past the row.  NT: streaming (non-temporal)
-// loads for data read exactly once.
+// group is either entirely inside or entirely past the row; a group past the row loads the
+// row's first group instead (always mapped) and selects `fill`, with no branch around the
+// load, so that a caller's loads of several groups all issue before the first wait.  NT:
+// streaming (non-temporal) loads for data read exactly once.
 template <int DT, bool VEC, bool NT>
 __device__ __forceinline__ void load8(const void* row, long e0, long V, float (&v)[8], float fill) {
-  if (e0 >= V) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = fill;
-    return;
-  }
   if constexpr (VEC) {
+    const bool in = e0 < V;
+    const long ea = in ? e0 : 0;
     if constexpr (DT == kBF16) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + e0);
+      const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + ea);
       u32x4 w;
       if constexpr (NT) w = __builtin_nontemporal_load(p); else w = *p;
-      v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
-      v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
-      v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xffff0000u);
-      v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xffff0000u);
+      const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = in ? __uint_as_float(d[k] << 16) : fill;
+        v[2 * k + 1] = in ? __uint_as_float(d[k] & 0xffff0000u) : fill;
+      }
     } else {
-      const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(row) + e0);
+      const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(row) + ea);
       f32x4 a, b;
       if constexpr (NT) { a = __builtin_nontemporal_load(p); b = __builtin_nontemporal_load(p + 1); }
       else { a = p[0]; b = p[1]; }
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      v[0] = in ? a.x : fill; v[1] = in ? a.y : fill; v[2] = in ? a.z : fill; v[3] = in ? a.w : fill;
+      v[4] = in ? b.x : fill; v[5] = in ? b.y : fill; v[6] = in ? b.z : fill; v[7] = in ? b.w : fill;
     }
-  } else if (e0 + 8 <= V) {
-    load8_granules<DT>(row, e0, v);
   } else {
+    if (e0 >= V) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = (e0 + k < V) ? load_scalar<DT>(row, e0 + k) : fill;
+      for (int k = 0; k < 8; ++k) v[k] = fill;
+    } else if (e0 + 8 <= V) {
+      load8_granules<DT>(row, e0, v);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = (e0 + k < V) ? load_scalar<DT>(row, e0 + k) : fill;
+    }
   }
 }
 
