@@ -349,7 +349,7 @@ spec_status spec_verify_tree(const void* node_logits, int logit_dtype, const int
   p.V = V;
   p.P = chunks(V, sv::kWaveChunk);
   p.WG1 = chunks(p.P, sv::kWavesPerBlock);
-  p.WH = chunks(p.P, sv::kTreeHelperChunks);
+  p.WH = (int)sv::tree_helpers(p.P, false);
   p.c2 = static_cast<float>(kLog2e / static_cast<double>(temperature));
   const bool vec = (V % 8 == 0) && aligned16(node_logits);
   SPEC_TRACE_FILL(p);
@@ -387,7 +387,7 @@ spec_status spec_verify_tree_greedy(const void* node_logits, int logit_dtype, co
   p.V = V;
   p.P = chunks(V, sv::kWaveChunk);
   p.WG1 = chunks(p.P, sv::kWavesPerBlock);
-  p.WH = chunks(p.P, sv::kTreeHelperChunks);
+  p.WH = (int)sv::tree_helpers(p.P, false);
   const bool vec = (V % 8 == 0) && aligned16(node_logits);
   SPEC_TRACE_FILL(p);
   return sv::launch_tree_greedy(p, logit_dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_EHIP;

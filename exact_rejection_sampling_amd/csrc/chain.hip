@@ -537,6 +537,10 @@ constexpr int kMassRegs = 8;
 // A rejection whose residual mass (from the fp32 terminal weights) is below this is drawn
 // again, exactly, by chain_exact_kernel.
 constexpr double kExactBelow = 0.05;
+// Terminal chunks each block of chain_exact_kernel covers: the kernel runs after every chain
+// call, almost always to find nothing to redraw, and fewer blocks find that sooner.
+constexpr int kExactChunks = 8;
+__host__ __device__ __forceinline__ int exact_blocks(int S2) { return (S2 + kExactChunks - 1) / kExactChunks; }
 
 // Statistics of row i: (m, log Z, p(x), a) of a reached draft row, (m, log Z, NaN, NaN)
 // of the reached bonus row, NaN otherwise.
@@ -886,20 +890,24 @@ __global__ __launch_bounds__(kBlock) void chain_exact_kernel(ChainParams p) {
   __shared__ int s_imin[kWavesPerBlock];
   __shared__ int s_lost;
   __shared__ double s_before, s_total;
-  const int b = blockIdx.x / p.S2, c = blockIdx.x % p.S2;
+  __shared__ double s_own[kExactChunks][3];   // the selecting block's own chunks' sums
+  const int X = exact_blocks(p.S2);
+  const int b = blockIdx.x / X, x = blockIdx.x % X;
+  const int c_begin = x * kExactChunks, c_end = min(c_begin + kExactChunks, p.S2);
+  const bool selects = x == X - 1;
   SPEC_STAMP(p, 1, 1);
   unsigned* rec = reinterpret_cast<unsigned*>(p.part + (size_t)b * p.R * p.SL);
   const unsigned pend = rec[0];
   const int chain_status = p.req_status[b];
   const unsigned dirty = fetch_u32(dirty_word(p.part));
-  SPEC_TAG(p, 1, SPEC_TRACE_TAG(pend ? kTraceExact : kTraceExactIdle, b, c));
+  SPEC_TAG(p, 1, SPEC_TRACE_TAG(pend ? kTraceExact : kTraceExactIdle, b, x));
   if (dirty != 0u || chain_status == SPEC_REQ_INTERNAL) {
     // A wait of the chain kernel gave up on this request: a word published after its
     // consumer cleared it may be left over.  Every block of the chain kernel has finished
     // now, so zeroing the request's words here leaves them clean for later calls.  On a
     // dirty workspace (a wait of an earlier call gave up) no result of this call can be
     // trusted: every request fails.
-    if (c == 0) {
+    if (x == 0) {
       if (dirty != 0u) chain_fail(p, b, SPEC_REQ_INTERNAL);
       chain_scrub(p, b);
     }
@@ -918,41 +926,42 @@ __global__ __launch_bounds__(kBlock) void chain_exact_kernel(ChainParams p) {
   if constexpr (QT != kSparseQ) qrow = row_ptr<QT>(p.q, (size_t)b * p.G + d.A, p.V);
   const double r = (double)d.r_ref, iza = (double)d.inv_z;
 
-  // 1. this chunk's sums
+  // 1. the sums of this block's chunks, one chunk at a time
   float lv[kTermSlabs][8], qv[kTermSlabs][8];
   bool bad = false;
-  term_inputs<DT, QT, VEC, true, PROC>(p, lrow, qrow, c, d, rowid, lv, qv, bad);
-  double m = 0.0, dm = 0.0, em = 0.0;
+  if (tid == 0) {
+    s_lost = 0;
+    s_before = 0.0;
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    term_inputs<DT, QT, VEC, true, PROC>(p, lrow, qrow, c, d, rowid, lv, qv, bad);
+    double m = 0.0, dm = 0.0, em = 0.0;
 #pragma unroll
-  for (int s = 0; s < kTermSlabs; ++s)
+    for (int s = 0; s < kTermSlabs; ++s)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      double e;
-      const double w = exact_w(pin(lv[s][k]), pin(qv[s][k]), p.c2d, r, iza, e);
-      m += w;
-      em += e;
-      dm += w > 0.0 ? e : 0.0;
-    }
-  if (bad) m = NAN;
-  {
+      for (int k = 0; k < 8; ++k) {
+        double e;
+        const double w = exact_w(pin(lv[s][k]), pin(qv[s][k]), p.c2d, r, iza, e);
+        m += w;
+        em += e;
+        dm += w > 0.0 ? e : 0.0;
+      }
+    if (bad) m = NAN;
     const double wm = wave_sum_d(m), wd = wave_sum_d(dm), we = wave_sum_d(em);
     if (lane == 0) {
       s_red[0][wave] = wm;
       s_red[1][wave] = wd;
       s_red[2][wave] = we;
     }
+    __syncthreads();
+    if (tid < 3) {
+      const double v = (s_red[tid][0] + s_red[tid][1]) + (s_red[tid][2] + s_red[tid][3]);
+      if (selects) s_own[c - c_begin][tid] = v;
+      else publish_mass(xmass_word(p, b, c, tid), v);
+    }
+    __syncthreads();
   }
-  if (tid == 0) {
-    s_lost = 0;
-    s_before = 0.0;
-  }
-  __syncthreads();
-  double own[3];
-#pragma unroll
-  for (int k = 0; k < 3; ++k) own[k] = (s_red[k][0] + s_red[k][1]) + (s_red[k][2] + s_red[k][3]);
-  if (c != p.S2 - 1) {
-    if (tid == 0)
-      for (int k = 0; k < 3; ++k) publish_mass(xmass_word(p, b, c, k), own[k]);
+  if (!selects) {
     SPEC_STAMP(p, 1, 3);
     return;
   }
@@ -962,7 +971,7 @@ __global__ __launch_bounds__(kBlock) void chain_exact_kernel(ChainParams p) {
   const float ut = p.u[(size_t)b * p.R + G];
   const int my_stop = tid < p.st.n_stop ? p.st.stop[tid] : 0;
   auto word = [&](int cc, int k) -> double {
-    if (cc == p.S2 - 1) return own[k];
+    if (cc >= c_begin) return s_own[cc - c_begin][k];
     const unsigned long long bits = await_u64(reinterpret_cast<const unsigned long long*>(xmass_word(p, b, cc, k)));
     if (bits == 0ull) s_lost = 1;
     return -__longlong_as_double(static_cast<long long>(bits));
@@ -1208,7 +1217,7 @@ hipError_t launch_typed(ChainParams p, hipStream_t s) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the exact redraws of small residuals, and the scrub of requests whose waits gave up
-  chain_exact_kernel<DT, QT, VEC, PROC><<<dim3((unsigned)((size_t)p.B * p.S2)), dim3(kBlock), 0, s>>>(p);
+  chain_exact_kernel<DT, QT, VEC, PROC><<<dim3((unsigned)((size_t)p.B * exact_blocks(p.S2))), dim3(kBlock), 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -217,9 +217,18 @@ constexpr int kTreeHelperChunks = 4 * kTreeHelperBatch;
 // dependent rounds of loads per pass.
 constexpr int kResidHelperBatch = 1;
 constexpr int kResidHelperChunks = 4 * kResidHelperBatch;
+// Helpers per request at most.  Every helper of a request stays resident from the walker's
+// first order to its last, and the walker needs all of them, so a request's helpers on one
+// XCD (an eighth of them: blocks go to the eight XCDs in turn) plus its
+// walker must fit the XCD's slots at once: 256 helpers are 32 per XCD, against 64 slots at
+// two blocks per CU on 32 CUs.  Past that (vocabularies beyond 2^22) a helper takes every
+// kMaxTreeHelpers-th group of chunks in turn.  The residual tree's V <= 2^21 keeps it at
+// P / 4 <= 256 helpers.
+constexpr int kMaxTreeHelpers = 256;
 inline long tree_helpers(long P, bool residual) {
   const long per = residual ? kResidHelperChunks : kTreeHelperChunks;
-  return (P + per - 1) / per;
+  const long h = (P + per - 1) / per;
+  return h < kMaxTreeHelpers ? h : kMaxTreeHelpers;
 }
 
 // Workspace carving: 256 bytes of global counters, kCounterSlots 32-bit counters per

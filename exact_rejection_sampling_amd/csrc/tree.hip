@@ -842,15 +842,18 @@ __device__ void helper_item(const TreeParams& p, int b, int h) {
     float2* dst = p.deep + ((size_t)b * 2 + (gen & 1u)) * p.P;
     constexpr int HB = RESID ? kResidHelperBatch : kTreeHelperBatch;     // chunks per wave
     constexpr int HC = RESID ? kResidHelperChunks : kTreeHelperChunks;   // chunks per helper
+    // helper h's groups of HC chunks: h, h + WH, h + 2 WH, ... (one group unless the request
+    // has more chunk groups than kMaxTreeHelpers)
+    for (int c0 = h * HC; c0 < p.P; c0 += p.WH * HC) {
     ChunkRegs<DT> r[HB];
 #pragma unroll
     for (int k = 0; k < HB; ++k) {
-      const int c = h * HC + k * kWavesPerBlock + wave;
+      const int c = c0 + k * kWavesPerBlock + wave;
       if (c < p.P) chunk_load<DT, VEC>(row, p.V, c, lane, r[k]);
     }
 #pragma unroll
     for (int k = 0; k < HB; ++k) {
-      const int c = h * HC + k * kWavesPerBlock + wave;
+      const int c = c0 + k * kWavesPerBlock + wave;
       if (c < p.P) {
         // the same per-chunk summary the root blocks form (one chunk per wave)
         float v[kStatVecs][8];
@@ -872,6 +875,7 @@ __device__ void helper_item(const TreeParams& p, int b, int h) {
           if (lane == 0) publish_f2(dst + c, make_float2(m, z));
         }
       }
+    }
     }
   }
   if (threadIdx.x == 0) {
