@@ -190,3 +190,44 @@ def test_truncations_on_piled_values(V):
     p = np.array([1.0, 0.5, 0.9, 0.99, 0.3, 1.0] * 2, np.float32)
     say(f"chain_ex truncations on piled values V={V}")
     check(x, None, None, k, p)
+
+
+@pytest.mark.parametrize("dt,V,T", [("f32", 32000, 1.0), ("bf16", 128256, 0.8), ("f32", 4096, 0.25)])
+def test_top_p_boundaries_just_outside_the_flag_window(dt, V, T):
+    """The oracle flags a top-p decision whose deciding mass lies within 1e-5 of the target
+    p * Z.  Here every request's p is placed 2e-5 * Z above or below the mass of its top m
+    distinct values (m = 1..32, fewer on very peaked rows), so the boundary is never flagged and the kept set must be
+    exactly the oracle's: m or m + 1 values.  gamma = 0 gives one row per request, so p
+    decides one boundary; a wrong kept set changes log Z of the bonus row by the boundary
+    token's share (far above the 1e-5 tolerance) and usually the token.  The GPU's masses are
+    fp64 sums of fp32 weights 2^((s - ref) c2): relative errors near 1e-7 per weight where the
+    mass lies, so 2e-5 leaves a wide margin."""
+    B = 64
+    x = synth.make_chain(B, 0, V, seed=V + int(T * 10), logit_dtype=dt, sigma=3.0, noise=1.0, temperature=T)
+    L = oracle.decode(x.logits, x.logit_dtype)[:, 0].astype(np.float32).astype(np.float64)
+    Tf = float(np.float32(T))
+    p = np.empty(B, np.float32)
+    for b in range(B):
+        s = L[b]
+        w = np.exp((s - s.max()) / Tf)
+        Z = w.sum()
+        uniq, inv = np.unique(s, return_inverse=True)
+        mass = np.bincount(inv, weights=w)[::-1]          # per distinct value, largest first
+        # m = 1 + b % 32 values, fewer where the row is so peaked that a value near the
+        # boundary holds under 1e-4 of the mass (its own boundary would then be flagged)
+        m = 1 + b % 32
+        while m > 1 and not (mass[m - 1] > 1e-4 * Z and mass[m] > 1e-4 * Z):
+            m -= 1
+        top = mass[:m].sum()                              # mass of the top m distinct values
+        sign = 1.0 if (b // 32) % 2 == 0 else -1.0
+        p[b] = np.float32((top + sign * 2e-5 * Z) / Z)
+        if not p[b] < 1.0:                                # p >= 1 turns top-p off: go below instead
+            p[b] = np.float32((top - 2e-5 * Z) / Z)
+    k = np.zeros(B, np.int32)
+    say(f"chain_ex top-p boundaries 2e-5 from the target, {dt} V={V} T={T}")
+    got = run_chain_proc(x, None, None, k, p)
+    exp = oracle_chain_proc(x, None, None, k, p)
+    _, pflag = oracle.process_rows(x.logits, x.logit_dtype, x.temperature, None, None, k, p)
+    assert not pflag.any(), "a boundary placed outside the window was flagged"
+    s = compare_chain(got, exp, max_flag_frac=0.1)
+    print(s)
