@@ -721,8 +721,12 @@ def timeline_thresh(args, torch, sv, synth, lib):
     print(f"Trace build, {args.timeline_calls} traced calls; per row (block) times in us. Calls of the trace build: "
           f"{off:.1f} us with tracing off, {on:.1f} us on (the whole processed chain call).")
     print()
-    print("| rows (top-k, top-p) | count per call | median duration | max duration | pass 0 | pass 1 (bins) | "
-          "collect | resolve top-k | top-p | radix / end |")
+    print("Stamps, window path: sample and window choice | window pass | window bins | top-k | top-p | end. "
+          "Full path (top-1, and any row whose window fell back): sample and counting pass | (none) | collect | "
+          "top-k | top-p | radix and end.")
+    print()
+    print("| rows (top-k, top-p) | count per call | median duration | max duration | stamp 1→2 | 2→3 | 3→4 | "
+          "4→5 | 5→6 | 6→end |")
     print("|---|---|---|---|---|---|---|---|---|---|")
     nc = max(1, args.timeline_calls)
     for kval in sorted(set(r_["k"] for r_ in rows if r_["kind"] != 0)):
@@ -731,14 +735,17 @@ def timeline_thresh(args, torch, sv, synth, lib):
             if not sel:
                 continue
             f = lambda key: _med([r_[key] for r_ in sel])
-            nrad = sum(r_["radix"] for r_ in sel)
+            nrad = sum(1 for r_ in sel if r_["radix"] == 1)
+            nfb = sum(1 for r_ in sel if r_["radix"] == 2)
+            note = (f" (radix in {nrad})" if nrad else "") + (f" (window fell back in {nfb})" if nfb else "")
             print(f"| k={kval}, p={pval:g} | {len(sel) // nc} | {f('dur'):.2f} | {max(r_['dur'] for r_ in sel):.2f} | "
                   f"{f('p0'):.2f} | {f('p1'):.2f} | {f('col'):.2f} | {f('res'):.2f} | {f('topp'):.2f} | "
-                  f"{f('rest'):.2f}{' (radix in %d)' % nrad if nrad else ''} |")
+                  f"{f('rest'):.2f}{note} |")
     slow = sorted(rows, key=lambda r_: -r_["dur"] if np.isfinite(r_["dur"]) else 0)[:8]
     print()
-    print("Slowest rows: " + "; ".join(f"k={r_['k']} p={r_['p']:g} {r_['dur']:.1f} us (collected {r_['n']}"
-                                      f"{', radix' if r_['radix'] else ''})" for r_ in slow))
+    print("Slowest rows: " + "; ".join(f"k={r_['k']} p={r_['p']:g} {r_['dur']:.1f} us"
+                                      f"{' (radix)' if r_['radix'] == 1 else (' (window fell back)' if r_['radix'] == 2 else '')}"
+                                      for r_ in slow))
     ends = [r_["end"] for r_ in rows if np.isfinite(r_["end"])]
     print()
     print(f"Last row ends at {np.percentile(ends, 100):.2f} us (p90 {np.percentile(ends, 90):.2f}, "

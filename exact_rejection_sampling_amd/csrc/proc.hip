@@ -9,19 +9,24 @@
 //    p * (total mass): the smallest tie-closed set of top tokens whose probability reaches p.
 // Counts are integers; masses are fp64 sums of fp32 weights 2^((s - ref) c2) (ref a value of
 // the row, which cancels in every ratio), whose rounding (about 1e-16 relative per add) is
-// far inside the 1e-5 relative window around a top-p boundary that parity tests exclude.  Usual path, two
-// or three passes over the row: a sample of the row (one batch per thread, spread over it)
-// fixes the range of 4096 LDS bins linear in s; (1) one pass adds every candidate's count
-// and weight to its bin (values outside the range go to the end bins) and finds the row's
-// max, min and count; then for each selection the bin where the count or mass from the top
-// reaches its target, (2) a pass that collects that bin's candidates into LDS, and an exact
-// resolution among them.  With both selections on, one collecting pass serves both
-// whenever the top-p bin is fixed before tau_k is.  Top-1 keeps the maximum's ties whatever
-// top-p is.  A bin with more than 1024 candidates (values piled on a few points) falls back
-// to radix selection over the bits in which the candidate keys differ, 12 bits per pass,
-// with fixed-point masses (each weight scaled by the largest power of two that keeps every
-// sum below 2^53).  The row's threshold is tau_p when top-p is on (it is at least tau_k),
-// else tau_k, or -inf.
+// far inside the 1e-5 relative window around a top-p boundary that parity tests exclude.
+// First a sample of the row (one batch per thread, spread over it).  Window path (the usual
+// one): from the sample, a value t_lo with about 2k candidates above it in the row (top-k),
+// or about 3300 (top-p alone); one pass collects every candidate at or above t_lo, with its
+// weight, into LDS and keeps only the count and weight of the rest; the thresholds are
+// resolved inside the window (bins over it, then the deciding bin's candidates), which is
+// used only when it provably holds them.  Full path (top-1, k above about 1600, or a window
+// that overflows or misses): the sample fixes the range of 4096
+// LDS bins linear in s; (1) one pass adds every candidate's count and weight to its bin
+// (values outside the range go to the end bins) and finds the row's max, min and count; then
+// for each selection the bin where the count or mass from the top reaches its target, (2) a
+// pass that collects that bin's candidates into LDS, and an exact resolution among them.
+// With both selections on, one collecting pass serves both whenever the top-p bin is fixed
+// before tau_k is.  Top-1 keeps the maximum's ties whatever top-p is.  A bin with more than
+// 1024 candidates (values piled on a few points) falls back to radix selection over the bits
+// in which the candidate keys differ, 12 bits per pass, with fixed-point masses (each weight
+// scaled by the largest power of two that keeps every sum below 2^53).  The row's threshold
+// is tau_p when top-p is on (it is at least tau_k), else tau_k, or -inf.
 //
 // Method: [M7.1] "M7.1 - Speculative Decoding: Draft, Verify, Accept, Reject" §0x06J (the
 // verified p is the row after top-k and top-p); [Tiny] "Exact Speculative and Assisted
@@ -272,9 +277,21 @@ struct BinLds {
   unsigned cnt[kBins];
   double mass[kBins];                   // fp64 sums of fp32 weights relative to the bins' reference
 };
+// The window path (below): every candidate at or above a value t_lo estimated from the
+// sample, with its weight, collected in one pass; then bins over the window alone.
+constexpr int kWinCap = 4096;
+constexpr int kWinBins = 1024;
+struct WinLds {
+  float v[kWinCap];
+  float w[kWinCap];                     // fp32 weights relative to the bins' reference (or 1)
+  unsigned cnt[kWinBins];               // the sample's, then the window's, bin counts
+  double mass[kWinBins];                // the window's bin masses
+  int n;
+};
 union SelectLds {
   BinLds bins;
   RadixLds radix;
+  WinLds win;
 };
 struct Collected {
   float v[kCap];
@@ -307,10 +324,12 @@ __device__ __forceinline__ double block_sum_d(double v, double* scratch) {
 // The largest bin d whose F(d) = above + sum of val over bins >= d reaches `target` (block-
 // wide; -1 if none): returns d and, in *f_above, F(d + 1).  Thread t owns kBinsPerThread
 // consecutive bins, the highest to thread 0.
-template <class Val>
+template <class Val, int NB = kBins>
 __device__ __forceinline__ int find_bin(Val val, double above, double target, double* scratch, int* s_d, double* s_f, double* f_above) {
+  constexpr int kBinsPerThread = NB / kTB;
+  static_assert(NB % kTB == 0, "whole bins per thread");
   const int tid = threadIdx.x;
-  const int d_hi = kBins - 1 - tid * kBinsPerThread;
+  const int d_hi = NB - 1 - tid * kBinsPerThread;
   double run = 0.0;
 #pragma unroll
   for (int i = 0; i < kBinsPerThread; ++i) run += val(d_hi - i);
@@ -426,67 +445,281 @@ __device__ __forceinline__ float resolve(const Collected& L, int n, float floor_
   return r;
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(ThreshParams p) {
-  __shared__ double s_scratch[kTW];
-  __shared__ SelectLds s_sel;
-  __shared__ Collected s_col, s_col2;
-  __shared__ float s_m[kTW], s_mn[kTW];
-  __shared__ int s_fault, s_d;
-  __shared__ double s_f;
-  const size_t row = blockIdx.x;
-  SPEC_STAMP(p, 4, 1);
-  const int b = static_cast<int>(row / p.R);
-  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
-  const int k = p.top_k ? p.top_k[b] : 0;
-  const float tp = p.top_p ? p.top_p[b] : 1.0f;
-  const bool use_k = k >= 1, use_p = tp > 0.0f && tp < 1.0f;   // false for NaN
-  SPEC_TAG(p, 4, SPEC_TRACE_TAG((use_k ? 1 : 0) | (use_p ? 2 : 0), row, k));
-  SPEC_TRACE_ONLY(trace_word(p.trace, 4, blockIdx.x, 9, __float_as_uint(tp)));
-  if (!use_k && !use_p) {
-    if (threadIdx.x == 0) p.thresh[row] = -INFINITY;
-    return;
-  }
-  const void* lrow = row_ptr<DT>(p.logits, row, p.V);
-  if (threadIdx.x == 0) s_fault = 0;
-  __syncthreads();
-  // The bins' range comes from a sample: one batch per thread, the threads' batches spread
-  // over the row.  The pass that follows counts and weighs every candidate into bins over
-  // that range (values outside it fall into the end bins) and finds the row's true maximum,
-  // minimum and count, and any NaN / +inf (which makes the row invalid for the verifier,
-  // and then no threshold is needed) on the way.
-  const long step = (long)kTB * kVec * kU;
-  const long iters = (p.V + step - 1) / step;
-  {
-    float sm = -INFINITY, smn = INFINITY;
-    const long e0 = (long)threadIdx.x * kVec + (long)(threadIdx.x % iters) * step;
-    if (e0 < p.V) {
-      float s[kU][8];
-      unsigned ok[kU];
-      cand_batch<DT, VEC>(p, lrow, row, e0, (long)kTB * kVec, s, ok);
+// An empty asm hides a value from the compiler.
+__device__ __forceinline__ float opaque(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// v[j] for a lane-varying j in [0, 8), by a select tree (no branch, no indexed registers:
+// the values are hidden from the compiler first, which would otherwise turn the tree back
+// into an indexed load from a stack copy of v).
+__device__ __forceinline__ float pick8(const float (&v)[8], int j) {
+  const bool b0 = j & 1, b1 = j & 2, b2 = j & 4;
+  float x[8];
 #pragma unroll
-      for (int u = 0; u < kU; ++u)
+  for (int i = 0; i < 8; ++i) x[i] = opaque(v[i]);
+  const float a0 = b0 ? x[1] : x[0], a1 = b0 ? x[3] : x[2], a2 = b0 ? x[5] : x[4], a3 = b0 ? x[7] : x[6];
+  const float c0 = b1 ? a1 : a0, c1 = b1 ? a3 : a2;
+  return b2 ? c1 : c0;
+}
+
+// Inclusive prefix sum of an int over the lanes of a wave (lanes that do not run add 0).
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  v += dpp_i<0x111>(0, v);        // row_shr:1
+  v += dpp_i<0x112>(0, v);        // row_shr:2
+  v += dpp_i<0x114>(0, v);        // row_shr:4
+  v += dpp_i<0x118>(0, v);        // row_shr:8
+  v += dpp_i<0x142, 0xa>(0, v);   // row_bcast:15 into rows 1, 3
+  v += dpp_i<0x143, 0xc>(0, v);   // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// The window path.  It wants the top 2k candidates (at least k + 256) for top-k (top-p then
+// works among the top-k survivors), or the largest window (about 3300) for top-p alone, and
+// from the sample (each thread's batch smp at smp_e0) takes t_lo, a value with about that
+// many candidates above it in the row.  One pass collects every candidate at or above t_lo,
+// with its weight, into LDS (wave-aggregated appends) and keeps only the count and weight of
+// the rest.  The thresholds are then resolved over the window exactly as the full path
+// resolves them over the row (bins, then the deciding bin's candidates), and the window is
+// used only when it provably holds them: at least k candidates for top-k, the target mass
+// reached inside it for top-p.  Returns false -- the full path then runs -- when the window
+// cannot hold 2k, overflows, or misses.  On true, *tau_out is the row's threshold (-inf for
+// a faulty row or no candidates).
+template <int DT, bool VEC>
+__device__ bool window_select(const ThreshParams& p, const void* lrow, size_t row, int k, float tp, bool use_k,
+                              bool use_p, const float (&smp)[kU][8], const unsigned (&smp_ok)[kU], long smp_e0,
+                              float SM, float SMN, WinLds& W, Collected& C1, Collected& C2, double* s_scratch,
+                              float* s_m, float* s_mn, int* s_fault, int* s_d, double* s_f, float* tau_out) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+  const float ref = SM;                 // the weights' reference value
+  const long stride = (long)kTB * kVec, step = stride * kU;
+  // 1. the sample's counts in bins linear over [SMN, SM]
+  const float sscale = static_cast<float>(kWinBins) / (SM - SMN);
+  if (!(isfinite(sscale) && sscale > 0.0f)) return false;
+  auto sbin = [&](float v) {
+    return static_cast<int>(fminf(fmaxf((v - SMN) * sscale, 0.0f), static_cast<float>(kWinBins - 1)));
+  };
+  const bool p_alone = use_p && !use_k;
+  for (int j = tid; j < kWinBins; j += kTB) W.cnt[j] = 0u;
+  __syncthreads();
+  int npos = 0;                         // sampled positions inside the row
+#pragma unroll
+  for (int u = 0; u < kU; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (smp_e0 + u * stride + e < p.V) ++npos;
+      if ((smp_ok[u] >> e) & 1u) atomicAdd(&W.cnt[sbin(smp[u][e])], 1u);
+    }
+  const double S_pos = block_sum_d(static_cast<double>(npos), s_scratch);   // (its barriers end the adds)
+  double fa;
+  // 2. candidates wanted from the top of the row: for top-k, 2k (at least k + 256); for
+  //    top-p alone the largest window, since an estimate of the nucleus from the sample rests
+  //    on the few sampled values that carry its mass and errs either way by large factors
+  //    (a window that misses is detected after the pass and falls back)
+  const double room = 0.8 * kWinCap;
+  const double want = p_alone ? room : fmax(2.0 * k, k + 256.0);
+  if (!(want <= room)) return false;
+  // 3. t_lo: the lower edge of the sample bin where the sample's count from the top reaches
+  //    want scaled to the sample (every candidate when the sample has fewer)
+  {
+    auto scnt = [&](int d) { return d >= 0 ? (double)W.cnt[d] : 0.0; };
+    const double r = fmax(1.0, ceil(want * S_pos / (double)p.V));
+    const int bw = find_bin<decltype(scnt), kWinBins>(scnt, 0.0, r, s_scratch, s_d, s_f, &fa);
+    const float t_lo = bw <= 0 ? -INFINITY : SMN + static_cast<float>(bw) / sscale;
+    // 4. the pass: the window into LDS, the rest counted and weighed in registers
+    if (tid == 0) W.n = 0;
+    __syncthreads();
+    SPEC_STAMP(p, 4, 2);   // window chosen
+    float m = -INFINITY, mn = INFINITY;
+    unsigned cnt = 0u;
+    double low_mass = 0.0;
+    bool fault = false;
+    // wave-uniform trip count: a lane past the row end loads nothing it uses (cand_batch
+    // marks no candidate there)
+    for (long base = (long)wave * kWave * kVec; base < p.V; base += step) {
+      const long e0 = base + (long)lane * kVec;
+      float sv[kU][8];
+      unsigned ok[kU];
+      cand_batch<DT, VEC>(p, lrow, row, e0, stride, sv, ok);
+      unsigned hit = 0u;                 // bit 8u + e: element e of vector u joins the window
+      float lw = 0.0f;                   // this batch's weights below the window (fp32 partial)
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
+          fault |= !(sv[u][e] < INFINITY);   // NaN or +inf; positions past the row read as -inf
           const bool c = (ok[u] >> e) & 1u;
-          sm = fmaxf(sm, c ? s[u][e] : -INFINITY);
-          smn = fminf(smn, c ? s[u][e] : INFINITY);
+          m = fmaxf(m, c ? sv[u][e] : -INFINITY);
+          mn = fminf(mn, c ? sv[u][e] : INFINITY);
+          const bool in = c && sv[u][e] >= t_lo;
+          hit |= (in ? 1u : 0u) << (8 * u + e);
+          if (p_alone && c && !in) lw += __builtin_amdgcn_exp2f((sv[u][e] - ref) * p.c2);
         }
+        cnt += __popc(ok[u]);
+      }
+      if (p_alone) low_mass += (double)lw;
+      const int mine = __popc(hit);
+      if (__ballot(mine > 0)) {
+        const int incl = wave_incl_scan_i(mine);
+        int at = 0;
+        if (lane == kWave - 1) at = atomicAdd(&W.n, incl);
+        at = __builtin_amdgcn_readlane(at, kWave - 1) + incl - mine;
+        // the lanes' few hits (usually none or one per lane), each value picked out of its
+        // vector by a select tree rather than one branch per position
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          unsigned h = (hit >> (8 * u)) & 0xffu;
+          while (h) {
+            const int j = __builtin_ctz(h);
+            h &= h - 1u;
+            const float v = pick8(sv[u], j);
+            if (at < kWinCap) {
+              W.v[at] = v;
+              W.w[at] = use_p ? __builtin_amdgcn_exp2f((v - ref) * p.c2) : 1.0f;
+            }
+            ++at;
+          }
+        }
+      }
     }
-    const float wm = wave_max(sm), wmn = -wave_max(-smn);
+    if (fault) *s_fault = 1;
+    const float wm = wave_max(m), wmn = -wave_max(-mn);
+    const double wc = wave_sum_d(static_cast<double>(cnt));
     if (lane == 0) {
       s_m[wave] = wm;
       s_mn[wave] = wmn;
+      s_scratch[wave] = wc;
     }
-  }
-  __syncthreads();
-  float SM = -INFINITY, SMN = INFINITY;
+    __syncthreads();
+    float M = -INFINITY, MN = INFINITY;
+    double C = 0.0;
 #pragma unroll
-  for (int w = 0; w < kTW; ++w) {
-    SM = fmaxf(SM, s_m[w]);
-    SMN = fminf(SMN, s_mn[w]);
+    for (int w = 0; w < kTW; ++w) {
+      M = fmaxf(M, s_m[w]);
+      MN = fminf(MN, s_mn[w]);
+      C += s_scratch[w];
+    }
+    const int n = W.n;
+    __syncthreads();
+    SPEC_STAMP(p, 4, 3);   // window pass done
+    const double W_low = p_alone ? block_sum_d(low_mass, s_scratch) : 0.0;
+    if (*s_fault || C <= 0.0) {         // the verifier reports the row; no threshold is needed
+      *tau_out = -INFINITY;
+      return true;
+    }
+    const bool sel_k = use_k && (double)k < C;
+    if (M == MN) {                      // one distinct value: it is kept whatever k and p are
+      *tau_out = M;
+      return true;
+    }
+    if (n > kWinCap || (sel_k && n < k) || !((M - ref) * p.c2 < 64.0f)) return false;
+    // 5. bins linear over the window [wlo, M]: counts and weights
+    float lo_v = INFINITY;
+    for (int j = tid; j < n; j += kTB) lo_v = fminf(lo_v, W.v[j]);
+    const float wlo_w = -wave_max(-lo_v);
+    if (lane == 0) s_mn[wave] = wlo_w;
+    __syncthreads();
+    float wlo = INFINITY;
+#pragma unroll
+    for (int w = 0; w < kTW; ++w) wlo = fminf(wlo, s_mn[w]);
+    const float wscale = static_cast<float>(kWinBins) / (M - wlo);
+    if (!(n > 0 && M > wlo && isfinite(wscale) && wscale > 0.0f)) return false;
+    auto wbin = [&](float v) {
+      return static_cast<int>(fminf(fmaxf((v - wlo) * wscale, 0.0f), static_cast<float>(kWinBins - 1)));
+    };
+    for (int j = tid; j < kWinBins; j += kTB) {
+      W.cnt[j] = 0u;
+      W.mass[j] = 0.0;
+    }
+    __syncthreads();
+    for (int j = tid; j < n; j += kTB) {
+      const int d = wbin(W.v[j]);
+      atomicAdd(&W.cnt[d], 1u);
+      if (use_p) atomicAdd(&W.mass[d], (double)W.w[j]);
+    }
+    __syncthreads();
+    SPEC_STAMP(p, 4, 4);   // window binned
+    // the candidates of window bin d into L (n_d of them; false if more than kCap)
+    auto gather = [&](int d, Collected& L) -> int {
+      if (tid == 0) L.n = 0;
+      __syncthreads();
+      for (int j = tid; j < n; j += kTB) {
+        if (wbin(W.v[j]) != d) continue;
+        const int i = atomicAdd(&L.n, 1);
+        if (i < kCap) {
+          L.v[i] = W.v[j];
+          L.w[i] = (double)W.w[j];
+        }
+      }
+      __syncthreads();
+      const int nd = L.n;
+      __syncthreads();
+      return nd;
+    };
+    float tau = -INFINITY, tau_k = -INFINITY;
+    int dk = -1, nk = 0;
+    if (sel_k) {
+      double fk = 0.0;
+      auto wcnt = [&](int d) { return d >= 0 ? (double)W.cnt[d] : 0.0; };
+      dk = find_bin<decltype(wcnt), kWinBins>(wcnt, 0.0, (double)k, s_scratch, s_d, s_f, &fk);
+      if (dk < 0) return false;
+      nk = gather(dk, C1);
+      if (nk > kCap) return false;
+      tau_k = resolve(C1, nk, -INFINITY, false, fk, (double)k, s_m);
+      tau = tau_k;
+    }
+    SPEC_STAMP(p, 4, 5);   // top-k resolved
+    if (use_p) {
+      // survivors of top-k: every window candidate above bin dk and those of bin dk at or
+      // above tau_k; without top-k every candidate, those below the window too
+      double part = 0.0;
+      if (sel_k)
+        for (int i = tid; i < nk; i += kTB)
+          if (C1.v[i] >= tau_k) part += C1.w[i];
+      part = block_sum_d(part, s_scratch);
+      auto valp = [&](int d) -> double {
+        if (d < 0 || (sel_k && d < dk)) return 0.0;
+        return (sel_k && d == dk) ? part : W.mass[d];
+      };
+      double t = 0.0;
+      for (int d = tid; d < kWinBins; d += kTB) t += valp(d);
+      const double total = block_sum_d(t, s_scratch) + W_low;
+      const double target = (double)tp * total;
+      double fp = 0.0;
+      const int dp = find_bin<decltype(valp), kWinBins>(valp, 0.0, target, s_scratch, s_d, s_f, &fp);
+      if (dp < 0) return false;         // the target mass lies below the window
+      if (sel_k && dp == dk) {
+        tau = resolve(C1, nk, tau_k, true, fp, target, s_m);
+      } else {
+        const int np = gather(dp, C2);
+        if (np > kCap) return false;
+        tau = resolve(C2, np, -INFINITY, true, fp, target, s_m);
+      }
+    }
+    SPEC_STAMP(p, 4, 6);   // top-p resolved
+    *tau_out = tau;
+    return true;
   }
-  __syncthreads();
+}
+
+// The full path: bins over the value range near the top of the row, counted and weighed in
+// one pass, the deciding bins' candidates collected in another, and radix selection for
+// rows the bins cannot decide.  The window path's fallback; kept out of line so that its
+// registers do not add to the window path's.
+template <int DT, bool VEC>
+__attribute__((noinline)) __device__ float full_select(const ThreshParams p, const void* lrow, size_t row, int k,
+                                                       float tp, bool use_k, bool use_p, float SM, float SMN,
+                                                       SelectLds& s_sel, Collected& s_col, Collected& s_col2,
+                                                       double* s_scratch, float* s_m, float* s_mn, int* s_fault_p,
+                                                       int* s_d_p, double* s_f_p) {
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const long step = (long)kTB * kVec * kU;
+  const float ref = SM;                 // the weights' reference value
+  int& s_fault = *s_fault_p;
+  int& s_d = *s_d_p;
+  double& s_f = *s_f_p;
+  float tau = -INFINITY;
   // Only values near the top can hold a threshold: the bins cover [lo, SM] with lo the
   // sample's minimum or, if higher, the cut SM - cut / c2, below which a weight is under
   // 2^-cut.  Top-p keeps a set whose mass reaches p of the total, and the candidates below
@@ -503,7 +736,6 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
   // (top-1 keeps the maximum's ties whatever top-p is: no bins needed)
   const bool binned = !(use_k && k == 1) && SM > vb.lo && isfinite(SM - vb.lo) && isfinite(vb.scale) &&
                       vb.scale > 0.0f;
-  const float ref = SM;                 // the weights' reference value
   BinLds& L = s_sel.bins;
   if (binned) {
     for (int j = threadIdx.x; j < kBins; j += kTB) {
@@ -564,7 +796,6 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
   const double W_low = use_p ? block_sum_d(low_mass, s_scratch) : 0.0;
   SPEC_STAMP(p, 4, 2);   // sample and fused pass done
   SPEC_STAMP(p, 4, 3);
-  float tau = -INFINITY;
   if (!s_fault && C > 0.0) {
     const bool sel_k = use_k && (double)k < C;
     // the radix fallback's fixed point: the largest scale that keeps every sum of weights
@@ -663,6 +894,83 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
       }
     }
   }
+  return tau;
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(ThreshParams p) {
+  __shared__ double s_scratch[kTW];
+  __shared__ SelectLds s_sel;
+  __shared__ Collected s_col, s_col2;
+  __shared__ float s_m[kTW], s_mn[kTW];
+  __shared__ int s_fault, s_d;
+  __shared__ double s_f;
+  const size_t row = blockIdx.x;
+  SPEC_STAMP(p, 4, 1);
+  const int b = static_cast<int>(row / p.R);
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const int k = p.top_k ? p.top_k[b] : 0;
+  const float tp = p.top_p ? p.top_p[b] : 1.0f;
+  const bool use_k = k >= 1, use_p = tp > 0.0f && tp < 1.0f;   // false for NaN
+  SPEC_TAG(p, 4, SPEC_TRACE_TAG((use_k ? 1 : 0) | (use_p ? 2 : 0), row, k));
+  SPEC_TRACE_ONLY(trace_word(p.trace, 4, blockIdx.x, 9, __float_as_uint(tp)));
+  if (!use_k && !use_p) {
+    if (threadIdx.x == 0) p.thresh[row] = -INFINITY;
+    return;
+  }
+  const void* lrow = row_ptr<DT>(p.logits, row, p.V);
+  if (threadIdx.x == 0) s_fault = 0;
+  __syncthreads();
+  // The bins' range comes from a sample: one batch per thread, the threads' batches spread
+  // over the row.  The pass that follows counts and weighs every candidate into bins over
+  // that range (values outside it fall into the end bins) and finds the row's true maximum,
+  // minimum and count, and any NaN / +inf (which makes the row invalid for the verifier,
+  // and then no threshold is needed) on the way.
+  const long step = (long)kTB * kVec * kU;
+  const long iters = (p.V + step - 1) / step;
+  // this thread's sample batch, kept for the window path's estimate
+  const long smp_e0 = (long)threadIdx.x * kVec + (long)(threadIdx.x % iters) * step;
+  float smp[kU][8];
+  unsigned smp_ok[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) smp_ok[u] = 0u;
+  {
+    float sm = -INFINITY, smn = INFINITY;
+    if (smp_e0 < p.V) {
+      cand_batch<DT, VEC>(p, lrow, row, smp_e0, (long)kTB * kVec, smp, smp_ok);
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool c = (smp_ok[u] >> e) & 1u;
+          sm = fmaxf(sm, c ? smp[u][e] : -INFINITY);
+          smn = fminf(smn, c ? smp[u][e] : INFINITY);
+        }
+    }
+    const float wm = wave_max(sm), wmn = -wave_max(-smn);
+    if (lane == 0) {
+      s_m[wave] = wm;
+      s_mn[wave] = wmn;
+    }
+  }
+  __syncthreads();
+  float SM = -INFINITY, SMN = INFINITY;
+#pragma unroll
+  for (int w = 0; w < kTW; ++w) {
+    SM = fmaxf(SM, s_m[w]);
+    SMN = fminf(SMN, s_mn[w]);
+  }
+  __syncthreads();
+  float tau = -INFINITY;
+  bool decided = false;
+  const bool windowed = !(use_k && k == 1) && SM > SMN && isfinite(SM - SMN);
+  if (windowed)
+    decided = window_select<DT, VEC>(p, lrow, row, k, tp, use_k, use_p, smp, smp_ok, smp_e0, SM, SMN, s_sel.win,
+                                     s_col, s_col2, s_scratch, s_m, s_mn, &s_fault, &s_d, &s_f, &tau);
+  SPEC_TRACE_ONLY(if (windowed && !decided) trace_word(p.trace, 4, blockIdx.x, 11, 2ull));   // window fell back
+  if (!decided)
+    tau = full_select<DT, VEC>(p, lrow, row, k, tp, use_k, use_p, SM, SMN, s_sel, s_col, s_col2, s_scratch, s_m,
+                               s_mn, &s_fault, &s_d, &s_f);
   if (threadIdx.x == 0) p.thresh[row] = tau;
   SPEC_STAMP(p, 4, 7);
 }

@@ -231,3 +231,19 @@ def test_top_p_boundaries_just_outside_the_flag_window(dt, V, T):
     assert not pflag.any(), "a boundary placed outside the window was flagged"
     s = compare_chain(got, exp, max_flag_frac=0.1)
     print(s)
+
+
+@pytest.mark.parametrize("sigma,k,tp", [(0.1, 0, 0.9), (3.0, 0, 0.9), (2.0, 1600, 1.0), (2.0, 1700, 1.0),
+                                        (0.1, 3000, 0.5)])
+def test_threshold_window_and_full_paths(sigma, k, tp):
+    """The threshold pass decides most rows from a window of the top candidates collected in
+    one pass, and falls back to the full path when the window cannot hold the selection: k
+    above about 1600 (k = 1700 here; 1600 still fits), or a top-p nucleus larger than the
+    window (near-flat rows, sigma = 0.1, where p = 0.9 keeps most of the row; the window misses
+    and the row takes the full path).  Every case must equal the oracle."""
+    x = synth.make_chain(16, 2, 50000, seed=int(sigma * 100) + k + int(tp * 10), logit_dtype="bf16", sigma=sigma,
+                         noise=0.5, temperature=1.0)
+    kk = np.full(x.B, k, np.int32)
+    pp = np.full(x.B, tp, np.float32)
+    say(f"chain_ex threshold paths sigma={sigma} k={k} p={tp}")
+    check(x, None, None, kk, pp)
