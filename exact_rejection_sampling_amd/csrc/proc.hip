@@ -154,6 +154,150 @@ constexpr int kDigit = 12;
 constexpr int kBins = 1 << kDigit;
 constexpr int kBinsPerThread = kBins / kTB;
 
+// ------------------------------------------------------------------ lean streaming passes
+// One thread's kU vectors of a batch lying wholly inside the row, loaded and not yet used:
+// the logits (one 16-byte vector per 8 bf16, two per 8 fp32), the bias and the mask word.
+template <int DT>
+struct RawBatch {
+  u32x4 l[kU][DT == kBF16 ? 1 : 2];
+  f32x4 b[kU][2];
+  unsigned m[kU];
+};
+
+// The loads of the batch at row position eb + lane * 8 (eb, a multiple of 32, is uniform over
+// the wave): addresses are a uniform base plus a 32-bit lane offset, so that no load needs a
+// 64-bit address register of its own.
+template <int DT, bool BIAS, bool MASK>
+__device__ __forceinline__ void load_raw(const ThreshParams& p, const void* lrow, size_t row, long eb, unsigned lane,
+                                         long stride, RawBatch<DT>& r) {
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const long e = eb + u * stride;
+    if constexpr (DT == kBF16) {
+      r.l[u][0] = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(lrow) + e)[lane];
+    } else {
+      const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const float*>(lrow) + e);
+      r.l[u][0] = q[2 * lane];
+      r.l[u][1] = q[2 * lane + 1];
+    }
+    if constexpr (BIAS) {
+      const f32x4* q = reinterpret_cast<const f32x4*>(p.bias + e);
+      r.b[u][0] = q[2 * lane];
+      r.b[u][1] = q[2 * lane + 1];
+    }
+    if constexpr (MASK) r.m[u] = (p.allowed + row * p.W + (e >> 5))[lane >> 2];
+  }
+}
+
+// s = l + b of a loaded batch, and each vector's 8 allowed bits (all set without a mask).
+// Nothing is tested here: NaN, +inf and masked tokens keep their values.
+template <int DT, bool BIAS, bool MASK>
+__device__ __forceinline__ void unpack_raw(const RawBatch<DT>& r, long e0, float (&s)[kU][8], unsigned (&al)[kU]) {
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    if constexpr (DT == kBF16) {
+      const u32x4 w = r.l[u][0];
+      s[u][0] = __uint_as_float(w.x << 16); s[u][1] = __uint_as_float(w.x & 0xffff0000u);
+      s[u][2] = __uint_as_float(w.y << 16); s[u][3] = __uint_as_float(w.y & 0xffff0000u);
+      s[u][4] = __uint_as_float(w.z << 16); s[u][5] = __uint_as_float(w.z & 0xffff0000u);
+      s[u][6] = __uint_as_float(w.w << 16); s[u][7] = __uint_as_float(w.w & 0xffff0000u);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        s[u][4 * h + 0] = __uint_as_float(r.l[u][h].x); s[u][4 * h + 1] = __uint_as_float(r.l[u][h].y);
+        s[u][4 * h + 2] = __uint_as_float(r.l[u][h].z); s[u][4 * h + 3] = __uint_as_float(r.l[u][h].w);
+      }
+    }
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        s[u][4 * h + 0] += r.b[u][h].x; s[u][4 * h + 1] += r.b[u][h].y;
+        s[u][4 * h + 2] += r.b[u][h].z; s[u][4 * h + 3] += r.b[u][h].w;
+      }
+    }
+    // e0 is a multiple of 8 and the vectors of a batch lie a multiple of 32 apart, so every
+    // vector's 8 bits sit at the same place in its mask word
+    al[u] = MASK ? (r.m[u] >> (e0 & 31)) & 0xffu : 0xffu;
+  }
+}
+
+// v when bit j of the allowed bits is set, else -inf (two bit operations, no compare).
+__device__ __forceinline__ float masked_value(float v, unsigned al, int j) {
+  const unsigned t = static_cast<unsigned>(static_cast<int>(al << (31 - j)) >> 31);   // all ones if allowed
+  return __uint_as_float((__float_as_uint(v) & t) | (0xff800000u & ~t));
+}
+
+// Streams the row once, wave w taking the batches at w * 512 + i * kTB * kU * 8.  Batches
+// wholly inside the row go to fast(s, al, e0) -- s = l + b untested, al the allowed bits --
+// from a ring of NBUF register buffers, each reloaded with the batch NBUF ahead as soon as it
+// has been used, so that NBUF - 1 batches stay in flight while one is used; the rest go to
+// slow(s, ok, e0) with cand_batch's candidate bits.
+template <int DT, bool VEC, bool BIAS, bool MASK, int NBUF, class Fast, class Slow>
+__device__ __forceinline__ void row_pass(const ThreshParams& p, const void* lrow, size_t row, Fast&& fast, Slow&& slow) {
+  static_assert(NBUF >= 2, "at least one batch in flight");
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const unsigned ulane = static_cast<unsigned>(lane);
+  const long stride = (long)kTB * kVec, step = stride * kU;
+  long base = (long)wave * kWave * kVec;
+  // a batch at `base` is wholly inside the row when base <= last_fast (uniform over the wave)
+  const long last_fast = VEC ? (long)p.V - ((kWave - 1) * kVec + (kU - 1) * stride + kVec) : -1;
+  // nf batches wholly inside the row, at base + t * step; the main loop takes NBUF of them per
+  // trip with no exit in between (every trip runs the same straight line, so the compiler's
+  // waits are exact), and the last nf mod NBUF follow it
+  const int nf = base <= last_fast ? static_cast<int>((last_fast - base) / step) + 1 : 0;
+  if (nf > 0) {
+    const long first = base;
+    // Rows start their walk at different batches (the shared bias row is read at different
+    // places at once rather than every block on the same lines), and loads past the last
+    // batch re-read it, which stays in bounds.
+    const int rot = static_cast<int>((row * 7) % static_cast<size_t>(nf));
+    auto pos = [&](int t) {
+      int i = min(t, nf - 1) + rot;
+      i = i >= nf ? i - nf : i;
+      return first + static_cast<long>(i) * step;
+    };
+    RawBatch<DT> buf[NBUF];
+    float s[kU][8];
+    unsigned al[kU];
+#pragma unroll
+    for (int i = 0; i < NBUF; ++i) load_raw<DT, BIAS, MASK>(p, lrow, row, pos(i), ulane, stride, buf[i]);
+    int t = 0;
+    for (; t + NBUF <= nf; t += NBUF) {
+#pragma unroll
+      for (int i = 0; i < NBUF; ++i) {
+        const long e0 = pos(t + i) + lane * kVec;
+        unpack_raw<DT, BIAS, MASK>(buf[i], e0, s, al);
+        fast(s, al, e0);
+        // the buffer just used takes the batch NBUF ahead
+        load_raw<DT, BIAS, MASK>(p, lrow, row, pos(t + i + NBUF), ulane, stride, buf[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NBUF; ++i) {
+      if (t + i < nf) {
+        const long e0 = pos(t + i) + lane * kVec;
+        unpack_raw<DT, BIAS, MASK>(buf[i], e0, s, al);
+        fast(s, al, e0);
+      }
+    }
+    base = first + static_cast<long>(nf) * step;
+  }
+  for (; base < p.V; base += step) {
+    float s[kU][8];
+    unsigned ok[kU];
+    cand_batch<DT, VEC>(p, lrow, row, base + lane * kVec, stride, s, ok);
+    slow(s, ok, base + lane * kVec);
+  }
+}
+
+// Batches in flight per wave in the window pass and in the top-1 pass.
+#ifndef SPEC_THRESH_NBUF_WIN
+#define SPEC_THRESH_NBUF_WIN 2
+#endif
+#ifndef SPEC_THRESH_NBUF_TOP1
+#define SPEC_THRESH_NBUF_TOP1 3
+#endif
+
 struct RadixLds {
   unsigned long long bin[kBins];        // counts, or masses in fixed point
   double scan[kTW];
@@ -475,6 +619,116 @@ __device__ __forceinline__ int wave_incl_scan_i(int v) {
   return v;
 }
 
+// The window path's pass over the row: every candidate with s >= t_cmp (t_cmp finite, so -inf
+// and NaN never qualify) is appended to the window with its weight (1 without top-p); with
+// PALONE, the weights of the allowed tokens below t_cmp are summed into *low.  A NaN or +inf
+// anywhere in the row sets *fault.  Per element the fast batches spend the bf16 unpack, the
+// bias add, one class test and one compare (with PALONE also the mask applied to the value,
+// and the weight): the mask is applied to a vector's 8 hit bits at once.
+template <int DT, bool VEC, bool BIAS, bool MASK, bool PALONE>
+__device__ __forceinline__ void window_pass(const ThreshParams& p, const void* lrow, size_t row, float t_cmp, float ref,
+                                            bool use_p, WinLds& W, bool* fault_out, double* low_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  // weights 2^(s c2 - fp32(ref c2)): the rounding of ref c2 scales every weight of the row
+  // alike, so it cancels in every mass ratio; one fma per weight
+  const float c2 = p.c2, rc2 = ref * c2;
+  bool fault = false;
+  double low_mass = 0.0;
+  // this thread's hits (bit 8u + j: element j of vector u) appended to the window, the
+  // wave's places taken with one LDS atomic
+  auto append = [&](const float (&s)[kU][8], unsigned hit) {
+    const int mine = __popc(hit);
+    if (!__ballot(mine > 0)) return;
+    const int incl = wave_incl_scan_i(mine);
+    int at = 0;
+    if (lane == kWave - 1) at = atomicAdd(&W.n, incl);
+    at = __builtin_amdgcn_readlane(at, kWave - 1) + incl - mine;
+    // the lanes' few hits (usually none or one per lane), each value picked out of its
+    // vector by a select tree rather than one branch per position
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      unsigned h = (hit >> (8 * u)) & 0xffu;
+      while (h) {
+        const int j = __builtin_ctz(h);
+        h &= h - 1u;
+        const float v = pick8(s[u], j);
+        if (at < kWinCap) {
+          W.v[at] = v;
+          W.w[at] = use_p ? __builtin_amdgcn_exp2f(fmaf(v, c2, -rc2)) : 1.0f;
+        }
+        ++at;
+      }
+    }
+  };
+  row_pass<DT, VEC, BIAS, MASK, SPEC_THRESH_NBUF_WIN>(
+      p, lrow, row,
+      [&](const float (&s)[kU][8], const unsigned (&al)[kU], long) {
+        unsigned hit = 0u;
+        float lw = 0.0f;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          unsigned hb = 0u;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            fault |= !(s[u][j] < INFINITY);   // NaN or +inf, masked or not
+            if constexpr (PALONE) {
+              const float v = MASK ? masked_value(s[u][j], al[u], j) : s[u][j];
+              const bool in = v >= t_cmp;
+              hb |= (in ? 1u : 0u) << j;
+              lw += in ? 0.0f : __builtin_amdgcn_exp2f(fmaf(v, c2, -rc2));   // 0 for -inf
+            } else {
+              hb |= (s[u][j] >= t_cmp ? 1u : 0u) << j;
+            }
+          }
+          if constexpr (!PALONE && MASK) hb &= al[u];
+          hit |= hb << (8 * u);
+        }
+        if constexpr (PALONE) low_mass += (double)lw;
+        append(s, hit);
+      },
+      [&](const float (&s)[kU][8], const unsigned (&ok)[kU], long) {
+        unsigned hit = 0u;
+        float lw = 0.0f;
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            fault |= !(s[u][j] < INFINITY);   // positions past the row read as -inf
+            const bool c = (ok[u] >> j) & 1u;
+            const bool in = c && s[u][j] >= t_cmp;
+            hit |= (in ? 1u : 0u) << (8 * u + j);
+            if (PALONE && c && !in) lw += __builtin_amdgcn_exp2f(fmaf(s[u][j], c2, -rc2));
+          }
+        if constexpr (PALONE) low_mass += (double)lw;
+        append(s, hit);
+      });
+  *fault_out = fault;
+  *low_out = low_mass;
+}
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void window_pass_any(const ThreshParams& p, const void* lrow, size_t row, float t_cmp,
+                                                float ref, bool use_p, bool p_alone, WinLds& W, bool* fault,
+                                                double* low) {
+  if (p.bias) {
+    if (p.allowed) {
+      if (p_alone) window_pass<DT, VEC, true, true, true>(p, lrow, row, t_cmp, ref, use_p, W, fault, low);
+      else window_pass<DT, VEC, true, true, false>(p, lrow, row, t_cmp, ref, use_p, W, fault, low);
+    } else {
+      if (p_alone) window_pass<DT, VEC, true, false, true>(p, lrow, row, t_cmp, ref, use_p, W, fault, low);
+      else window_pass<DT, VEC, true, false, false>(p, lrow, row, t_cmp, ref, use_p, W, fault, low);
+    }
+  } else {
+    if (p.allowed) {
+      if (p_alone) window_pass<DT, VEC, false, true, true>(p, lrow, row, t_cmp, ref, use_p, W, fault, low);
+      else window_pass<DT, VEC, false, true, false>(p, lrow, row, t_cmp, ref, use_p, W, fault, low);
+    } else {
+      if (p_alone) window_pass<DT, VEC, false, false, true>(p, lrow, row, t_cmp, ref, use_p, W, fault, low);
+      else window_pass<DT, VEC, false, false, false>(p, lrow, row, t_cmp, ref, use_p, W, fault, low);
+    }
+  }
+}
+
 // The window path.  It wants the top 2k candidates (at least k + 256) for top-k (top-p then
 // works among the top-k survivors), or the largest window (about 3300) for top-p alone, and
 // from the sample (each thread's batch smp at smp_e0) takes t_lo, a value with about that
@@ -487,13 +741,12 @@ __device__ __forceinline__ int wave_incl_scan_i(int v) {
 // cannot hold 2k, overflows, or misses.  On true, *tau_out is the row's threshold (-inf for
 // a faulty row or no candidates).
 template <int DT, bool VEC>
-__device__ bool window_select(const ThreshParams& p, const void* lrow, size_t row, int k, float tp, bool use_k,
+__device__ __forceinline__ bool window_select(const ThreshParams& p, const void* lrow, size_t row, int k, float tp, bool use_k,
                               bool use_p, const float (&smp)[kU][8], const unsigned (&smp_ok)[kU], long smp_e0,
-                              float SM, float SMN, WinLds& W, Collected& C1, Collected& C2, double* s_scratch,
+                              long smp_stride, float SM, float SMN, WinLds& W, Collected& C1, Collected& C2, double* s_scratch,
                               float* s_m, float* s_mn, int* s_fault, int* s_d, double* s_f, float* tau_out) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   const float ref = SM;                 // the weights' reference value
-  const long stride = (long)kTB * kVec, step = stride * kU;
   // 1. the sample's counts in bins linear over [SMN, SM]
   const float sscale = static_cast<float>(kWinBins) / (SM - SMN);
   if (!(isfinite(sscale) && sscale > 0.0f)) return false;
@@ -508,7 +761,7 @@ __device__ bool window_select(const ThreshParams& p, const void* lrow, size_t ro
   for (int u = 0; u < kU; ++u)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if (smp_e0 + u * stride + e < p.V) ++npos;
+      if (smp_e0 + u * smp_stride + e < p.V) ++npos;
       if ((smp_ok[u] >> e) & 1u) atomicAdd(&W.cnt[sbin(smp[u][e])], 1u);
     }
   const double S_pos = block_sum_d(static_cast<double>(npos), s_scratch);   // (its barriers end the adds)
@@ -527,102 +780,55 @@ __device__ bool window_select(const ThreshParams& p, const void* lrow, size_t ro
     const double r = fmax(1.0, ceil(want * S_pos / (double)p.V));
     const int bw = find_bin<decltype(scnt), kWinBins>(scnt, 0.0, r, s_scratch, s_d, s_f, &fa);
     const float t_lo = bw <= 0 ? -INFINITY : SMN + static_cast<float>(bw) / sscale;
-    // 4. the pass: the window into LDS, the rest counted and weighed in registers
+    // 4. the pass: the window into LDS, the rest weighed in registers (top-p alone)
     if (tid == 0) W.n = 0;
     __syncthreads();
     SPEC_STAMP(p, 4, 2);   // window chosen
-    float m = -INFINITY, mn = INFINITY;
-    unsigned cnt = 0u;
-    double low_mass = 0.0;
     bool fault = false;
-    // wave-uniform trip count: a lane past the row end loads nothing it uses (cand_batch
-    // marks no candidate there)
-    for (long base = (long)wave * kWave * kVec; base < p.V; base += step) {
-      const long e0 = base + (long)lane * kVec;
-      float sv[kU][8];
-      unsigned ok[kU];
-      cand_batch<DT, VEC>(p, lrow, row, e0, stride, sv, ok);
-      unsigned hit = 0u;                 // bit 8u + e: element e of vector u joins the window
-      float lw = 0.0f;                   // this batch's weights below the window (fp32 partial)
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          fault |= !(sv[u][e] < INFINITY);   // NaN or +inf; positions past the row read as -inf
-          const bool c = (ok[u] >> e) & 1u;
-          m = fmaxf(m, c ? sv[u][e] : -INFINITY);
-          mn = fminf(mn, c ? sv[u][e] : INFINITY);
-          const bool in = c && sv[u][e] >= t_lo;
-          hit |= (in ? 1u : 0u) << (8 * u + e);
-          if (p_alone && c && !in) lw += __builtin_amdgcn_exp2f((sv[u][e] - ref) * p.c2);
-        }
-        cnt += __popc(ok[u]);
-      }
-      if (p_alone) low_mass += (double)lw;
-      const int mine = __popc(hit);
-      if (__ballot(mine > 0)) {
-        const int incl = wave_incl_scan_i(mine);
-        int at = 0;
-        if (lane == kWave - 1) at = atomicAdd(&W.n, incl);
-        at = __builtin_amdgcn_readlane(at, kWave - 1) + incl - mine;
-        // the lanes' few hits (usually none or one per lane), each value picked out of its
-        // vector by a select tree rather than one branch per position
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          unsigned h = (hit >> (8 * u)) & 0xffu;
-          while (h) {
-            const int j = __builtin_ctz(h);
-            h &= h - 1u;
-            const float v = pick8(sv[u], j);
-            if (at < kWinCap) {
-              W.v[at] = v;
-              W.w[at] = use_p ? __builtin_amdgcn_exp2f((v - ref) * p.c2) : 1.0f;
-            }
-            ++at;
-          }
-        }
-      }
-    }
+    double low_mass = 0.0;
+    window_pass_any<DT, VEC>(p, lrow, row, fmaxf(t_lo, -0x1.fffffep127f), ref, use_p, p_alone, W, &fault, &low_mass);
     if (fault) *s_fault = 1;
-    const float wm = wave_max(m), wmn = -wave_max(-mn);
-    const double wc = wave_sum_d(static_cast<double>(cnt));
-    if (lane == 0) {
-      s_m[wave] = wm;
-      s_mn[wave] = wmn;
-      s_scratch[wave] = wc;
-    }
     __syncthreads();
-    float M = -INFINITY, MN = INFINITY;
-    double C = 0.0;
-#pragma unroll
-    for (int w = 0; w < kTW; ++w) {
-      M = fmaxf(M, s_m[w]);
-      MN = fminf(MN, s_mn[w]);
-      C += s_scratch[w];
-    }
     const int n = W.n;
-    __syncthreads();
     SPEC_STAMP(p, 4, 3);   // window pass done
-    const double W_low = p_alone ? block_sum_d(low_mass, s_scratch) : 0.0;
-    if (*s_fault || C <= 0.0) {         // the verifier reports the row; no threshold is needed
+    const double W_low = p_alone ? block_sum_d(low_mass, s_scratch) : 0.0;   // (its barriers order n's read)
+    if (*s_fault) {                     // the verifier reports the row; no threshold is needed
       *tau_out = -INFINITY;
       return true;
     }
-    const bool sel_k = use_k && (double)k < C;
-    if (M == MN) {                      // one distinct value: it is kept whatever k and p are
-      *tau_out = M;
+    // With t_lo = -inf the window holds every candidate; otherwise the row may hold more.
+    const bool all_in = !(t_lo > -INFINITY);
+    if (n == 0) {
+      if (!all_in) return false;
+      *tau_out = -INFINITY;             // no candidate at all
       return true;
     }
-    if (n > kWinCap || (sel_k && n < k) || !((M - ref) * p.c2 < 64.0f)) return false;
-    // 5. bins linear over the window [wlo, M]: counts and weights
-    float lo_v = INFINITY;
-    for (int j = tid; j < n; j += kTB) lo_v = fminf(lo_v, W.v[j]);
-    const float wlo_w = -wave_max(-lo_v);
-    if (lane == 0) s_mn[wave] = wlo_w;
+    if (n > kWinCap) return false;
+    // top-k selects when the row has more than k candidates: known when the window holds them
+    // all; otherwise a window of at least k holds the top k (fewer: the full path decides)
+    if (use_k && !all_in && n < k) return false;
+    const bool sel_k = use_k && (!all_in || k < n);
+    // 5. bins linear over the window [wlo, M] (M, the row's largest candidate, is in it: the
+    //    window path runs only when the sample holds two distinct values, so t_lo <= SM <= M)
+    float lo_v = INFINITY, hi_v = -INFINITY;
+    for (int j = tid; j < n; j += kTB) {
+      lo_v = fminf(lo_v, W.v[j]);
+      hi_v = fmaxf(hi_v, W.v[j]);
+    }
+    const float wlo_w = -wave_max(-lo_v), whi_w = wave_max(hi_v);
+    if (lane == 0) {
+      s_mn[wave] = wlo_w;
+      s_m[wave] = whi_w;
+    }
     __syncthreads();
-    float wlo = INFINITY;
+    float wlo = INFINITY, M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kTW; ++w) wlo = fminf(wlo, s_mn[w]);
+    for (int w = 0; w < kTW; ++w) {
+      wlo = fminf(wlo, s_mn[w]);
+      M = fmaxf(M, s_m[w]);
+    }
+    __syncthreads();
+    if (!((M - ref) * p.c2 < 64.0f)) return false;
     const float wscale = static_cast<float>(kWinBins) / (M - wlo);
     if (!(n > 0 && M > wlo && isfinite(wscale) && wscale > 0.0f)) return false;
     auto wbin = [&](float v) {
@@ -897,6 +1103,60 @@ __attribute__((noinline)) __device__ float full_select(const ThreshParams p, con
   return tau;
 }
 
+// Top-1 keeps the row's largest candidate value and its ties, whatever top-p is: one pass
+// for the largest allowed value and any NaN / +inf.
+template <int DT, bool VEC, bool BIAS, bool MASK>
+__device__ __forceinline__ void top1_pass(const ThreshParams& p, const void* lrow, size_t row, float* m_out,
+                                          bool* fault_out) {
+  float m = -INFINITY;
+  bool fault = false;
+  row_pass<DT, VEC, BIAS, MASK, SPEC_THRESH_NBUF_TOP1>(
+      p, lrow, row,
+      [&](const float (&s)[kU][8], const unsigned (&al)[kU], long) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            fault |= !(s[u][j] < INFINITY);
+            m = fmaxf(m, MASK ? masked_value(s[u][j], al[u], j) : s[u][j]);
+          }
+      },
+      [&](const float (&s)[kU][8], const unsigned (&ok)[kU], long) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            fault |= !(s[u][j] < INFINITY);
+            m = fmaxf(m, ((ok[u] >> j) & 1u) ? s[u][j] : -INFINITY);
+          }
+      });
+  *m_out = m;
+  *fault_out = fault;
+}
+
+// The top-1 threshold: the largest candidate, or -inf for a faulty row or one without candidates.
+template <int DT, bool VEC>
+__device__ __forceinline__ float top1_select(const ThreshParams& p, const void* lrow, size_t row, float* s_m, int* s_fault) {
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  float m;
+  bool fault;
+  if (p.bias) {
+    if (p.allowed) top1_pass<DT, VEC, true, true>(p, lrow, row, &m, &fault);
+    else top1_pass<DT, VEC, true, false>(p, lrow, row, &m, &fault);
+  } else {
+    if (p.allowed) top1_pass<DT, VEC, false, true>(p, lrow, row, &m, &fault);
+    else top1_pass<DT, VEC, false, false>(p, lrow, row, &m, &fault);
+  }
+  if (fault) *s_fault = 1;
+  const float wm = wave_max(m);
+  if (lane == 0) s_m[wave] = wm;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kTW; ++w) M = fmaxf(M, s_m[w]);
+  return (*s_fault || !(M > -INFINITY)) ? -INFINITY : M;
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(ThreshParams p) {
   __shared__ double s_scratch[kTW];
@@ -909,6 +1169,22 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
   SPEC_STAMP(p, 4, 1);
   const int b = static_cast<int>(row / p.R);
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+  const void* lrow = row_ptr<DT>(p.logits, row, p.V);
+  // This thread's sample batch, for the window path's estimate, is read first, with the
+  // request's top-k and top-p in flight beside it: eight consecutive threads read one stretch
+  // of 64 tokens (whole 128-byte lines of bf16 logits), and the block's kTB / 8 * kU stretches
+  // are spread evenly over the row, at a row-dependent offset (so that the rows' reads of the
+  // shared bias row spread over its lines).  Rows that need no sample waste one batch.
+  const long stretches = (p.V + 63) / 64;
+  const long gap = max(1L, stretches / ((long)(kTB / 8) * kU));
+  const long smp_e0 =
+      ((long)(threadIdx.x >> 3) * gap + (long)(row % (size_t)gap)) * 64 + (long)(threadIdx.x & 7) * kVec;
+  const long smp_stride = (long)(kTB / 8) * gap * 64;
+  float smp[kU][8];
+  unsigned smp_ok[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) smp_ok[u] = 0u;
+  if (smp_e0 < p.V) cand_batch<DT, VEC>(p, lrow, row, smp_e0, smp_stride, smp, smp_ok);
   const int k = p.top_k ? p.top_k[b] : 0;
   const float tp = p.top_p ? p.top_p[b] : 1.0f;
   const bool use_k = k >= 1, use_p = tp > 0.0f && tp < 1.0f;   // false for NaN
@@ -918,35 +1194,26 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
     if (threadIdx.x == 0) p.thresh[row] = -INFINITY;
     return;
   }
-  const void* lrow = row_ptr<DT>(p.logits, row, p.V);
   if (threadIdx.x == 0) s_fault = 0;
   __syncthreads();
-  // The bins' range comes from a sample: one batch per thread, the threads' batches spread
-  // over the row.  The pass that follows counts and weighs every candidate into bins over
-  // that range (values outside it fall into the end bins) and finds the row's true maximum,
-  // minimum and count, and any NaN / +inf (which makes the row invalid for the verifier,
-  // and then no threshold is needed) on the way.
-  const long step = (long)kTB * kVec * kU;
-  const long iters = (p.V + step - 1) / step;
-  // this thread's sample batch, kept for the window path's estimate
-  const long smp_e0 = (long)threadIdx.x * kVec + (long)(threadIdx.x % iters) * step;
-  float smp[kU][8];
-  unsigned smp_ok[kU];
-#pragma unroll
-  for (int u = 0; u < kU; ++u) smp_ok[u] = 0u;
+  if (use_k && k == 1) {
+    const float t1 = top1_select<DT, VEC>(p, lrow, row, s_m, &s_fault);
+    if (threadIdx.x == 0) p.thresh[row] = t1;
+    SPEC_STAMP(p, 4, 7);
+    return;
+  }
+  // The sample's range [SMN, SM]: the window path's bins over the sample, or the full path's
+  // bins over the row (values outside it fall into the end bins).
   {
     float sm = -INFINITY, smn = INFINITY;
-    if (smp_e0 < p.V) {
-      cand_batch<DT, VEC>(p, lrow, row, smp_e0, (long)kTB * kVec, smp, smp_ok);
 #pragma unroll
-      for (int u = 0; u < kU; ++u)
+    for (int u = 0; u < kU; ++u)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool c = (smp_ok[u] >> e) & 1u;
-          sm = fmaxf(sm, c ? smp[u][e] : -INFINITY);
-          smn = fminf(smn, c ? smp[u][e] : INFINITY);
-        }
-    }
+      for (int e = 0; e < 8; ++e) {
+        const bool c = (smp_ok[u] >> e) & 1u;
+        sm = fmaxf(sm, c ? smp[u][e] : -INFINITY);
+        smn = fminf(smn, c ? smp[u][e] : INFINITY);
+      }
     const float wm = wave_max(sm), wmn = -wave_max(-smn);
     if (lane == 0) {
       s_m[wave] = wm;
@@ -963,9 +1230,9 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
   __syncthreads();
   float tau = -INFINITY;
   bool decided = false;
-  const bool windowed = !(use_k && k == 1) && SM > SMN && isfinite(SM - SMN);
+  const bool windowed = SM > SMN && isfinite(SM - SMN);
   if (windowed)
-    decided = window_select<DT, VEC>(p, lrow, row, k, tp, use_k, use_p, smp, smp_ok, smp_e0, SM, SMN, s_sel.win,
+    decided = window_select<DT, VEC>(p, lrow, row, k, tp, use_k, use_p, smp, smp_ok, smp_e0, smp_stride, SM, SMN, s_sel.win,
                                      s_col, s_col2, s_scratch, s_m, s_mn, &s_fault, &s_d, &s_f, &tau);
   SPEC_TRACE_ONLY(if (windowed && !decided) trace_word(p.trace, 4, blockIdx.x, 11, 2ull));   // window fell back
   if (!decided)
