@@ -210,6 +210,7 @@ spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, con
   const bool truncate = o.top_k || o.top_p;
   p.pr = proc_spec(o, V, truncate ? reinterpret_cast<float*>(ws + L.thresh) : nullptr);
   p.thresh_ws = truncate ? reinterpret_cast<float*>(ws + L.thresh) : nullptr;
+  p.summ_ws = truncate ? reinterpret_cast<float2*>(ws + L.summ) : nullptr;
   p.q_index = gamma > 0 ? o.q_index : nullptr;
   p.q_k = o.q_k;
   p.part = reinterpret_cast<float2*>(ws + L.part);
@@ -243,6 +244,7 @@ spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, con
     t.top_k = o.top_k;
     t.top_p = o.top_p;
     t.thresh = p.thresh_ws;
+    t.summ = p.summ_ws;
     t.rows = B * (gamma + 1);
     t.R = gamma + 1;
     t.V = V;

@@ -173,17 +173,25 @@ __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
       }
     }
   }
-  // wave w streams chunks first + 4k of this slice (k < CPW)
-  const long first = (long)slice * kWavesPerBlock * p.CPW + wave;
-  float m, z;
+  // A row whose kept set the threshold pass summarized is not streamed: its first slice
+  // publishes that summary and the others an empty range.
+  float2 summ = make_float2(0.0f, 0.0f);
   if constexpr (PROC)
-    wave_row_summary_proc<DT, VEC>(p, rowid, first, lane, m, z);
-  else
-    wave_row_summary<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, p.P, first, kWavesPerBlock, p.CPW, lane,
-                              p.c2, m, z);
-  if (lane == 0) {
-    s_wm[wave] = m;
-    s_wz[wave] = z;
+    if (p.summ_ws) summ = p.summ_ws[rowid];
+  const bool summarized = summ.y > 0.0f;   // block-uniform
+  if (!summarized) {
+    // wave w streams chunks first + 4k of this slice (k < CPW)
+    const long first = (long)slice * kWavesPerBlock * p.CPW + wave;
+    float m, z;
+    if constexpr (PROC)
+      wave_row_summary_proc<DT, VEC>(p, rowid, first, lane, m, z);
+    else
+      wave_row_summary<DT, VEC>(row_ptr<DT>(p.logits, rowid, p.V), p.V, p.P, first, kWavesPerBlock, p.CPW, lane,
+                                p.c2, m, z);
+    if (lane == 0) {
+      s_wm[wave] = m;
+      s_wz[wave] = z;
+    }
   }
   if constexpr (QT == kSparseQ) {
     if (slice == 0 && i < p.G) {        // block-uniform: the whole block searches the row
@@ -195,7 +203,9 @@ __device__ void stats_item(const ChainParams& p, int b, int i, int slice) {
   if (gathers) gather_publish(p, b, i, gx, gl, gq);
   __syncthreads();
   SPEC_STAMP(p, 0, 2);
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && summarized) {
+    publish_f2(p.part + rowid * p.SL + slice, slice == 0 ? summ : make_float2(-INFINITY, 0.0f));
+  } else if (threadIdx.x == 0) {
     // the slice's summary: M = max of the waves' maxima, Z = sum of their sums rescaled
     // to M (NaN if any wave saw NaN or +inf; (-inf, 0) if every element was -inf).  Z >= 1
     // otherwise (the maximum contributes 2^0), so the published word is never zero.
@@ -579,6 +589,8 @@ __device__ void chain_clear_summaries(const ChainParams& p, int b, const ChainDe
   for (int j = tid; j < 3 * p.G; j += kBlock) clear_u64(gather_rec(p, b, 0) + j);
   if (p.thresh_ws)   // written by the threshold pass, read by this request's blocks only
     for (int j = tid; j < p.R; j += kBlock) store_wt(p.thresh_ws + (size_t)b * p.R + j, 0.0f);
+  if (p.summ_ws)
+    for (int j = tid; j < p.R; j += kBlock) clear_f2(p.summ_ws + (size_t)b * p.R + j);
 }
 // ... and the chunk masses, once the selector has read them for the last time.
 __device__ void chain_clear_masses(const ChainParams& p, int b) {
@@ -877,6 +889,8 @@ __device__ void chain_scrub(const ChainParams& p, int b) {
   for (int j = tid; j < 3 * p.S2; j += kBlock) clear_mass(p.xmass + (size_t)b * p.S2 * 3 + j);
   if (p.thresh_ws)
     for (int j = tid; j < p.R; j += kBlock) store_wt(p.thresh_ws + (size_t)b * p.R + j, 0.0f);
+  if (p.summ_ws)
+    for (int j = tid; j < p.R; j += kBlock) clear_f2(p.summ_ws + (size_t)b * p.R + j);
 }
 
 __device__ __forceinline__ double* xmass_word(const ChainParams& p, int b, int c, int k) {

@@ -101,6 +101,9 @@ struct ChainParams {
   StopSpec st;
   ProcSpec pr;
   float* thresh_ws;          // the workspace's threshold words (cleared by the selectors), or null
+  float2* summ_ws;           // [B*R] the threshold pass's kept-set summaries (max, Z) (Z > 0; zero
+                             //   for a row it leaves to the statistics pass; cleared by the
+                             //   selectors), or null
   const int32_t* q_index;    // [B, G, q_k] token indices of sparse draft rows (q then holds
   int q_k;                   //   [B, G, q_k] fp32 values), or null for dense rows
   // workspace
@@ -257,7 +260,7 @@ inline unsigned* request_counters(void* ws) {
 // slot s of request b: request_counters(ws)[b * kCounterSlots + s]
 
 struct ChainLayout {
-  size_t part, gath, tmass, thresh, xmass, total;
+  size_t part, gath, tmass, thresh, summ, xmass, total;
 };
 // The chain's statistics pass uses finer slices than the other streaming passes: its
 // terminal items fill the statistics tail, which shrinks as the slices do.
@@ -275,6 +278,7 @@ inline ChainLayout chain_layout(long B, long G, long V) {
   L.gath = o;   o = align256(o + sizeof(unsigned long long) * 3 * B * G);
   L.tmass = o;  o = align256(o + sizeof(double) * B * S2);
   L.thresh = o; o = align256(o + sizeof(float) * B * R);
+  L.summ = o;   o = align256(o + sizeof(float2) * B * R);
   L.xmass = o;  o = align256(o + sizeof(double) * 3 * B * S2);
   L.total = o;
   return L;
@@ -288,6 +292,9 @@ struct ThreshParams {
   const int32_t* top_k;      // [B] or null (0: off)
   const float* top_p;        // [B] or null (>= 1: off)
   float* thresh;             // [rows] out: -inf when nothing is truncated
+  float2* summ;              // [rows] out: the kept set's (max, Z) where the pass holds every kept
+                             //   token (Z = sum of 2^(s c2 - fp32(max c2)), the form the
+                             //   statistics pass sums); left zero otherwise
   int rows, R, V, W;
   float c2;                  // fp32(log2(e) / T)
   SPEC_TRACE_MEMBER

@@ -295,7 +295,7 @@ __device__ __forceinline__ void row_pass(const ThreshParams& p, const void* lrow
 #define SPEC_THRESH_NBUF_WIN 2
 #endif
 #ifndef SPEC_THRESH_NBUF_TOP1
-#define SPEC_THRESH_NBUF_TOP1 3
+#define SPEC_THRESH_NBUF_TOP1 2
 #endif
 
 struct RadixLds {
@@ -904,6 +904,16 @@ __device__ __forceinline__ bool window_select(const ThreshParams& p, const void*
       }
     }
     SPEC_STAMP(p, 4, 6);   // top-p resolved
+    // every kept token (a candidate with s >= tau, tau a window value) is in the window:
+    // its summary spares the statistics pass the row
+    if (p.summ && tau > -INFINITY) {
+      const float R = M * p.c2;
+      double z = 0.0;
+      for (int j = tid; j < n; j += kTB)
+        if (W.v[j] >= tau) z += (double)__builtin_amdgcn_exp2f(fmaf(W.v[j], p.c2, -R));
+      z = block_sum_d(z, s_scratch);
+      if (tid == 0) p.summ[row] = make_float2(M, static_cast<float>(z));
+    }
     *tau_out = tau;
     return true;
   }
@@ -1107,9 +1117,14 @@ __attribute__((noinline)) __device__ float full_select(const ThreshParams p, con
 // for the largest allowed value and any NaN / +inf.
 template <int DT, bool VEC, bool BIAS, bool MASK>
 __device__ __forceinline__ void top1_pass(const ThreshParams& p, const void* lrow, size_t row, float* m_out,
-                                          bool* fault_out) {
-  float m = -INFINITY;
+                                          float* m2_out, bool* fault_out) {
+  // the lane's two largest values with multiplicity: m2 == m when its largest is tied
+  float m = -INFINITY, m2 = -INFINITY;
   bool fault = false;
+  auto see = [&](float v) {
+    m2 = fmaxf(m2, fminf(v, m));
+    m = fmaxf(m, v);
+  };
   row_pass<DT, VEC, BIAS, MASK, SPEC_THRESH_NBUF_TOP1>(
       p, lrow, row,
       [&](const float (&s)[kU][8], const unsigned (&al)[kU], long) {
@@ -1118,7 +1133,7 @@ __device__ __forceinline__ void top1_pass(const ThreshParams& p, const void* lro
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             fault |= !(s[u][j] < INFINITY);
-            m = fmaxf(m, MASK ? masked_value(s[u][j], al[u], j) : s[u][j]);
+            see(MASK ? masked_value(s[u][j], al[u], j) : s[u][j]);
           }
       },
       [&](const float (&s)[kU][8], const unsigned (&ok)[kU], long) {
@@ -1127,25 +1142,30 @@ __device__ __forceinline__ void top1_pass(const ThreshParams& p, const void* lro
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             fault |= !(s[u][j] < INFINITY);
-            m = fmaxf(m, ((ok[u] >> j) & 1u) ? s[u][j] : -INFINITY);
+            see(((ok[u] >> j) & 1u) ? s[u][j] : -INFINITY);
           }
       });
   *m_out = m;
+  *m2_out = m2;
   *fault_out = fault;
 }
 
-// The top-1 threshold: the largest candidate, or -inf for a faulty row or one without candidates.
+// The top-1 threshold: the largest candidate, or -inf for a faulty row or one without
+// candidates.  The kept set is the largest value's ties; when the largest value is unique
+// its summary (M, 2^(M c2 - fp32(M c2))) is written for the statistics pass (a row with a
+// tied maximum is left to that pass).
 template <int DT, bool VEC>
-__device__ __forceinline__ float top1_select(const ThreshParams& p, const void* lrow, size_t row, float* s_m, int* s_fault) {
+__device__ __forceinline__ float top1_select(const ThreshParams& p, const void* lrow, size_t row, float* s_m,
+                                             double* s_scratch, int* s_fault) {
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
-  float m;
+  float m, m2;
   bool fault;
   if (p.bias) {
-    if (p.allowed) top1_pass<DT, VEC, true, true>(p, lrow, row, &m, &fault);
-    else top1_pass<DT, VEC, true, false>(p, lrow, row, &m, &fault);
+    if (p.allowed) top1_pass<DT, VEC, true, true>(p, lrow, row, &m, &m2, &fault);
+    else top1_pass<DT, VEC, true, false>(p, lrow, row, &m, &m2, &fault);
   } else {
-    if (p.allowed) top1_pass<DT, VEC, false, true>(p, lrow, row, &m, &fault);
-    else top1_pass<DT, VEC, false, false>(p, lrow, row, &m, &fault);
+    if (p.allowed) top1_pass<DT, VEC, false, true>(p, lrow, row, &m, &m2, &fault);
+    else top1_pass<DT, VEC, false, false>(p, lrow, row, &m, &m2, &fault);
   }
   if (fault) *s_fault = 1;
   const float wm = wave_max(m);
@@ -1154,7 +1174,14 @@ __device__ __forceinline__ float top1_select(const ThreshParams& p, const void* 
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kTW; ++w) M = fmaxf(M, s_m[w]);
-  return (*s_fault || !(M > -INFINITY)) ? -INFINITY : M;
+  const bool none = *s_fault || !(M > -INFINITY);
+  if (p.summ && !none) {                // block-uniform
+    // copies of M: 2 stands for "two or more" in a lane
+    const double c = block_sum_d(m == M ? (m2 == M ? 2.0 : 1.0) : 0.0, s_scratch);
+    if (threadIdx.x == 0 && c == 1.0)
+      p.summ[row] = make_float2(M, __builtin_amdgcn_exp2f(fmaf(M, p.c2, -(M * p.c2))));
+  }
+  return none ? -INFINITY : M;
 }
 
 template <int DT, bool VEC>
@@ -1197,7 +1224,7 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
   if (threadIdx.x == 0) s_fault = 0;
   __syncthreads();
   if (use_k && k == 1) {
-    const float t1 = top1_select<DT, VEC>(p, lrow, row, s_m, &s_fault);
+    const float t1 = top1_select<DT, VEC>(p, lrow, row, s_m, s_scratch, &s_fault);
     if (threadIdx.x == 0) p.thresh[row] = t1;
     SPEC_STAMP(p, 4, 7);
     return;

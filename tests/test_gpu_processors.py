@@ -247,3 +247,42 @@ def test_threshold_window_and_full_paths(sigma, k, tp):
     pp = np.full(x.B, tp, np.float32)
     say(f"chain_ex threshold paths sigma={sigma} k={k} p={tp}")
     check(x, None, None, kk, pp)
+
+
+@pytest.mark.parametrize("tied", [False, True])
+def test_top1_kept_set_with_unique_and_tied_maxima(tied):
+    """Top-1 on every request keeps each row's largest value with its ties.  With a unique
+    maximum the threshold pass hands the statistics pass the row's summary (max, Z); with a
+    tied one the row is streamed as usual.  Every row holds one value above all others, once
+    or three times; half the requests draft one of its copies.  Tokens, statuses and the
+    per-row statistics (max and log Z) must equal the oracle's."""
+    x = synth.make_chain(24, 3, 32000, seed=77 if tied else 78, logit_dtype="bf16", temperature=0.8)
+    rng = np.random.default_rng(5)
+    top = np.uint16(np.float32(30.0).view(np.uint32) >> 16)   # 30.0 in bf16
+    for b in range(x.B):
+        for r in range(x.gamma + 1):
+            pos = rng.choice(x.V, size=3 if tied else 1, replace=False)
+            x.logits[b, r, pos] = top
+            if r < x.gamma and b % 2 == 0:
+                x.tokens[b, r] = pos[0]
+    k = np.ones(x.B, np.int32)
+    p = np.where(np.arange(x.B) % 3 == 0, 0.5, 1.0).astype(np.float32)
+    say(f"chain_ex top-1, {'tied' if tied else 'unique'} maxima")
+    got, exp, s = check(x, None, None, k, p)
+    assert (got["req_status"] == 0).all()
+
+
+@pytest.mark.parametrize("k,tp", [(20, 1.0), (0, 0.9), (300, 0.95)])
+def test_window_summaries_with_bias_and_masks(k, tp):
+    """Rows decided by the threshold pass's window (top-k, top-p alone, both) reach the
+    verifier as kept-set summaries rather than through the statistics stream; with bias and
+    masks on, the per-row statistics, tokens and statuses must equal the oracle's.  Peaked rows
+    (1% of entries boosted by +8) put the nucleus inside the window."""
+    x = synth.make_chain(32, 4, 50000, seed=k + int(tp * 100), logit_dtype="bf16", sigma=2.5, boost_frac=0.01,
+                         boost=8.0, noise=1.0, temperature=0.8)
+    bias, words, _, _ = synth.make_processors(x.B, x.gamma + 1, x.V, seed=k + 1, with_top_k=False,
+                                              with_top_p=False)
+    kk = np.full(x.B, k, np.int32)
+    pp = np.full(x.B, tp, np.float32)
+    say(f"chain_ex window summaries k={k} p={tp}")
+    check(x, bias, words, kk, pp)
