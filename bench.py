@@ -424,10 +424,12 @@ def _med(v):
     return float(np.median(v)) if v.size else float("nan")
 
 
-def timeline_chain(args, torch, sv, synth, lib):
+def timeline_chain(args, torch, sv, synth, lib, proc=False):
     """Per-block timeline of the headline chain call from the trace build: when the statistics
     stream ends, and each selector's steps (decision, own chunk mass, every mass in, rescan,
-    outputs, workspace cleared), then the exact-redraw kernel.  Prints a markdown summary."""
+    outputs, workspace cleared), then the exact-redraw kernel.  Prints a markdown summary.
+    With proc, the chain kernel of the processors line (bias, masks, top-k, top-p; the
+    threshold pass runs first and is not part of the times)."""
     import ctypes
     x = synth.make_config(3, 0)
     B, G, V = x.B, x.gamma, x.V
@@ -438,7 +440,13 @@ def timeline_chain(args, torch, sv, synth, lib):
     sets = device_copies(lambda: (lt.clone(), qt.clone()), lt.numel() * 2 + qt.numel() * 4)
     del lt, qt
     ws = torch.zeros(sv.chain_workspace_bytes(B, G, V) + 512, dtype=torch.uint8, device=dev)
-    calls = [sv.prepare_chain(s_[0], s_[1], tt, ut, float(x.temperature), workspace_tensor=ws) for s_ in sets]
+    kw = {}
+    if proc:
+        bias, words, k, p = synth.make_processors(B, G + 1, V, seed=11)
+        kw = dict(bias=torch.from_numpy(bias).to(dev), allowed=torch.from_numpy(words.view(np.int32)).to(dev),
+                  top_k=torch.from_numpy(k).to(dev), top_p=torch.from_numpy(p).to(dev))
+    calls = [sv.prepare_chain(s_[0], s_[1], tt, ut, float(x.temperature), workspace_tensor=ws, **kw)
+             for s_ in sets]
     stream = torch.cuda.current_stream()
     cap = 8192
     buf = torch.zeros(TRACE_KERNELS * cap * TRACE_WORDS, dtype=torch.int64, device=dev)
@@ -470,6 +478,8 @@ def timeline_chain(args, torch, sv, synth, lib):
                                f"{nz.min()}..{nz.max()} ({nz.size}); slot-1 records tagged "
                                f"{np.count_nonzero(raw[1][:, 0])}")
         chain_end = np.nanmax(t)
+        T = kind == 2
+        term_start = _med(t[T, 0]) if T.any() else float("nan")
         stats_done = np.array([np.nanmax(t[S & (b == r), 1]) for r in range(B)])
         sel = {r: t[L & (b == r)][0] for r in range(B)}
         steps = np.array([[sel[r][1] - sel[r][0],                 # start -> decided
@@ -498,14 +508,15 @@ def timeline_chain(args, torch, sv, synth, lib):
                          sub_med=np.nanmedian(sub, axis=0), sub_last=sub[last],
                          after_stats_last=float(sel_end[last] - stats_done[last]),
                          k3_gap=float(k3_start - chain_end), k3_span=float(k3_end - k3_start),
-                         k3_exact=int((e["kind"] == 5).sum()), total=float(k3_end)))
+                         k3_exact=int((e["kind"] == 5).sum()), total=float(k3_end), term_start=term_start))
     assert lib.spec_trace_set(ctypes.c_void_p(0), 0) == 0
     g = lambda k: _med([r_[k] for r_ in rows])
     sm = np.median(np.array([r_["steps_med"] for r_ in rows]), axis=0)
     sl = np.median(np.array([r_["steps_last"] for r_ in rows]), axis=0)
     names = ["dispatch -> decision", "decision -> own chunk mass", "own mass -> every mass in",
              "masses in -> rescan done", "rescan -> outputs written", "outputs -> workspace cleared"]
-    print(f"## chain_kernel timeline: B={B} gamma={G} V={V} bf16 logits, fp32 q, T={x.temperature}")
+    what = ", bias, masks, top-k, top-p (chain kernel after the threshold pass)" if proc else ""
+    print(f"## chain_kernel timeline: B={B} gamma={G} V={V} bf16 logits, fp32 q, T={x.temperature}{what}")
     print()
     print(f"Trace build, {args.timeline_calls} traced calls; medians over calls. Times in us from the "
           f"first block's start (s_memrealtime, 10 ns ticks). Calls of the trace build: "
@@ -516,6 +527,7 @@ def timeline_chain(args, torch, sv, synth, lib):
     print("|---|---|")
     print(f"| median statistics item (start -> published) | {g('stats_item'):.2f} |")
     print(f"| statistics stream ends (last item's stream done) | {g('stream_end'):.2f} |")
+    print(f"| median terminal item start | {g('term_start'):.2f} |")
     print(f"| last-finishing request: its statistics done | {g('last_req_stats'):.2f} |")
     print(f"| last-finishing request: selector dispatched | {g('sel_start_last'):.2f} |")
     print(f"| last-finishing request: selector done | {g('sel_end_last'):.2f} |")
@@ -833,7 +845,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true",
                     help="print the chain bandwidth sweep over batch sizes (one JSON line per point) instead")
-    ap.add_argument("--timeline", choices=["chain", "tree", "tree_residual", "thresh"],
+    ap.add_argument("--timeline", choices=["chain", "chain_proc", "tree", "tree_residual", "thresh"],
                     help="print a per-block timeline summary (markdown) of one workload instead, from the "
                          "trace build (python -m exact_rejection_sampling_amd.build --trace)")
     ap.add_argument("--timeline-calls", type=int, default=5)
@@ -857,7 +869,8 @@ def main():
         from exact_rejection_sampling_amd import build as _build
         lib = sv.load_library(_build.TRACE_LIB, install=True)
         fn = dict(chain=timeline_chain, tree=timeline_tree, tree_residual=timeline_tree_residual,
-                  thresh=timeline_thresh)[args.timeline]
+                  thresh=timeline_thresh,
+                  chain_proc=lambda *a: timeline_chain(*a, proc=True))[args.timeline]
         fn(args, torch, sv, synth, lib)
         return
     sv.load_library()
