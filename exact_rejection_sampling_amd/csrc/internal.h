@@ -296,6 +296,8 @@ struct ThreshParams {
                              //   token (Z = sum of 2^(s c2 - fp32(max c2)), the form the
                              //   statistics pass sums); left zero otherwise
   int rows, R, V, W;
+  int cus;                   // compute units when two blocks share each (rows are then taken
+                             //   heaviest first, lightest in the blocks that share a CU), or 0
   float c2;                  // fp32(log2(e) / T)
   SPEC_TRACE_MEMBER
 };

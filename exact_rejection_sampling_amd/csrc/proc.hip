@@ -1184,6 +1184,81 @@ __device__ __forceinline__ float top1_select(const ThreshParams& p, const void* 
   return none ? -INFINITY : M;
 }
 
+// Rows in order of cost, heaviest first: 0 top-p alone (a weight per element), 1 top-k
+// with k >= 2, 2 top-1, 3 neither (nothing to do).
+__device__ __forceinline__ int row_cost_class(const ThreshParams& p, int b) {
+  const int k = p.top_k ? p.top_k[b] : 0;
+  const float tp = p.top_p ? p.top_p[b] : 1.0f;
+  const bool use_k = k >= 1, use_p = tp > 0.0f && tp < 1.0f;
+  if (!use_k) return use_p ? 0 : 3;
+  return k == 1 ? 2 : 1;
+}
+
+// The row block j takes.  Sorted by cost class, then request, then row, the rows go out
+// heaviest first; with more rows than CUs but at most two per CU, the blocks that share a
+// CU (those below rows - CUs, and those from CUs up, as the dispatcher fills each CU once
+// before any twice) take the rows after the heaviest CUs - (rows - CUs), so that the
+// heaviest rows run alone and a shared CU pairs middle rows with the lightest ones.  A
+// bijection on [0, rows): any row order gives the same thresholds.  Wave 0 computes it
+// from every request's top-k and top-p; the others wait at the barrier.
+__device__ size_t balanced_row(const ThreshParams& p, unsigned j, long* s_row) {
+  if (threadIdx.x < kWave) {
+    constexpr int kKept = 4;          // the classes of the first 4 * 64 requests stay in registers
+    const int lane = threadIdx.x;
+    const int R = p.R, B = p.rows / R;
+    int kept[kKept];
+    long cnt[4] = {0, 0, 0, 0};       // requests per class
+#pragma unroll
+    for (int t = 0; t < kKept; ++t) {
+      const int b = t * kWave + lane;
+      kept[t] = b < B ? row_cost_class(p, b) : 4;
+    }
+    for (int b0 = 0; b0 < B; b0 += kWave) {
+      const int t = b0 / kWave, b = b0 + lane;
+      int c = 4;
+#pragma unroll
+      for (int u = 0; u < kKept; ++u)
+        if (t == u) c = kept[u];
+      if (t >= kKept && b < B) c = row_cost_class(p, b);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) cnt[cc] += __popcll(__ballot(c == cc));
+    }
+    const long rows = p.rows, cus = p.cus, d = rows - cus;   // d: CUs that hold two rows
+    long srt = j;                     // j's place in the sorted order
+    if (d > 0 && d <= cus) {
+      if (j >= d && j < cus) srt = j - d;            // alone on a CU: the heaviest rows
+      else if (j < d) srt = cus - d + j;             // first of a pair
+    }
+    int c = 0;
+    long base = 0;
+    while (c < 3 && srt >= base + cnt[c] * R) {
+      base += cnt[c] * R;
+      ++c;
+    }
+    const long q = srt - base, want = q / R;          // the want-th request of class c
+    long seen = 0, req = 0;
+    for (int b0 = 0; b0 < B; b0 += kWave) {
+      const int t = b0 / kWave, b = b0 + lane;
+      int cb = 4;
+#pragma unroll
+      for (int u = 0; u < kKept; ++u)
+        if (t == u) cb = kept[u];
+      if (t >= kKept && b < B) cb = row_cost_class(p, b);
+      unsigned long long m = __ballot(cb == c);
+      const long n = __popcll(m);
+      if (seen + n > want) {
+        for (long i = seen; i < want; ++i) m &= m - 1ull;   // drop the set bits before it
+        req = b0 + __ffsll(static_cast<long long>(m)) - 1;
+        break;
+      }
+      seen += n;
+    }
+    if (lane == 0) *s_row = req * R + q % R;
+  }
+  __syncthreads();
+  return static_cast<size_t>(*s_row);
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(ThreshParams p) {
   __shared__ double s_scratch[kTW];
@@ -1192,8 +1267,9 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
   __shared__ float s_m[kTW], s_mn[kTW];
   __shared__ int s_fault, s_d;
   __shared__ double s_f;
-  const size_t row = blockIdx.x;
+  __shared__ long s_row;
   SPEC_STAMP(p, 4, 1);
+  const size_t row = p.cus > 0 && p.rows > p.cus ? balanced_row(p, blockIdx.x, &s_row) : blockIdx.x;
   const int b = static_cast<int>(row / p.R);
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   const void* lrow = row_ptr<DT>(p.logits, row, p.V);
@@ -1270,7 +1346,18 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
 }
 
 template <int DT, bool VEC>
-hipError_t launch_typed(const ThreshParams& p, hipStream_t s) {
+hipError_t launch_typed(ThreshParams p, hipStream_t s) {
+  static int s_cus[64] = {0};        // per device ordinal: CUs if two blocks share each, -1 if not
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (s_cus[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, thresh_kernel<DT, VEC>, kTB, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidValue;
+    s_cus[dev] = (per_cu == 2 && cus > 0) ? cus : -1;
+  }
+  p.cus = s_cus[dev] > 0 ? s_cus[dev] : 0;
   thresh_kernel<DT, VEC><<<dim3((unsigned)p.rows), dim3(kTB), 0, s>>>(p);
   return hipGetLastError();
 }
