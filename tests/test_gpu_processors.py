@@ -286,3 +286,20 @@ def test_window_summaries_with_bias_and_masks(k, tp):
     pp = np.full(x.B, tp, np.float32)
     say(f"chain_ex window summaries k={k} p={tp}")
     check(x, bias, words, kk, pp)
+
+
+@pytest.mark.parametrize("B,gamma", [(300, 0), (100, 3), (300, 1)])
+def test_rows_mapped_heaviest_first(B, gamma):
+    """The threshold pass maps blocks to rows by cost class (top-p alone, top-k >= 2, top-1,
+    neither).  With 300 and 400 rows it takes the shared-CU order on a 256-CU device, with 600
+    rows the plain heaviest-first order, and with 300 requests it reads the classes beyond the
+    first 256 requests again.  Mixed top-k and top-p per request; every row's threshold must
+    reach the verifier whatever block computed it, so tokens, statuses and statistics must
+    equal the oracle's."""
+    x = synth.make_chain(B, gamma, 4096, seed=B + gamma, logit_dtype="bf16", sigma=2.5, boost_frac=0.01,
+                         boost=8.0, noise=1.0, temperature=0.8)
+    rng = np.random.default_rng(B * 10 + gamma)
+    k = rng.choice(np.array([0, 1, 20, 300], np.int32), size=B)
+    p = rng.choice(np.array([1.0, 0.5, 0.9], np.float32), size=B)
+    say(f"chain_ex rows mapped by cost, B={B} gamma={gamma}")
+    check(x, None, None, k, p)
