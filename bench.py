@@ -725,6 +725,7 @@ def timeline_thresh(args, torch, sv, synth, lib):
             tp = float(np.array([raw[i, 8] & np.uint64(0xffffffff)], dtype=np.uint64).astype(np.uint32).view(np.float32)[0])
             n1 = int(raw[i, 9] & np.uint64(0xffffffff))
             rows.append(dict(kind=int(kind[i]), k=int(kk[i]), p=tp, n=n1, radix=int(raw[i, 10]),
+                             block=i, where=int(raw[i, 11]), rep=len(rows) // max(1, len(kind)),
                              dur=t[i, 6] - t[i, 0], p0=t[i, 1] - t[i, 0],
                              p1=t[i, 2] - t[i, 1], col=t[i, 3] - t[i, 2], res=t[i, 4] - t[i, 3],
                              topp=t[i, 5] - t[i, 4], rest=t[i, 6] - t[i, 5], start=t[i, 0], end=t[i, 6]))
@@ -762,6 +763,23 @@ def timeline_thresh(args, torch, sv, synth, lib):
     print()
     print(f"Last row ends at {np.percentile(ends, 100):.2f} us (p90 {np.percentile(ends, 90):.2f}, "
           f"median {np.median(ends):.2f}) after the first row's start.")
+    # placement (first traced call): which blocks share a CU
+    first = [r_ for r_ in rows[:len(recs[0]["kind"])]]
+    by_cu = {}
+    for r_ in first:
+        by_cu.setdefault(r_["where"], []).append(r_)
+    shared = [sorted(v, key=lambda r_: r_["block"]) for v in by_cu.values() if len(v) > 1]
+    gaps = {}
+    for v in shared:
+        g_ = v[-1]["block"] - v[0]["block"]
+        gaps[g_] = gaps.get(g_, 0) + 1
+    top = sorted(gaps.items(), key=lambda kv: -kv[1])[:4]
+    low = sum(1 for v in shared for r_ in v if r_["block"] < 256)
+    print()
+    print(f"Placement (first traced call, from the hardware IDs): {len(by_cu)} CUs used, {len(shared)} with more "
+          f"than one row; block-index gaps within a shared CU (gap: CUs): "
+          + ", ".join(f"{g_}: {c_}" for g_, c_ in top)
+          + f"; blocks below 256 among the shared: {low}.")
 
 
 class _CachedSynth:

@@ -1293,6 +1293,14 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
   const bool use_k = k >= 1, use_p = tp > 0.0f && tp < 1.0f;   // false for NaN
   SPEC_TAG(p, 4, SPEC_TRACE_TAG((use_k ? 1 : 0) | (use_p ? 2 : 0), row, k));
   SPEC_TRACE_ONLY(trace_word(p.trace, 4, blockIdx.x, 9, __float_as_uint(tp)));
+  // where the block runs: XCC, then shader engine, shader array and CU (a register read)
+  SPEC_TRACE_ONLY({
+    unsigned hw;
+    unsigned xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    trace_word(p.trace, 4, blockIdx.x, 12, ((unsigned long long)(xcc & 0xfu) << 16) | ((hw >> 8) & 0xffu));
+  });
   if (!use_k && !use_p) {
     if (threadIdx.x == 0) p.thresh[row] = -INFINITY;
     return;
