@@ -1194,11 +1194,11 @@ __device__ __forceinline__ int row_cost_class(const ThreshParams& p, int b) {
   return k == 1 ? 2 : 1;
 }
 
-// The row block j takes.  Sorted by cost class, then request, then row, the rows go out
-// heaviest first; with more rows than CUs but at most two per CU, the blocks that share a
-// CU (those below rows - CUs, and those from CUs up, as the dispatcher fills each CU once
-// before any twice) take the rows after the heaviest CUs - (rows - CUs), so that the
-// heaviest rows run alone and a shared CU pairs middle rows with the lightest ones.  A
+// The row block j takes when there are more rows than CUs but at most two per CU.  Sorted by
+// cost class, then request, then row, the rows are dealt so that the blocks that share a CU
+// (those below rows - CUs, and those from CUs up, as the dispatcher fills each CU once before
+// any twice) take the rows after the heaviest CUs - (rows - CUs): the heaviest rows run alone
+// and a shared CU pairs a middle row with one of the lightest.  A
 // bijection on [0, rows): any row order gives the same thresholds.  Wave 0 computes it
 // from every request's top-k and top-p; the others wait at the barrier.
 __device__ size_t balanced_row(const ThreshParams& p, unsigned j, long* s_row) {
@@ -1224,11 +1224,9 @@ __device__ size_t balanced_row(const ThreshParams& p, unsigned j, long* s_row) {
       for (int cc = 0; cc < 4; ++cc) cnt[cc] += __popcll(__ballot(c == cc));
     }
     const long rows = p.rows, cus = p.cus, d = rows - cus;   // d: CUs that hold two rows
-    long srt = j;                     // j's place in the sorted order
-    if (d > 0 && d <= cus) {
-      if (j >= d && j < cus) srt = j - d;            // alone on a CU: the heaviest rows
-      else if (j < d) srt = cus - d + j;             // first of a pair
-    }
+    long srt = j;                     // j's place in the sorted order (the second of a pair)
+    if (j >= d && j < cus) srt = j - d;              // alone on a CU: the heaviest rows
+    else if (j < d) srt = cus - d + j;               // first of a pair
     int c = 0;
     long base = 0;
     while (c < 3 && srt >= base + cnt[c] * R) {
@@ -1269,7 +1267,10 @@ __global__ __launch_bounds__(kTB, kTB >= 1024 ? 1 : 4) void thresh_kernel(Thresh
   __shared__ double s_f;
   __shared__ long s_row;
   SPEC_STAMP(p, 4, 1);
-  const size_t row = p.cus > 0 && p.rows > p.cus ? balanced_row(p, blockIdx.x, &s_row) : blockIdx.x;
+  // the shared-CU order only where some CUs hold two rows (then at most 2 * CUs rows, so the
+  // mapping reads at most that many requests' top-k and top-p)
+  const size_t row =
+      p.cus > 0 && p.rows > p.cus && p.rows <= 2 * p.cus ? balanced_row(p, blockIdx.x, &s_row) : blockIdx.x;
   const int b = static_cast<int>(row / p.R);
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   const void* lrow = row_ptr<DT>(p.logits, row, p.V);

@@ -291,11 +291,11 @@ def test_window_summaries_with_bias_and_masks(k, tp):
 @pytest.mark.parametrize("B,gamma", [(300, 0), (100, 3), (300, 1)])
 def test_rows_mapped_heaviest_first(B, gamma):
     """The threshold pass maps blocks to rows by cost class (top-p alone, top-k >= 2, top-1,
-    neither).  With 300 and 400 rows it takes the shared-CU order on a 256-CU device, with 600
-    rows the plain heaviest-first order, and with 300 requests it reads the classes beyond the
-    first 256 requests again.  Mixed top-k and top-p per request; every row's threshold must
-    reach the verifier whatever block computed it, so tokens, statuses and statistics must
-    equal the oracle's."""
+    neither) when some CUs hold two rows.  With 300 and 400 rows it takes that order on a
+    256-CU device (300 requests: the classes beyond the first 256 are read again); with 600
+    rows the rows keep their own order.  Mixed top-k and top-p per request; every row's
+    threshold must reach the verifier whatever block computed it, so tokens, statuses and
+    statistics must equal the oracle's."""
     x = synth.make_chain(B, gamma, 4096, seed=B + gamma, logit_dtype="bf16", sigma=2.5, boost_frac=0.01,
                          boost=8.0, noise=1.0, temperature=0.8)
     rng = np.random.default_rng(B * 10 + gamma)
