@@ -607,7 +607,7 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
   __shared__ double s_scan2[2 * kWavesPerBlock];
   __shared__ int s_imin[kWavesPerBlock];
   __shared__ int s_imin2[2 * kWavesPerBlock];
-  __shared__ int s_timeout;
+  __shared__ int s_timeout, s_cstar;
   __shared__ double s_before, s_total;
   const int tid = threadIdx.x, G = p.G;
   const double* tm = p.tmass + (size_t)b * p.S2;
@@ -623,7 +623,10 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
   // 1. running mass over the chunks in order: thread t owns a contiguous run of chunks
   //    and extends the block-exclusive prefix over it.  W is the running value after the
   //    last chunk, computed the same way, so u * W < W always finds a chunk whose running
-  //    value exceeds the target.
+  //    value exceeds the target.  With at most 64 chunks they all sit in wave 0, one per
+  //    lane, whose prefix is the block-wide one (the other waves add zeros), and wave 0
+  //    also picks the chunk: one barrier instead of the block scans' five.
+  const bool one_wave = p.S2 <= kWave;
   const int per = (p.S2 + kBlock - 1) / kBlock;
   const int c_lo = min(tid * per, p.S2), c_hi = min(c_lo + per, p.S2);
   double mv[kMassRegs];
@@ -634,18 +637,42 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
     lost |= (bits == 0ull);
     return -__longlong_as_double(static_cast<long long>(bits));
   };
-  double mine = 0.0;
+  double mine = 0.0, excl = 0.0;
+  if (one_wave) {
+    if (tid < kWave) {                  // wave 0: lane c holds chunk c (c_lo = c, per = 1)
+      mine = c_lo < c_hi ? mass_at(c_lo) : 0.0;
+      mv[0] = mine;
+      excl = 0.0 + wave_shr1_d(wave_incl_scan_d(mine, tid));   // as block_excl_scan_d forms it
+      const double Wl = __shfl(excl + mine, p.S2 - 1, kWave);
+      const bool lost_w = wave_any(lost);
+      const bool failed_w = lost_w || !(isfinite(Wl) && Wl > 0.0);
+      int cs = p.S2 - 1;
+      if (!failed_w) {
+        const double t = (double)ut * Wl;
+        const unsigned long long hit = __ballot(c_lo < c_hi && excl + mine > t);
+        if (hit) cs = __ffsll(static_cast<long long>(hit)) - 1;
+      }
+      const double before = __shfl(excl, cs, kWave);
+      if (tid == 0) {
+        s_total = Wl;
+        s_timeout = lost_w ? 1 : 0;
+        s_before = before;
+        s_cstar = cs;
+      }
+    }
+  } else {
 #pragma unroll
-  for (int k = 0; k < kMassRegs; ++k) {
-    const int c = c_lo + k;
-    mv[k] = c < c_hi ? mass_at(c) : 0.0;
-    mine += mv[k];
+    for (int k = 0; k < kMassRegs; ++k) {
+      const int c = c_lo + k;
+      mv[k] = c < c_hi ? mass_at(c) : 0.0;
+      mine += mv[k];
+    }
+    for (int c = c_lo + kMassRegs; c < c_hi; ++c) mine += mass_at(c);
+    if (lost) s_timeout = 1;
+    double tot;
+    excl = block_excl_scan_d(mine, s_scan, &tot);
+    if (c_lo < c_hi && c_hi == p.S2) s_total = excl + mine;
   }
-  for (int c = c_lo + kMassRegs; c < c_hi; ++c) mine += mass_at(c);
-  if (lost) s_timeout = 1;
-  double tot;
-  const double excl = block_excl_scan_d(mine, s_scan, &tot);
-  if (c_lo < c_hi && c_hi == p.S2) s_total = excl + mine;
   __syncthreads();
   const double W = s_total;
   const bool failed = s_timeout || !(isfinite(W) && W > 0.0);   // uniform across the block
@@ -659,26 +686,29 @@ __device__ void chain_select(const ChainParams& p, int b, const ChainDecision& d
   if (failed) chain_clear_masses(p, b);
   if (!failed) {
     t = (double)ut * W;
-    int cand = 0x7fffffff;          // first chunk of this thread's run whose running value passes t
-    double run = excl;
-    for (int c = c_lo; c < c_hi; ++c) {
-      const double mc = c - c_lo < kMassRegs ? mv[c - c_lo] : mass_at(c);
-      const double nxt = run + mc;
-      if (nxt > t) {
-        cand = c;
-        break;
+    int cstar = s_cstar;            // (one wave: picked already)
+    if (!one_wave) {
+      int cand = 0x7fffffff;        // first chunk of this thread's run whose running value passes t
+      double run = excl;
+      for (int c = c_lo; c < c_hi; ++c) {
+        const double mc = c - c_lo < kMassRegs ? mv[c - c_lo] : mass_at(c);
+        const double nxt = run + mc;
+        if (nxt > t) {
+          cand = c;
+          break;
+        }
+        run = nxt;
       }
-      run = nxt;
+      // a chunk is always found (t < W and the last running value is W); clamp regardless
+      cstar = block_min_i(cand, s_imin);
+      if (cstar == 0x7fffffff) cstar = p.S2 - 1;
+      if (cstar >= c_lo && cstar < c_hi) {       // the owner of cstar records the mass before it
+        double before = excl;
+        for (int c = c_lo; c < cstar; ++c) before += c - c_lo < kMassRegs ? mv[c - c_lo] : mass_at(c);
+        s_before = before;
+      }
+      __syncthreads();
     }
-    // a chunk is always found (t < W and the last running value is W); clamp regardless
-    int cstar = block_min_i(cand, s_imin);
-    if (cstar == 0x7fffffff) cstar = p.S2 - 1;
-    if (cstar >= c_lo && cstar < c_hi) {       // the owner of cstar records the mass before it
-      double before = excl;
-      for (int c = c_lo; c < cstar; ++c) before += c - c_lo < kMassRegs ? mv[c - c_lo] : mass_at(c);
-      s_before = before;
-    }
-    __syncthreads();
     const double rem = t - s_before;   // target mass inside chunk cstar
     chain_clear_masses(p, b);          // every thread has read its masses for the last time
     SPEC_STAMP(p, 0, 11);   // chunk picked
