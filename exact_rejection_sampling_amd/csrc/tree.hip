@@ -443,7 +443,7 @@ __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
   const int N = p.N;
   const int32_t* par = p.parents + (size_t)b * N;
   const int32_t* tok = p.node_tokens + (size_t)b * N;
-  // the tree's validation: loads now, verdict after the root's sample (before any status)
+  // the tree's validation: loads now, outcome after the root's sample (before any status)
   const TreeCheck check = tree_check_issue(p, par, tok, N);
 
   int v = 0, depth = 0;
@@ -619,7 +619,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
   const int32_t* tok = p.node_tokens + (size_t)b * N;
   unsigned long long* d = p.desc + (size_t)b * p.desc_words;
   unsigned g1 = 0;   // thread 0: the generation of the current node's first pass order
-  // the tree's validation: loads now, verdict once the root's summaries are staged
+  // the tree's validation: loads now, outcome once the root's summaries are staged
   const TreeCheck check = tree_check_issue(p, par, tok, N);
 
   int v = 0, depth = 0, hop = 0;
