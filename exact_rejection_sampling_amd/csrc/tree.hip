@@ -75,8 +75,10 @@ __device__ int sample_row(const TreeParams& p, const float2* part, const void* r
   __shared__ float s_r;
   __shared__ double s_z;
   __shared__ int s_imin[kWavesPerBlock];
+  __shared__ int s_imin2[2 * kWavesPerBlock];
   __shared__ double s_before;
   __shared__ double s_total;
+  __shared__ int s_cstar;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   const float c2 = p.c2;
 
@@ -91,49 +93,82 @@ __device__ int sample_row(const TreeParams& p, const float2* part, const void* r
   const float R = s_r;
 
   // chunk masses 2^(r_j - R) Z_j in vocabulary order; thread t owns a contiguous run
-  const int per = (p.P + kBlock - 1) / kBlock;
-  const int c_lo = min(tid * per, p.P), c_hi = min(c_lo + per, p.P);
-  double mine = 0.0;
-  for (int c = c_lo; c < c_hi; ++c) {
+  auto mass_of = [&](int c) -> double {
     const float2 s = summary<DT, VEC, PUBLISHED>(part, c);
-    mine += (double)s.y * exp2((double)(s.x * c2) - (double)R);
+    return (double)s.y * exp2((double)(s.x * c2) - (double)R);
+  };
+  const bool ok_u = uv >= 0.0f && uv < 1.0f;
+  int cstar;
+  double Z;
+  if (p.P <= 2 * kWave) {
+    // At most 128 chunks: wave 0 holds chunks l and 64 + l in lane l and forms the running
+    // masses as the block's first two waves would (one chunk per thread, wave 1 offset by
+    // wave 0's total), so Z and every running value are the block-wide ones; it also picks
+    // the chunk.  One barrier instead of the block scan's, the minimum's and the owner's.
+    if (wave == 0) {
+      const double ma = lane < p.P ? mass_of(lane) : 0.0;
+      const double mb = kWave + lane < p.P ? mass_of(kWave + lane) : 0.0;
+      const double ia = wave_incl_scan_d(ma, lane), ib = wave_incl_scan_d(mb, lane);
+      const double ea = 0.0 + wave_shr1_d(ia);
+      const double eb = (0.0 + __shfl(ia, kWave - 1, kWave)) + wave_shr1_d(ib);
+      const int last = p.P - 1;
+      const double Zw = last < kWave ? __shfl(ea + ma, last, kWave) : __shfl(eb + mb, last - kWave, kWave);
+      int cs = p.P - 1;
+      if (isfinite(Zw) && Zw > 0.0 && ok_u) {
+        const double t = (double)uv * Zw;
+        const unsigned long long ha = __ballot(lane < p.P && ea + ma > t);
+        const unsigned long long hb = __ballot(kWave + lane < p.P && eb + mb > t);
+        if (ha) cs = __ffsll(static_cast<long long>(ha)) - 1;
+        else if (hb) cs = kWave + __ffsll(static_cast<long long>(hb)) - 1;
+      }
+      const double before = cs < kWave ? __shfl(ea, cs, kWave) : __shfl(eb, cs - kWave, kWave);
+      if (lane == 0) {
+        s_total = Zw;
+        s_before = before;
+        s_cstar = cs;
+      }
+    }
+    __syncthreads();
+    Z = s_total;
+    cstar = s_cstar;
+    if (!(isfinite(Z) && Z > 0.0)) { *status = SPEC_REQ_NONFINITE; return -1; }
+    if (!ok_u) { *status = SPEC_REQ_BADUNIFORM; return -1; }
+  } else {
+    const int per = (p.P + kBlock - 1) / kBlock;
+    const int c_lo = min(tid * per, p.P), c_hi = min(c_lo + per, p.P);
+    double mine = 0.0;
+    for (int c = c_lo; c < c_hi; ++c) mine += mass_of(c);
+    double tot;
+    const double excl = block_excl_scan_d(mine, s_scan, &tot);
+    double run_end = excl;
+    for (int c = c_lo; c < c_hi; ++c) run_end += mass_of(c);
+    if (c_lo < c_hi && c_hi == p.P) s_total = run_end;
+    __syncthreads();
+    Z = s_total;
+    if (!(isfinite(Z) && Z > 0.0)) { *status = SPEC_REQ_NONFINITE; return -1; }
+    if (!ok_u) { *status = SPEC_REQ_BADUNIFORM; return -1; }
+    const double t = (double)uv * Z;
+    int cand = kNoPick;          // first chunk of this thread's run whose running value passes t
+    {
+      double run = excl;
+      for (int c = c_lo; c < c_hi; ++c) {
+        const double nxt = run + mass_of(c);
+        if (nxt > t) { cand = c; break; }
+        run = nxt;
+      }
+    }
+    if (tid == 0) s_before = 0.0;
+    // a chunk is always found (t < Z and the last running value is Z); clamp regardless
+    cstar = block_min_i(cand, s_imin);
+    if (cstar == kNoPick) cstar = p.P - 1;
+    if (cstar >= c_lo && cstar < c_hi) {
+      double run = excl;
+      for (int c = c_lo; c < cstar; ++c) run += mass_of(c);
+      s_before = run;
+    }
+    __syncthreads();
   }
-  double tot;
-  const double excl = block_excl_scan_d(mine, s_scan, &tot);
-  double run_end = excl;
-  for (int c = c_lo; c < c_hi; ++c) {
-    const float2 s = summary<DT, VEC, PUBLISHED>(part, c);
-    run_end += (double)s.y * exp2((double)(s.x * c2) - (double)R);
-  }
-  if (c_lo < c_hi && c_hi == p.P) s_total = run_end;
-  __syncthreads();
-  const double Z = s_total;
-  if (!(isfinite(Z) && Z > 0.0)) { *status = SPEC_REQ_NONFINITE; return -1; }
-  if (!(uv >= 0.0f && uv < 1.0f)) { *status = SPEC_REQ_BADUNIFORM; return -1; }
   const double t = (double)uv * Z;
-  int cand = kNoPick;          // first chunk of this thread's run whose running value passes t
-  {
-    double run = excl;
-    for (int c = c_lo; c < c_hi; ++c) {
-      const float2 s = summary<DT, VEC, PUBLISHED>(part, c);
-      const double nxt = run + (double)s.y * exp2((double)(s.x * c2) - (double)R);
-      if (nxt > t) { cand = c; break; }
-      run = nxt;
-    }
-  }
-  if (tid == 0) s_before = 0.0;
-  // a chunk is always found (t < Z and the last running value is Z); clamp regardless
-  int cstar = block_min_i(cand, s_imin);
-  if (cstar == kNoPick) cstar = p.P - 1;
-  if (cstar >= c_lo && cstar < c_hi) {
-    double run = excl;
-    for (int c = c_lo; c < cstar; ++c) {
-      const float2 s = summary<DT, VEC, PUBLISHED>(part, c);
-      run += (double)s.y * exp2((double)(s.x * c2) - (double)R);
-    }
-    s_before = run;
-  }
-  __syncthreads();
 
   // rescan chunk cstar (one slab) in the chunk's own units 2^(l c2 - r_c)
   const float rc = summary<DT, VEC, PUBLISHED>(part, cstar).x * c2;
@@ -160,8 +195,9 @@ __device__ int sample_row(const TreeParams& p, const float2* part, const void* r
     if (off + incl[k] > rem && e[k] > 0.0f) pick = (int)(e0 + k);
   // the first position whose running value passes the target; rounding may leave the
   // target just past the chunk's last positive weight: then take that weight
-  pick = block_min_i(pick, s_imin);
-  const int y = pick != kNoPick ? pick : -block_min_i(-last_pos, s_imin);
+  int last_any;
+  pick = block_min_max_i(pick, last_pos, s_imin2, &last_any);
+  const int y = pick != kNoPick ? pick : last_any;
   *status = 0;
   return y;
 }
