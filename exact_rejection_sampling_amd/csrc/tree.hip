@@ -560,11 +560,23 @@ __device__ __forceinline__ int next_child(const int32_t* par, int N, int v, int 
 __device__ double mass_prefix(const double* mass, int P, int c_lo, int c_hi, double* total) {
   __shared__ double s_scan[kWavesPerBlock];
   __shared__ double s_total;
-  double mine = 0.0;
-  for (int c = c_lo; c < c_hi; ++c) mine += mass[c];
-  double tot;
-  const double excl = block_excl_scan_d(mine, s_scan, &tot);
-  if (c_lo < c_hi && c_hi == P) s_total = excl + mine;
+  double excl = 0.0;
+  if (P <= kWave) {
+    // every chunk in wave 0 (one per thread): its prefix is the block-wide one, as the other
+    // waves would only add zeros
+    if (wave_id() == 0) {
+      const int lane = threadIdx.x;
+      const double mine = lane < P ? mass[lane] : 0.0;
+      excl = 0.0 + wave_shr1_d(wave_incl_scan_d(mine, lane));
+      if (lane == P - 1) s_total = excl + mine;
+    }
+  } else {
+    double mine = 0.0;
+    for (int c = c_lo; c < c_hi; ++c) mine += mass[c];
+    double tot;
+    excl = block_excl_scan_d(mine, s_scan, &tot);
+    if (c_lo < c_hi && c_hi == P) s_total = excl + mine;
+  }
   __syncthreads();
   *total = s_total;
   __syncthreads();
@@ -580,31 +592,57 @@ __device__ int residual_pick(const TreeParams& p, int b, const unsigned long lon
                              float u) {
   __shared__ double s_scan[kWavesPerBlock];
   __shared__ int s_imin[kWavesPerBlock];
-  __shared__ double s_before;
+  __shared__ int s_imin2[2 * kWavesPerBlock];
+  __shared__ double s_before, s_w;
+  __shared__ int s_cstar;
   const int tid = threadIdx.x;
-  const int per = (p.P + kBlock - 1) / kBlock;
-  const int c_lo = min(tid * per, p.P), c_hi = min(c_lo + per, p.P);
+  int cstar;
   double W;
-  const double excl = mass_prefix(mass, p.P, c_lo, c_hi, &W);
-  const double t = (double)u * W;
-  int cand = kNoPick;
-  {
-    double run = excl;
-    for (int c = c_lo; c < c_hi; ++c) {
-      const double nxt = run + mass[c];
-      if (nxt > t) { cand = c; break; }
-      run = nxt;
+  if (p.P <= kWave) {
+    // every chunk in wave 0: the running masses as mass_prefix forms them, and the pick,
+    // with one barrier
+    if (wave_id() == 0) {
+      const double mine = tid < p.P ? mass[tid] : 0.0;
+      const double excl = 0.0 + wave_shr1_d(wave_incl_scan_d(mine, tid));
+      const double Ww = __shfl(excl + mine, p.P - 1, kWave);
+      const double tw = (double)u * Ww;
+      const unsigned long long hit = __ballot(tid < p.P && excl + mine > tw);
+      const int cs = hit ? __ffsll(static_cast<long long>(hit)) - 1 : p.P - 1;
+      const double before = __shfl(excl, cs, kWave);
+      if (tid == 0) {
+        s_w = Ww;
+        s_before = before;
+        s_cstar = cs;
+      }
     }
+    __syncthreads();
+    W = s_w;
+    cstar = s_cstar;
+  } else {
+    const int per = (p.P + kBlock - 1) / kBlock;
+    const int c_lo = min(tid * per, p.P), c_hi = min(c_lo + per, p.P);
+    const double excl = mass_prefix(mass, p.P, c_lo, c_hi, &W);
+    const double t = (double)u * W;
+    int cand = kNoPick;
+    {
+      double run = excl;
+      for (int c = c_lo; c < c_hi; ++c) {
+        const double nxt = run + mass[c];
+        if (nxt > t) { cand = c; break; }
+        run = nxt;
+      }
+    }
+    if (tid == 0) s_before = 0.0;
+    cstar = block_min_i(cand, s_imin);   // a chunk is always found (t < W); clamp regardless
+    if (cstar == kNoPick) cstar = p.P - 1;
+    if (cstar >= c_lo && cstar < c_hi) {
+      double run = excl;
+      for (int c = c_lo; c < cstar; ++c) run += mass[c];
+      s_before = run;
+    }
+    __syncthreads();
   }
-  if (tid == 0) s_before = 0.0;
-  int cstar = block_min_i(cand, s_imin);   // a chunk is always found (t < W); clamp regardless
-  if (cstar == kNoPick) cstar = p.P - 1;
-  if (cstar >= c_lo && cstar < c_hi) {
-    double run = excl;
-    for (int c = c_lo; c < cstar; ++c) run += mass[c];
-    s_before = run;
-  }
-  __syncthreads();
+  const double t = (double)u * W;
   const double rem = t - s_before;
   const long e0 = (long)cstar * kWaveChunk + (long)tid * kVec;
   float gv[1][8];
@@ -626,8 +664,9 @@ __device__ int residual_pick(const TreeParams& p, int b, const unsigned long lon
 #pragma unroll
   for (int k = 7; k >= 0; --k)
     if (off + incl[k] > rem && g[k] > 0.0f) pick = (int)(e0 + k);
-  pick = block_min_i(pick, s_imin);
-  return pick != kNoPick ? pick : -block_min_i(-last_pos, s_imin);
+  int last_any;
+  pick = block_min_max_i(pick, last_pos, s_imin2, &last_any);
+  return pick != kNoPick ? pick : last_any;
 }
 
 // Walk of request b by the last root block, residual-update verifier ([M7.7] §0x09A):
