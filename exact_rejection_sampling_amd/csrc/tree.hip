@@ -508,9 +508,12 @@ __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
       if (code != 0) { tree_fail(p, b, code); return; }
     }
     if (status != 0) { tree_fail(p, b, status); return; }
-    int cand = kNoPick;           // this thread's lowest matching child (c rises)
-    for (int c = v + 1 + tid; c < N; c += kBlock)
-      if (cand == kNoPick && par[c] == v && tok[c] == y) cand = c;
+    // this thread's lowest matching child: first the node whose parent and token it holds
+    // since the validation (1 + tid), then the nodes beyond those (c rises)
+    int cand = kNoPick;
+    if (1 + tid < N && 1 + tid > v && check.pv == v && check.tv == y) cand = 1 + tid;
+    for (int c = 1 + kBlock + tid; c < N; c += kBlock)
+      if (cand == kNoPick && c > v && par[c] == v && tok[c] == y) cand = c;
     const int child = block_min_i(cand, s_imin);
     if (child == kNoPick) {
       for (int i = tid; i < N; i += kBlock) {
@@ -545,11 +548,15 @@ __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
 }
 
 // Next child of v after `after` in index order (children have larger indices than their
-// parent), block-wide; kNoPick if there is none.
-__device__ __forceinline__ int next_child(const int32_t* par, int N, int v, int after, int* s_imin) {
+// parent), block-wide; kNoPick if there is none.  Thread t holds node 1 + t's parent since
+// the validation (k); only the nodes beyond those are read again.
+__device__ __forceinline__ int next_child(const TreeCheck& k, const int32_t* par, int N, int v, int after,
+                                          int* s_imin) {
+  const int tid = threadIdx.x;
   int cand = kNoPick;
-  for (int c = after + 1 + threadIdx.x; c < N; c += kBlock)
-    if (cand == kNoPick && par[c] == v) cand = c;
+  if (1 + tid < N && 1 + tid > after && k.pv == v) cand = 1 + tid;
+  for (int c = 1 + kBlock + tid; c < N; c += kBlock)
+    if (cand == kNoPick && c > after && par[c] == v) cand = c;
   return block_min_i(cand, s_imin);
 }
 
@@ -736,7 +743,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
 
     // 2. the children, in index order
     int i = 0, accepted = kNoPick;
-    int c = next_child(par, N, v, v, s_imin);
+    int c = next_child(check, par, N, v, v, s_imin);
     while (c != kNoPick) {
       // the accept test's loads, issued together: thread 0 the child's q(x), u and the row's
       // logit at x; threads 1 .. kBlock - 1 the q values at x of the staged rejected children
@@ -836,7 +843,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
         if (i - 1 < kResidStage) s_invw[i - 1] = invw;
       }
       SPEC_STAMP_AT(p, 3, prec, 3);
-      c = next_child(par, N, v, c, s_imin);
+      c = next_child(check, par, N, v, c, s_imin);
     }
     if (accepted != kNoPick) {
       if (tid == 0) {
