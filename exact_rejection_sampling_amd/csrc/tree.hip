@@ -686,6 +686,8 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
   __shared__ int s_lost, s_status, s_accept;
   __shared__ int s_imin[kWavesPerBlock];
   __shared__ float s_red[kWavesPerBlock];
+  __shared__ float s_rz_r;
+  __shared__ double s_rz_z;
   __shared__ double s_scan[kWavesPerBlock];
   __shared__ float2 s_sum[kTreeStage];
   __shared__ double s_mass[kTreeStage];
@@ -726,17 +728,37 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
     }
     if (s_lost) { tree_fail(p, b, SPEC_REQ_INTERNAL); return; }
     // reference exponent r = fp32(max raw logit * c2) and Z = sum 2^(l c2 - r) in fp64
-    float m = -INFINITY;
-    for (int c = tid; c < P; c += kBlock) m = fmaxf(m, s_sum[c].x);
-    m = wave_max(m);
-    if (lane == 0) s_red[wave] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    const float r = m * p.c2;
-    double zt = 0.0;
-    for (int c = tid; c < P; c += kBlock) zt += (double)s_sum[c].y * exp2((double)(s_sum[c].x * p.c2) - (double)r);
+    float r;
     double Z;
-    block_excl_scan_d(zt, s_scan, &Z);
+    if (P <= kWave) {
+      // every summary in wave 0 (one per thread): r and Z as the block-wide reductions form
+      // them (the other waves would add -inf to the maximum and zeros to the sum), one barrier
+      if (wave == 0) {
+        const float mw = wave_max(lane < P ? s_sum[lane].x : -INFINITY);
+        const float rw = mw * p.c2;
+        const double zt =
+            lane < P ? (double)s_sum[lane].y * exp2((double)(s_sum[lane].x * p.c2) - (double)rw) : 0.0;
+        const double Zw = 0.0 + __shfl(wave_incl_scan_d(zt, lane), kWave - 1, kWave);
+        if (lane == 0) {
+          s_rz_r = rw;
+          s_rz_z = Zw;
+        }
+      }
+      __syncthreads();
+      r = s_rz_r;
+      Z = s_rz_z;
+    } else {
+      float m = -INFINITY;
+      for (int c = tid; c < P; c += kBlock) m = fmaxf(m, s_sum[c].x);
+      m = wave_max(m);
+      if (lane == 0) s_red[wave] = m;
+      __syncthreads();
+      m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+      r = m * p.c2;
+      double zt = 0.0;
+      for (int c = tid; c < P; c += kBlock) zt += (double)s_sum[c].y * exp2((double)(s_sum[c].x * p.c2) - (double)r);
+      block_excl_scan_d(zt, s_scan, &Z);
+    }
     if (!(isfinite(Z) && Z > 0.0)) { tree_fail(p, b, SPEC_REQ_NONFINITE); return; }
     const float inv_z = (float)(1.0 / Z);
     SPEC_STAMP_AT(p, 3, trec, 3);
