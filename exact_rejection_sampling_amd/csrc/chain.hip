@@ -250,6 +250,11 @@ __device__ __forceinline__ void chain_decide(const ChainParams& p, int b, RowSta
     __syncthreads();
     return;
   }
+  // the decision is a chain of dependent steps on the call's critical path, sharing its SIMD
+  // with streaming waves: the highest wave priority lets it issue first (measured 1 us off
+  // the headline call; levels 1 and 2 gave less, and raising the selector's waves as well
+  // gave nothing)
+  __builtin_amdgcn_s_setprio(3);
   constexpr int kPre = 4;                       // slices per lane and pass kept in registers
   const int lane = threadIdx.x & (kWave - 1);
   const float c2 = p.c2;
@@ -427,6 +432,7 @@ __device__ __forceinline__ void chain_decide(const ChainParams& p, int b, RowSta
     s_dec.inv_z = drawn ? (float)(1.0 / rs.z[A]) : 0.0f;
   }
   SPEC_STAMP(p, 0, 10);  // decided (before the block barrier)
+  __builtin_amdgcn_s_setprio(0);
   __syncthreads();
 }
 
