@@ -34,7 +34,9 @@ def test_config1_small(run):
 @pytest.mark.parametrize("V,dtype,T", [
     (1, "f32", 1.0), (2, "bf16", 0.8), (7, "f32", 1.3), (33, "bf16", 0.8), (2047, "f32", 1.0),
     (2048, "bf16", 0.8), (2049, "f32", 0.8), (8191, "bf16", 1.0), (8193, "bf16", 0.5),
-    (20003, "bf16", 0.8), (32000, "bf16", 0.8), (32000, "f32", 1.0)])
+    (20003, "bf16", 0.8), (32000, "bf16", 0.8), (32000, "f32", 1.0),
+    # 64 terminal chunks, the most the selector's one-wave pick takes, and one element more
+    (262144, "bf16", 0.8), (262145, "f32", 1.0)])
 def test_ragged_vocab(V, dtype, T):
     x = synth.make_chain(16, 5, V, seed=77 + V, logit_dtype=dtype, sigma=3.0, boost_frac=0.01,
                          noise=1.0, temperature=T)

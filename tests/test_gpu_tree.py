@@ -46,7 +46,10 @@ def test_config5_deep_variant():
 
 
 @pytest.mark.parametrize("V,dtype,N,T", [(1, "bf16", 3, 1.0), (5, "f32", 9, 0.7), (2049, "bf16", 31, 1.0),
-                                         (8193, "f32", 17, 1.3), (40000, "bf16", 63, 0.9)])
+                                         (8193, "f32", 17, 1.3), (40000, "bf16", 63, 0.9),
+                                         # 128 chunk summaries, the most the walker's one-wave
+                                         # sample takes, and one element more
+                                         (262144, "bf16", 15, 1.0), (262145, "f32", 15, 0.8)])
 def test_ragged(V, dtype, N, T):
     x = synth.make_tree(8, N, V, seed=V + N, logit_dtype=dtype, temperature=T,
                         max_depth=min(6, N - 1), max_children=4, boost=6.0)

@@ -56,7 +56,10 @@ def test_per_child_proposals_and_bf16_q():
 
 
 @pytest.mark.parametrize("V,dt", [(1, "f32"), (7, "bf16"), (2049, "f32"), (4097, "bf16"), (20003, "bf16"),
-                                  (65536, "f32")])
+                                  (65536, "f32"),
+                                  # 64 chunks, the most the walker's one-wave steps take, and one
+                                  # element more
+                                  (131072, "bf16"), (131073, "f32")])
 def test_ragged(V, dt):
     x = synth.make_tree_residual(12, 17, V, seed=60 + V, logit_dtype=dt, sigma=2.0, noise=1.5,
                                  temperature=0.9, max_depth=3, max_children=3)
