@@ -221,7 +221,7 @@ spec_status spec_verify_chain_ex(const void* target_logits, int logit_dtype, con
   p.G = gamma;
   p.R = gamma + 1;
   p.V = V;
-  const sv::Slicing sl = sv::slicing((long)B * (gamma + 1), V, sv::kChainTargetBlocks);
+  const sv::Slicing sl = sv::chain_slicing((long)B * (gamma + 1), V, logit_dtype == SPEC_F32 ? 4 : 2);
   p.P = sl.P;
   p.CPW = sl.CPW;
   p.SL = sl.SL;

@@ -1262,7 +1262,7 @@ hipError_t launch_typed(ChainParams p, hipStream_t s) {
   }
   const long per_req = (long)p.R * p.SL + p.S2;
   p.LAG = (int)lag_requests(p.J > 1 ? kLazyLagTenths : kLagTenths, s_resident[dev], per_req, p.B);
-  const unsigned long long blocks = (unsigned long long)p.B * ((unsigned long long)p.R * p.SL + p.S2);  // == chain_blocks
+  const unsigned long long blocks = (unsigned long long)p.B * ((unsigned long long)p.R * p.SL + p.S2);  // <= chain_blocks
   chain_kernel<DT, QT, VEC, PROC><<<dim3((unsigned)blocks), dim3(kBlock), chain_dyn_lds(), s>>>(p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

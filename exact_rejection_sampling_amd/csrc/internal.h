@@ -268,10 +268,18 @@ struct ChainLayout {
 #define SPEC_CHAIN_TARGET_BLOCKS 4096
 #endif
 constexpr long kChainTargetBlocks = SPEC_CHAIN_TARGET_BLOCKS;
-// The chain uses no counters: its regions start after the global header.
+// The target counts blocks of bf16 logits: fp32 rows take twice as many blocks, so that a
+// statistics item streams the same bytes in either dtype (fp32 calls at config 3 measured
+// 53.1 us with one wave chunk per wave against 54.5 us with two; bf16 calls are fastest
+// with two).  A larger target never gives fewer slices, so the fp32 slicing bounds both.
+inline Slicing chain_slicing(long rows, long V, int logit_bytes) {
+  return slicing(rows, V, logit_bytes > 2 ? 2 * kChainTargetBlocks : kChainTargetBlocks);
+}
+// The chain uses no counters: its regions start after the global header.  The summaries'
+// region holds the fp32 slicing, the larger one.
 inline ChainLayout chain_layout(long B, long G, long V) {
   const long R = G + 1, S2 = (V + kTermChunk - 1) / kTermChunk;
-  const long SL = slicing(B * R, V, kChainTargetBlocks).SL;
+  const long SL = chain_slicing(B * R, V, 4).SL;
   ChainLayout L;
   size_t o = kGlobalCounterBytes;
   L.part = o;   o = align256(o + sizeof(float2) * B * R * SL);
@@ -334,10 +342,11 @@ inline TreeLayout tree_layout(long B, long N, long V, bool residual = false) {
 }
 
 // Grid sizes of the launches.  A dispatch counts work-items in 32 bits, so a launch
-// holds at most floor((2^32 - 1) / kBlock) blocks; grid_fits says whether it does.
+// holds at most floor((2^32 - 1) / kBlock) blocks; grid_fits says whether it does.  The
+// chain's is the grid of fp32 logits, the larger one.
 inline unsigned long long chain_blocks(long B, long G, long V) {
   const long R = G + 1, S2 = (V + kTermChunk - 1) / kTermChunk;
-  return (unsigned long long)B * ((unsigned long long)R * slicing(B * R, V, kChainTargetBlocks).SL + S2);
+  return (unsigned long long)B * ((unsigned long long)R * chain_slicing(B * R, V, 4).SL + S2);
 }
 inline unsigned long long greedy_blocks(long B, long G, long V) {
   const long R = G + 1;
