@@ -387,6 +387,8 @@ spec_status spec_verify_tree_greedy(const void* node_logits, int logit_dtype, co
   p.part = reinterpret_cast<float2*>(ws + L.part);
   p.deep = reinterpret_cast<float2*>(ws + L.deep);
   p.order = reinterpret_cast<unsigned long long*>(ws + L.order);
+  p.spec = reinterpret_cast<float2*>(ws + L.spec);
+  p.stag = reinterpret_cast<unsigned*>(ws + L.stag);
   p.counters = sv::request_counters(workspace);
   p.B = B;
   p.N = N;

@@ -197,6 +197,11 @@ struct TreeParams {
                              // double-buffered by order generation
   unsigned long long* order; // [B] the walking block's order to its helpers
   unsigned* counters;        // per-request slots: [b*4 + 0] root arrivals, [b*4 + 1] helpers gone
+  // greedy trees only (null otherwise): the summaries of the root's child that the helpers
+  // stream before the first order [B*P], and that child + 1 per request [B] (kNoSpec when
+  // the root has no child to stream; 0 until published)
+  float2* spec;
+  unsigned* stag;
   int B, N, V, P, WG1, WH;
   float c2;
   // residual-update verifier only
@@ -328,7 +333,7 @@ inline GreedyLayout greedy_layout(long B, long G, long V) {
   return L;
 }
 
-struct TreeLayout { size_t part, deep, order, desc, total; };
+struct TreeLayout { size_t part, deep, order, desc, spec, stag, total; };
 inline TreeLayout tree_layout(long B, long N, long V, bool residual = false) {
   const long P = (V + 2047) / 2048;
   TreeLayout L;
@@ -337,6 +342,8 @@ inline TreeLayout tree_layout(long B, long N, long V, bool residual = false) {
   L.deep = o;   o = align256(o + sizeof(float2) * B * 2 * P);
   L.order = o;  o = align256(o + sizeof(unsigned long long) * B);
   L.desc = o;   if (residual) o = align256(o + sizeof(unsigned long long) * B * (3 + 2 * N));
+  L.spec = o;   if (!residual) o = align256(o + sizeof(float2) * B * P);
+  L.stag = o;   if (!residual) o = align256(o + sizeof(unsigned) * B);
   L.total = o;
   return L;
 }

@@ -153,3 +153,57 @@ def test_workspace_returns_to_zero_and_repeats():
     assert int(ws.count_nonzero()) == 0
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+def _streamed_ahead_request(kind, rng, N, V):
+    """One request whose root children are laid out for one outcome of the helpers' guess of
+    the root child: 'hit' (the walk's child is the guess), 'tie' (two tokens share the root
+    maximum; the walk takes the lower token, and so does the guess), 'miss' (the walk's child
+    is node 280, past the nodes the guess looks at, while nodes 1..4 are root children too),
+    'none' (no root child among nodes 1..256 has a finite logit: nothing is streamed ahead)
+    and 'stay' (no root child carries the root's argmax token)."""
+    par = np.full(N, 1, np.int32)
+    par[0] = -1
+    par[1] = 0
+    rows = rng.normal(0.0, 1.0, (N, V)).astype(np.float32)
+    tok = rng.permutation(V)[:N].astype(np.int32)          # distinct tokens
+    kids = {"hit": [1, 2, 3, 4, 5], "tie": [1, 2, 3, 4, 5], "miss": [1, 2, 3, 4, 280],
+            "none": [1, 270, 290], "stay": [1, 2, 3, 4, 5]}[kind]
+    for c in kids:
+        par[c] = 0
+    target = {"hit": 3, "tie": 5, "miss": 280, "none": 290, "stay": None}[kind]
+    if kind == "none":
+        rows[0, tok[1]] = -np.inf                          # node 1 cannot be guessed
+    if kind == "tie":
+        lo, hi = sorted(int(t) for t in rng.choice(V, 2, replace=False))
+        tok[5], tok[2] = lo, hi                            # node 2 carries the higher token
+        rows[0, lo] = rows[0, hi] = 10.0
+    elif target is not None:
+        rows[0, tok[target]] = 10.0
+    if target is not None:                                 # two more levels below the target
+        a, bb = (6, 7) if target < 256 else (target + 1, target + 2)
+        par[a], par[bb] = target, a
+        rows[target, tok[a]] = 10.0
+        rows[a, tok[bb]] = 10.0
+    return par, tok, rows
+
+
+def test_root_child_streamed_ahead_hit_miss_and_none():
+    """The greedy tree's helpers stream one root child's row ahead of the first order; every
+    outcome of that guess gives the oracle's walk, and the workspace returns to zero."""
+    B, N, V = 10, 300, 5000
+    rng = np.random.default_rng(97)
+    kinds = ["hit", "tie", "miss", "none", "stay"] * 2
+    parts = [_streamed_ahead_request(k, rng, N, V) for k in kinds]
+    parents = np.stack([p[0] for p in parts])
+    tokens = np.stack([p[1] for p in parts])
+    logits = np.stack([p[2] for p in parts])
+    x = synth.TreeInputs(B, N, V, np.float32(1.0), "f32", logits, tokens, parents, np.zeros((B, N), np.float32))
+    ws = torch.zeros(sv.tree_workspace_bytes(B, N, V) + 512, dtype=torch.uint8, device=DEV)
+    say("tree_greedy streamed-ahead root child: hit, tie, miss, none, stay")
+    got, exp = run(x, workspace_tensor=ws), expected(x)
+    compare_exact(got, exp, KEYS)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+    want = {"hit": 3, "tie": 3, "miss": 3, "none": 3, "stay": 0}
+    assert got["accepted_len"].tolist() == [want[k] for k in kinds]
