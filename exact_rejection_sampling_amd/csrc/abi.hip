@@ -434,6 +434,8 @@ spec_status spec_verify_tree_residual(const void* node_logits, int logit_dtype, 
   p.deep = reinterpret_cast<float2*>(ws + L.deep);
   p.order = reinterpret_cast<unsigned long long*>(ws + L.order);
   p.desc = reinterpret_cast<unsigned long long*>(ws + L.desc);
+  p.spec = reinterpret_cast<float2*>(ws + L.spec);
+  p.stag = reinterpret_cast<unsigned*>(ws + L.stag);
   p.desc_words = 3 + 2 * N;
   p.counters = sv::request_counters(workspace);
   p.B = B;

@@ -197,9 +197,10 @@ struct TreeParams {
                              // double-buffered by order generation
   unsigned long long* order; // [B] the walking block's order to its helpers
   unsigned* counters;        // per-request slots: [b*4 + 0] root arrivals, [b*4 + 1] helpers gone
-  // greedy trees only (null otherwise): the summaries of the root's child that the helpers
-  // stream before the first order [B*P], and that child + 1 per request [B] (kNoSpec when
-  // the root has no child to stream; 0 until published)
+  // greedy and residual-update trees (null for the sampled membership walk): the summaries
+  // of the root's child that the helpers stream before the first order [B*P], and that
+  // child + 1 per request [B] (kNoSpec when the root has no child to stream; 0 until
+  // published)
   float2* spec;
   unsigned* stag;
   int B, N, V, P, WG1, WH;
@@ -342,8 +343,8 @@ inline TreeLayout tree_layout(long B, long N, long V, bool residual = false) {
   L.deep = o;   o = align256(o + sizeof(float2) * B * 2 * P);
   L.order = o;  o = align256(o + sizeof(unsigned long long) * B);
   L.desc = o;   if (residual) o = align256(o + sizeof(unsigned long long) * B * (3 + 2 * N));
-  L.spec = o;   if (!residual) o = align256(o + sizeof(float2) * B * P);
-  L.stag = o;   if (!residual) o = align256(o + sizeof(unsigned) * B);
+  L.spec = o;   o = align256(o + sizeof(float2) * B * P);
+  L.stag = o;   o = align256(o + sizeof(unsigned) * B);
   L.total = o;
   return L;
 }

@@ -13,8 +13,10 @@
 //     blocks to summarize the child's row (each helper streams 8 chunks of it); otherwise
 //     y is the terminal token and the helpers are dismissed.
 // In the greedy tree (the argmax in place of the sample) the helpers first stream ahead the
-// one root child a walk leaving the root can take, and the walker reads those summaries
-// instead of ordering that row.  Otherwise only rows on the walked path are read.  Waits: the helpers wait for their walker, a
+// one root child a walk leaving the root can take, and in the residual-update tree the
+// root's first child (the first one tested); the walker reads those summaries instead of
+// ordering that row when its walk goes there.  Otherwise only rows on the walked path are
+// read.  Waits: the helpers wait for their walker, a
 // lower-numbered block; the walker waits for its request's other root blocks and helpers,
 // which follow it directly.  Each XCD dispatches the workgroups it is given in index order,
 // so once every earlier request has finished, all of a request's workgroups are dispatched
@@ -730,8 +732,12 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
   unsigned g1 = 0;   // thread 0: the generation of the current node's first pass order
   // the tree's validation: loads now, outcome once the root's summaries are staged
   const TreeCheck check = tree_check_issue(p, par, tok, N);
+  // which root child the helpers stream ahead (read now, awaited once a root child is accepted)
+  unsigned stag = p.spec && tid == 0 ? fetch_u32(p.stag + b) : 0u;
+  __shared__ int s_ahead;
 
   int v = 0, depth = 0, hop = 0;
+  bool ahead = false;   // this row's summaries are the streamed-ahead ones
   while (true) {
     const unsigned long long trec = hop_record(p, b, hop++);
     SPEC_TAG_AT(p, 3, trec, SPEC_TRACE_TAG(kTraceNode, b, v));
@@ -740,14 +746,15 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
     // 1. the row's chunk summaries: the root items' or, below the root, the helpers'
     if (tid == 0) s_lost = 0;
     __syncthreads();
-    float2* src = v == 0 ? p.part + (size_t)b * P : p.deep + ((size_t)b * 2 + (gen & 1u)) * P;
+    float2* src = v == 0 ? p.part + (size_t)b * P
+                 : ahead ? p.spec + (size_t)b * P : p.deep + ((size_t)b * 2 + (gen & 1u)) * P;
     stage_summaries(src, s_sum, P, &s_lost);
     SPEC_STAMP_AT(p, 3, trec, 2);
     if (v == 0) {
       const int code = tree_check_done(par, tok, N, p.V, check);
       if (code != 0) { tree_fail(p, b, code); return; }
     }
-    if (v != 0) {
+    if (v != 0 && !ahead) {   // (the streamed-ahead words are cleared by the last helper)
       for (int c = tid; c < P; c += kBlock) clear_f2(src + c);
       vmem_wait();
     }
@@ -896,14 +903,24 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
       if (tid == 0) {
         p.out_tokens[(size_t)b * N + depth] = tok[accepted];
         p.out_nodes[(size_t)b * N + depth] = accepted;
-        publish_order(p, b, ++gen, static_cast<unsigned>(accepted) + 1u);   // summarize its row
+        bool hit = false;
+        if (v == 0 && p.spec) {
+          for (unsigned spins = 0; stag == 0u && spins < kSpinLimit; ++spins) {
+            __builtin_amdgcn_s_sleep(1);
+            stag = fetch_u32(p.stag + b);
+          }
+          hit = stag == static_cast<unsigned>(accepted) + 1u;   // (a tag that never came: no hit)
+        }
+        if (!hit) publish_order(p, b, ++gen, static_cast<unsigned>(accepted) + 1u);   // summarize its row
         s_gen = gen;
+        s_ahead = hit ? 1 : 0;
       }
       SPEC_STAMP_AT(p, 3, trec, 4);
       ++depth;
       v = accepted;
       __syncthreads();
       gen = s_gen;
+      ahead = s_ahead != 0;
       continue;
     }
 
@@ -1032,8 +1049,25 @@ __device__ void helper_speculate(const TreeParams& p, int b, int h) {
                                          p.spec + (size_t)b * p.P, h);
 }
 
+// Before the first order, a residual-update tree's helpers stream ahead the row of the
+// root's first child (the lowest index among nodes 1..kBlock whose parent is the root): the
+// child the walker tests first, whose row it needs next whenever that child is accepted.
+// Helper 0 publishes which child it is (the tag), as for the greedy tree.
+template <int DT, bool VEC>
+__device__ void helper_speculate_first(const TreeParams& p, int b, int h) {
+  __shared__ int s_imin[kWavesPerBlock];
+  const int tid = threadIdx.x, N = p.N, c = 1 + tid;
+  const int cand = c < N && p.parents[(size_t)b * N + c] == 0 ? c : kNoPick;
+  const int child = block_min_i(cand, s_imin);
+  if (h == 0 && tid == 0) publish_u32(p.stag + b, child == kNoPick ? kNoSpec : static_cast<unsigned>(child) + 1u);
+  if (child == kNoPick) return;
+  helper_summaries<DT, VEC, true, false>(p, row_ptr<DT>(p.logits, (size_t)b * N + child, p.V),
+                                         p.spec + (size_t)b * p.P, h);
+}
+
 // Helper h of request b: summarizes its chunks of every row the walker orders, until
-// dismissed (in a greedy tree, first those of the root child it streams ahead); the
+// dismissed (in a greedy or residual-update tree, first those of the root child it streams
+// ahead); the
 // last helper of the request to leave returns the order word, and the streamed-ahead
 // words, to zero.
 template <int DT, int QT, bool VEC, bool RESID, bool ARGMAX>
@@ -1043,8 +1077,11 @@ __device__ void helper_item(const TreeParams& p, int b, int h) {
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   const unsigned long long* order = p.order + b;
   unsigned last_gen = 0;
-  if constexpr (ARGMAX)
+  if constexpr (ARGMAX) {
     if (p.spec) helper_speculate<DT, VEC>(p, b, h);
+  } else if constexpr (RESID) {
+    if (p.spec) helper_speculate_first<DT, VEC>(p, b, h);
+  }
   while (true) {
     if (threadIdx.x == 0) {
       unsigned long long o = fetch_u64(order);
@@ -1070,7 +1107,7 @@ __device__ void helper_item(const TreeParams& p, int b, int h) {
     const void* row = row_ptr<DT>(p.logits, (size_t)b * p.N + (code - 1u), p.V);
     helper_summaries<DT, VEC, RESID, ARGMAX>(p, row, p.deep + ((size_t)b * 2 + (gen & 1u)) * p.P, h);
   }
-  if constexpr (ARGMAX) {
+  if constexpr (ARGMAX || RESID) {
     // this block's summary stores are complete before it counts itself out, so that the
     // last helper's clears below follow every helper's stores
     vmem_wait();
@@ -1083,7 +1120,7 @@ __device__ void helper_item(const TreeParams& p, int b, int h) {
       reset_counter(&p.counters[(size_t)b * kCounterSlots + 1]);
     }
   }
-  if constexpr (ARGMAX) {
+  if constexpr (ARGMAX || RESID) {
     if (p.spec) {           // the streamed-ahead child's words, read (or not) by the walker
       __syncthreads();
       if (s_last) {

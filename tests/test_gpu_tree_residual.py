@@ -197,3 +197,60 @@ def test_extreme_temperatures(T):
     say(f"tree_residual T={T}")
     got, exp = check(x)
     print("accepted", got["accepted_len"].tolist(), "flagged", int(exp["flagged"].sum()))
+
+
+def _first_child_request(kind, rng, N, V):
+    """One request for the helpers' streamed-ahead first root child (node 1, the child the
+    walker tests first): 'hit' accepts node 1; 'miss' rejects node 1 and accepts node 2;
+    'far' rejects nodes 1, 2 and 3 and accepts node 280.  A rejected child's proposal is a point
+    mass at its token, so that its acceptance probability p(x) stays far below its uniform;
+    an accepted child has uniform 0.  The walk below the accepted child goes two levels
+    deeper, and the filler nodes hang under node 3, which is reached only in 'far', where it
+    is rejected before its children are read."""
+    par = np.full(N, 3, np.int32)
+    par[0], par[1], par[2], par[3] = -1, 0, 0, 0
+    tok = rng.integers(0, V, N).astype(np.int32)
+    logits = rng.normal(0.0, 1.0, (N, V)).astype(np.float32)
+    q = np.exp(rng.normal(0.0, 1.0, (N, V))).astype(np.float32)
+    q /= q.sum(axis=1, keepdims=True)
+    u_acc = np.full(N, 0.5, np.float32)
+    u_draw = rng.random(N).astype(np.float32)
+
+    def reject(c):
+        q[c] = 0.0
+        q[c, tok[c]] = 1.0
+        u_acc[c] = np.float32(0.999999)
+
+    if kind == "far":
+        par[280] = 0
+    accepted = {"hit": 1, "miss": 2, "far": 280}[kind]
+    for c in {"hit": [], "miss": [1], "far": [1, 2, 3]}[kind]:
+        reject(c)
+    u_acc[accepted] = 0.0
+    a, bb = (4, 5) if accepted < 4 else (accepted + 1, accepted + 2)
+    par[a], par[bb] = accepted, a
+    u_acc[a] = u_acc[bb] = 0.0
+    return par, tok, logits, q, u_acc, u_draw
+
+
+def test_first_root_child_streamed_ahead_hit_and_miss():
+    """The residual-update tree's helpers stream the root's first child ahead of the first
+    order; a walk that accepts it, one that rejects it, and one that accepts a child past the
+    streamed range all match the oracle, and the workspace returns to zero."""
+    B, N, V = 6, 300, 3000
+    rng = np.random.default_rng(131)
+    kinds = ["hit", "miss", "far"] * 2
+    parts = [_first_child_request(k, rng, N, V) for k in kinds]
+    x = synth.TreeResidualInputs(B, N, V, np.float32(1.0), "f32", np.stack([p[2] for p in parts]),
+                                 np.stack([p[3] for p in parts]), np.stack([p[1] for p in parts]),
+                                 np.stack([p[0] for p in parts]), np.stack([p[4] for p in parts]),
+                                 np.stack([p[5] for p in parts]))
+    ws = torch.zeros(sv.tree_residual_workspace_bytes(B, N, V) + 512, dtype=torch.uint8, device="cuda:0")
+    say("tree_residual streamed-ahead first child: hit, miss, far")
+    got = run(x, workspace_tensor=ws)
+    exp = expected(x)
+    compare_exact(got, exp, KEYS, flagged=exp["flagged"])
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+    assert not exp["flagged"].any()
+    assert got["out_nodes"][:, 0].tolist() == [{"hit": 1, "miss": 2, "far": 280}[k] for k in kinds]
