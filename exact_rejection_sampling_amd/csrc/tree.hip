@@ -551,7 +551,7 @@ __device__ void tree_walk(const TreeParams& p, int b, unsigned& gen) {
       return;
     }
     if (tid == 0) {
-      p.out_tokens[(size_t)b * N + depth] = tok[child];
+      p.out_tokens[(size_t)b * N + depth] = y;   // the child matched by carrying token y
       p.out_nodes[(size_t)b * N + depth] = child;
       bool hit = false;
       if (ARGMAX && v == 0 && p.spec) {
@@ -796,7 +796,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
     SPEC_STAMP_AT(p, 3, trec, 3);
 
     // 2. the children, in index order
-    int i = 0, accepted = kNoPick;
+    int i = 0, accepted = kNoPick, accepted_x = 0;
     int c = next_child(check, par, N, v, v, s_imin);
     while (c != kNoPick) {
       // the accept test's loads, issued together: thread 0 the child's q(x), u and the row's
@@ -853,7 +853,11 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
       }
       __syncthreads();
       if (s_status) { tree_fail(p, b, s_status); return; }
-      if (s_accept) { accepted = c; break; }
+      if (s_accept) {
+        accepted = c;
+        accepted_x = x;
+        break;
+      }
       // rejected: the residual's chunk masses from a helper pass
       if (tid == 0) {
         const unsigned tag = gen + 1u;    // this pass order's generation, g1 + i
@@ -901,7 +905,7 @@ __device__ void tree_walk_residual(const TreeParams& p, int b, unsigned& gen) {
     }
     if (accepted != kNoPick) {
       if (tid == 0) {
-        p.out_tokens[(size_t)b * N + depth] = tok[accepted];
+        p.out_tokens[(size_t)b * N + depth] = accepted_x;
         p.out_nodes[(size_t)b * N + depth] = accepted;
         bool hit = false;
         if (v == 0 && p.spec) {
